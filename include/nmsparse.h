@@ -1,0 +1,224 @@
+/*
+ * nmsparse.h - C ABI of the MI355X (gfx950) N:M semi-structured sparsity library.
+ *
+ * The library implements the data-parallel hot path of post-training N:M
+ * sparsification of LLM linear layers: importance scores, per-group top-N mask
+ * selection, packing of kept values with their in-group positions, the
+ * sliding-window decomposition of (2N-2):2N into overlapping 2:4 windows, and
+ * the structured-sparse linear layer Y = X * W_hat^T on packed weights
+ * (bf16, and int8 activations x ternary int8 weights).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers owned by the caller unless the comment says
+ *    host.  The library never allocates, frees or synchronises; work is enqueued
+ *    on `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
+ *    call returns immediately.  NM_OK means "enqueued"; results are valid once
+ *    the caller synchronises the stream.
+ *  - Every argument is validated before anything is enqueued; on an error
+ *    nothing is written and the status says why.  nm_last_error() then returns
+ *    a message (thread-local, valid until the next call on this thread).
+ *    A failed kernel launch returns NM_ERR_DEVICE with HIP's message.
+ *  - Matrices are row-major with an explicit leading dimension (in elements,
+ *    except where noted).  Weights are [R = out_features, K = in_features];
+ *    activations are [tokens, K]; an N:M group is M consecutive weights of a
+ *    row along K.
+ *  - Mask bits: one bit per weight, LSB-first, uint8 [R, ldm bytes], ldm >= ceil(K/8).
+ *  - Packed weights: vals [R, ldv] holds the kept values of group g at
+ *    vals[g*N .. g*N+N-1] in ascending in-group position; idx [R, ldi uint32
+ *    words] is an LSB-first bitstream of b = ceil(log2 M)-bit in-group
+ *    positions, field j of a row at bits j*b .. j*b+b-1.  For 2:4 this is two
+ *    2-bit positions per group, 16 fields per word.  Every group always
+ *    carries N distinct ascending positions (padded with value 0 when a mask
+ *    row has fewer than N bits in a group).
+ *  - Lifted (slide) format: the 2:4 packed format over K' = (2 - 2/N) K, one
+ *    2:4 group per window, windows of a 2N-group in order.
+ *  - Alignment: base pointers must be 16-byte aligned and leading dimensions
+ *    multiples of 16 bytes where a kernel uses vector access (NM_ERR_ALIGN).
+ *  - Aliasing: outputs must not overlap inputs (NM_ERR_ALIAS).
+ *  - Calls are stateless and thread-safe; calls on different streams may overlap.
+ */
+#ifndef NMSPARSE_H
+#define NMSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NM_ABI_VERSION 1
+
+typedef void* nm_stream_t;
+
+typedef enum {
+    NM_OK = 0,
+    NM_ERR_NULL = 1,      /* required pointer is NULL */
+    NM_ERR_SHAPE = 2,     /* sizes negative, inconsistent, or beyond int32 exactness */
+    NM_ERR_PATTERN = 3,   /* unsupported N:M (or slide N) */
+    NM_ERR_DTYPE = 4,     /* unsupported dtype combination */
+    NM_ERR_ALIGN = 5,     /* pointer / leading dimension alignment */
+    NM_ERR_WORKSPACE = 6, /* workspace NULL or too small */
+    NM_ERR_DEVICE = 7,    /* HIP error (launch or device query) */
+    NM_ERR_ALIAS = 8      /* an output overlaps an input */
+} nm_status;
+
+typedef enum { NM_F32 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3 } nm_dtype;
+
+typedef enum { NM_SCORE_HESSIAN = 0, NM_SCORE_MAGNITUDE = 1 } nm_score_mode;
+
+int nm_abi_version(void);
+const char* nm_last_error(void);
+
+/* ---------------------------------------------------------------- curvature
+ * Diagonal Gauss-Newton proxy of a linear layer's Hessian from calibration
+ * activations: H[k] = sum_i X[i,k]^2.  ("Sparsity Induction", section 2C: the
+ * diagonal proxy lets importance scores refresh in O(d_in).)
+ * X: [n, K] bf16 or f32, leading dim ldx elements.  H: [K] f32 out.
+ * Accumulation is in f32 in a fixed (run-to-run identical) order.
+ * ws: device workspace of nm_colsumsq_workspace(n, K) bytes (may be NULL if 0). */
+size_t nm_colsumsq_workspace(int64_t n, int64_t K);
+nm_status nm_hdiag_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx,
+                            float* H, void* ws, size_t ws_bytes, nm_stream_t stream);
+
+/* Hutchinson estimate of the Hessian diagonal of the layer's quadratic output
+ * energy L(W) = ||X W^T||_F^2 with Rademacher probes ("SparseForge", Methodology
+ * 2: the diagonal is estimated stochastically because the full Hessian is
+ * prohibitive):  D = (1/P) sum_p V_p .* (H V_p),  H V = 2 (V X^T) X.
+ * V_p[o,k] in {-1,+1} is bit (k mod 64) of SplitMix64 output number
+ * p*2^40 + o*ceil(K/64) + floor(k/64) of a generator seeded with `seed`
+ * (bit set -> -1); it is generated in registers, never stored.
+ * X: [n, K] bf16 (ldx elements).  D: [R, K] f32 out (ldd elements).
+ * Both products run on bf16 MFMA with f32 accumulation; V X^T is rounded to
+ * bf16 before the second product.  Requires K % 64 == 0, n % 64 == 0.
+ * ws: nm_hutchinson_workspace(n, K, R, probes) bytes. */
+size_t nm_hutchinson_workspace(int64_t n, int64_t K, int64_t R, int probes);
+nm_status nm_hdiag_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes,
+                              uint64_t seed, float* D, int64_t ldd, void* ws, size_t ws_bytes,
+                              nm_stream_t stream);
+
+/* ---------------------------------------------------------------- score
+ * Importance score ("SparseForge", Methodology 2: s = (H + eps) * W^2 with H a
+ * Hessian-diagonal approximation; "Sparse-BitNet", section 2: magnitude |W|).
+ * HESSIAN: s = (h + eps) * (w * w) in f32, one rounding per operation in the
+ * order t = w*w, u = h + eps, s = u*t.  MAGNITUDE: s = |w| (H ignored).
+ * W: [R, K] bf16 or f32 (ldw).  H: f32, ldh == 0 -> one [K] vector for all rows,
+ * ldh >= K -> [R, K] (e.g. a Hutchinson diagonal).  S: [R, K] f32 out (lds). */
+nm_status nm_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
+                   const float* H, int64_t ldh, float eps, nm_score_mode mode,
+                   float* S, int64_t lds, nm_stream_t stream);
+
+/* Per-tensor standardisation statistics of a score matrix ("SparseForge",
+ * Methodology 2: scores are standardised before the temperature sigmoid).
+ * stats[0] = mean, stats[1] = population standard deviation, both f64, by a
+ * fixed-order two-pass reduction in f64.  ws: nm_stats_workspace(R, K) bytes. */
+size_t nm_stats_workspace(int64_t R, int64_t K);
+nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats,
+                         void* ws, size_t ws_bytes, nm_stream_t stream);
+
+/* Soft gate and annealing to a hard N:M mask ("SparseForge", Methodology 2
+ * and 3).  With z = (s - mean)/std (z = 0 when std == 0), for t = 0..steps-1:
+ *   T_t = T0 * rho^t,  beta_t = t/(steps-1),  g_t = sigmoid(z / T_t),
+ *   m_t = (1 - beta_t) g_t + beta_t h,   h = top-N of s per group,
+ *   lmid[t] = sum m_t (1 - m_t)   (f64, fixed-order reduction).
+ * The final projection keeps the top-N of m_{steps-1} per group -> hard_mask.
+ * m_final (nullable): m_{steps-1} as f32 [R, K] (ldf).  stats: device [2] from
+ * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0, steps >= 1.
+ * ws: nm_gate_workspace(R, K, steps) bytes. */
+size_t nm_gate_workspace(int64_t R, int64_t K, int steps);
+nm_status nm_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats,
+                  int N, int M, float T0, float rho, int steps,
+                  float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
+                  void* ws, size_t ws_bytes, nm_stream_t stream);
+
+/* ---------------------------------------------------------------- mask
+ * N:M top-N selection ("Sparse-BitNet", sections 1-2: keep the N largest of
+ * every M consecutive weights; "SparseForge", Methodology 3: the hard target is
+ * the top-N per group).  Ties go to the lower index, NaN ranks lowest, -0 equals
+ * +0; exactly N bits are set per group.  S: [R, K] f32 (lds).
+ * Supported: M in {4, 8}, 1 <= N < M, K % M == 0. */
+nm_status nm_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int M,
+                  uint8_t* mask, int64_t ldm, nm_stream_t stream);
+
+/* ---------------------------------------------------------------- pack
+ * Pack kept values and in-group positions (the compressed storage of an N:M
+ * weight; "SlideSparse", section 2C: weights are packed once, off the request
+ * path).  For each group the first N set mask bits (ascending) are kept;
+ * groups with fewer bits are padded with value 0 at the smallest unused
+ * positions.  W: [R, K] (ldw) of dtype wdt; vals: [R, ldv] of dtype vdt
+ * (f32 -> bf16 rounds to nearest even; otherwise the dtype must match);
+ * idx: [R, ldi] uint32 words.  Supported: M in {4, 8}, 1 <= N < M. */
+nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
+                  const uint8_t* mask, int64_t ldm, int N, int M, nm_dtype vdt,
+                  void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream);
+
+/* Fused score -> top-N mask -> pack in one pass over the weight.  The score is
+ * taken from Wsc (dtype sdt, lds_ elements; HESSIAN with H/ldh/eps as in
+ * nm_score, or MAGNITUDE), the packed values from Wv (dtype wdt, ldwv), which
+ * may be the same tensor.  Distinct tensors give "quantise then mask"
+ * ("Sparse-BitNet", section 2): the mask comes from high-precision master
+ * weights and is applied to their ternary code.  mask may be NULL. */
+nm_status nm_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh,
+                        float eps, nm_score_mode mode,
+                        const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N, int M,
+                        uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv,
+                        uint32_t* idx, int64_t ldi, nm_stream_t stream);
+
+/* ---------------------------------------------------------------- slide
+ * Sliding-window decomposition ("SlideSparse", section 2A): every 2N-wide group
+ * with at most 2N-2 kept positions is covered by N-1 windows of width 4 and
+ * stride 2 (window w covers positions 2w..2w+3), each a 2:4 group of the
+ * lifted weight of width K' = (2 - 2/N) K.  Kept positions (first 2N-2 set
+ * mask bits) are visited in ascending order and assigned to the earliest
+ * covering window with a free slot; windows are padded with value 0 at their
+ * smallest unused positions.  Output: lifted 2:4 vals [R, ldv] (ldv >= K'/2)
+ * and idx [R, ldi] (ldi >= K'/32).  Supported: 2 <= Ns <= 8, K % (2 Ns) == 0.
+ * Positions beyond a window's capacity (masks with more than 2N-2 bits in a
+ * group) are dropped. */
+nm_status nm_slide_decompose(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
+                             const uint8_t* mask, int64_t ldm, int Ns, nm_dtype vdt,
+                             void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream);
+
+/* Fused (2Ns-2):2Ns mask selection and slide decomposition: top-(2Ns-2) of
+ * every 2Ns by the score of Wsc (as nm_prune_pack), then the decomposition of
+ * Wv under that mask.  mask may be NULL. */
+nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh,
+                         float eps, nm_score_mode mode,
+                         const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int Ns,
+                         uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv,
+                         uint32_t* idx, int64_t ldi, nm_stream_t stream);
+
+/* Per-tensor scale of a ternary layer: alpha = mean |W| over R x K, reduced in
+ * f64 in a fixed order and rounded to f32 ("Sparse-BitNet", section 1-2:
+ * 1.58-bit weights carry one high-precision scale).  alpha: device f32 [1].
+ * ws: nm_stats_workspace(R, K) bytes. */
+nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha,
+                     void* ws, size_t ws_bytes, nm_stream_t stream);
+
+/* ---------------------------------------------------------------- sparse GEMM
+ * Structured-sparse linear layer Y = X * W_hat^T on packed weights
+ * ("SlideSparse", sections 2B-2C: the lifted activation is an index remap,
+ * applied while the activation tile is staged; the product then runs on 2:4
+ * sparse matrix instructions).  Runs on gfx950 SMFMAC (the packed weight is
+ * the sparse operand).
+ *   X: [Mtok, K] (ldx elements), K the ORIGINAL input width.
+ *   vals/idx: 2:4 packed weight over K (Ns == 0) or over the lifted width
+ *   K' = (2 - 2/Ns) K (Ns >= 3; supported Ns == 4, i.e. 6:8), rows R.
+ *   xdt/vdt: BF16/BF16 (f32 accumulation) or I8/I8 (exact int32 accumulation).
+ *   ydt: for BF16 inputs BF16 or F32; for I8 inputs I32 (raw sums), F32 or BF16.
+ *   Float outputs are y = acc when x_scale == NULL and w_scale == 1, else
+ *   y = (w_scale * x_scale[m]) * acc in f32 (x_scale NULL counts as 1).
+ *   Requires K % 16 == 0 (Ns == 0) or K % 8 == 0 (Ns == 4).
+ *   int8 requires K' * 127 * 127 < 2^31 so that int32 accumulation is exact.
+ * ws: nm_spmm_workspace(...) bytes (0 for most shapes; used for split-K). */
+size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
+nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,
+                  const void* vals, nm_dtype vdt, const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi,
+                  int Ns, const float* x_scale, float w_scale, void* Y, nm_dtype ydt, int64_t ldy,
+                  void* ws, size_t ws_bytes, nm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NMSPARSE_H */

@@ -1,0 +1,519 @@
+// Weight-side kernels of the N:M path: curvature column sums, importance
+// scores, top-N group masks, packing, the fused score->mask->pack pass and the
+// sliding-window (2N-2):2N decomposition.  All of them are bound by HBM
+// bandwidth: each weight is read once and its packed form written once.
+//
+// Sources: "SparseForge" (Methodology 2: s = (H+eps) W^2), "Sparse-BitNet"
+// (sections 1-2: N:M groups, magnitude top-N on master weights, quantise then
+// mask), "SlideSparse" (section 2A: N-1 width-4 stride-2 windows per 2N group),
+// "Sparsity Induction" (section 2C: diagonal Gauss-Newton proxy).
+#include "nm_internal.h"
+
+namespace nm {
+
+// ------------------------------------------------------------------ generic element access
+__device__ __forceinline__ float load_f32(const void* p, nm_dtype dt, int64_t i) {
+    switch (dt) {
+        case NM_F32: return ((const float*)p)[i];
+        case NM_BF16: return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+        case NM_I8: return (float)((const int8_t*)p)[i];
+        default: return (float)((const int32_t*)p)[i];
+    }
+}
+
+// dst[j] (vdt) <- src[i] (sdt): same dtype copies bits, f32 -> bf16 rounds to nearest even.
+__device__ __forceinline__ void store_conv(void* dst, nm_dtype vdt, int64_t j, const void* src, nm_dtype sdt,
+                                           int64_t i) {
+    if (vdt == NM_BF16) {
+        ((uint16_t*)dst)[j] = (sdt == NM_BF16) ? ((const uint16_t*)src)[i]
+                                                : (uint16_t)f32_to_bf16_bits(load_f32(src, sdt, i));
+    } else if (vdt == NM_I8) {
+        ((int8_t*)dst)[j] = ((const int8_t*)src)[i];
+    } else if (vdt == NM_F32) {
+        ((float*)dst)[j] = load_f32(src, sdt, i);
+    } else {
+        ((int32_t*)dst)[j] = ((const int32_t*)src)[i];
+    }
+}
+
+__device__ __forceinline__ void store_zero(void* dst, nm_dtype vdt, int64_t j) {
+    if (vdt == NM_BF16) ((uint16_t*)dst)[j] = 0;
+    else if (vdt == NM_I8) ((int8_t*)dst)[j] = 0;
+    else ((uint32_t*)dst)[j] = 0;
+}
+
+// Hessian-aware score with one rounding per operation: t = w*w, u = h+eps, s = u*t.
+__device__ __forceinline__ float hess_score(float w, float h, float eps) {
+    float t = __fmul_rn(w, w);
+    float u = __fadd_rn(h, eps);
+    return __fmul_rn(u, t);
+}
+
+__device__ __forceinline__ float score_at(const void* W, nm_dtype wdt, int64_t woff, const float* H, int64_t hoff,
+                                          float eps, nm_score_mode mode) {
+    float w = load_f32(W, wdt, woff);
+    return mode == NM_SCORE_MAGNITUDE ? fabsf(w) : hess_score(w, H[hoff], eps);
+}
+
+// Runtime-M top-N bits (M <= 16) with the same rule as topn_bits<M>.
+__device__ __forceinline__ uint32_t topn_bits_rt(const float* k, int M, int N) {
+    uint32_t bits = 0;
+    for (int i = 0; i < M; ++i) {
+        int beaten = 0;
+        for (int j = 0; j < M; ++j) {
+            if (j == i) continue;
+            beaten += ((j < i) ? (k[j] >= k[i]) : (k[j] > k[i])) ? 1 : 0;
+        }
+        if (beaten < N) bits |= 1u << i;
+    }
+    return bits;
+}
+
+__device__ __forceinline__ uint32_t mask_bits_at(const uint8_t* mask, int64_t ldm, int64_t r, int64_t k0, int M) {
+    uint32_t b = 0;
+    for (int i = 0; i < M; ++i) {
+        int64_t k = k0 + i;
+        b |= (uint32_t)((mask[r * ldm + (k >> 3)] >> (k & 7)) & 1u) << i;
+    }
+    return b;
+}
+
+// ------------------------------------------------------------------ A1: colsumsq
+constexpr int kColRows = 32;  // rows per partial block
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsumsq_partial_kernel(const T* __restrict__ X, int64_t n, int64_t K,
+                                                               int64_t ldx, float* __restrict__ part) {
+    constexpr int VEC = 16 / sizeof(T);
+    __shared__ float red[4][64 * VEC];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 64 * VEC + lane * VEC;
+    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
+    const int64_t r1 = r0 + kColRows < n ? r0 + kColRows : n;
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+    if (c0 < K) {
+        for (int64_t r = r0 + wave; r < r1; r += 4) {
+            const uint4 q = *(const uint4*)(X + r * ldx + c0);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                float x;
+                if constexpr (sizeof(T) == 2) x = bf16_bits_to_f32((u[v >> 1] >> (16 * (v & 1))) & 0xffffu);
+                else x = __uint_as_float(u[v]);
+                acc[v] = __fadd_rn(acc[v], __fmul_rn(x, x));
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[wave][lane * VEC + v] = acc[v];
+    __syncthreads();
+    if (wave == 0 && c0 < K) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const int c = lane * VEC + v;
+            float s = __fadd_rn(__fadd_rn(red[0][c], red[1][c]), __fadd_rn(red[2][c], red[3][c]));
+            part[(int64_t)blockIdx.y * K + c0 + v] = s;
+        }
+    }
+}
+
+__global__ void colsumsq_final_kernel(const float* __restrict__ part, int S, int64_t K, float* __restrict__ H) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= K) return;
+    float s = 0.f;
+    for (int i = 0; i < S; ++i) s = __fadd_rn(s, part[(int64_t)i * K + c]);
+    H[c] = s;
+}
+
+size_t colsumsq_ws(int64_t n, int64_t K) { return (size_t)ceil_div(n, kColRows) * (size_t)K * sizeof(float); }
+
+void launch_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx, float* H, void* ws,
+                     hipStream_t s) {
+    const int64_t S = ceil_div(n, kColRows);
+    float* part = (float*)ws;
+    if (n > 0) {
+        if (xdt == NM_BF16) {
+            dim3 g((unsigned)ceil_div(K, 64 * 8), (unsigned)S);
+            hipLaunchKernelGGL(colsumsq_partial_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, n, K, ldx,
+                               part);
+        } else {
+            dim3 g((unsigned)ceil_div(K, 64 * 4), (unsigned)S);
+            hipLaunchKernelGGL(colsumsq_partial_kernel<float>, g, dim3(256), 0, s, (const float*)X, n, K, ldx, part);
+        }
+    }
+    hipLaunchKernelGGL(colsumsq_final_kernel, dim3((unsigned)ceil_div(K, 256)), dim3(256), 0, s, part, (int)S, K, H);
+}
+
+// ------------------------------------------------------------------ A3: score
+__global__ __launch_bounds__(256) void score_kernel(const void* __restrict__ W, nm_dtype wdt, int64_t R, int64_t K,
+                                                    int64_t ldw, const float* __restrict__ H, int64_t ldh, float eps,
+                                                    nm_score_mode mode, float* __restrict__ S, int64_t lds) {
+    const int64_t total = R * K;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / K, k = t - r * K;
+        S[r * lds + k] = score_at(W, wdt, r * ldw + k, H, r * ldh + k, eps, mode);
+    }
+}
+
+void launch_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const float* H, int64_t ldh,
+                  float eps, nm_score_mode mode, float* S, int64_t lds, hipStream_t s) {
+    const int64_t total = R * K;
+    if (total == 0) return;
+    hipLaunchKernelGGL(score_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, W, wdt, R, K, ldw,
+                       H, ldh, eps, mode, S, lds);
+}
+
+// ------------------------------------------------------------------ A7: mask
+// One thread per mask byte (8 consecutive weights: two 4-groups or one 8-group).
+__global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ S, int64_t R, int64_t K, int64_t lds,
+                                                   int N, int M, uint8_t* __restrict__ mask, int64_t ldm) {
+    const int64_t bpr = ceil_div(K, 8);
+    const int64_t total = R * bpr;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / bpr, b = t - r * bpr;
+        const int64_t k0 = b * 8;
+        uint32_t byte = 0;
+        for (int g = 0; g < 8 / M; ++g) {
+            const int64_t kg = k0 + g * M;
+            if (kg >= K) break;
+            float key[8];
+            for (int i = 0; i < M; ++i) key[i] = rank_key(S[r * lds + kg + i]);
+            byte |= topn_bits_rt(key, M, N) << (g * M);
+        }
+        mask[r * ldm + b] = (uint8_t)byte;
+    }
+}
+
+void launch_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int M, uint8_t* mask, int64_t ldm,
+                 hipStream_t s) {
+    const int64_t total = R * ceil_div(K, 8);
+    if (total == 0) return;
+    hipLaunchKernelGGL(mask_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, S, R, K, lds, N, M,
+                       mask, ldm);
+}
+
+// ------------------------------------------------------------------ A8: pack (generic N:M)
+// A thread owns G consecutive groups of a row, G chosen so the chunk's index
+// bits fill whole 32-bit words; it streams its fields LSB-first into words.
+struct BitWriter {
+    uint64_t acc = 0;
+    int nbits = 0;
+    uint32_t* out;
+    __device__ BitWriter(uint32_t* o) : out(o) {}
+    __device__ __forceinline__ void put(uint32_t v, int b) {
+        acc |= (uint64_t)v << nbits;
+        nbits += b;
+        if (nbits >= 32) {
+            *out++ = (uint32_t)acc;
+            acc >>= 32;
+            nbits -= 32;
+        }
+    }
+    __device__ __forceinline__ void flush() {
+        if (nbits > 0) *out++ = (uint32_t)acc;
+        acc = 0;
+        nbits = 0;
+    }
+};
+
+// Streams mask bits LSB-first into whole bytes (chunks start on a byte boundary).
+struct MaskWriter {
+    uint32_t acc = 0;
+    int nbits = 0;
+    uint8_t* out;
+    __device__ MaskWriter(uint8_t* o) : out(o) {}
+    __device__ __forceinline__ void put(uint32_t v, int b) {
+        if (!out) return;
+        acc |= v << nbits;
+        nbits += b;
+        while (nbits >= 8) {
+            *out++ = (uint8_t)acc;
+            acc >>= 8;
+            nbits -= 8;
+        }
+    }
+    __device__ __forceinline__ void flush() {
+        if (out && nbits > 0) *out++ = (uint8_t)acc;
+        acc = 0;
+        nbits = 0;
+    }
+};
+
+inline int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
+
+// Select positions for one group: the first N set bits ascending, padded with
+// the smallest unset positions; returns them ascending in pos[], and whether
+// each carries a real value in real[] (bitmask).
+__device__ __forceinline__ uint32_t select_positions(uint32_t bits, int M, int N, int* pos) {
+    uint32_t chosen = 0, real = 0;
+    int cnt = 0;
+    for (int i = 0; i < M && cnt < N; ++i)
+        if ((bits >> i) & 1u) { chosen |= 1u << i; real |= 1u << i; ++cnt; }
+    for (int i = 0; i < M && cnt < N; ++i)
+        if (!((chosen >> i) & 1u)) { chosen |= 1u << i; ++cnt; }
+    int c = 0;
+    for (int i = 0; i < M; ++i)
+        if ((chosen >> i) & 1u) pos[c++] = i;
+    return real;
+}
+
+// mode_sel: 0 = bits from mask_in; 1 = select from score of Wsc.
+__global__ __launch_bounds__(256) void pack_generic_kernel(
+    int mode_sel, const void* __restrict__ Wsc, nm_dtype sdt, int64_t ldsc, const float* __restrict__ H, int64_t ldh,
+    float eps, nm_score_mode smode, const uint8_t* __restrict__ mask_in, uint8_t* __restrict__ mask_out, int64_t ldm,
+    const void* __restrict__ Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N, int M, int G, nm_dtype vdt,
+    void* __restrict__ vals, int64_t ldv, uint32_t* __restrict__ idx, int64_t ldi) {
+    const int b = (M == 4) ? 2 : 3;
+    const int64_t groups = K / M;
+    const int64_t cpr = ceil_div(groups, G);
+    const int64_t total = R * cpr;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / cpr, c = t - r * cpr;
+        const int64_t g0 = c * G;
+        const int64_t g1 = g0 + G < groups ? g0 + G : groups;
+        BitWriter bw(idx + r * ldi + (g0 * N * b) / 32);
+        MaskWriter mw(mode_sel ? (mask_out ? mask_out + r * ldm + (g0 * M) / 8 : nullptr) : nullptr);
+        for (int64_t g = g0; g < g1; ++g) {
+            const int64_t k0 = g * M;
+            uint32_t bits;
+            if (mode_sel == 0) {
+                bits = mask_bits_at(mask_in, ldm, r, k0, M);
+            } else {
+                float key[8];
+                for (int i = 0; i < M; ++i)
+                    key[i] = rank_key(score_at(Wsc, sdt, r * ldsc + k0 + i, H, r * ldh + k0 + i, eps, smode));
+                bits = topn_bits_rt(key, M, N);
+                mw.put(bits, M);
+            }
+            int pos[8];
+            const uint32_t real = select_positions(bits, M, N, pos);
+            for (int j = 0; j < N; ++j) {
+                const int64_t slot = g * N + j;
+                if ((real >> pos[j]) & 1u) store_conv(vals, vdt, r * ldv + slot, Wv, wdt, r * ldwv + k0 + pos[j]);
+                else store_zero(vals, vdt, r * ldv + slot);
+                bw.put((uint32_t)pos[j], b);
+            }
+        }
+        bw.flush();
+        mw.flush();
+    }
+}
+
+static int pack_chunk_groups(int N, int M) {
+    const int b = index_bits(M);
+    int G = 32 / gcd_i(N * b, 32);
+    if (M == 4 && (G & 1)) G *= 2;  // keep 4-groups paired so mask bytes are owned by one thread
+    return G;
+}
+
+void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                 int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
+    const int G = pack_chunk_groups(N, M);
+    const int64_t total = R * ceil_div(K / M, G);
+    if (total == 0) return;
+    hipLaunchKernelGGL(pack_generic_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, 0,
+                       (const void*)nullptr, NM_F32, (int64_t)0, (const float*)nullptr, (int64_t)0, 0.f,
+                       NM_SCORE_MAGNITUDE, mask, (uint8_t*)nullptr, ldm, W, wdt, ldw, R, K, N, M, G, vdt, vals, ldv,
+                       idx, ldi);
+}
+
+// ------------------------------------------------------------------ fused 2:4 fast path
+// Lane = 8 consecutive weights (two 4-groups); a quad of lanes = 32 weights =
+// one 32-bit index word, assembled across the quad with two xor-shuffles.
+// The lane writes its 4 kept values (8 bytes) and its mask byte directly.
+template <typename TW, bool HESS, bool HFULL>
+__global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict__ W, int64_t ldw,
+                                                           const float* __restrict__ H, int64_t ldh, float eps,
+                                                           int64_t R, int64_t K, uint8_t* __restrict__ mask,
+                                                           int64_t ldm, uint16_t* __restrict__ vals, int64_t ldv,
+                                                           uint32_t* __restrict__ idx, int64_t ldi) {
+    const int64_t wpr = (K + 31) >> 5;
+    const int64_t total = R * wpr * 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+        const int q = (int)(t & 3);
+        const int64_t wd = t >> 2;
+        const int64_t r = wd / wpr, wi = wd - r * wpr;
+        const int64_t k0 = (wi * 4 + q) * 8;
+        uint32_t nib = 0;
+        if (k0 < K) {
+            float w[8];
+            uint32_t wb[8];  // bf16 bit patterns of the values to store
+            if constexpr (sizeof(TW) == 2) {
+                const uint4 v = *(const uint4*)(W + r * ldw + k0);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    wb[i] = (u[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                    w[i] = bf16_bits_to_f32(wb[i]);
+                }
+            } else {
+                const float4 a = *(const float4*)(W + r * ldw + k0);
+                const float4 c = *(const float4*)(W + r * ldw + k0 + 4);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wb[i] = f32_to_bf16_bits(w[i]);
+            }
+            float key[8];
+            if constexpr (HESS) {
+                const float* hp = H + (HFULL ? r * ldh : 0) + k0;
+                const float4 h0 = *(const float4*)hp;
+                const float4 h1 = *(const float4*)(hp + 4);
+                const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) key[i] = rank_key(hess_score(w[i], h[i], eps));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) key[i] = rank_key(fabsf(w[i]));
+            }
+            uint32_t packed[2];
+            uint32_t mbyte = 0;
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
+                const uint32_t bits = topn_bits<4>(kk, 2);
+                const uint32_t p0 = __builtin_ctz(bits);
+                const uint32_t p1 = 31u - __builtin_clz(bits);
+                uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v0 = (p0 == (uint32_t)i) ? wb[4 * gi + i] : v0;
+                    v1 = (p1 == (uint32_t)i) ? wb[4 * gi + i] : v1;
+                }
+                packed[gi] = v0 | (v1 << 16);
+                mbyte |= bits << (4 * gi);
+                nib |= (p0 | (p1 << 2)) << (4 * gi);
+            }
+            *(uint2*)(vals + r * ldv + (k0 >> 1)) = make_uint2(packed[0], packed[1]);
+            if (mask) mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
+        }
+        uint32_t v = nib << (8 * q);
+        v |= (uint32_t)__shfl_xor((int)v, 1);
+        v |= (uint32_t)__shfl_xor((int)v, 2);
+        if (q == 0) idx[r * ldi + wi] = v;
+    }
+}
+
+void launch_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                       nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N,
+                       int M, uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
+                       int64_t ldi, hipStream_t s) {
+    const bool fast = (N == 2 && M == 4 && Wsc == Wv && sdt == wdt && ldsc == ldwv && vdt == NM_BF16 &&
+                       (sdt == NM_BF16 || sdt == NM_F32) && (K % 8) == 0);
+    if (fast) {
+        const int64_t total = R * ceil_div(K, 32) * 4;
+        if (total == 0) return;
+        const dim3 g(grid_cap(ceil_div(total, 256), 16384)), b(256);
+        const bool hess = mode == NM_SCORE_HESSIAN, hfull = ldh != 0;
+#define NM_PP24(TW, HS, HF)                                                                                         \
+    hipLaunchKernelGGL((prune_pack24_kernel<TW, HS, HF>), g, b, 0, s, (const TW*)Wv, ldwv, H, ldh, eps, R, K, mask, \
+                       ldm, (uint16_t*)vals, ldv, idx, ldi)
+        if (sdt == NM_BF16) {
+            if (!hess) NM_PP24(uint16_t, false, false);
+            else if (hfull) NM_PP24(uint16_t, true, true);
+            else NM_PP24(uint16_t, true, false);
+        } else {
+            if (!hess) NM_PP24(float, false, false);
+            else if (hfull) NM_PP24(float, true, true);
+            else NM_PP24(float, true, false);
+        }
+#undef NM_PP24
+        return;
+    }
+    const int G = pack_chunk_groups(N, M);
+    const int64_t total = R * ceil_div(K / M, G);
+    if (total == 0) return;
+    hipLaunchKernelGGL(pack_generic_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, 1, Wsc, sdt,
+                       ldsc, H, ldh, eps, mode, (const uint8_t*)nullptr, mask, ldm, Wv, wdt, ldwv, R, K, N, M, G, vdt,
+                       vals, ldv, idx, ldi);
+}
+
+// ------------------------------------------------------------------ A9: slide decomposition
+// A thread owns Gt consecutive 2N-groups of a row (Gt chosen so that the
+// chunk's 4 index bits per window fill whole words).  Per group: kept
+// positions ascending go to the earliest covering window with a free slot;
+// windows are padded with value 0 at their smallest unused positions.
+__global__ __launch_bounds__(256) void slide_kernel(int select, const void* __restrict__ Wsc, nm_dtype sdt,
+                                                    int64_t ldsc, const float* __restrict__ H, int64_t ldh, float eps,
+                                                    nm_score_mode smode, const uint8_t* __restrict__ mask_in,
+                                                    uint8_t* __restrict__ mask_out, int64_t ldm,
+                                                    const void* __restrict__ Wv, nm_dtype wdt, int64_t ldwv, int64_t R,
+                                                    int64_t K, int Ns, int Gt, nm_dtype vdt, void* __restrict__ vals,
+                                                    int64_t ldv, uint32_t* __restrict__ idx, int64_t ldi) {
+    const int Mg = 2 * Ns, Wn = Ns - 1;
+    const int64_t groups = K / Mg;
+    const int64_t cpr = ceil_div(groups, Gt);
+    const int64_t total = R * cpr;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / cpr, c = t - r * cpr;
+        const int64_t g0 = c * Gt;
+        const int64_t g1 = g0 + Gt < groups ? g0 + Gt : groups;
+        BitWriter bw(idx + r * ldi + (g0 * Wn * 4) / 32);
+        MaskWriter mw(select && mask_out ? mask_out + r * ldm + (g0 * Mg) / 8 : nullptr);
+        for (int64_t g = g0; g < g1; ++g) {
+            const int64_t k0 = g * Mg;
+            uint32_t bits;
+            if (select) {
+                float key[16];
+                for (int i = 0; i < Mg; ++i)
+                    key[i] = rank_key(score_at(Wsc, sdt, r * ldsc + k0 + i, H, r * ldh + k0 + i, eps, smode));
+                bits = topn_bits_rt(key, Mg, Mg - 2);
+                mw.put(bits, Mg);
+            } else {
+                bits = mask_bits_at(mask_in, ldm, r, k0, Mg);
+            }
+            int wl[8][2];
+            int wc[8];
+            for (int w = 0; w < Wn; ++w) wc[w] = 0;
+            for (int p = 0; p < Mg; ++p) {
+                if (!((bits >> p) & 1u)) continue;
+                const int wa = p / 2 - 1, wb = p / 2;
+                if (wa >= 0 && wa < Wn && wc[wa] < 2) wl[wa][wc[wa]++] = p - 2 * wa;
+                else if (wb < Wn && wc[wb] < 2) wl[wb][wc[wb]++] = p - 2 * wb;
+            }
+            for (int w = 0; w < Wn; ++w) {
+                int loc[2], isv[2], cnt = 0;
+                for (int q = 0; q < wc[w]; ++q) { loc[cnt] = wl[w][q]; isv[cnt] = 1; ++cnt; }
+                for (int l = 0; l < 4 && cnt < 2; ++l) {
+                    bool taken = false;
+                    for (int q = 0; q < cnt; ++q) taken |= (loc[q] == l);
+                    if (!taken) { loc[cnt] = l; isv[cnt] = 0; ++cnt; }
+                }
+                if (loc[0] > loc[1]) {
+                    int tl = loc[0]; loc[0] = loc[1]; loc[1] = tl;
+                    int tv = isv[0]; isv[0] = isv[1]; isv[1] = tv;
+                }
+                const int64_t wg = g * Wn + w;
+                for (int j = 0; j < 2; ++j) {
+                    const int64_t slot = wg * 2 + j;
+                    if (isv[j]) store_conv(vals, vdt, r * ldv + slot, Wv, wdt, r * ldwv + k0 + 2 * w + loc[j]);
+                    else store_zero(vals, vdt, r * ldv + slot);
+                    bw.put((uint32_t)loc[j], 2);
+                }
+            }
+        }
+        bw.flush();
+        mw.flush();
+    }
+}
+
+void launch_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                  nm_score_mode mode, bool select, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K,
+                  int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm, nm_dtype vdt, void* vals,
+                  int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
+    // chunk of Gt groups: Gt * (Ns-1) windows * 4 bits must be a multiple of 32,
+    // and (for mask bytes written bit by bit) chunks never share a mask byte with
+    // another thread: Gt * 2Ns must be a multiple of 8.
+    int Gt = 8 / gcd_i(Ns - 1, 8);
+    while ((Gt * 2 * Ns) % 8) Gt *= 2;
+    const int64_t total = R * ceil_div(K / (2 * Ns), Gt);
+    if (total == 0) return;
+    hipLaunchKernelGGL(slide_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, select ? 1 : 0, Wsc,
+                       sdt, ldsc, H, ldh, eps, mode, mask_in, mask_out, ldm, Wv, wdt, ldwv, R, K, Ns, Gt, vdt, vals,
+                       ldv, idx, ldi);
+}
+
+}  // namespace nm

@@ -1,0 +1,435 @@
+// Structured-sparse linear layer Y = X * W_hat^T on packed 2:4 weights, on the
+// gfx950 sparse matrix instructions (SMFMAC): the packed weight is the sparse
+// A operand, X^T the dense B operand, Y^T the accumulator tile.
+//
+// "SlideSparse" (sections 2A-2C): a (2N-2):2N weight is stored as overlapping
+// 2:4 windows over the lifted width K' = (2 - 2/N) K; the activation is lifted
+// to match by a pure index remap.  Here the lift happens while an activation
+// chunk is staged from global memory into LDS: 16 bytes of original columns
+// (one 8-wide group in bf16, two in int8) become 24 bytes of lifted columns
+// (windows 0-3, 2-5, 4-7 of each group), so X is read from HBM once at its
+// original size and the MFMA fragment reads stay plain 16-byte LDS loads.
+//
+// Operand layouts of the two instructions (gfx950, verified on hardware with
+// integer data):
+//   v_smfmac_f32_32x32x32_bf16: lane l holds A row (l%32), 8 compressed bf16
+//     that cover K [16*(l/32), +16) (two kept per 4-group), with their 2-bit
+//     in-group positions in bits [2e+1:2e] of the index operand; B column
+//     (l%32) as 16 bf16 at K = 16*(e/8) + 8*(l/32) + e%8; C column (l%32),
+//     rows 8*(e/4) + 4*(l/32) + e%4.
+//   v_smfmac_i32_32x32x64_i8: the same with 16 compressed int8 covering K
+//     [32*(l/32), +32), B as 32 int8 at K = 32*(e/16) + 16*(l/32) + e%16.
+// For both, the fragment of depth d (one instruction) is 16 bytes of
+// compressed values at byte 32d + 16(l/32) of a row's step, and two 16-byte B
+// reads at bytes 64d + 16(l/32) and 64d + 32 + 16(l/32) of a token's step.
+#include "nm_internal.h"
+
+namespace nm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+struct SpmmArgs {
+    const uint8_t* X;      // [Mtok, ldx] elements of T
+    const uint8_t* vals;   // [R, ldv] elements of T
+    const uint32_t* idx;   // [R, ldi] words
+    const float* x_scale;  // [Mtok] or null
+    void* Y;               // [Mtok, ldy] of ydt
+    void* part;            // split-K partials [KS][Mtok][R] (f32 or i32) or null
+    int64_t ldx, ldv, ldi, ldy;
+    int64_t Mtok, K, R;
+    int64_t comp_bytes;    // packed value bytes per row (K'/2 * sizeof(T))
+    int64_t idx_words;     // index words per row (K'/32: two 2-bit fields per 4 lifted columns)
+    float w_scale;
+    int scaled;
+    int ydt;
+    int nsteps, KS, steps_per_split;
+    int tiles_r, tiles_t;
+};
+
+// Per-(T, lift) step geometry.  A step stages 128 bytes of original activation
+// columns per token; LIFT (6:8 via N = 4) expands them to 192 lifted bytes.
+template <typename T, bool LIFT>
+struct Geo {
+    static constexpr int KO = 128 / (int)sizeof(T);           // original columns per step
+    static constexpr int KL = LIFT ? KO * 3 / 2 : KO;          // lifted columns per step
+    static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;      // lifted K per instruction
+    static constexpr int ND = KL / KDEP;                       // instructions per step
+    static constexpr int AV = KL / 2 * (int)sizeof(T);         // compressed bytes per row per step
+    static constexpr int AI = KL / 32;                         // index words per row per step
+    static constexpr int BV = KL * (int)sizeof(T);             // lifted bytes per token per step
+    static constexpr int AVS = AV + 16;                        // LDS row strides (padded)
+    static constexpr int AIS = AI | 1;
+    static constexpr int BS = BV + 16;
+};
+
+template <typename T, bool LIFT, int WR, int WT, int SR, int ST>
+struct Tile {
+    using G = Geo<T, LIFT>;
+    static constexpr int NT = WR * WT * 64;
+    static constexpr int BR = WR * SR * 32;
+    static constexpr int BT = WT * ST * 32;
+    static constexpr int A_BYTES = BR * G::AVS;
+    static constexpr int I_BYTES = BR * G::AIS * 4;
+    static constexpr int B_BYTES = BT * G::BS;
+    static constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
+    static constexpr int NA = BR * (G::AV / 16);               // A 16-byte chunks per step
+    static constexpr int NI = BR * G::AI;                      // index words per step
+    static constexpr int NB = BT * 8;                          // X 16-byte chunks per step
+    static constexpr int PA = (NA + NT - 1) / NT;
+    static constexpr int PI = (NI + NT - 1) / NT;
+    static constexpr int PB = (NB + NT - 1) / NT;
+};
+
+// Block index -> (R tile, token tile).  Workgroups are dispatched round-robin
+// over the 8 XCDs; the remap gives each XCD a contiguous range of tiles, and
+// the range is walked in groups of 8 R tiles so that the blocks resident on one
+// XCD at a time share their weight and activation tiles in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int nb, int tiles_r, int tiles_t, int& tr, int& tt) {
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int base = nb >> 3, rem = nb & 7;
+    const int id = xcd * base + (xcd < rem ? xcd : rem) + loc;
+    const int GR = 8;
+    const int per_group = GR * tiles_t;
+    const int grp = id / per_group;
+    const int first = grp * GR;
+    const int gsz = (tiles_r - first) < GR ? (tiles_r - first) : GR;
+    const int in = id - grp * per_group;
+    tr = first + in % gsz;
+    tt = in / gsz;
+}
+
+template <typename T, bool LIFT, int WR, int WT, int SR, int ST>
+__global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
+    using G = Geo<T, LIFT>;
+    using TL = Tile<T, LIFT, WR, WT, SR, ST>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave % WR, wt = wave / WR;
+    const int nb = gridDim.x;
+    int tr, tt;
+    tile_of(blockIdx.x, nb, a.tiles_r, a.tiles_t, tr, tt);
+    const int64_t r0 = (int64_t)tr * TL::BR, t0 = (int64_t)tt * TL::BT;
+    const int split = blockIdx.y;
+    const int s_begin = split * a.steps_per_split;
+    const int s_end = (s_begin + a.steps_per_split) < a.nsteps ? (s_begin + a.steps_per_split) : a.nsteps;
+
+    uint4 ra[TL::PA];
+    uint32_t ri[TL::PI];
+    uint4 rb[TL::PB];
+
+    auto load_step = [&](int s) {
+#pragma unroll
+        for (int p = 0; p < TL::PA; ++p) {
+            const int c = tid + p * TL::NT;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c < TL::NA) {
+                const int row = c / (G::AV / 16), part = c % (G::AV / 16);
+                int64_t gr = r0 + row;
+                gr = gr < a.R ? gr : a.R - 1;
+                const int64_t off = (int64_t)s * G::AV + part * 16;
+                if (off < a.comp_bytes)
+                    v = *(const uint4*)(a.vals + gr * a.ldv * (int64_t)sizeof(T) + off);
+            }
+            ra[p] = v;
+        }
+#pragma unroll
+        for (int p = 0; p < TL::PI; ++p) {
+            const int c = tid + p * TL::NT;
+            uint32_t v = 0x44444444u;  // padding groups: positions (0,1) with zero values
+            if (c < TL::NI) {
+                const int row = c / G::AI, part = c % G::AI;
+                int64_t gr = r0 + row;
+                gr = gr < a.R ? gr : a.R - 1;
+                const int64_t w = (int64_t)s * G::AI + part;
+                if (w < a.idx_words) v = a.idx[gr * a.ldi + w];
+            }
+            ri[p] = v;
+        }
+#pragma unroll
+        for (int p = 0; p < TL::PB; ++p) {
+            const int c = tid + p * TL::NT;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c < TL::NB) {
+                const int row = c / 8, part = c % 8;
+                const int64_t gt = t0 + row;
+                const int64_t col = (int64_t)s * G::KO + part * (16 / (int)sizeof(T));
+                if (gt < a.Mtok && col < a.K)
+                    v = *(const uint4*)(a.X + (gt * a.ldx + col) * (int64_t)sizeof(T));
+            }
+            rb[p] = v;
+        }
+    };
+
+    auto store_step = [&](int buf) {
+        uint8_t* sA = smem + buf * TL::STAGE;
+        uint32_t* sI = (uint32_t*)(sA + TL::A_BYTES);
+        uint8_t* sB = sA + TL::A_BYTES + TL::I_BYTES;
+#pragma unroll
+        for (int p = 0; p < TL::PA; ++p) {
+            const int c = tid + p * TL::NT;
+            if (c < TL::NA) {
+                const int row = c / (G::AV / 16), part = c % (G::AV / 16);
+                *(uint4*)(sA + row * G::AVS + part * 16) = ra[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < TL::PI; ++p) {
+            const int c = tid + p * TL::NT;
+            if (c < TL::NI) {
+                const int row = c / G::AI, part = c % G::AI;
+                sI[row * G::AIS + part] = ri[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < TL::PB; ++p) {
+            const int c = tid + p * TL::NT;
+            if (c < TL::NB) {
+                const int row = c / 8, part = c % 8;
+                if constexpr (!LIFT) {
+                    *(uint4*)(sB + row * G::BS + part * 16) = rb[p];
+                } else {
+                    // 16 original bytes -> 24 lifted bytes (windows 0-3, 2-5, 4-7 of each 8-group)
+                    const uint4 q = rb[p];
+                    uint2* d = (uint2*)(sB + row * G::BS + part * 24);
+                    if constexpr (sizeof(T) == 2) {
+                        d[0] = make_uint2(q.x, q.y);
+                        d[1] = make_uint2(q.y, q.z);
+                        d[2] = make_uint2(q.z, q.w);
+                    } else {
+                        const uint32_t m0 = (q.x >> 16) | (q.y << 16);
+                        const uint32_t m1 = (q.z >> 16) | (q.w << 16);
+                        d[0] = make_uint2(q.x, m0);
+                        d[1] = make_uint2(q.y, q.z);
+                        d[2] = make_uint2(m1, q.w);
+                    }
+                }
+            }
+        }
+    };
+
+    using AccV = typename std::conditional<sizeof(T) == 2, f32x16_t, i32x16_t>::type;
+    AccV acc[SR][ST];
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[i][j] = AccV{};
+
+    const int h = lane >> 5, l32 = lane & 31;
+
+    if (s_begin < s_end) {
+        load_step(s_begin);
+        store_step(0);
+        __syncthreads();
+    }
+    for (int s = s_begin; s < s_end; ++s) {
+        const int buf = (s - s_begin) & 1;
+        const bool more = (s + 1) < s_end;
+        if (more) load_step(s + 1);
+        const uint8_t* sA = smem + buf * TL::STAGE;
+        const uint32_t* sI = (const uint32_t*)(sA + TL::A_BYTES);
+        const uint8_t* sB = sA + TL::A_BYTES + TL::I_BYTES;
+#pragma unroll
+        for (int d = 0; d < G::ND; ++d) {
+            uint4 fa[SR];
+            uint32_t fi[SR];
+            uint4 fb[ST][2];
+#pragma unroll
+            for (int i = 0; i < SR; ++i) {
+                const int row = (wr * SR + i) * 32 + l32;
+                fa[i] = *(const uint4*)(sA + row * G::AVS + d * 32 + h * 16);
+                if constexpr (sizeof(T) == 2) fi[i] = sI[row * G::AIS + d] >> (16 * h);
+                else fi[i] = sI[row * G::AIS + 2 * d + h];
+            }
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                const int tok = (wt * ST + j) * 32 + l32;
+                fb[j][0] = *(const uint4*)(sB + tok * G::BS + d * 64 + h * 16);
+                fb[j][1] = *(const uint4*)(sB + tok * G::BS + d * 64 + 32 + h * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < SR; ++i)
+#pragma unroll
+                for (int j = 0; j < ST; ++j) {
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x8_t av = __builtin_bit_cast(bf16x8_t, fa[i]);
+                        const uint4 b0 = fb[j][0], b1 = fb[j][1];
+                        i32x8_t bi = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                        bf16x16_t bv = __builtin_bit_cast(bf16x16_t, bi);
+                        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(av, bv, acc[i][j], (int)fi[i], 0, 0);
+                    } else {
+                        i32x4_t av = __builtin_bit_cast(i32x4_t, fa[i]);
+                        const uint4 b0 = fb[j][0], b1 = fb[j][1];
+                        i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                        acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(av, bv, acc[i][j], (int)fi[i], 0, 0);
+                    }
+                }
+        }
+        if (more) store_step(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds token column l32, rows 8*(e/4) + 4*h + e%4 of each sub-tile
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int64_t tok = t0 + (wt * ST + j) * 32 + l32;
+            if (tok >= a.Mtok) continue;
+            const int64_t rbase = r0 + (wr * SR + i) * 32 + 4 * h;
+            float xs = 1.0f;
+            if (a.scaled && a.x_scale) xs = a.x_scale[tok];
+            const float sc = __fmul_rn(a.w_scale, xs);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t rr = rbase + 8 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t r = rr + e;
+                    if (r >= a.R) continue;
+                    const auto v = acc[i][j][4 * g + e];
+                    if (a.part) {
+                        const int64_t o = ((int64_t)split * a.Mtok + tok) * a.R + r;
+                        if constexpr (sizeof(T) == 2) ((float*)a.part)[o] = v;
+                        else ((int32_t*)a.part)[o] = v;
+                        continue;
+                    }
+                    const int64_t o = tok * a.ldy + r;
+                    if (a.ydt == NM_I32) {
+                        ((int32_t*)a.Y)[o] = (int32_t)v;
+                    } else {
+                        const float f = a.scaled ? __fmul_rn(sc, (float)v) : (float)v;
+                        if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
+                        else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
+                    }
+                }
+            }
+        }
+}
+
+// Split-K reduction: partials summed in split order, then the epilogue.
+template <typename Acc>
+__global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
+    const int64_t total = a.Mtok * a.R;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tok = t / a.R, r = t - tok * a.R;
+        Acc v = 0;
+        for (int z = 0; z < a.KS; ++z) v += ((const Acc*)a.part)[(int64_t)z * total + t];
+        const int64_t o = tok * a.ldy + r;
+        if (a.ydt == NM_I32) {
+            ((int32_t*)a.Y)[o] = (int32_t)v;
+        } else {
+            float f = (float)v;
+            if (a.scaled) {
+                const float xs = a.x_scale ? a.x_scale[tok] : 1.0f;
+                f = __fmul_rn(__fmul_rn(a.w_scale, xs), f);
+            }
+            if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
+            else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+struct SpmmPlan {
+    bool large;
+    int tiles_r, tiles_t, nsteps, KS, steps_per_split;
+};
+
+template <typename T, bool LIFT>
+static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R) {
+    using G = Geo<T, LIFT>;
+    SpmmPlan p{};
+    p.large = Mtok > 128;
+    const int BR = 128;
+    const int BT = p.large ? 128 : 32;
+    p.tiles_r = (int)ceil_div(R, BR);
+    p.tiles_t = (int)ceil_div(Mtok, BT);
+    p.nsteps = (int)ceil_div(K, G::KO);
+    const int64_t blocks = (int64_t)p.tiles_r * p.tiles_t;
+    int KS = 1;
+    if (!p.large) {
+        const int64_t target = 1024;
+        while ((int64_t)KS * blocks < target && KS * 4 <= p.nsteps) KS *= 2;
+    }
+    if (p.nsteps == 0) {
+        p.KS = 1;
+        p.steps_per_split = 0;
+        return p;
+    }
+    p.steps_per_split = (int)ceil_div(p.nsteps, KS);
+    p.KS = (int)ceil_div(p.nsteps, p.steps_per_split);
+    return p;
+}
+
+size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
+    SpmmPlan p = (xdt == NM_I8) ? (Ns ? plan_for<int8_t, true>(Mtok, K, R) : plan_for<int8_t, false>(Mtok, K, R))
+                                : (Ns ? plan_for<uint16_t, true>(Mtok, K, R) : plan_for<uint16_t, false>(Mtok, K, R));
+    if (p.KS <= 1) return 0;
+    return (size_t)p.KS * (size_t)Mtok * (size_t)R * 4;
+}
+
+template <typename T, bool LIFT>
+static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
+    const SpmmPlan p = plan_for<T, LIFT>(a.Mtok, a.K, a.R);
+    a.nsteps = p.nsteps;
+    a.KS = p.KS;
+    a.steps_per_split = p.steps_per_split;
+    a.tiles_r = p.tiles_r;
+    a.tiles_t = p.tiles_t;
+    a.part = nullptr;
+    if (p.KS > 1) {
+        const size_t need = (size_t)p.KS * (size_t)a.Mtok * (size_t)a.R * 4;
+        if (!ws || ws_bytes < need) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", need);
+        a.part = ws;
+    }
+    const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
+    if (p.large)
+        hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((spmm_kernel<T, LIFT, 4, 1, 1, 1>), grid, dim3(256), 0, s, a);
+    if (p.KS > 1) {
+        const int64_t total = a.Mtok * a.R;
+        const dim3 g(grid_cap(ceil_div(total, 256), 8192));
+        if (sizeof(T) == 2) hipLaunchKernelGGL(spmm_reduce_kernel<float>, g, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(spmm_reduce_kernel<int32_t>, g, dim3(256), 0, s, a);
+    }
+    return check_launch("nm_spmm");
+}
+
+nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                      const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                      float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
+    SpmmArgs a{};
+    a.X = (const uint8_t*)X;
+    a.vals = (const uint8_t*)vals;
+    a.idx = idx;
+    a.x_scale = x_scale;
+    a.Y = Y;
+    a.ldx = ldx;
+    a.ldv = ldv;
+    a.ldi = ldi;
+    a.ldy = ldy;
+    a.Mtok = Mtok;
+    a.K = K;
+    a.R = R;
+    const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
+    const int64_t es = xdt == NM_I8 ? 1 : 2;
+    a.comp_bytes = Kl / 2 * es;
+    a.idx_words = Kl / 32;
+    a.w_scale = w_scale;
+    a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
+    a.ydt = (int)ydt;
+    if (Mtok == 0 || R == 0) return NM_OK;
+    if (xdt == NM_I8) return Ns ? run_spmm<int8_t, true>(a, ws, ws_bytes, s) : run_spmm<int8_t, false>(a, ws, ws_bytes, s);
+    return Ns ? run_spmm<uint16_t, true>(a, ws, ws_bytes, s) : run_spmm<uint16_t, false>(a, ws, ws_bytes, s);
+}
+
+}  // namespace nm

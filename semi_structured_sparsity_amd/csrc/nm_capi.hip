@@ -1,0 +1,383 @@
+// C ABI of libnmsparse: argument validation, error reporting and dispatch to
+// the kernels.  Nothing is enqueued unless every check passes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "nm_internal.h"
+
+namespace nm {
+
+static thread_local char g_err[512] = "";
+
+nm_status set_error(nm_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+nm_status check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(NM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return NM_OK;
+}
+
+static int64_t esize(nm_dtype d) { return d == NM_BF16 ? 2 : d == NM_I8 ? 1 : 4; }
+static bool dtype_ok(nm_dtype d) { return d == NM_F32 || d == NM_BF16 || d == NM_I8 || d == NM_I32; }
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+// Byte range touched by a row-major [rows, cols] view with leading dimension ld.
+static Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es) {
+    if (!p || rows <= 0 || cols <= 0) return {0, 0};
+    const uintptr_t b = (uintptr_t)p;
+    return {b, b + (uintptr_t)(((rows - 1) * ld + cols) * es)};
+}
+static bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+#define NM_REQ(cond, st, ...)                                                \
+    do {                                                                     \
+        if (!(cond)) return set_error(st, __VA_ARGS__);                      \
+    } while (0)
+
+static nm_status check_pattern(int N, int M, const char* fn) {
+    NM_REQ(M == 4 || M == 8, NM_ERR_PATTERN, "%s: M must be 4 or 8 (got %d)", fn, M);
+    NM_REQ(N >= 1 && N < M, NM_ERR_PATTERN, "%s: need 1 <= N < M (got N=%d, M=%d)", fn, N, M);
+    return NM_OK;
+}
+
+static int64_t idx_words_needed(int64_t K, int N, int M) { return (K / M * N * index_bits(M) + 31) / 32; }
+
+static nm_status check_score_src(const void* W, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh,
+                                 nm_score_mode mode, int64_t R, int64_t K, const char* fn) {
+    NM_REQ(W || R * K == 0, NM_ERR_NULL, "%s: score source is NULL", fn);
+    NM_REQ(sdt == NM_F32 || sdt == NM_BF16, NM_ERR_DTYPE, "%s: score source must be f32 or bf16", fn);
+    NM_REQ(ldsc >= K, NM_ERR_SHAPE, "%s: score leading dimension %lld < K %lld", fn, (long long)ldsc, (long long)K);
+    NM_REQ(mode == NM_SCORE_HESSIAN || mode == NM_SCORE_MAGNITUDE, NM_ERR_SHAPE, "%s: unknown score mode", fn);
+    if (mode == NM_SCORE_HESSIAN) {
+        NM_REQ(H || R * K == 0, NM_ERR_NULL, "%s: H is NULL in HESSIAN mode", fn);
+        NM_REQ(ldh == 0 || ldh >= K, NM_ERR_SHAPE, "%s: ldh must be 0 or >= K", fn);
+    }
+    return NM_OK;
+}
+
+}  // namespace nm
+
+using namespace nm;
+
+extern "C" {
+
+int nm_abi_version(void) { return NM_ABI_VERSION; }
+
+const char* nm_last_error(void) { return g_err; }
+
+size_t nm_colsumsq_workspace(int64_t n, int64_t K) { return (n <= 0 || K <= 0) ? 0 : colsumsq_ws(n, K); }
+
+nm_status nm_hdiag_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx, float* H, void* ws,
+                            size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_hdiag_colsumsq";
+    NM_REQ(n >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    if (K == 0) return NM_OK;
+    NM_REQ(H, NM_ERR_NULL, "%s: H is NULL", fn);
+    NM_REQ(X || n == 0, NM_ERR_NULL, "%s: X is NULL", fn);
+    NM_REQ(xdt == NM_BF16 || xdt == NM_F32, NM_ERR_DTYPE, "%s: X must be bf16 or f32", fn);
+    NM_REQ(ldx >= K, NM_ERR_SHAPE, "%s: ldx < K", fn);
+    const int64_t vec = 16 / esize(xdt);
+    NM_REQ(K % vec == 0 && ldx % vec == 0 && aligned16(X), NM_ERR_ALIGN,
+           "%s: X must be 16-byte aligned with K and ldx multiples of %lld", fn, (long long)vec);
+    const size_t need = nm_colsumsq_workspace(n, K);
+    NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(!overlap(span(H, 1, K, K, 4), span(X, n, K, ldx, esize(xdt))), NM_ERR_ALIAS, "%s: H overlaps X", fn);
+    launch_colsumsq(X, xdt, n, K, ldx, H, ws, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+size_t nm_hutchinson_workspace(int64_t n, int64_t K, int64_t R, int probes) {
+    if (n <= 0 || K <= 0 || R <= 0 || probes <= 0) return 0;
+    return hutch_ws(n, K, R, probes);
+}
+
+nm_status nm_hdiag_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes, uint64_t seed,
+                              float* D, int64_t ldd, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_hdiag_hutchinson";
+    NM_REQ(n >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(probes >= 1, NM_ERR_SHAPE, "%s: probes must be >= 1", fn);
+    if (R == 0 || K == 0) return NM_OK;
+    NM_REQ(X && D, NM_ERR_NULL, "%s: NULL pointer", fn);
+    NM_REQ(n >= 1, NM_ERR_SHAPE, "%s: need at least one calibration row", fn);
+    NM_REQ(ldx >= K && ldd >= K, NM_ERR_SHAPE, "%s: leading dimension < K", fn);
+    NM_REQ(K % 64 == 0 && n % 64 == 0 && ldx % 8 == 0 && aligned16(X), NM_ERR_ALIGN,
+           "%s: need K %% 64 == 0, n %% 64 == 0, 16-byte aligned X with ldx %% 8 == 0", fn);
+    NM_REQ((int64_t)probes * R < (1LL << 31) && (uint64_t)R * (uint64_t)(K / 64) < (1ull << 40), NM_ERR_SHAPE,
+           "%s: too many probe rows", fn);
+    const size_t need = hutch_ws(n, K, R, probes);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(!overlap(span(D, R, K, ldd, 4), span(X, n, K, ldx, 2)), NM_ERR_ALIAS, "%s: D overlaps X", fn);
+    launch_hutchinson(X, n, K, ldx, R, probes, seed, D, ldd, ws, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+nm_status nm_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const float* H, int64_t ldh,
+                   float eps, nm_score_mode mode, float* S, int64_t lds, nm_stream_t stream) {
+    const char* fn = "nm_score";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    if (R * K == 0) return NM_OK;
+    nm_status st = check_score_src(W, wdt, ldw, H, ldh, mode, R, K, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(S, NM_ERR_NULL, "%s: S is NULL", fn);
+    NM_REQ(lds >= K, NM_ERR_SHAPE, "%s: lds < K", fn);
+    const Range rs = span(S, R, K, lds, 4);
+    NM_REQ(!overlap(rs, span(W, R, K, ldw, esize(wdt))), NM_ERR_ALIAS, "%s: S overlaps W", fn);
+    if (mode == NM_SCORE_HESSIAN)
+        NM_REQ(!overlap(rs, span(H, ldh ? R : 1, K, ldh ? ldh : K, 4)), NM_ERR_ALIAS, "%s: S overlaps H", fn);
+    launch_score(W, wdt, R, K, ldw, H, ldh, eps, mode, S, lds, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+size_t nm_stats_workspace(int64_t R, int64_t K) { return reduce_ws(R, K); }
+
+nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats, void* ws, size_t ws_bytes,
+                         nm_stream_t stream) {
+    const char* fn = "nm_score_stats";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(stats, NM_ERR_NULL, "%s: stats is NULL", fn);
+    NM_REQ(S || R * K == 0, NM_ERR_NULL, "%s: S is NULL", fn);
+    NM_REQ(lds >= K, NM_ERR_SHAPE, "%s: lds < K", fn);
+    const size_t need = reduce_ws(R, K);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(!overlap(span(stats, 1, 2, 2, 8), span(S, R, K, lds, 4)), NM_ERR_ALIAS, "%s: stats overlaps S", fn);
+    launch_stats(S, R, K, lds, stats, ws, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+size_t nm_gate_workspace(int64_t R, int64_t K, int steps) { return gate_ws(R, K, steps); }
+
+nm_status nm_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
+                  float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
+                  void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_gate";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    nm_status st = check_pattern(N, M, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
+    NM_REQ(steps >= 1 && steps <= 64, NM_ERR_SHAPE, "%s: steps must be in [1, 64]", fn);
+    NM_REQ(T0 > 0.f && rho > 0.f, NM_ERR_SHAPE, "%s: T0 and rho must be positive", fn);
+    NM_REQ(stats && lmid, NM_ERR_NULL, "%s: stats / lmid is NULL", fn);
+    NM_REQ((S && hard_mask) || R * K == 0, NM_ERR_NULL, "%s: NULL pointer", fn);
+    NM_REQ(lds >= K && ldm >= (K + 7) / 8 && (!m_final || ldf >= K), NM_ERR_SHAPE, "%s: leading dimension too small",
+           fn);
+    const size_t need = gate_ws(R, K, steps);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    const Range rs = span(S, R, K, lds, 4);
+    NM_REQ(!overlap(rs, span(hard_mask, R, (K + 7) / 8, ldm, 1)) && !overlap(rs, span(m_final, R, K, ldf, 4)) &&
+               !overlap(rs, span(lmid, 1, steps, steps, 8)),
+           NM_ERR_ALIAS, "%s: an output overlaps S", fn);
+    launch_gate(S, R, K, lds, stats, N, M, T0, rho, steps, m_final, ldf, hard_mask, ldm, lmid, ws,
+                (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+nm_status nm_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int M, uint8_t* mask, int64_t ldm,
+                  nm_stream_t stream) {
+    const char* fn = "nm_mask";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    nm_status st = check_pattern(N, M, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
+    if (R * K == 0) return NM_OK;
+    NM_REQ(S && mask, NM_ERR_NULL, "%s: NULL pointer", fn);
+    NM_REQ(lds >= K && ldm >= (K + 7) / 8, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    NM_REQ(!overlap(span(mask, R, (K + 7) / 8, ldm, 1), span(S, R, K, lds, 4)), NM_ERR_ALIAS, "%s: mask overlaps S",
+           fn);
+    launch_mask(S, R, K, lds, N, M, mask, ldm, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+static nm_status check_pack_out(const char* fn, nm_dtype wdt, nm_dtype vdt, int64_t R, int64_t K, int64_t slots,
+                                int64_t words, const void* vals, int64_t ldv, const uint32_t* idx, int64_t ldi) {
+    NM_REQ(dtype_ok(wdt) && dtype_ok(vdt), NM_ERR_DTYPE, "%s: unknown dtype", fn);
+    NM_REQ(vdt == wdt || (wdt == NM_F32 && vdt == NM_BF16), NM_ERR_DTYPE,
+           "%s: value dtype must equal the weight dtype (or f32 -> bf16)", fn);
+    NM_REQ(vals && idx, NM_ERR_NULL, "%s: vals / idx is NULL", fn);
+    NM_REQ(ldv >= slots && ldi >= words, NM_ERR_SHAPE, "%s: ldv/ldi too small (need %lld / %lld)", fn,
+           (long long)slots, (long long)words);
+    NM_REQ(!overlap(span(vals, R, slots, ldv, esize(vdt)), span(idx, R, words, ldi, 4)), NM_ERR_ALIAS,
+           "%s: vals overlaps idx", fn);
+    (void)K;
+    return NM_OK;
+}
+
+nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                  int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi,
+                  nm_stream_t stream) {
+    const char* fn = "nm_pack";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    nm_status st = check_pattern(N, M, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
+    if (R * K == 0) return NM_OK;
+    NM_REQ(W && mask, NM_ERR_NULL, "%s: W / mask is NULL", fn);
+    NM_REQ(ldw >= K && ldm >= (K + 7) / 8, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    const int64_t slots = K / M * N, words = idx_words_needed(K, N, M);
+    st = check_pack_out(fn, wdt, vdt, R, K, slots, words, vals, ldv, idx, ldi);
+    if (st != NM_OK) return st;
+    const Range rv = span(vals, R, slots, ldv, esize(vdt)), ri = span(idx, R, words, ldi, 4);
+    const Range rw = span(W, R, K, ldw, esize(wdt)), rm = span(mask, R, (K + 7) / 8, ldm, 1);
+    NM_REQ(!overlap(rv, rw) && !overlap(rv, rm) && !overlap(ri, rw) && !overlap(ri, rm), NM_ERR_ALIAS,
+           "%s: an output overlaps an input", fn);
+    launch_pack(W, wdt, R, K, ldw, mask, ldm, N, M, vdt, vals, ldv, idx, ldi, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+nm_status nm_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                        nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N,
+                        int M, uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
+                        int64_t ldi, nm_stream_t stream) {
+    const char* fn = "nm_prune_pack";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    nm_status st = check_pattern(N, M, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
+    if (R * K == 0) return NM_OK;
+    st = check_score_src(Wsc, sdt, ldsc, H, ldh, mode, R, K, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(Wv, NM_ERR_NULL, "%s: Wv is NULL", fn);
+    NM_REQ(ldwv >= K, NM_ERR_SHAPE, "%s: ldwv < K", fn);
+    NM_REQ(!mask || ldm >= (K + 7) / 8, NM_ERR_SHAPE, "%s: ldm too small", fn);
+    const int64_t slots = K / M * N, words = idx_words_needed(K, N, M);
+    st = check_pack_out(fn, wdt, vdt, R, K, slots, words, vals, ldv, idx, ldi);
+    if (st != NM_OK) return st;
+    // the fused 2:4 path reads 16-byte vectors and writes 8-byte value pairs
+    if (N == 2 && M == 4 && Wsc == Wv && vdt == NM_BF16) {
+        const int64_t vec = 16 / esize(wdt);
+        NM_REQ(aligned16(Wv) && ldwv % vec == 0 && ((uintptr_t)vals & 7u) == 0 && ldv % 4 == 0 &&
+                   (mode == NM_SCORE_MAGNITUDE || (aligned16(H) && ldh % 4 == 0)),
+               NM_ERR_ALIGN, "%s: fused 2:4 path needs 16-byte aligned W (ld %% %lld), H (ldh %% 4) and vals (ldv %% 4)",
+               fn, (long long)vec);
+    }
+    const Range rv = span(vals, R, slots, ldv, esize(vdt)), ri = span(idx, R, words, ldi, 4);
+    const Range rm = span(mask, R, (K + 7) / 8, ldm, 1);
+    const Range in[3] = {span(Wsc, R, K, ldsc, esize(sdt)), span(Wv, R, K, ldwv, esize(wdt)),
+                         mode == NM_SCORE_HESSIAN ? span(H, ldh ? R : 1, K, ldh ? ldh : K, 4) : Range{0, 0}};
+    for (const Range& x : in)
+        NM_REQ(!overlap(rv, x) && !overlap(ri, x) && !overlap(rm, x), NM_ERR_ALIAS, "%s: an output overlaps an input",
+               fn);
+    NM_REQ(!overlap(rm, rv) && !overlap(rm, ri), NM_ERR_ALIAS, "%s: mask overlaps vals/idx", fn);
+    launch_prune_pack(Wsc, sdt, ldsc, H, ldh, eps, mode, Wv, wdt, ldwv, R, K, N, M, mask, ldm, vdt, vals, ldv, idx, ldi,
+                      (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+static nm_status slide_common(const char* fn, bool select, const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H,
+                              int64_t ldh, float eps, nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv,
+                              int64_t R, int64_t K, int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm,
+                              nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream) {
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(Ns >= 2 && Ns <= 8, NM_ERR_PATTERN, "%s: slide N must be in [2, 8] (got %d)", fn, Ns);
+    NM_REQ(K % (2 * Ns) == 0, NM_ERR_SHAPE, "%s: K %% 2N != 0", fn);
+    if (R * K == 0) return NM_OK;
+    if (select) {
+        nm_status st = check_score_src(Wsc, sdt, ldsc, H, ldh, mode, R, K, fn);
+        if (st != NM_OK) return st;
+        NM_REQ(!mask_out || ldm >= (K + 7) / 8, NM_ERR_SHAPE, "%s: ldm too small", fn);
+    } else {
+        NM_REQ(mask_in, NM_ERR_NULL, "%s: mask is NULL", fn);
+        NM_REQ(ldm >= (K + 7) / 8, NM_ERR_SHAPE, "%s: ldm too small", fn);
+    }
+    NM_REQ(Wv, NM_ERR_NULL, "%s: W is NULL", fn);
+    NM_REQ(ldwv >= K, NM_ERR_SHAPE, "%s: ldw < K", fn);
+    const int64_t Kl = K / (2 * Ns) * 4 * (Ns - 1);
+    const int64_t slots = Kl / 2, words = (Kl + 31) / 32;
+    nm_status st = check_pack_out(fn, wdt, vdt, R, K, slots, words, vals, ldv, idx, ldi);
+    if (st != NM_OK) return st;
+    const Range rv = span(vals, R, slots, ldv, esize(vdt)), ri = span(idx, R, words, ldi, 4);
+    const Range rm = select ? span(mask_out, R, (K + 7) / 8, ldm, 1) : Range{0, 0};
+    const Range in[4] = {select ? span(Wsc, R, K, ldsc, esize(sdt)) : Range{0, 0}, span(Wv, R, K, ldwv, esize(wdt)),
+                         (select && mode == NM_SCORE_HESSIAN) ? span(H, ldh ? R : 1, K, ldh ? ldh : K, 4) : Range{0, 0},
+                         select ? Range{0, 0} : span(mask_in, R, (K + 7) / 8, ldm, 1)};
+    for (const Range& x : in)
+        NM_REQ(!overlap(rv, x) && !overlap(ri, x) && !overlap(rm, x), NM_ERR_ALIAS, "%s: an output overlaps an input",
+               fn);
+    NM_REQ(!overlap(rm, rv) && !overlap(rm, ri), NM_ERR_ALIAS, "%s: mask overlaps vals/idx", fn);
+    launch_slide(Wsc, sdt, ldsc, H, ldh, eps, mode, select, Wv, wdt, ldwv, R, K, Ns, mask_in, mask_out, ldm, vdt, vals,
+                 ldv, idx, ldi, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+nm_status nm_slide_decompose(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask,
+                             int64_t ldm, int Ns, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi,
+                             nm_stream_t stream) {
+    return slide_common("nm_slide_decompose", false, nullptr, NM_F32, 0, nullptr, 0, 0.f, NM_SCORE_MAGNITUDE, W, wdt,
+                        ldw, R, K, Ns, mask, nullptr, ldm, vdt, vals, ldv, idx, ldi, stream);
+}
+
+nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                         nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int Ns,
+                         uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
+                         int64_t ldi, nm_stream_t stream) {
+    return slide_common("nm_prune_slide", true, Wsc, sdt, ldsc, H, ldh, eps, mode, Wv, wdt, ldwv, R, K, Ns, nullptr,
+                        mask, ldm, vdt, vals, ldv, idx, ldi, stream);
+}
+
+nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
+                     size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_absmean";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(alpha, NM_ERR_NULL, "%s: alpha is NULL", fn);
+    NM_REQ(W || R * K == 0, NM_ERR_NULL, "%s: W is NULL", fn);
+    NM_REQ(dtype_ok(wdt), NM_ERR_DTYPE, "%s: unknown dtype", fn);
+    NM_REQ(ldw >= K, NM_ERR_SHAPE, "%s: ldw < K", fn);
+    const size_t need = reduce_ws(R, K);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(!overlap(span(alpha, 1, 1, 1, 4), span(W, R, K, ldw, esize(wdt))), NM_ERR_ALIAS, "%s: alpha overlaps W",
+           fn);
+    launch_absmean(W, wdt, R, K, ldw, alpha, ws, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
+    if (Mtok <= 0 || K <= 0 || R <= 0) return 0;
+    return spmm_ws(Mtok, K, R, Ns, xdt);
+}
+
+nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, nm_dtype vdt,
+                  const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                  float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_spmm";
+    NM_REQ(Mtok >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported patterns are plain 2:4 (Ns=0) and 6:8 via slide (Ns=4)",
+           fn);
+    NM_REQ((xdt == NM_BF16 && vdt == NM_BF16 && (ydt == NM_BF16 || ydt == NM_F32)) ||
+               (xdt == NM_I8 && vdt == NM_I8 && (ydt == NM_I32 || ydt == NM_F32 || ydt == NM_BF16)),
+           NM_ERR_DTYPE, "%s: supported: bf16 x bf16 -> bf16/f32, int8 x int8 -> int32/f32/bf16", fn);
+    const int64_t kmult = Ns == 0 ? (xdt == NM_BF16 ? 16 : 32) : (xdt == NM_BF16 ? 32 : 64);
+    NM_REQ(K % kmult == 0, NM_ERR_SHAPE, "%s: K must be a multiple of %lld for this dtype and pattern", fn,
+           (long long)kmult);
+    const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
+    if (xdt == NM_I8) NM_REQ(Kl * 127 * 127 < (1LL << 31), NM_ERR_SHAPE, "%s: int8 sum may overflow int32", fn);
+    if (Mtok == 0 || R == 0) return NM_OK;
+    NM_REQ(Y, NM_ERR_NULL, "%s: Y is NULL", fn);
+    NM_REQ(ldy >= R, NM_ERR_SHAPE, "%s: ldy < R", fn);
+    if (K == 0) return set_error(NM_ERR_SHAPE, "%s: K == 0", fn);
+    NM_REQ(X && vals && idx, NM_ERR_NULL, "%s: NULL input", fn);
+    const int64_t es = esize(xdt);
+    NM_REQ(ldx >= K && ldv >= Kl / 2 && ldi >= Kl / 32, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    NM_REQ(aligned16(X) && aligned16(vals) && (ldx * es) % 16 == 0 && (ldv * es) % 16 == 0, NM_ERR_ALIGN,
+           "%s: X and vals must be 16-byte aligned with 16-byte row strides", fn);
+    NM_REQ(((uintptr_t)idx & 3u) == 0, NM_ERR_ALIGN, "%s: idx must be 4-byte aligned", fn);
+    const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
+    NM_REQ(!overlap(ry, span(X, Mtok, K, ldx, es)) && !overlap(ry, span(vals, R, Kl / 2, ldv, es)) &&
+               !overlap(ry, span(idx, R, Kl / 32, ldi, 4)) && !overlap(ry, span(x_scale, 1, Mtok, Mtok, 4)),
+           NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
+    const size_t need = spmm_ws(Mtok, K, R, Ns, xdt);
+    NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (need) NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
+    return launch_spmm(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, Y, ydt, ldy, ws, ws_bytes,
+                       (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the HIP translation units of libnmsparse.
+// Device helpers, the thread-local error slot, and the host-side launchers
+// that the C ABI (nm_capi.hip) calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nmsparse.h"
+
+namespace nm {
+
+// ------------------------------------------------------------------ errors
+nm_status set_error(nm_status st, const char* fmt, ...);
+nm_status check_launch(const char* what);
+
+// ------------------------------------------------------------------ numerics
+// bf16 is the upper half of an IEEE binary32: widening is exact; narrowing
+// rounds to nearest even and keeps NaN quiet.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Rank key of a score for top-N selection: NaN ranks below everything and
+// -0 compares equal to +0 (x + 0 maps -0 to +0).
+__device__ __forceinline__ float rank_key(float x) { return (x != x) ? -__builtin_inff() : __fadd_rn(x, 0.0f); }
+
+// Keep-bits of the top-N of M keys (ties to the lower index): bit i set iff
+// fewer than N members beat member i; j beats i iff key_j > key_i, or the keys
+// are equal and j < i.
+template <int M>
+__device__ __forceinline__ uint32_t topn_bits(const float (&k)[M], int N) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        int beaten = 0;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            if (j == i) continue;
+            bool b = (j < i) ? (k[j] >= k[i]) : (k[j] > k[i]);
+            beaten += b ? 1 : 0;
+        }
+        bits |= (beaten < N ? 1u : 0u) << i;
+    }
+    return bits;
+}
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) as a counter-based
+// generator: output number i of a generator seeded with s is the variant-13
+// finaliser applied to s + (i+1) * 0x9E3779B97F4A7C15.
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+    uint64_t z = seed + (i + 1ull) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+inline int index_bits(int M) {
+    int b = 0;
+    while ((1 << b) < M) ++b;
+    return b;
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int grid_cap(int64_t blocks, int64_t cap = 1 << 20) { return (int)(blocks < 1 ? 1 : (blocks > cap ? cap : blocks)); }
+
+// ------------------------------------------------------------------ launchers
+// colsumsq
+size_t colsumsq_ws(int64_t n, int64_t K);
+void launch_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx, float* H, void* ws,
+                     hipStream_t s);
+// score / mask / pack
+void launch_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const float* H, int64_t ldh,
+                  float eps, nm_score_mode mode, float* S, int64_t lds, hipStream_t s);
+void launch_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int M, uint8_t* mask, int64_t ldm,
+                 hipStream_t s);
+void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                 int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s);
+void launch_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                       nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N,
+                       int M, uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
+                       int64_t ldi, hipStream_t s);
+void launch_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
+                  nm_score_mode mode, bool select, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K,
+                  int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm, nm_dtype vdt, void* vals,
+                  int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s);
+// reductions / gate
+size_t reduce_ws(int64_t R, int64_t K);
+size_t gate_ws(int64_t R, int64_t K, int steps);
+void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats, void* ws, hipStream_t s);
+void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
+                    hipStream_t s);
+void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
+                 float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
+                 void* ws, hipStream_t s);
+// sparse GEMM
+size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
+nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                      const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                      float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
+// Hutchinson
+size_t hutch_ws(int64_t n, int64_t K, int64_t R, int probes);
+void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes, uint64_t seed,
+                       float* D, int64_t ldd, void* ws, hipStream_t s);
+
+}  // namespace nm

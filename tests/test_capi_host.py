@@ -1,0 +1,89 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+the header declares, and rejects bad arguments before touching the GPU (the
+validation paths below return before any HIP call)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "nmsparse.h"
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def nm():
+    import semi_structured_sparsity_amd as m
+    return m
+
+
+def test_library_exports_every_declared_symbol(nm):
+    syms = declared_symbols()
+    assert len(syms) >= 18
+    for s in syms:
+        assert hasattr(nm.raw, s), f"libnmsparse.so does not export {s}"
+        assert s in nm.SIGNATURES, f"binding has no signature for {s}"
+    assert nm.nm_abi_version() == 1
+
+
+def test_binding_functions_have_c_names(nm):
+    for s in declared_symbols():
+        if s.endswith("_workspace") or s in ("nm_last_error",):
+            continue
+        assert callable(getattr(nm, s)), f"no Python wrapper named {s}"
+
+
+def _st(nm, code):
+    return nm.STATUS_NAMES[code]
+
+
+def test_validation_errors_without_gpu(nm):
+    r = nm.raw
+    S = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+    # unsupported N:M
+    assert _st(nm, r.nm_mask(S, 4, 8, 8, 4, 6, S, 1, None)) == "NM_ERR_PATTERN"
+    assert _st(nm, r.nm_mask(S, 4, 8, 8, 4, 4, S, 1, None)) == "NM_ERR_PATTERN"
+    assert "M must be 4 or 8" in nm.last_error() or "N < M" in nm.last_error()
+    # K not a multiple of M
+    assert _st(nm, r.nm_mask(S, 4, 10, 10, 2, 4, S, 2, None)) == "NM_ERR_SHAPE"
+    # NULL pointers
+    assert _st(nm, r.nm_mask(None, 4, 8, 8, 2, 4, S, 1, None)) == "NM_ERR_NULL"
+    # slide N out of range and K not a multiple of 2N
+    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 16, 16, S, 2, 9, 1, S, 8, S, 1, None)) == "NM_ERR_PATTERN"
+    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 12, 12, S, 2, 4, 1, S, 8, S, 1, None)) == "NM_ERR_SHAPE"
+    # sparse GEMM: unsupported slide N, bad dtype pairing, K multiple, int32 overflow bound
+    Y = ctypes.c_void_p(0x100000)
+    assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, S, 1, S, 8, 32, 4, 3, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_PATTERN"
+    assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_spmm(S, 2, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 2, 8, None, 0, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_spmm(S, 1, 4, 40, 40, S, 1, S, 8, 20, 4, 0, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    big = 1 << 20
+    assert _st(nm, r.nm_spmm(S, 2, 4, big, big, S, 2, S, 8, big, big, 0, None, 1.0, Y, 3, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    # misaligned activation pointer
+    assert _st(nm, r.nm_spmm(ctypes.c_void_p(0x1002), 1, 4, 64, 64, S, 1, S, 8, 32, 4, 0, None, 1.0, Y, 1, 8, None, 0,
+                             None)) == "NM_ERR_ALIGN"
+    # output aliasing an input
+    assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, ctypes.c_void_p(0x8000), 1, ctypes.c_void_p(0x9000), 8, 32, 4, 0, None,
+                             1.0, S, 1, 8, None, 0, None)) == "NM_ERR_ALIAS"
+    # workspace missing
+    assert _st(nm, r.nm_score_stats(S, 4, 8, 8, Y, None, 0, None)) == "NM_ERR_WORKSPACE"
+    # gate: steps out of range, T0 not positive
+    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, 0.5, 0.5, 0, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, -1.0, 0.5, 8, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
+    # Hutchinson alignment rules
+    assert _st(nm, r.nm_hdiag_hutchinson(S, 64, 100, 100, 8, 2, 1, Y, 100, S, 1 << 30, None)) == "NM_ERR_ALIGN"
+    # pack dtype rule (bf16 weights cannot pack to int8)
+    assert _st(nm, r.nm_pack(S, 1, 4, 8, 8, S, 1, 2, 4, 2, Y, 4, S, 1, None)) == "NM_ERR_DTYPE"
+
+
+def test_empty_inputs_are_noops(nm):
+    r = nm.raw
+    assert r.nm_mask(None, 0, 8, 8, 2, 4, None, 1, None) == 0
+    assert r.nm_spmm(None, 1, 0, 64, 64, None, 1, None, 8, 32, 4, 0, None, 1.0, None, 1, 8, None, 0, None) == 0
+    assert r.nm_pack(None, 1, 0, 8, 8, None, 1, 2, 4, 1, None, 4, None, 1, None) == 0

@@ -1,0 +1,180 @@
+"""GPU parity of the weight-side kernels against the CPU oracle, called through
+the C ABI: curvature column sums, scores, top-N masks, packing, the fused
+score->mask->pack pass, the sliding-window decomposition and the ternary
+scale.  Integer, mask and index outputs must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._util import bf16_np, dev, host, np_bf16, u32_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nm():
+    import semi_structured_sparsity_amd as m
+    return m
+
+
+def _bf16(a):
+    return np_bf16(O.f32_to_bf16(a))
+
+
+# ------------------------------------------------------------------ A1
+@pytest.mark.parametrize("n,K,dt", [(512, 4096, "bf16"), (100, 264, "bf16"), (37, 72, "f32"), (1, 8, "bf16")])
+def test_colsumsq(nm, n, K, dt):
+    g = np.random.default_rng(n + K)
+    Xf = g.standard_normal((n, K)).astype(np.float32)
+    X = _bf16(Xf) if dt == "bf16" else torch.from_numpy(Xf)
+    H = nm.nm_hdiag_colsumsq(X.to(dev())).cpu().numpy().astype(np.float64)
+    ref = O.colsumsq(host(X))
+    # any summation order of n positive float terms is within (n-1)u/(1-(n-1)u) of the exact sum
+    u = 2.0 ** -24
+    bound = (n * u / (1 - n * u)) * ref + 1e-30
+    assert (np.abs(H - ref) <= bound).all()
+
+
+# ------------------------------------------------------------------ A3
+def test_score_tiny24_and_full_curvature(nm):
+    W, H, _ = synth.tiny24_inputs()
+    S = nm.nm_score(W.to(dev()), H.to(dev()), 1e-6).cpu().numpy()
+    assert np.array_equal(S, O.score(W.numpy(), H.numpy(), 1e-6))
+    g = np.random.default_rng(3)
+    Wb = _bf16(g.standard_normal((96, 200)) * 0.02)
+    Hf = g.uniform(-0.5, 2, (96, 200)).astype(np.float32)  # a Hutchinson diagonal may be negative
+    S = nm.nm_score(Wb.to(dev()), torch.from_numpy(Hf).to(dev()), 1e-6).cpu().numpy()
+    assert np.array_equal(S, O.score(host(Wb), Hf, 1e-6))
+    S = nm.nm_score(Wb.to(dev()), None, 0.0, nm.NM_SCORE_MAGNITUDE).cpu().numpy()
+    assert np.array_equal(S, O.score(host(Wb), None, 0.0, O.SCORE_MAGNITUDE))
+
+
+# ------------------------------------------------------------------ A7
+@pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (3, 4), (6, 8), (4, 8), (2, 8), (7, 8)])
+def test_mask_with_ties_nan_signed_zero(nm, N, M):
+    g = np.random.default_rng(N * 10 + M)
+    R, K = 67, 8 * M + M  # ragged: not a multiple of 8 bytes when M = 4
+    S = g.integers(0, 5, (R, K)).astype(np.float32)
+    S[g.random((R, K)) < 0.05] = np.nan
+    S[g.random((R, K)) < 0.05] = -0.0
+    S[g.random((R, K)) < 0.02] = -np.inf
+    mask = nm.nm_mask(torch.from_numpy(S).to(dev()), N, M).cpu().numpy()
+    ref = O.topn_mask(S, N, M)
+    assert np.array_equal(mask, ref)
+
+
+# ------------------------------------------------------------------ A8
+@pytest.mark.parametrize("N,M,dt", [(2, 4, "bf16"), (2, 4, "f32"), (6, 8, "bf16"), (1, 4, "i8"), (6, 8, "i8"),
+                                    (3, 8, "bf16"), (7, 8, "i8")])
+def test_pack_with_short_groups(nm, N, M, dt):
+    g = np.random.default_rng(100 + N * 10 + M)
+    R, K = 45, 40 * M
+    Wf = g.standard_normal((R, K)).astype(np.float32)
+    if dt == "bf16":
+        W, vdt = _bf16(Wf), nm.NM_BF16
+    elif dt == "f32":
+        W, vdt = torch.from_numpy(Wf), nm.NM_BF16
+    else:
+        W, vdt = torch.from_numpy(g.integers(-1, 2, (R, K)).astype(np.int8)), nm.NM_I8
+    bits = g.random((R, K)) < (N / M)  # any number of bits per group: short groups get padded
+    mask = O.bool_to_mask(bits)
+    vals, idx = nm.nm_pack(W.to(dev()), torch.from_numpy(mask).to(dev()), N, M, vdt)
+    v_ref, i_ref = O.pack(host(W), mask, N, M, {nm.NM_BF16: O.BF16, nm.NM_I8: O.I8}[vdt])
+    assert np.array_equal(host(vals), v_ref)
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
+# ------------------------------------------------------------------ fused A3 + A7 + A8
+@pytest.mark.parametrize("case", ["tiny24", "bf16_hess", "bf16_hess_full", "bf16_mag", "generic68", "generic14"])
+def test_prune_pack_fused(nm, case):
+    g = np.random.default_rng(7)
+    if case == "tiny24":
+        W, H, _ = synth.tiny24_inputs()
+        N, M, mode, Hn = 2, 4, nm.NM_SCORE_HESSIAN, H.numpy()
+    else:
+        R, K = 131, 264  # ragged rows; K not a multiple of 32 (partial index word)
+        W = _bf16(g.standard_normal((R, K)) * 0.02)
+        N, M = {"generic68": (6, 8), "generic14": (1, 4)}.get(case, (2, 4))
+        mode = nm.NM_SCORE_MAGNITUDE if case == "bf16_mag" else nm.NM_SCORE_HESSIAN
+        if case == "bf16_hess_full":
+            Hn = g.uniform(0.1, 1, (R, K)).astype(np.float32)
+        else:
+            Hn = g.uniform(0.1, 1, K).astype(np.float32)
+        H = torch.from_numpy(Hn)
+    Hd = None if mode == nm.NM_SCORE_MAGNITUDE else H.to(dev())
+    vals, idx, mask = nm.nm_prune_pack(W.to(dev()), Hd, 1e-6, mode, N, M)
+    Wn = host(W)
+    S = O.score(Wn, None if mode == nm.NM_SCORE_MAGNITUDE else Hn, 1e-6,
+                O.SCORE_MAGNITUDE if mode == nm.NM_SCORE_MAGNITUDE else O.SCORE_HESSIAN)
+    m_ref = O.topn_mask(S, N, M)
+    v_ref, i_ref = O.pack(Wn, m_ref, N, M, O.BF16)
+    assert np.array_equal(mask.cpu().numpy(), m_ref)
+    assert np.array_equal(host(vals), v_ref)
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
+def test_prune_pack_ternary_quant_then_mask(nm):
+    """Mask from the bf16 master weights, values from the ternary code."""
+    Wf, Wt = synth.ternary68_weights(R=70, K=256)
+    vals, idx, mask = nm.nm_prune_pack(Wf.to(dev()), None, 0.0, nm.NM_SCORE_MAGNITUDE, 6, 8, Wv=Wt.to(dev()))
+    m_ref = O.topn_mask(O.score(host(Wf), None, 0.0, O.SCORE_MAGNITUDE), 6, 8)
+    v_ref, i_ref = O.pack(Wt.numpy(), m_ref, 6, 8, O.I8)
+    assert np.array_equal(mask.cpu().numpy(), m_ref)
+    assert np.array_equal(vals.cpu().numpy(), v_ref)
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
+# ------------------------------------------------------------------ A9
+@pytest.mark.parametrize("Ns", [2, 3, 4, 5, 6, 7, 8])
+def test_slide_decompose_all_n(nm, Ns):
+    g = np.random.default_rng(200 + Ns)
+    M = 2 * Ns
+    R, K = 29, M * 21
+    W = _bf16(g.standard_normal((R, K)))
+    # masks with at most 2N-2 bits per group (the (2N-2):2N family), some sparser
+    keep = O.topn_mask(g.random((R, K)).astype(np.float32), M - 2, M) if M <= 8 else None
+    if keep is None:
+        bits = np.zeros((R, K), bool)
+        for r in range(R):
+            for gi in range(K // M):
+                sel = g.choice(M, size=g.integers(0, M - 1), replace=False)
+                bits[r, gi * M + sel] = True
+        keep = O.bool_to_mask(bits)
+    else:
+        drop = g.random((R, K)) < 0.1
+        keep = O.bool_to_mask(O.mask_to_bool(keep, K) & ~drop)
+    vals, idx = nm.nm_slide_decompose(W.to(dev()), torch.from_numpy(keep).to(dev()), Ns)
+    v_ref, i_ref, bad = O.slide_decompose(host(W), keep, Ns)
+    assert bad == 0
+    assert np.array_equal(host(vals), v_ref)
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "ternary"])
+def test_prune_slide_fused(nm, kind):
+    if kind == "bf16":
+        W = synth.slide68_weight(R=90, K=512)
+        Wv = None
+        v_host = host(W)
+    else:
+        W, Wt = synth.ternary68_weights(R=90, K=512)
+        Wv = Wt.to(dev())
+        v_host = Wt.numpy()
+    vals, idx, mask = nm.nm_prune_slide(W.to(dev()), None, 0.0, nm.NM_SCORE_MAGNITUDE, 4, Wv=Wv)
+    m_ref = O.topn_mask(O.score(host(W), None, 0.0, O.SCORE_MAGNITUDE), 6, 8)
+    v_ref, i_ref, bad = O.slide_decompose(v_host, m_ref, 4)
+    assert bad == 0
+    assert np.array_equal(mask.cpu().numpy(), m_ref)
+    assert np.array_equal(host(vals), v_ref)
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
+# ------------------------------------------------------------------ A10
+def test_absmean(nm):
+    Wf, _ = synth.ternary68_weights(R=300, K=2560)
+    a = float(nm.nm_absmean(Wf.to(dev())).cpu()[0])
+    ref = np.float32(O.absmean(host(Wf)))
+    # both reduce in double (different orders) and round once to float
+    assert abs(a - ref) <= 2 * np.spacing(ref)
