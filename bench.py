@@ -1,0 +1,286 @@
+"""Benchmark of the N:M sparsification hot path on one MI355X.
+
+One step = one pass of the whole path on the 2:4 bf16 Llama-7B-shaped layers:
+  1. H = column sums of squares of the calibration activations X_cal [512, 4096]
+  2. fused Hessian score (H + eps) W^2 -> top-2 of 4 -> packed bf16 values +
+     2-bit indices (+ mask bits), for W_a [4096, 4096] and W_b [11008, 4096]
+  3. the structured-sparse GEMM Y = X W_hat^T on both packed layers at
+     M = 1, 16, 128 and 2048 tokens.
+Inputs are synthetic (seeded, LLM-shaped) and resident in HBM before timing.
+
+Prints ONE JSON line.  value = dense-equivalent SpMM TFLOP per step (2*M*R*K
+summed over the eight products) divided by the whole step time.  The line also
+carries per-kernel HIP-event timings, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TOKENS = (1, 16, 128, 2048)
+LAYERS = (("W_a", 4096, 0), ("W_b", 11008, 1))
+K = 4096
+N_CAL = 512
+EPS = 1e-6
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--pmc-pass", action="store_true",
+                   help="run one step plus a plain 256 MiB copy (for HBM counter scaling) and exit")
+    return p.parse_args()
+
+
+class Step:
+    """Preallocated buffers and the raw C-ABI calls of one step."""
+
+    def __init__(self, nm, torch, synth, dev):
+        self.nm, self.torch = nm, torch
+        bf = torch.bfloat16
+        self.Xcal = synth.llama24_calib(N_CAL, K).to(dev)
+        self.H = torch.empty(K, dtype=torch.float32, device=dev)
+        self.ws_h = torch.empty(max(1, nm.raw.nm_colsumsq_workspace(N_CAL, K)), dtype=torch.uint8, device=dev)
+        self.layers = []
+        for name, R, tid in LAYERS:
+            W = synth.llama24_weight(R, K, tensor_id=tid).to(dev)
+            vals = torch.empty((R, K // 2), dtype=bf, device=dev)
+            idx = torch.empty((R, K // 32), dtype=torch.int32, device=dev)
+            mask = torch.empty((R, K // 8), dtype=torch.uint8, device=dev)
+            self.layers.append(dict(name=name, R=R, W=W, vals=vals, idx=idx, mask=mask))
+        self.X = {M: synth.activations_bf16(1, M, K).to(dev) for M in TOKENS}
+        self.Y = {(l["name"], M): torch.empty((M, l["R"]), dtype=bf, device=dev) for l in self.layers for M in TOKENS}
+        need = max(nm.raw.nm_spmm_workspace(M, K, l["R"], 0, nm.NM_BF16) for l in self.layers for M in TOKENS)
+        self.ws_s = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def launches(self):
+        """(kernel name, callable) in step order."""
+        nm, r = self.nm, self.nm.raw
+        out = []
+
+        def chk(st):
+            if st != 0:
+                raise nm.NMError(st, nm.last_error())
+
+        def colsumsq(stream):
+            chk(r.nm_hdiag_colsumsq(self.Xcal.data_ptr(), nm.NM_BF16, N_CAL, K, K, self.H.data_ptr(),
+                                    self.ws_h.data_ptr(), self.ws_h.numel(), stream))
+        out.append(("colsumsq", colsumsq))
+        for l in self.layers:
+            def prune(stream, l=l):
+                chk(r.nm_prune_pack(l["W"].data_ptr(), nm.NM_BF16, K, self.H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN,
+                                    l["W"].data_ptr(), nm.NM_BF16, K, l["R"], K, 2, 4, l["mask"].data_ptr(), K // 8,
+                                    nm.NM_BF16, l["vals"].data_ptr(), K // 2, l["idx"].data_ptr(), K // 32, stream))
+            out.append((f"prune_pack {l['name']}", prune))
+        for l in self.layers:
+            for M in TOKENS:
+                def spmm(stream, l=l, M=M):
+                    Y = self.Y[(l["name"], M)]
+                    chk(r.nm_spmm(self.X[M].data_ptr(), nm.NM_BF16, M, K, K, l["vals"].data_ptr(), nm.NM_BF16,
+                                  l["idx"].data_ptr(), l["R"], K // 2, K // 32, 0, None, 1.0, Y.data_ptr(), nm.NM_BF16,
+                                  l["R"], self.ws_s.data_ptr(), self.ws_s.numel(), stream))
+                out.append((f"spmm {l['name']} M={M}", spmm))
+        return out
+
+    def run(self, stream):
+        for _, f in self.launches():
+            f(stream)
+
+
+def algorithmic_work():
+    """Per-launch algorithmic bytes (HBM-bound kernels) or flops (GEMMs)."""
+    w = {"colsumsq": dict(bound="hbm", bytes=N_CAL * K * 2 + K * 4)}
+    for name, R, _ in LAYERS:
+        # read W (2 B) ; write 2 of 4 values (1 B), 2-bit indices (0.125 B), mask bit (0.125 B) per weight; read H
+        w[f"prune_pack {name}"] = dict(bound="hbm", bytes=int(R * K * 3.25) + K * 4)
+        for M in TOKENS:
+            packed = R * K // 2 * 2 + R * K // 32 * 4
+            w[f"spmm {name} M={M}"] = dict(
+                bound="mfma",
+                flops_dense_eq=2 * M * R * K,          # dense-equivalent work
+                flops=2 * M * R * K // 2,              # multiply-adds on kept weights only (2 of 4)
+                bytes=packed + M * K * 2 + M * R * 2)  # packed weight + X + Y
+    return w
+
+
+def cpu_baseline(target_s: float):
+    """The oracle on a row sample of the same step, scaled to dense-eq TFLOP/s."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    import torch
+
+    def bits(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    Xcal = bits(synth.llama24_calib(N_CAL, K))
+    Ws = {name: bits(synth.llama24_weight(R, K, tensor_id=tid)) for name, R, tid in LAYERS}
+    Xs = {M: bits(synth.activations_bf16(1, M, K)) for M in TOKENS}
+
+    def run(rows):
+        t0 = time.perf_counter()
+        H = O.colsumsq(Xcal).astype(np.float32)
+        flops = 0
+        for name, R, tid in LAYERS:
+            W = np.ascontiguousarray(Ws[name][:rows])
+            S = O.score(W, H, EPS)
+            mask = O.topn_mask(S, 2, 4)
+            O.pack(W, mask, 2, 4)
+            for M in TOKENS:
+                O.masked_matmul(Xs[M], W, mask)
+                flops += 2 * M * rows * K
+        return time.perf_counter() - t0, flops
+
+    # time a small sample, then size the real one to the target
+    t_small, _ = run(8)
+    rows = int(max(8, min(4096, 8 * target_s / max(t_small, 1e-3))))
+    t, flops = run(rows)
+    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=O.num_threads(), kind="oracle",
+                sample=f"whole step on the first {rows} output rows of each layer (H, score, top-2 of 4, pack, "
+                       f"and the masked matmul at M=1,16,128,2048), {t:.1f} s")
+
+
+def traffic_for(kernel_file: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
+    source has not changed since they were taken."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+        e = d.get(kernel)
+        if not e:
+            return None
+        src = (ROOT / "semi_structured_sparsity_amd" / "csrc" / kernel_file).read_bytes()
+        if hashlib.sha256(src).hexdigest() != e["source_sha256"]:
+            return None
+        return int(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs on a single MI355X. "
+              "The sharding design is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import semi_structured_sparsity_amd as nm
+    import synth
+
+    dev = torch.device("cuda:0")
+    st = Step(nm, torch, synth, dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    if args.pmc_pass:
+        st.run(sh)
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        a.copy_(b)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": "done", "copy_bytes": 256 << 20}))
+        return
+
+    for _ in range(args.warmup):
+        st.run(sh)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st.run(sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+
+    # per-kernel durations: HIP events around each launch on the launch stream
+    launches = st.launches()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+          for _ in range(args.steps)]
+    for s in range(args.steps):
+        for j, (_, f) in enumerate(launches):
+            ev[s][j][0].record(stream)
+            f(sh)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    work = algorithmic_work()
+    kernels = []
+    for j, (name, _) in enumerate(launches):
+        t_ms = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
+        w = work[name]
+        k = dict(name=name, us=round(t_ms * 1e3, 2), bound=w["bound"])
+        if w["bound"] == "hbm":
+            k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
+            k["frac"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
+        else:
+            k["eff_TFLOPs"] = round(w["flops_dense_eq"] / (t_ms * 1e-3) / 1e12, 2)
+            k["TFLOPs"] = round(w["flops"] / (t_ms * 1e-3) / 1e12, 2)
+            k["frac"] = round(k["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+            k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
+        kernels.append(k)
+    dom = max(kernels, key=lambda k: k["us"])
+    wd = work[dom["name"]]
+    if dom["bound"] == "hbm":
+        kfile = "k_prune.hip"
+        roof = dict(bound="hbm", achieved=dom["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s", frac=dom["frac"])
+    else:
+        kfile = "k_spmm.hip"
+        roof = dict(bound="mfma", achieved=dom["TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=dom["frac"])
+    roof["kernel"] = dom["name"]
+    roof["traffic"] = traffic_for(kfile, dom["name"])
+
+    spmm_flops = sum(w["flops_dense_eq"] for n, w in work.items() if n.startswith("spmm"))
+    maskpack = [k for k in kernels if k["name"].startswith("prune_pack")]
+    mp_bytes = sum(work[k["name"]]["bytes"] for k in maskpack)
+    mp_us = sum(k["us"] for k in maskpack)
+    spmm_us = sum(k["us"] for k in kernels if k["name"].startswith("spmm"))
+
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": "N:M SpMM effective TFLOP/s + mask/pack GB/s, as % of MI355X roofline",
+        "value": round(spmm_flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama24: 2:4 bf16 Llama-7B-shaped layers W 4096x4096 and 11008x4096 (1% outlier "
+                               "input channels x20), H from X_cal 512x4096, fused score/top-2-of-4/pack, "
+                               "SpMM at M in {1,16,128,2048}",
+                   "pattern": "2:4", "K": K, "tokens": list(TOKENS)},
+        "spmm_effective_TFLOPs": round(spmm_flops / (spmm_us * 1e-6) / 1e12, 2),
+        "maskpack_GBps": round(mp_bytes / (mp_us * 1e-6) / 1e9, 1),
+        "maskpack_frac_hbm": round(mp_bytes / (mp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -80,6 +80,7 @@ def _declare(L):
         "or_stats": (None, [P, I64, P, P]),
         "or_gate_anneal": (None, [P, I64, I64, D, D, I, I, D, D, I, P, P, I64, P]),
         "or_gate_value": (D, [F, D, D, D, D, I]),
+        "or_num_threads": (I, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -324,6 +325,10 @@ def gate_anneal(S: np.ndarray, mu: float, sigma: float, N: int, M: int, T0: floa
     lm = np.empty(steps, np.float64)
     lib().or_gate_anneal(_p(S), R, K, mu, sigma, N, M, T0, rho, steps, _p(mf), _p(hm), hm.shape[1], _p(lm))
     return mf, hm, lm
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
 
 
 def gate_value(s: float, mu: float, sigma: float, T0: float, rho: float, t: int) -> float:

@@ -34,6 +34,7 @@
  *   [SA]  "SALR" summary, Methodology 1 (magnitude pruning of the frozen base).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -379,7 +380,7 @@ void or_lift(const void* X, int xdt, int64_t Mt, int64_t K, int Ns, void* Xl) {
 void or_masked_matmul(const void* X, int xdt, int64_t Mt, int64_t K, int64_t ldx,
                       const void* W, int wdt, int64_t R, int64_t ldw,
                       const uint8_t* mask, int64_t ldm, double* Y) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < Mt; ++m)
         for (int64_t o = 0; o < R; ++o) {
             double acc = 0.0;
@@ -577,6 +578,9 @@ void or_gate_anneal(const float* S, int64_t R, int64_t K, double mu, double sigm
     free(mlast);
     free(h);
 }
+
+/* Number of threads the parallel loops above use. */
+int or_num_threads(void) { return omp_get_max_threads(); }
 
 /* Gate value for a single element at step t (for sampled checks). */
 double or_gate_value(float s, double mu, double sigma, double T0, double rho, int t) {
