@@ -314,6 +314,269 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
         }
 }
 
+
+// ------------------------------------------------------------------ ring-pipelined kernel (plain 2:4, many tokens)
+// Block tile 2*SR*32 weight rows x 2*ST*32 tokens, 4 waves (2 x 2), each wave
+// SR x ST 32x32 SMFMAC tiles.  Operands stream from global memory straight into
+// an NS-stage LDS ring with global_load_lds (16 bytes per lane, placed
+// lane-major), so no registers stage them and NS-1 stages are in flight while
+// one is consumed.  The loads are issued from inline assembly and counted by
+// hand (s_waitcnt vmcnt), and the stage hand-off uses an LDS-only barrier, so
+// the compiler never drains the whole ring.
+// LDS layouts (16-byte chunks XOR-swizzled so that any 16 consecutive rows of
+// a fragment read hit distinct banks):
+//   A values: row r (64 B = 4 chunks), logical chunk c stored at c ^ ((r>>2)&3)
+//   A index : row r, AI words, unswizzled
+//   X       : token t (128 B = 8 chunks), logical chunk c stored at c ^ ((t>>1)&7)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// A block-uniform pointer, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// saddr form: uniform 64-bit base in SGPRs + per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16s(uint32_t lds, const void* base, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(uint32_t lds, const void* base, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* g) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename T, int SR, int ST, int KB, int NS>
+struct Ring {
+    static constexpr int BR = 2 * SR * 32;             // weight rows per block
+    static constexpr int BT = 2 * ST * 32;             // tokens per block
+    static constexpr int KO = KB / (int)sizeof(T);     // original columns per stage (KB bytes of X per token)
+    static constexpr int ND = KB / 64;                 // SMFMAC depths per stage
+    static constexpr int AROW = KB / 2;                // compressed bytes per weight row per stage
+    static constexpr int AI = KO / 32;                 // index words per row per stage
+    static constexpr int A_OFF = 0;
+    static constexpr int I_OFF = BR * AROW;
+    static constexpr int B_OFF = I_OFF + BR * AI * 4;
+    static constexpr int STAGE = B_OFF + BT * KB;
+    static constexpr int NA = BR * AROW / 1024 / 4;    // A wave-instructions per wave
+    static constexpr bool I16 = AI >= 4;               // index rows loaded in 16-byte pieces (else dwords)
+    static constexpr int NI = BR * AI * 4 / (I16 ? 1024 : 256) / 4;
+    static constexpr int NB = BT * KB / 1024 / 4;      // X wave-instructions per wave
+    static constexpr int PER = NA + NI + NB;           // loads per wave per stage
+    static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
+    static_assert(NA >= 1 && NI >= 1 && NB >= 1, "tile too small for 4 waves");
+    static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
+    // XOR swizzles of 16-byte chunks (16 consecutive rows of a fragment read hit distinct banks)
+    __device__ static int swa(int r) { return AROW == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+    __device__ static int swb(int t) { return KB == 128 ? ((t >> 1) & 7) : (t & 15); }
+};
+
+template <int SR, int ST>
+struct RingFrag {          // fragments of one SMFMAC depth
+    i32x4_t a[SR];         // compressed values per row sub-tile
+    uint32_t iw[SR];       // index fields per row sub-tile
+    i32x8_t b[ST];         // X fragment per token sub-tile
+};
+
+// NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
+template <typename T, int SR, int ST, int KB, int NS, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
+    using RG = Ring<T, SR, ST, KB, NS>;
+    using FR = RingFrag<SR, ST>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * RG::STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave & 1, wt = wave >> 1;
+    int tr, tt;
+    tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
+    const int64_t r0 = (int64_t)tr * RG::BR, t0 = (int64_t)tt * RG::BT;
+    const int nsteps = a.nsteps;
+    const uint32_t sbase = lds_addr(smem);
+    const int64_t es = sizeof(T);
+
+    // per-lane byte offsets (from the block's base pointers, which live in SGPRs)
+    // at stage 0; stage s adds s * (row bytes per stage)
+    constexpr int ACH = RG::AROW / 16, BCH = KB / 16;  // 16-byte chunks per row
+    const void* baseA = uniform_ptr(a.vals + r0 * a.ldv * es);
+    const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
+    const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
+    const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
+    uint32_t oA[RG::NA], oI[RG::NI], oB[RG::NB];
+#pragma unroll
+    for (int i = 0; i < RG::NA; ++i) {
+        const int row = (wave * RG::NA + i) * (64 / ACH) + lane / ACH;
+        const int c = (lane % ACH) ^ RG::swa(row);
+        const int64_t gr = row < rmax ? row : rmax;
+        oA[i] = (uint32_t)(gr * a.ldv * es + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < RG::NI; ++i) {
+        const int q = (wave * RG::NI + i) * 64 + lane;  // piece index (16-byte or dword)
+        constexpr int PPR = RG::I16 ? RG::AI / 4 : RG::AI;   // pieces per row
+        const int row = q / PPR, part = q % PPR;
+        const int64_t gr = row < rmax ? row : rmax;
+        oI[i] = (uint32_t)(gr * a.ldi * 4 + part * (RG::I16 ? 16 : 4));
+    }
+#pragma unroll
+    for (int i = 0; i < RG::NB; ++i) {
+        const int row = (wave * RG::NB + i) * (64 / BCH) + lane / BCH;
+        const int c = (lane % BCH) ^ RG::swb(row);
+        const int64_t gt = row < tmax ? row : tmax;
+        oB[i] = (uint32_t)(gt * a.ldx * es + c * 16);
+    }
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const uint32_t st = sbase + (uint32_t)((s % NS) * RG::STAGE);
+#pragma unroll
+        for (int i = 0; i < RG::NA; ++i)
+            dma16s(st + RG::A_OFF + (wave * RG::NA + i) * 1024, baseA, oA[i] + (uint32_t)(s * RG::AROW));
+#pragma unroll
+        for (int i = 0; i < RG::NI; ++i) {
+            if constexpr (RG::I16)
+                dma16s(st + RG::I_OFF + (wave * RG::NI + i) * 1024, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+            else
+                dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+        }
+#pragma unroll
+        for (int i = 0; i < RG::NB; ++i)
+            dma16s(st + RG::B_OFF + (wave * RG::NB + i) * 1024, baseB, oB[i] + (uint32_t)(s * KB));
+    };
+    const int h = lane >> 5, l32 = lane & 31;
+    auto read_depth = [&](int slot, int d, FR& f) __attribute__((always_inline)) {
+        const uint8_t* sA = smem + slot * RG::STAGE + RG::A_OFF;
+        const uint32_t* sI = (const uint32_t*)(smem + slot * RG::STAGE + RG::I_OFF);
+        const uint8_t* sB = smem + slot * RG::STAGE + RG::B_OFF;
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int row = (wr * SR + i) * 32 + l32;
+            f.a[i] = *(const i32x4_t*)(sA + row * RG::AROW + ((2 * d + h) ^ RG::swa(row)) * 16);
+            if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d] >> (16 * h);
+            else f.iw[i] = sI[row * RG::AI + 2 * d + h];
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int tok = (wt * ST + j) * 32 + l32;
+            const i32x4_t lo = *(const i32x4_t*)(sB + tok * KB + ((4 * d + h) ^ RG::swb(tok)) * 16);
+            const i32x4_t hi = *(const i32x4_t*)(sB + tok * KB + ((4 * d + 2 + h) ^ RG::swb(tok)) * 16);
+            f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    using AccV = typename std::conditional<sizeof(T) == 2, f32x16_t, i32x16_t>::type;
+    AccV acc[SR][ST];
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[i][j] = AccV{};
+
+    auto mfmas = [&](const FR& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                if constexpr (sizeof(T) == 2)
+                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                                         __builtin_bit_cast(bf16x16_t, f.b[j]),
+                                                                         acc[i][j], (int)f.iw[i], 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[i], f.b[j], acc[i][j], (int)f.iw[i], 0, 0);
+            }
+    };
+
+    // Prologue: stages 0..NS-1 fill the ring; wait for stage 0 (the other NS-1
+    // may stay in flight) and read its depth 0.  Every depth step reads the next
+    // depth's fragments before issuing the current depth's SMFMACs.  The last
+    // depth of stage S waits for stage S+1 (stages S+2..S+NS-1 may stay in
+    // flight), passes the barrier, reads depth 0 of stage S+1 and refills the
+    // slot of stage S (fully read into registers by every wave) with stage S+NS.
+    FR fa, fb;
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+        if (p < nsteps) issue(p);
+    if (nsteps >= NS) wait_vm_barrier<(NS - 1) * RG::PER>();
+    else wait_vm_barrier<0>();
+    if (nsteps > 0) read_depth(0, 0, fa);
+    for (int S = 0; S < nsteps; ++S) {
+        const int slot = S % NS;
+#pragma unroll
+        for (int d = 0; d < RG::ND; d += 2) {
+            read_depth(slot, d + 1, fb);
+            mfmas(fa);
+            if (d + 2 < RG::ND) {
+                read_depth(slot, d + 2, fa);
+            } else if (S + 1 < nsteps) {
+                if (S + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * RG::PER>();
+                else wait_vm_barrier<0>();
+                read_depth((S + 1) % NS, 0, fa);
+                if (S + NS < nsteps) issue(S + NS);
+            }
+            mfmas(fb);
+        }
+    }
+    wait_vm_all();
+
+    // Epilogue.  Lane holds token column l32 and rows 8*(e/4) + 4*h + e%4 of
+    // each 32x32 sub-tile.  Tiles fully inside Y with plain bf16 output take
+    // 8-byte vector stores with no per-element tests.
+    const bool fast = (r0 + RG::BR <= a.R) && (t0 + RG::BT <= a.Mtok) && !a.scaled && a.ydt == NM_BF16;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                const int64_t tok = t0 + (wt * ST + j) * 32 + l32;
+                uint16_t* yrow = (uint16_t*)a.Y + tok * a.ldy + r0 + (wr * SR + i) * 32 + 4 * h;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t w0 = f32_to_bf16_bits((float)acc[i][j][4 * g]) |
+                                        (f32_to_bf16_bits((float)acc[i][j][4 * g + 1]) << 16);
+                    const uint32_t w1 = f32_to_bf16_bits((float)acc[i][j][4 * g + 2]) |
+                                        (f32_to_bf16_bits((float)acc[i][j][4 * g + 3]) << 16);
+                    *(uint2*)(yrow + 8 * g) = make_uint2(w0, w1);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                const int64_t tok = t0 + (wt * ST + j) * 32 + l32;
+                const bool tok_ok = tok < a.Mtok;
+                const float xs = (a.scaled && a.x_scale && tok_ok) ? a.x_scale[tok] : 1.0f;
+                const float sc = __fmul_rn(a.w_scale, xs);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t r = r0 + (wr * SR + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    if (tok_ok && r < a.R) {
+                        const auto v = acc[i][j][e];
+                        const int64_t o = tok * a.ldy + r;
+                        if (a.ydt == NM_I32) {
+                            ((int32_t*)a.Y)[o] = (int32_t)v;
+                        } else {
+                            const float f = a.scaled ? __fmul_rn(sc, (float)v) : (float)v;
+                            if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
+                            else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
+                        }
+                    }
+                }
+            }
+    }
+}
+
 // Split-K reduction: partials summed in split order, then the epilogue.
 template <typename Acc>
 __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
@@ -339,20 +602,31 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
-    bool large;
+    bool large, ring, wide;
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
+// SR, ST, NS of the ring kernel
+// ring shapes: wide (256 x 256 tile, 3 stages of 128 B) and narrow (256 x 128 tile, 2 stages of 256 B)
+#define NM_RING_WIDE T, 4, 4, 128, 3
+#define NM_RING_NARROW T, 4, 2, 256, 2
+
 template <typename T, bool LIFT>
-static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R) {
+static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
     using G = Geo<T, LIFT>;
     SpmmPlan p{};
     p.large = Mtok > 128;
-    const int BR = 128;
-    const int BT = p.large ? 128 : 32;
+    using RW = Ring<NM_RING_WIDE>;
+    using RN = Ring<NM_RING_NARROW>;
+    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0 && (K % RW::KO) == 0;
+    // the wide tile moves 27% fewer bytes per MAC; use it when it still gives
+    // at least one full wave of tiles on 256 CUs
+    p.wide = p.ring && ceil_div(R, RW::BR) * ceil_div(Mtok, RW::BT) >= 256;
+    const int BR = p.ring ? (p.wide ? RW::BR : RN::BR) : 128;
+    const int BT = p.ring ? (p.wide ? RW::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
     p.tiles_t = (int)ceil_div(Mtok, BT);
-    p.nsteps = (int)ceil_div(K, G::KO);
+    p.nsteps = (int)ceil_div(K, p.ring ? (p.wide ? RW::KO : RN::KO) : G::KO);
     const int64_t blocks = (int64_t)p.tiles_r * p.tiles_t;
     int KS = 1;
     if (!p.large) {
@@ -378,7 +652,11 @@ size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
 
 template <typename T, bool LIFT>
 static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
-    const SpmmPlan p = plan_for<T, LIFT>(a.Mtok, a.K, a.R);
+    // the ring kernel loads 16-byte pieces of the index rows
+    const bool ring_ok = ((uintptr_t)a.idx & 15u) == 0 && (a.ldi % 4) == 0 &&
+                         a.R * a.ldv * (int64_t)sizeof(T) < (1LL << 32) && a.R * a.ldi * 4 < (1LL << 32) &&
+                         a.Mtok * a.ldx * (int64_t)sizeof(T) < (1LL << 32);
+    const SpmmPlan p = plan_for<T, LIFT>(a.Mtok, a.K, a.R, ring_ok);
     a.nsteps = p.nsteps;
     a.KS = p.KS;
     a.steps_per_split = p.steps_per_split;
@@ -391,7 +669,12 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         a.part = ws;
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
-    if (p.large)
+    if (p.ring) {
+        if constexpr (!LIFT) {
+            if (p.wide) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_WIDE>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW>), grid, dim3(256), 0, s, a);
+        }
+    } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((spmm_kernel<T, LIFT, 4, 1, 1, 1>), grid, dim3(256), 0, s, a);
