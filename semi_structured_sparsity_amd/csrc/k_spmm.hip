@@ -577,6 +577,165 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
     }
 }
 
+
+// ------------------------------------------------------------------ skinny kernel (few tokens: weight-streaming)
+// For few tokens the product is bound by the HBM stream of the packed weight.
+// A block of KSPLIT waves owns 32*SRk weight rows and 32*STk tokens; wave w
+// walks its own slice of the SMFMAC depths, loading the packed values, their
+// index words and the X fragments straight from global memory into registers
+// (X is small and stays in L2).  The KSPLIT partial tiles are then summed
+// through LDS in wave order (deterministic) and written out.
+// With LIFT the X fragment is gathered in lifted order: lifted column L reads
+// original column (L / 4(N-1)) * 2N + 2 * ((L % 4(N-1)) / 4) + L % 4, in windows
+// of 4 consecutive original columns (N = 4 here: 12 lifted per 8 original).
+template <typename T, bool LIFT>
+__device__ __forceinline__ int lift_col(int L) {
+    if constexpr (!LIFT) return L;
+    else return (L / 12) * 8 + 2 * ((L % 12) / 4) + (L & 3);
+}
+
+template <typename T, bool LIFT>
+__device__ __forceinline__ i32x8_t load_xfrag(const uint8_t* xrow, int Lbase, int h) {
+    // element e of the fragment is lifted column Lbase + KE*(e/(EL/2)) + (EL/2)*h + e%(EL/2), where
+    // bf16: EL = 16 elements (KE = 16), int8: EL = 32 elements (KE = 32)
+    constexpr int es = sizeof(T);
+    constexpr int HALF = 16 / es;  // elements per 16-byte half
+    i32x8_t r;
+    if constexpr (!LIFT) {
+        const i32x4_t lo = *(const i32x4_t*)(xrow + (int64_t)(Lbase + HALF * h) * es);
+        const i32x4_t hi = *(const i32x4_t*)(xrow + (int64_t)(Lbase + 2 * HALF + HALF * h) * es);
+        r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int L0 = Lbase + q * 2 * HALF + HALF * h;   // 16 bytes of lifted columns = HALF elements
+#pragma unroll
+            for (int win = 0; win < HALF / 4; ++win) {
+                const int oc = lift_col<T, true>(L0 + 4 * win);  // window start (even column)
+                if constexpr (es == 2) {
+                    const uint32_t* p = (const uint32_t*)(xrow + (int64_t)oc * 2);
+                    w[q * 4 + 2 * win] = p[0];
+                    w[q * 4 + 2 * win + 1] = p[1];
+                } else {
+                    const uint16_t* p = (const uint16_t*)(xrow + oc);
+                    w[q * 4 + win] = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+                }
+            }
+        }
+        r = i32x8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
+    return r;
+}
+
+template <typename T, bool LIFT, int SRk, int STk, int KSPLIT>
+__global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
+    constexpr int es = sizeof(T);
+    constexpr int KDEP = es == 2 ? 32 : 64;      // lifted columns per SMFMAC
+    __shared__ float red[KSPLIT * 64 * 16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t r0 = (int64_t)blockIdx.x * (32 * SRk), t0 = (int64_t)blockIdx.y * (32 * STk);
+    const int64_t Kl = a.comp_bytes * 2 / es;     // lifted width
+    const int D = (int)(Kl / KDEP);
+    const int per = (D + KSPLIT - 1) / KSPLIT;
+    const int d0 = wave * per, d1 = d0 + per < D ? d0 + per : D;
+
+    const uint8_t* arow[SRk];
+    const uint32_t* irow[SRk];
+#pragma unroll
+    for (int i = 0; i < SRk; ++i) {
+        int64_t r = r0 + 32 * i + l32;
+        r = r < a.R ? r : a.R - 1;
+        arow[i] = a.vals + r * a.ldv * es + 16 * h;
+        irow[i] = a.idx + r * a.ldi;
+    }
+    const uint8_t* xrow[STk];
+    bool tok_ok[STk];
+#pragma unroll
+    for (int j = 0; j < STk; ++j) {
+        int64_t t = t0 + 32 * j + l32;
+        tok_ok[j] = t < a.Mtok;
+        t = tok_ok[j] ? t : 0;
+        xrow[j] = a.X + t * a.ldx * es;
+    }
+    using AccV = typename std::conditional<es == 2, f32x16_t, i32x16_t>::type;
+    AccV acc[SRk][STk];
+#pragma unroll
+    for (int i = 0; i < SRk; ++i)
+#pragma unroll
+        for (int j = 0; j < STk; ++j) acc[i][j] = AccV{};
+
+    constexpr int U = 4;  // depths in flight per wave
+    for (int d = d0; d < d1; d += U) {
+        i32x4_t fa[U][SRk];
+        uint32_t fi[U][SRk];
+        i32x8_t fb[U][STk];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int dd = d + u < d1 ? d + u : d1 - 1;   // tail depths repeat a valid one, then are skipped
+#pragma unroll
+            for (int i = 0; i < SRk; ++i) {
+                fa[u][i] = *(const i32x4_t*)(arow[i] + (int64_t)dd * 32);
+                if constexpr (es == 2) fi[u][i] = irow[i][dd] >> (16 * h);
+                else fi[u][i] = irow[i][2 * dd + h];
+            }
+#pragma unroll
+            for (int j = 0; j < STk; ++j)
+                fb[u][j] = tok_ok[j] ? load_xfrag<T, LIFT>(xrow[j], dd * KDEP, h) : i32x8_t{};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (d + u < d1) {
+#pragma unroll
+                for (int i = 0; i < SRk; ++i)
+#pragma unroll
+                    for (int j = 0; j < STk; ++j) {
+                        if constexpr (es == 2)
+                            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, fa[u][i]), __builtin_bit_cast(bf16x16_t, fb[u][j]),
+                                acc[i][j], (int)fi[u][i], 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(fa[u][i], fb[u][j], acc[i][j],
+                                                                               (int)fi[u][i], 0, 0);
+                    }
+            }
+        }
+    }
+
+    // fixed-order reduction of the KSPLIT partial tiles, one 32x32 sub-tile at a time
+#pragma unroll
+    for (int i = 0; i < SRk; ++i)
+#pragma unroll
+        for (int j = 0; j < STk; ++j) {
+            __syncthreads();
+            *(AccV*)&red[(wave * 64 + lane) * 16] = acc[i][j];
+            __syncthreads();
+            for (int q = tid; q < 1024; q += KSPLIT * 64) {
+                const int tok = q >> 5, row = q & 31;                      // Y element (token, row) of the sub-tile
+                const int src_lane = tok + 32 * ((row >> 2) & 1), e = 4 * (row >> 3) + (row & 3);
+                const int64_t gt = t0 + 32 * j + tok, gr = r0 + 32 * i + row;
+                using AccS = typename std::conditional<es == 2, float, int32_t>::type;
+                AccS v = 0;
+                for (int w = 0; w < KSPLIT; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
+                if (gt < a.Mtok && gr < a.R) {
+                    const int64_t o = gt * a.ldy + gr;
+                    if (a.ydt == NM_I32) {
+                        ((int32_t*)a.Y)[o] = (int32_t)v;
+                    } else {
+                        float f = (float)v;
+                        if (a.scaled) {
+                            const float xs = a.x_scale ? a.x_scale[gt] : 1.0f;
+                            f = __fmul_rn(__fmul_rn(a.w_scale, xs), f);
+                        }
+                        if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
+                        else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
+                    }
+                }
+            }
+        }
+}
+
 // Split-K reduction: partials summed in split order, then the epilogue.
 template <typename Acc>
 __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
@@ -603,6 +762,7 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
     bool large, ring, wide;
+    int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
@@ -626,10 +786,16 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     const int BT = p.ring ? (p.wide ? RW::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
     p.tiles_t = (int)ceil_div(Mtok, BT);
+    {
+        constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;
+        const int64_t Kl = LIFT ? K / 8 * 12 : K;
+        p.skinny = 0;
+        if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
+    }
     p.nsteps = (int)ceil_div(K, p.ring ? (p.wide ? RW::KO : RN::KO) : G::KO);
     const int64_t blocks = (int64_t)p.tiles_r * p.tiles_t;
     int KS = 1;
-    if (!p.large) {
+    if (!p.large && !p.skinny) {
         const int64_t target = 1024;
         while ((int64_t)KS * blocks < target && KS * 4 <= p.nsteps) KS *= 2;
     }
@@ -669,7 +835,13 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         a.part = ws;
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
-    if (p.ring) {
+    if (p.skinny == 1) {
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(512), 0, s, a);
+    } else if (p.skinny == 2) {
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(512), 0, s, a);
+    } else if (p.skinny == 3) {
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
+    } else if (p.ring) {
         if constexpr (!LIFT) {
             if (p.wide) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_WIDE>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW>), grid, dim3(256), 0, s, a);
