@@ -628,12 +628,13 @@ __device__ __forceinline__ i32x8_t load_xfrag(const uint8_t* xrow, int Lbase, in
     return r;
 }
 
-template <typename T, bool LIFT, int SRk, int STk, int KSPLIT>
+template <typename T, bool LIFT, int SRk, int STk, int KSPLIT, int U>
 __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
     constexpr int es = sizeof(T);
     constexpr int KDEP = es == 2 ? 32 : 64;      // lifted columns per SMFMAC
     __shared__ float red[KSPLIT * 64 * 16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t r0 = (int64_t)blockIdx.x * (32 * SRk), t0 = (int64_t)blockIdx.y * (32 * STk);
     const int64_t Kl = a.comp_bytes * 2 / es;     // lifted width
@@ -650,13 +651,13 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
         arow[i] = a.vals + r * a.ldv * es + 16 * h;
         irow[i] = a.idx + r * a.ldi;
     }
+    // B columns are independent in the product, so lanes past the last token load a valid
+    // token's row and their (unwritten) output columns are simply discarded
     const uint8_t* xrow[STk];
-    bool tok_ok[STk];
 #pragma unroll
     for (int j = 0; j < STk; ++j) {
         int64_t t = t0 + 32 * j + l32;
-        tok_ok[j] = t < a.Mtok;
-        t = tok_ok[j] ? t : 0;
+        t = t < a.Mtok ? t : a.Mtok - 1;
         xrow[j] = a.X + t * a.ldx * es;
     }
     using AccV = typename std::conditional<es == 2, f32x16_t, i32x16_t>::type;
@@ -666,14 +667,16 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < STk; ++j) acc[i][j] = AccV{};
 
-    constexpr int U = 4;  // depths in flight per wave
-    for (int d = d0; d < d1; d += U) {
+    // U depths per batch: every load of a batch is issued before its first SMFMAC.  Full
+    // batches run branch-free; the short last batch (depth bounds are wave-uniform) takes a
+    // separate path so that the compiler does not sink the loads of full batches into branches.
+    auto batch = [&](int d, int n) __attribute__((always_inline)) {
         i32x4_t fa[U][SRk];
         uint32_t fi[U][SRk];
         i32x8_t fb[U][STk];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int dd = d + u < d1 ? d + u : d1 - 1;   // tail depths repeat a valid one, then are skipped
+            const int dd = u < n ? d + u : d;
 #pragma unroll
             for (int i = 0; i < SRk; ++i) {
                 fa[u][i] = *(const i32x4_t*)(arow[i] + (int64_t)dd * 32);
@@ -681,12 +684,12 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                 else fi[u][i] = irow[i][2 * dd + h];
             }
 #pragma unroll
-            for (int j = 0; j < STk; ++j)
-                fb[u][j] = tok_ok[j] ? load_xfrag<T, LIFT>(xrow[j], dd * KDEP, h) : i32x8_t{};
+            for (int j = 0; j < STk; ++j) fb[u][j] = load_xfrag<T, LIFT>(xrow[j], dd * KDEP, h);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the SMFMACs
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (d + u < d1) {
+            if (u < n) {
 #pragma unroll
                 for (int i = 0; i < SRk; ++i)
 #pragma unroll
@@ -701,7 +704,10 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                     }
             }
         }
-    }
+    };
+    int d = d0;
+    for (; d + U <= d1; d += U) batch(d, U);
+    if (d < d1) batch(d, d1 - d);
 
     // fixed-order reduction of the KSPLIT partial tiles, one 32x32 sub-tile at a time
 #pragma unroll
@@ -836,11 +842,19 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
     if (p.skinny == 1) {
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(512), 0, s, a);
+        // 32-row tiles, 4 waves split K, 16 depths in flight per wave
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
     } else if (p.skinny == 2) {
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(512), 0, s, a);
+        // two 32-row tiles per wave share each X fragment when that still leaves >= 200 blocks
+        if (ceil_div(a.R, 64) >= 200)
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 4, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
     } else if (p.skinny == 3) {
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
+        if (ceil_div(a.R, 64) >= 128)
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
     } else if (p.ring) {
         if constexpr (!LIFT) {
             if (p.wide) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_WIDE>), grid, dim3(256), 0, s, a);
