@@ -316,7 +316,7 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
 
 
 // ------------------------------------------------------------------ ring-pipelined kernel (plain 2:4, many tokens)
-// Block tile 2*SR*32 weight rows x 2*ST*32 tokens, 4 waves (2 x 2), each wave
+// Block tile WRN*SR*32 weight rows x WTN*ST*32 tokens, WRN x WTN waves, each wave
 // SR x ST 32x32 SMFMAC tiles.  Operands stream from global memory straight into
 // an NS-stage LDS ring with global_load_lds (16 bytes per lane, placed
 // lane-major), so no registers stage them and NS-1 stages are in flight while
@@ -355,16 +355,25 @@ __device__ __forceinline__ void dma4s(uint32_t lds, const void* base, uint32_t o
 __device__ __forceinline__ void dma4(uint32_t lds, const void* g) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
+// Wait until at most N vector-memory loads of this wave are in flight and all its LDS
+// reads are done, then meet the other waves.  The wait is a compiler builtin, so the
+// compiler's own wait-count bookkeeping knows that every earlier LDS read has completed;
+// the barrier is an opaque statement that no memory access moves across.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_sched_barrier(0);  // SMFMACs written after the barrier stay after it
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int SR, int ST, int KB, int NS>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN>
 struct Ring {
-    static constexpr int BR = 2 * SR * 32;             // weight rows per block
-    static constexpr int BT = 2 * ST * 32;             // tokens per block
+    static constexpr int NW = WRN * WTN;               // waves per block (WRN along rows, WTN along tokens)
+    static constexpr int BR = WRN * SR * 32;           // weight rows per block
+    static constexpr int BT = WTN * ST * 32;           // tokens per block
     static constexpr int KO = KB / (int)sizeof(T);     // original columns per stage (KB bytes of X per token)
     static constexpr int ND = KB / 64;                 // SMFMAC depths per stage
     static constexpr int AROW = KB / 2;                // compressed bytes per weight row per stage
@@ -373,13 +382,15 @@ struct Ring {
     static constexpr int I_OFF = BR * AROW;
     static constexpr int B_OFF = I_OFF + BR * AI * 4;
     static constexpr int STAGE = B_OFF + BT * KB;
-    static constexpr int NA = BR * AROW / 1024 / 4;    // A wave-instructions per wave
+    static constexpr int NA = BR * AROW / 1024 / NW;   // A wave-instructions per wave
     static constexpr bool I16 = AI >= 4;               // index rows loaded in 16-byte pieces (else dwords)
-    static constexpr int NI = BR * AI * 4 / (I16 ? 1024 : 256) / 4;
-    static constexpr int NB = BT * KB / 1024 / 4;      // X wave-instructions per wave
+    static constexpr int NI = BR * AI * 4 / (I16 ? 1024 : 256) / NW;
+    static constexpr int NB = BT * KB / 1024 / NW;     // X wave-instructions per wave
     static constexpr int PER = NA + NI + NB;           // loads per wave per stage
     static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
-    static_assert(NA >= 1 && NI >= 1 && NB >= 1, "tile too small for 4 waves");
+    static_assert(NA >= 1 && NI >= 1 && NB >= 1, "tile too small for its waves");
+    static_assert(BR * AROW % (1024 * NW) == 0 && BT * KB % (1024 * NW) == 0, "loads must split evenly over the waves");
+    static_assert(BR * AI * 4 % ((I16 ? 1024 : 256) * NW) == 0, "index loads must split evenly over the waves");
     static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
     // XOR swizzles of 16-byte chunks (16 consecutive rows of a fragment read hit distinct banks)
     __device__ static int swa(int r) { return AROW == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
@@ -394,14 +405,14 @@ struct RingFrag {          // fragments of one SMFMAC depth
 };
 
 // NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
-template <typename T, int SR, int ST, int KB, int NS, int OCC = 1>
-__global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
-    using RG = Ring<T, SR, ST, KB, NS>;
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int OCC = 1>
+__global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs a) {
+    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN>;
     using FR = RingFrag<SR, ST>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * RG::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave & 1, wt = wave >> 1;
+    const int wr = wave % WRN, wt = wave / WRN;
     int tr, tt;
     tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
     const int64_t r0 = (int64_t)tr * RG::BR, t0 = (int64_t)tt * RG::BT;
@@ -464,7 +475,9 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
         for (int i = 0; i < SR; ++i) {
             const int row = (wr * SR + i) * 32 + l32;
             f.a[i] = *(const i32x4_t*)(sA + row * RG::AROW + ((2 * d + h) ^ RG::swa(row)) * 16);
-            if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d] >> (16 * h);
+            // bf16: the lane's 16 index bits are selected (shifted by 16h) at the SMFMAC, so
+            // that no VALU op waits on this read ahead of unrelated SMFMACs
+            if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d];
             else f.iw[i] = sI[row * RG::AI + 2 * d + h];
         }
 #pragma unroll
@@ -483,6 +496,7 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < ST; ++j) acc[i][j] = AccV{};
 
+    const uint32_t ish = 16u * (uint32_t)h;
     auto mfmas = [&](const FR& f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SR; ++i)
@@ -491,7 +505,7 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
                 if constexpr (sizeof(T) == 2)
                     acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
                                                                          __builtin_bit_cast(bf16x16_t, f.b[j]),
-                                                                         acc[i][j], (int)f.iw[i], 0, 0);
+                                                                         acc[i][j], (int)(f.iw[i] >> ish), 0, 0);
                 else
                     acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[i], f.b[j], acc[i][j], (int)f.iw[i], 0, 0);
             }
@@ -510,7 +524,10 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
     if (nsteps >= NS) wait_vm_barrier<(NS - 1) * RG::PER>();
     else wait_vm_barrier<0>();
     if (nsteps > 0) read_depth(0, 0, fa);
-    for (int S = 0; S < nsteps; ++S) {
+    // One stage.  HasNext (all but the last stage) hands over to stage S+1 at its last
+    // depth; the last stage is peeled off so that the steady-state loop carries no
+    // branch around LDS reads, which keeps the compiler's wait counts exact.
+    auto stage = [&](int S, auto has_next) __attribute__((always_inline)) {
         const int slot = S % NS;
 #pragma unroll
         for (int d = 0; d < RG::ND; d += 2) {
@@ -518,7 +535,7 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
             mfmas(fa);
             if (d + 2 < RG::ND) {
                 read_depth(slot, d + 2, fa);
-            } else if (S + 1 < nsteps) {
+            } else if constexpr (decltype(has_next)::value) {
                 if (S + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * RG::PER>();
                 else wait_vm_barrier<0>();
                 read_depth((S + 1) % NS, 0, fa);
@@ -526,7 +543,10 @@ __global__ __launch_bounds__(256, OCC) void spmm_ring_kernel(SpmmArgs a) {
             }
             mfmas(fb);
         }
-    }
+    };
+    int S = 0;
+    for (; S + 1 < nsteps; ++S) stage(S, std::true_type{});
+    if (S < nsteps) stage(S, std::false_type{});
     wait_vm_all();
 
     // Epilogue.  Lane holds token column l32 and rows 8*(e/4) + 4*h + e%4 of
@@ -767,29 +787,32 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
-    bool large, ring, wide;
+    bool large, ring, big;
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
-// SR, ST, NS of the ring kernel
-// ring shapes: wide (256 x 256 tile, 3 stages of 128 B) and narrow (256 x 128 tile, 2 stages of 256 B)
-#define NM_RING_WIDE T, 4, 4, 128, 3
-#define NM_RING_NARROW T, 4, 2, 256, 2
+// Ring shapes (T, SR, ST, KB, NS, WRN, WTN):
+//   narrow: 256 x 128 tile, 4 waves (one per SIMD), 2 stages of 256 B of X per token
+//   big   : 256 x 256 tile, 8 waves (two per SIMD), 3 stages of 128 B; bf16 only (the int8
+//           index rows of a 128-byte stage do not split over 8 waves)
+#define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
+#define NM_RING_BIG uint16_t, 4, 2, 128, 3, 2, 4
 
 template <typename T, bool LIFT>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
     using G = Geo<T, LIFT>;
     SpmmPlan p{};
     p.large = Mtok > 128;
-    using RW = Ring<NM_RING_WIDE>;
+    using RB = Ring<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
-    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0 && (K % RW::KO) == 0;
-    // the wide tile moves 27% fewer bytes per MAC; use it when it still gives
-    // at least one full wave of tiles on 256 CUs
-    p.wide = p.ring && ceil_div(R, RW::BR) * ceil_div(Mtok, RW::BT) >= 256;
-    const int BR = p.ring ? (p.wide ? RW::BR : RN::BR) : 128;
-    const int BT = p.ring ? (p.wide ? RW::BT : RN::BT) : (p.large ? 128 : 32);
+    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0;
+    // the big tile moves a third fewer bytes per MAC than the narrow one but needs
+    // every LDS byte of a CU; with fewer than two rounds of its tiles on 256 CUs the
+    // narrow tile's finer grain balances better (measured on the 2048-token layers)
+    p.big = p.ring && sizeof(T) == 2 && (K % RB::KO) == 0 && ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
+    const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
+    const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
     p.tiles_t = (int)ceil_div(Mtok, BT);
     {
@@ -798,7 +821,7 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
         p.skinny = 0;
         if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
     }
-    p.nsteps = (int)ceil_div(K, p.ring ? (p.wide ? RW::KO : RN::KO) : G::KO);
+    p.nsteps = (int)ceil_div(K, p.ring ? (p.big ? RB::KO : RN::KO) : G::KO);
     const int64_t blocks = (int64_t)p.tiles_r * p.tiles_t;
     int KS = 1;
     if (!p.large && !p.skinny) {
@@ -857,8 +880,13 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
             hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
     } else if (p.ring) {
         if constexpr (!LIFT) {
-            if (p.wide) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_WIDE>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW>), grid, dim3(256), 0, s, a);
+            if constexpr (sizeof(T) == 2) {
+                if (p.big) {
+                    hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
+                    return check_launch("nm_spmm");
+                }
+            }
+            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW>), grid, dim3(256), 0, s, a);
         }
     } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);

@@ -52,6 +52,23 @@ SHAPES = [  # (tokens, R, K): small-token split-K path and large-tile paths (the
 ]
 
 
+@pytest.mark.parametrize("Mt,R,K", [(4096, 8192, 128), (4100, 8200, 192)])
+def test_spmm_big_tile_integer_exact_sampled(nm, Mt, R, K):
+    """Shapes with >= 512 tiles of 256 x 256 take the 8-wave ring kernel.  Integer-valued
+    inputs make every sum exact; outputs are compared on a random sample plus the whole
+    ragged last row and column of tiles."""
+    g = np.random.default_rng(Mt + R + K)
+    X = _int_bf16(g, (Mt, K), 8)
+    W = _int_bf16(g, (R, K), 8)
+    mask, vals, idx = _pack_case(W, 0, score=O.score(W, None, 0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32))
+    v, i = _to_dev(vals, idx)
+    Y = nm.nm_spmm(np_bf16(X).to(dev()), v, i, R=R, ydt=nm.NM_F32).cpu().numpy()
+    tm = np.concatenate([g.integers(0, Mt, 20000), np.repeat(np.arange(Mt - 260, Mt), 8), g.integers(0, Mt, 4096)])
+    ro = np.concatenate([g.integers(0, R, 20000), g.integers(0, R, 260 * 8), g.integers(R - 260, R, 4096)])
+    ref = O.masked_matmul_at(X, W, mask, tm, ro)
+    assert np.array_equal(Y[tm, ro].astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("Mt,R,K", SHAPES)
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns):
