@@ -79,71 +79,66 @@ __device__ __forceinline__ uint32_t mask_bits_at(const uint8_t* mask, int64_t ld
 }
 
 // ------------------------------------------------------------------ A1: colsumsq
-constexpr int kColRows = 32;  // rows per partial block
+// One launch, no workspace.  A block owns CG column groups of 16 bytes (64 bf16 or 32
+// fp32 columns) over all rows: lane (cg, rl) walks rows rl, rl + 32, ... with eight
+// 16-byte loads in flight, then the 32 row-lane partials of each column are summed in
+// row-lane order through LDS, so the result does not depend on scheduling.
+constexpr int kColCG = 8, kColRL = 32;
 
 template <typename T>
-__global__ __launch_bounds__(256) void colsumsq_partial_kernel(const T* __restrict__ X, int64_t n, int64_t K,
-                                                               int64_t ldx, float* __restrict__ part) {
-    constexpr int VEC = 16 / sizeof(T);
-    __shared__ float red[4][64 * VEC];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * 64 * VEC + lane * VEC;
-    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
-    const int64_t r1 = r0 + kColRows < n ? r0 + kColRows : n;
+__global__ __launch_bounds__(256) void colsumsq_kernel(const T* __restrict__ X, int64_t n, int64_t K, int64_t ldx,
+                                                       float* __restrict__ H) {
+    constexpr int VEC = 16 / sizeof(T), CG = kColCG, RL = kColRL, U = 8;
+    __shared__ float red[RL][CG * VEC + 1];
+    const int cg = threadIdx.x % CG, rl = threadIdx.x / CG;
+    const int64_t c0 = (int64_t)blockIdx.x * CG * VEC + cg * VEC;
     float acc[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    if (c0 < K) {
-        for (int64_t r = r0 + wave; r < r1; r += 4) {
-            const uint4 q = *(const uint4*)(X + r * ldx + c0);
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                float x;
-                if constexpr (sizeof(T) == 2) x = bf16_bits_to_f32((u[v >> 1] >> (16 * (v & 1))) & 0xffffu);
-                else x = __uint_as_float(u[v]);
-                acc[v] = __fadd_rn(acc[v], __fmul_rn(x, x));
-            }
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) red[wave][lane * VEC + v] = acc[v];
-    __syncthreads();
-    if (wave == 0 && c0 < K) {
+    auto add = [&](const uint4& q) __attribute__((always_inline)) {
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            const int c = lane * VEC + v;
-            float s = __fadd_rn(__fadd_rn(red[0][c], red[1][c]), __fadd_rn(red[2][c], red[3][c]));
-            part[(int64_t)blockIdx.y * K + c0 + v] = s;
+            float x;
+            if constexpr (sizeof(T) == 2) x = bf16_bits_to_f32((u[v >> 1] >> (16 * (v & 1))) & 0xffffu);
+            else x = __uint_as_float(u[v]);
+            acc[v] = __fadd_rn(acc[v], __fmul_rn(x, x));
+        }
+    };
+    if (c0 < K) {
+        int64_t r = rl;
+        for (; r + (U - 1) * RL < n; r += U * RL) {
+            uint4 q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) q[u] = *(const uint4*)(X + (r + u * RL) * ldx + c0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) add(q[u]);
+        }
+        for (; r < n; r += RL) add(*(const uint4*)(X + r * ldx + c0));
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[rl][cg * VEC + v] = acc[v];
+    __syncthreads();
+    if (threadIdx.x < CG * VEC) {
+        const int64_t col = (int64_t)blockIdx.x * CG * VEC + threadIdx.x;
+        if (col < K) {
+            float s = 0.f;
+            for (int i = 0; i < RL; ++i) s = __fadd_rn(s, red[i][threadIdx.x]);
+            H[col] = s;
         }
     }
 }
 
-__global__ void colsumsq_final_kernel(const float* __restrict__ part, int S, int64_t K, float* __restrict__ H) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= K) return;
-    float s = 0.f;
-    for (int i = 0; i < S; ++i) s = __fadd_rn(s, part[(int64_t)i * K + c]);
-    H[c] = s;
-}
+size_t colsumsq_ws(int64_t, int64_t) { return 0; }
 
-size_t colsumsq_ws(int64_t n, int64_t K) { return (size_t)ceil_div(n, kColRows) * (size_t)K * sizeof(float); }
-
-void launch_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx, float* H, void* ws,
-                     hipStream_t s) {
-    const int64_t S = ceil_div(n, kColRows);
-    float* part = (float*)ws;
-    if (n > 0) {
-        if (xdt == NM_BF16) {
-            dim3 g((unsigned)ceil_div(K, 64 * 8), (unsigned)S);
-            hipLaunchKernelGGL(colsumsq_partial_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, n, K, ldx,
-                               part);
-        } else {
-            dim3 g((unsigned)ceil_div(K, 64 * 4), (unsigned)S);
-            hipLaunchKernelGGL(colsumsq_partial_kernel<float>, g, dim3(256), 0, s, (const float*)X, n, K, ldx, part);
-        }
-    }
-    hipLaunchKernelGGL(colsumsq_final_kernel, dim3((unsigned)ceil_div(K, 256)), dim3(256), 0, s, part, (int)S, K, H);
+void launch_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx, float* H, void*, hipStream_t s) {
+    if (K == 0) return;
+    if (xdt == NM_BF16)
+        hipLaunchKernelGGL(colsumsq_kernel<uint16_t>, dim3((unsigned)ceil_div(K, kColCG * 8)), dim3(256), 0, s,
+                           (const uint16_t*)X, n, K, ldx, H);
+    else
+        hipLaunchKernelGGL(colsumsq_kernel<float>, dim3((unsigned)ceil_div(K, kColCG * 4)), dim3(256), 0, s,
+                           (const float*)X, n, K, ldx, H);
 }
 
 // ------------------------------------------------------------------ A3: score

@@ -656,11 +656,16 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
-    const int64_t r0 = (int64_t)blockIdx.x * (32 * SRk), t0 = (int64_t)blockIdx.y * (32 * STk);
+    // blockIdx.y splits the depths over blocks (partials then go to a.part); one block
+    // column always covers every token (32 * STk >= Mtok)
+    const int64_t r0 = (int64_t)blockIdx.x * (32 * SRk), t0 = 0;
+    const int split = blockIdx.y;
     const int64_t Kl = a.comp_bytes * 2 / es;     // lifted width
     const int D = (int)(Kl / KDEP);
-    const int per = (D + KSPLIT - 1) / KSPLIT;
-    const int d0 = wave * per, d1 = d0 + per < D ? d0 + per : D;
+    const int Db = (D + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int bd0 = split * Db < D ? split * Db : D, bd1 = bd0 + Db < D ? bd0 + Db : D;
+    const int per = (bd1 - bd0 + KSPLIT - 1) / KSPLIT;
+    const int d0 = bd0 + wave * per, d1 = d0 + per < bd1 ? d0 + per : bd1;
 
     const uint8_t* arow[SRk];
     const uint32_t* irow[SRk];
@@ -687,16 +692,18 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < STk; ++j) acc[i][j] = AccV{};
 
-    // U depths per batch: every load of a batch is issued before its first SMFMAC.  Full
-    // batches run branch-free; the short last batch (depth bounds are wave-uniform) takes a
-    // separate path so that the compiler does not sink the loads of full batches into branches.
-    auto batch = [&](int d, int n) __attribute__((always_inline)) {
-        i32x4_t fa[U][SRk];
-        uint32_t fi[U][SRk];
-        i32x8_t fb[U][STk];
+    // U depths per batch: every load of a batch is issued before its first SMFMAC.  Every
+    // batch has a compile-time depth count and runs branch-free (the depth bounds are
+    // wave-uniform), so the compiler neither sinks loads into branches nor issues loads
+    // for depths past the end.
+    auto batch = [&](int d, auto nb) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb)::value;   // depths in this batch (compile time)
+        i32x4_t fa[NB][SRk];
+        uint32_t fi[NB][SRk];
+        i32x8_t fb[NB][STk];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int dd = u < n ? d + u : d;
+        for (int u = 0; u < NB; ++u) {
+            const int dd = d + u;
 #pragma unroll
             for (int i = 0; i < SRk; ++i) {
                 fa[u][i] = *(const i32x4_t*)(arow[i] + (int64_t)dd * 32);
@@ -708,26 +715,31 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the SMFMACs
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u < n) {
+        for (int u = 0; u < NB; ++u)
 #pragma unroll
-                for (int i = 0; i < SRk; ++i)
+            for (int i = 0; i < SRk; ++i)
 #pragma unroll
-                    for (int j = 0; j < STk; ++j) {
-                        if constexpr (es == 2)
-                            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, fa[u][i]), __builtin_bit_cast(bf16x16_t, fb[u][j]),
-                                acc[i][j], (int)fi[u][i], 0, 0);
-                        else
-                            acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(fa[u][i], fb[u][j], acc[i][j],
-                                                                               (int)fi[u][i], 0, 0);
-                    }
-            }
-        }
+                for (int j = 0; j < STk; ++j) {
+                    if constexpr (es == 2)
+                        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, fa[u][i]), __builtin_bit_cast(bf16x16_t, fb[u][j]), acc[i][j],
+                            (int)fi[u][i], 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(fa[u][i], fb[u][j], acc[i][j],
+                                                                           (int)fi[u][i], 0, 0);
+                }
     };
+    // full batches of U, then the remainder as batches of U/2, U/4, ..., 1 (each branch-free)
     int d = d0;
-    for (; d + U <= d1; d += U) batch(d, U);
-    if (d < d1) batch(d, d1 - d);
+    for (; d + U <= d1; d += U) batch(d, std::integral_constant<int, U>{});
+    if constexpr (U > 8)
+        if (d + 8 <= d1) { batch(d, std::integral_constant<int, 8>{}); d += 8; }
+    if constexpr (U > 4)
+        if (d + 4 <= d1) { batch(d, std::integral_constant<int, 4>{}); d += 4; }
+    if constexpr (U > 2)
+        if (d + 2 <= d1) { batch(d, std::integral_constant<int, 2>{}); d += 2; }
+    if constexpr (U > 1)
+        if (d < d1) batch(d, std::integral_constant<int, 1>{});
 
     // fixed-order reduction of the KSPLIT partial tiles, one 32x32 sub-tile at a time
 #pragma unroll
@@ -744,7 +756,9 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                 using AccS = typename std::conditional<es == 2, float, int32_t>::type;
                 AccS v = 0;
                 for (int w = 0; w < KSPLIT; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
-                if (gt < a.Mtok && gr < a.R) {
+                if (a.part) {
+                    if (gt < a.Mtok && gr < a.R) ((AccS*)a.part)[((int64_t)split * a.Mtok + gt) * a.R + gr] = v;
+                } else if (gt < a.Mtok && gr < a.R) {
                     const int64_t o = gt * a.ldy + gr;
                     if (a.ydt == NM_I32) {
                         ((int32_t*)a.Y)[o] = (int32_t)v;
@@ -822,9 +836,18 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
         if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
     }
     p.nsteps = (int)ceil_div(K, p.ring ? (p.big ? RB::KO : RN::KO) : G::KO);
+    if (p.skinny) {
+        // K split over blocks (partials + a fixed-order reduce) where the row tiles alone
+        // leave the chip short of blocks; measured on the 4096- and 11008-row layers
+        p.KS = 1;
+        if (p.skinny == 1 && sizeof(T) == 2 && ceil_div(R, 32) <= 512) p.KS = 2;
+        if (p.skinny == 3 && ceil_div(R, 64) < 128) p.KS = 4;
+        p.steps_per_split = 0;
+        return p;
+    }
     const int64_t blocks = (int64_t)p.tiles_r * p.tiles_t;
     int KS = 1;
-    if (!p.large && !p.skinny) {
+    if (!p.large) {
         const int64_t target = 1024;
         while ((int64_t)KS * blocks < target && KS * 4 <= p.nsteps) KS *= 2;
     }
@@ -866,18 +889,15 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
     if (p.skinny == 1) {
         // 32-row tiles, 4 waves split K, 16 depths in flight per wave
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
     } else if (p.skinny == 2) {
         // two 32-row tiles per wave share each X fragment when that still leaves >= 200 blocks
         if (ceil_div(a.R, 64) >= 200)
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 4, 8>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 4, 8>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
     } else if (p.skinny == 3) {
-        if (ceil_div(a.R, 64) >= 128)
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), 1), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 32), 1), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
         if constexpr (!LIFT) {
             if constexpr (sizeof(T) == 2) {

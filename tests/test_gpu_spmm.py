@@ -45,9 +45,10 @@ def _to_dev(vals, idx):
     return v.to(dev()), torch.from_numpy(idx.view(np.int32)).to(dev())
 
 
-SHAPES = [  # (tokens, R, K): small-token split-K path and large-tile paths (the 256x256 ring tile needs
-    # at least 256 tiles), ragged edges
-    (1, 64, 256), (16, 100, 256), (37, 257, 128), (129, 130, 256), (300, 200, 192), (64, 96, 4096), (260, 160, 4096),
+SHAPES = [  # (tokens, R, K): few-token kernel (with and without a K split over blocks), many-token
+    # LDS-ring kernel, the register-staged kernel (K not a multiple of the ring stage), ragged edges
+    (1, 64, 256), (16, 100, 256), (37, 257, 128), (100, 300, 512), (129, 130, 256), (300, 200, 192), (64, 96, 4096),
+    (260, 160, 4096),
     (2048, 8192, 256), (2100, 8200, 256),
 ]
 
