@@ -315,80 +315,104 @@ void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
 }
 
 // ------------------------------------------------------------------ fused 2:4 fast path
-// Lane = 8 consecutive weights (two 4-groups); a quad of lanes = 32 weights =
-// one 32-bit index word, assembled across the quad with two xor-shuffles.
+// Lane = 8 consecutive weights (two 4-groups) of PR rows; a quad of lanes = 32 weights =
+// one 32-bit index word, assembled across the quad with two xor-shuffles.  Block
+// (256 lanes) = 2048 columns x PR rows: the PR rows' loads are all issued before any
+// selection, and the curvature H (one row, shared by all rows) is read once per lane.
 // The lane writes its 4 kept values (8 bytes) and its mask byte directly.
+constexpr int kPP24Rows = 4;
+
 template <typename TW, bool HESS, bool HFULL>
 __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict__ W, int64_t ldw,
                                                            const float* __restrict__ H, int64_t ldh, float eps,
                                                            int64_t R, int64_t K, uint8_t* __restrict__ mask,
                                                            int64_t ldm, uint16_t* __restrict__ vals, int64_t ldv,
-                                                           uint32_t* __restrict__ idx, int64_t ldi) {
-    const int64_t wpr = (K + 31) >> 5;
-    const int64_t total = R * wpr * 4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-        const int q = (int)(t & 3);
-        const int64_t wd = t >> 2;
-        const int64_t r = wd / wpr, wi = wd - r * wpr;
-        const int64_t k0 = (wi * 4 + q) * 8;
-        uint32_t nib = 0;
-        if (k0 < K) {
-            float w[8];
-            uint32_t wb[8];  // bf16 bit patterns of the values to store
-            if constexpr (sizeof(TW) == 2) {
-                const uint4 v = *(const uint4*)(W + r * ldw + k0);
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+                                                           uint32_t* __restrict__ idx, int64_t ldi, int64_t row_base) {
+    constexpr int PR = kPP24Rows;
+    const int q = threadIdx.x & 3;
+    const int64_t k0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
+    const bool col_ok = k0 < K;
+    uint32_t wb[PR][8];  // bf16 bit patterns of the values (the stored form)
+    float w[PR][8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    wb[i] = (u[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-                    w[i] = bf16_bits_to_f32(wb[i]);
-                }
-            } else {
-                const float4 a = *(const float4*)(W + r * ldw + k0);
-                const float4 c = *(const float4*)(W + r * ldw + k0 + 4);
-                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-                w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p < R ? r0 + p : R - 1;   // rows past the end re-read the last row, never stored
+        const int64_t kc = col_ok ? k0 : 0;
+        if constexpr (sizeof(TW) == 2) {
+            const uint4 v = *(const uint4*)(W + r * ldw + kc);
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) wb[i] = f32_to_bf16_bits(w[i]);
-            }
-            float key[8];
-            if constexpr (HESS) {
-                const float* hp = H + (HFULL ? r * ldh : 0) + k0;
+            for (int i = 0; i < 8; ++i) wb[p][i] = (u[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+        } else {
+            const float4 a = *(const float4*)(W + r * ldw + kc);
+            const float4 c = *(const float4*)(W + r * ldw + kc + 4);
+            w[p][0] = a.x; w[p][1] = a.y; w[p][2] = a.z; w[p][3] = a.w;
+            w[p][4] = c.x; w[p][5] = c.y; w[p][6] = c.z; w[p][7] = c.w;
+        }
+    }
+    float hsh[8];
+    if constexpr (HESS && !HFULL) {
+        const float* hp = H + (col_ok ? k0 : 0);
+        const float4 h0 = *(const float4*)hp;
+        const float4 h1 = *(const float4*)(hp + 4);
+        hsh[0] = h0.x; hsh[1] = h0.y; hsh[2] = h0.z; hsh[3] = h0.w;
+        hsh[4] = h1.x; hsh[5] = h1.y; hsh[6] = h1.z; hsh[7] = h1.w;
+    }
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (sizeof(TW) == 2) w[p][i] = bf16_bits_to_f32(wb[p][i]);
+            else wb[p][i] = f32_to_bf16_bits(w[p][i]);
+        }
+        float key[8];
+        if constexpr (HESS) {
+            float h[8];
+            if constexpr (HFULL) {
+                const float* hp = H + (r < R ? r : R - 1) * ldh + (col_ok ? k0 : 0);
                 const float4 h0 = *(const float4*)hp;
                 const float4 h1 = *(const float4*)(hp + 4);
-                const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) key[i] = rank_key(hess_score(w[i], h[i], eps));
+                h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+                h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) key[i] = rank_key(fabsf(w[i]));
+                for (int i = 0; i < 8; ++i) h[i] = hsh[i];
             }
-            uint32_t packed[2];
-            uint32_t mbyte = 0;
 #pragma unroll
-            for (int gi = 0; gi < 2; ++gi) {
-                const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
-                const uint32_t bits = topn_bits<4>(kk, 2);
-                const uint32_t p0 = __builtin_ctz(bits);
-                const uint32_t p1 = 31u - __builtin_clz(bits);
-                uint32_t v0 = 0, v1 = 0;
+            for (int i = 0; i < 8; ++i) key[i] = rank_key(hess_score(w[p][i], h[i], eps));
+        } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v0 = (p0 == (uint32_t)i) ? wb[4 * gi + i] : v0;
-                    v1 = (p1 == (uint32_t)i) ? wb[4 * gi + i] : v1;
-                }
-                packed[gi] = v0 | (v1 << 16);
-                mbyte |= bits << (4 * gi);
-                nib |= (p0 | (p1 << 2)) << (4 * gi);
+            for (int i = 0; i < 8; ++i) key[i] = rank_key(fabsf(w[p][i]));
+        }
+        uint32_t packed[2];
+        uint32_t mbyte = 0, nib = 0;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
+            const uint32_t bits = topn_bits<4>(kk, 2);
+            const uint32_t p0 = __builtin_ctz(bits);
+            const uint32_t p1 = 31u - __builtin_clz(bits);
+            uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v0 = (p0 == (uint32_t)i) ? wb[p][4 * gi + i] : v0;
+                v1 = (p1 == (uint32_t)i) ? wb[p][4 * gi + i] : v1;
             }
+            packed[gi] = v0 | (v1 << 16);
+            mbyte |= bits << (4 * gi);
+            nib |= (p0 | (p1 << 2)) << (4 * gi);
+        }
+        const bool ok = col_ok && r < R;
+        if (ok) {
             *(uint2*)(vals + r * ldv + (k0 >> 1)) = make_uint2(packed[0], packed[1]);
             if (mask) mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
         }
-        uint32_t v = nib << (8 * q);
+        uint32_t v = ok ? nib << (8 * q) : 0u;
         v |= (uint32_t)__shfl_xor((int)v, 1);
         v |= (uint32_t)__shfl_xor((int)v, 2);
-        if (q == 0) idx[r * ldi + wi] = v;
+        if (q == 0 && ok) idx[r * ldi + (k0 >> 5)] = v;
     }
 }
 
@@ -399,23 +423,26 @@ void launch_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float*
     const bool fast = (N == 2 && M == 4 && Wsc == Wv && sdt == wdt && ldsc == ldwv && vdt == NM_BF16 &&
                        (sdt == NM_BF16 || sdt == NM_F32) && (K % 8) == 0);
     if (fast) {
-        const int64_t total = R * ceil_div(K, 32) * 4;
-        if (total == 0) return;
-        const dim3 g(grid_cap(ceil_div(total, 256), 16384)), b(256);
+        if (R == 0 || K == 0) return;
         const bool hess = mode == NM_SCORE_HESSIAN, hfull = ldh != 0;
-#define NM_PP24(TW, HS, HF)                                                                                         \
-    hipLaunchKernelGGL((prune_pack24_kernel<TW, HS, HF>), g, b, 0, s, (const TW*)Wv, ldwv, H, ldh, eps, R, K, mask, \
-                       ldm, (uint16_t*)vals, ldv, idx, ldi)
-        if (sdt == NM_BF16) {
-            if (!hess) NM_PP24(uint16_t, false, false);
-            else if (hfull) NM_PP24(uint16_t, true, true);
-            else NM_PP24(uint16_t, true, false);
-        } else {
-            if (!hess) NM_PP24(float, false, false);
-            else if (hfull) NM_PP24(float, true, true);
-            else NM_PP24(float, true, false);
-        }
+        constexpr int64_t kRowsPerLaunch = 65535LL * kPP24Rows;  // grid.y limit
+        for (int64_t rb = 0; rb < R; rb += kRowsPerLaunch) {
+            const int64_t nr = R - rb < kRowsPerLaunch ? R - rb : kRowsPerLaunch;
+            const dim3 g((unsigned)ceil_div(K, 256 * 8), (unsigned)ceil_div(nr, kPP24Rows)), b(256);
+#define NM_PP24(TW, HS, HF)                                                                                    \
+    hipLaunchKernelGGL((prune_pack24_kernel<TW, HS, HF>), g, b, 0, s, (const TW*)Wv, ldwv, H, ldh, eps, R, K, \
+                       mask, ldm, (uint16_t*)vals, ldv, idx, ldi, rb)
+            if (sdt == NM_BF16) {
+                if (!hess) NM_PP24(uint16_t, false, false);
+                else if (hfull) NM_PP24(uint16_t, true, true);
+                else NM_PP24(uint16_t, true, false);
+            } else {
+                if (!hess) NM_PP24(float, false, false);
+                else if (hfull) NM_PP24(float, true, true);
+                else NM_PP24(float, true, false);
+            }
 #undef NM_PP24
+        }
         return;
     }
     const int G = pack_chunk_groups(N, M);
