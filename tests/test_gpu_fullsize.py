@@ -1,0 +1,184 @@
+"""Parity at the full workload sizes, in the launch configurations the benchmark
+times: every stage runs on the GPU at its real shape through the C ABI, and the
+oracle checks a sample of rows of each output (masks, packs and indices bit for
+bit; bf16 products to 2e-2 * ||x|| * ||w_hat|| and the float-accumulation bound;
+int8 products exactly).  Each stage is fed the GPU's own output of the previous
+stage, so a failure names the stage.
+
+Workloads (seeded synthetic inputs):
+  llama24  : 2:4 bf16, W 4096x4096 and 11008x4096 (1% outlier columns), H from
+             X_cal 512x4096, Hessian score, SpMM at M in {1, 16, 128, 2048}
+  slide68  : 6:8 by |W| on W 14336x4096 bf16, sliding-window decomposition
+             (exact reconstruction), lifted SpMM at M in {1, 64, 512, 4096}
+  ternary68: W 6912x2560 ternary under a 6:8 mask from the latent |W_fp|,
+             int8 activations with per-token scales, M in {1, 256, 2048}
+  hessian24: W 28672x8192 bf16, Hutchinson diagonal (8 probes) from X 1024x8192,
+             z-scored sigmoid gate annealed to a 2:4 hard mask, SpMM at M = 8192
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests._util import bf16_np, dev, host, row_norms, u32_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nm():
+    import semi_structured_sparsity_amd as m
+    return m
+
+
+def _rows(g, R, n=48):
+    return np.unique(np.r_[0, 1, R - 2, R - 1, g.integers(0, R, n)])
+
+
+def _check_bf16_product(Y16, Y32, X, Wrows, mask_rows, rows, Ns=0):
+    """Y16/Y32: GPU outputs [M, R] (bf16 and f32) on their sampled columns `rows`."""
+    K = X.shape[1]
+    ref = O.masked_matmul(X, Wrows, mask_rows)                         # [M, rows] fp64
+    Wm = np.where(O.mask_to_bool(mask_rows, K), O.bf16_to_f32(Wrows), 0)
+    xf = O.bf16_to_f32(X)
+    tol = 2e-2 * row_norms(xf)[:, None] * row_norms(Wm)[None, :]
+    y16 = Y16[:, rows].float().cpu().numpy().astype(np.float64)
+    y32 = Y32[:, rows].cpu().numpy().astype(np.float64)
+    assert (np.abs(y16 - ref) <= tol).all()
+    absdot = np.abs(xf).astype(np.float64) @ np.abs(Wm).astype(np.float64).T
+    kterms = K if not Ns else K // 8 * 12                                # products summed per output
+    assert (np.abs(y32 - ref) <= 1.01 * kterms * 2.0 ** -24 * absdot + 1e-30).all()
+    assert torch.equal(Y16[:, rows].cpu(), torch.from_numpy(y32.astype(np.float32)).to(torch.bfloat16))
+
+
+# ------------------------------------------------------------------ llama24
+def test_llama24_full_size(nm):
+    g = np.random.default_rng(101)
+    K, eps = 4096, 1e-6
+    Xcal = synth.llama24_calib(512, K)
+    H = nm.nm_hdiag_colsumsq(Xcal.to(dev()))
+    Hh = H.cpu().numpy()
+    ref = O.colsumsq(host(Xcal))
+    n = 512
+    assert (np.abs(Hh.astype(np.float64) - ref) <= n * 2.0 ** -24 / (1 - n * 2.0 ** -24) * ref + 1e-30).all()
+    for name, R, tid in (("W_a", 4096, 0), ("W_b", 11008, 1)):
+        W = synth.llama24_weight(R, K, tensor_id=tid)
+        Wd = W.to(dev())
+        vals, idx, mask = nm.nm_prune_pack(Wd, H, eps, nm.NM_SCORE_HESSIAN, 2, 4)
+        rows = _rows(g, R)
+        Wr = host(W)[rows]
+        m_ref = O.topn_mask(O.score(Wr, Hh, eps), 2, 4)
+        v_ref, i_ref = O.pack(Wr, m_ref, 2, 4)
+        assert np.array_equal(mask.cpu().numpy()[rows], m_ref), name
+        assert np.array_equal(bf16_np(vals)[rows], v_ref), name
+        assert np.array_equal(u32_np(idx)[rows], i_ref), name
+        for M in (1, 16, 128, 2048):
+            X = synth.activations_bf16(1, M, K)
+            Xd = X.to(dev())
+            Y16 = nm.nm_spmm(Xd, vals, idx, R=R)
+            Y32 = nm.nm_spmm(Xd, vals, idx, R=R, ydt=nm.NM_F32)
+            _check_bf16_product(Y16, Y32, host(X), Wr, m_ref, rows)
+
+
+# ------------------------------------------------------------------ slide68
+def test_slide68_full_size(nm):
+    g = np.random.default_rng(202)
+    R, K, Ns = 14336, 4096, 4
+    W = synth.slide68_weight(R, K)
+    Wd = W.to(dev())
+    vals, idx, mask = nm.nm_prune_slide(Wd, None, 0.0, nm.NM_SCORE_MAGNITUDE, Ns)
+    rows = _rows(g, R)
+    Wr = host(W)[rows]
+    m_ref = O.topn_mask(O.score(Wr, None, 0.0, O.SCORE_MAGNITUDE), 6, 8)
+    v_ref, i_ref, bad = O.slide_decompose(Wr, m_ref, Ns)
+    assert bad == 0
+    vg, ig = bf16_np(vals)[rows], u32_np(idx)[rows]
+    assert np.array_equal(mask.cpu().numpy()[rows], m_ref)
+    assert np.array_equal(vg, v_ref) and np.array_equal(ig, i_ref)
+    # the overlapping 2:4 windows reconstruct the 6:8-pruned weight exactly
+    rec = O.slide_fold(vg, ig, K, Ns)
+    assert np.array_equal(rec, np.where(O.mask_to_bool(m_ref, K), O.bf16_to_f32(Wr).astype(np.float64), 0.0))
+    for M in (1, 64, 512, 4096):
+        X = synth.activations_bf16(2, M, K)
+        Xd = X.to(dev())
+        Y16 = nm.nm_spmm(Xd, vals, idx, R=R, Ns=Ns)
+        Y32 = nm.nm_spmm(Xd, vals, idx, R=R, Ns=Ns, ydt=nm.NM_F32)
+        _check_bf16_product(Y16, Y32, host(X), Wr, m_ref, rows, Ns=Ns)
+
+
+# ------------------------------------------------------------------ ternary68
+def test_ternary68_full_size(nm):
+    g = np.random.default_rng(303)
+    R, K, Ns = 6912, 2560, 4
+    Wf, Wt = synth.ternary68_weights(R, K)
+    Wfd, Wtd = Wf.to(dev()), Wt.to(dev())
+    vals, idx, mask = nm.nm_prune_slide(Wfd, None, 0.0, nm.NM_SCORE_MAGNITUDE, Ns, Wv=Wtd, vdt=nm.NM_I8)
+    alpha = nm.nm_absmean(Wfd)
+    a_ref = O.absmean(host(Wf))
+    assert abs(float(alpha.cpu()) - np.float32(a_ref)) <= 1e-6 * a_ref
+    rows = _rows(g, R)
+    m_ref = O.topn_mask(O.score(host(Wf)[rows], None, 0.0, O.SCORE_MAGNITUDE), 6, 8)
+    Wtr = Wt.numpy()[rows]
+    v_ref, i_ref, bad = O.slide_decompose(Wtr, m_ref, Ns)
+    assert bad == 0
+    assert np.array_equal(mask.cpu().numpy()[rows], m_ref)
+    assert np.array_equal(vals.cpu().numpy()[rows], v_ref) and np.array_equal(u32_np(idx)[rows], i_ref)
+    a = float(alpha.cpu())
+    for M in (1, 256, 2048):
+        Xq, sx = synth.ternary68_activations(M, K)
+        Xd, sxd = Xq.to(dev()), sx.to(dev())
+        acc = nm.nm_spmm(Xd, vals, idx, R=R, Ns=Ns, ydt=nm.NM_I32)
+        y = nm.nm_spmm(Xd, vals, idx, R=R, Ns=Ns, x_scale=sxd, w_scale=a, ydt=nm.NM_F32)
+        acc_ref, y_ref = O.masked_matmul_i8(Xq.numpy(), Wtr, m_ref, sx.numpy(), a)
+        assert np.array_equal(acc.cpu().numpy()[:, rows], acc_ref)
+        assert np.array_equal(y.cpu().numpy()[:, rows], y_ref)
+
+
+# ------------------------------------------------------------------ hessian24
+def test_hessian24_full_size(nm):
+    g = np.random.default_rng(404)
+    R, K, n, P = 28672, 8192, 1024, synth.HESSIAN24_PROBES
+    seed, eps = synth.HESSIAN24_SEED, synth.HESSIAN24_EPS
+    X = synth.hessian24_calib(n, K)
+    W = synth.hessian24_weight(R, K)
+    Xd, Wd = X.to(dev()), W.to(dev())
+    D = nm.nm_hdiag_hutchinson(Xd, R, P, seed)
+    rows = _rows(g, R, n=12)
+    Dr = D[torch.from_numpy(rows).to(dev())].cpu().numpy()
+    # Hutchinson rows against the oracle's double-precision estimate
+    Xh = host(X)
+    ref = O.hutchinson_rows(Xh, P, seed, rows)
+    U = O.hutchinson_u_rows(Xh, P, seed, rows)
+    xk = np.sqrt((O.bf16_to_f32(Xh).astype(np.float64) ** 2).sum(0))
+    tol = 2e-2 * (2.0 / P) * np.sqrt((U ** 2).sum(-1)).sum(1)[:, None] * xk[None, :]
+    assert (np.abs(Dr.astype(np.float64) - ref) <= tol).all()
+    # score with the full per-weight curvature
+    S = nm.nm_score(Wd, D, eps)
+    Wr = host(W)[rows]
+    Sr = O.score(Wr, Dr, eps)
+    assert np.array_equal(S[torch.from_numpy(rows).to(dev())].cpu().numpy(), Sr)
+    del D
+    # per-tensor statistics of S, then the gate fed those statistics
+    st = nm.nm_score_stats(S).cpu().numpy()
+    Sh = S.cpu().numpy()
+    mu, sg = O.stats(Sh)
+    assert abs(st[0] - mu) <= 1e-12 * abs(mu) and abs(st[1] - sg) <= 1e-12 * sg
+    del Sh
+    stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
+    _, hm, _ = nm.nm_gate(S, stats, 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS,
+                          want_m=False)
+    _, h_ref, _ = O.gate_anneal(Sr, mu, sg, 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS)
+    hmh = hm.cpu().numpy()
+    assert np.array_equal(hmh[rows], h_ref)
+    del S
+    # the annealed hard mask is 2:4: pack it and multiply at M = 8192
+    vals, idx = nm.nm_pack(Wd, hm, 2, 4)
+    v_ref, i_ref = O.pack(Wr, h_ref, 2, 4)
+    assert np.array_equal(bf16_np(vals)[rows], v_ref) and np.array_equal(u32_np(idx)[rows], i_ref)
+    M = 8192
+    Xs = synth.activations_bf16(4, M, K)
+    Xsd = Xs.to(dev())
+    Y16 = nm.nm_spmm(Xsd, vals, idx, R=R)
+    Y32 = nm.nm_spmm(Xsd, vals, idx, R=R, ydt=nm.NM_F32)
+    _check_bf16_product(Y16, Y32, host(Xs), Wr, h_ref, rows)
