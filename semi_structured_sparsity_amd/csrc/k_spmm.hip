@@ -747,6 +747,8 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < STk; ++j) {
             __syncthreads();
+            // one vector store of the whole accumulator (storing its 16 elements one by one
+            // through bit casts was compiled into four copies of the first 16 bytes)
             *(AccV*)&red[(wave * 64 + lane) * 16] = acc[i][j];
             __syncthreads();
             for (int q = tid; q < 1024; q += KSPLIT * 64) {
