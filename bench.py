@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements on the other workloads")
     p.add_argument("--eager", action="store_true",
                    help="time the step as individual launches instead of one HIP-graph replay")
     p.add_argument("--pmc-pass", action="store_true",
@@ -176,6 +177,166 @@ def cpu_baseline(target_s: float):
                        f"and the masked matmul at M=1,16,128,2048), {t:.1f} s")
 
 
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+
+
+def measure_rows(nm, torch, synth, dev, reps: int = 5):
+    """Every hot-path row at the full size of each workload: kernel time from HIP events
+    around the raw C call (median of `reps`, each after a 1 GiB write that evicts L2 and
+    the Infinity Cache), with its algorithmic bytes or flops and the roofline fraction."""
+    r = nm.raw
+    bf, f32, i8, i32, u8 = torch.bfloat16, torch.float32, torch.int8, torch.int32, torch.uint8
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    flush = torch.empty(1 << 30, dtype=u8, device=dev)
+    out = []
+
+    def chk(st):
+        if st != 0:
+            raise nm.NMError(st, nm.last_error())
+
+    def timed(f):
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    def row(cfg, rowid, name, f, bound, work):
+        t = timed(f)
+        e = dict(config=cfg, row=rowid, name=name, us=round(t * 1e6, 2), bound=bound)
+        if bound == "hbm":
+            e["GBps"] = round(work / t / 1e9, 1)
+            e["frac"] = round(e["GBps"] / HBM_PEAK_GBPS, 4)
+        elif bound == "mfma":
+            e["TFLOPs"] = round(work / t / 1e12, 2)
+            e["frac"] = round(e["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+        elif bound == "mfma_i8":
+            e["TOPs"] = round(work / t / 1e12, 2)
+            e["frac"] = round(e["TOPs"] / INT8_PEAK_TOPS, 4)
+        else:  # launch-latency bound: absolute time only
+            e["GBps"] = round(work / t / 1e9, 3)
+        out.append(e)
+
+    def ws_for(n):
+        return torch.empty(max(int(n), 1), dtype=u8, device=dev)
+
+    def spmm(X, xdt, M, K, vals, vdt, idx, R, Ns, Y, ydt, xs=None, a=1.0, ws=None):
+        Kl = K // 8 * 12 if Ns else K
+        return lambda: chk(r.nm_spmm(X.data_ptr(), xdt, M, K, K, vals.data_ptr(), vdt, idx.data_ptr(), R, Kl // 2,
+                                     Kl // 32, Ns, None if xs is None else xs.data_ptr(), a, Y.data_ptr(), ydt, R,
+                                     None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), sh))
+
+    # ---- tiny24: fused Hessian score / top-2 of 4 / pack from fp32 W, SpMM at M = 16 (launch-latency bound)
+    W, H, X = synth.tiny24_inputs()
+    W, H, X = W.to(dev), H.to(dev), X.to(dev)
+    R, K = W.shape
+    vals, idx, mask = (torch.empty((R, K // 2), dtype=bf, device=dev), torch.empty((R, K // 32), dtype=i32, device=dev),
+                       torch.empty((R, K // 8), dtype=u8, device=dev))
+    row("tiny24", "A3+A7+A8", "prune_pack 256x256 (f32 -> bf16)", lambda: chk(r.nm_prune_pack(
+        W.data_ptr(), nm.NM_F32, K, H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN, W.data_ptr(), nm.NM_F32, K, R, K, 2, 4,
+        mask.data_ptr(), K // 8, nm.NM_BF16, vals.data_ptr(), K // 2, idx.data_ptr(), K // 32, sh)), "latency",
+        R * K * 5.25)
+    Y = torch.empty((16, R), dtype=bf, device=dev)
+    ws = ws_for(r.nm_spmm_workspace(16, K, R, 0, nm.NM_BF16))
+    row("tiny24", "A12", "spmm 256x256 M=16", spmm(X, nm.NM_BF16, 16, K, vals, nm.NM_BF16, idx, R, 0, Y, nm.NM_BF16, ws=ws),
+        "latency", R * K * 1.125 + 16 * K * 2 + 16 * R * 2)
+
+    # ---- slide68: 6:8 by |W| + sliding-window decomposition; lifted SpMM
+    R, K, Ns = 14336, 4096, 4
+    Kl = K // 8 * 12
+    W = synth.slide68_weight(R, K).to(dev)
+    vals, idx, mask = (torch.empty((R, Kl // 2), dtype=bf, device=dev), torch.empty((R, Kl // 32), dtype=i32, device=dev),
+                       torch.empty((R, K // 8), dtype=u8, device=dev))
+    row("slide68", "A3+A7+A9", "prune_slide 14336x4096 (6:8 -> 3 windows)", lambda: chk(r.nm_prune_slide(
+        W.data_ptr(), nm.NM_BF16, K, None, 0, 0.0, nm.NM_SCORE_MAGNITUDE, W.data_ptr(), nm.NM_BF16, K, R, K, Ns,
+        mask.data_ptr(), K // 8, nm.NM_BF16, vals.data_ptr(), Kl // 2, idx.data_ptr(), Kl // 32, sh)), "hbm",
+        R * K * (2 + 1.5 + 0.1875 + 0.125))
+    for M in (1, 64, 512, 4096):
+        X = synth.activations_bf16(2, M, K).to(dev)
+        Y = torch.empty((M, R), dtype=bf, device=dev)
+        ws = ws_for(r.nm_spmm_workspace(M, K, R, Ns, nm.NM_BF16))
+        f = spmm(X, nm.NM_BF16, M, K, vals, nm.NM_BF16, idx, R, Ns, Y, nm.NM_BF16, ws=ws)
+        if M <= 64:
+            row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "hbm", R * K * 1.6875 + M * K * 2 + M * R * 2)
+        else:
+            row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "mfma", 2 * M * R * Kl // 2)
+    del W, vals, idx, mask
+
+    # ---- ternary68: 6:8 mask from |W_fp| on the ternary code, alpha = mean|W_fp|, int8 SpMM
+    R, K, Ns = 6912, 2560, 4
+    Kl = K // 8 * 12
+    Wf, Wt = synth.ternary68_weights(R, K)
+    Wf, Wt = Wf.to(dev), Wt.to(dev)
+    vals, idx, mask = (torch.empty((R, Kl // 2), dtype=i8, device=dev), torch.empty((R, Kl // 32), dtype=i32, device=dev),
+                       torch.empty((R, K // 8), dtype=u8, device=dev))
+    row("ternary68", "A3+A7+A9+A10", "prune_slide 6912x2560 (|W_fp| mask on W_t)", lambda: chk(r.nm_prune_slide(
+        Wf.data_ptr(), nm.NM_BF16, K, None, 0, 0.0, nm.NM_SCORE_MAGNITUDE, Wt.data_ptr(), nm.NM_I8, K, R, K, Ns,
+        mask.data_ptr(), K // 8, nm.NM_I8, vals.data_ptr(), Kl // 2, idx.data_ptr(), Kl // 32, sh)), "hbm",
+        R * K * (2 + 1 + 0.75 + 0.1875 + 0.125))
+    alpha = torch.empty(1, dtype=f32, device=dev)
+    wsa = ws_for(r.nm_stats_workspace(R, K))
+    row("ternary68", "A10", "absmean 6912x2560", lambda: chk(r.nm_absmean(
+        Wf.data_ptr(), nm.NM_BF16, R, K, K, alpha.data_ptr(), wsa.data_ptr(), wsa.numel(), sh)), "hbm", R * K * 2)
+    a = float(alpha.cpu())
+    for M in (1, 256, 2048):
+        Xq, sx = synth.ternary68_activations(M, K)
+        Xq, sx = Xq.to(dev), sx.to(dev)
+        Y = torch.empty((M, R), dtype=f32, device=dev)
+        ws = ws_for(r.nm_spmm_workspace(M, K, R, Ns, nm.NM_I8))
+        f = spmm(Xq, nm.NM_I8, M, K, vals, nm.NM_I8, idx, R, Ns, Y, nm.NM_F32, xs=sx, a=a, ws=ws)
+        if M <= 256:
+            row("ternary68", "A11+A13", f"spmm int8 lifted 6912x2560 M={M}", f, "hbm",
+                R * K * (0.75 + 0.09375) + M * K + 4 * M + 4 * M * R)
+        else:
+            row("ternary68", "A11+A13", f"spmm int8 lifted 6912x2560 M={M}", f, "mfma_i8", 2 * M * R * Kl // 2)
+    del Wf, Wt, vals, idx, mask
+
+    # ---- hessian24: Hutchinson diagonal, score, z-score statistics, gate/anneal, pack, SpMM M = 8192
+    R, K, n, P = 28672, 8192, 1024, synth.HESSIAN24_PROBES
+    Xc = synth.hessian24_calib(n, K).to(dev)
+    W = synth.hessian24_weight(R, K).to(dev)
+    D = torch.empty((R, K), dtype=f32, device=dev)
+    wsh = ws_for(r.nm_hutchinson_workspace(n, K, R, P))
+    row("hessian24", "A2", "hutchinson 28672x8192, 8 probes, X 1024x8192", lambda: chk(r.nm_hdiag_hutchinson(
+        Xc.data_ptr(), n, K, K, R, P, synth.HESSIAN24_SEED, D.data_ptr(), K, wsh.data_ptr(), wsh.numel(), sh)),
+        "mfma", 2 * P * 2 * R * K * n)
+    del wsh
+    S = torch.empty((R, K), dtype=f32, device=dev)
+    row("hessian24", "A3", "score (H+eps) W^2, per-weight H", lambda: chk(r.nm_score(
+        W.data_ptr(), nm.NM_BF16, R, K, K, D.data_ptr(), K, synth.HESSIAN24_EPS, nm.NM_SCORE_HESSIAN, S.data_ptr(), K,
+        sh)), "hbm", R * K * 10)
+    del D
+    st = torch.empty(2, dtype=torch.float64, device=dev)
+    wss = ws_for(r.nm_stats_workspace(R, K))
+    row("hessian24", "A4", "score mean/std (f64)", lambda: chk(r.nm_score_stats(
+        S.data_ptr(), R, K, K, st.data_ptr(), wss.data_ptr(), wss.numel(), sh)), "hbm", R * K * 4)
+    hm = torch.empty((R, K // 8), dtype=u8, device=dev)
+    steps = synth.HESSIAN24_STEPS
+    lm = torch.empty(steps, dtype=torch.float64, device=dev)
+    wsg = ws_for(r.nm_gate_workspace(R, K, steps))
+    row("hessian24", "A5+A6+A7", "gate/anneal -> 2:4 hard mask", lambda: chk(r.nm_gate(
+        S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps, None, K,
+        hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "hbm", R * K * 4.125)
+    del S
+    vals, idx = torch.empty((R, K // 2), dtype=bf, device=dev), torch.empty((R, K // 32), dtype=i32, device=dev)
+    row("hessian24", "A8", "pack 28672x8192 from the hard mask", lambda: chk(r.nm_pack(
+        W.data_ptr(), nm.NM_BF16, R, K, K, hm.data_ptr(), K // 8, 2, 4, nm.NM_BF16, vals.data_ptr(), K // 2,
+        idx.data_ptr(), K // 32, sh)), "hbm", R * K * 3.25)
+    M = 8192
+    X = synth.activations_bf16(4, M, K).to(dev)
+    Y = torch.empty((M, R), dtype=bf, device=dev)
+    ws = ws_for(r.nm_spmm_workspace(M, K, R, 0, nm.NM_BF16))
+    row("hessian24", "A12", "spmm 28672x8192 M=8192", spmm(X, nm.NM_BF16, M, K, vals, nm.NM_BF16, idx, R, 0, Y,
+                                                            nm.NM_BF16, ws=ws), "mfma", 2 * M * R * K // 2)
+    return out
+
+
 def traffic_for(kernel_file: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
     source has not changed since they were taken."""
@@ -294,6 +455,7 @@ def main():
     mp_us = sum(k["us"] for k in maskpack)
     spmm_us = sum(k["us"] for k in kernels if k["name"].startswith("spmm"))
 
+    rows = None if args.no_rows else measure_rows(nm, torch, synth, dev)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     line = {
         "metric": "N:M SpMM effective TFLOP/s + mask/pack GB/s, as % of MI355X roofline",
@@ -318,6 +480,7 @@ def main():
         "timing": "eager launches" if args.eager else "HIP graph replay of the whole step (checked equal to eager)",
         "roofline": roof,
         "kernels": kernels,
+        "rows": rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -111,20 +111,23 @@ nm_status nm_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ld
 
 /* Per-tensor standardisation statistics of a score matrix ("SparseForge",
  * Methodology 2: scores are standardised before the temperature sigmoid).
- * stats[0] = mean, stats[1] = population standard deviation, both f64, by a
- * fixed-order two-pass reduction in f64.  ws: nm_stats_workspace(R, K) bytes. */
+ * stats[0] = mean, stats[1] = population standard deviation, both f64, from one
+ * pass: per-thread shifted sums turned into (count, mean, squared deviations),
+ * combined pairwise in a fixed order (run-to-run identical; equal to a two-pass
+ * f64 evaluation to about 1e-15 relative).  ws: nm_stats_workspace(R, K) bytes. */
 size_t nm_stats_workspace(int64_t R, int64_t K);
 nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats,
                          void* ws, size_t ws_bytes, nm_stream_t stream);
 
 /* Soft gate and annealing to a hard N:M mask ("SparseForge", Methodology 2
  * and 3).  With z = (s - mean)/std (z = 0 when std == 0), for t = 0..steps-1:
- *   T_t = T0 * rho^t,  beta_t = t/(steps-1),  g_t = sigmoid(z / T_t),
+ *   T_t = T0 * rho^t,  beta_t = t/(steps-1),  g_t = sigmoid(z / T_t)
+ *   (f32, hardware 2^x and reciprocal: about 1e-7 relative),
  *   m_t = (1 - beta_t) g_t + beta_t h,   h = top-N of s per group,
  *   lmid[t] = sum m_t (1 - m_t)   (f64, fixed-order reduction).
  * The final projection keeps the top-N of m_{steps-1} per group -> hard_mask.
  * m_final (nullable): m_{steps-1} as f32 [R, K] (ldf).  stats: device [2] from
- * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0, steps >= 1.
+ * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0, 1 <= steps <= 64.
  * ws: nm_gate_workspace(R, K, steps) bytes. */
 size_t nm_gate_workspace(int64_t R, int64_t K, int steps);
 nm_status nm_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats,

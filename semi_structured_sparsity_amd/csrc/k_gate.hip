@@ -38,70 +38,206 @@ __device__ __forceinline__ float load_elem(const void* p, nm_dtype dt, int64_t i
     return (float)((const int32_t*)p)[i];
 }
 
-// kind 0: sum x; 1: sum (x - center[0])^2; 2: sum |x|
+// Moments of a thread's, a block's or the tensor's elements: count, mean, sum of
+// squared deviations.  Combined pairwise (Chan et al.'s update), always in the same
+// order, so the statistics are run-to-run identical.
+struct Moments {
+    double n, mean, m2;
+};
+__device__ __forceinline__ Moments moments_combine(Moments a, Moments b) {
+    if (a.n == 0.0) return b;
+    if (b.n == 0.0) return a;
+    const double n = a.n + b.n, d = b.mean - a.mean;
+    return Moments{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
+}
+
+// Elements of [R, K] (leading dim ld) are visited in units of VEC consecutive
+// elements of a row; thread u of the fixed grid takes units u, u + stride, ...,
+// UN units per round with all UN loads issued before any is used.  When VEC > 1
+// the caller guarantees K % VEC == 0, ld % VEC == 0 and 16-byte alignment.
+template <typename T, int VEC, typename F>
+__device__ __forceinline__ void for_units(const T* __restrict__ X, int64_t R, int64_t K, int64_t ld, F&& f) {
+    constexpr int UN = 4;
+    const int64_t upr = K / VEC, total = R * upr;
+    const int64_t stride = (int64_t)kRedBlocks * kRedThreads;
+    const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
+    if (u0 >= total) return;
+    int64_t r = u0 / upr, c = u0 - r * upr;
+    const int64_t dr = stride / upr, dc = stride - dr * upr;
+    auto step = [&]() __attribute__((always_inline)) {
+        r += dr;
+        c += dc;
+        if (c >= upr) {
+            c -= upr;
+            r += 1;
+        }
+    };
+    for (int64_t u = u0; u < total; u += UN * stride) {
+        float x[UN][VEC];
+#pragma unroll
+        for (int j = 0; j < UN; ++j) {
+            const bool ok = u + j * stride < total;
+            const int64_t rr = ok ? r : 0, cc = ok ? c : 0;
+            if constexpr (VEC == 1) {
+                x[j][0] = load_elem(X, sizeof(T) == 2 ? NM_BF16 : NM_F32, rr * ld + cc);
+            } else {
+                const uint4 q = *(const uint4*)(X + rr * ld + cc * VEC);
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    if constexpr (sizeof(T) == 2) x[j][v] = bf16_bits_to_f32((w[v >> 1] >> (16 * (v & 1))) & 0xffffu);
+                    else x[j][v] = __uint_as_float(w[v]);
+                }
+            }
+            step();
+        }
+#pragma unroll
+        for (int j = 0; j < UN; ++j)
+            if (u + j * stride < total) f(x[j]);
+    }
+}
+
+// Per-tensor mean and population standard deviation in one pass: each thread keeps
+// sums of (x - c) and (x - c)^2 about its first element c, turns them into moments,
+// and the moments are combined in a fixed tree per block.
+template <int VEC>
+__global__ __launch_bounds__(kRedThreads) void moments_partial_kernel(const float* __restrict__ S, int64_t R, int64_t K,
+                                                                      int64_t ld, double* __restrict__ part) {
+    __shared__ double sh[3][kRedThreads];
+    double n = 0.0, s1 = 0.0, s2 = 0.0, c = 0.0;
+    bool first = true;
+    for_units<float, VEC>(S, R, K, ld, [&](const float* x) {
+        if (first) {
+            c = (double)x[0];
+            first = false;
+        }
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const double d = (double)x[v] - c;
+            s1 += d;
+            s2 += d * d;
+        }
+        n += VEC;
+    });
+    Moments m{n, n > 0.0 ? c + s1 / n : 0.0, n > 0.0 ? s2 - s1 * (s1 / n) : 0.0};
+    if (m.m2 < 0.0) m.m2 = 0.0;
+    sh[0][threadIdx.x] = m.n;
+    sh[1][threadIdx.x] = m.mean;
+    sh[2][threadIdx.x] = m.m2;
+    __syncthreads();
+    for (int w = kRedThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            const Moments o = moments_combine(Moments{sh[0][threadIdx.x], sh[1][threadIdx.x], sh[2][threadIdx.x]},
+                                              Moments{sh[0][threadIdx.x + w], sh[1][threadIdx.x + w],
+                                                      sh[2][threadIdx.x + w]});
+            sh[0][threadIdx.x] = o.n;
+            sh[1][threadIdx.x] = o.mean;
+            sh[2][threadIdx.x] = o.m2;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < 3) part[threadIdx.x * kRedBlocks + blockIdx.x] = sh[threadIdx.x][0];
+}
+
+// One thread combines the block moments in block order.
+__global__ void moments_final_kernel(const double* __restrict__ part, double* __restrict__ stats) {
+    if (threadIdx.x != 0) return;
+    Moments m{0.0, 0.0, 0.0};
+    for (int i = 0; i < kRedBlocks; ++i)
+        m = moments_combine(m, Moments{part[i], part[kRedBlocks + i], part[2 * kRedBlocks + i]});
+    stats[0] = m.n > 0.0 ? m.mean : 0.0;
+    stats[1] = m.n > 0.0 ? sqrt(m.m2 / m.n) : 0.0;
+}
+
+// sum |x| (for the ternary scale), f64 per thread, fixed-order LDS tree per block
+template <typename T, int VEC>
+__global__ __launch_bounds__(kRedThreads) void abssum_partial_kernel(const T* __restrict__ X, int64_t R, int64_t K,
+                                                                     int64_t ld, double* __restrict__ part) {
+    __shared__ double sh[kRedThreads];
+    double acc = 0.0;
+    for_units<T, VEC>(X, R, K, ld, [&](const float* x) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc += fabs((double)x[v]);
+    });
+    const double s = block_sum(acc, sh);
+    if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
+// kind 2: sum |x| for any dtype, element by element (the general path)
 __global__ __launch_bounds__(kRedThreads) void reduce_partial_kernel(const void* __restrict__ X, nm_dtype dt,
-                                                                     int64_t R, int64_t K, int64_t ld, int kind,
-                                                                     const double* __restrict__ center,
+                                                                     int64_t R, int64_t K, int64_t ld,
                                                                      double* __restrict__ part) {
     __shared__ double sh[kRedThreads];
     const int64_t total = R * K;
-    const double c = (kind == 1) ? center[0] : 0.0;
     double acc = 0.0;
     for (int64_t t = (int64_t)blockIdx.x * kRedThreads + threadIdx.x; t < total; t += (int64_t)kRedBlocks * kRedThreads) {
         const int64_t r = t / K, k = t - r * K;
-        const double x = (double)load_elem(X, dt, r * ld + k);
-        if (kind == 0) acc += x;
-        else if (kind == 1) acc += (x - c) * (x - c);
-        else acc += fabs(x);
+        acc += fabs((double)load_elem(X, dt, r * ld + k));
     }
     const double s = block_sum(acc, sh);
     if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
 
-// out_kind 0: out_d[slot] = sum/n ; 1: out_d[slot] = sqrt(sum/n) ; 2: out_f[0] = (float)(sum/n)
+// out_f[0] = (float)(sum of the block partials, in block order, / n)
 __global__ __launch_bounds__(kRedThreads) void reduce_final_kernel(const double* __restrict__ part, int nparts,
-                                                                   int64_t n, int out_kind, double* out_d, int slot,
-                                                                   float* out_f) {
+                                                                   int64_t n, float* out_f) {
     __shared__ double sh[kRedThreads];
     double acc = 0.0;
     for (int i = threadIdx.x; i < nparts; i += kRedThreads) acc += part[i];
     const double s = block_sum(acc, sh);
-    if (threadIdx.x == 0) {
-        const double m = n > 0 ? s / (double)n : 0.0;
-        if (out_kind == 0) out_d[slot] = m;
-        else if (out_kind == 1) out_d[slot] = sqrt(m);
-        else out_f[0] = (float)m;
-    }
+    if (threadIdx.x == 0) out_f[0] = (float)(n > 0 ? s / (double)n : 0.0);
 }
 
-size_t reduce_ws(int64_t, int64_t) { return (size_t)kRedBlocks * sizeof(double); }
+size_t reduce_ws(int64_t, int64_t) { return (size_t)3 * kRedBlocks * sizeof(double); }
+
+static bool vec_ok(const void* p, int64_t K, int64_t ld, int vec) {
+    return (K % vec) == 0 && (ld % vec) == 0 && (((uintptr_t)p) & 15) == 0;
+}
 
 void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats, void* ws, hipStream_t s) {
     double* part = (double*)ws;
-    const int64_t n = R * K;
-    hipLaunchKernelGGL(reduce_partial_kernel, dim3(kRedBlocks), dim3(kRedThreads), 0, s, (const void*)S, NM_F32, R, K,
-                       lds, 0, (const double*)nullptr, part);
-    hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, kRedBlocks, n, 0,
-                       stats, 0, (float*)nullptr);
-    hipLaunchKernelGGL(reduce_partial_kernel, dim3(kRedBlocks), dim3(kRedThreads), 0, s, (const void*)S, NM_F32, R, K,
-                       lds, 1, (const double*)stats, part);
-    hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, kRedBlocks, n, 1,
-                       stats, 1, (float*)nullptr);
+    if (vec_ok(S, K, lds, 4))
+        hipLaunchKernelGGL(moments_partial_kernel<4>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
+    else
+        hipLaunchKernelGGL(moments_partial_kernel<1>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
+    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(64), 0, s, (const double*)part, stats);
 }
 
 void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
                     hipStream_t s) {
     double* part = (double*)ws;
-    hipLaunchKernelGGL(reduce_partial_kernel, dim3(kRedBlocks), dim3(kRedThreads), 0, s, W, wdt, R, K, ldw, 2,
-                       (const double*)nullptr, part);
+    const dim3 g(kRedBlocks), b(kRedThreads);
+    if (wdt == NM_BF16 && vec_ok(W, K, ldw, 8))
+        hipLaunchKernelGGL((abssum_partial_kernel<uint16_t, 8>), g, b, 0, s, (const uint16_t*)W, R, K, ldw, part);
+    else if (wdt == NM_F32 && vec_ok(W, K, ldw, 4))
+        hipLaunchKernelGGL((abssum_partial_kernel<float, 4>), g, b, 0, s, (const float*)W, R, K, ldw, part);
+    else
+        hipLaunchKernelGGL(reduce_partial_kernel, g, b, 0, s, W, wdt, R, K, ldw, part);
     hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, kRedBlocks, R * K,
-                       2, (double*)nullptr, 0, alpha);
+                       alpha);
 }
 
 // ------------------------------------------------------------------ gate / anneal
 // A thread owns one mask byte: 8 consecutive scores of a row (two 4-groups or
 // one 8-group).  For every step it forms the gate, the blend with the hard
 // target and the binary-preference term; the block sums that term per step.
+// SMAX bounds the step count at compile time so that the per-step sums live in
+// registers.  The gate uses the hardware 2^x and reciprocal (about 1 ulp each):
+// sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)).
+__device__ __forceinline__ uint32_t group_topn_bits(const float* key, int g0, int M, int N) {
+    uint32_t gb = 0;
+    for (int i = 0; i < M; ++i) {
+        int beaten = 0;
+        for (int j = 0; j < M; ++j) {
+            if (j == i) continue;
+            beaten += ((j < i) ? (key[g0 + j] >= key[g0 + i]) : (key[g0 + j] > key[g0 + i])) ? 1 : 0;
+        }
+        if (beaten < N) gb |= 1u << i;
+    }
+    return gb;
+}
+
+template <int SMAX>
 __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restrict__ S, int64_t R, int64_t K,
                                                            int64_t lds, const double* __restrict__ stats, int N, int M,
                                                            float T0, float rho, int steps, float* __restrict__ m_final,
@@ -109,72 +245,107 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
                                                            double* __restrict__ part) {
     __shared__ double sh[kRedThreads];
     const double mu = stats[0], sigma = stats[1];
+    const double inv_sigma = sigma > 0.0 ? 1.0 / sigma : 0.0;   // z = 0 when the scores are constant
     const int64_t bpr = (K + 7) / 8;
     const int64_t total = R * bpr;
-    double lm[kMaxSteps];
-    for (int t = 0; t < steps; ++t) lm[t] = 0.0;
-    for (int64_t u = (int64_t)blockIdx.x * kRedThreads + threadIdx.x; u < total; u += (int64_t)kRedBlocks * kRedThreads) {
-        const int64_t r = u / bpr, b = u - r * bpr;
+    float cs[SMAX], beta[SMAX];  // log2(e) / T_t and the blend factor of step t
+    double lm[SMAX];
+#pragma unroll
+    for (int t = 0; t < SMAX; ++t) {
+        const float T = T0 * powf(rho, (float)t);
+        cs[t] = 1.4426950408889634f / T;
+        beta[t] = steps > 1 ? (float)t / (float)(steps - 1) : 1.0f;
+        lm[t] = 0.0;
+    }
+    const bool vec = (lds % 4) == 0 && (((uintptr_t)S) & 15) == 0 && (m_final == nullptr || ((ldf % 4) == 0 &&
+                                                                          (((uintptr_t)m_final) & 15) == 0));
+    const int64_t stride = (int64_t)kRedBlocks * kRedThreads;
+    const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
+    int64_t r = u0 / bpr, b = u0 - r * bpr;                   // (row, byte) of unit u, advanced without division
+    const int64_t dr = stride / bpr, db = stride - dr * bpr;
+    for (int64_t u = u0; u < total; u += stride) {
         const int64_t k0 = b * 8;
         const int ne = (K - k0) < 8 ? (int)(K - k0) : 8;
         float s[8], z[8], key[8];
+        if (vec && ne == 8) {
+            const float4 v0 = *(const float4*)(S + r * lds + k0);
+            const float4 v1 = *(const float4*)(S + r * lds + k0 + 4);
+            s[0] = v0.x; s[1] = v0.y; s[2] = v0.z; s[3] = v0.w; s[4] = v1.x; s[5] = v1.y; s[6] = v1.z; s[7] = v1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = i < ne ? S[r * lds + k0 + i] : 0.f;
+        }
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
-            s[i] = i < ne ? S[r * lds + k0 + i] : 0.f;
-            z[i] = sigma > 0.0 ? (float)(((double)s[i] - mu) / sigma) : 0.f;
+            z[i] = sigma > 0.0 ? (float)(((double)s[i] - mu) * inv_sigma) : 0.f;
             key[i] = rank_key(s[i]);
         }
         // hard target h: top-N of the score per group
         uint32_t hbits = 0;
-        for (int g = 0; g * M < ne; ++g) {
-            float kk[8];
-            for (int i = 0; i < M; ++i) kk[i] = key[g * M + i];
-            uint32_t gb = 0;
-            for (int i = 0; i < M; ++i) {
-                int beaten = 0;
-                for (int j = 0; j < M; ++j) {
-                    if (j == i) continue;
-                    beaten += ((j < i) ? (kk[j] >= kk[i]) : (kk[j] > kk[i])) ? 1 : 0;
-                }
-                if (beaten < N) gb |= 1u << i;
-            }
-            hbits |= gb << (g * M);
+        if (M == 4 && ne == 8) {
+            const float k0v[4] = {key[0], key[1], key[2], key[3]}, k1v[4] = {key[4], key[5], key[6], key[7]};
+            hbits = topn_bits<4>(k0v, N) | (topn_bits<4>(k1v, N) << 4);
+        } else if (M == 8 && ne == 8) {
+            hbits = topn_bits<8>(key, N);
+        } else {
+            for (int g = 0; g * M < ne; ++g) hbits |= group_topn_bits(key, g * M, M, N) << (g * M);
         }
+        float hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = ((hbits >> i) & 1u) ? 1.0f : 0.0f;
         float m[8];
-        for (int t = 0; t < steps; ++t) {
-            const float T = T0 * powf(rho, (float)t);
-            const float beta = steps > 1 ? (float)t / (float)(steps - 1) : 1.0f;
-            double acc = 0.0;
-            for (int i = 0; i < ne; ++i) {
-                const float g = 1.0f / (1.0f + expf(-z[i] / T));
-                const float hv = ((hbits >> i) & 1u) ? 1.0f : 0.0f;
-                m[i] = (1.0f - beta) * g + beta * hv;
-                acc += (double)m[i] * (1.0 - (double)m[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < SMAX; ++t) {
+            if (t < steps) {
+                double acc = 0.0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
+                    const float g = __builtin_amdgcn_rcpf(1.0f + e);
+                    m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];
+                    const double md = i < ne ? (double)m[i] : 0.0;   // past the row end: adds 0
+                    acc += md * (1.0 - md);
+                }
+                lm[t] += acc;
             }
-            lm[t] += acc;
         }
         // final projection: top-N of m_{steps-1}
+        float km[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) km[i] = rank_key(m[i]);
         uint32_t fbits = 0;
-        for (int g = 0; g * M < ne; ++g) {
-            float kk[8];
-            for (int i = 0; i < M; ++i) kk[i] = rank_key(m[g * M + i]);
-            uint32_t gb = 0;
-            for (int i = 0; i < M; ++i) {
-                int beaten = 0;
-                for (int j = 0; j < M; ++j) {
-                    if (j == i) continue;
-                    beaten += ((j < i) ? (kk[j] >= kk[i]) : (kk[j] > kk[i])) ? 1 : 0;
-                }
-                if (beaten < N) gb |= 1u << i;
-            }
-            fbits |= gb << (g * M);
+        if (M == 4 && ne == 8) {
+            const float k0v[4] = {km[0], km[1], km[2], km[3]}, k1v[4] = {km[4], km[5], km[6], km[7]};
+            fbits = topn_bits<4>(k0v, N) | (topn_bits<4>(k1v, N) << 4);
+        } else if (M == 8 && ne == 8) {
+            fbits = topn_bits<8>(km, N);
+        } else {
+            for (int g = 0; g * M < ne; ++g) fbits |= group_topn_bits(km, g * M, M, N) << (g * M);
         }
         hard_mask[r * ldm + b] = (uint8_t)fbits;
-        if (m_final)
-            for (int i = 0; i < ne; ++i) m_final[r * ldf + k0 + i] = m[i];
+        if (m_final) {
+            if (vec && ne == 8) {
+                *(float4*)(m_final + r * ldf + k0) = make_float4(m[0], m[1], m[2], m[3]);
+                *(float4*)(m_final + r * ldf + k0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+            } else {
+                for (int i = 0; i < ne; ++i) m_final[r * ldf + k0 + i] = m[i];
+            }
+        }
+        r += dr;
+        b += db;
+        if (b >= bpr) {
+            b -= bpr;
+            r += 1;
+        }
     }
-    for (int t = 0; t < steps; ++t) {
-        const double v = block_sum(lm[t], sh);
-        if (threadIdx.x == 0) part[(int64_t)t * kRedBlocks + blockIdx.x] = v;
+#pragma unroll
+    for (int t = 0; t < SMAX; ++t) {
+        if (t < steps) {
+            const double v = block_sum(lm[t], sh);
+            if (threadIdx.x == 0) part[(int64_t)t * kRedBlocks + blockIdx.x] = v;
+        }
     }
 }
 
@@ -195,8 +366,13 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
                  float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
                  void* ws, hipStream_t s) {
     double* part = (double*)ws;
-    hipLaunchKernelGGL(gate_kernel, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, rho,
-                       steps, m_final, ldf, hard_mask, ldm, part);
+#define NM_GATE(SM)                                                                                            \
+    hipLaunchKernelGGL(gate_kernel<SM>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, \
+                       rho, steps, m_final, ldf, hard_mask, ldm, part)
+    if (steps <= 8) NM_GATE(8);
+    else if (steps <= 16) NM_GATE(16);
+    else NM_GATE(kMaxSteps);
+#undef NM_GATE
     hipLaunchKernelGGL(gate_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, steps, lmid);
 }
 

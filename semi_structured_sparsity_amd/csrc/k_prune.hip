@@ -152,10 +152,73 @@ __global__ __launch_bounds__(256) void score_kernel(const void* __restrict__ W, 
     }
 }
 
+// bf16 fast path: lane = 8 consecutive weights of PR rows (16-byte loads, all PR rows'
+// loads issued first), two 16-byte stores of S per row.
+constexpr int kScoreRows = 4;
+
+template <bool HESS, bool HFULL>
+__global__ __launch_bounds__(256) void score8_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                     const float* __restrict__ H, int64_t ldh, float eps, int64_t R,
+                                                     int64_t K, float* __restrict__ S, int64_t lds, int64_t row_base) {
+    constexpr int PR = kScoreRows;
+    const int64_t k0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (k0 >= K) return;
+    const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
+    uint4 wq[PR];
+    float4 hq[PR][2];
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p < R ? r0 + p : R - 1;
+        wq[p] = *(const uint4*)(W + r * ldw + k0);
+        if constexpr (HESS) {
+            if (HFULL || p == 0) {
+                const float* hp = H + (HFULL ? r * ldh : 0) + k0;
+                hq[p][0] = *(const float4*)hp;
+                hq[p][1] = *(const float4*)(hp + 4);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p;
+        if (r >= R) break;
+        const uint32_t u[4] = {wq[p].x, wq[p].y, wq[p].z, wq[p].w};
+        float o[8];
+        const float4 h0 = HESS ? hq[HFULL ? p : 0][0] : float4{}, h1 = HESS ? hq[HFULL ? p : 0][1] : float4{};
+        const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = bf16_bits_to_f32((u[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+            o[i] = HESS ? hess_score(w, h[i], eps) : fabsf(w);
+        }
+        *(float4*)(S + r * lds + k0) = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4*)(S + r * lds + k0 + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+}
+
 void launch_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const float* H, int64_t ldh,
                   float eps, nm_score_mode mode, float* S, int64_t lds, hipStream_t s) {
     const int64_t total = R * K;
     if (total == 0) return;
+    const bool hess = mode == NM_SCORE_HESSIAN;
+    if (wdt == NM_BF16 && (K % 8) == 0 && (((uintptr_t)W) & 15) == 0 && (ldw % 8) == 0 && (((uintptr_t)S) & 15) == 0 &&
+        (lds % 4) == 0 && (!hess || ((((uintptr_t)H) & 15) == 0 && (ldh % 4) == 0))) {
+        constexpr int64_t kRowsPerLaunch = 65535LL * kScoreRows;
+        for (int64_t rb = 0; rb < R; rb += kRowsPerLaunch) {
+            const int64_t nr = R - rb < kRowsPerLaunch ? R - rb : kRowsPerLaunch;
+            const dim3 g((unsigned)ceil_div(K, 256 * 8), (unsigned)ceil_div(nr, kScoreRows)), b(256);
+            if (!hess)
+                hipLaunchKernelGGL((score8_kernel<false, false>), g, b, 0, s, (const uint16_t*)W, ldw, H, ldh, eps, R,
+                                   K, S, lds, rb);
+            else if (ldh)
+                hipLaunchKernelGGL((score8_kernel<true, true>), g, b, 0, s, (const uint16_t*)W, ldw, H, ldh, eps, R, K,
+                                   S, lds, rb);
+            else
+                hipLaunchKernelGGL((score8_kernel<true, false>), g, b, 0, s, (const uint16_t*)W, ldw, H, ldh, eps, R,
+                                   K, S, lds, rb);
+        }
+        return;
+    }
     hipLaunchKernelGGL(score_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, W, wdt, R, K, ldw,
                        H, ldh, eps, mode, S, lds);
 }
@@ -303,16 +366,6 @@ static int pack_chunk_groups(int N, int M) {
     return G;
 }
 
-void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
-                 int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
-    const int G = pack_chunk_groups(N, M);
-    const int64_t total = R * ceil_div(K / M, G);
-    if (total == 0) return;
-    hipLaunchKernelGGL(pack_generic_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, 0,
-                       (const void*)nullptr, NM_F32, (int64_t)0, (const float*)nullptr, (int64_t)0, 0.f,
-                       NM_SCORE_MAGNITUDE, mask, (uint8_t*)nullptr, ldm, W, wdt, ldw, R, K, N, M, G, vdt, vals, ldv,
-                       idx, ldi);
-}
 
 // ------------------------------------------------------------------ fused 2:4 fast path
 // Lane = 8 consecutive weights (two 4-groups) of PR rows; a quad of lanes = 32 weights =
@@ -322,7 +375,9 @@ void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
 // The lane writes its 4 kept values (8 bytes) and its mask byte directly.
 constexpr int kPP24Rows = 4;
 
-template <typename TW, bool HESS, bool HFULL>
+// FM: the kept positions come from the mask (input) instead of the score: per group
+// the first two set bits ascending, padded with the smallest unset positions (value 0).
+template <typename TW, bool HESS, bool HFULL, bool FM = false>
 __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict__ W, int64_t ldw,
                                                            const float* __restrict__ H, int64_t ldh, float eps,
                                                            int64_t R, int64_t K, uint8_t* __restrict__ mask,
@@ -335,10 +390,12 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
     const bool col_ok = k0 < K;
     uint32_t wb[PR][8];  // bf16 bit patterns of the values (the stored form)
     float w[PR][8];
+    uint32_t mbin[PR];   // FM: the input mask byte of each row
 #pragma unroll
     for (int p = 0; p < PR; ++p) {
         const int64_t r = r0 + p < R ? r0 + p : R - 1;   // rows past the end re-read the last row, never stored
         const int64_t kc = col_ok ? k0 : 0;
+        if constexpr (FM) mbin[p] = mask[r * ldm + (kc >> 3)];
         if constexpr (sizeof(TW) == 2) {
             const uint4 v = *(const uint4*)(W + r * ldw + kc);
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -368,7 +425,10 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
             else wb[p][i] = f32_to_bf16_bits(w[p][i]);
         }
         float key[8];
-        if constexpr (HESS) {
+        if constexpr (FM) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) key[i] = 0.f;
+        } else if constexpr (HESS) {
             float h[8];
             if constexpr (HFULL) {
                 const float* hp = H + (r < R ? r : R - 1) * ldh + (col_ok ? k0 : 0);
@@ -390,15 +450,26 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
         uint32_t mbyte = 0, nib = 0;
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-            const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
-            const uint32_t bits = topn_bits<4>(kk, 2);
+            uint32_t bits, real;
+            if constexpr (FM) {
+                const uint32_t b4 = (mbin[p] >> (4 * gi)) & 0xFu;
+                const uint32_t s1 = b4 & (0u - b4), s2 = (b4 ^ s1) & (0u - (b4 ^ s1));
+                real = s1 | s2;                                   // first two set bits
+                const uint32_t f = ~real & 0xFu, f1 = f & (0u - f), f2 = (f ^ f1) & (0u - (f ^ f1));
+                const int have = (s1 != 0) + (s2 != 0);
+                bits = real | (have < 2 ? f1 : 0u) | (have < 1 ? f2 : 0u);
+            } else {
+                const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
+                bits = topn_bits<4>(kk, 2);
+                real = bits;
+            }
             const uint32_t p0 = __builtin_ctz(bits);
             const uint32_t p1 = 31u - __builtin_clz(bits);
             uint32_t v0 = 0, v1 = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                v0 = (p0 == (uint32_t)i) ? wb[p][4 * gi + i] : v0;
-                v1 = (p1 == (uint32_t)i) ? wb[p][4 * gi + i] : v1;
+                v0 = (p0 == (uint32_t)i && ((real >> i) & 1u)) ? wb[p][4 * gi + i] : v0;
+                v1 = (p1 == (uint32_t)i && ((real >> i) & 1u)) ? wb[p][4 * gi + i] : v1;
             }
             packed[gi] = v0 | (v1 << 16);
             mbyte |= bits << (4 * gi);
@@ -407,13 +478,44 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
         const bool ok = col_ok && r < R;
         if (ok) {
             *(uint2*)(vals + r * ldv + (k0 >> 1)) = make_uint2(packed[0], packed[1]);
-            if (mask) mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
+            if (!FM && mask) mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
         }
         uint32_t v = ok ? nib << (8 * q) : 0u;
         v |= (uint32_t)__shfl_xor((int)v, 1);
         v |= (uint32_t)__shfl_xor((int)v, 2);
         if (q == 0 && ok) idx[r * ldi + (k0 >> 5)] = v;
     }
+}
+
+void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                 int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
+    const int64_t vec = wdt == NM_F32 ? 4 : 8;
+    const bool fast = N == 2 && M == 4 && vdt == NM_BF16 && (wdt == NM_BF16 || wdt == NM_F32) && (K % 8) == 0 &&
+                      (((uintptr_t)W) & 15) == 0 && (ldw % vec) == 0 && (((uintptr_t)vals) & 7) == 0 && (ldv % 4) == 0;
+    if (fast) {
+        if (R == 0 || K == 0) return;
+        constexpr int64_t kRowsPerLaunch = 65535LL * kPP24Rows;  // grid.y limit
+        for (int64_t rb = 0; rb < R; rb += kRowsPerLaunch) {
+            const int64_t nr = R - rb < kRowsPerLaunch ? R - rb : kRowsPerLaunch;
+            const dim3 g((unsigned)ceil_div(K, 256 * 8), (unsigned)ceil_div(nr, kPP24Rows)), b(256);
+            if (wdt == NM_BF16)
+                hipLaunchKernelGGL((prune_pack24_kernel<uint16_t, false, false, true>), g, b, 0, s, (const uint16_t*)W,
+                                   ldw, (const float*)nullptr, (int64_t)0, 0.f, R, K, (uint8_t*)mask, ldm,
+                                   (uint16_t*)vals, ldv, idx, ldi, rb);
+            else
+                hipLaunchKernelGGL((prune_pack24_kernel<float, false, false, true>), g, b, 0, s, (const float*)W, ldw,
+                                   (const float*)nullptr, (int64_t)0, 0.f, R, K, (uint8_t*)mask, ldm, (uint16_t*)vals,
+                                   ldv, idx, ldi, rb);
+        }
+        return;
+    }
+    const int G = pack_chunk_groups(N, M);
+    const int64_t total = R * ceil_div(K / M, G);
+    if (total == 0) return;
+    hipLaunchKernelGGL(pack_generic_kernel, dim3(grid_cap(ceil_div(total, 256), 8192)), dim3(256), 0, s, 0,
+                       (const void*)nullptr, NM_F32, (int64_t)0, (const float*)nullptr, (int64_t)0, 0.f,
+                       NM_SCORE_MAGNITUDE, mask, (uint8_t*)nullptr, ldm, W, wdt, ldw, R, K, N, M, G, vdt, vals, ldv,
+                       idx, ldi);
 }
 
 void launch_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
@@ -522,10 +624,206 @@ __global__ __launch_bounds__(256) void slide_kernel(int select, const void* __re
     }
 }
 
+// 6:8 fast path (Ns = 4, values copied without conversion).  Lane = one 8-group of
+// PR rows; its 6 kept positions go to the 3 windows by the same greedy rule as
+// slide_kernel, giving 6 values and 12 index bits per group.  The 12-bit fields of
+// 8 consecutive groups (96 bits = 3 words) are assembled across the lanes with
+// xor-shuffles.  SEL: 0 |W|, 1 Hessian with a row-vector H, 2 Hessian with a full
+// H, 3 kept positions from the input mask.
+constexpr int kS68Rows = 4;
+
+template <typename TS, typename TV, int SEL>
+__global__ __launch_bounds__(256) void slide68_kernel(const TS* __restrict__ Wsc, int64_t ldsc,
+                                                      const float* __restrict__ H, int64_t ldh, float eps,
+                                                      const TV* __restrict__ Wv, int64_t ldwv, int64_t R, int64_t K,
+                                                      const uint8_t* __restrict__ mask_in, uint8_t* __restrict__ mask_out,
+                                                      int64_t ldm, TV* __restrict__ vals, int64_t ldv,
+                                                      uint32_t* __restrict__ idx, int64_t ldi, int64_t row_base) {
+    constexpr int PR = kS68Rows;
+    const int64_t groups = K / 8;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool gok = g < groups;
+    const int64_t k0 = (gok ? g : 0) * 8;
+    const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
+    const int j8 = threadIdx.x & 7;
+    uint32_t vraw[PR][4];   // the 8 values' bits: bf16 -> 4 words, int8 -> 2 words
+    float sc[PR][8];
+    uint32_t mb[PR];
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p < R ? r0 + p : R - 1;
+        if constexpr (sizeof(TV) == 2) {
+            const uint4 q = *(const uint4*)(Wv + r * ldwv + k0);
+            vraw[p][0] = q.x; vraw[p][1] = q.y; vraw[p][2] = q.z; vraw[p][3] = q.w;
+        } else {
+            const uint2 q = *(const uint2*)(Wv + r * ldwv + k0);
+            vraw[p][0] = q.x; vraw[p][1] = q.y; vraw[p][2] = 0; vraw[p][3] = 0;
+        }
+        if constexpr (SEL == 3) {
+            mb[p] = mask_in[r * ldm + (k0 >> 3)];
+        } else if constexpr (sizeof(TS) == 2) {
+            const uint4 q = *(const uint4*)(Wsc + r * ldsc + k0);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sc[p][i] = bf16_bits_to_f32((u[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+        } else {
+            const float4 a = *(const float4*)(Wsc + r * ldsc + k0);
+            const float4 c = *(const float4*)(Wsc + r * ldsc + k0 + 4);
+            sc[p][0] = a.x; sc[p][1] = a.y; sc[p][2] = a.z; sc[p][3] = a.w;
+            sc[p][4] = c.x; sc[p][5] = c.y; sc[p][6] = c.z; sc[p][7] = c.w;
+        }
+    }
+    float hrow[8];
+    if constexpr (SEL == 1) {
+        const float4 h0 = *(const float4*)(H + k0);
+        const float4 h1 = *(const float4*)(H + k0 + 4);
+        hrow[0] = h0.x; hrow[1] = h0.y; hrow[2] = h0.z; hrow[3] = h0.w;
+        hrow[4] = h1.x; hrow[5] = h1.y; hrow[6] = h1.z; hrow[7] = h1.w;
+    }
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+        const int64_t r = r0 + p;
+        const bool ok = gok && r < R;
+        uint32_t bits;
+        if constexpr (SEL == 3) {
+            bits = mb[p];
+        } else {
+            float h[8];
+            if constexpr (SEL == 2) {
+                const float* hp = H + (r < R ? r : R - 1) * ldh + k0;
+                const float4 h0 = *(const float4*)hp;
+                const float4 h1 = *(const float4*)(hp + 4);
+                h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+                h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+            } else if constexpr (SEL == 1) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = hrow[i];
+            }
+            float key[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                key[i] = rank_key(SEL == 0 ? fabsf(sc[p][i]) : hess_score(sc[p][i], h[i], eps));
+            bits = topn_bits<8>(key, 6);
+            if (mask_out && ok) mask_out[r * ldm + (k0 >> 3)] = (uint8_t)bits;
+        }
+        // kept positions ascending -> earliest covering window with a free slot
+        int wc[3] = {0, 0, 0}, wl[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (!((bits >> q) & 1u)) continue;
+            const int wa = q / 2 - 1, wb = q / 2;
+            if (wa >= 0 && wa < 3 && wc[wa] < 2) {
+                wl[wa][wc[wa]] = q - 2 * wa;
+                ++wc[wa];
+            } else if (wb < 3 && wc[wb] < 2) {
+                wl[wb][wc[wb]] = q - 2 * wb;
+                ++wc[wb];
+            }
+        }
+        uint32_t v12 = 0, outv[3];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            int loc[2] = {wl[w][0], wl[w][1]}, isv[2] = {wc[w] > 0, wc[w] > 1};
+            // pad with the smallest unused local positions (value 0)
+            int cnt = wc[w];
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const bool taken = (cnt > 0 && loc[0] == l) || (cnt > 1 && loc[1] == l);
+                if (cnt < 2 && !taken) {
+                    loc[cnt] = l;
+                    isv[cnt] = 0;
+                    ++cnt;
+                }
+            }
+            if (loc[0] > loc[1]) {
+                const int tl = loc[0]; loc[0] = loc[1]; loc[1] = tl;
+                const int tv = isv[0]; isv[0] = isv[1]; isv[1] = tv;
+            }
+            uint32_t e[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int pos = 2 * w + loc[q];
+                uint32_t x;
+                if constexpr (sizeof(TV) == 2) x = (vraw[p][pos >> 1] >> (16 * (pos & 1))) & 0xffffu;
+                else x = (vraw[p][pos >> 2] >> (8 * (pos & 3))) & 0xffu;
+                e[q] = isv[q] ? x : 0u;
+            }
+            outv[w] = sizeof(TV) == 2 ? (e[0] | (e[1] << 16)) : (e[0] | (e[1] << 8));
+            v12 |= (uint32_t)(loc[0] | (loc[1] << 2)) << (4 * w);
+        }
+        if (ok) {
+            if constexpr (sizeof(TV) == 2) {
+                uint32_t* vp = (uint32_t*)(vals + r * ldv + 6 * g);
+                vp[0] = outv[0]; vp[1] = outv[1]; vp[2] = outv[2];
+            } else {
+                uint16_t* vp = (uint16_t*)(vals + r * ldv + 6 * g);
+                vp[0] = (uint16_t)outv[0]; vp[1] = (uint16_t)outv[1]; vp[2] = (uint16_t)outv[2];
+            }
+        }
+        // 12 index bits at bit 12*j8 of the cluster's 3 words
+        const uint32_t f = ok ? v12 : 0u;
+        const int pos = 12 * j8, wd = pos >> 5, sh = pos & 31;
+        const uint32_t lo = f << sh, hi = sh > 20 ? f >> (32 - sh) : 0u;
+        uint32_t c0 = wd == 0 ? lo : 0u;
+        uint32_t c1 = wd == 1 ? lo : (wd == 0 ? hi : 0u);
+        uint32_t c2 = wd == 2 ? lo : (wd == 1 ? hi : 0u);
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            c0 |= (uint32_t)__shfl_xor((int)c0, m);
+            c1 |= (uint32_t)__shfl_xor((int)c1, m);
+            c2 |= (uint32_t)__shfl_xor((int)c2, m);
+        }
+        if (j8 == 0 && gok && r < R) {
+            const int64_t w0 = (g / 8) * 3, nbits = 12 * groups;
+            uint32_t* ip = idx + r * ldi + w0;
+            ip[0] = c0;
+            if (32 * (w0 + 1) < nbits) ip[1] = c1;
+            if (32 * (w0 + 2) < nbits) ip[2] = c2;
+        }
+    }
+}
+
 void launch_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
                   nm_score_mode mode, bool select, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K,
                   int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm, nm_dtype vdt, void* vals,
                   int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
+    if (Ns == 4 && (K % 8) == 0 && wdt == vdt && (wdt == NM_BF16 || wdt == NM_I8) &&
+        (!select || sdt == NM_BF16 || sdt == NM_F32)) {
+        const int64_t ev = wdt == NM_BF16 ? 2 : 1;
+        const bool vals_ok = (((uintptr_t)vals) & (ev == 2 ? 3 : 1)) == 0 && (ldv % 2) == 0;
+        const bool wv_ok = (((uintptr_t)Wv) & (ev == 2 ? 15 : 7)) == 0 && (ldwv % 8) == 0;
+        const bool ws_ok = !select || ((((uintptr_t)Wsc) & 15) == 0 && (ldsc % (sdt == NM_F32 ? 4 : 8)) == 0);
+        const bool h_ok = !select || mode == NM_SCORE_MAGNITUDE || ((((uintptr_t)H) & 15) == 0 && (ldh % 4) == 0);
+        if (vals_ok && wv_ok && ws_ok && h_ok) {
+            if (R == 0 || K == 0) return;
+            const int sel = !select ? 3 : (mode == NM_SCORE_MAGNITUDE ? 0 : (ldh ? 2 : 1));
+            constexpr int64_t kRowsPerLaunch = 65535LL * kS68Rows;
+            for (int64_t rb = 0; rb < R; rb += kRowsPerLaunch) {
+                const int64_t nr = R - rb < kRowsPerLaunch ? R - rb : kRowsPerLaunch;
+                const dim3 g((unsigned)ceil_div(K / 8, 256), (unsigned)ceil_div(nr, kS68Rows)), b(256);
+#define NM_S68(TS, TV, SL)                                                                                         \
+    hipLaunchKernelGGL((slide68_kernel<TS, TV, SL>), g, b, 0, s, (const TS*)Wsc, ldsc, H, ldh, eps, (const TV*)Wv, \
+                       ldwv, R, K, mask_in, mask_out, ldm, (TV*)vals, ldv, idx, ldi, rb)
+#define NM_S68_SEL(TS, TV)                          \
+    do {                                            \
+        if (sel == 0) NM_S68(TS, TV, 0);            \
+        else if (sel == 1) NM_S68(TS, TV, 1);       \
+        else if (sel == 2) NM_S68(TS, TV, 2);       \
+        else NM_S68(TS, TV, 3);                     \
+    } while (0)
+                if (wdt == NM_BF16) {
+                    if (!select || sdt == NM_BF16) NM_S68_SEL(uint16_t, uint16_t);
+                    else NM_S68_SEL(float, uint16_t);
+                } else {
+                    if (!select || sdt == NM_BF16) NM_S68_SEL(uint16_t, int8_t);
+                    else NM_S68_SEL(float, int8_t);
+                }
+#undef NM_S68_SEL
+#undef NM_S68
+            }
+            return;
+        }
+    }
     // chunk of Gt groups: Gt * (Ns-1) windows * 4 bits must be a multiple of 32,
     // and (for mask bytes written bit by bit) chunks never share a mask byte with
     // another thread: Gt * 2Ns must be a multiple of 8.

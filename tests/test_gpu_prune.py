@@ -49,6 +49,9 @@ def test_score_tiny24_and_full_curvature(nm):
     assert np.array_equal(S, O.score(host(Wb), Hf, 1e-6))
     S = nm.nm_score(Wb.to(dev()), None, 0.0, nm.NM_SCORE_MAGNITUDE).cpu().numpy()
     assert np.array_equal(S, O.score(host(Wb), None, 0.0, O.SCORE_MAGNITUDE))
+    Hrow = g.uniform(0.1, 1.0, 200).astype(np.float32)  # one curvature per input column, shared by the rows
+    S = nm.nm_score(Wb.to(dev()), torch.from_numpy(Hrow).to(dev()), 1e-6).cpu().numpy()
+    assert np.array_equal(S, O.score(host(Wb), Hrow, 1e-6))
 
 
 # ------------------------------------------------------------------ A7
