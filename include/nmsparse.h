@@ -124,7 +124,8 @@ nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, doub
  *   T_t = T0 * rho^t,  beta_t = t/(steps-1),  g_t = sigmoid(z / T_t)
  *   (f32, hardware 2^x and reciprocal: about 1e-7 relative),
  *   m_t = (1 - beta_t) g_t + beta_t h,   h = top-N of s per group,
- *   lmid[t] = sum m_t (1 - m_t)   (f64, fixed-order reduction).
+ *   lmid[t] = sum m_t (1 - m_t)   (summed over 8 consecutive scores in f32, then
+ *   in f64 in a fixed order).
  * The final projection keeps the top-N of m_{steps-1} per group -> hard_mask.
  * m_final (nullable): m_{steps-1} as f32 [R, K] (ldf).  stats: device [2] from
  * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0, 1 <= steps <= 64.

@@ -18,6 +18,7 @@ namespace nm {
 constexpr int kRedBlocks = 1024;
 constexpr int kRedThreads = 256;
 constexpr int kMaxSteps = 64;
+constexpr int kGateBlocks = 2048;  // gate grid (its per-step partials are summed in block order)
 
 __device__ __forceinline__ double block_sum(double v, double* sh) {
     sh[threadIdx.x] = v;
@@ -57,7 +58,7 @@ __device__ __forceinline__ Moments moments_combine(Moments a, Moments b) {
 // the caller guarantees K % VEC == 0, ld % VEC == 0 and 16-byte alignment.
 template <typename T, int VEC, typename F>
 __device__ __forceinline__ void for_units(const T* __restrict__ X, int64_t R, int64_t K, int64_t ld, F&& f) {
-    constexpr int UN = 4;
+    constexpr int UN = 8;
     const int64_t upr = K / VEC, total = R * upr;
     const int64_t stride = (int64_t)kRedBlocks * kRedThreads;
     const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
     }
     const bool vec = (lds % 4) == 0 && (((uintptr_t)S) & 15) == 0 && (m_final == nullptr || ((ldf % 4) == 0 &&
                                                                           (((uintptr_t)m_final) & 15) == 0));
-    const int64_t stride = (int64_t)kRedBlocks * kRedThreads;
+    const int64_t stride = (int64_t)kGateBlocks * kRedThreads;
     const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
     int64_t r = u0 / bpr, b = u0 - r * bpr;                   // (row, byte) of unit u, advanced without division
     const int64_t dr = stride / bpr, db = stride - dr * bpr;
@@ -299,16 +300,16 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
 #pragma unroll
         for (int t = 0; t < SMAX; ++t) {
             if (t < steps) {
-                double acc = 0.0;
+                float acc = 0.f;   // <= 8 terms in [0, 1/4]: f32 here, f64 across units
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float e = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
                     const float g = __builtin_amdgcn_rcpf(1.0f + e);
                     m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];
-                    const double md = i < ne ? (double)m[i] : 0.0;   // past the row end: adds 0
-                    acc += md * (1.0 - md);
+                    const float mm = i < ne ? m[i] : 0.f;   // past the row end: adds 0
+                    acc += mm * (1.0f - mm);
                 }
-                lm[t] += acc;
+                lm[t] += (double)acc;
             }
         }
         // final projection: top-N of m_{steps-1}
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
     for (int t = 0; t < SMAX; ++t) {
         if (t < steps) {
             const double v = block_sum(lm[t], sh);
-            if (threadIdx.x == 0) part[(int64_t)t * kRedBlocks + blockIdx.x] = v;
+            if (threadIdx.x == 0) part[(int64_t)t * kGateBlocks + blockIdx.x] = v;
         }
     }
 }
@@ -354,20 +355,20 @@ __global__ __launch_bounds__(kRedThreads) void gate_final_kernel(const double* _
     __shared__ double sh[kRedThreads];
     for (int t = 0; t < steps; ++t) {
         double acc = 0.0;
-        for (int i = threadIdx.x; i < kRedBlocks; i += kRedThreads) acc += part[(int64_t)t * kRedBlocks + i];
+        for (int i = threadIdx.x; i < kGateBlocks; i += kRedThreads) acc += part[(int64_t)t * kGateBlocks + i];
         const double s = block_sum(acc, sh);
         if (threadIdx.x == 0) lmid[t] = s;
     }
 }
 
-size_t gate_ws(int64_t, int64_t, int steps) { return (size_t)kRedBlocks * (size_t)(steps > 0 ? steps : 1) * sizeof(double); }
+size_t gate_ws(int64_t, int64_t, int steps) { return (size_t)kGateBlocks * (size_t)(steps > 0 ? steps : 1) * sizeof(double); }
 
 void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
                  float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
                  void* ws, hipStream_t s) {
     double* part = (double*)ws;
 #define NM_GATE(SM)                                                                                            \
-    hipLaunchKernelGGL(gate_kernel<SM>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, \
+    hipLaunchKernelGGL(gate_kernel<SM>, dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, \
                        rho, steps, m_final, ldf, hard_mask, ldm, part)
     if (steps <= 8) NM_GATE(8);
     else if (steps <= 16) NM_GATE(16);

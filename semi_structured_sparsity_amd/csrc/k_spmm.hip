@@ -369,21 +369,25 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false>
 struct Ring {
     static constexpr int NW = WRN * WTN;               // waves per block (WRN along rows, WTN along tokens)
     static constexpr int BR = WRN * SR * 32;           // weight rows per block
     static constexpr int BT = WTN * ST * 32;           // tokens per block
     static constexpr int KO = KB / (int)sizeof(T);     // original columns per stage (KB bytes of X per token)
-    static constexpr int ND = KB / 64;                 // SMFMAC depths per stage
-    static constexpr int AROW = KB / 2;                // compressed bytes per weight row per stage
-    static constexpr int AI = KO / 32;                 // index words per row per stage
+    static constexpr int KL = LIFT ? KO * 3 / 2 : KO;  // lifted columns per stage (6:8: 12 per 8)
+    static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;
+    static constexpr int ND = KL / KDEP;               // SMFMAC depths per stage
+    static constexpr int AROW = KL / 2 * (int)sizeof(T);  // compressed bytes per weight row per stage
+    static constexpr int ACH = AROW / 16;              // 16-byte chunks per weight row per stage
+    static constexpr int AI = KL / 32;                 // index words per row per stage
     static constexpr int A_OFF = 0;
     static constexpr int I_OFF = BR * AROW;
     static constexpr int B_OFF = I_OFF + BR * AI * 4;
     static constexpr int STAGE = B_OFF + BT * KB;
     static constexpr int NA = BR * AROW / 1024 / NW;   // A wave-instructions per wave
-    static constexpr bool I16 = AI >= 4;               // index rows loaded in 16-byte pieces (else dwords)
+    // index rows loaded in 16-byte pieces when whole pieces split evenly over the waves, else dwords
+    static constexpr bool I16 = AI % 4 == 0 && (BR * AI * 4) % (1024 * NW) == 0;
     static constexpr int NI = BR * AI * 4 / (I16 ? 1024 : 256) / NW;
     static constexpr int NB = BT * KB / 1024 / NW;     // X wave-instructions per wave
     static constexpr int PER = NA + NI + NB;           // loads per wave per stage
@@ -392,8 +396,22 @@ struct Ring {
     static_assert(BR * AROW % (1024 * NW) == 0 && BT * KB % (1024 * NW) == 0, "loads must split evenly over the waves");
     static_assert(BR * AI * 4 % ((I16 ? 1024 : 256) * NW) == 0, "index loads must split evenly over the waves");
     static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
-    // XOR swizzles of 16-byte chunks (16 consecutive rows of a fragment read hit distinct banks)
+    static_assert(ACH == 4 || ACH == 8 || ACH == 12, "weight-row chunk count without a swizzle");
+    static_assert(!LIFT || sizeof(T) == 2, "the lifted gather is written for bf16 activations");
+    // Swizzles of 16-byte chunks, so that the 16 lanes served together by a 16-byte LDS read
+    // hit distinct banks (checked on the hardware with an LDS probe):
+    //   weight rows of 4 or 8 chunks: logical chunk c at c ^ swa(r);
+    //   rows of 12 chunks (lifted): logical chunk c at (c + 3 ((r >> 2) & 3)) mod 12;
+    //   X rows: logical chunk c at c ^ swb(t).
     __device__ static int swa(int r) { return AROW == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+    __device__ static int achunk(int r, int c) {     // physical chunk of logical chunk c in row r
+        if constexpr (ACH == 12) return (c + 3 * ((r >> 2) & 3)) % 12;
+        else return c ^ swa(r);
+    }
+    __device__ static int alogical(int r, int p) {   // logical chunk held by physical chunk p of row r
+        if constexpr (ACH == 12) return (p + 12 - 3 * ((r >> 2) & 3)) % 12;
+        else return p ^ swa(r);
+    }
     __device__ static int swb(int t) { return KB == 128 ? ((t >> 1) & 7) : (t & 15); }
 };
 
@@ -405,9 +423,9 @@ struct RingFrag {          // fragments of one SMFMAC depth
 };
 
 // NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int OCC = 1>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int OCC = 1>
 __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs a) {
-    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN>;
+    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN, LIFT>;
     using FR = RingFrag<SR, ST>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * RG::STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -430,8 +448,8 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     uint32_t oA[RG::NA], oI[RG::NI], oB[RG::NB];
 #pragma unroll
     for (int i = 0; i < RG::NA; ++i) {
-        const int row = (wave * RG::NA + i) * (64 / ACH) + lane / ACH;
-        const int c = (lane % ACH) ^ RG::swa(row);
+        const int q = (wave * RG::NA + i) * 64 + lane;       // 16-byte chunk of the block's stage, row-major
+        const int row = q / ACH, c = RG::alogical(row, q % ACH);
         const int64_t gr = row < rmax ? row : rmax;
         oA[i] = (uint32_t)(gr * a.ldv * es + c * 16);
     }
@@ -474,7 +492,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
 #pragma unroll
         for (int i = 0; i < SR; ++i) {
             const int row = (wr * SR + i) * 32 + l32;
-            f.a[i] = *(const i32x4_t*)(sA + row * RG::AROW + ((2 * d + h) ^ RG::swa(row)) * 16);
+            f.a[i] = *(const i32x4_t*)(sA + row * RG::AROW + RG::achunk(row, 2 * d + h) * 16);
             // bf16: the lane's 16 index bits are selected (shifted by 16h) at the SMFMAC, so
             // that no VALU op waits on this read ahead of unrelated SMFMACs
             if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d];
@@ -483,9 +501,32 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
             const int tok = (wt * ST + j) * 32 + l32;
-            const i32x4_t lo = *(const i32x4_t*)(sB + tok * KB + ((4 * d + h) ^ RG::swb(tok)) * 16);
-            const i32x4_t hi = *(const i32x4_t*)(sB + tok * KB + ((4 * d + 2 + h) ^ RG::swb(tok)) * 16);
-            f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const uint8_t* trow = sB + tok * KB;
+            const int sw = RG::swb(tok);
+            if constexpr (!LIFT) {
+                const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ sw) * 16);
+                const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ sw) * 16);
+                f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                // lifted column L reads original column (L/12)*8 + 2*((L%12)/4) + L%4: the fragment is
+                // gathered window by window (4 lifted columns = 4 consecutive original ones) from the
+                // stage's original columns
+                int wv[8];
+                auto at = [&](int byte) __attribute__((always_inline)) {   // LDS address of a stage byte
+                    return trow + (((byte >> 4) ^ sw) << 4) + (byte & 15);
+                };
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+#pragma unroll
+                    for (int win = 0; win < 2; ++win) {
+                        const int Lw = 32 * d + 16 * q + 8 * h + 4 * win;
+                        const int ob = ((Lw / 12) * 8 + 2 * ((Lw % 12) / 4)) * 2;
+                        wv[q * 4 + win * 2] = *(const int*)at(ob);
+                        wv[q * 4 + win * 2 + 1] = *(const int*)at(ob + 4);
+                    }
+                }
+                f.b[j] = i32x8_t{wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]};
+            }
         }
     };
 
@@ -812,8 +853,11 @@ struct SpmmPlan {
 //   narrow: 256 x 128 tile, 4 waves (one per SIMD), 2 stages of 256 B of X per token
 //   big   : 256 x 256 tile, 8 waves (two per SIMD), 3 stages of 128 B; bf16 only (the int8
 //           index rows of a 128-byte stage do not split over 8 waves)
+//   lift  : 128 x 128 tile, 4 waves, 2 stages of 256 B of original X per token (384 B of
+//           lifted columns), for the 6:8 sliding-window products
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
 #define NM_RING_BIG uint16_t, 4, 2, 128, 3, 2, 4
+#define NM_RING_LIFT T, 2, 2, 256, 2, 2, 2, true
 
 template <typename T, bool LIFT>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
@@ -822,13 +866,17 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     p.large = Mtok > 128;
     using RB = Ring<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
-    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0;
+    using RL = Ring<uint16_t, 2, 2, 256, 2, 2, 2, true>;   // NM_RING_LIFT at bf16
+    // int8 lifted products stay on the register-gather kernel: gathering 4-byte windows of
+    // int8 X out of LDS cost more than the tile saved (measured on the 6912x2560 layer)
+    p.ring = ring_ok && p.large && (!LIFT || sizeof(T) == 2) && (K % (LIFT ? RL::KO : RN::KO)) == 0;
     // the big tile moves a third fewer bytes per MAC than the narrow one but needs
     // every LDS byte of a CU; with fewer than two rounds of its tiles on 256 CUs the
     // narrow tile's finer grain balances better (measured on the 2048-token layers)
-    p.big = p.ring && sizeof(T) == 2 && (K % RB::KO) == 0 && ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
-    const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
-    const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
+    p.big = p.ring && !LIFT && sizeof(T) == 2 && (K % RB::KO) == 0 &&
+            ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
+    const int BR = p.ring ? (LIFT ? RL::BR : (p.big ? RB::BR : RN::BR)) : 128;
+    const int BT = p.ring ? (LIFT ? RL::BT : (p.big ? RB::BT : RN::BT)) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
     p.tiles_t = (int)ceil_div(Mtok, BT);
     {
@@ -837,7 +885,7 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
         p.skinny = 0;
         if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
     }
-    p.nsteps = (int)ceil_div(K, p.ring ? (p.big ? RB::KO : RN::KO) : G::KO);
+    p.nsteps = (int)ceil_div(K, p.ring ? (LIFT ? RL::KO : (p.big ? RB::KO : RN::KO)) : G::KO);
     if (p.skinny) {
         // K split over blocks (partials + a fixed-order reduce) where the row tiles alone
         // leave the chip short of blocks; measured on the 4096- and 11008-row layers
@@ -901,7 +949,9 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     } else if (p.skinny == 3) {
         hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
-        if constexpr (!LIFT) {
+        if constexpr (LIFT) {
+            if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_LIFT>), grid, dim3(256), 0, s, a);
+        } else {
             if constexpr (sizeof(T) == 2) {
                 if (p.big) {
                     hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
