@@ -369,7 +369,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false>
+// A global_load_lds instruction costs about the same per 128-byte line it touches
+// whatever part of the line it uses (measured on the hardware), and a row's index
+// words for one stage fill only a few bytes of a line.  With IG > 1 the index
+// words are therefore loaded for IG stages at once (IG consecutive 16-byte pieces
+// of a row), into two group buffers after the ring: group h (stages h*IG ..
+// h*IG+IG-1) is loaded in IG batches of rows, one batch with each of the stages
+// (h-1)*IG+1 .. h*IG, so every stage issues the same number of loads.  Within a
+// row of a group buffer, piece c is stored at c ^ ((r>>2) & (IG-1)).
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int IG = 1>
 struct Ring {
     static constexpr int NW = WRN * WTN;               // waves per block (WRN along rows, WTN along tokens)
     static constexpr int BR = WRN * SR * 32;           // weight rows per block
@@ -382,19 +390,26 @@ struct Ring {
     static constexpr int ACH = AROW / 16;              // 16-byte chunks per weight row per stage
     static constexpr int AI = KL / 32;                 // index words per row per stage
     static constexpr int A_OFF = 0;
-    static constexpr int I_OFF = BR * AROW;
-    static constexpr int B_OFF = I_OFF + BR * AI * 4;
+    static constexpr int I_OFF = BR * AROW;                           // IG == 1: index words in the stage
+    static constexpr int B_OFF = I_OFF + (IG == 1 ? BR * AI * 4 : 0);
     static constexpr int STAGE = B_OFF + BT * KB;
+    static constexpr int IGRP = BR * AI * 4 * IG;                     // IG > 1: bytes of one index group
+    static constexpr int G_OFF = NS * STAGE;                          // IG > 1: the two group buffers
+    static constexpr int LDS = NS * STAGE + (IG > 1 ? 2 * IGRP : 0);
     static constexpr int NA = BR * AROW / 1024 / NW;   // A wave-instructions per wave
     // index rows loaded in 16-byte pieces when whole pieces split evenly over the waves, else dwords
-    static constexpr bool I16 = AI % 4 == 0 && (BR * AI * 4) % (1024 * NW) == 0;
-    static constexpr int NI = BR * AI * 4 / (I16 ? 1024 : 256) / NW;
+    static constexpr bool I16 = IG > 1 || (AI % 4 == 0 && (BR * AI * 4) % (1024 * NW) == 0);
+    static constexpr int NI = IG > 1 ? IGRP / 1024 / NW / IG : BR * AI * 4 / (I16 ? 1024 : 256) / NW;
     static constexpr int NB = BT * KB / 1024 / NW;     // X wave-instructions per wave
     static constexpr int PER = NA + NI + NB;           // loads per wave per stage
-    static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
+    static_assert(LDS <= 160 * 1024, "LDS ring too large");
     static_assert(NA >= 1 && NI >= 1 && NB >= 1, "tile too small for its waves");
     static_assert(BR * AROW % (1024 * NW) == 0 && BT * KB % (1024 * NW) == 0, "loads must split evenly over the waves");
-    static_assert(BR * AI * 4 % ((I16 ? 1024 : 256) * NW) == 0, "index loads must split evenly over the waves");
+    static_assert(IG > 1 || BR * AI * 4 % ((I16 ? 1024 : 256) * NW) == 0, "index loads must split evenly over the waves");
+    // grouped index loads: the ring waits for every load at each stage end (NS == 2), one
+    // 16-byte piece per row per stage, and a power-of-two group
+    static_assert(IG == 1 || (NS == 2 && AI * 4 == 16 && (IG & (IG - 1)) == 0 && IGRP % (1024 * NW * IG) == 0),
+                  "grouped index loads need NS == 2, 16 index bytes per row per stage, IG a power of two");
     static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
     static_assert(ACH == 4 || ACH == 8 || ACH == 12, "weight-row chunk count without a swizzle");
     static_assert(!LIFT || sizeof(T) == 2, "the lifted gather is written for bf16 activations");
@@ -423,11 +438,11 @@ struct RingFrag {          // fragments of one SMFMAC depth
 };
 
 // NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int OCC = 1>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int OCC = 1, int IG = 1>
 __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs a) {
-    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN, LIFT>;
+    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN, LIFT, IG>;
     using FR = RingFrag<SR, ST>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * RG::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[RG::LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave % WRN, wt = wave / WRN;
@@ -446,6 +461,21 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
     uint32_t oA[RG::NA], oI[RG::NI], oB[RG::NB];
+    // IG > 1: per batch p and instruction i, the row's byte offset and the piece (stage of the group)
+    uint32_t gI[IG > 1 ? IG : 1][RG::NI];
+    int gC[IG > 1 ? IG : 1][RG::NI];
+    if constexpr (IG > 1) {
+#pragma unroll
+        for (int p = 0; p < IG; ++p)
+#pragma unroll
+            for (int i = 0; i < RG::NI; ++i) {
+                const int q = ((p * RG::NW + wave) * RG::NI + i) * 64 + lane;   // 16-byte slot of the group buffer
+                const int row = q / IG, c = (q % IG) ^ ((row >> 2) & (IG - 1));
+                const int64_t gr = row < rmax ? row : rmax;
+                gI[p][i] = (uint32_t)(gr * a.ldi * 4);
+                gC[p][i] = c;
+            }
+    }
 #pragma unroll
     for (int i = 0; i < RG::NA; ++i) {
         const int q = (wave * RG::NA + i) * 64 + lane;       // 16-byte chunk of the block's stage, row-major
@@ -468,35 +498,58 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
         const int64_t gt = row < tmax ? row : tmax;
         oB[i] = (uint32_t)(gt * a.ldx * es + c * 16);
     }
+    // IG > 1: batch p of index group g (stages past the last are clamped to it: read, never used)
+    auto issue_group = [&](int g, int p) __attribute__((always_inline)) {
+        const uint32_t gb = sbase + (uint32_t)(RG::G_OFF + (g & 1) * RG::IGRP);
+#pragma unroll
+        for (int i = 0; i < RG::NI; ++i) {
+            const int stg = g * IG + gC[p][i];
+            const int sc = stg < nsteps ? stg : nsteps - 1;
+            dma16s(gb + (uint32_t)(((p * RG::NW + wave) * RG::NI + i) * 1024), baseI, gI[p][i] + (uint32_t)(sc * 16));
+        }
+    };
     auto issue = [&](int s) __attribute__((always_inline)) {
         const uint32_t st = sbase + (uint32_t)((s % NS) * RG::STAGE);
 #pragma unroll
         for (int i = 0; i < RG::NA; ++i)
             dma16s(st + RG::A_OFF + (wave * RG::NA + i) * 1024, baseA, oA[i] + (uint32_t)(s * RG::AROW));
+        if constexpr (IG > 1) {
+            // stage s >= 1 carries batch (s-1) % IG of group (s-1) / IG + 1; group 0 is loaded up front
+            if (s >= 1) issue_group((s - 1) / IG + 1, (s - 1) % IG);
+        } else {
 #pragma unroll
-        for (int i = 0; i < RG::NI; ++i) {
-            if constexpr (RG::I16)
-                dma16s(st + RG::I_OFF + (wave * RG::NI + i) * 1024, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
-            else
-                dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+            for (int i = 0; i < RG::NI; ++i) {
+                if constexpr (RG::I16)
+                    dma16s(st + RG::I_OFF + (wave * RG::NI + i) * 1024, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+                else
+                    dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+            }
         }
 #pragma unroll
         for (int i = 0; i < RG::NB; ++i)
             dma16s(st + RG::B_OFF + (wave * RG::NB + i) * 1024, baseB, oB[i] + (uint32_t)(s * KB));
     };
     const int h = lane >> 5, l32 = lane & 31;
-    auto read_depth = [&](int slot, int d, FR& f) __attribute__((always_inline)) {
+    auto read_depth = [&](int S, int d, FR& f) __attribute__((always_inline)) {
+        const int slot = S % NS;
         const uint8_t* sA = smem + slot * RG::STAGE + RG::A_OFF;
         const uint32_t* sI = (const uint32_t*)(smem + slot * RG::STAGE + RG::I_OFF);
         const uint8_t* sB = smem + slot * RG::STAGE + RG::B_OFF;
+        const uint32_t* sG = (const uint32_t*)(smem + RG::G_OFF + ((S / IG) & 1) * RG::IGRP);
 #pragma unroll
         for (int i = 0; i < SR; ++i) {
             const int row = (wr * SR + i) * 32 + l32;
             f.a[i] = *(const i32x4_t*)(sA + row * RG::AROW + RG::achunk(row, 2 * d + h) * 16);
             // bf16: the lane's 16 index bits are selected (shifted by 16h) at the SMFMAC, so
             // that no VALU op waits on this read ahead of unrelated SMFMACs
-            if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d];
-            else f.iw[i] = sI[row * RG::AI + 2 * d + h];
+            if constexpr (IG > 1) {
+                const int pc = (S % IG) ^ ((row >> 2) & (IG - 1));
+                if constexpr (sizeof(T) == 2) f.iw[i] = sG[row * (4 * IG) + pc * 4 + d];
+                else f.iw[i] = sG[row * (4 * IG) + pc * 4 + 2 * d + h];
+            } else {
+                if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d];
+                else f.iw[i] = sI[row * RG::AI + 2 * d + h];
+            }
         }
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
@@ -559,6 +612,12 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     // flight), passes the barrier, reads depth 0 of stage S+1 and refills the
     // slot of stage S (fully read into registers by every wave) with stage S+NS.
     FR fa, fb;
+    if constexpr (IG > 1) {
+        if (nsteps > 0) {
+#pragma unroll
+            for (int p = 0; p < IG; ++p) issue_group(0, p);
+        }
+    }
 #pragma unroll
     for (int p = 0; p < NS; ++p)
         if (p < nsteps) issue(p);
@@ -569,17 +628,16 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     // depth; the last stage is peeled off so that the steady-state loop carries no
     // branch around LDS reads, which keeps the compiler's wait counts exact.
     auto stage = [&](int S, auto has_next) __attribute__((always_inline)) {
-        const int slot = S % NS;
 #pragma unroll
         for (int d = 0; d < RG::ND; d += 2) {
-            read_depth(slot, d + 1, fb);
+            read_depth(S, d + 1, fb);
             mfmas(fa);
             if (d + 2 < RG::ND) {
-                read_depth(slot, d + 2, fa);
+                read_depth(S, d + 2, fa);
             } else if constexpr (decltype(has_next)::value) {
                 if (S + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * RG::PER>();
                 else wait_vm_barrier<0>();
-                read_depth((S + 1) % NS, 0, fa);
+                read_depth(S + 1, 0, fa);
                 if (S + NS < nsteps) issue(S + NS);
             }
             mfmas(fb);
@@ -958,7 +1016,8 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
                     return check_launch("nm_spmm");
                 }
             }
-            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW>), grid, dim3(256), 0, s, a);
+            // bf16: index words loaded 4 stages at a time (whole 64-byte runs of a row)
+            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, false, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);
         }
     } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);

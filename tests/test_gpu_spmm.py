@@ -48,7 +48,7 @@ def _to_dev(vals, idx):
 SHAPES = [  # (tokens, R, K): few-token kernel (with and without a K split over blocks), many-token
     # LDS-ring kernel, the register-staged kernel (K not a multiple of the ring stage), ragged edges
     (1, 64, 256), (16, 100, 256), (37, 257, 128), (100, 300, 512), (129, 130, 256), (300, 200, 192), (64, 96, 4096),
-    (260, 160, 4096),
+    (260, 160, 4096), (300, 200, 640), (520, 260, 1152),   # ring stage counts that end mid index group
     (2048, 8192, 256), (2100, 8200, 256),
 ]
 
