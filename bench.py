@@ -178,6 +178,12 @@ def cpu_baseline(target_s: float):
 
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz full-rate lane operations per
+# second; a transcendental (2^x, 1/x) issues at a quarter of that rate.
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+# the gate's work per score and step, in full-rate lane operations: one 2^x and one
+# reciprocal (4 each), then the scale, 1 + e, the blend toward h (2) and m (1 - m) (2)
+GATE_OPS_PER_STEP = 4 + 4 + 1 + 1 + 2 + 2
 
 
 def measure_rows(nm, torch, synth, dev, reps: int = 5):
@@ -219,6 +225,9 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         elif bound == "mfma_i8":
             e["TOPs"] = round(work / t / 1e12, 2)
             e["frac"] = round(e["TOPs"] / INT8_PEAK_TOPS, 4)
+        elif bound == "alu":
+            e["GOPs"] = round(work / t / 1e9, 1)
+            e["frac"] = round(e["GOPs"] / VALU_PEAK_GOPS, 4)
         else:  # launch-latency bound: absolute time only
             e["GBps"] = round(work / t / 1e9, 3)
         out.append(e)
@@ -322,7 +331,7 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     wsg = ws_for(r.nm_gate_workspace(R, K, steps))
     row("hessian24", "A5+A6+A7", "gate/anneal -> 2:4 hard mask", lambda: chk(r.nm_gate(
         S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps, None, K,
-        hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "hbm", R * K * 4.125)
+        hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "alu", R * K * steps * GATE_OPS_PER_STEP)
     del S
     vals, idx = torch.empty((R, K // 2), dtype=bf, device=dev), torch.empty((R, K // 32), dtype=i32, device=dev)
     row("hessian24", "A8", "pack 28672x8192 from the hard mask", lambda: chk(r.nm_pack(

@@ -52,6 +52,25 @@ __device__ __forceinline__ Moments moments_combine(Moments a, Moments b) {
     return Moments{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
 }
 
+// Fixed-order tree of the block's per-thread moments; the result is left in sh[*][0].
+__device__ __forceinline__ void block_moments(Moments m, double (*sh)[kRedThreads]) {
+    sh[0][threadIdx.x] = m.n;
+    sh[1][threadIdx.x] = m.mean;
+    sh[2][threadIdx.x] = m.m2;
+    __syncthreads();
+    for (int w = kRedThreads / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+            const Moments o = moments_combine(Moments{sh[0][threadIdx.x], sh[1][threadIdx.x], sh[2][threadIdx.x]},
+                                              Moments{sh[0][threadIdx.x + w], sh[1][threadIdx.x + w],
+                                                      sh[2][threadIdx.x + w]});
+            sh[0][threadIdx.x] = o.n;
+            sh[1][threadIdx.x] = o.mean;
+            sh[2][threadIdx.x] = o.m2;
+        }
+        __syncthreads();
+    }
+}
+
 // Elements of [R, K] (leading dim ld) are visited in units of VEC consecutive
 // elements of a row; thread u of the fixed grid takes units u, u + stride, ...,
 // UN units per round with all UN loads issued before any is used.  When VEC > 1
@@ -122,32 +141,26 @@ __global__ __launch_bounds__(kRedThreads) void moments_partial_kernel(const floa
     });
     Moments m{n, n > 0.0 ? c + s1 / n : 0.0, n > 0.0 ? s2 - s1 * (s1 / n) : 0.0};
     if (m.m2 < 0.0) m.m2 = 0.0;
-    sh[0][threadIdx.x] = m.n;
-    sh[1][threadIdx.x] = m.mean;
-    sh[2][threadIdx.x] = m.m2;
-    __syncthreads();
-    for (int w = kRedThreads / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) {
-            const Moments o = moments_combine(Moments{sh[0][threadIdx.x], sh[1][threadIdx.x], sh[2][threadIdx.x]},
-                                              Moments{sh[0][threadIdx.x + w], sh[1][threadIdx.x + w],
-                                                      sh[2][threadIdx.x + w]});
-            sh[0][threadIdx.x] = o.n;
-            sh[1][threadIdx.x] = o.mean;
-            sh[2][threadIdx.x] = o.m2;
-        }
-        __syncthreads();
-    }
+    block_moments(m, sh);
     if (threadIdx.x < 3) part[threadIdx.x * kRedBlocks + blockIdx.x] = sh[threadIdx.x][0];
 }
 
-// One thread combines the block moments in block order.
-__global__ void moments_final_kernel(const double* __restrict__ part, double* __restrict__ stats) {
-    if (threadIdx.x != 0) return;
+// The block moments are combined in a fixed tree: thread t folds blocks t, t + 256,
+// ... in order, then the threads' moments meet in the block tree.  (A combine
+// divides in f64; a single thread folding all blocks one after another would
+// spend its time waiting on those divisions.)
+__global__ __launch_bounds__(kRedThreads) void moments_final_kernel(const double* __restrict__ part,
+                                                                    double* __restrict__ stats) {
+    __shared__ double sh[3][kRedThreads];
     Moments m{0.0, 0.0, 0.0};
-    for (int i = 0; i < kRedBlocks; ++i)
+    for (int i = threadIdx.x; i < kRedBlocks; i += kRedThreads)
         m = moments_combine(m, Moments{part[i], part[kRedBlocks + i], part[2 * kRedBlocks + i]});
-    stats[0] = m.n > 0.0 ? m.mean : 0.0;
-    stats[1] = m.n > 0.0 ? sqrt(m.m2 / m.n) : 0.0;
+    block_moments(m, sh);
+    if (threadIdx.x == 0) {
+        const double nn = sh[0][0], mean = sh[1][0], m2 = sh[2][0];
+        stats[0] = nn > 0.0 ? mean : 0.0;
+        stats[1] = nn > 0.0 ? sqrt(m2 / nn) : 0.0;
+    }
 }
 
 // sum |x| (for the ternary scale), f64 per thread, fixed-order LDS tree per block
@@ -201,7 +214,7 @@ void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* sta
         hipLaunchKernelGGL(moments_partial_kernel<4>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
     else
         hipLaunchKernelGGL(moments_partial_kernel<1>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
-    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(64), 0, s, (const double*)part, stats);
+    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, stats);
 }
 
 void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,

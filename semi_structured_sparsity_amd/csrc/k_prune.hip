@@ -632,6 +632,87 @@ __global__ __launch_bounds__(256) void slide_kernel(int select, const void* __re
 // H, 3 kept positions from the input mask.
 constexpr int kS68Rows = 4;
 
+// The window assignment depends only on the group's 8 keep bits, so it is tabulated
+// for all 256 masks at compile time (same greedy rule and zero padding as
+// slide_kernel).  Entry: byte-permute selectors that cut each window's two values
+// out of the group's raw bits (selector byte 0x0c gives a zero byte), and the
+// group's 12 index bits.  bf16: window w reads elements 2w..2w+3 = words w, w+1
+// of the group; int8: bytes 2w..2w+3 of the group's 8 bytes.
+struct SlideWin {
+    int loc[3][2];
+    bool val[3][2];
+};
+constexpr SlideWin slide_windows(uint32_t bits) {
+    SlideWin r{};
+    int wc[3] = {0, 0, 0}, wl[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+    for (int q = 0; q < 8; ++q) {
+        if (!((bits >> q) & 1u)) continue;
+        const int wa = q / 2 - 1, wb = q / 2;
+        if (wa >= 0 && wa < 3 && wc[wa] < 2) {
+            wl[wa][wc[wa]] = q - 2 * wa;
+            ++wc[wa];
+        } else if (wb < 3 && wc[wb] < 2) {
+            wl[wb][wc[wb]] = q - 2 * wb;
+            ++wc[wb];
+        }
+    }
+    for (int w = 0; w < 3; ++w) {
+        int loc[2] = {wl[w][0], wl[w][1]};
+        bool isv[2] = {wc[w] > 0, wc[w] > 1};
+        int cnt = wc[w];
+        for (int l = 0; l < 4 && cnt < 2; ++l) {
+            const bool taken = (cnt > 0 && loc[0] == l) || (cnt > 1 && loc[1] == l);
+            if (!taken) {
+                loc[cnt] = l;
+                isv[cnt] = false;
+                ++cnt;
+            }
+        }
+        if (loc[0] > loc[1]) {
+            const int tl = loc[0]; loc[0] = loc[1]; loc[1] = tl;
+            const bool tv = isv[0]; isv[0] = isv[1]; isv[1] = tv;
+        }
+        r.loc[w][0] = loc[0]; r.loc[w][1] = loc[1];
+        r.val[w][0] = isv[0]; r.val[w][1] = isv[1];
+    }
+    return r;
+}
+struct SlideLut {
+    uint32_t e[256][4];   // bf16: 3 selectors + index bits; int8: sel0 | sel1 << 16, sel2 | bits << 16
+};
+constexpr SlideLut make_slide_lut(bool bf16) {
+    SlideLut t{};
+    for (uint32_t m = 0; m < 256; ++m) {
+        const SlideWin sw = slide_windows(m);
+        uint32_t v12 = 0, sel[3] = {0, 0, 0};
+        for (int w = 0; w < 3; ++w) {
+            v12 |= (uint32_t)(sw.loc[w][0] | (sw.loc[w][1] << 2)) << (4 * w);
+            for (int q = 0; q < 2; ++q) {
+                const int p = sw.loc[w][q];
+                if (bf16) {
+                    const uint32_t b0 = sw.val[w][q] ? (uint32_t)(2 * p) : 0x0cu;
+                    const uint32_t b1 = sw.val[w][q] ? (uint32_t)(2 * p + 1) : 0x0cu;
+                    sel[w] |= (b0 | (b1 << 8)) << (16 * q);
+                } else {
+                    const uint32_t b = sw.val[w][q] ? (uint32_t)(2 * w + p) : 0x0cu;
+                    sel[w] |= b << (8 * q);
+                }
+            }
+            if (!bf16) sel[w] |= 0x0c0c0000u;
+        }
+        if (bf16) {
+            t.e[m][0] = sel[0]; t.e[m][1] = sel[1]; t.e[m][2] = sel[2]; t.e[m][3] = v12;
+        } else {
+            t.e[m][0] = (sel[0] & 0xffffu) | (sel[1] << 16);
+            t.e[m][1] = (sel[2] & 0xffffu) | (v12 << 16);
+            t.e[m][2] = 0; t.e[m][3] = 0;
+        }
+    }
+    return t;
+}
+__device__ const SlideLut kSlideLutBf16 = make_slide_lut(true);
+__device__ const SlideLut kSlideLutI8 = make_slide_lut(false);
+
 template <typename TS, typename TV, int SEL>
 __global__ __launch_bounds__(256) void slide68_kernel(const TS* __restrict__ Wsc, int64_t ldsc,
                                                       const float* __restrict__ H, int64_t ldh, float eps,
@@ -646,6 +727,9 @@ __global__ __launch_bounds__(256) void slide68_kernel(const TS* __restrict__ Wsc
     const int64_t k0 = (gok ? g : 0) * 8;
     const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
     const int j8 = threadIdx.x & 7;
+    __shared__ uint4 lut[256];
+    lut[threadIdx.x] = *(const uint4*)(sizeof(TV) == 2 ? kSlideLutBf16.e[threadIdx.x] : kSlideLutI8.e[threadIdx.x]);
+    __syncthreads();
     uint32_t vraw[PR][4];   // the 8 values' bits: bf16 -> 4 words, int8 -> 2 words
     float sc[PR][8];
     uint32_t mb[PR];
@@ -706,50 +790,19 @@ __global__ __launch_bounds__(256) void slide68_kernel(const TS* __restrict__ Wsc
             bits = topn_bits<8>(key, 6);
             if (mask_out && ok) mask_out[r * ldm + (k0 >> 3)] = (uint8_t)bits;
         }
-        // kept positions ascending -> earliest covering window with a free slot
-        int wc[3] = {0, 0, 0}, wl[3][2] = {{0, 0}, {0, 0}, {0, 0}};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (!((bits >> q) & 1u)) continue;
-            const int wa = q / 2 - 1, wb = q / 2;
-            if (wa >= 0 && wa < 3 && wc[wa] < 2) {
-                wl[wa][wc[wa]] = q - 2 * wa;
-                ++wc[wa];
-            } else if (wb < 3 && wc[wb] < 2) {
-                wl[wb][wc[wb]] = q - 2 * wb;
-                ++wc[wb];
-            }
-        }
-        uint32_t v12 = 0, outv[3];
-#pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            int loc[2] = {wl[w][0], wl[w][1]}, isv[2] = {wc[w] > 0, wc[w] > 1};
-            // pad with the smallest unused local positions (value 0)
-            int cnt = wc[w];
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                const bool taken = (cnt > 0 && loc[0] == l) || (cnt > 1 && loc[1] == l);
-                if (cnt < 2 && !taken) {
-                    loc[cnt] = l;
-                    isv[cnt] = 0;
-                    ++cnt;
-                }
-            }
-            if (loc[0] > loc[1]) {
-                const int tl = loc[0]; loc[0] = loc[1]; loc[1] = tl;
-                const int tv = isv[0]; isv[0] = isv[1]; isv[1] = tv;
-            }
-            uint32_t e[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int pos = 2 * w + loc[q];
-                uint32_t x;
-                if constexpr (sizeof(TV) == 2) x = (vraw[p][pos >> 1] >> (16 * (pos & 1))) & 0xffffu;
-                else x = (vraw[p][pos >> 2] >> (8 * (pos & 3))) & 0xffu;
-                e[q] = isv[q] ? x : 0u;
-            }
-            outv[w] = sizeof(TV) == 2 ? (e[0] | (e[1] << 16)) : (e[0] | (e[1] << 8));
-            v12 |= (uint32_t)(loc[0] | (loc[1] << 2)) << (4 * w);
+        // kept positions ascending -> earliest covering window with a free slot (tabulated)
+        const uint4 L = lut[bits & 0xffu];
+        uint32_t v12, outv[3];
+        if constexpr (sizeof(TV) == 2) {
+            outv[0] = __builtin_amdgcn_perm(vraw[p][1], vraw[p][0], L.x);
+            outv[1] = __builtin_amdgcn_perm(vraw[p][2], vraw[p][1], L.y);
+            outv[2] = __builtin_amdgcn_perm(vraw[p][3], vraw[p][2], L.z);
+            v12 = L.w;
+        } else {
+            outv[0] = __builtin_amdgcn_perm(vraw[p][1], vraw[p][0], (L.x & 0xffffu) | 0x0c0c0000u);
+            outv[1] = __builtin_amdgcn_perm(vraw[p][1], vraw[p][0], (L.x >> 16) | 0x0c0c0000u);
+            outv[2] = __builtin_amdgcn_perm(vraw[p][1], vraw[p][0], (L.y & 0xffffu) | 0x0c0c0000u);
+            v12 = L.y >> 16;
         }
         if (ok) {
             if constexpr (sizeof(TV) == 2) {

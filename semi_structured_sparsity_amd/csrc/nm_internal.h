@@ -32,20 +32,24 @@ __device__ __forceinline__ float rank_key(float x) { return (x != x) ? -__builti
 // Keep-bits of the top-N of M keys (ties to the lower index): bit i set iff
 // fewer than N members beat member i; j beats i iff key_j > key_i, or the keys
 // are equal and j < i.
+// Keys come from rank_key (never NaN), so for i < j exactly one of "i beats j"
+// (k_i >= k_j) and "j beats i" (k_j > k_i) holds: one comparison per pair.
 template <int M>
 __device__ __forceinline__ uint32_t topn_bits(const float (&k)[M], int N) {
+    int beaten[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) beaten[i] = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+#pragma unroll
+        for (int j = i + 1; j < M; ++j) {
+            const int ib = k[i] >= k[j] ? 1 : 0;
+            beaten[j] += ib;
+            beaten[i] += 1 - ib;
+        }
     uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-        int beaten = 0;
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            if (j == i) continue;
-            bool b = (j < i) ? (k[j] >= k[i]) : (k[j] > k[i]);
-            beaten += b ? 1 : 0;
-        }
-        bits |= (beaten < N ? 1u : 0u) << i;
-    }
+    for (int i = 0; i < M; ++i) bits |= (beaten[i] < N ? 1u : 0u) << i;
     return bits;
 }
 
