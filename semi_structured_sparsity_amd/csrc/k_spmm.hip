@@ -969,7 +969,43 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     return p;
 }
 
+// ------------------------------------------------------------------ 6:8 activation lift
+// The overlapping 2:4 windows of a 6:8 group (offsets 0, 2, 4 of its 8 columns)
+// multiply the lifted activation XL[m, 12q + 4w + j] = X[m, 8q + 2w + j].  For many
+// tokens it is written out once (memory-bound, 1.5x the bytes of X) so that the
+// product runs on the plain 2:4 kernels; one lane = one 8-column group.
+template <typename T>
+__global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int64_t ldx, int64_t Mtok, int64_t K,
+                                                   T* __restrict__ XL, int64_t ldl) {
+    const int64_t gpr = K / 8, total = Mtok * gpr;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += stride) {
+        const int64_t m = u / gpr, q = u - m * gpr;
+        if constexpr (sizeof(T) == 2) {
+            const uint4 v = *(const uint4*)(X + m * ldx + 8 * q);   // elements (0,1) (2,3) (4,5) (6,7)
+            uint2* o = (uint2*)(XL + m * ldl + 12 * q);
+            o[0] = make_uint2(v.x, v.y);
+            o[1] = make_uint2(v.y, v.z);
+            o[2] = make_uint2(v.z, v.w);
+        } else {
+            const uint2 v = *(const uint2*)(X + m * ldx + 8 * q);   // bytes 0-3, 4-7
+            uint32_t* o = (uint32_t*)(XL + m * ldl + 12 * q);
+            o[0] = v.x;
+            o[1] = (v.x >> 16) | (v.y << 16);
+            o[2] = v.y;
+        }
+    }
+}
+
+// 6:8 products with more than this many tokens lift X into the workspace first
+constexpr int64_t kLiftTokens = 128;
+static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
+    return ((size_t)Mtok * (size_t)(K / 8 * 12) * (size_t)es + 255) & ~(size_t)255;
+}
+
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
+    if (Ns && Mtok > kLiftTokens)
+        return lift_bytes(Mtok, K, xdt == NM_I8 ? 1 : 2) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
     SpmmPlan p = (xdt == NM_I8) ? (Ns ? plan_for<int8_t, true>(Mtok, K, R) : plan_for<int8_t, false>(Mtok, K, R))
                                 : (Ns ? plan_for<uint16_t, true>(Mtok, K, R) : plan_for<uint16_t, false>(Mtok, K, R));
     if (p.KS <= 1) return 0;
@@ -978,6 +1014,22 @@ size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
 
 template <typename T, bool LIFT>
 static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
+    if constexpr (LIFT) {
+        if (a.Mtok > kLiftTokens) {
+            const int64_t Kl = a.K / 8 * 12;
+            const size_t xl = lift_bytes(a.Mtok, a.K, sizeof(T));
+            if (!ws || ws_bytes < xl)
+                return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", xl);
+            T* XL = (T*)ws;
+            const dim3 g(grid_cap(ceil_div(a.Mtok * (a.K / 8), 256), 8192));
+            hipLaunchKernelGGL(lift_kernel<T>, g, dim3(256), 0, s, (const T*)a.X, a.ldx, a.Mtok, a.K, XL, Kl);
+            SpmmArgs b = a;
+            b.X = (const uint8_t*)XL;
+            b.ldx = Kl;
+            b.K = Kl;
+            return run_spmm<T, false>(b, (uint8_t*)ws + xl, ws_bytes - xl, s);
+        }
+    }
     // the ring kernel loads 16-byte pieces of the index rows
     const bool ring_ok = ((uintptr_t)a.idx & 15u) == 0 && (a.ldi % 4) == 0 &&
                          a.R * a.ldv * (int64_t)sizeof(T) < (1LL << 32) && a.R * a.ldi * 4 < (1LL << 32) &&
