@@ -4,11 +4,14 @@
 //
 // "SlideSparse" (sections 2A-2C): a (2N-2):2N weight is stored as overlapping
 // 2:4 windows over the lifted width K' = (2 - 2/N) K; the activation is lifted
-// to match by a pure index remap.  Here the lift happens while an activation
-// chunk is staged from global memory into LDS: 16 bytes of original columns
-// (one 8-wide group in bf16, two in int8) become 24 bytes of lifted columns
-// (windows 0-3, 2-5, 4-7 of each group), so X is read from HBM once at its
-// original size and the MFMA fragment reads stay plain 16-byte LDS loads.
+// to match by a pure index remap (windows 0-3, 2-5, 4-7 of each 8-column group).
+// Where that remap happens depends on the token count:
+//   few tokens (weight-streaming kernel): the X fragment is gathered in lifted
+//     order straight from global memory into registers;
+//   many tokens: lift_kernel writes the lifted activation once (1.5x the bytes
+//     of X, small next to the product) and the plain 2:4 kernels multiply it;
+//   the register-staged kernel (K off the ring's grid) lifts 16 original bytes
+//     into 24 lifted bytes while staging them into LDS.
 //
 // Operand layouts of the two instructions (gfx950, verified on hardware with
 // integer data):
@@ -377,13 +380,13 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // h*IG+IG-1) is loaded in IG batches of rows, one batch with each of the stages
 // (h-1)*IG+1 .. h*IG, so every stage issues the same number of loads.  Within a
 // row of a group buffer, piece c is stored at c ^ ((r>>2) & (IG-1)).
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int IG = 1>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int IG = 1>
 struct Ring {
     static constexpr int NW = WRN * WTN;               // waves per block (WRN along rows, WTN along tokens)
     static constexpr int BR = WRN * SR * 32;           // weight rows per block
     static constexpr int BT = WTN * ST * 32;           // tokens per block
     static constexpr int KO = KB / (int)sizeof(T);     // original columns per stage (KB bytes of X per token)
-    static constexpr int KL = LIFT ? KO * 3 / 2 : KO;  // lifted columns per stage (6:8: 12 per 8)
+    static constexpr int KL = KO;
     static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;
     static constexpr int ND = KL / KDEP;               // SMFMAC depths per stage
     static constexpr int AROW = KL / 2 * (int)sizeof(T);  // compressed bytes per weight row per stage
@@ -411,22 +414,13 @@ struct Ring {
     static_assert(IG == 1 || (NS == 2 && AI * 4 == 16 && (IG & (IG - 1)) == 0 && IGRP % (1024 * NW * IG) == 0),
                   "grouped index loads need NS == 2, 16 index bytes per row per stage, IG a power of two");
     static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
-    static_assert(ACH == 4 || ACH == 8 || ACH == 12, "weight-row chunk count without a swizzle");
-    static_assert(!LIFT || sizeof(T) == 2, "the lifted gather is written for bf16 activations");
+    static_assert(ACH == 4 || ACH == 8, "weight-row chunk count without a swizzle");
     // Swizzles of 16-byte chunks, so that the 16 lanes served together by a 16-byte LDS read
     // hit distinct banks (checked on the hardware with an LDS probe):
-    //   weight rows of 4 or 8 chunks: logical chunk c at c ^ swa(r);
-    //   rows of 12 chunks (lifted): logical chunk c at (c + 3 ((r >> 2) & 3)) mod 12;
-    //   X rows: logical chunk c at c ^ swb(t).
+    //   weight rows: logical chunk c at c ^ swa(r);  X rows: logical chunk c at c ^ swb(t).
     __device__ static int swa(int r) { return AROW == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
-    __device__ static int achunk(int r, int c) {     // physical chunk of logical chunk c in row r
-        if constexpr (ACH == 12) return (c + 3 * ((r >> 2) & 3)) % 12;
-        else return c ^ swa(r);
-    }
-    __device__ static int alogical(int r, int p) {   // logical chunk held by physical chunk p of row r
-        if constexpr (ACH == 12) return (p + 12 - 3 * ((r >> 2) & 3)) % 12;
-        else return p ^ swa(r);
-    }
+    __device__ static int achunk(int r, int c) { return c ^ swa(r); }      // physical chunk of logical c
+    __device__ static int alogical(int r, int p) { return p ^ swa(r); }    // logical chunk at physical p
     __device__ static int swb(int t) { return KB == 128 ? ((t >> 1) & 7) : (t & 15); }
 };
 
@@ -438,9 +432,9 @@ struct RingFrag {          // fragments of one SMFMAC depth
 };
 
 // NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
-template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, bool LIFT = false, int OCC = 1, int IG = 1>
+template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int OCC = 1, int IG = 1>
 __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs a) {
-    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN, LIFT, IG>;
+    using RG = Ring<T, SR, ST, KB, NS, WRN, WTN, IG>;
     using FR = RingFrag<SR, ST>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[RG::LDS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -556,30 +550,9 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
             const int tok = (wt * ST + j) * 32 + l32;
             const uint8_t* trow = sB + tok * KB;
             const int sw = RG::swb(tok);
-            if constexpr (!LIFT) {
-                const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ sw) * 16);
-                const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ sw) * 16);
-                f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            } else {
-                // lifted column L reads original column (L/12)*8 + 2*((L%12)/4) + L%4: the fragment is
-                // gathered window by window (4 lifted columns = 4 consecutive original ones) from the
-                // stage's original columns
-                int wv[8];
-                auto at = [&](int byte) __attribute__((always_inline)) {   // LDS address of a stage byte
-                    return trow + (((byte >> 4) ^ sw) << 4) + (byte & 15);
-                };
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-#pragma unroll
-                    for (int win = 0; win < 2; ++win) {
-                        const int Lw = 32 * d + 16 * q + 8 * h + 4 * win;
-                        const int ob = ((Lw / 12) * 8 + 2 * ((Lw % 12) / 4)) * 2;
-                        wv[q * 4 + win * 2] = *(const int*)at(ob);
-                        wv[q * 4 + win * 2 + 1] = *(const int*)at(ob + 4);
-                    }
-                }
-                f.b[j] = i32x8_t{wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]};
-            }
+            const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ sw) * 16);
+            const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ sw) * 16);
+            f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
 
@@ -911,11 +884,9 @@ struct SpmmPlan {
 //   narrow: 256 x 128 tile, 4 waves (one per SIMD), 2 stages of 256 B of X per token
 //   big   : 256 x 256 tile, 8 waves (two per SIMD), 3 stages of 128 B; bf16 only (the int8
 //           index rows of a 128-byte stage do not split over 8 waves)
-//   lift  : 128 x 128 tile, 4 waves, 2 stages of 256 B of original X per token (384 B of
-//           lifted columns), for the 6:8 sliding-window products
+// (6:8 products with many tokens run here on the lifted activation.)
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
 #define NM_RING_BIG uint16_t, 4, 2, 128, 3, 2, 4
-#define NM_RING_LIFT T, 2, 2, 256, 2, 2, 2, true
 
 template <typename T, bool LIFT>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
@@ -924,17 +895,15 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     p.large = Mtok > 128;
     using RB = Ring<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
-    using RL = Ring<uint16_t, 2, 2, 256, 2, 2, 2, true>;   // NM_RING_LIFT at bf16
-    // int8 lifted products stay on the register-gather kernel: gathering 4-byte windows of
-    // int8 X out of LDS cost more than the tile saved (measured on the 6912x2560 layer)
-    p.ring = ring_ok && p.large && (!LIFT || sizeof(T) == 2) && (K % (LIFT ? RL::KO : RN::KO)) == 0;
+    // lifted products reach here with few tokens only (more are lifted first)
+    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0;
     // the big tile moves a third fewer bytes per MAC than the narrow one but needs
     // every LDS byte of a CU; with fewer than two rounds of its tiles on 256 CUs the
     // narrow tile's finer grain balances better (measured on the 2048-token layers)
     p.big = p.ring && !LIFT && sizeof(T) == 2 && (K % RB::KO) == 0 &&
             ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
-    const int BR = p.ring ? (LIFT ? RL::BR : (p.big ? RB::BR : RN::BR)) : 128;
-    const int BT = p.ring ? (LIFT ? RL::BT : (p.big ? RB::BT : RN::BT)) : (p.large ? 128 : 32);
+    const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
+    const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
     p.tiles_t = (int)ceil_div(Mtok, BT);
     {
@@ -943,7 +912,7 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
         p.skinny = 0;
         if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
     }
-    p.nsteps = (int)ceil_div(K, p.ring ? (LIFT ? RL::KO : (p.big ? RB::KO : RN::KO)) : G::KO);
+    p.nsteps = (int)ceil_div(K, p.ring ? (p.big ? RB::KO : RN::KO) : G::KO);
     if (p.skinny) {
         // K split over blocks (partials + a fixed-order reduce) where the row tiles alone
         // leave the chip short of blocks; measured on the 4096- and 11008-row layers
@@ -1059,9 +1028,7 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     } else if (p.skinny == 3) {
         hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
-        if constexpr (LIFT) {
-            if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_LIFT>), grid, dim3(256), 0, s, a);
-        } else {
+        if constexpr (!LIFT) {
             if constexpr (sizeof(T) == 2) {
                 if (p.big) {
                     hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
@@ -1069,7 +1036,7 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
                 }
             }
             // bf16: index words loaded 4 stages at a time (whole 64-byte runs of a row)
-            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, false, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);
         }
     } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
