@@ -670,6 +670,198 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
 }
 
 
+// ------------------------------------------------------------------ K-split ring kernel (a few hundred tokens)
+// With 65..256 tokens the 256-row tiles of the ring kernel are too few to fill the
+// chip, and the weight-streaming kernel reads X from L2 in half lines once per 64
+// weight rows.  Here a block of 4 waves owns a 32*SR x 32*ST tile; each stage (KB
+// bytes of X per token, four SMFMAC depths) arrives in an NS-stage LDS ring by
+// whole-line DMA as in the ring kernel, and wave w computes depth w of every stage
+// over the whole tile.  The four partial tiles are summed through LDS in wave order.
+// gridDim.y splits the stages over blocks (partials + the fixed-order reduce kernel).
+template <typename T, int SR, int ST, int KB, int NS>
+__global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
+    constexpr int es = sizeof(T);
+    constexpr int KO = KB / es, KDEP = es == 2 ? 32 : 64;
+    static_assert(KO / KDEP == 4, "one depth per wave per stage");
+    constexpr int BR = 32 * SR, BT = 32 * ST;
+    constexpr int AROW = KO / 2 * es, ACH = AROW / 16, AI = KO / 32, BCH = KB / 16;
+    static_assert(ACH == 8 && BCH == 16, "swizzles below are for 8-chunk weight rows and 16-chunk X rows");
+    constexpr int I_OFF = BR * AROW, B_OFF = I_OFF + BR * AI * 4, STAGE = B_OFF + BT * KB;
+    constexpr int NA = BR * AROW / 1024 / 4, NI = BR * AI * 4 / 256 / 4, NB = BT * KB / 1024 / 4;
+    constexpr int PER = NA + NI + NB;   // loads per wave per stage
+    static_assert(NA >= 1 && NI >= 1 && NB >= 1 && (BR * AROW) % 4096 == 0 && (BR * AI * 4) % 1024 == 0 &&
+                      (BT * KB) % 4096 == 0,
+                  "loads must split evenly over the 4 waves");
+    constexpr int RED = 4 * 64 * 16 * 4;                // one sub-tile of all four waves
+    constexpr int LDS = NS * STAGE > RED ? NS * STAGE : RED;
+    static_assert(LDS <= 160 * 1024, "LDS ring too large");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    int tr, tt;
+    tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
+    const int64_t r0 = (int64_t)tr * BR, t0 = (int64_t)tt * BT;
+    const int split = blockIdx.y;
+    const int s_begin = split * a.steps_per_split;
+    const int s_end = (s_begin + a.steps_per_split) < a.nsteps ? (s_begin + a.steps_per_split) : a.nsteps;
+    const int nloc = s_end > s_begin ? s_end - s_begin : 0;
+    const uint32_t sbase = lds_addr(smem);
+    auto swa = [](int r) { return (r >> 1) & 7; };   // weight row r: logical chunk c at c ^ swa(r)
+    auto swb = [](int t) { return t & 15; };         // X token t: logical chunk c at c ^ swb(t)
+
+    const void* baseA = uniform_ptr(a.vals + r0 * a.ldv * es);
+    const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
+    const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
+    const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
+    uint32_t oA[NA], oI[NI], oB[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int q = (wave * NA + i) * 64 + lane;
+        const int row = q / ACH, c = (q % ACH) ^ swa(row);
+        const int64_t gr = row < rmax ? row : rmax;
+        oA[i] = (uint32_t)(gr * a.ldv * es + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int q = (wave * NI + i) * 64 + lane;   // index word of the stage's [BR, AI] block
+        const int row = q / AI, part = q % AI;
+        const int64_t gr = row < rmax ? row : rmax;
+        oI[i] = (uint32_t)(gr * a.ldi * 4 + part * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int row = (wave * NB + i) * (64 / BCH) + lane / BCH;
+        const int c = (lane % BCH) ^ swb(row);
+        const int64_t gt = row < tmax ? row : tmax;
+        oB[i] = (uint32_t)(gt * a.ldx * es + c * 16);
+    }
+    auto issue = [&](int sl) __attribute__((always_inline)) {   // local stage sl of this block's range
+        const int sg = s_begin + sl;
+        const uint32_t st = sbase + (uint32_t)((sl % NS) * STAGE);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) dma16s(st + (wave * NA + i) * 1024, baseA, oA[i] + (uint32_t)(sg * AROW));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma4s(st + I_OFF + (wave * NI + i) * 256, baseI, oI[i] + (uint32_t)(sg * AI * 4));
+#pragma unroll
+        for (int i = 0; i < NB; ++i) dma16s(st + B_OFF + (wave * NB + i) * 1024, baseB, oB[i] + (uint32_t)(sg * KB));
+    };
+    struct Frag {
+        i32x4_t a[SR];
+        uint32_t iw[SR];
+        i32x8_t b[ST];
+    };
+    const int d = wave;   // this wave's depth in every stage
+    auto read = [&](int sl, Frag& f) __attribute__((always_inline)) {
+        const uint8_t* sA = smem + (sl % NS) * STAGE;
+        const uint32_t* sI = (const uint32_t*)(sA + I_OFF);
+        const uint8_t* sB = sA + B_OFF;
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int row = i * 32 + l32;
+            f.a[i] = *(const i32x4_t*)(sA + row * AROW + ((2 * d + h) ^ swa(row)) * 16);
+            if constexpr (es == 2) f.iw[i] = sI[row * AI + d];
+            else f.iw[i] = sI[row * AI + 2 * d + h];
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int tok = j * 32 + l32;
+            const uint8_t* trow = sB + tok * KB;
+            const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ swb(tok)) * 16);
+            const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ swb(tok)) * 16);
+            f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    using AccV = typename std::conditional<es == 2, f32x16_t, i32x16_t>::type;
+    AccV acc[SR][ST];
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[i][j] = AccV{};
+    const uint32_t ish = 16u * (uint32_t)h;
+    auto mfmas = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                if constexpr (es == 2)
+                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                                         __builtin_bit_cast(bf16x16_t, f.b[j]),
+                                                                         acc[i][j], (int)(f.iw[i] >> ish), 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[i], f.b[j], acc[i][j], (int)f.iw[i], 0, 0);
+            }
+    };
+
+    // Prologue fills the ring and reads stage 0.  Step S issues the SMFMACs of stage S,
+    // waits for stage S+1 (stages S+2.. may stay in flight), meets the other waves (so
+    // stage S's slot has been read by all), refills that slot with stage S+NS and reads
+    // stage S+1 into the other fragment set.
+    Frag fa, fb;
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+        if (p < nloc) issue(p);
+    if (nloc >= NS) wait_vm_barrier<(NS - 1) * PER>();
+    else wait_vm_barrier<0>();
+    if (nloc > 0) read(0, fa);
+    auto step = [&](int S, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+        mfmas(cur);
+        if (S + 1 < nloc) {
+            if (S + NS - 1 < nloc) wait_vm_barrier<(NS - 2) * PER>();
+            else wait_vm_barrier<0>();
+            if (S + NS < nloc) issue(S + NS);
+            read(S + 1, nxt);
+        }
+    };
+    int S = 0;
+    for (; S + 1 < nloc; S += 2) {
+        step(S, fa, fb);
+        step(S + 1, fb, fa);
+    }
+    if (S < nloc) step(S, fa, fb);
+    wait_vm_all();
+
+    // The four partial tiles are summed in wave order through LDS, one 32x32 sub-tile at a
+    // time (whole-vector stores of the accumulators), by all 256 threads, which then write
+    // the outputs along the rows (or the split's partials).
+    float* red = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            __syncthreads();
+            *(AccV*)&red[(wave * 64 + lane) * 16] = acc[i][j];
+            __syncthreads();
+            for (int q = tid; q < 1024; q += 256) {
+                const int tk = q >> 5, row = q & 31;   // Y element (token, row) of the sub-tile
+                const int src_lane = tk + 32 * ((row >> 2) & 1), e = 4 * (row >> 3) + (row & 3);
+                const int64_t gt = t0 + 32 * j + tk, gr = r0 + 32 * i + row;
+                using AccS = typename std::conditional<es == 2, float, int32_t>::type;
+                AccS v = 0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
+                if (gt >= a.Mtok || gr >= a.R) continue;
+                if (a.part) {
+                    ((AccS*)a.part)[((int64_t)split * a.Mtok + gt) * a.R + gr] = v;
+                    continue;
+                }
+                const int64_t o = gt * a.ldy + gr;
+                if (a.ydt == NM_I32) {
+                    ((int32_t*)a.Y)[o] = (int32_t)v;
+                } else {
+                    float f = (float)v;
+                    if (a.scaled) {
+                        const float xs = a.x_scale ? a.x_scale[gt] : 1.0f;
+                        f = __fmul_rn(__fmul_rn(a.w_scale, xs), f);
+                    }
+                    if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
+                    else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
+                }
+            }
+        }
+}
+
 // ------------------------------------------------------------------ skinny kernel (few tokens: weight-streaming)
 // For few tokens the product is bound by the HBM stream of the packed weight.
 // A block of KSPLIT waves owns 32*SRk weight rows and 32*STk tokens; wave w
@@ -875,7 +1067,7 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
-    bool large, ring, big;
+    bool large, ring, big, mid;
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
@@ -892,6 +1084,22 @@ template <typename T, bool LIFT>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
     using G = Geo<T, LIFT>;
     SpmmPlan p{};
+    // 65..256 tokens: the K-split ring kernel on 64 x 128 tiles, with the stages split over
+    // enough blocks to give every CU a tile (each split keeps >= 4 stages)
+    {
+        constexpr int KOm = 256 / (int)sizeof(T);
+        p.mid = ring_ok && !LIFT && Mtok > 64 && Mtok <= 256 && (K % KOm) == 0;
+        if (p.mid) {
+            p.tiles_r = (int)ceil_div(R, 64);
+            p.tiles_t = (int)ceil_div(Mtok, 128);
+            p.nsteps = (int)(K / KOm);
+            int KS = 1;
+            while ((int64_t)p.tiles_r * p.tiles_t * KS < 256 && p.nsteps >= 8 * KS) KS *= 2;
+            p.steps_per_split = (int)ceil_div(p.nsteps, KS);
+            p.KS = (int)ceil_div(p.nsteps, p.steps_per_split);
+            return p;
+        }
+    }
     p.large = Mtok > 128;
     using RB = Ring<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
@@ -967,7 +1175,7 @@ __global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int6
 }
 
 // 6:8 products with more than this many tokens lift X into the workspace first
-constexpr int64_t kLiftTokens = 128;
+constexpr int64_t kLiftTokens = 64;
 static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
     return ((size_t)Mtok * (size_t)(K / 8 * 12) * (size_t)es + 255) & ~(size_t)255;
 }
@@ -1016,7 +1224,9 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         a.part = ws;
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
-    if (p.skinny == 1) {
+    if (p.mid) {
+        hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
+    } else if (p.skinny == 1) {
         // 32-row tiles, 4 waves split K, 16 depths in flight per wave
         hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
     } else if (p.skinny == 2) {
