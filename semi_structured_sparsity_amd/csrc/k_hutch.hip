@@ -164,11 +164,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------------ gemm2: D = (2/P) sum_p V_p .* (U_p X)
-// grid.x: tiles over R, grid.y: tiles over K (output columns).
-__global__ __launch_bounds__(256) void hutch_gemm2_kernel(const uint16_t* __restrict__ U, const uint16_t* __restrict__ XT,
+// grid.x: tiles over R, grid.y: tiles over K (output columns).  Two blocks per CU (the
+// register budget is held to 256 per lane), so one block's tile loads hide behind the
+// other's MFMAs.  One flat pipeline over
+// (probe, inner step): the next step's tiles (the next probe's first ones at a probe's
+// end) are loaded while the current step's MFMAs run.  At each probe's first step the
+// block's 256 Rademacher words (128 rows x 2 blocks of 64 columns) are generated once,
+// one per thread, into LDS (by probe parity, so that a wave still applying the previous
+// probe's signs is never overwritten); the probe's end applies them to G and adds into D.
+__global__ __launch_bounds__(256, 2) void hutch_gemm2_kernel(const uint16_t* __restrict__ U, const uint16_t* __restrict__ XT,
                                                           int64_t n, int64_t K, int64_t R, int P, uint64_t seed,
                                                           float* __restrict__ D, int64_t ldd) {
     __shared__ __attribute__((aligned(16))) uint8_t sm[2][2][HT * HS];  // [buf][A|B]
+    __shared__ uint64_t sV[2][2 * HT];   // [probe parity][column block][row]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wt = wave >> 1;
     const int h = lane >> 5, l32 = lane & 31;
@@ -176,71 +184,76 @@ __global__ __launch_bounds__(256) void hutch_gemm2_kernel(const uint16_t* __rest
     const int64_t col0 = (int64_t)blockIdx.y * HT;  // weight column k
     const int64_t kblocks = K / 64;
     const int nsteps = (int)(n / HK);
+    const int total = P * nsteps;
 
-    f32x16_h dacc[2][2];
+    f32x16_h dacc[2][2], acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dacc[i][j] = f32x16_h{};
+        for (int j = 0; j < 2; ++j) {
+            dacc[i][j] = f32x16_h{};
+            acc[i][j] = f32x16_h{};
+        }
 
     uint4 ra[4], rb[4];
-    for (int p = 0; p < P; ++p) {
-        const uint16_t* Up = U + (int64_t)p * R * n;
-        f32x16_h acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_h{};
-        load_tile(Up, n, R, row0, 0, ra);
-        load_tile(XT, n, K, col0, 0, rb);
-        store_tile(sm[0][0], ra);
-        store_tile(sm[0][1], rb);
-        __syncthreads();
-        for (int s = 0; s < nsteps; ++s) {
-            const bool more = s + 1 < nsteps;
-            if (more) {
-                load_tile(Up, n, R, row0, (int64_t)(s + 1) * HK, ra);
-                load_tile(XT, n, K, col0, (int64_t)(s + 1) * HK, rb);
-            }
-            const uint8_t* a = sm[s & 1][0];
-            const uint8_t* b = sm[s & 1][1];
-#pragma unroll
-            for (int d = 0; d < HK / 16; ++d) {
-                uint4 fa[2], fb[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) fa[i] = *(const uint4*)(a + ((wr * 2 + i) * 32 + l32) * HS + d * 32 + h * 16);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) fb[j] = *(const uint4*)(b + ((wt * 2 + j) * 32 + l32) * HS + d * 32 + h * 16);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_h, fa[i]),
-                                                                            __builtin_bit_cast(bf16x8_h, fb[j]),
-                                                                            acc[i][j], 0, 0, 0);
-            }
-            if (more) {
-                store_tile(sm[(s + 1) & 1][0], ra);
-                store_tile(sm[(s + 1) & 1][1], rb);
-            }
-            __syncthreads();
+    auto load = [&](int t) __attribute__((always_inline)) {
+        const int p = t / nsteps, s = t - p * nsteps;
+        load_tile(U + (int64_t)p * R * n, n, R, row0, (int64_t)s * HK, ra);
+        load_tile(XT, n, K, col0, (int64_t)s * HK, rb);
+    };
+    load(0);
+    store_tile(sm[0][0], ra);
+    store_tile(sm[0][1], rb);
+    for (int t = 0; t < total; ++t) {
+        const int p = t / nsteps, s = t - p * nsteps;
+        if (s == 0) {   // this probe's sign words (read at its last step, after at least one barrier)
+            const int64_t o = row0 + (tid & (HT - 1)), oc = o < R ? o : R - 1;
+            const int64_t kb = (col0 >> 6) + (tid >> 7);
+            sV[p & 1][tid] = rad_word(seed, p, oc, kb < kblocks ? kb : kblocks - 1, kblocks);
         }
-        // D += V_p .* G for this probe; lane holds column k = col0 + .. + l32
+        __syncthreads();
+        const bool more = t + 1 < total;
+        if (more) load(t + 1);
+        const uint8_t* a = sm[t & 1][0];
+        const uint8_t* b = sm[t & 1][1];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t k = col0 + (wt * 2 + j) * 32 + l32;
-            const int64_t kc = k < K ? k : K - 1;
-            const int kb = (int)(kc >> 6), kbit = (int)(kc & 63);
+        for (int d = 0; d < HK / 16; ++d) {
+            uint4 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = *(const uint4*)(a + ((wr * 2 + i) * 32 + l32) * HS + d * 32 + h * 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[j] = *(const uint4*)(b + ((wt * 2 + j) * 32 + l32) * HS + d * 32 + h * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_h, fa[i]),
+                                                                        __builtin_bit_cast(bf16x8_h, fb[j]),
+                                                                        acc[i][j], 0, 0, 0);
+        }
+        if (s == nsteps - 1) {
+            // D += V_p .* G: lane holds columns k = col0 + wt*64 + j*32 + l32 (one 64-column
+            // block per wave column: word block wt, bit j*32 + l32) and rows 8(e/4)+4h+e%4
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    int64_t o = row0 + (wr * 2 + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-                    o = o < R ? o : R - 1;
-                    const uint64_t w = rad_word(seed, p, o, kb, kblocks);
-                    const float g = acc[i][j][e];
-                    dacc[i][j][e] += ((w >> kbit) & 1ull) ? -g : g;
+                    const int orow = (wr * 2 + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                    const uint64_t w = sV[p & 1][wt * HT + orow];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float g = acc[i][j][e];
+                        dacc[i][j][e] += ((w >> (j * 32 + l32)) & 1ull) ? -g : g;
+                    }
                 }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_h{};
+        }
+        if (more) {
+            store_tile(sm[(t + 1) & 1][0], ra);
+            store_tile(sm[(t + 1) & 1][1], rb);
         }
     }
     const float scale = 2.0f / (float)P;
