@@ -216,7 +216,7 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
  *   Requires K % 16 == 0 (Ns == 0) or K % 8 == 0 (Ns == 4).
  *   int8 requires K' * 127 * 127 < 2^31 so that int32 accumulation is exact.
  * ws: nm_spmm_workspace(...) bytes: 0 for most plain 2:4 shapes; split-K partials for
- * few tokens on few rows; for 6:8 with more than 32 tokens, the lifted activation
+ * few tokens on few rows; for 6:8, the lifted activation
  * [Mtok, K'] that the plain kernels then multiply. */
 size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
 nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,

@@ -670,10 +670,10 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
 }
 
 
-// ------------------------------------------------------------------ K-split ring kernel (a few hundred tokens)
-// With 33..256 tokens the 256-row tiles of the ring kernel are too few to fill the
-// chip, and the weight-streaming kernel reads X from L2 in half lines once per 64
-// weight rows.  Here a block of 4 waves owns a 32*SR x 32*ST tile; each stage (KB
+// ------------------------------------------------------------------ K-split ring kernel (up to 256 tokens)
+// With up to 256 tokens the 256-row tiles of the ring kernel are too few to fill the
+// chip, and a weight-streaming kernel that loads SMFMAC fragments straight from
+// memory touches a 128-byte line for every 32 bytes of weight (one row per lane).  Here a block of 4 waves owns a 32*SR x 32*ST tile; each stage (KB
 // bytes of X per token, four SMFMAC depths) arrives in an NS-stage LDS ring by
 // whole-line DMA as in the ring kernel, and wave w computes depth w of every stage
 // over the whole tile.  The four partial tiles are summed through LDS in wave order.
@@ -1068,7 +1068,7 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
     bool large, ring, big;
-    int mid;     // K-split ring: 0 none, else token sub-tiles per block (2: 64 tokens, 4: 128)
+    int mid;     // K-split ring: 0 none, else 32-token sub-tiles per block (1, 2 or 4)
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
@@ -1085,19 +1085,20 @@ template <typename T, bool LIFT>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
     using G = Geo<T, LIFT>;
     SpmmPlan p{};
-    // 33..256 tokens: the K-split ring kernel on 64 x 64 (<= 64 tokens) or 64 x 128 tiles,
-    // with the stages split over enough blocks to give every CU a tile (each split keeps
-    // >= 4 stages)
+    // up to 256 tokens: the K-split ring kernel on 64 x 32, 64 x 64 or 64 x 128 tiles, with
+    // the stages split over blocks while fewer than 160 tiles would run (each split keeps
+    // >= 4 stages; measured on the 4096- and 11008-row layers: 64 tiles run best in 4
+    // splits, 172 tiles unsplit, as the partials' reduce costs more than it gains there)
     {
         constexpr int KOm = 256 / (int)sizeof(T);
-        const bool mid = ring_ok && !LIFT && Mtok > 32 && Mtok <= 256 && (K % KOm) == 0;
-        p.mid = mid ? (Mtok <= 64 ? 2 : 4) : 0;
+        const bool mid = ring_ok && !LIFT && Mtok <= 256 && (K % KOm) == 0;
+        p.mid = mid ? (Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 4)) : 0;
         if (p.mid) {
             p.tiles_r = (int)ceil_div(R, 64);
             p.tiles_t = (int)ceil_div(Mtok, 32 * p.mid);
             p.nsteps = (int)(K / KOm);
             int KS = 1;
-            while ((int64_t)p.tiles_r * p.tiles_t * KS < 256 && p.nsteps >= 8 * KS) KS *= 2;
+            while ((int64_t)p.tiles_r * p.tiles_t * KS < 160 && p.nsteps >= 8 * KS) KS *= 2;
             p.steps_per_split = (int)ceil_div(p.nsteps, KS);
             p.KS = (int)ceil_div(p.nsteps, p.steps_per_split);
             return p;
@@ -1177,8 +1178,10 @@ __global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int6
     }
 }
 
-// 6:8 products with more than this many tokens lift X into the workspace first
-constexpr int64_t kLiftTokens = 32;
+// 6:8 products with more than this many tokens lift X into the workspace first (all of
+// them: the plain kernels on the lifted activation beat the in-kernel gathers at every
+// token count measured)
+constexpr int64_t kLiftTokens = 0;
 static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
     return ((size_t)Mtok * (size_t)(K / 8 * 12) * (size_t)es + 255) & ~(size_t)255;
 }
@@ -1228,7 +1231,8 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
     if (p.mid) {
-        if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3>), grid, dim3(256), 0, s, a);
+        if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 3>), grid, dim3(256), 0, s, a);
+        else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
     } else if (p.skinny == 1) {
         // 32-row tiles, 4 waves split K, 16 depths in flight per wave
