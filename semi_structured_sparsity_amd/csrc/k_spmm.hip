@@ -5,13 +5,10 @@
 // "SlideSparse" (sections 2A-2C): a (2N-2):2N weight is stored as overlapping
 // 2:4 windows over the lifted width K' = (2 - 2/N) K; the activation is lifted
 // to match by a pure index remap (windows 0-3, 2-5, 4-7 of each 8-column group).
-// Where that remap happens depends on the token count:
-//   few tokens (weight-streaming kernel): the X fragment is gathered in lifted
-//     order straight from global memory into registers;
-//   many tokens: lift_kernel writes the lifted activation once (1.5x the bytes
-//     of X, small next to the product) and the plain 2:4 kernels multiply it;
-//   the register-staged kernel (K off the ring's grid) lifts 16 original bytes
-//     into 24 lifted bytes while staging them into LDS.
+// Here lift_kernel writes the lifted activation once into the workspace (1.5x the
+// bytes of X, small next to the product) and the plain 2:4 kernels multiply it;
+// that measured faster than gathering lifted fragments inside the product kernels
+// at every token count tried.
 //
 // Operand layouts of the two instructions (gfx950, verified on hardware with
 // integer data):
@@ -54,25 +51,25 @@ struct SpmmArgs {
     int tiles_r, tiles_t;
 };
 
-// Per-(T, lift) step geometry.  A step stages 128 bytes of original activation
-// columns per token; LIFT (6:8 via N = 4) expands them to 192 lifted bytes.
-template <typename T, bool LIFT>
+// Per-dtype step geometry of the register-staged kernel: a step stages 128 bytes of
+// activation columns per token.
+template <typename T>
 struct Geo {
-    static constexpr int KO = 128 / (int)sizeof(T);           // original columns per step
-    static constexpr int KL = LIFT ? KO * 3 / 2 : KO;          // lifted columns per step
-    static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;      // lifted K per instruction
+    static constexpr int KO = 128 / (int)sizeof(T);           // columns per step
+    static constexpr int KL = KO;
+    static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;      // K per instruction
     static constexpr int ND = KL / KDEP;                       // instructions per step
     static constexpr int AV = KL / 2 * (int)sizeof(T);         // compressed bytes per row per step
     static constexpr int AI = KL / 32;                         // index words per row per step
-    static constexpr int BV = KL * (int)sizeof(T);             // lifted bytes per token per step
+    static constexpr int BV = KL * (int)sizeof(T);             // bytes per token per step
     static constexpr int AVS = AV + 16;                        // LDS row strides (padded)
     static constexpr int AIS = AI | 1;
     static constexpr int BS = BV + 16;
 };
 
-template <typename T, bool LIFT, int WR, int WT, int SR, int ST>
+template <typename T, int WR, int WT, int SR, int ST>
 struct Tile {
-    using G = Geo<T, LIFT>;
+    using G = Geo<T>;
     static constexpr int NT = WR * WT * 64;
     static constexpr int BR = WR * SR * 32;
     static constexpr int BT = WT * ST * 32;
@@ -106,10 +103,10 @@ __device__ __forceinline__ void tile_of(int bid, int nb, int tiles_r, int tiles_
     tt = in / gsz;
 }
 
-template <typename T, bool LIFT, int WR, int WT, int SR, int ST>
+template <typename T, int WR, int WT, int SR, int ST>
 __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
-    using G = Geo<T, LIFT>;
-    using TL = Tile<T, LIFT, WR, WT, SR, ST>;
+    using G = Geo<T>;
+    using TL = Tile<T, WR, WT, SR, ST>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -194,24 +191,7 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
             const int c = tid + p * TL::NT;
             if (c < TL::NB) {
                 const int row = c / 8, part = c % 8;
-                if constexpr (!LIFT) {
-                    *(uint4*)(sB + row * G::BS + part * 16) = rb[p];
-                } else {
-                    // 16 original bytes -> 24 lifted bytes (windows 0-3, 2-5, 4-7 of each 8-group)
-                    const uint4 q = rb[p];
-                    uint2* d = (uint2*)(sB + row * G::BS + part * 24);
-                    if constexpr (sizeof(T) == 2) {
-                        d[0] = make_uint2(q.x, q.y);
-                        d[1] = make_uint2(q.y, q.z);
-                        d[2] = make_uint2(q.z, q.w);
-                    } else {
-                        const uint32_t m0 = (q.x >> 16) | (q.y << 16);
-                        const uint32_t m1 = (q.z >> 16) | (q.w << 16);
-                        d[0] = make_uint2(q.x, m0);
-                        d[1] = make_uint2(q.y, q.z);
-                        d[2] = make_uint2(m1, q.w);
-                    }
-                }
+                *(uint4*)(sB + row * G::BS + part * 16) = rb[p];
             }
         }
     };
@@ -869,53 +849,21 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
 // index words and the X fragments straight from global memory into registers
 // (X is small and stays in L2).  The KSPLIT partial tiles are then summed
 // through LDS in wave order (deterministic) and written out.
-// With LIFT the X fragment is gathered in lifted order: lifted column L reads
-// original column (L / 4(N-1)) * 2N + 2 * ((L % 4(N-1)) / 4) + L % 4, in windows
-// of 4 consecutive original columns (N = 4 here: 12 lifted per 8 original).
-template <typename T, bool LIFT>
-__device__ __forceinline__ int lift_col(int L) {
-    if constexpr (!LIFT) return L;
-    else return (L / 12) * 8 + 2 * ((L % 12) / 4) + (L & 3);
-}
-
-template <typename T, bool LIFT>
-__device__ __forceinline__ i32x8_t load_xfrag(const uint8_t* xrow, int Lbase, int h) {
-    // element e of the fragment is lifted column Lbase + KE*(e/(EL/2)) + (EL/2)*h + e%(EL/2), where
+template <typename T>
+__device__ __forceinline__ i32x8_t load_xfrag(const uint8_t* xrow, int Kbase, int h) {
+    // element e of the fragment is column Kbase + KE*(e/(EL/2)) + (EL/2)*h + e%(EL/2), where
     // bf16: EL = 16 elements (KE = 16), int8: EL = 32 elements (KE = 32)
     constexpr int es = sizeof(T);
     constexpr int HALF = 16 / es;  // elements per 16-byte half
-    i32x8_t r;
-    if constexpr (!LIFT) {
-        const i32x4_t lo = *(const i32x4_t*)(xrow + (int64_t)(Lbase + HALF * h) * es);
-        const i32x4_t hi = *(const i32x4_t*)(xrow + (int64_t)(Lbase + 2 * HALF + HALF * h) * es);
-        r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-        uint32_t w[8];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int L0 = Lbase + q * 2 * HALF + HALF * h;   // 16 bytes of lifted columns = HALF elements
-#pragma unroll
-            for (int win = 0; win < HALF / 4; ++win) {
-                const int oc = lift_col<T, true>(L0 + 4 * win);  // window start (even column)
-                if constexpr (es == 2) {
-                    const uint32_t* p = (const uint32_t*)(xrow + (int64_t)oc * 2);
-                    w[q * 4 + 2 * win] = p[0];
-                    w[q * 4 + 2 * win + 1] = p[1];
-                } else {
-                    const uint16_t* p = (const uint16_t*)(xrow + oc);
-                    w[q * 4 + win] = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
-                }
-            }
-        }
-        r = i32x8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    }
-    return r;
+    const i32x4_t lo = *(const i32x4_t*)(xrow + (int64_t)(Kbase + HALF * h) * es);
+    const i32x4_t hi = *(const i32x4_t*)(xrow + (int64_t)(Kbase + 2 * HALF + HALF * h) * es);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <typename T, bool LIFT, int SRk, int STk, int KSPLIT, int U>
+template <typename T, int SRk, int STk, int KSPLIT, int U>
 __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
     constexpr int es = sizeof(T);
-    constexpr int KDEP = es == 2 ? 32 : 64;      // lifted columns per SMFMAC
+    constexpr int KDEP = es == 2 ? 32 : 64;      // columns per SMFMAC
     __shared__ float red[KSPLIT * 64 * 16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -924,7 +872,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
     // column always covers every token (32 * STk >= Mtok)
     const int64_t r0 = (int64_t)blockIdx.x * (32 * SRk), t0 = 0;
     const int split = blockIdx.y;
-    const int64_t Kl = a.comp_bytes * 2 / es;     // lifted width
+    const int64_t Kl = a.comp_bytes * 2 / es;     // multiplied width
     const int D = (int)(Kl / KDEP);
     const int Db = (D + (int)gridDim.y - 1) / (int)gridDim.y;
     const int bd0 = split * Db < D ? split * Db : D, bd1 = bd0 + Db < D ? bd0 + Db : D;
@@ -975,7 +923,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                 else fi[u][i] = irow[i][2 * dd + h];
             }
 #pragma unroll
-            for (int j = 0; j < STk; ++j) fb[u][j] = load_xfrag<T, LIFT>(xrow[j], dd * KDEP, h);
+            for (int j = 0; j < STk; ++j) fb[u][j] = load_xfrag<T>(xrow[j], dd * KDEP, h);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the SMFMACs
 #pragma unroll
@@ -1081,9 +1029,9 @@ struct SpmmPlan {
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
 #define NM_RING_BIG uint16_t, 4, 2, 128, 3, 2, 4
 
-template <typename T, bool LIFT>
+template <typename T>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
-    using G = Geo<T, LIFT>;
+    using G = Geo<T>;
     SpmmPlan p{};
     // up to 256 tokens: the K-split ring kernel on 64 x 32, 64 x 64 or 64 x 128 tiles, with
     // the stages split over blocks while fewer than 160 tiles would run (each split keeps
@@ -1091,7 +1039,7 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     // splits, 172 tiles unsplit, as the partials' reduce costs more than it gains there)
     {
         constexpr int KOm = 256 / (int)sizeof(T);
-        const bool mid = ring_ok && !LIFT && Mtok <= 256 && (K % KOm) == 0;
+        const bool mid = ring_ok && Mtok <= 256 && (K % KOm) == 0;
         p.mid = mid ? (Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 4)) : 0;
         if (p.mid) {
             p.tiles_r = (int)ceil_div(R, 64);
@@ -1107,12 +1055,11 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     p.large = Mtok > 128;
     using RB = Ring<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
-    // lifted products reach here with few tokens only (more are lifted first)
-    p.ring = ring_ok && p.large && !LIFT && (K % RN::KO) == 0;
+    p.ring = ring_ok && p.large && (K % RN::KO) == 0;
     // the big tile moves a third fewer bytes per MAC than the narrow one but needs
     // every LDS byte of a CU; with fewer than two rounds of its tiles on 256 CUs the
     // narrow tile's finer grain balances better (measured on the 2048-token layers)
-    p.big = p.ring && !LIFT && sizeof(T) == 2 && (K % RB::KO) == 0 &&
+    p.big = p.ring && sizeof(T) == 2 && (K % RB::KO) == 0 &&
             ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
     const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
     const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
@@ -1120,9 +1067,8 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     p.tiles_t = (int)ceil_div(Mtok, BT);
     {
         constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;
-        const int64_t Kl = LIFT ? K / 8 * 12 : K;
         p.skinny = 0;
-        if (!p.large && Kl % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
+        if (!p.large && K % KDEP == 0) p.skinny = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 3);
     }
     p.nsteps = (int)ceil_div(K, p.ring ? (p.big ? RB::KO : RN::KO) : G::KO);
     if (p.skinny) {
@@ -1178,46 +1124,27 @@ __global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int6
     }
 }
 
-// 6:8 products with more than this many tokens lift X into the workspace first (all of
-// them: the plain kernels on the lifted activation beat the in-kernel gathers at every
-// token count measured)
-constexpr int64_t kLiftTokens = 0;
+// 6:8 products lift X into the workspace first: the plain kernels on the lifted
+// activation beat in-kernel gathers at every token count measured
 static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
     return ((size_t)Mtok * (size_t)(K / 8 * 12) * (size_t)es + 255) & ~(size_t)255;
 }
 
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
-    if (Ns && Mtok > kLiftTokens)
-        return lift_bytes(Mtok, K, xdt == NM_I8 ? 1 : 2) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
-    SpmmPlan p = (xdt == NM_I8) ? (Ns ? plan_for<int8_t, true>(Mtok, K, R) : plan_for<int8_t, false>(Mtok, K, R))
-                                : (Ns ? plan_for<uint16_t, true>(Mtok, K, R) : plan_for<uint16_t, false>(Mtok, K, R));
+    if (Ns) return lift_bytes(Mtok, K, xdt == NM_I8 ? 1 : 2) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
+    SpmmPlan p = (xdt == NM_I8) ? plan_for<int8_t>(Mtok, K, R) : plan_for<uint16_t>(Mtok, K, R);
     if (p.KS <= 1) return 0;
     return (size_t)p.KS * (size_t)Mtok * (size_t)R * 4;
 }
 
-template <typename T, bool LIFT>
+// plain 2:4 product of X [Mtok, K] (K = the lifted width for 6:8)
+template <typename T>
 static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
-    if constexpr (LIFT) {
-        if (a.Mtok > kLiftTokens) {
-            const int64_t Kl = a.K / 8 * 12;
-            const size_t xl = lift_bytes(a.Mtok, a.K, sizeof(T));
-            if (!ws || ws_bytes < xl)
-                return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", xl);
-            T* XL = (T*)ws;
-            const dim3 g(grid_cap(ceil_div(a.Mtok * (a.K / 8), 256), 8192));
-            hipLaunchKernelGGL(lift_kernel<T>, g, dim3(256), 0, s, (const T*)a.X, a.ldx, a.Mtok, a.K, XL, Kl);
-            SpmmArgs b = a;
-            b.X = (const uint8_t*)XL;
-            b.ldx = Kl;
-            b.K = Kl;
-            return run_spmm<T, false>(b, (uint8_t*)ws + xl, ws_bytes - xl, s);
-        }
-    }
     // the ring kernel loads 16-byte pieces of the index rows
     const bool ring_ok = ((uintptr_t)a.idx & 15u) == 0 && (a.ldi % 4) == 0 &&
                          a.R * a.ldv * (int64_t)sizeof(T) < (1LL << 32) && a.R * a.ldi * 4 < (1LL << 32) &&
                          a.Mtok * a.ldx * (int64_t)sizeof(T) < (1LL << 32);
-    const SpmmPlan p = plan_for<T, LIFT>(a.Mtok, a.K, a.R, ring_ok);
+    const SpmmPlan p = plan_for<T>(a.Mtok, a.K, a.R, ring_ok);
     a.nsteps = p.nsteps;
     a.KS = p.KS;
     a.steps_per_split = p.steps_per_split;
@@ -1236,17 +1163,17 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         else hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
     } else if (p.skinny == 1) {
         // 32-row tiles, 4 waves split K, 16 depths in flight per wave
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
     } else if (p.skinny == 2) {
         // two 32-row tiles per wave share each X fragment when that still leaves >= 200 blocks
         if (ceil_div(a.R, 64) >= 200)
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, 2, 2, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 1, 2, 4, 8>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((spmm_skinny_kernel<T, 1, 2, 4, 8>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
     } else if (p.skinny == 3) {
-        hipLaunchKernelGGL((spmm_skinny_kernel<T, LIFT, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_skinny_kernel<T, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
-        if constexpr (!LIFT) {
+        {
             if constexpr (sizeof(T) == 2) {
                 if (p.big) {
                     hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
@@ -1257,9 +1184,9 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
             hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);
         }
     } else if (p.large)
-        hipLaunchKernelGGL((spmm_kernel<T, LIFT, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_kernel<T, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((spmm_kernel<T, LIFT, 4, 1, 1, 1>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((spmm_kernel<T, 4, 1, 1, 1>), grid, dim3(256), 0, s, a);
     if (p.KS > 1) {
         const int64_t total = a.Mtok * a.R;
         const dim3 g(grid_cap(ceil_div(total, 256), 8192));
@@ -1293,8 +1220,23 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
     a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
     a.ydt = (int)ydt;
     if (Mtok == 0 || R == 0) return NM_OK;
-    if (xdt == NM_I8) return Ns ? run_spmm<int8_t, true>(a, ws, ws_bytes, s) : run_spmm<int8_t, false>(a, ws, ws_bytes, s);
-    return Ns ? run_spmm<uint16_t, true>(a, ws, ws_bytes, s) : run_spmm<uint16_t, false>(a, ws, ws_bytes, s);
+    if (Ns) {
+        // 6:8: lift X into the workspace, then the plain product over the lifted width
+        const size_t xl = lift_bytes(Mtok, K, es);
+        if (!ws || ws_bytes < xl) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", xl);
+        const dim3 g(grid_cap(ceil_div(Mtok * (K / 8), 256), 8192));
+        if (xdt == NM_I8)
+            hipLaunchKernelGGL(lift_kernel<int8_t>, g, dim3(256), 0, s, (const int8_t*)X, ldx, Mtok, K, (int8_t*)ws, Kl);
+        else
+            hipLaunchKernelGGL(lift_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, ldx, Mtok, K,
+                               (uint16_t*)ws, Kl);
+        a.X = (const uint8_t*)ws;
+        a.ldx = Kl;
+        a.K = Kl;
+        ws = (uint8_t*)ws + xl;
+        ws_bytes -= xl;
+    }
+    return xdt == NM_I8 ? run_spmm<int8_t>(a, ws, ws_bytes, s) : run_spmm<uint16_t>(a, ws, ws_bytes, s);
 }
 
 }  // namespace nm
