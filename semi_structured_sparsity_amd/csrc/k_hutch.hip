@@ -65,7 +65,10 @@ __device__ __forceinline__ void store_tile(uint8_t* s, const uint4 (&r)[4]) {
 }
 
 // ------------------------------------------------------------------ gemm1: U = V X^T
-// grid.x: tiles over P*R stacked probe rows, grid.y: tiles over n.
+// grid.x: tiles of 64*SR stacked probe rows, grid.y: tiles of 128 over n.  V is made
+// in registers, so only X is loaded; SR row sub-tiles per wave reuse each X fragment
+// SR times.
+template <int SR>
 __global__ __launch_bounds__(256) void hutch_gemm1_kernel(const uint16_t* __restrict__ X, int64_t ldx, int64_t n,
                                                           int64_t K, int64_t R, int P, uint64_t seed,
                                                           uint16_t* __restrict__ U) {
@@ -73,27 +76,27 @@ __global__ __launch_bounds__(256) void hutch_gemm1_kernel(const uint16_t* __rest
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wt = wave >> 1;
     const int h = lane >> 5, l32 = lane & 31;
-    const int64_t row0 = (int64_t)blockIdx.x * HT;  // stacked row index p*R + o
-    const int64_t col0 = (int64_t)blockIdx.y * HT;  // calibration row i
+    const int64_t row0 = (int64_t)blockIdx.x * (64 * SR);  // stacked row index p*R + o
+    const int64_t col0 = (int64_t)blockIdx.y * HT;          // calibration row i
     const int64_t PR = (int64_t)P * R;
     const int64_t kblocks = K / 64;
 
-    // the two A sub-tile rows this lane generates
-    int pr[2];
-    int64_t orow[2];
-    bool rvalid[2];
+    // the SR A sub-tile rows this lane generates
+    int pr[SR];
+    int64_t orow[SR];
+    bool rvalid[SR];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t sr = row0 + (wr * 2 + i) * 32 + l32;
+    for (int i = 0; i < SR; ++i) {
+        const int64_t sr = row0 + (wr * SR + i) * 32 + l32;
         rvalid[i] = sr < PR;
         const int64_t srr = rvalid[i] ? sr : 0;
         pr[i] = (int)(srr / R);
         orow[i] = srr - (int64_t)pr[i] * R;
     }
 
-    f32x16_h acc[2][2];
+    f32x16_h acc[SR][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SR; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_h{};
 
@@ -106,9 +109,9 @@ __global__ __launch_bounds__(256) void hutch_gemm1_kernel(const uint16_t* __rest
         const bool more = s + 1 < nsteps;
         if (more) load_tile(X, ldx, n, col0, (int64_t)(s + 1) * HK, rb);
         const uint8_t* b = sB[s & 1];
-        uint64_t word[2];
+        uint64_t word[SR];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) word[i] = rad_word(seed, pr[i], orow[i], s, kblocks);
+        for (int i = 0; i < SR; ++i) word[i] = rad_word(seed, pr[i], orow[i], s, kblocks);
 #pragma unroll
         for (int d = 0; d < HK / 16; ++d) {
             uint4 fb[2];
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(256) void hutch_gemm1_kernel(const uint16_t* __rest
                 fb[j] = *(const uint4*)(b + tok * HS + d * 32 + h * 16);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < SR; ++i) {
                 const uint32_t byte = (uint32_t)(word[i] >> (16 * d + 8 * h)) & 0xffu;
                 const bf16x8_h av = __builtin_bit_cast(bf16x8_h, signs_to_bf16x8(byte));
 #pragma unroll
@@ -132,14 +135,14 @@ __global__ __launch_bounds__(256) void hutch_gemm1_kernel(const uint16_t* __rest
     }
     // store U (bf16, round to nearest even): lane holds column i = l32, rows 8(e/4)+4h+e%4
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SR; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t ci = col0 + (wt * 2 + j) * 32 + l32;
             if (ci >= n) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t sr = row0 + (wr * 2 + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
+                const int64_t sr = row0 + (wr * SR + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
                 if (sr < PR) U[sr * n + ci] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
             }
         }
@@ -280,7 +283,8 @@ void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t
     uint16_t* U = (uint16_t*)ws;
     uint16_t* XT = U + (size_t)probes * (size_t)R * (size_t)n;
     const uint16_t* Xb = (const uint16_t*)X;
-    hipLaunchKernelGGL(hutch_gemm1_kernel, dim3((unsigned)ceil_div((int64_t)probes * R, HT), (unsigned)ceil_div(n, HT)),
+    constexpr int SR1 = 2;   // 128 stacked rows per block (256 measured no faster: the sign generation bounds it)
+    hipLaunchKernelGGL(hutch_gemm1_kernel<SR1>, dim3((unsigned)ceil_div((int64_t)probes * R, 64 * SR1), (unsigned)ceil_div(n, HT)),
                        dim3(256), 0, s, Xb, ldx, n, K, R, probes, seed, U);
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 64), (unsigned)ceil_div(n, 64)), dim3(256), 0, s,
                        Xb, ldx, n, K, XT);
