@@ -203,12 +203,13 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
 /* ---------------------------------------------------------------- sparse GEMM
  * Structured-sparse linear layer Y = X * W_hat^T on packed weights
  * ("SlideSparse", sections 2B-2C: the lifted activation is an index remap,
- * applied while the activation tile is staged; the product then runs on 2:4
- * sparse matrix instructions).  Runs on gfx950 SMFMAC (the packed weight is
- * the sparse operand).
+ * written once into the workspace here; the product then runs on 2:4 sparse
+ * matrix instructions).  Runs on gfx950 SMFMAC (the packed weight is the
+ * sparse operand).
  *   X: [Mtok, K] (ldx elements), K the ORIGINAL input width.
  *   vals/idx: 2:4 packed weight over K (Ns == 0) or over the lifted width
- *   K' = (2 - 2/Ns) K (Ns >= 3; supported Ns == 4, i.e. 6:8), rows R.
+ *   K' = (2 - 2/Ns) K (Ns >= 3; supported Ns == 4, i.e. 6:8), rows R;
+ *   ldv >= K'/2, ldi >= ceil(K'/32).
  *   xdt/vdt: BF16/BF16 (f32 accumulation) or I8/I8 (exact int32 accumulation).
  *   ydt: for BF16 inputs BF16 or F32; for I8 inputs I32 (raw sums), F32 or BF16.
  *   Float outputs are y = acc when x_scale == NULL and w_scale == 1, else

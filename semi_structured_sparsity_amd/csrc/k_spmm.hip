@@ -43,7 +43,7 @@ struct SpmmArgs {
     int64_t ldx, ldv, ldi, ldy;
     int64_t Mtok, K, R;
     int64_t comp_bytes;    // packed value bytes per row (K'/2 * sizeof(T))
-    int64_t idx_words;     // index words per row (K'/32: two 2-bit fields per 4 lifted columns)
+    int64_t idx_words;     // index words per row (ceil(K'/32): two 2-bit fields per 4 lifted columns)
     float w_scale;
     int scaled;
     int ydt;
@@ -1215,7 +1215,7 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
     const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
     const int64_t es = xdt == NM_I8 ? 1 : 2;
     a.comp_bytes = Kl / 2 * es;
-    a.idx_words = Kl / 32;
+    a.idx_words = (Kl + 31) / 32;   // the bitstream's last word is partial when K' % 32 == 16
     a.w_scale = w_scale;
     a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
     a.ydt = (int)ydt;

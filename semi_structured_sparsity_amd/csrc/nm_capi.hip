@@ -365,13 +365,14 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
     if (K == 0) return set_error(NM_ERR_SHAPE, "%s: K == 0", fn);
     NM_REQ(X && vals && idx, NM_ERR_NULL, "%s: NULL input", fn);
     const int64_t es = esize(xdt);
-    NM_REQ(ldx >= K && ldv >= Kl / 2 && ldi >= Kl / 32, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    const int64_t iw = (Kl + 31) / 32;   // index words per row
+    NM_REQ(ldx >= K && ldv >= Kl / 2 && ldi >= iw, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
     NM_REQ(aligned16(X) && aligned16(vals) && (ldx * es) % 16 == 0 && (ldv * es) % 16 == 0, NM_ERR_ALIGN,
            "%s: X and vals must be 16-byte aligned with 16-byte row strides", fn);
     NM_REQ(((uintptr_t)idx & 3u) == 0, NM_ERR_ALIGN, "%s: idx must be 4-byte aligned", fn);
     const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
     NM_REQ(!overlap(ry, span(X, Mtok, K, ldx, es)) && !overlap(ry, span(vals, R, Kl / 2, ldv, es)) &&
-               !overlap(ry, span(idx, R, Kl / 32, ldi, 4)) && !overlap(ry, span(x_scale, 1, Mtok, Mtok, 4)),
+               !overlap(ry, span(idx, R, iw, ldi, 4)) && !overlap(ry, span(x_scale, 1, Mtok, Mtok, 4)),
            NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
     const size_t need = spmm_ws(Mtok, K, R, Ns, xdt);
     NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);

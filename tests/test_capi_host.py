@@ -65,6 +65,8 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, r.nm_spmm(S, 1, 4, 40, 40, S, 1, S, 8, 20, 4, 0, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
     big = 1 << 20
     assert _st(nm, r.nm_spmm(S, 2, 4, big, big, S, 2, S, 8, big, big, 0, None, 1.0, Y, 3, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    # 6:8 over K = 96: lifted width 144 -> 4.5 index words per row, so ldi = 4 is too small
+    assert _st(nm, r.nm_spmm(S, 1, 4, 96, 96, S, 1, S, 8, 72, 4, 4, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
     # misaligned activation pointer
     assert _st(nm, r.nm_spmm(ctypes.c_void_p(0x1002), 1, 4, 64, 64, S, 1, S, 8, 32, 4, 0, None, 1.0, Y, 1, 8, None, 0,
                              None)) == "NM_ERR_ALIGN"

@@ -50,6 +50,7 @@ SHAPES = [  # (tokens, R, K): few-token kernel (with and without a K split over 
     (1, 64, 256), (16, 100, 256), (37, 257, 128), (100, 300, 512), (129, 130, 256), (300, 200, 192), (64, 96, 4096),
     (260, 160, 4096), (300, 200, 640), (520, 260, 1152),   # ring stage counts that end mid index group
     (2048, 8192, 256), (2100, 8200, 256),
+    (20, 100, 96), (50, 70, 64),   # K off the rings' stage grid: weight-streaming / register-staged kernels
 ]
 
 
@@ -111,7 +112,8 @@ def test_spmm_bf16_random_tolerance(nm, Mt, R, K, Ns):
                        torch.from_numpy(Y32.astype(np.float32)).to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("Mt,R,K", [(1, 70, 2560), (33, 96, 256), (256, 130, 512), (300, 64, 2560)])
+@pytest.mark.parametrize("Mt,R,K", [(1, 70, 2560), (33, 96, 256), (256, 130, 512), (300, 64, 2560),
+                                    (20, 100, 192), (70, 90, 128)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_spmm_int8_exact(nm, Mt, R, K, Ns):
     g = np.random.default_rng(Mt + R + K + Ns)
