@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements on the other workloads")
     p.add_argument("--eager", action="store_true",
                    help="time the step as individual launches instead of one HIP-graph replay")
+    p.add_argument("--streams", choices=("one", "layers", "small"), default="layers",
+                   help="capture the step on one stream, or forked after H into the two layers' chains "
+                        "(default), or the few-token products beside the 2048-token ones")
     p.add_argument("--pmc-pass", action="store_true",
                    help="run one step plus a plain 256 MiB copy (for HBM counter scaling) and exit")
     return p.parse_args()
@@ -68,12 +71,15 @@ class Step:
             self.layers.append(dict(name=name, R=R, W=W, vals=vals, idx=idx, mask=mask))
         self.X = {M: synth.activations_bf16(1, M, K).to(dev) for M in TOKENS}
         self.Y = {(l["name"], M): torch.empty((M, l["R"]), dtype=bf, device=dev) for l in self.layers for M in TOKENS}
-        need = max(nm.raw.nm_spmm_workspace(M, K, l["R"], 0, nm.NM_BF16) for l in self.layers for M in TOKENS)
-        self.ws_s = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        for l in self.layers:   # one workspace per layer: the two layers' chains may run concurrently
+            need = max(nm.raw.nm_spmm_workspace(M, K, l["R"], 0, nm.NM_BF16) for M in TOKENS)
+            l["ws"] = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def launches(self):
-        """(kernel name, callable) in step order."""
+        """(kernel name, callable) in step order; each callable takes a stream handle.
+        The first launch (H) feeds both layers; after it, each layer's launches depend
+        only on that layer's earlier launches."""
         nm, r = self.nm, self.nm.raw
         out = []
 
@@ -97,13 +103,43 @@ class Step:
                     Y = self.Y[(l["name"], M)]
                     chk(r.nm_spmm(self.X[M].data_ptr(), nm.NM_BF16, M, K, K, l["vals"].data_ptr(), nm.NM_BF16,
                                   l["idx"].data_ptr(), l["R"], K // 2, K // 32, 0, None, 1.0, Y.data_ptr(), nm.NM_BF16,
-                                  l["R"], self.ws_s.data_ptr(), self.ws_s.numel(), stream))
+                                  l["R"], l["ws"].data_ptr(), l["ws"].numel(), stream))
                 out.append((f"spmm {l['name']} M={M}", spmm))
         return out
 
     def run(self, stream):
         for _, f in self.launches():
             f(stream)
+
+    def run_two(self, main, side, split="layers"):
+        """The step on two torch streams, forked after H and joined at the end, so that
+        independent kernels can share the GPU.  split="layers": W_a's chain on `main`,
+        W_b's on `side`.  split="small": H and both packs on `main`, then the two
+        2048-token products on `main` and the few-token products on `side`."""
+        torch = self.torch
+        launches = self.launches()
+        fork = torch.cuda.Event()
+        if split == "layers":
+            launches[0][1](main.cuda_stream)
+            fork.record(main)
+            side.wait_event(fork)
+            for name, f in launches[1:]:
+                f((main if self.layers[0]["name"] in name else side).cuda_stream)
+        else:
+            rest = []
+            for name, f in launches:
+                if name.startswith("spmm"):
+                    rest.append((name, f))
+                else:
+                    f(main.cuda_stream)
+            fork.record(main)
+            side.wait_event(fork)
+            big = f"M={TOKENS[-1]}"
+            for name, f in sorted(rest, key=lambda t: not t[0].endswith(big) or "W_a" in t[0]):
+                f((main if name.endswith(big) else side).cuda_stream)
+        join = torch.cuda.Event()
+        join.record(side)
+        main.wait_event(join)
 
     def outputs(self):
         out = [self.H]
@@ -390,9 +426,9 @@ def main():
         print(json.dumps({"pmc_pass": "done", "copy_bytes": 256 << 20}))
         return
 
-    # The step's 11 launches are captured once into a HIP graph and replayed, so the
-    # timed region measures the GPU rather than Python's launch overhead.  The replay
-    # is checked bit for bit against an eager run of the same step.
+    # The step's launches are captured once into a HIP graph and replayed, so the timed
+    # region measures the GPU rather than Python's launch overhead.  The replay is
+    # checked bit for bit against an eager run of the same step.
     graph_ok = None
     if args.eager:
         run_step = lambda: st.run(sh)
@@ -401,8 +437,13 @@ def main():
         torch.cuda.synchronize()
         ref = st.snapshot()
         g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
         with torch.cuda.graph(g):
-            st.run(torch.cuda.current_stream(dev).cuda_stream)
+            cur = torch.cuda.current_stream(dev)
+            if args.streams == "one":
+                st.run(cur.cuda_stream)
+            else:
+                st.run_two(cur, side, args.streams)
         st.clear_outputs()
         g.replay()
         torch.cuda.synchronize()
@@ -486,7 +527,12 @@ def main():
         "spmm_effective_TFLOPs": round(spmm_flops / (spmm_us * 1e-6) / 1e12, 2),
         "maskpack_GBps": round(mp_bytes / (mp_us * 1e-6) / 1e9, 1),
         "maskpack_frac_hbm": round(mp_bytes / (mp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "timing": "eager launches" if args.eager else "HIP graph replay of the whole step (checked equal to eager)",
+        "timing": "eager launches" if args.eager else (
+            "HIP graph replay of the whole step" + {
+                "one": " on one stream",
+                "layers": ", the two layers' chains on two streams after H",
+                "small": ", the few-token products on a second stream beside the 2048-token ones"}[args.streams] +
+            " (checked equal to an eager step)"),
         "roofline": roof,
         "kernels": kernels,
         "rows": rows,
