@@ -68,6 +68,7 @@ def _declare(L):
         "or_slide_decompose": (I64, [P, I, I64, I64, I64, P, I64, I, I, P, I64, P, I64]),
         "or_slide_fold": (None, [P, I, I64, P, I64, I64, I64, I, P]),
         "or_lift": (None, [P, I, I64, I64, I, P]),
+        "or_quant_i8": (None, [P, I64, I64, I64, P, P]),
         "or_masked_matmul": (None, [P, I, I64, I64, I64, P, I, I64, I64, P, I64, P]),
         "or_masked_matmul_at": (None, [P, I, I64, I64, P, I, I64, P, I64, P, P, I64, P]),
         "or_masked_matmul_i8": (I64, [P, I64, I64, I64, P, I64, I64, P, I64, P, F, P, P]),
@@ -225,6 +226,24 @@ def lift(X: np.ndarray, Ns: int) -> np.ndarray:
     Xl = np.empty((Mt, lifted_width(K, Ns)), X.dtype)
     lib().or_lift(_p(X), _dt(X), Mt, K, Ns, _p(Xl))
     return Xl
+
+
+def quant_i8(X: np.ndarray):
+    """Per-token absmax int8 quantisation of bf16 X [Mt, K] (uint16 bits):
+    returns (X_q int8 [Mt, K], s_x float32 [Mt]) with X ~= s_x[:, None] * X_q."""
+    X = _c(X, np.uint16)
+    Mt, K = X.shape
+    Xq = np.empty((Mt, K), np.int8)
+    sx = np.empty(Mt, np.float32)
+    lib().or_quant_i8(_p(X), Mt, K, K, _p(Xq), _p(sx))
+    return Xq, sx
+
+
+def quant_lift(X: np.ndarray, Ns: int):
+    """The online step of the int8 slide path: quantise per token, then lift
+    (Ns = 0: no lift).  Returns (X_q lifted int8 [Mt, K'], s_x float32 [Mt])."""
+    Xq, sx = quant_i8(X)
+    return (lift(Xq, Ns) if Ns else Xq), sx
 
 
 # ---------------------------------------------------------------- A12 / A13

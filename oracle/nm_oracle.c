@@ -29,8 +29,9 @@
  *         group; quantise then mask).
  *   [SS]  "SlideSparse" summary: section 2A (N-1 overlapping width-4 windows
  *         with stride 2 cover any (2N-2):2N block; expansion 2-2/N), 2B
- *         (activation lifting is a pure index remap) and 2C (offline packer,
- *         sparse GEMM per request).
+ *         (activation lifting is a pure index remap, fused into the per-token
+ *         quantisation) and 2C (offline packer; per request: quantise + lift,
+ *         then the sparse GEMM).
  *   [SA]  "SALR" summary, Methodology 1 (magnitude pruning of the frozen base).
  */
 #include <math.h>
@@ -370,6 +371,35 @@ void or_lift(const void* X, int xdt, int64_t Mt, int64_t K, int Ns, void* Xl) {
                 for (int l = 0; l < 4; ++l)
                     memcpy((char*)Xl + (size_t)(m * Kl + g * 4 * (Ns - 1) + 4 * w + l) * es,
                            (const char*)X + (size_t)(m * K + g * 2 * Ns + 2 * w + l) * es, es);
+}
+
+/* ------------------------------------------------------------------ per-token int8 quantisation [SS 2B, 2C]
+ * The online step before the int8 sparse product: each token row of X is
+ * scaled by its own absolute maximum, s = max|x| / 127, and rounded to the
+ * nearest integer, q = rint(x / s) (ties to even), so that x ~= s * q with
+ * q in [-127, 127].  The pages name per-token INT8 quantisation and fuse the
+ * lift into it without fixing the formula; this is the plain absmax reading.
+ * The quotients decide integers, so they are computed in float (one rounding
+ * per operation); a zero row gives s = 0 and q = 0.  Inputs are finite. */
+void or_quant_i8(const uint16_t* X, int64_t Mt, int64_t K, int64_t ldx, int8_t* Xq, float* sx) {
+    for (int64_t m = 0; m < Mt; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float a = fabsf(bf16_to_f32(X[m * ldx + k]));
+            if (a > amax) amax = a;
+        }
+        const float s = amax / 127.0f;
+        sx[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float q = 0.0f;
+            if (s > 0.0f) {
+                q = rintf(bf16_to_f32(X[m * ldx + k]) / s);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+            }
+            Xq[m * K + k] = (int8_t)q;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------ A12 / A13

@@ -243,6 +243,60 @@ def test_lifted_product_equals_dense_masked(Ns):
     assert np.array_equal(O.masked_matmul(X, W, mask), X.astype(np.float64) @ Wm.T)
 
 
+# ------------------------------------------------------------------ per-token int8 quantisation (SlideSparse 2B/2C)
+def test_quant_unit_scale_is_round_half_even():
+    """A row whose absolute maximum is 127 has scale exactly 1, so the codes are the
+    values rounded to the nearest integer with ties to even (numpy's rint)."""
+    vals = np.array([127, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 0.25, -126.5, 63.75, 7.0], np.float32)
+    X = O.f32_to_bf16(vals[None, :])
+    xf = O.bf16_to_f32(X)[0]
+    Xq, sx = O.quant_i8(X)
+    assert sx[0] == 1.0
+    assert np.array_equal(Xq[0], np.rint(xf).astype(np.int8))
+    assert list(Xq[0, 1:8]) == [-2, -2, 0, 0, 2, 2, 4]
+
+
+def test_quant_power_of_two_scales_and_zero_row():
+    """max|x| = 127 * 2^e gives scale 2^e exactly: codes are rint(x / 2^e); a zero row has
+    scale 0 and codes 0; the extreme element always maps to +-127."""
+    g = _rng(70)
+    rows = []
+    for e in (-6, -1, 0, 3):
+        r = g.integers(-126, 127, 16).astype(np.float32) * 2.0 ** e + 0.25 * 2.0 ** e
+        r[5] = -127 * 2.0 ** e
+        rows.append(r)
+    X = O.f32_to_bf16(np.stack(rows + [np.zeros(16, np.float32)]))
+    xf = O.bf16_to_f32(X).astype(np.float64)
+    Xq, sx = O.quant_i8(X)
+    for i, e in enumerate((-6, -1, 0, 3)):
+        assert sx[i] == 2.0 ** e
+        assert np.array_equal(Xq[i], np.rint(xf[i] / 2.0 ** e).astype(np.int8))
+        assert Xq[i, 5] == -127
+    assert sx[-1] == 0.0 and not Xq[-1].any()
+
+
+def test_quant_error_bound_and_lift():
+    """Random rows: |x - s q| <= s/2 (plus the float rounding of s and of x/s), |q| <= 127
+    with the absmax element at +-127; the lifted codes are the codes remapped by the lift."""
+    g = _rng(71)
+    Mt, K = 9, 64
+    a = g.uniform(0.5, 2.0, Mt)
+    X = O.f32_to_bf16((a[:, None] * g.uniform(-1, 1, (Mt, K))).astype(np.float32))
+    xf = O.bf16_to_f32(X).astype(np.float64)
+    Xq, sx = O.quant_i8(X)
+    s = sx.astype(np.float64)[:, None]
+    assert (np.abs(xf - s * Xq) <= s * (0.5 + 1e-5)).all()
+    assert (np.abs(Xq.astype(np.int32)) <= 127).all()
+    assert (np.abs(Xq[np.arange(Mt), np.abs(xf).argmax(1)]) == 127).all()
+    XL, sx2 = O.quant_lift(X, 4)
+    assert np.array_equal(sx2, sx) and np.array_equal(XL, O.lift(Xq, 4))
+    # lift by its definition: lifted column 12q + 4w + l holds column 8q + 2w + l
+    for c in range(O.lifted_width(K, 4)):
+        q, r = divmod(c, 12)
+        w, l = divmod(r, 4)
+        assert np.array_equal(XL[:, c], Xq[:, 8 * q + 2 * w + l])
+
+
 # ------------------------------------------------------------------ A12 / A13
 def test_masked_matmul_bruteforce_tiny():
     g = _rng(40)
