@@ -167,7 +167,8 @@ def algorithmic_work():
         for M in TOKENS:
             packed = R * K // 2 * 2 + R * K // 32 * 4
             w[f"spmm {name} M={M}"] = dict(
-                bound="mfma",
+                # up to 128 tokens the product is bound by the packed weight's HBM stream
+                bound="hbm" if M <= 128 else "mfma",
                 flops_dense_eq=2 * M * R * K,          # dense-equivalent work
                 flops=2 * M * R * K // 2,              # multiply-adds on kept weights only (2 of 4)
                 bytes=packed + M * K * 2 + M * R * 2)  # packed weight + X + Y
@@ -328,6 +329,15 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     wsa = ws_for(r.nm_stats_workspace(R, K))
     row("ternary68", "A10", "absmean 6912x2560", lambda: chk(r.nm_absmean(
         Wf.data_ptr(), nm.NM_BF16, R, K, K, alpha.data_ptr(), wsa.data_ptr(), wsa.numel(), sh)), "hbm", R * K * 2)
+    # the online step before the int8 product, from bf16 activations (SlideSparse 2B/2C)
+    Mq = 2048
+    Xb = synth.ternary68_activations_bf16(Mq, K).to(dev)
+    XLq = torch.empty((Mq, Kl), dtype=i8, device=dev)
+    sxq = torch.empty(Mq, dtype=f32, device=dev)
+    row("ternary68", "NEXT-1", f"quant_lift {Mq}x{K} bf16 -> int8 lifted + s_x", lambda: chk(r.nm_quant_lift(
+        Xb.data_ptr(), nm.NM_BF16, Mq, K, K, Ns, XLq.data_ptr(), Kl, sxq.data_ptr(), sh)), "hbm",
+        Mq * K * 2 + Mq * Kl + Mq * 4)
+    del Xb, XLq, sxq
     a = float(alpha.cpu())
     for M in (1, 256, 2048):
         Xq, sx = synth.ternary68_activations(M, K)
@@ -479,14 +489,11 @@ def main():
         t_ms = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
         w = work[name]
         k = dict(name=name, us=round(t_ms * 1e3, 2), bound=w["bound"])
-        if w["bound"] == "hbm":
-            k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
-            k["frac"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
-        else:
+        k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
+        if "flops" in w:
             k["eff_TFLOPs"] = round(w["flops_dense_eq"] / (t_ms * 1e-3) / 1e12, 2)
             k["TFLOPs"] = round(w["flops"] / (t_ms * 1e-3) / 1e12, 2)
-            k["frac"] = round(k["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
-            k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
+        k["frac"] = round(k["GBps"] / HBM_PEAK_GBPS if w["bound"] == "hbm" else k["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
         kernels.append(k)
     dom = max(kernels, key=lambda k: k["us"])
     wd = work[dom["name"]]
@@ -504,6 +511,22 @@ def main():
     mp_bytes = sum(work[k["name"]]["bytes"] for k in maskpack)
     mp_us = sum(k["us"] for k in maskpack)
     spmm_us = sum(k["us"] for k in kernels if k["name"].startswith("spmm"))
+
+    # context only (never on the library path): hipBLASLt's dense bf16 GEMM of the dominant
+    # product's shape, X [2048, 4096] x W_b^T, with the same HIP-event timing
+    Xd, Wd = st.X[TOKENS[-1]], st.layers[-1]["W"]
+    for _ in range(3):
+        torch.matmul(Xd, Wd.t())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        torch.matmul(Xd, Wd.t())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    dense_ctx = dict(what=f"torch.matmul (hipBLASLt) dense bf16, same shape as {dom['name']}; context only",
+                     us=round(dense_us, 2), sparse_us=dom["us"],
+                     sparse_speedup=round(dense_us / dom["us"], 3))
 
     rows = None if args.no_rows else measure_rows(nm, torch, synth, dev)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
@@ -534,6 +557,7 @@ def main():
                 "small": ", the few-token products on a second stream beside the 2048-token ones"}[args.streams] +
             " (checked equal to an eager step)"),
         "roofline": roof,
+        "dense_context": dense_ctx,
         "kernels": kernels,
         "rows": rows,
         "cpu_baseline": cpu,

@@ -193,6 +193,21 @@ nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const floa
                          uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv,
                          uint32_t* idx, int64_t ldi, nm_stream_t stream);
 
+/* Online step of the int8 slide path ("SlideSparse", sections 2B-2C: the
+ * activation lift is an index remap fused into the per-token quantisation
+ * kernel, ahead of the sparse GEMM).  Token row m of X (bf16 [Mtok, K], ldx):
+ *   x_scale[m] = max_k |X[m,k]| / 127   (f32; 0 for a zero row),
+ *   q[m,k] = rint(X[m,k] / x_scale[m]) clamped to [-127, 127]   (f32, ties to
+ *   even; 0 for a zero row),
+ * written lifted when Ns == 4: Xq[m, 12g + 4w + l] = q[m, 8g + 2w + l], i.e.
+ * int8 [Mtok, K' = 3K/2] (ldq >= K'), the activation nm_spmm multiplies with
+ * Ns = 0 over K' against a slide-decomposed weight; Ns == 0 writes q as is
+ * (ldq >= K).  Requires K % 8 == 0, X 16-byte aligned with 16-byte row
+ * strides, Xq 4-byte (lifted) or 8-byte aligned rows.  x_scale: device f32
+ * [Mtok].  Allocates nothing. */
+nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq,
+                        int64_t ldq, float* x_scale, nm_stream_t stream);
+
 /* Per-tensor scale of a ternary layer: alpha = mean |W| over R x K, reduced in
  * f64 in a fixed order and rounded to f32 ("Sparse-BitNet", section 1-2:
  * 1.58-bit weights carry one high-precision scale).  alpha: device f32 [1].

@@ -64,6 +64,7 @@ SIGNATURES = {
     "nm_prune_slide": (_I, [_P, _I, _I64, _P, _I64, _F, _I, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _I, _P, _I64, _P,
                             _I64, _P]),
     "nm_absmean": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "nm_quant_lift": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
     "nm_spmm_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_spmm": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P, _SZ, _P]),
 }
@@ -238,6 +239,16 @@ def nm_absmean(W: torch.Tensor) -> torch.Tensor:
     ws = _ws(raw.nm_stats_workspace(R, K), W.device)
     _check(raw.nm_absmean(_ptr(W), dtype_code(W), R, K, _ld(W), _ptr(a), _ptr(ws), ws.numel(), _stream(W)))
     return a
+
+
+def nm_quant_lift(X: torch.Tensor, Ns: int = 4) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per-token int8 codes of bf16 X (lifted for Ns = 4) and their scales."""
+    Mtok, K = X.shape
+    Kl = K // 8 * 12 if Ns else K
+    Xq = torch.empty((Mtok, Kl), dtype=torch.int8, device=X.device)
+    sx = torch.empty(Mtok, dtype=torch.float32, device=X.device)
+    _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, _ptr(Xq), Kl, _ptr(sx), _stream(X)))
+    return Xq, sx
 
 
 def nm_spmm(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, R: int | None = None, Ns: int = 0,

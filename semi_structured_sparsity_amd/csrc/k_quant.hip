@@ -1,0 +1,82 @@
+// Per-token int8 quantisation fused with the 6:8 activation lift ("SlideSparse",
+// sections 2B-2C: the lift is a pure index remap, done inside the per-token
+// quantisation kernel, so that the online step of the int8 path reads the bf16
+// activation once and writes the lifted int8 codes the sparse product consumes).
+// Token row m: s = max|x| / 127 and q = rint(x / s), ties to even, in f32 (the
+// quotients decide integers); a zero row gives s = 0 and codes 0.  With the lift,
+// lifted column 12g + 4w + l holds the code of column 8g + 2w + l (windows at
+// offsets 0, 2, 4 of each 8-column group).
+//
+// One block of 256 threads per token row: pass 1 takes the absolute maximum over
+// 16-byte loads of 8 columns; pass 2 re-reads the row (it is L2-resident by then),
+// rounds, and writes each 8-column group as 12 lifted bytes (three dwords) or, without
+// the lift, 8 bytes.
+#include "nm_internal.h"
+
+namespace nm {
+
+constexpr int kQuantThreads = 256;
+
+template <bool LIFT>
+__global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                   int64_t K, int8_t* __restrict__ Xq, int64_t ldq,
+                                                                   float* __restrict__ sx) {
+    __shared__ float red[kQuantThreads / 64];
+    const int64_t m = blockIdx.x;
+    const uint16_t* xr = X + m * ldx;
+    const int64_t groups = K / 8;
+    float amax = 0.0f;
+    for (int64_t g = threadIdx.x; g < groups; g += kQuantThreads) {
+        const uint4 v = *(const uint4*)(xr + 8 * g);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // |bf16| as f32 bits: clear the sign, widen
+            amax = fmaxf(amax, __builtin_bit_cast(float, (w[i] & 0x7fffu) << 16));
+            amax = fmaxf(amax, __builtin_bit_cast(float, (w[i] >> 16 & 0x7fffu) << 16));
+        }
+    }
+    // max over the wave, then over the 4 waves
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (threadIdx.x == 0) sx[m] = s;
+
+    int8_t* qr = Xq + m * ldq;
+    for (int64_t g = threadIdx.x; g < groups; g += kQuantThreads) {
+        const uint4 v = *(const uint4*)(xr + 8 * g);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = __builtin_bit_cast(float, ((w[i >> 1] >> (16 * (i & 1))) & 0xffffu) << 16);
+            float q = 0.0f;
+            if (s > 0.0f) q = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.0f), 127.0f);
+            b[i] = (uint32_t)(int32_t)q & 0xffu;
+        }
+        const uint32_t lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+        const uint32_t hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        if constexpr (LIFT) {
+            uint32_t* o = (uint32_t*)(qr + 12 * g);   // windows: bytes 0-3, 2-5, 4-7
+            o[0] = lo;
+            o[1] = (lo >> 16) | (hi << 16);
+            o[2] = hi;
+        } else {
+            *(uint2*)(qr + 8 * g) = make_uint2(lo, hi);
+        }
+    }
+}
+
+void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq, int64_t ldq,
+                       float* x_scale, hipStream_t s) {
+    if (Mtok == 0) return;
+    if (Ns) hipLaunchKernelGGL(quant_lift_kernel<true>, dim3((unsigned)Mtok), dim3(kQuantThreads), 0, s,
+                               (const uint16_t*)X, ldx, K, Xq, ldq, x_scale);
+    else hipLaunchKernelGGL(quant_lift_kernel<false>, dim3((unsigned)Mtok), dim3(kQuantThreads), 0, s,
+                            (const uint16_t*)X, ldx, K, Xq, ldq, x_scale);
+}
+
+}  // namespace nm

@@ -339,6 +339,25 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
     return check_launch(fn);
 }
 
+nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq,
+                        int64_t ldq, float* x_scale, nm_stream_t stream) {
+    const char* fn = "nm_quant_lift";
+    NM_REQ(Mtok >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported: no lift (Ns=0) and the 6:8 lift (Ns=4)", fn);
+    NM_REQ(xdt == NM_BF16, NM_ERR_DTYPE, "%s: X must be bf16", fn);
+    NM_REQ(K % 8 == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 8", fn);
+    if (Mtok == 0 || K == 0) return NM_OK;
+    NM_REQ(X && Xq && x_scale, NM_ERR_NULL, "%s: NULL argument", fn);
+    const int64_t Kl = Ns ? K / 8 * 12 : K;
+    NM_REQ(ldx >= K && ldq >= Kl, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    NM_REQ(aligned16(X) && (ldx * 2) % 16 == 0 && ((uintptr_t)Xq & (Ns ? 3u : 7u)) == 0 && ldq % (Ns ? 4 : 8) == 0,
+           NM_ERR_ALIGN, "%s: X needs 16-byte aligned rows, Xq 4-byte (lifted) or 8-byte aligned rows", fn);
+    const Range rx = span(X, Mtok, K, ldx, 2), rq = span(Xq, Mtok, Kl, ldq, 1), rs = span(x_scale, 1, Mtok, Mtok, 4);
+    NM_REQ(!overlap(rq, rx) && !overlap(rs, rx) && !overlap(rq, rs), NM_ERR_ALIAS, "%s: outputs overlap", fn);
+    launch_quant_lift(X, Mtok, K, ldx, Ns, Xq, ldq, x_scale, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
 size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
     if (Mtok <= 0 || K <= 0 || R <= 0) return 0;
     return spmm_ws(Mtok, K, R, Ns, xdt);

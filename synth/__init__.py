@@ -132,6 +132,13 @@ def ternary68_activations(tokens: int, K: int = 2560):
     return Xq, sx
 
 
+def ternary68_activations_bf16(tokens: int, K: int = 2560) -> torch.Tensor:
+    """Unquantised activations for the int8 path: row m = a_m * U(-1, 1), a_m ~ U(0.5, 2), bf16."""
+    g = rng(3, 40 + tokens)
+    a = g.uniform(0.5, 2.0, size=(tokens, 1))
+    return to_bf16((a * g.uniform(-1.0, 1.0, size=(tokens, K))).astype(np.float32))
+
+
 # ---------------------------------------------------------------- hessian24 (config index 4)
 def hessian24_weight(R: int = 28672, K: int = 8192) -> torch.Tensor:
     """W [out=R, in=K] bf16 ~ 0.015 N(0,1)."""
