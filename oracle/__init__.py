@@ -69,6 +69,10 @@ def _declare(L):
         "or_slide_fold": (None, [P, I, I64, P, I64, I64, I64, I, P]),
         "or_lift": (None, [P, I, I64, I64, I, P]),
         "or_quant_i8": (None, [P, I64, I64, I64, P, P]),
+        "or_e4m3_decode": (None, [P, I64, P]),
+        "or_e4m3_encode": (None, [P, I64, P]),
+        "or_quant_fp8": (None, [P, I64, I64, I64, P, P]),
+        "or_masked_matmul_fp8": (None, [P, I64, I64, P, I64, P, I64, P]),
         "or_masked_matmul": (None, [P, I, I64, I64, I64, P, I, I64, I64, P, I64, P]),
         "or_masked_matmul_at": (None, [P, I, I64, I64, P, I, I64, P, I64, P, P, I64, P]),
         "or_masked_matmul_i8": (I64, [P, I64, I64, I64, P, I64, I64, P, I64, P, F, P, P]),
@@ -239,11 +243,51 @@ def quant_i8(X: np.ndarray):
     return Xq, sx
 
 
-def quant_lift(X: np.ndarray, Ns: int):
-    """The online step of the int8 slide path: quantise per token, then lift
-    (Ns = 0: no lift).  Returns (X_q lifted int8 [Mt, K'], s_x float32 [Mt])."""
-    Xq, sx = quant_i8(X)
-    return (lift(Xq, Ns) if Ns else Xq), sx
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    """OCP FP8 e4m3 codes (uint8) -> float32 values."""
+    c = _c(c, np.uint8)
+    y = np.empty(c.shape, np.float32)
+    lib().or_e4m3_decode(_p(c), c.size, _p(y))
+    return y
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest OCP FP8 e4m3 code, ties to even, saturating at 448."""
+    x = _c(x, np.float32)
+    c = np.empty(x.shape, np.uint8)
+    lib().or_e4m3_encode(_p(x), x.size, _p(c))
+    return c
+
+
+def quant_fp8(X: np.ndarray):
+    """Per-token FP8 quantisation of bf16 X: (codes uint8 [Mt, K], s_x float32 [Mt]),
+    s_x = max|x| / 448, code = e4m3(x / s_x)."""
+    X = _c(X, np.uint16)
+    Mt, K = X.shape
+    Xq = np.empty((Mt, K), np.uint8)
+    sx = np.empty(Mt, np.float32)
+    lib().or_quant_fp8(_p(X), Mt, K, K, _p(Xq), _p(sx))
+    return Xq, sx
+
+
+def quant_lift(X: np.ndarray, Ns: int, fp8: bool = False):
+    """The online step of the slide path: quantise per token (int8, or FP8 e4m3 codes),
+    then lift (Ns = 0: no lift).  Returns (codes lifted [Mt, K'], s_x float32 [Mt])."""
+    Xq, sx = quant_fp8(X) if fp8 else quant_i8(X)
+    if not Ns:
+        return Xq, sx
+    return (lift(Xq.view(np.int8), Ns).view(np.uint8) if fp8 else lift(Xq, Ns)), sx
+
+
+def masked_matmul_fp8(Xq: np.ndarray, Wq: np.ndarray, mask: np.ndarray | None = None) -> np.ndarray:
+    """Y = X (mask*W)^T over FP8 codes, in double."""
+    Xq, Wq = _c(Xq, np.uint8), _c(Wq, np.uint8)
+    Mt, K = Xq.shape
+    R = Wq.shape[0]
+    Y = np.empty((Mt, R), np.float64)
+    m = None if mask is None else _c(mask, np.uint8)
+    lib().or_masked_matmul_fp8(_p(Xq), Mt, K, _p(Wq), R, _p(m), 0 if m is None else m.shape[1], _p(Y))
+    return Y
 
 
 # ---------------------------------------------------------------- A12 / A13

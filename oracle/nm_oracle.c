@@ -402,6 +402,74 @@ void or_quant_i8(const uint16_t* X, int64_t Mt, int64_t K, int64_t ldx, int8_t* 
     }
 }
 
+/* ------------------------------------------------------------------ FP8 e4m3 [SS 3, precisions]
+ * OCP FP8 e4m3 ("fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 holds the subnormals m/8 * 2^-6; code 0x7f / 0xff is NaN; no
+ * infinities; the largest finite magnitude is 448.  Decoding is exact in float.
+ * Encoding rounds to the nearest code, ties to the code with the even low bit
+ * (round-half-even), found by brute force over the 127 finite magnitudes;
+ * magnitudes past 448 saturate to 448 (a reading: the pages fix no overflow
+ * rule; every value the quantisation below produces is within 448 anyway). */
+static float e4m3_decode(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexpf((float)m, -9);
+    else v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return (c & 0x80) ? -v : v;
+}
+static uint8_t e4m3_encode(float x) {
+    if (x != x) return 0x7f;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;   /* -0 keeps its sign, as in IEEE conversions */
+    const float a = fabsf(x);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 127; ++c) {           /* finite non-negative codes, ascending value */
+        const double d = fabs((double)a - (double)e4m3_decode((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+void or_e4m3_decode(const uint8_t* c, int64_t n, float* y) {
+    for (int64_t i = 0; i < n; ++i) y[i] = e4m3_decode(c[i]);
+}
+void or_e4m3_encode(const float* x, int64_t n, uint8_t* c) {
+    for (int64_t i = 0; i < n; ++i) c[i] = e4m3_encode(x[i]);
+}
+/* Per-token FP8 quantisation: s = max|x| / 448, code = e4m3(x / s) in float. */
+void or_quant_fp8(const uint16_t* X, int64_t Mt, int64_t K, int64_t ldx, uint8_t* Xq, float* sx) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < Mt; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float a = fabsf(bf16_to_f32(X[m * ldx + k]));
+            if (a > amax) amax = a;
+        }
+        const float s = amax / 448.0f;
+        sx[m] = s;
+        for (int64_t k = 0; k < K; ++k)
+            Xq[m * K + k] = s > 0.0f ? e4m3_encode(bf16_to_f32(X[m * ldx + k]) / s) : 0;
+    }
+}
+/* Y[m,o] = sum_k x[m,k] w[o,k] over FP8 codes (mask: as or_masked_matmul), in double:
+ * each product of two e4m3 values is exact. */
+void or_masked_matmul_fp8(const uint8_t* X, int64_t Mt, int64_t K, const uint8_t* W, int64_t R,
+                          const uint8_t* mask, int64_t ldm, double* Y) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < Mt; ++m)
+        for (int64_t o = 0; o < R; ++o) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                if (mask && !mask_get(mask, ldm, o, k)) continue;
+                acc += (double)e4m3_decode(X[m * K + k]) * (double)e4m3_decode(W[o * K + k]);
+            }
+            Y[m * R + o] = acc;
+        }
+}
+
 /* ------------------------------------------------------------------ A12 / A13
  * The structured-sparse linear layer is, by definition, the dense product with
  * the masked weight: Y[m,o] = sum_k X[m,k] * (mask * W)[o,k].  Double

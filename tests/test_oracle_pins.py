@@ -297,6 +297,69 @@ def test_quant_error_bound_and_lift():
         assert np.array_equal(XL[:, c], Xq[:, 8 * q + 2 * w + l])
 
 
+# ------------------------------------------------------------------ FP8 e4m3 (SlideSparse: FP8 among the precisions)
+def test_e4m3_decode_all_codes_matches_torch():
+    c = np.arange(256, dtype=np.uint8)
+    d = O.e4m3_decode(c)
+    t = torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(d), np.isnan(t))
+    assert np.array_equal(d[~np.isnan(d)], t[~np.isnan(t)])
+    assert d[0x7e] == 448.0 and d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_matches_torch_rounding_and_saturates():
+    """Round-half-even against torch's float8_e4m3fn cast on every finite value, every
+    midpoint between neighbouring codes, and random values; past 448 the oracle
+    saturates (torch gives NaN there, so those are checked by value)."""
+    fin = O.e4m3_decode(np.arange(127, dtype=np.uint8)).astype(np.float64)
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    g = _rng(72)
+    rnd = np.concatenate([g.uniform(-448, 448, 4000), g.uniform(-2.0 ** -5, 2.0 ** -5, 2000)]).astype(np.float32)
+    for x in (fin.astype(np.float32), -fin.astype(np.float32), mids, -mids, rnd):
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(O.e4m3_encode(x), ref)
+    assert list(O.e4m3_encode(np.array([448.0, 449.0, 1e6, -500.0], np.float32))) == [0x7e, 0x7e, 0x7e, 0xfe]
+
+
+def test_quant_fp8_unit_scale_zero_row_and_error_bound():
+    g = _rng(73)
+    Mt, K = 6, 40
+    a = g.uniform(0.5, 2.0, (Mt, 1))
+    Xf = (a * g.uniform(-1, 1, (Mt, K))).astype(np.float32)
+    Xf[0] = np.clip(Xf[0] * 300, -447, 447)
+    Xf[0, 3] = 448.0                       # max|x| = 448: scale exactly 1
+    Xf[1] = 0.0
+    X = O.f32_to_bf16(Xf)
+    xf = O.bf16_to_f32(X)
+    Xq, sx = O.quant_fp8(X)
+    assert sx[0] == 1.0
+    assert np.array_equal(Xq[0], torch.from_numpy(xf[0]).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert sx[1] == 0.0 and not Xq[1].any()
+    dq = O.e4m3_decode(Xq).astype(np.float64) * sx[:, None]
+    # e4m3 keeps 4 significant bits: relative error <= 2^-4 for normals, absolute
+    # <= 2^-10 * s in the subnormal range, plus the float rounding of s and x / s
+    err = np.abs(dq - xf.astype(np.float64))
+    bound = np.maximum(np.abs(xf) * 2.0 ** -4, 2.0 ** -10 * sx[:, None]) * (1 + 1e-5)
+    assert (err <= bound).all()
+    XL, sx2 = O.quant_lift(X, 4, fp8=True)
+    assert np.array_equal(sx2, sx) and np.array_equal(XL, O.lift(Xq.view(np.int8), 4).view(np.uint8))
+
+
+def test_masked_matmul_fp8_against_decoded_values():
+    g = _rng(74)
+    Mt, R, K = 3, 5, 24
+    Xq = g.integers(0, 256, (Mt, K)).astype(np.uint8)
+    Wq = g.integers(0, 256, (R, K)).astype(np.uint8)
+    Xq[(Xq & 0x7f) == 0x7f] = 0x00          # no NaN codes
+    Wq[(Wq & 0x7f) == 0x7f] = 0x38
+    mask = O.topn_mask(g.random((R, K)).astype(np.float32), 6, 8)
+    xd = torch.from_numpy(Xq).view(torch.float8_e4m3fn).double().numpy()
+    wd = torch.from_numpy(Wq).view(torch.float8_e4m3fn).double().numpy()
+    wm = np.where(O.mask_to_bool(mask, K), wd, 0.0)
+    assert np.array_equal(O.masked_matmul_fp8(Xq, Wq, mask), xd @ wm.T)
+    assert np.array_equal(O.masked_matmul_fp8(Xq, Wq), xd @ wd.T)
+
+
 # ------------------------------------------------------------------ A12 / A13
 def test_masked_matmul_bruteforce_tiny():
     g = _rng(40)
