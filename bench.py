@@ -215,6 +215,7 @@ def cpu_baseline(target_s: float):
 
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 # VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz full-rate lane operations per
 # second; a transcendental (2^x, 1/x) issues at a quarter of that rate.
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
@@ -262,6 +263,9 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         elif bound == "mfma_i8":
             e["TOPs"] = round(work / t / 1e12, 2)
             e["frac"] = round(e["TOPs"] / INT8_PEAK_TOPS, 4)
+        elif bound == "mfma_fp8":
+            e["TFLOPs"] = round(work / t / 1e12, 2)
+            e["frac"] = round(e["TFLOPs"] / FP8_PEAK_TFLOPS, 4)
         elif bound == "alu":
             e["GOPs"] = round(work / t / 1e9, 1)
             e["frac"] = round(e["GOPs"] / VALU_PEAK_GOPS, 4)
@@ -312,7 +316,35 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
             row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "hbm", R * K * 1.6875 + M * K * 2 + M * R * 2)
         else:
             row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "mfma", 2 * M * R * Kl // 2)
-    del W, vals, idx, mask
+    # FP8 e4m3 precision of the same layer (SlideSparse section 3): the weight's codes slide-packed
+    # under the |W| mask, the activation quantised per token and lifted once, the product over K'
+    Wq = W.to(torch.float8_e4m3fn)
+    vq = torch.empty((R, Kl // 2), dtype=torch.float8_e4m3fn, device=dev)
+    row("slide68", "NEXT-2", "prune_slide 14336x4096 (|W| mask on fp8 codes)", lambda: chk(r.nm_prune_slide(
+        W.data_ptr(), nm.NM_BF16, K, None, 0, 0.0, nm.NM_SCORE_MAGNITUDE, Wq.data_ptr(), nm.NM_FP8, K, R, K, Ns,
+        mask.data_ptr(), K // 8, nm.NM_FP8, vq.data_ptr(), Kl // 2, idx.data_ptr(), Kl // 32, sh)), "hbm",
+        R * K * (2 + 1 + 0.75 + 0.1875 + 0.125))
+    del Wq
+    for M in (1, 4096):
+        X = synth.activations_bf16(2, M, K).to(dev)
+        XL = torch.empty((M, Kl), dtype=torch.float8_e4m3fn, device=dev)
+        sx = torch.empty(M, dtype=f32, device=dev)
+        if M > 1:
+            row("slide68", "NEXT-2", f"quant_lift {M}x{K} bf16 -> fp8 lifted + s_x", lambda: chk(r.nm_quant_lift(
+                X.data_ptr(), nm.NM_BF16, M, K, K, Ns, nm.NM_FP8, XL.data_ptr(), Kl, sx.data_ptr(), sh)), "hbm",
+                M * K * 2 + M * Kl + M * 4)
+        else:
+            chk(r.nm_quant_lift(X.data_ptr(), nm.NM_BF16, M, K, K, Ns, nm.NM_FP8, XL.data_ptr(), Kl, sx.data_ptr(), sh))
+        Y = torch.empty((M, R), dtype=bf, device=dev)
+        ws = ws_for(r.nm_spmm_workspace(M, Kl, R, 0, nm.NM_FP8))
+        f = spmm(XL, nm.NM_FP8, M, Kl, vq, nm.NM_FP8, idx, R, 0, Y, nm.NM_BF16, xs=sx, a=1.0, ws=ws)
+        if M <= 64:
+            row("slide68", "NEXT-2", f"spmm fp8 lifted 14336x4096 M={M}", f, "hbm",
+                R * Kl * (0.5 + 0.0625) + M * Kl + 4 * M + M * R * 2)
+        else:
+            row("slide68", "NEXT-2", f"spmm fp8 lifted 14336x4096 M={M}", f, "mfma_fp8", 2 * M * R * Kl // 2)
+        del X, XL, sx, Y
+    del W, vals, vq, idx, mask
 
     # ---- ternary68: 6:8 mask from |W_fp| on the ternary code, alpha = mean|W_fp|, int8 SpMM
     R, K, Ns = 6912, 2560, 4
@@ -335,7 +367,7 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     XLq = torch.empty((Mq, Kl), dtype=i8, device=dev)
     sxq = torch.empty(Mq, dtype=f32, device=dev)
     row("ternary68", "NEXT-1", f"quant_lift {Mq}x{K} bf16 -> int8 lifted + s_x", lambda: chk(r.nm_quant_lift(
-        Xb.data_ptr(), nm.NM_BF16, Mq, K, K, Ns, XLq.data_ptr(), Kl, sxq.data_ptr(), sh)), "hbm",
+        Xb.data_ptr(), nm.NM_BF16, Mq, K, K, Ns, nm.NM_I8, XLq.data_ptr(), Kl, sxq.data_ptr(), sh)), "hbm",
         Mq * K * 2 + Mq * Kl + Mq * 4)
     del Xb, XLq, sxq
     a = float(alpha.cpu())

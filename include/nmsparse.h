@@ -63,7 +63,12 @@ typedef enum {
     NM_ERR_ALIAS = 8      /* an output overlaps an input */
 } nm_status;
 
-typedef enum { NM_F32 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3 } nm_dtype;
+/* NM_FP8: OCP FP8 e4m3 codes, one byte each (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; no infinities, 0x7f/0xff NaN, largest finite 448).  FP8 is
+ * one of the precisions the sliding-window product runs in ("SlideSparse",
+ * section 3); here it is carried as raw codes by the packers and multiplied by
+ * nm_spmm with f32 accumulation. */
+typedef enum { NM_F32 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3, NM_FP8 = 4 } nm_dtype;
 
 typedef enum { NM_SCORE_HESSIAN = 0, NM_SCORE_MAGNITUDE = 1 } nm_score_mode;
 
@@ -193,25 +198,30 @@ nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const floa
                          uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv,
                          uint32_t* idx, int64_t ldi, nm_stream_t stream);
 
-/* Online step of the int8 slide path ("SlideSparse", sections 2B-2C: the
+/* Online step of the slide path ("SlideSparse", sections 2B-2C: the
  * activation lift is an index remap fused into the per-token quantisation
- * kernel, ahead of the sparse GEMM).  Token row m of X (bf16 [Mtok, K], ldx):
- *   x_scale[m] = max_k |X[m,k]| / 127   (f32; 0 for a zero row),
- *   q[m,k] = rint(X[m,k] / x_scale[m]) clamped to [-127, 127]   (f32, ties to
- *   even; 0 for a zero row),
- * written lifted when Ns == 4: Xq[m, 12g + 4w + l] = q[m, 8g + 2w + l], i.e.
- * int8 [Mtok, K' = 3K/2] (ldq >= K'), the activation nm_spmm multiplies with
- * Ns = 0 over K' against a slide-decomposed weight; Ns == 0 writes q as is
- * (ldq >= K).  Requires K % 8 == 0, X 16-byte aligned with 16-byte row
- * strides, Xq 4-byte (lifted) or 8-byte aligned rows.  x_scale: device f32
- * [Mtok].  Allocates nothing. */
-nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq,
-                        int64_t ldq, float* x_scale, nm_stream_t stream);
+ * kernel, ahead of the sparse GEMM; INT8 and FP8 are among its precisions).
+ * Token row m of X (bf16 [Mtok, K], ldx), all in f32 with one rounding per
+ * operation (the quotients decide the codes):
+ *   qdt == NM_I8:  x_scale[m] = max_k |X[m,k]| / 127,
+ *                  q = rint(X[m,k] / x_scale[m]) clamped to [-127, 127] (ties to even);
+ *   qdt == NM_FP8: x_scale[m] = max_k |X[m,k]| / 448,
+ *                  q = the e4m3 code nearest X[m,k] / x_scale[m] (ties to even; the
+ *                  quotient is within 448, and is clamped to it);
+ *   a zero row gives x_scale = 0 and codes 0.
+ * Written lifted when Ns == 4: Xq[m, 12g + 4w + l] = q[m, 8g + 2w + l], i.e.
+ * one byte per code, [Mtok, K' = 3K/2] (ldq >= K'), the activation nm_spmm
+ * multiplies with Ns = 0 over K' against a slide-decomposed weight; Ns == 0
+ * writes q as is (ldq >= K).  Requires K % 8 == 0, X 16-byte aligned with
+ * 16-byte row strides, Xq 4-byte (lifted) or 8-byte aligned rows.  x_scale:
+ * device f32 [Mtok].  Allocates nothing. */
+nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt,
+                        void* Xq, int64_t ldq, float* x_scale, nm_stream_t stream);
 
 /* Per-tensor scale of a ternary layer: alpha = mean |W| over R x K, reduced in
  * f64 in a fixed order and rounded to f32 ("Sparse-BitNet", section 1-2:
- * 1.58-bit weights carry one high-precision scale).  alpha: device f32 [1].
- * ws: nm_stats_workspace(R, K) bytes. */
+ * 1.58-bit weights carry one high-precision scale).  W: f32, bf16, int8 or
+ * int32 (not FP8).  alpha: device f32 [1].  ws: nm_stats_workspace(R, K) bytes. */
 nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha,
                      void* ws, size_t ws_bytes, nm_stream_t stream);
 
@@ -225,11 +235,14 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
  *   vals/idx: 2:4 packed weight over K (Ns == 0) or over the lifted width
  *   K' = (2 - 2/Ns) K (Ns >= 3; supported Ns == 4, i.e. 6:8), rows R;
  *   ldv >= K'/2, ldi >= ceil(K'/32).
- *   xdt/vdt: BF16/BF16 (f32 accumulation) or I8/I8 (exact int32 accumulation).
- *   ydt: for BF16 inputs BF16 or F32; for I8 inputs I32 (raw sums), F32 or BF16.
+ *   xdt/vdt: BF16/BF16 (f32 accumulation), I8/I8 (exact int32 accumulation) or
+ *   FP8/FP8 (e4m3 codes; exact products, f32 accumulation).
+ *   ydt: for BF16 inputs BF16 or F32; for I8 inputs I32 (raw sums), F32 or BF16;
+ *   for FP8 inputs F32 or BF16.
  *   Float outputs are y = acc when x_scale == NULL and w_scale == 1, else
  *   y = (w_scale * x_scale[m]) * acc in f32 (x_scale NULL counts as 1).
- *   Requires K % 16 == 0 (Ns == 0) or K % 8 == 0 (Ns == 4).
+ *   Requires K % 16 (bf16) or K % 32 (one-byte types) == 0 for Ns == 0, and
+ *   K % 32 (bf16) or K % 64 (one-byte types) == 0 for Ns == 4.
  *   int8 requires K' * 127 * 127 < 2^31 so that int32 accumulation is exact.
  * ws: nm_spmm_workspace(...) bytes: 0 for most plain 2:4 shapes; split-K partials for
  * few tokens on few rows; for 6:8, the lifted activation

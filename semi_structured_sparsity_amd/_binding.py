@@ -23,10 +23,12 @@ LIB_PATH = _PKG / "libnmsparse.so"
 NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_DTYPE, NM_ERR_ALIGN, NM_ERR_WORKSPACE, NM_ERR_DEVICE, NM_ERR_ALIAS = range(9)
 STATUS_NAMES = ["NM_OK", "NM_ERR_NULL", "NM_ERR_SHAPE", "NM_ERR_PATTERN", "NM_ERR_DTYPE", "NM_ERR_ALIGN",
                 "NM_ERR_WORKSPACE", "NM_ERR_DEVICE", "NM_ERR_ALIAS"]
-NM_F32, NM_BF16, NM_I8, NM_I32 = 0, 1, 2, 3
+NM_F32, NM_BF16, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4
 NM_SCORE_HESSIAN, NM_SCORE_MAGNITUDE = 0, 1
 
-_DT = {torch.float32: NM_F32, torch.bfloat16: NM_BF16, torch.int8: NM_I8, torch.int32: NM_I32}
+# NM_FP8 travels as torch.float8_e4m3fn (OCP e4m3 codes, one byte each)
+_DT = {torch.float32: NM_F32, torch.bfloat16: NM_BF16, torch.int8: NM_I8, torch.int32: NM_I32,
+       torch.float8_e4m3fn: NM_FP8}
 _TORCH = {v: k for k, v in _DT.items()}
 
 
@@ -64,7 +66,7 @@ SIGNATURES = {
     "nm_prune_slide": (_I, [_P, _I, _I64, _P, _I64, _F, _I, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _I, _P, _I64, _P,
                             _I64, _P]),
     "nm_absmean": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _SZ, _P]),
-    "nm_quant_lift": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
+    "nm_quant_lift": (_I, [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _P]),
     "nm_spmm_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_spmm": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P, _SZ, _P]),
 }
@@ -241,13 +243,13 @@ def nm_absmean(W: torch.Tensor) -> torch.Tensor:
     return a
 
 
-def nm_quant_lift(X: torch.Tensor, Ns: int = 4) -> tuple[torch.Tensor, torch.Tensor]:
-    """Per-token int8 codes of bf16 X (lifted for Ns = 4) and their scales."""
+def nm_quant_lift(X: torch.Tensor, Ns: int = 4, qdt: int = NM_I8) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per-token int8 or FP8 codes of bf16 X (lifted for Ns = 4) and their scales."""
     Mtok, K = X.shape
     Kl = K // 8 * 12 if Ns else K
-    Xq = torch.empty((Mtok, Kl), dtype=torch.int8, device=X.device)
+    Xq = torch.empty((Mtok, Kl), dtype=_TORCH[qdt], device=X.device)
     sx = torch.empty(Mtok, dtype=torch.float32, device=X.device)
-    _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, _ptr(Xq), Kl, _ptr(sx), _stream(X)))
+    _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, qdt, _ptr(Xq), Kl, _ptr(sx), _stream(X)))
     return Xq, sx
 
 
@@ -258,7 +260,7 @@ def nm_spmm(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, R: int | Non
     R = vals.shape[0] if R is None else R
     xdt = dtype_code(X)
     if ydt is None:
-        ydt = NM_BF16 if xdt == NM_BF16 else NM_I32
+        ydt = {NM_BF16: NM_BF16, NM_I8: NM_I32, NM_FP8: NM_F32}[xdt]
     Y = out if out is not None else torch.empty((Mtok, R), dtype=_TORCH[ydt], device=X.device)
     need = raw.nm_spmm_workspace(Mtok, K, R, Ns, xdt)
     if need and (ws is None or ws.numel() < need):

@@ -27,7 +27,7 @@ __device__ __forceinline__ void store_conv(void* dst, nm_dtype vdt, int64_t j, c
     if (vdt == NM_BF16) {
         ((uint16_t*)dst)[j] = (sdt == NM_BF16) ? ((const uint16_t*)src)[i]
                                                 : (uint16_t)f32_to_bf16_bits(load_f32(src, sdt, i));
-    } else if (vdt == NM_I8) {
+    } else if (vdt == NM_I8 || vdt == NM_FP8) {   // one-byte values are copied as they are
         ((int8_t*)dst)[j] = ((const int8_t*)src)[i];
     } else if (vdt == NM_F32) {
         ((float*)dst)[j] = load_f32(src, sdt, i);
@@ -38,7 +38,7 @@ __device__ __forceinline__ void store_conv(void* dst, nm_dtype vdt, int64_t j, c
 
 __device__ __forceinline__ void store_zero(void* dst, nm_dtype vdt, int64_t j) {
     if (vdt == NM_BF16) ((uint16_t*)dst)[j] = 0;
-    else if (vdt == NM_I8) ((int8_t*)dst)[j] = 0;
+    else if (vdt == NM_I8 || vdt == NM_FP8) ((int8_t*)dst)[j] = 0;   // FP8 code 0 is +0
     else ((uint32_t*)dst)[j] = 0;
 }
 
@@ -840,7 +840,7 @@ void launch_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, i
                   nm_score_mode mode, bool select, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K,
                   int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm, nm_dtype vdt, void* vals,
                   int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s) {
-    if (Ns == 4 && (K % 8) == 0 && wdt == vdt && (wdt == NM_BF16 || wdt == NM_I8) &&
+    if (Ns == 4 && (K % 8) == 0 && wdt == vdt && (wdt == NM_BF16 || wdt == NM_I8 || wdt == NM_FP8) &&
         (!select || sdt == NM_BF16 || sdt == NM_F32)) {
         const int64_t ev = wdt == NM_BF16 ? 2 : 1;
         const bool vals_ok = (((uintptr_t)vals) & (ev == 2 ? 3 : 1)) == 0 && (ldv % 2) == 0;

@@ -33,6 +33,41 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
+// OCP FP8 e4m3 code: one byte, multiplied by v_smfmac_f32_32x32x64_fp8_fp8 with the
+// int8 instruction's operand layout and f32 accumulation.
+struct fp8e4m3 {
+    uint8_t v;
+};
+
+// Accumulator types and the sparse instruction of each operand type.  A is the
+// lane's 16 bytes of compressed values, B its 32 bytes of the dense operand, idx
+// its index bits (bf16: the lane's 16-bit half already selected).
+template <typename T>
+struct Mma {   // bf16
+    using Acc = f32x16_t;
+    using AccS = float;
+    __device__ static Acc run(i32x4_t a, i32x8_t b, Acc c, int idx) {
+        return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                         __builtin_bit_cast(bf16x16_t, b), c, idx, 0, 0);
+    }
+};
+template <>
+struct Mma<int8_t> {
+    using Acc = i32x16_t;
+    using AccS = int32_t;
+    __device__ static Acc run(i32x4_t a, i32x8_t b, Acc c, int idx) {
+        return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
+    }
+};
+template <>
+struct Mma<fp8e4m3> {
+    using Acc = f32x16_t;
+    using AccS = float;
+    __device__ static Acc run(i32x4_t a, i32x8_t b, Acc c, int idx) {
+        return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c, idx, 0, 0);
+    }
+};
+
 struct SpmmArgs {
     const uint8_t* X;      // [Mtok, ldx] elements of T
     const uint8_t* vals;   // [R, ldv] elements of T
@@ -196,7 +231,7 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
         }
     };
 
-    using AccV = typename std::conditional<sizeof(T) == 2, f32x16_t, i32x16_t>::type;
+    using AccV = typename Mma<T>::Acc;
     AccV acc[SR][ST];
 #pragma unroll
     for (int i = 0; i < SR; ++i)
@@ -239,20 +274,10 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
             for (int i = 0; i < SR; ++i)
 #pragma unroll
                 for (int j = 0; j < ST; ++j) {
-                    if constexpr (sizeof(T) == 2) {
-                        bf16x8_t av = __builtin_bit_cast(bf16x8_t, fa[i]);
-                        const uint4 b0 = fb[j][0], b1 = fb[j][1];
-                        i32x8_t bi = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                        bf16x16_t bv = __builtin_bit_cast(bf16x16_t, bi);
-                        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(av, bv, acc[i][j], (int)fi[i], 0, 0);
-                    } else {
-                        i32x4_t av = __builtin_bit_cast(i32x4_t, fa[i]);
-                        const uint4 b0 = fb[j][0], b1 = fb[j][1];
-                        i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                        acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(av, bv, acc[i][j], (int)fi[i], 0, 0);
-                    }
+                    const uint4 b0 = fb[j][0], b1 = fb[j][1];
+                    const i32x8_t bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                        (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+                    acc[i][j] = Mma<T>::run(__builtin_bit_cast(i32x4_t, fa[i]), bv, acc[i][j], (int)fi[i]);
                 }
         }
         if (more) store_step(buf ^ 1);
@@ -280,8 +305,7 @@ __global__ __launch_bounds__(WR* WT * 64) void spmm_kernel(SpmmArgs a) {
                     const auto v = acc[i][j][4 * g + e];
                     if (a.part) {
                         const int64_t o = ((int64_t)split * a.Mtok + tok) * a.R + r;
-                        if constexpr (sizeof(T) == 2) ((float*)a.part)[o] = v;
-                        else ((int32_t*)a.part)[o] = v;
+                        ((typename Mma<T>::AccS*)a.part)[o] = v;
                         continue;
                     }
                     const int64_t o = tok * a.ldy + r;
@@ -536,7 +560,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
         }
     };
 
-    using AccV = typename std::conditional<sizeof(T) == 2, f32x16_t, i32x16_t>::type;
+    using AccV = typename Mma<T>::Acc;
     AccV acc[SR][ST];
 #pragma unroll
     for (int i = 0; i < SR; ++i)
@@ -549,12 +573,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
         for (int i = 0; i < SR; ++i)
 #pragma unroll
             for (int j = 0; j < ST; ++j) {
-                if constexpr (sizeof(T) == 2)
-                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
-                                                                         __builtin_bit_cast(bf16x16_t, f.b[j]),
-                                                                         acc[i][j], (int)(f.iw[i] >> ish), 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[i], f.b[j], acc[i][j], (int)f.iw[i], 0, 0);
+                acc[i][j] = Mma<T>::run(f.a[i], f.b[j], acc[i][j], (int)(sizeof(T) == 2 ? f.iw[i] >> ish : f.iw[i]));
             }
     };
 
@@ -753,7 +772,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
             f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    using AccV = typename std::conditional<es == 2, f32x16_t, i32x16_t>::type;
+    using AccV = typename Mma<T>::Acc;
     AccV acc[SR][ST];
 #pragma unroll
     for (int i = 0; i < SR; ++i)
@@ -765,12 +784,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int i = 0; i < SR; ++i)
 #pragma unroll
             for (int j = 0; j < ST; ++j) {
-                if constexpr (es == 2)
-                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
-                                                                         __builtin_bit_cast(bf16x16_t, f.b[j]),
-                                                                         acc[i][j], (int)(f.iw[i] >> ish), 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(f.a[i], f.b[j], acc[i][j], (int)f.iw[i], 0, 0);
+                acc[i][j] = Mma<T>::run(f.a[i], f.b[j], acc[i][j], (int)(es == 2 ? f.iw[i] >> ish : f.iw[i]));
             }
     };
 
@@ -817,7 +831,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
                 const int tk = q >> 5, row = q & 31;   // Y element (token, row) of the sub-tile
                 const int src_lane = tk + 32 * ((row >> 2) & 1), e = 4 * (row >> 3) + (row & 3);
                 const int64_t gt = t0 + 32 * j + tk, gr = r0 + 32 * i + row;
-                using AccS = typename std::conditional<es == 2, float, int32_t>::type;
+                using AccS = typename Mma<T>::AccS;
                 AccS v = 0;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
@@ -897,7 +911,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
         t = t < a.Mtok ? t : a.Mtok - 1;
         xrow[j] = a.X + t * a.ldx * es;
     }
-    using AccV = typename std::conditional<es == 2, f32x16_t, i32x16_t>::type;
+    using AccV = typename Mma<T>::Acc;
     AccV acc[SRk][STk];
 #pragma unroll
     for (int i = 0; i < SRk; ++i)
@@ -932,13 +946,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
             for (int i = 0; i < SRk; ++i)
 #pragma unroll
                 for (int j = 0; j < STk; ++j) {
-                    if constexpr (es == 2)
-                        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, fa[u][i]), __builtin_bit_cast(bf16x16_t, fb[u][j]), acc[i][j],
-                            (int)fi[u][i], 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(fa[u][i], fb[u][j], acc[i][j],
-                                                                           (int)fi[u][i], 0, 0);
+                    acc[i][j] = Mma<T>::run(fa[u][i], fb[u][j], acc[i][j], (int)fi[u][i]);
                 }
     };
     // full batches of U, then the remainder as batches of U/2, U/4, ..., 1 (each branch-free)
@@ -967,7 +975,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                 const int tok = q >> 5, row = q & 31;                      // Y element (token, row) of the sub-tile
                 const int src_lane = tok + 32 * ((row >> 2) & 1), e = 4 * (row >> 3) + (row & 3);
                 const int64_t gt = t0 + 32 * j + tok, gr = r0 + 32 * i + row;
-                using AccS = typename std::conditional<es == 2, float, int32_t>::type;
+                using AccS = typename Mma<T>::AccS;
                 AccS v = 0;
                 for (int w = 0; w < KSPLIT; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
                 if (a.part) {
@@ -1131,8 +1139,9 @@ static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
 }
 
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
-    if (Ns) return lift_bytes(Mtok, K, xdt == NM_I8 ? 1 : 2) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
-    SpmmPlan p = (xdt == NM_I8) ? plan_for<int8_t>(Mtok, K, R) : plan_for<uint16_t>(Mtok, K, R);
+    if (Ns) return lift_bytes(Mtok, K, xdt == NM_BF16 ? 2 : 1) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
+    // the plan depends on the element size only (int8 and FP8 share it)
+    SpmmPlan p = (xdt == NM_BF16) ? plan_for<uint16_t>(Mtok, K, R) : plan_for<int8_t>(Mtok, K, R);
     if (p.KS <= 1) return 0;
     return (size_t)p.KS * (size_t)Mtok * (size_t)R * 4;
 }
@@ -1190,7 +1199,8 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     if (p.KS > 1) {
         const int64_t total = a.Mtok * a.R;
         const dim3 g(grid_cap(ceil_div(total, 256), 8192));
-        if (sizeof(T) == 2) hipLaunchKernelGGL(spmm_reduce_kernel<float>, g, dim3(256), 0, s, a);
+        if (std::is_same<typename Mma<T>::AccS, float>::value)
+            hipLaunchKernelGGL(spmm_reduce_kernel<float>, g, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(spmm_reduce_kernel<int32_t>, g, dim3(256), 0, s, a);
     }
     return check_launch("nm_spmm");
@@ -1213,7 +1223,7 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
     a.K = K;
     a.R = R;
     const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
-    const int64_t es = xdt == NM_I8 ? 1 : 2;
+    const int64_t es = xdt == NM_BF16 ? 2 : 1;
     a.comp_bytes = Kl / 2 * es;
     a.idx_words = (Kl + 31) / 32;   // the bitstream's last word is partial when K' % 32 == 16
     a.w_scale = w_scale;
@@ -1225,7 +1235,7 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
         const size_t xl = lift_bytes(Mtok, K, es);
         if (!ws || ws_bytes < xl) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", xl);
         const dim3 g(grid_cap(ceil_div(Mtok * (K / 8), 256), 8192));
-        if (xdt == NM_I8)
+        if (es == 1)   // int8 or FP8 codes: the lift moves bytes
             hipLaunchKernelGGL(lift_kernel<int8_t>, g, dim3(256), 0, s, (const int8_t*)X, ldx, Mtok, K, (int8_t*)ws, Kl);
         else
             hipLaunchKernelGGL(lift_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, ldx, Mtok, K,
@@ -1236,7 +1246,9 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
         ws = (uint8_t*)ws + xl;
         ws_bytes -= xl;
     }
-    return xdt == NM_I8 ? run_spmm<int8_t>(a, ws, ws_bytes, s) : run_spmm<uint16_t>(a, ws, ws_bytes, s);
+    if (xdt == NM_I8) return run_spmm<int8_t>(a, ws, ws_bytes, s);
+    if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ws, ws_bytes, s);
+    return run_spmm<uint16_t>(a, ws, ws_bytes, s);
 }
 
 }  // namespace nm

@@ -24,8 +24,8 @@ nm_status check_launch(const char* what) {
     return NM_OK;
 }
 
-static int64_t esize(nm_dtype d) { return d == NM_BF16 ? 2 : d == NM_I8 ? 1 : 4; }
-static bool dtype_ok(nm_dtype d) { return d == NM_F32 || d == NM_BF16 || d == NM_I8 || d == NM_I32; }
+static int64_t esize(nm_dtype d) { return d == NM_BF16 ? 2 : (d == NM_I8 || d == NM_FP8) ? 1 : 4; }
+static bool dtype_ok(nm_dtype d) { return d == NM_F32 || d == NM_BF16 || d == NM_I8 || d == NM_I32 || d == NM_FP8; }
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Range {
@@ -329,7 +329,7 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
     NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
     NM_REQ(alpha, NM_ERR_NULL, "%s: alpha is NULL", fn);
     NM_REQ(W || R * K == 0, NM_ERR_NULL, "%s: W is NULL", fn);
-    NM_REQ(dtype_ok(wdt), NM_ERR_DTYPE, "%s: unknown dtype", fn);
+    NM_REQ(dtype_ok(wdt) && wdt != NM_FP8, NM_ERR_DTYPE, "%s: W must be f32, bf16, int8 or int32", fn);
     NM_REQ(ldw >= K, NM_ERR_SHAPE, "%s: ldw < K", fn);
     const size_t need = reduce_ws(R, K);
     NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
@@ -339,12 +339,13 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
     return check_launch(fn);
 }
 
-nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq,
-                        int64_t ldq, float* x_scale, nm_stream_t stream) {
+nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt,
+                        void* Xq, int64_t ldq, float* x_scale, nm_stream_t stream) {
     const char* fn = "nm_quant_lift";
     NM_REQ(Mtok >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
     NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported: no lift (Ns=0) and the 6:8 lift (Ns=4)", fn);
-    NM_REQ(xdt == NM_BF16, NM_ERR_DTYPE, "%s: X must be bf16", fn);
+    NM_REQ(xdt == NM_BF16 && (qdt == NM_I8 || qdt == NM_FP8), NM_ERR_DTYPE, "%s: X must be bf16, codes I8 or FP8",
+           fn);
     NM_REQ(K % 8 == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 8", fn);
     if (Mtok == 0 || K == 0) return NM_OK;
     NM_REQ(X && Xq && x_scale, NM_ERR_NULL, "%s: NULL argument", fn);
@@ -354,7 +355,7 @@ nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, in
            NM_ERR_ALIGN, "%s: X needs 16-byte aligned rows, Xq 4-byte (lifted) or 8-byte aligned rows", fn);
     const Range rx = span(X, Mtok, K, ldx, 2), rq = span(Xq, Mtok, Kl, ldq, 1), rs = span(x_scale, 1, Mtok, Mtok, 4);
     NM_REQ(!overlap(rq, rx) && !overlap(rs, rx) && !overlap(rq, rs), NM_ERR_ALIAS, "%s: outputs overlap", fn);
-    launch_quant_lift(X, Mtok, K, ldx, Ns, Xq, ldq, x_scale, (hipStream_t)stream);
+    launch_quant_lift(X, Mtok, K, ldx, Ns, qdt, Xq, ldq, x_scale, (hipStream_t)stream);
     return check_launch(fn);
 }
 
@@ -371,8 +372,10 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
     NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported patterns are plain 2:4 (Ns=0) and 6:8 via slide (Ns=4)",
            fn);
     NM_REQ((xdt == NM_BF16 && vdt == NM_BF16 && (ydt == NM_BF16 || ydt == NM_F32)) ||
-               (xdt == NM_I8 && vdt == NM_I8 && (ydt == NM_I32 || ydt == NM_F32 || ydt == NM_BF16)),
-           NM_ERR_DTYPE, "%s: supported: bf16 x bf16 -> bf16/f32, int8 x int8 -> int32/f32/bf16", fn);
+               (xdt == NM_I8 && vdt == NM_I8 && (ydt == NM_I32 || ydt == NM_F32 || ydt == NM_BF16)) ||
+               (xdt == NM_FP8 && vdt == NM_FP8 && (ydt == NM_F32 || ydt == NM_BF16)),
+           NM_ERR_DTYPE, "%s: supported: bf16 x bf16 -> bf16/f32, int8 x int8 -> int32/f32/bf16, fp8 x fp8 -> f32/bf16",
+           fn);
     const int64_t kmult = Ns == 0 ? (xdt == NM_BF16 ? 16 : 32) : (xdt == NM_BF16 ? 32 : 64);
     NM_REQ(K % kmult == 0, NM_ERR_SHAPE, "%s: K must be a multiple of %lld for this dtype and pattern", fn,
            (long long)kmult);

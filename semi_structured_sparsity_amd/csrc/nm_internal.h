@@ -103,8 +103,8 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
                  float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
                  void* ws, hipStream_t s);
 // sparse GEMM
-void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, int8_t* Xq, int64_t ldq,
-                       float* x_scale, hipStream_t s);
+void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt, void* Xq,
+                       int64_t ldq, float* x_scale, hipStream_t s);
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
 nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
                       const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,

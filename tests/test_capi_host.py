@@ -82,6 +82,15 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, r.nm_hdiag_hutchinson(S, 64, 100, 100, 8, 2, 1, Y, 100, S, 1 << 30, None)) == "NM_ERR_ALIGN"
     # pack dtype rule (bf16 weights cannot pack to int8)
     assert _st(nm, r.nm_pack(S, 1, 4, 8, 8, S, 1, 2, 4, 2, Y, 4, S, 1, None)) == "NM_ERR_DTYPE"
+    # FP8: only FP8 x FP8 -> f32/bf16 products, one-byte K multiples, codes from bf16 only, no FP8 absmean
+    F8 = nm.NM_FP8
+    assert _st(nm, r.nm_spmm(S, F8, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_spmm(S, F8, 4, 64, 64, S, F8, S, 8, 32, 4, 0, None, 1.0, Y, 3, 8, None, 0, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_spmm(S, F8, 4, 48, 48, S, F8, S, 8, 24, 4, 0, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_spmm(S, F8, 4, 96, 96, S, F8, S, 8, 72, 8, 4, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_quant_lift(S, 1, 4, 64, 64, 4, 0, Y, 96, S, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_quant_lift(S, F8, 4, 64, 64, 4, F8, Y, 96, S, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_absmean(S, F8, 4, 8, 8, Y, S, 1 << 20, None)) == "NM_ERR_DTYPE"
 
 
 def test_empty_inputs_are_noops(nm):
