@@ -435,6 +435,118 @@ struct RingFrag {          // fragments of one SMFMAC depth
     i32x8_t b[ST];         // X fragment per token sub-tile
 };
 
+// Words of the wave-private LDS buffer store_tile needs: SR sub-tiles x 64 lanes x 16
+// accumulators, each lane's 16 padded to 20 words (16-byte pieces of 16 consecutive lanes
+// then fall on distinct banks).
+template <int SR>
+constexpr int kStageWords = SR * 64 * 20;
+
+// Stores a wave's SR x ST accumulator tiles (rows from rw, tokens from tw).  A lane
+// holds token column l32 and rows 8*(e/4) + 4*h + e%4 of each 32x32 sub-tile.
+// bf16 tiles fully inside Y (inside) with 8-byte aligned rows are stored straight from
+// the accumulators, four consecutive rows per 8-byte store (measured as fast as staging
+// for them).  Everything else goes through a wave-private LDS buffer of kStageWords<SR>
+// words (stage, 16-byte aligned), since 4-byte outputs stored straight would scatter
+// every instruction over 32 token rows of Y: each 32-token column of sub-tiles is written
+// to LDS as whole accumulator vectors (stores of single extracted elements have been
+// miscompiled), read back as 4-row runs of one token (a lane's elements 4q..4q+3 are 4
+// consecutive rows), and stored as whole runs of Y's rows (32 lanes per token, 4
+// outputs per lane), scaled and converted on the way.  The caller has finished every
+// other use of the buffer.
+template <typename T, int SR, int ST>
+__device__ __forceinline__ void store_tile(const SpmmArgs& a, const typename Mma<T>::Acc (&acc)[SR][ST], int64_t rw,
+                                           int64_t tw, bool inside, uint32_t* stage, int lane) {
+    using AccV = typename Mma<T>::Acc;
+    using AccS = typename Mma<T>::AccS;
+    static_assert(SR == 4, "one token row of the wave's tile (4 sub-tiles) per half-wave");
+    const int h = lane >> 5, l32 = lane & 31;
+    if (inside && a.ydt == NM_BF16 && ((uintptr_t)a.Y % 8) == 0 && (a.ldy % 4) == 0) {
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int64_t tok = tw + j * 32 + l32;
+            const float sc = a.scaled ? __fmul_rn(a.w_scale, a.x_scale ? a.x_scale[tok] : 1.0f) : 1.0f;
+#pragma unroll
+            for (int i = 0; i < SR; ++i) {
+                uint16_t* yrow = (uint16_t*)a.Y + tok * a.ldy + rw + i * 32 + 4 * h;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float f[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = (float)acc[i][j][4 * g + e];
+                        if (a.scaled) f[e] = __fmul_rn(sc, f[e]);
+                    }
+                    *(uint2*)(yrow + 8 * g) = make_uint2(f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
+                                                         f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16));
+                }
+            }
+        }
+        return;
+    }
+    const int es = a.ydt == NM_BF16 ? 2 : 4;
+    // 16-byte (4-byte outputs) or 8-byte (bf16) vector stores need aligned rows of Y
+    const bool vec = ((uintptr_t)a.Y % (4 * es)) == 0 && (a.ldy * es) % (4 * es) == 0;
+    // reader: lane l32 of a half-wave takes rows 4*l32 .. 4*l32+3 of the wave's 128, which
+    // are elements 4q .. 4q+3 of lane (token + 32 h') in sub-tile i
+    const int ri = l32 >> 3, rq = (l32 & 7) >> 1, rh = l32 & 1;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i) *(AccV*)&stage[(i * 64 + lane) * 20] = acc[i][j];
+        // lgkmcnt(0): this wave's LDS writes are done before any lane reads another's
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int tk = 2 * p + h;   // lanes 0-31 and 32-63 take two tokens per pass
+            const int64_t tok = tw + j * 32 + tk;
+            const uint4 raw = *(const uint4*)&stage[(ri * 64 + tk + 32 * rh) * 20 + 4 * rq];
+            const int64_t r = rw + 4 * l32;
+            if (tok >= a.Mtok || r >= a.R) continue;
+            const AccS v[4] = {__builtin_bit_cast(AccS, raw.x), __builtin_bit_cast(AccS, raw.y),
+                               __builtin_bit_cast(AccS, raw.z), __builtin_bit_cast(AccS, raw.w)};
+            const int64_t o = tok * a.ldy + r;
+            const bool full = vec && r + 3 < a.R;
+            if (a.ydt == NM_I32) {
+                if (full) {
+                    *(uint4*)((int32_t*)a.Y + o) = raw;
+                } else {
+                    for (int e = 0; e < 4 && r + e < a.R; ++e) ((int32_t*)a.Y)[o + e] = (int32_t)v[e];
+                }
+                continue;
+            }
+            float f[4];
+            if (a.scaled) {
+                const float sc = __fmul_rn(a.w_scale, a.x_scale ? a.x_scale[tok] : 1.0f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[e] = __fmul_rn(sc, (float)v[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[e] = (float)v[e];
+            }
+            if (a.ydt == NM_F32) {
+                if (full) {
+                    *(float4*)((float*)a.Y + o) = make_float4(f[0], f[1], f[2], f[3]);
+                } else {
+                    for (int e = 0; e < 4 && r + e < a.R; ++e) ((float*)a.Y)[o + e] = f[e];
+                }
+            } else {
+                if (full) {
+                    *(uint2*)((uint16_t*)a.Y + o) = make_uint2(f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16),
+                                                               f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16));
+                } else {
+                    for (int e = 0; e < 4 && r + e < a.R; ++e) ((uint16_t*)a.Y)[o + e] = (uint16_t)f32_to_bf16_bits(f[e]);
+                }
+            }
+        }
+        // the next column of sub-tiles overwrites the buffer only after every lane has read it
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+}
+
 // NS-stage LDS ring of KB bytes of X per token per stage; see the comment block above.
 template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int OCC = 1, int IG = 1>
 __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs a) {
@@ -620,54 +732,230 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     if (S < nsteps) stage(S, std::false_type{});
     wait_vm_all();
 
-    // Epilogue.  Lane holds token column l32 and rows 8*(e/4) + 4*h + e%4 of
-    // each 32x32 sub-tile.  Tiles fully inside Y with plain bf16 output take
-    // 8-byte vector stores with no per-element tests.
-    const bool fast = (r0 + RG::BR <= a.R) && (t0 + RG::BT <= a.Mtok) && !a.scaled && a.ydt == NM_BF16;
-    if (fast) {
-#pragma unroll
-        for (int i = 0; i < SR; ++i)
-#pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                const int64_t tok = t0 + (wt * ST + j) * 32 + l32;
-                uint16_t* yrow = (uint16_t*)a.Y + tok * a.ldy + r0 + (wr * SR + i) * 32 + 4 * h;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t w0 = f32_to_bf16_bits((float)acc[i][j][4 * g]) |
-                                        (f32_to_bf16_bits((float)acc[i][j][4 * g + 1]) << 16);
-                    const uint32_t w1 = f32_to_bf16_bits((float)acc[i][j][4 * g + 2]) |
-                                        (f32_to_bf16_bits((float)acc[i][j][4 * g + 3]) << 16);
-                    *(uint2*)(yrow + 8 * g) = make_uint2(w0, w1);
-                }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SR; ++i)
-#pragma unroll
-            for (int j = 0; j < ST; ++j) {
-                const int64_t tok = t0 + (wt * ST + j) * 32 + l32;
-                const bool tok_ok = tok < a.Mtok;
-                const float xs = (a.scaled && a.x_scale && tok_ok) ? a.x_scale[tok] : 1.0f;
-                const float sc = __fmul_rn(a.w_scale, xs);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t r = r0 + (wr * SR + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-                    if (tok_ok && r < a.R) {
-                        const auto v = acc[i][j][e];
-                        const int64_t o = tok * a.ldy + r;
-                        if (a.ydt == NM_I32) {
-                            ((int32_t*)a.Y)[o] = (int32_t)v;
-                        } else {
-                            const float f = a.scaled ? __fmul_rn(sc, (float)v) : (float)v;
-                            if (a.ydt == NM_F32) ((float*)a.Y)[o] = f;
-                            else ((uint16_t*)a.Y)[o] = (uint16_t)f32_to_bf16_bits(f);
-                        }
-                    }
-                }
-            }
-    }
+    // every wave has finished reading the ring: its LDS becomes the output staging buffers
+    __syncthreads();
+    static_assert(RG::LDS >= RG::NW * kStageWords<SR> * 4, "staging buffers fit in the ring");
+    store_tile<T, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + RG::BR <= a.R && t0 + RG::BT <= a.Mtok,
+                          (uint32_t*)smem + wave * kStageWords<SR>, lane);
 }
 
+// ------------------------------------------------------------------ split ring kernel (256 x 256 tiles)
+// A 256 x 256 tile moves about a third fewer bytes per multiply-add than the 256 x 128
+// tile of the ring kernel, but a whole stage of it (256 bytes of X per token) does not
+// fit twice in LDS, and a 128-byte stage leaves each weight row's values for the stage
+// in half a line (a DMA instruction costs the same per line touched, whatever it uses).
+// Here the operands travel in separate buffers, each loaded in whole 128-byte lines:
+//   X      : a two-stage ring of 128 bytes per token per stage,
+//   values : groups of two stages (128 bytes per weight row), double-buffered,
+//   indices: groups of 64 bytes per weight row (IGS stages), double-buffered, each
+//            loaded in IB batches of rows, one batch per value group.
+// A loop iteration multiplies one value group (two stages).  At its top (after the
+// barrier that ends the previous group) it issues X stage 2g+1, the next value group and
+// one index batch; between its two stages it issues X stage 2g+2.  Every load is waited
+// for with an exact s_waitcnt vmcnt count, as loads of a wave complete in order.  Eight
+// waves (two per SIMD) of 128 x 64 each cover the tile; LDS holds exactly 160 KB.
+// Requires an even stage count (K a multiple of 256 bytes of X per token).
+template <typename T, int SR, int ST, int WRN, int WTN, int IP = 16>
+struct Ring2 {
+    static constexpr int NW = WRN * WTN;
+    static constexpr int BR = WRN * SR * 32;           // weight rows per block
+    static constexpr int BT = WTN * ST * 32;           // tokens per block
+    static constexpr int KB = 128;                     // X bytes per token per stage
+    static constexpr int KO = KB / (int)sizeof(T);     // columns per stage
+    static constexpr int KDEP = sizeof(T) == 2 ? 32 : 64;
+    static constexpr int ND = KO / KDEP;               // SMFMAC depths per stage (2)
+    static constexpr int AROW = KO / 2 * (int)sizeof(T);   // value bytes per row per stage (64)
+    static constexpr int AI = KO / 32;                 // index words per row per stage
+    static constexpr int IGS = 64 / (AI * 4);          // stages per index group
+    static constexpr int IB = IGS / 2;                 // index batches per group (one per value group)
+    static constexpr int XSTAGE = BT * KB;
+    static constexpr int AGRP = BR * 2 * AROW;         // one value group: two stages
+    static constexpr int IGRP = BR * 64;               // one index group
+    static constexpr int X_OFF = 0;
+    static constexpr int A_OFF = 2 * XSTAGE;
+    static constexpr int I_OFF = A_OFF + 2 * AGRP;
+    static constexpr int LDS = I_OFF + 2 * IGRP;
+    static constexpr int NBX = XSTAGE / 1024 / NW;     // X loads per wave per stage
+    static constexpr int NAG = AGRP / 1024 / NW;       // value loads per wave per group
+    static constexpr int NIG = IGRP / IB / (64 * IP) / NW;   // index loads (IP bytes per lane) per wave per batch
+    static_assert(ND == 2 && AROW == 64 && 2 * AROW == 128, "two depths of 64 value bytes per stage");
+    static_assert(IGS >= 2 && IGS % 2 == 0 && IB >= 1, "index groups cover whole value groups");
+    static_assert(NBX >= 1 && NAG >= 1 && NIG >= 1, "tile too small for its waves");
+    static_assert(XSTAGE % (1024 * NW) == 0 && AGRP % (1024 * NW) == 0 && IGRP % (IB * 64 * IP * NW) == 0,
+                  "loads must split evenly over the waves");
+    static_assert(IP == 16 || IP == 4, "index loads of 16 or 4 bytes per lane");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(NBX + NAG + NIG < 64, "vmcnt is a 6-bit field");
+    // 16-byte chunk swizzles (conflict-free 16-lane LDS reads):
+    //   value group row r (8 chunks): logical c at c ^ ((r >> 1) & 7)
+    //   X token t (8 chunks): logical c at c ^ ((t >> 1) & 7)
+    //   index group row r (4 pieces): logical p at p ^ ((r >> 2) & 3)
+    __device__ static int swa(int r) { return (r >> 1) & 7; }
+    __device__ static int swb(int t) { return (t >> 1) & 7; }
+    __device__ static int swi(int r) { return (r >> 2) & 3; }
+};
+
+template <typename T, int SR, int ST, int WRN, int WTN, int IP = 16>
+__global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs a) {
+    using RG = Ring2<T, SR, ST, WRN, WTN, IP>;
+    using FR = RingFrag<SR, ST>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[RG::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WRN, wt = wave / WRN;
+    int tr, tt;
+    tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
+    const int64_t r0 = (int64_t)tr * RG::BR, t0 = (int64_t)tt * RG::BT;
+    const int nsteps = a.nsteps;              // even, >= 2
+    const int NG = nsteps >> 1;               // value groups = loop iterations
+    const int NIGR = (nsteps + RG::IGS - 1) / RG::IGS;   // index groups
+    const uint32_t sbase = lds_addr(smem);
+    const int64_t es = sizeof(T);
+    // the last IP index bytes of a row (a partial last index group is clamped to them)
+    const uint32_t ilast = (uint32_t)(nsteps * RG::AI * 4 - IP);
+
+    const void* baseA = uniform_ptr(a.vals + r0 * a.ldv * es);
+    const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
+    const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
+    const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
+    uint32_t oA[RG::NAG], oI[RG::NIG], oB[RG::NBX];
+    int pI[RG::NIG];
+#pragma unroll
+    for (int i = 0; i < RG::NAG; ++i) {
+        const int q = (wave * RG::NAG + i) * 64 + lane;   // 16-byte chunk of the group buffer, row-major
+        const int row = q >> 3, c = (q & 7) ^ RG::swa(row);
+        const int64_t gr = row < rmax ? row : rmax;
+        oA[i] = (uint32_t)(gr * a.ldv * es + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < RG::NIG; ++i) {
+        // IP-byte unit q of one batch; row within the batch (batches start at multiples of
+        // 16 rows, so the swizzle of the batch-relative row equals that of the absolute row)
+        // and the unit's logical byte offset in the row's 64 bytes
+        const int q = (wave * RG::NIG + i) * 64 + lane;
+        const int row = q / (64 / IP), u = q % (64 / IP);
+        const int pb = u * IP;                                  // physical byte in the row
+        oI[i] = (uint32_t)row;
+        pI[i] = (((pb >> 4) ^ RG::swi(row)) << 4) | (pb & 15);  // logical byte
+    }
+#pragma unroll
+    for (int i = 0; i < RG::NBX; ++i) {
+        const int row = (wave * RG::NBX + i) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ RG::swb(row);
+        const int64_t gt = row < tmax ? row : tmax;
+        oB[i] = (uint32_t)(gt * a.ldx * es + c * 16);
+    }
+    auto issue_x = [&](int s) __attribute__((always_inline)) {
+        const uint32_t st = sbase + (uint32_t)(RG::X_OFF + (s & 1) * RG::XSTAGE);
+#pragma unroll
+        for (int i = 0; i < RG::NBX; ++i)
+            dma16s(st + (wave * RG::NBX + i) * 1024, baseB, oB[i] + (uint32_t)(s * RG::KB));
+    };
+    auto issue_a = [&](int g) __attribute__((always_inline)) {
+        const uint32_t st = sbase + (uint32_t)(RG::A_OFF + (g & 1) * RG::AGRP);
+#pragma unroll
+        for (int i = 0; i < RG::NAG; ++i)
+            dma16s(st + (wave * RG::NAG + i) * 1024, baseA, oA[i] + (uint32_t)(g * 2 * RG::AROW));
+    };
+    // batch b of index group j: rows [b * BR / IB, (b + 1) * BR / IB)
+    auto issue_i = [&](int j, int b) __attribute__((always_inline)) {
+        const uint32_t st = sbase + (uint32_t)(RG::I_OFF + (j & 1) * RG::IGRP + b * (RG::IGRP / RG::IB));
+#pragma unroll
+        for (int i = 0; i < RG::NIG; ++i) {
+            const int row = b * (RG::BR / RG::IB) + (int)oI[i];
+            const int64_t gr = row < rmax ? row : rmax;
+            uint32_t off = (uint32_t)(j * 64 + pI[i]);
+            off = off < ilast ? off : ilast;
+            if constexpr (IP == 16) dma16s(st + (wave * RG::NIG + i) * 1024, baseI, (uint32_t)(gr * a.ldi * 4) + off);
+            else dma4s(st + (wave * RG::NIG + i) * 256, baseI, (uint32_t)(gr * a.ldi * 4) + off);
+        }
+    };
+
+    const int h = lane >> 5, l32 = lane & 31;
+    auto read_depth = [&](int s, int d, FR& f) __attribute__((always_inline)) {
+        const int g = s >> 1, ss = s & 1, j = s / RG::IGS, si = s % RG::IGS;
+        const uint8_t* sA = smem + RG::A_OFF + (g & 1) * RG::AGRP;
+        const uint32_t* sI = (const uint32_t*)(smem + RG::I_OFF + (j & 1) * RG::IGRP);
+        const uint8_t* sB = smem + RG::X_OFF + (s & 1) * RG::XSTAGE;
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int row = (wr * SR + i) * 32 + l32;
+            f.a[i] = *(const i32x4_t*)(sA + row * 128 + ((4 * ss + 2 * d + h) ^ RG::swa(row)) * 16);
+            // index word w of the row's group: piece w / 4 (swizzled), word w % 4
+            const int w = si * RG::AI + (sizeof(T) == 2 ? d : 2 * d + h);
+            f.iw[i] = sI[row * 16 + ((w >> 2) ^ RG::swi(row)) * 4 + (w & 3)];
+        }
+#pragma unroll
+        for (int jj = 0; jj < ST; ++jj) {
+            const int tok = (wt * ST + jj) * 32 + l32;
+            const uint8_t* trow = sB + tok * RG::KB;
+            const int sw = RG::swb(tok);
+            const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ sw) * 16);
+            const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ sw) * 16);
+            f.b[jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    using AccV = typename Mma<T>::Acc;
+    AccV acc[SR][ST];
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[i][j] = AccV{};
+    const uint32_t ish = 16u * (uint32_t)h;
+    auto mfmas = [&](const FR& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                acc[i][j] = Mma<T>::run(f.a[i], f.b[j], acc[i][j], (int)(sizeof(T) == 2 ? f.iw[i] >> ish : f.iw[i]));
+    };
+
+    // Issue order: prologue [values 0, index group 0, X 0]; top(g) [X 2g+1, values g+1,
+    // index batch g % IB of group g / IB + 1]; mid(g) [X 2g+2].  Loads past the end are
+    // not issued; the waits count exactly the loads issued after the ones needed.  Each
+    // depth's fragments are read from LDS while the previous depth's SMFMACs issue.
+    constexpr int NAG = RG::NAG, NIG = RG::NIG;
+    FR fa, fb;
+    issue_a(0);
+#pragma unroll
+    for (int b = 0; b < RG::IB; ++b) issue_i(0, b);
+    issue_x(0);
+    wait_vm_barrier<0>();
+    read_depth(0, 0, fa);
+    for (int g = 0; g < NG; ++g) {
+        const int s0 = 2 * g;
+        const bool more = g + 1 < NG;                     // X 2g+2, values g+1 exist
+        const bool it = g / RG::IB + 1 < NIGR;            // a next index group exists
+        issue_x(s0 + 1);
+        if (more) issue_a(g + 1);
+        if (it) issue_i(g / RG::IB + 1, g % RG::IB);
+        read_depth(s0, 1, fb);
+        mfmas(fa);
+        // mid(g): X s0+1 done; the values and index batch of top(g) may stay in flight
+        if (more && it) wait_vm_barrier<NAG + NIG>();
+        else if (more) wait_vm_barrier<NAG>();
+        else wait_vm_barrier<0>();
+        read_depth(s0 + 1, 0, fa);
+        if (more) issue_x(s0 + 2);
+        mfmas(fb);
+        read_depth(s0 + 1, 1, fb);
+        mfmas(fa);
+        if (more) {
+            // top(g+1): X s0+2 was the last load issued, so everything is waited for
+            wait_vm_barrier<0>();
+            read_depth(s0 + 2, 0, fa);
+        }
+        mfmas(fb);
+    }
+    wait_vm_all();
+
+    // every wave has finished reading the ring: its LDS becomes the output staging buffers
+    __syncthreads();
+    static_assert(RG::LDS >= RG::NW * kStageWords<SR> * 4, "staging buffers fit in the ring");
+    store_tile<T, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + RG::BR <= a.R && t0 + RG::BT <= a.Mtok,
+                          (uint32_t*)smem + wave * kStageWords<SR>, lane);
+}
 
 // ------------------------------------------------------------------ K-split ring kernel (up to 256 tokens)
 // With up to 256 tokens the 256-row tiles of the ring kernel are too few to fill the
@@ -1029,13 +1317,13 @@ struct SpmmPlan {
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
-// Ring shapes (T, SR, ST, KB, NS, WRN, WTN):
-//   narrow: 256 x 128 tile, 4 waves (one per SIMD), 2 stages of 256 B of X per token
-//   big   : 256 x 256 tile, 8 waves (two per SIMD), 3 stages of 128 B; bf16 only (the int8
-//           index rows of a 128-byte stage do not split over 8 waves)
-// (6:8 products with many tokens run here on the lifted activation.)
+// Many-token tiles (6:8 products with many tokens run here on the lifted activation):
+//   narrow: ring kernel (T, SR, ST, KB, NS, WRN, WTN), 256 x 128 tile, 4 waves (one per
+//           SIMD), 2 stages of 256 B of X per token
+//   big   : split ring kernel (T, SR, ST, WRN, WTN, IP), 256 x 256 tile, 8 waves (two per
+//           SIMD); bf16 index batches load 4 bytes per lane (16 do not split over 8 waves)
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
-#define NM_RING_BIG uint16_t, 4, 2, 128, 3, 2, 4
+#define NM_RING_BIG T, 4, 2, 2, 4, (sizeof(T) == 2 ? 4 : 16)
 
 template <typename T>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
@@ -1061,14 +1349,13 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
         }
     }
     p.large = Mtok > 128;
-    using RB = Ring<NM_RING_BIG>;
+    using RB = Ring2<NM_RING_BIG>;
     using RN = Ring<NM_RING_NARROW>;
     p.ring = ring_ok && p.large && (K % RN::KO) == 0;
-    // the big tile moves a third fewer bytes per MAC than the narrow one but needs
-    // every LDS byte of a CU; with fewer than two rounds of its tiles on 256 CUs the
-    // narrow tile's finer grain balances better (measured on the 2048-token layers)
-    p.big = p.ring && sizeof(T) == 2 && (K % RB::KO) == 0 &&
-            ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 512;
+    // the big tile moves about a third fewer bytes per multiply-add; with fewer of its
+    // tiles than CUs the narrow tile's finer grain fills the chip better (measured: 11008
+    // rows x 2048 tokens (344 big tiles) run 7% faster big, 4096 x 2048 (128) 20% slower)
+    p.big = p.ring && (K % (2 * RB::KO)) == 0 && ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 256;
     const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
     const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
@@ -1183,11 +1470,9 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         hipLaunchKernelGGL((spmm_skinny_kernel<T, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
         {
-            if constexpr (sizeof(T) == 2) {
-                if (p.big) {
-                    hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
-                    return check_launch("nm_spmm");
-                }
+            if (p.big) {
+                hipLaunchKernelGGL((spmm_ring2_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
+                return check_launch("nm_spmm");
             }
             // bf16: index words loaded 4 stages at a time (whole 64-byte runs of a row)
             hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);

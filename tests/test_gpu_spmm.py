@@ -54,20 +54,40 @@ SHAPES = [  # (tokens, R, K): few-token kernel (with and without a K split over 
 ]
 
 
-@pytest.mark.parametrize("Mt,R,K", [(4096, 8192, 128), (4100, 8200, 192)])
-def test_spmm_big_tile_integer_exact_sampled(nm, Mt, R, K):
-    """Shapes with >= 512 tiles of 256 x 256 take the 8-wave ring kernel.  Integer-valued
-    inputs make every sum exact; outputs are compared on a random sample plus the whole
-    ragged last row and column of tiles."""
+@pytest.mark.parametrize("Mt,R,K,dt", [(4096, 8192, 128, "bf16"), (4100, 8200, 384, "bf16"), (2100, 8200, 1152, "bf16"),
+                                       (4100, 8200, 192, "bf16"), (2100, 8200, 768, "i8"), (2100, 8300, 1280, "fp8")])
+def test_spmm_big_tile_integer_exact_sampled(nm, Mt, R, K, dt):
+    """Shapes with >= 256 tiles of 256 x 256 take the split-ring kernel (K = 192 falls back
+    to the register-staged one): stage counts of one value group, and ones that end mid
+    index group (clamped index loads), ragged last tiles, all three operand types.
+    Integer-valued inputs make every sum exact; outputs are compared on a random sample
+    plus the whole ragged last row and column of tiles."""
     g = np.random.default_rng(Mt + R + K)
-    X = _int_bf16(g, (Mt, K), 8)
-    W = _int_bf16(g, (R, K), 8)
-    mask, vals, idx = _pack_case(W, 0, score=O.score(W, None, 0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32))
-    v, i = _to_dev(vals, idx)
-    Y = nm.nm_spmm(np_bf16(X).to(dev()), v, i, R=R, ydt=nm.NM_F32).cpu().numpy()
+    if dt == "bf16":
+        X, W = _int_bf16(g, (Mt, K), 8), _int_bf16(g, (R, K), 8)
+        Xo, Wo = X, W
+    elif dt == "i8":
+        X, W = g.integers(-8, 9, (Mt, K)).astype(np.int8), g.integers(-8, 9, (R, K)).astype(np.int8)
+        Xo, Wo = X, W
+    else:
+        X = O.e4m3_encode(g.integers(-8, 9, (Mt, K)).astype(np.float32))
+        W = O.e4m3_encode(g.integers(-8, 9, (R, K)).astype(np.float32))
+        Xo, Wo = O.e4m3_decode(X), O.e4m3_decode(W)
+    S = np.abs(Wo.astype(np.float32) if dt != "bf16" else O.bf16_to_f32(W)) + g.random((R, K)).astype(np.float32)
+    mask = O.topn_mask(S, 2, 4)
+    vals, idx = O.pack(W.view(np.int8) if dt == "fp8" else W, mask, 2, 4)
+    if dt == "bf16":
+        v, Xd = np_bf16(vals).to(dev()), np_bf16(X).to(dev())
+    elif dt == "i8":
+        v, Xd = torch.from_numpy(vals).to(dev()), torch.from_numpy(X).to(dev())
+    else:
+        v = torch.from_numpy(vals.view(np.uint8)).view(torch.float8_e4m3fn).to(dev())
+        Xd = torch.from_numpy(X).view(torch.float8_e4m3fn).to(dev())
+    i = torch.from_numpy(idx.view(np.int32)).to(dev())
+    Y = nm.nm_spmm(Xd, v, i, R=R, ydt=nm.NM_I32 if dt == "i8" else nm.NM_F32).cpu().numpy()
     tm = np.concatenate([g.integers(0, Mt, 20000), np.repeat(np.arange(Mt - 260, Mt), 8), g.integers(0, Mt, 4096)])
     ro = np.concatenate([g.integers(0, R, 20000), g.integers(0, R, 260 * 8), g.integers(R - 260, R, 4096)])
-    ref = O.masked_matmul_at(X, W, mask, tm, ro)
+    ref = O.masked_matmul_at(Xo, Wo, mask, tm, ro)
     assert np.array_equal(Y[tm, ro].astype(np.float64), ref)
 
 
