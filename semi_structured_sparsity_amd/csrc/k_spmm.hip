@@ -1312,6 +1312,7 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
     bool large, ring, big;
+    int64_t split_rows;  // > 0: big tiles on rows [0, split_rows), narrow tiles on the rest
     int mid;     // K-split ring: 0 none, else 32-token sub-tiles per block (1, 2 or 4)
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
@@ -1324,6 +1325,18 @@ struct SpmmPlan {
 //           SIMD); bf16 index batches load 4 bytes per lane (16 do not split over 8 waves)
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
 #define NM_RING_BIG T, 4, 2, 2, 4, (sizeof(T) == 2 ? 4 : 16)
+
+// Compute units of the current device (cached per device).
+static int64_t device_cus() {
+    static int64_t cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        cache[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    }
+    return cache[dev];
+}
 
 template <typename T>
 static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
@@ -1355,7 +1368,33 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     // the big tile moves about a third fewer bytes per multiply-add; with fewer of its
     // tiles than CUs the narrow tile's finer grain fills the chip better (measured: 11008
     // rows x 2048 tokens (344 big tiles) run 7% faster big, 4096 x 2048 (128) 20% slower)
-    p.big = p.ring && (K % (2 * RB::KO)) == 0 && ceil_div(R, RB::BR) * ceil_div(Mtok, RB::BT) >= 256;
+    // Tile choice by whole rounds of tiles over the CUs.  The big tile moves about a third
+    // fewer bytes per multiply-add; a round of big tiles takes about 1.5x a round of
+    // narrow ones (1.4x on 11008 rows x 2048 tokens, 1.8x on 28672 x 8192).  Candidates:
+    // all narrow, all big, and whole rounds of big tiles over the first rows with the
+    // remaining rows in narrow tiles (a second launch), so that a short last round of big
+    // tiles becomes a round of half-size ones.
+    p.big = false;
+    p.split_rows = 0;
+    if (p.ring && (K % (2 * RB::KO)) == 0) {
+        const int64_t cus = device_cus();
+        const int64_t ttb = ceil_div(Mtok, RB::BT), tb = ceil_div(R, RB::BR) * ttb;
+        const int64_t ttn = ceil_div(Mtok, RN::BT), tn = ceil_div(R, RN::BR) * ttn;
+        int64_t best = 2 * ceil_div(tn, cus);
+        if (3 * ceil_div(tb, cus) < best) {
+            best = 3 * ceil_div(tb, cus);
+            p.big = true;
+        }
+        const int64_t rtb = (tb / cus) * cus / ttb;   // big row tiles that fill whole rounds
+        if (rtb >= 1 && rtb * RB::BR < R) {
+            const int64_t rest = R - rtb * RB::BR;
+            const int64_t c = 3 * ceil_div(rtb * ttb, cus) + 2 * ceil_div(ceil_div(rest, RN::BR) * ttn, cus);
+            if (c < best) {
+                p.big = false;
+                p.split_rows = rtb * RB::BR;
+            }
+        }
+    }
     const int BR = p.ring ? (p.big ? RB::BR : RN::BR) : 128;
     const int BT = p.ring ? (p.big ? RB::BT : RN::BT) : (p.large ? 128 : 32);
     p.tiles_r = (int)ceil_div(R, BR);
@@ -1469,14 +1508,31 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     } else if (p.skinny == 3) {
         hipLaunchKernelGGL((spmm_skinny_kernel<T, 2, 4, 4, 4>), dim3((unsigned)ceil_div(a.R, 64), p.KS), dim3(256), 0, s, a);
     } else if (p.ring) {
-        {
-            if (p.big) {
-                hipLaunchKernelGGL((spmm_ring2_kernel<NM_RING_BIG>), grid, dim3(512), 0, s, a);
-                return check_launch("nm_spmm");
-            }
+        using RB = Ring2<NM_RING_BIG>;
+        using RN = Ring<NM_RING_NARROW>;
+        // one launch on rows [r_begin, r_end) of the product
+        auto launch = [&](bool big, int64_t r_begin, int64_t r_end) {
+            SpmmArgs b = a;
+            const int64_t es = sizeof(T), ys = a.ydt == NM_BF16 ? 2 : 4;
+            b.vals = a.vals + r_begin * a.ldv * es;
+            b.idx = a.idx + r_begin * a.ldi;
+            b.Y = (uint8_t*)a.Y + r_begin * ys;
+            b.R = r_end - r_begin;
+            b.tiles_r = (int)ceil_div(b.R, big ? RB::BR : RN::BR);
+            b.tiles_t = (int)ceil_div(a.Mtok, big ? RB::BT : RN::BT);
+            b.nsteps = (int)(a.K / (big ? RB::KO : RN::KO));
+            const dim3 g((unsigned)(b.tiles_r * b.tiles_t));
+            if (big) hipLaunchKernelGGL((spmm_ring2_kernel<NM_RING_BIG>), g, dim3(512), 0, s, b);
             // bf16: index words loaded 4 stages at a time (whole 64-byte runs of a row)
-            hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), g, dim3(256), 0, s, b);
+        };
+        if (p.split_rows > 0) {
+            launch(true, 0, p.split_rows);
+            launch(false, p.split_rows, a.R);
+        } else {
+            launch(p.big, 0, a.R);
         }
+        return check_launch("nm_spmm");
     } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
     else

@@ -54,12 +54,15 @@ SHAPES = [  # (tokens, R, K): few-token kernel (with and without a K split over 
 ]
 
 
-@pytest.mark.parametrize("Mt,R,K,dt", [(4096, 8192, 128, "bf16"), (4100, 8200, 384, "bf16"), (2100, 8200, 1152, "bf16"),
-                                       (4100, 8200, 192, "bf16"), (2100, 8200, 768, "i8"), (2100, 8300, 1280, "fp8")])
+@pytest.mark.parametrize("Mt,R,K,dt", [(4096, 8192, 128, "bf16"), (4000, 4000, 384, "bf16"), (4000, 4000, 768, "i8"),
+                                       (4100, 8200, 384, "bf16"), (2100, 8200, 1152, "bf16"), (4100, 8200, 192, "bf16"),
+                                       (2100, 8200, 768, "i8"), (2100, 8300, 1280, "fp8")])
 def test_spmm_big_tile_integer_exact_sampled(nm, Mt, R, K, dt):
-    """Shapes with >= 256 tiles of 256 x 256 take the split-ring kernel (K = 192 falls back
-    to the register-staged one): stage counts of one value group, and ones that end mid
-    index group (clamped index loads), ragged last tiles, all three operand types.
+    """Many-token shapes whose tile plan uses 256 x 256 tiles (the split-ring kernel): all
+    rows in them (the first three cases), or whole rounds of them over the first rows and
+    256 x 128 tiles on the rest (the last four; K = 192 falls back to the register-staged
+    kernel).  Stage counts of one value group, and ones that end mid index group (clamped
+    index loads), ragged last tiles, all three operand types.
     Integer-valued inputs make every sum exact; outputs are compared on a random sample
     plus the whole ragged last row and column of tiles."""
     g = np.random.default_rng(Mt + R + K)
