@@ -77,6 +77,8 @@ def _declare(L):
         "or_masked_matmul_at": (None, [P, I, I64, I64, P, I, I64, P, I64, P, P, I64, P]),
         "or_masked_matmul_i8": (I64, [P, I64, I64, I64, P, I64, I64, P, I64, P, F, P, P]),
         "or_absmean": (D, [P, I, I64]),
+        "or_lowrank_u": (None, [P, I, I64, I64, P, I, I64, P]),
+        "or_sparse_lowrank": (None, [P, I, I64, I64, P, I, I64, P, I64, P, I, P, I, I64, P]),
         "or_apply_mask_i8": (None, [P, I64, I64, P, I64, P]),
         "or_splitmix64_at": (U64, [U64, U64]),
         "or_rademacher": (I, [U64, I, I64, I64, I64]),
@@ -310,6 +312,30 @@ def masked_matmul_at(X, W, mask, rows_m, rows_o) -> np.ndarray:
     m = None if mask is None else _c(mask, np.uint8)
     lib().or_masked_matmul_at(_p(X), _dt(X), K, K, _p(W), _dt(W), K, _p(m), 0 if m is None else m.shape[1],
                               _p(rm), _p(ro), rm.size, _p(Y))
+    return Y
+
+
+def lowrank_u(X: np.ndarray, A: np.ndarray) -> np.ndarray:
+    """u = X A^T in double (exact value of the adapter's intermediate).  X [Mt, K], A [r, K]."""
+    X, A = _c(X), _c(A)
+    Mt, K = X.shape
+    r = A.shape[0]
+    U = np.empty((Mt, r), np.float64)
+    lib().or_lowrank_u(_p(X), _dt(X), Mt, K, _p(A), _dt(A), r, _p(U))
+    return U
+
+
+def sparse_lowrank(X: np.ndarray, W: np.ndarray, mask: np.ndarray | None, A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """Y = X (mask*W)^T + bf16(X A^T) B^T in double (SALR section 3).  A [r, K], B [R, r]."""
+    X, W, A, B = _c(X), _c(W), _c(A), _c(B)
+    Mt, K = X.shape
+    R = W.shape[0]
+    r = A.shape[0]
+    assert A.shape[1] == K and B.shape == (R, r)
+    Y = np.empty((Mt, R), np.float64)
+    m = None if mask is None else _c(mask, np.uint8)
+    lib().or_sparse_lowrank(_p(X), _dt(X), Mt, K, _p(W), _dt(W), R, _p(m), 0 if m is None else m.shape[1],
+                            _p(A), _dt(A), _p(B), _dt(B), r, _p(Y))
     return Y
 
 

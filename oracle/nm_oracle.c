@@ -32,7 +32,9 @@
  *         (activation lifting is a pure index remap, fused into the per-token
  *         quantisation) and 2C (offline packer; per request: quantise + lift,
  *         then the sparse GEMM).
- *   [SA]  "SALR" summary, Methodology 1 (magnitude pruning of the frozen base).
+ *   [SA]  "SALR" summary, Methodology 1 (magnitude pruning of the frozen base),
+ *         2 (truncated-SVD adapter of the pruning residual) and 3 (all low-rank
+ *         adapters stacked along the rank into one product).
  */
 #include <math.h>
 #include <omp.h>
@@ -504,6 +506,61 @@ void or_masked_matmul_at(const void* X, int xdt, int64_t K, int64_t ldx,
         }
         Y[q] = acc;
     }
+}
+
+/* ------------------------------------------------------------------ sparse + low-rank linear
+ * [SA] section 3 (adapter concatenation): every low-rank adapter of a layer (the
+ * fine-tuning adapter and the truncated-SVD adapter of the pruning residual, section 2)
+ * is stacked along the rank, so the layer is one structured-sparse product plus one
+ * rank-r product on the same input:
+ *   Y[m,o] = sum_k X[m,k] (mask*W)[o,k]  +  sum_j u[m,j] B[o,j],
+ *   u[m,j] = bf16( sum_k X[m,k] A[j,k] ),
+ * with A [r, K] (the stacked down-projections) and B [R, r] (the stacked
+ * up-projections).  Reading: the pages fix no precision for the adapter's
+ * intermediate; it is an activation of the layer, so it is held in bf16, rounded
+ * once (to nearest, ties to even) from its exact value.  Everything else is in double. */
+
+/* Correct bf16 rounding of a double: round to float with round-to-odd (truncate toward
+ * zero, then set the last bit when inexact), then to bf16 to nearest even; with 16 more
+ * bits than bf16 the intermediate cannot create a false tie. */
+static uint16_t bf16_of_double(double d) {
+    float f = (float)d;
+    if (isfinite(f) && (double)f != d) {
+        if (fabs((double)f) > fabs(d)) f = nextafterf(f, 0.0f);
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        u |= 1u;
+        memcpy(&f, &u, 4);
+    }
+    return f32_to_bf16(f);
+}
+
+/* u[m, j] = sum_k X[m,k] A[j,k] in double (exact value; the layer rounds it to bf16). */
+void or_lowrank_u(const void* X, int xdt, int64_t Mt, int64_t K, const void* A, int adt, int64_t r, double* U) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < Mt; ++m)
+        for (int64_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += load_as_double(X, xdt, m * K + k) * load_as_double(A, adt, j * K + k);
+            U[m * r + j] = acc;
+        }
+}
+
+void or_sparse_lowrank(const void* X, int xdt, int64_t Mt, int64_t K, const void* W, int wdt, int64_t R,
+                       const uint8_t* mask, int64_t ldm, const void* A, int adt, const void* B, int bdt, int64_t r,
+                       double* Y) {
+    double* U = (double*)malloc((size_t)(Mt * r > 0 ? Mt * r : 1) * sizeof(double));
+    or_lowrank_u(X, xdt, Mt, K, A, adt, r, U);
+    or_masked_matmul(X, xdt, Mt, K, K, W, wdt, R, K, mask, ldm, Y);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < Mt; ++m)
+        for (int64_t o = 0; o < R; ++o) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < r; ++j)
+                acc += (double)bf16_to_f32(bf16_of_double(U[m * r + j])) * load_as_double(B, bdt, o * r + j);
+            Y[m * R + o] += acc;
+        }
+    free(U);
 }
 
 /* Integer form for int8 activations and ternary int8 weights: the exact sum in

@@ -525,3 +525,74 @@ def test_anneal_projection_invariants():
         gt = np.array([[O.gate_value(float(S[r, k]), mu, sg, 0.5, 0.5, t) for k in range(K)] for r in range(R)])
         mt = ((1 - beta) * gt + beta * hb).astype(np.float32)
         assert np.array_equal(O.topn_mask(mt, 2, 4), h)
+
+
+# ------------------------------------------------------------------ sparse + low-rank linear (SALR 2-3)
+def _int_bf16(g, shape, lim):
+    return O.f32_to_bf16(g.integers(-lim, lim + 1, shape).astype(np.float32))
+
+
+def test_lowrank_u_matches_numpy():
+    g = _rng(51)
+    X, A = _int_bf16(g, (7, 40), 9), _int_bf16(g, (5, 40), 9)
+    U = O.lowrank_u(X, A)
+    assert np.array_equal(U, O.bf16_to_f32(X).astype(np.int64) @ O.bf16_to_f32(A).astype(np.int64).T)
+
+
+def test_sparse_lowrank_reduces_to_masked_product_and_to_adapter():
+    """A = 0 leaves the structured-sparse product; an empty mask leaves the adapter
+    product u B^T, with u held in bf16 (integers up to 256 are exact there)."""
+    g = _rng(52)
+    Mt, R, K, r = 6, 9, 32, 4
+    X, W = _int_bf16(g, (Mt, K), 3), _int_bf16(g, (R, K), 5)
+    A, B = _int_bf16(g, (r, K), 2), _int_bf16(g, (R, r), 7)
+    mask = O.topn_mask(O.score(W, None, 0.0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32), 2, 4)
+    zeroA = np.zeros_like(A)
+    assert np.array_equal(O.sparse_lowrank(X, W, mask, zeroA, B), O.masked_matmul(X, W, mask))
+    empty = np.zeros_like(mask)
+    Xi, Ai, Bi = (O.bf16_to_f32(t).astype(np.int64) for t in (X, A, B))
+    u = Xi @ Ai.T
+    assert np.abs(u).max() <= 256
+    assert np.array_equal(O.sparse_lowrank(X, W, empty, A, B), (u @ Bi.T).astype(np.float64))
+
+
+def test_sparse_lowrank_rounds_the_adapter_intermediate_to_bf16():
+    """u = 257 is not a bf16 value: it rounds to 256 (tie to even) and 259 to 260."""
+    K = 2
+    X = O.f32_to_bf16(np.array([[1.0, 1.0], [1.0, 3.0]], np.float32))
+    A = O.f32_to_bf16(np.array([[1.0, 256.0]], np.float32))          # u = 257, 769
+    B = O.f32_to_bf16(np.array([[1.0]], np.float32))
+    W = np.zeros((1, K), np.uint16)
+    Y = O.sparse_lowrank(X, W, None, A, B)
+    assert Y[0, 0] == 256.0 and Y[1, 0] == 768.0                       # 769 -> 768 (ulp 4, nearest)
+    A2 = O.f32_to_bf16(np.array([[3.0, 256.0]], np.float32))         # u = 259 -> 260
+    assert O.sparse_lowrank(X[:1], W, None, A2, B)[0, 0] == 260.0
+
+
+def test_sparse_lowrank_full_rank_residual_restores_dense_product():
+    """SALR section 2: the adapter carries the pruning residual E = W - mask*W.  At full
+    rank (A = I, B = E) the layer computes the dense product X W^T exactly."""
+    g = _rng(53)
+    Mt, R, K = 5, 8, 16
+    X, W = _int_bf16(g, (Mt, K), 4), _int_bf16(g, (R, K), 6)
+    mask = O.topn_mask(O.score(W, None, 0.0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32), 2, 4)
+    keep = O.mask_to_bool(mask, K)
+    E = np.where(keep, 0, O.bf16_to_f32(W)).astype(np.float32)
+    A = O.f32_to_bf16(np.eye(K, dtype=np.float32))
+    Y = O.sparse_lowrank(X, W, mask, A, O.f32_to_bf16(E))
+    dense = O.bf16_to_f32(X).astype(np.float64) @ O.bf16_to_f32(W).astype(np.float64).T
+    assert np.array_equal(Y, dense)
+
+
+def test_sparse_lowrank_concatenation_equals_separate_adapters():
+    """SALR section 3: stacking two adapters along the rank gives the same layer output as
+    applying them one after the other."""
+    g = _rng(54)
+    Mt, R, K = 6, 10, 24
+    X, W = _int_bf16(g, (Mt, K), 3), _int_bf16(g, (R, K), 4)
+    mask = O.topn_mask(O.score(W, None, 0.0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32), 2, 4)
+    A1, B1 = _int_bf16(g, (3, K), 2), _int_bf16(g, (R, 3), 3)
+    A2, B2 = _int_bf16(g, (5, K), 2), _int_bf16(g, (R, 5), 3)
+    Ycat = O.sparse_lowrank(X, W, mask, np.concatenate([A1, A2]), np.concatenate([B1, B2], axis=1))
+    base = O.masked_matmul(X, W, mask)
+    assert np.array_equal(Ycat, O.sparse_lowrank(X, W, mask, A1, B1) + O.sparse_lowrank(X, W, mask, A2, B2) - base)
