@@ -316,6 +316,19 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
             row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "hbm", R * K * 1.6875 + M * K * 2 + M * R * 2)
         else:
             row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "mfma", 2 * M * R * Kl // 2)
+    # the same layer with a stacked rank-64 low-rank adapter pair (SALR section 3):
+    # Y = X W_hat^T + bf16(X A^T) B^T; flops: the sparse product + X A^T + u B^T
+    rank, M = 64, 4096
+    A, B = synth.adapter_bf16(2, rank, K, R)
+    A, B = A.to(dev), B.to(dev)
+    X = synth.activations_bf16(2, M, K).to(dev)
+    Y = torch.empty((M, R), dtype=bf, device=dev)
+    wsl = ws_for(r.nm_spmm_lowrank_workspace(M, K, R, Ns, rank))
+    row("slide68", "NEXT-3", f"spmm lifted + rank-{rank} adapter 14336x4096 M={M}", lambda: chk(r.nm_spmm_lowrank(
+        X.data_ptr(), M, K, K, vals.data_ptr(), idx.data_ptr(), R, Kl // 2, Kl // 32, Ns, A.data_ptr(), K,
+        B.data_ptr(), rank, rank, Y.data_ptr(), nm.NM_BF16, R, wsl.data_ptr(), wsl.numel(), sh)), "mfma",
+        2 * M * R * Kl // 2 + 2 * M * K * rank + 2 * M * R * rank)
+    del A, B, X, Y, wsl
     # FP8 e4m3 precision of the same layer (SlideSparse section 3): the weight's codes slide-packed
     # under the |W| mask, the activation quantised per token and lifted once, the product over K'
     Wq = W.to(torch.float8_e4m3fn)

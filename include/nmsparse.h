@@ -253,6 +253,27 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
                   int Ns, const float* x_scale, float w_scale, void* Y, nm_dtype ydt, int64_t ldy,
                   void* ws, size_t ws_bytes, nm_stream_t stream);
 
+/* Sparse layer with stacked low-rank adapters ("SALR", section 3: every adapter of a
+ * layer, the fine-tuning one and the truncated-SVD adapter of the pruning residual of
+ * section 2, is stacked along the rank so that one product serves them all):
+ *   Y = X W_hat^T + u B^T,   u = bf16(X A^T)   (u rounded once to nearest even from its
+ *   f32 sum; every other sum in f32, output rounded once to ydt).
+ *   X: bf16 [Mtok, K] (ldx), K the original width; vals/idx: bf16 2:4 packed weight as for
+ *   nm_spmm (Ns 0, or 4 for 6:8 over K' = 3K/2); A: bf16 [rank, K] (lda), the stacked
+ *   down-projections; B: bf16 [R, rank] (ldb), the stacked up-projections (the row-major
+ *   weights of a LoRA pair of linear layers).  rank: a multiple of 8 in [8, 256].
+ *   Y: [Mtok, R] (ldy), bf16 or f32.  No scales.
+ *   Requires K % 16 (Ns 0) or K % 32 (Ns 4) == 0; X, vals, idx, A and B 16-byte aligned
+ *   with 16-byte row strides.
+ * ws: nm_spmm_lowrank_workspace(Mtok, K, R, Ns, rank) bytes (u and its K-split partials,
+ * the lifted activation for Ns 4, and for products that are not run by the many-token
+ * kernels an f32 copy of the sparse product).  Allocates nothing. */
+size_t nm_spmm_lowrank_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank);
+nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, const uint32_t* idx,
+                          int64_t R, int64_t ldv, int64_t ldi, int Ns, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int rank, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                          nm_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

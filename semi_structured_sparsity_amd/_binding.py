@@ -69,6 +69,9 @@ SIGNATURES = {
     "nm_quant_lift": (_I, [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _P]),
     "nm_spmm_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_spmm": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P, _SZ, _P]),
+    "nm_spmm_lowrank_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
+    "nm_spmm_lowrank": (_I, [_P, _I64, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _I, _P, _I, _I64,
+                             _P, _SZ, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(raw, _name)
@@ -251,6 +254,23 @@ def nm_quant_lift(X: torch.Tensor, Ns: int = 4, qdt: int = NM_I8) -> tuple[torch
     sx = torch.empty(Mtok, dtype=torch.float32, device=X.device)
     _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, qdt, _ptr(Xq), Kl, _ptr(sx), _stream(X)))
     return Xq, sx
+
+
+def nm_spmm_lowrank(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                    R: int | None = None, Ns: int = 0, ydt: int = NM_BF16, out: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W_hat^T + bf16(X A^T) B^T: sparse layer plus stacked low-rank adapters (bf16)."""
+    Mtok, K = X.shape
+    R = vals.shape[0] if R is None else R
+    rank = A.shape[0]
+    Y = out if out is not None else torch.empty((Mtok, R), dtype=_TORCH[ydt], device=X.device)
+    need = raw.nm_spmm_lowrank_workspace(Mtok, K, R, Ns, rank)
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, X.device)
+    _check(raw.nm_spmm_lowrank(_ptr(X), Mtok, K, _ld(X), _ptr(vals), _ptr(idx), R, _ld(vals), _ld(idx), Ns,
+                               _ptr(A), _ld(A), _ptr(B), _ld(B), rank, _ptr(Y), ydt, _ld(Y), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(X)))
+    return Y
 
 
 def nm_spmm(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, R: int | None = None, Ns: int = 0,

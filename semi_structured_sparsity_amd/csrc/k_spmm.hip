@@ -84,6 +84,12 @@ struct SpmmArgs {
     int ydt;
     int nsteps, KS, steps_per_split;
     int tiles_r, tiles_t;
+    // rank-r adapter term added to the accumulators (bf16 products only; rank 0: none):
+    // u [Mtok, rank] (ldu) and the stacked up-projection B [R, rank] (ldb), both bf16
+    const uint16_t* lr_u;
+    const uint16_t* lr_b;
+    int64_t ldu, ldb;
+    int rank;
 };
 
 // Per-dtype step geometry of the register-staged kernel: a step stages 128 bytes of
@@ -435,6 +441,38 @@ struct RingFrag {          // fragments of one SMFMAC depth
     i32x8_t b[ST];         // X fragment per token sub-tile
 };
 
+// Adds the adapter term sum_j u[t, j] B[o, j] to a wave's SR x ST accumulator tiles
+// (rows from rw, tokens from tw) with dense bf16 MFMA (v_mfma_f32_32x32x16_bf16), whose
+// accumulator layout equals the sparse instruction's: the B rows are the A operand (lane
+// l: row l%32, 8 consecutive ranks from 8*(l/32)), the u rows the B operand.  rank is a
+// multiple of 8, so each lane's 8 ranks are all inside or all past the end (then zero).
+// Rows and tokens past the edges read the last valid one; their outputs are not stored.
+template <int SR, int ST>
+__device__ __forceinline__ void add_lowrank(const SpmmArgs& a, f32x16_t (&acc)[SR][ST], int64_t rw, int64_t tw,
+                                            int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    for (int k0 = 0; k0 < a.rank; k0 += 16) {
+        const bool ok = k0 + 8 * h < a.rank;
+        i32x4_t bl[SR], uu[ST];
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int64_t r = rw + i * 32 + l32 < a.R ? rw + i * 32 + l32 : a.R - 1;
+            bl[i] = ok ? *(const i32x4_t*)(a.lr_b + r * a.ldb + k0 + 8 * h) : i32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int64_t t = tw + j * 32 + l32 < a.Mtok ? tw + j * 32 + l32 : a.Mtok - 1;
+            uu[j] = ok ? *(const i32x4_t*)(a.lr_u + t * a.ldu + k0 + 8 * h) : i32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bl[i]),
+                                                                   __builtin_bit_cast(bf16x8_t, uu[j]), acc[i][j], 0, 0, 0);
+    }
+}
+
 // Words of the wave-private LDS buffer store_tile needs: SR sub-tiles x 64 lanes x 16
 // accumulators, each lane's 16 padded to 20 words (16-byte pieces of 16 consecutive lanes
 // then fall on distinct banks).
@@ -731,6 +769,9 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     for (; S + 1 < nsteps; ++S) stage(S, std::true_type{});
     if (S < nsteps) stage(S, std::false_type{});
     wait_vm_all();
+    if constexpr (sizeof(T) == 2) {
+        if (a.rank > 0) add_lowrank<SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, lane);
+    }
 
     // every wave has finished reading the ring: its LDS becomes the output staging buffers
     __syncthreads();
@@ -949,6 +990,9 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
         mfmas(fb);
     }
     wait_vm_all();
+    if constexpr (sizeof(T) == 2) {
+        if (a.rank > 0) add_lowrank<SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, lane);
+    }
 
     // every wave has finished reading the ring: its LDS becomes the output staging buffers
     __syncthreads();
@@ -1309,6 +1353,101 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ adapter term ("SALR", section 3)
+// All low-rank adapters of a layer stacked along the rank: Y = X W_hat^T + u B^T with
+// u = bf16(X A^T), A [rank, K], B [R, rank].  u is computed once per call here; the
+// many-token product kernels add u B^T to their accumulators (add_lowrank), the others
+// through lowrank_epilogue_kernel.
+
+// Partial u over one K chunk per wave: block = 32 tokens x (32 RT ranks), four waves on
+// four consecutive chunks of the block's K range (gridDim.y ranges); v_mfma_f32_32x32x16_bf16
+// with the tokens as the A operand and the rank rows of A as the B operand.  Partials go
+// to P[split][Mtok][rank] (split = 4 * blockIdx.y + wave).
+template <int RT>
+__global__ __launch_bounds__(256) void lowrank_u_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                        const uint16_t* __restrict__ A, int64_t lda, int64_t M,
+                                                        int64_t K, int rank, int64_t kchunk, float* __restrict__ P) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, l32 = lane & 31;
+    const int64_t t0 = (int64_t)blockIdx.x * 32;
+    const int split = blockIdx.y * 4 + wave;
+    const int64_t kb = split * kchunk, ke = kb + kchunk < K ? kb + kchunk : K;
+    const int64_t tok = t0 + l32 < M ? t0 + l32 : M - 1;
+    const uint16_t* xr = X + tok * ldx + 8 * h;
+    f32x16_t acc[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) acc[q] = f32x16_t{};
+    const uint16_t* ar[RT];
+    bool aok[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+        const int n = q * 32 + l32;
+        aok[q] = n < rank;
+        ar[q] = A + (int64_t)(aok[q] ? n : 0) * lda + 8 * h;
+    }
+#pragma unroll 4
+    for (int64_t k = kb; k < ke; k += 16) {
+        const i32x4_t xv = *(const i32x4_t*)(xr + k);
+#pragma unroll
+        for (int q = 0; q < RT; ++q) {
+            const i32x4_t av = aok[q] ? *(const i32x4_t*)(ar[q] + k) : i32x4_t{0, 0, 0, 0};
+            acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                             __builtin_bit_cast(bf16x8_t, av), acc[q], 0, 0, 0);
+        }
+    }
+    // lane holds rank column q*32 + l32 and token rows 8*(e/4) + 4*h + e%4
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+        const int n = q * 32 + l32;
+        if (n >= rank) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t t = t0 + 8 * (e / 4) + 4 * h + (e % 4);
+            if (t < M) P[((int64_t)split * M + t) * rank + n] = acc[q][e];
+        }
+    }
+}
+
+// u[m, n] = bf16(sum of the partials in split order)
+__global__ __launch_bounds__(256) void lowrank_u_reduce_kernel(const float* __restrict__ P, int S, int64_t M, int rank,
+                                                               uint16_t* __restrict__ U) {
+    const int64_t total = M * rank;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        float v = 0.0f;
+        for (int sp = 0; sp < S; ++sp) v += P[(int64_t)sp * total + i];
+        U[i] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+// Y[m, o] = P[m, o] + sum_j u[m, j] B[o, j] (j ascending, f32), converted to a.ydt.
+__global__ __launch_bounds__(256) void lowrank_epilogue_kernel(const float* __restrict__ P, SpmmArgs a) {
+    const int64_t total = a.Mtok * a.R;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t m = i / a.R, o = i - m * a.R;
+        const uint16_t* ur = a.lr_u + m * a.ldu;
+        const uint16_t* br = a.lr_b + o * a.ldb;
+        float lr = 0.0f;
+        for (int j = 0; j < a.rank; ++j) lr = __fmaf_rn(bf16_bits_to_f32(ur[j]), bf16_bits_to_f32(br[j]), lr);
+        const float v = P[i] + lr;
+        if (a.ydt == NM_F32) ((float*)a.Y)[m * a.ldy + o] = v;
+        else ((uint16_t*)a.Y)[m * a.ldy + o] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+// K chunking of the u product: four chunks per block, blocks along K until the grid has
+// about 256 blocks, chunks of at least 256 columns (a multiple of 16).
+struct LowRankPlan {
+    int ks;           // blocks along K
+    int64_t kchunk;   // columns per wave
+    int S() const { return 4 * ks; }
+};
+static LowRankPlan lowrank_plan(int64_t M, int64_t K) {
+    LowRankPlan p{1, 0};
+    const int64_t tiles = ceil_div(M, 32);
+    while (tiles * p.ks < 256 && K / (4 * p.ks * 2) >= 256) p.ks *= 2;
+    p.kchunk = ceil_div(ceil_div(K, (int64_t)p.S()), 16) * 16;
+    return p;
+}
+
 // ------------------------------------------------------------------ host side
 struct SpmmPlan {
     bool large, ring, big;
@@ -1491,6 +1630,23 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
         if (!ws || ws_bytes < need) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", need);
         a.part = ws;
     }
+    if (a.rank > 0 && !p.ring) {
+        // the other kernels carry no adapter term: they write the sparse product in f32
+        // into the workspace and lowrank_epilogue_kernel adds the term and converts
+        const size_t pb = ((size_t)a.Mtok * (size_t)a.R * 4 + 255) & ~(size_t)255;
+        if (!ws || ws_bytes < pb) return set_error(NM_ERR_WORKSPACE, "nm_spmm_lowrank: workspace too small");
+        SpmmArgs b = a;
+        b.rank = 0;
+        b.Y = ws;
+        b.ydt = NM_F32;
+        b.ldy = a.R;
+        b.scaled = 0;
+        const nm_status st = run_spmm<T>(b, (uint8_t*)ws + pb, ws_bytes - pb, s);
+        if (st != NM_OK) return st;
+        const dim3 g(grid_cap(ceil_div(a.Mtok * a.R, 256), 65536));
+        hipLaunchKernelGGL(lowrank_epilogue_kernel, g, dim3(256), 0, s, (const float*)ws, a);
+        return check_launch("nm_spmm_lowrank");
+    }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
     if (p.mid) {
         if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 3>), grid, dim3(256), 0, s, a);
@@ -1517,6 +1673,7 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
             b.vals = a.vals + r_begin * a.ldv * es;
             b.idx = a.idx + r_begin * a.ldi;
             b.Y = (uint8_t*)a.Y + r_begin * ys;
+            if (a.rank > 0) b.lr_b = a.lr_b + r_begin * a.ldb;
             b.R = r_end - r_begin;
             b.tiles_r = (int)ceil_div(b.R, big ? RB::BR : RN::BR);
             b.tiles_t = (int)ceil_div(a.Mtok, big ? RB::BT : RN::BT);
@@ -1547,9 +1704,22 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     return check_launch("nm_spmm");
 }
 
-nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
-                      const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
-                      float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t spmm_lowrank_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank) {
+    if (Mtok <= 0 || K <= 0 || R <= 0) return 0;
+    const LowRankPlan lp = lowrank_plan(Mtok, K);
+    const size_t u = round256((size_t)Mtok * rank * 2) + round256((size_t)lp.S() * Mtok * rank * 4);
+    const int64_t Kl = Ns ? K / 8 * 12 : K;
+    const SpmmPlan p = plan_for<uint16_t>(Mtok, Kl, R);
+    const size_t f32 = p.ring ? 0 : round256((size_t)Mtok * (size_t)R * 4);
+    return u + spmm_ws(Mtok, K, R, Ns, NM_BF16) + f32;
+}
+
+static nm_status spmm_impl(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                           const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                           float w_scale, const LowRankIn* lr, void* Y, nm_dtype ydt, int64_t ldy, void* ws,
+                           size_t ws_bytes, hipStream_t s) {
     SpmmArgs a{};
     a.X = (const uint8_t*)X;
     a.vals = (const uint8_t*)vals;
@@ -1571,6 +1741,36 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
     a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
     a.ydt = (int)ydt;
     if (Mtok == 0 || R == 0) return NM_OK;
+    if (lr) {
+        // u = bf16(X A^T) from the original X, into the front of the workspace
+        const LowRankPlan lp = lowrank_plan(Mtok, K);
+        const size_t ub = round256((size_t)Mtok * lr->rank * 2), pb = round256((size_t)lp.S() * Mtok * lr->rank * 4);
+        if (!ws || ws_bytes < ub + pb) return set_error(NM_ERR_WORKSPACE, "nm_spmm_lowrank: workspace too small");
+        uint16_t* U = (uint16_t*)ws;
+        float* P = (float*)((uint8_t*)ws + ub);
+        const dim3 g((unsigned)ceil_div(Mtok, 32), (unsigned)lp.ks);
+        const int RT = (int)ceil_div(lr->rank, 32);
+        const uint16_t* Xb = (const uint16_t*)X;
+        switch (RT) {
+            case 1: hipLaunchKernelGGL(lowrank_u_kernel<1>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 2: hipLaunchKernelGGL(lowrank_u_kernel<2>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 3: hipLaunchKernelGGL(lowrank_u_kernel<3>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 4: hipLaunchKernelGGL(lowrank_u_kernel<4>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 5: hipLaunchKernelGGL(lowrank_u_kernel<5>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 6: hipLaunchKernelGGL(lowrank_u_kernel<6>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 7: hipLaunchKernelGGL(lowrank_u_kernel<7>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            default: hipLaunchKernelGGL(lowrank_u_kernel<8>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+        }
+        const dim3 gr(grid_cap(ceil_div(Mtok * lr->rank, 256), 4096));
+        hipLaunchKernelGGL(lowrank_u_reduce_kernel, gr, dim3(256), 0, s, (const float*)P, lp.S(), Mtok, lr->rank, U);
+        a.lr_u = U;
+        a.ldu = lr->rank;
+        a.lr_b = lr->B;
+        a.ldb = lr->ldb;
+        a.rank = lr->rank;
+        ws = (uint8_t*)ws + ub + pb;
+        ws_bytes -= ub + pb;
+    }
     if (Ns) {
         // 6:8: lift X into the workspace, then the plain product over the lifted width
         const size_t xl = lift_bytes(Mtok, K, es);
@@ -1590,6 +1790,20 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
     if (xdt == NM_I8) return run_spmm<int8_t>(a, ws, ws_bytes, s);
     if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ws, ws_bytes, s);
     return run_spmm<uint16_t>(a, ws, ws_bytes, s);
+}
+
+nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                      const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                      float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
+    return spmm_impl(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, nullptr, Y, ydt, ldy, ws,
+                     ws_bytes, s);
+}
+
+nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                              const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const LowRankIn& lr,
+                              void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
+    return spmm_impl(X, NM_BF16, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, nullptr, 1.0f, &lr, Y, ydt, ldy, ws,
+                     ws_bytes, s);
 }
 
 }  // namespace nm

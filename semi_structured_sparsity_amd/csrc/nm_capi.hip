@@ -403,4 +403,44 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
                        (hipStream_t)stream);
 }
 
+size_t nm_spmm_lowrank_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank) {
+    if (Mtok <= 0 || K <= 0 || R <= 0 || rank <= 0) return 0;
+    return spmm_lowrank_ws(Mtok, K, R, Ns, rank);
+}
+
+nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, const uint32_t* idx,
+                          int64_t R, int64_t ldv, int64_t ldi, int Ns, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int rank, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                          nm_stream_t stream) {
+    const char* fn = "nm_spmm_lowrank";
+    NM_REQ(Mtok >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported patterns are plain 2:4 (Ns=0) and 6:8 via slide (Ns=4)",
+           fn);
+    NM_REQ(ydt == NM_BF16 || ydt == NM_F32, NM_ERR_DTYPE, "%s: Y must be bf16 or f32", fn);
+    NM_REQ(rank >= 8 && rank <= 256 && rank % 8 == 0, NM_ERR_SHAPE, "%s: rank must be a multiple of 8 in [8, 256]", fn);
+    const int64_t kmult = Ns == 0 ? 16 : 32;
+    NM_REQ(K % kmult == 0, NM_ERR_SHAPE, "%s: K must be a multiple of %lld", fn, (long long)kmult);
+    if (Mtok == 0 || R == 0) return NM_OK;
+    NM_REQ(K > 0, NM_ERR_SHAPE, "%s: K == 0", fn);
+    NM_REQ(X && vals && idx && A && B && Y, NM_ERR_NULL, "%s: NULL argument", fn);
+    const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
+    const int64_t iw = (Kl + 31) / 32;
+    NM_REQ(ldx >= K && ldv >= Kl / 2 && ldi >= iw && lda >= K && ldb >= rank && ldy >= R, NM_ERR_SHAPE,
+           "%s: leading dimension too small", fn);
+    NM_REQ(aligned16(X) && aligned16(vals) && aligned16(A) && aligned16(B) && aligned16(idx) && ldx % 8 == 0 &&
+               ldv % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldi % 4 == 0,
+           NM_ERR_ALIGN, "%s: X, vals, idx, A and B need 16-byte aligned bases and row strides", fn);
+    const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
+    NM_REQ(!overlap(ry, span(X, Mtok, K, ldx, 2)) && !overlap(ry, span(vals, R, Kl / 2, ldv, 2)) &&
+               !overlap(ry, span(idx, R, iw, ldi, 4)) && !overlap(ry, span(A, rank, K, lda, 2)) &&
+               !overlap(ry, span(B, R, rank, ldb, 2)),
+           NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
+    const size_t need = spmm_lowrank_ws(Mtok, K, R, Ns, rank);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
+    const LowRankIn lr{(const uint16_t*)A, lda, (const uint16_t*)B, ldb, rank};
+    return launch_spmm_lowrank(X, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, lr, Y, ydt, ldy, ws, ws_bytes,
+                               (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -106,6 +106,18 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
 void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt, void* Xq,
                        int64_t ldq, float* x_scale, hipStream_t s);
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
+// stacked low-rank adapters of a sparse layer: A [rank, K] (lda), B [R, rank] (ldb), bf16
+struct LowRankIn {
+    const uint16_t* A;
+    int64_t lda;
+    const uint16_t* B;
+    int64_t ldb;
+    int rank;
+};
+size_t spmm_lowrank_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank);
+nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                              const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const LowRankIn& lr,
+                              void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
 nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
                       const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
                       float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);

@@ -106,6 +106,14 @@ def activations_bf16(cfg: int, tokens: int, K: int, tensor_id: int = 20) -> torc
     return to_bf16(normal_f32(rng(cfg, tensor_id + tokens), (tokens, K)))
 
 
+def adapter_bf16(cfg: int, rank: int, K: int, R: int):
+    """Stacked low-rank adapter pair of a layer: A [rank, K] ~ N(0,1)/sqrt(K) (down-
+    projection) and B [R, rank] ~ 0.02 N(0,1) (up-projection), bf16."""
+    A = to_bf16(normal_f32(rng(cfg, 40), (rank, K), 1.0 / np.sqrt(K)))
+    B = to_bf16(normal_f32(rng(cfg, 41), (R, rank), 0.02))
+    return A, B
+
+
 # ---------------------------------------------------------------- slide68 (config index 2)
 def slide68_weight(R: int = 14336, K: int = 4096) -> torch.Tensor:
     return to_bf16(normal_f32(rng(2, 0), (R, K), 0.02))

@@ -91,6 +91,14 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, r.nm_quant_lift(S, 1, 4, 64, 64, 4, 0, Y, 96, S, None)) == "NM_ERR_DTYPE"
     assert _st(nm, r.nm_quant_lift(S, F8, 4, 64, 64, 4, F8, Y, 96, S, None)) == "NM_ERR_DTYPE"
     assert _st(nm, r.nm_absmean(S, F8, 4, 8, 8, Y, S, 1 << 20, None)) == "NM_ERR_DTYPE"
+    # sparse + low-rank: rank a multiple of 8 in [8, 256], bf16/f32 output, aligned A and B, enough workspace
+    lr = r.nm_spmm_lowrank
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 12, Y, 1, 8, S, 1 << 30, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 512, 512, Y, 1, 8, S, 1 << 30, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 16, Y, 3, 8, S, 1 << 30, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, ctypes.c_void_p(0x1008), 64, S, 16, 16, Y, 1, 8, S, 1 << 30,
+                      None)) == "NM_ERR_ALIGN"
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 16, Y, 1, 8, S, 16, None)) == "NM_ERR_WORKSPACE"
 
 
 def test_empty_inputs_are_noops(nm):
