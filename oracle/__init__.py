@@ -78,6 +78,8 @@ def _declare(L):
         "or_masked_matmul_i8": (I64, [P, I64, I64, I64, P, I64, I64, P, I64, P, F, P, P]),
         "or_absmean": (D, [P, I, I64]),
         "or_lowrank_u": (None, [P, I, I64, I64, P, I, I64, P]),
+        "or_bitmap_encode": (None, [P, I, I64, I64, P, I64, P, I, I64, P, I64]),
+        "or_bitmap_decode": (None, [P, I, I64, P, I64, I64, I64, P, I]),
         "or_sparse_lowrank": (None, [P, I, I64, I64, P, I, I64, P, I64, P, I, P, I, I64, P]),
         "or_apply_mask_i8": (None, [P, I64, I64, P, I64, P]),
         "or_splitmix64_at": (U64, [U64, U64]),
@@ -337,6 +339,30 @@ def sparse_lowrank(X: np.ndarray, W: np.ndarray, mask: np.ndarray | None, A: np.
     lib().or_sparse_lowrank(_p(X), _dt(X), Mt, K, _p(W), _dt(W), R, _p(m), 0 if m is None else m.shape[1],
                             _p(A), _dt(A), _p(B), _dt(B), r, _p(Y))
     return Y
+
+
+def bitmap_encode(W: np.ndarray, mask: np.ndarray, ldv: int | None = None):
+    """SALR bitmap format: (vals [R, ldv] kept values per row in column order, offs int32
+    [R, ceil(K/64) + 1] kept values before each 64-column block, the last = row count).
+    The bitmap is the mask itself."""
+    W = _c(W)
+    R, K = W.shape
+    ldv = K if ldv is None else ldv
+    vals = np.zeros((R, ldv), W.dtype)
+    nb = (K + 63) // 64
+    offs = np.zeros((R, nb + 1), np.int32)
+    mask = _c(mask, np.uint8)
+    lib().or_bitmap_encode(_p(W), _dt(W), R, K, _p(mask), mask.shape[1], _p(vals), _dt(W), ldv, _p(offs), nb + 1)
+    return vals, offs
+
+
+def bitmap_decode(vals: np.ndarray, mask: np.ndarray, K: int) -> np.ndarray:
+    vals = _c(vals)
+    R, ldv = vals.shape
+    Wd = np.zeros((R, K), vals.dtype)
+    mask = _c(mask, np.uint8)
+    lib().or_bitmap_decode(_p(vals), _dt(vals), ldv, _p(mask), mask.shape[1], R, K, _p(Wd), _dt(vals))
+    return Wd
 
 
 def masked_matmul_i8(Xq, W, mask, sx, alpha):

@@ -33,8 +33,9 @@
  *         quantisation) and 2C (offline packer; per request: quantise + lift,
  *         then the sparse GEMM).
  *   [SA]  "SALR" summary, Methodology 1 (magnitude pruning of the frozen base),
- *         2 (truncated-SVD adapter of the pruning residual) and 3 (all low-rank
- *         adapters stacked along the rank into one product).
+ *         2 (truncated-SVD adapter of the pruning residual), 3 (all low-rank
+ *         adapters stacked along the rank into one product) and 4 (bitmap of the
+ *         kept positions, compact values, lookup table for the decode).
  */
 #include <math.h>
 #include <omp.h>
@@ -561,6 +562,49 @@ void or_sparse_lowrank(const void* X, int xdt, int64_t Mt, int64_t K, const void
             Y[m * R + o] += acc;
         }
     free(U);
+}
+
+/* ------------------------------------------------------------------ bitmap format
+ * [SA] section 4: the pruned weight is stored as a bitmap of its nonzero positions plus
+ * a compact array of the kept values (no per-element column indices, unlike CSR), and a
+ * lookup table locates the values of each sub-block for the decode.  Reading: the bitmap
+ * is the 1-bit-per-weight mask (LSB-first, [R, ceil(K/8)] bytes); the values of row r
+ * are stored in ascending column order at vals[r, 0 .. nnz_r) (row stride ldv); the
+ * table holds, for each row r and each block b of 64 columns, offs[r, b] = the number of
+ * kept values of row r before column 64 b, with offs[r, K/64] = nnz_r.  A kept value
+ * whose position in its row is ldv or beyond is not stored (the caller sizes ldv to the
+ * largest row count).  The product is the masked product of A12. */
+void or_bitmap_encode(const void* W, int wdt, int64_t R, int64_t K, const uint8_t* mask, int64_t ldm,
+                      void* vals, int vdt, int64_t ldv, int32_t* offs, int64_t ldo) {
+    const int64_t nb = (K + 63) / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t count = 0;
+        for (int64_t b = 0; b < nb; ++b) {
+            offs[r * ldo + b] = (int32_t)count;
+            for (int64_t k = 64 * b; k < K && k < 64 * b + 64; ++k) {
+                if (!mask_get(mask, ldm, r, k)) continue;
+                if (count < ldv) convert_store(vals, vdt, r * ldv + count, W, wdt, r * K + k);
+                ++count;
+            }
+        }
+        offs[r * ldo + nb] = (int32_t)count;
+    }
+}
+
+/* Dense [R, K] from the bitmap format: W[r,k] = the value of k's rank among the row's
+ * kept positions where the bit is set (0 if it was not stored), else 0. */
+void or_bitmap_decode(const void* vals, int vdt, int64_t ldv, const uint8_t* mask, int64_t ldm, int64_t R, int64_t K,
+                      void* Wd, int wdt) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t count = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            if (mask_get(mask, ldm, r, k) && count < ldv) convert_store(Wd, wdt, r * K + k, vals, vdt, r * ldv + count);
+            else store_zero(Wd, wdt, r * K + k);
+            if (mask_get(mask, ldm, r, k)) ++count;
+        }
+    }
 }
 
 /* Integer form for int8 activations and ternary int8 weights: the exact sum in

@@ -596,3 +596,65 @@ def test_sparse_lowrank_concatenation_equals_separate_adapters():
     Ycat = O.sparse_lowrank(X, W, mask, np.concatenate([A1, A2]), np.concatenate([B1, B2], axis=1))
     base = O.masked_matmul(X, W, mask)
     assert np.array_equal(Ycat, O.sparse_lowrank(X, W, mask, A1, B1) + O.sparse_lowrank(X, W, mask, A2, B2) - base)
+
+
+# ------------------------------------------------------------------ bitmap format (SALR 4)
+def _unstructured_mask(W, density, g):
+    """Magnitude mask keeping the given fraction of the whole tensor (ties broken at random)."""
+    a = np.abs(O.bf16_to_f32(W)) + g.random(W.shape).astype(np.float32) * 1e-6
+    thr = np.quantile(a, 1.0 - density)
+    return O.bool_to_mask(a > thr)
+
+
+def test_bitmap_encode_matches_numpy_selection():
+    g = _rng(61)
+    R, K = 9, 200                                     # K off the 64-column grid
+    W = O.f32_to_bf16(g.standard_normal((R, K)).astype(np.float32))
+    mask = _unstructured_mask(W, 0.5, g)
+    keep = O.mask_to_bool(mask, K)
+    vals, offs = O.bitmap_encode(W, mask)
+    for r in range(R):
+        sel = W[r][keep[r]]
+        assert np.array_equal(vals[r, :sel.size], sel) and not vals[r, sel.size:].any()
+        before = np.concatenate([[0], np.cumsum(keep[r])])
+        assert np.array_equal(offs[r], before[np.minimum(np.arange(0, K + 64, 64), K)][: offs.shape[1]])
+    assert np.array_equal(offs[:, -1], keep.sum(axis=1))
+
+
+def test_bitmap_round_trip_and_product():
+    g = _rng(62)
+    R, K, Mt = 12, 256, 5
+    W = O.f32_to_bf16(g.standard_normal((R, K)).astype(np.float32))
+    X = O.f32_to_bf16(g.standard_normal((Mt, K)).astype(np.float32))
+    for density in (0.5, 0.75, 0.3):
+        mask = _unstructured_mask(W, density, g)
+        vals, _ = O.bitmap_encode(W, mask)
+        Wd = O.bitmap_decode(vals, mask, K)
+        assert np.array_equal(Wd, np.where(O.mask_to_bool(mask, K), W, 0).astype(np.uint16))
+        assert np.array_equal(O.masked_matmul(X, Wd, None), O.masked_matmul(X, W, mask))
+
+
+def test_bitmap_of_a_24_mask_holds_the_24_packed_values():
+    """For a 2:4 mask the compact values are exactly the 2:4 packed values (SALR's bitmap
+    and the 2-bit index format carry the same information)."""
+    g = _rng(63)
+    R, K = 7, 128
+    W = O.f32_to_bf16(g.standard_normal((R, K)).astype(np.float32))
+    mask = O.topn_mask(O.score(W, None, 0.0, O.SCORE_MAGNITUDE), 2, 4)
+    vals, offs = O.bitmap_encode(W, mask, ldv=K // 2)
+    pvals, _ = O.pack(W, mask, 2, 4)
+    assert np.array_equal(vals, pvals)
+    assert (offs == np.arange(0, K // 64 + 1) * 32).all()
+
+
+def test_bitmap_rows_beyond_capacity_drop_their_last_values():
+    g = _rng(64)
+    R, K, cap = 4, 64, 20
+    W = O.f32_to_bf16(g.standard_normal((R, K)).astype(np.float32))
+    keep = np.zeros((R, K), bool)
+    keep[:, :30] = True                               # 30 kept per row, 20 stored
+    mask = O.bool_to_mask(keep)
+    vals, offs = O.bitmap_encode(W, mask, ldv=cap)
+    assert (offs[:, -1] == 30).all()
+    Wd = O.bitmap_decode(vals, mask, K)
+    assert np.array_equal(Wd[:, :cap], W[:, :cap]) and not Wd[:, cap:].any()
