@@ -329,6 +329,36 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         B.data_ptr(), rank, rank, Y.data_ptr(), nm.NM_BF16, R, wsl.data_ptr(), wsl.numel(), sh)), "mfma",
         2 * M * R * Kl // 2 + 2 * M * K * rank + 2 * M * R * rank)
     del A, B, X, Y, wsl
+    # bitmap format (SALR section 4): the same 6:8 weight without the sliding-window
+    # expansion, and an unstructured 50% magnitude mask of it; decode into LDS + dense MFMA.
+    # Unstructured mask: |W| above the tensor's median (torch setup, not timed).
+    keep = W.abs() > W.abs().flatten().float().median().to(W.dtype)
+    umask = (keep.view(R, K // 8, 8).to(torch.int32) << torch.arange(8, device=dev, dtype=torch.int32)).sum(-1)
+    umask = umask.to(u8).contiguous()
+    popc = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int64, device=dev)
+    for label, mk in (("6:8", mask), ("unstructured 50%", umask)):
+        rown = popc[mk.long()].sum(1)
+        nnz, ldvb = int(rown.sum()), (int(rown.max()) + 63) // 64 * 64   # values stored; row capacity
+        bvals = torch.zeros((R, ldvb), dtype=bf, device=dev)
+        boffs = torch.empty((R, K // 64 + 1), dtype=i32, device=dev)
+        row("slide68", "NEXT-4", f"bitmap encode 14336x4096 ({label})", lambda: chk(r.nm_bitmap_encode(
+            W.data_ptr(), nm.NM_BF16, R, K, K, mk.data_ptr(), K // 8, bvals.data_ptr(), ldvb, boffs.data_ptr(),
+            K // 64 + 1, sh)), "hbm", R * K * 2 + R * K // 8 + nnz * 2 + R * (K // 64 + 1) * 4)
+        for M in (1, 4096):
+            X = synth.activations_bf16(2, M, K).to(dev)
+            Y = torch.empty((M, R), dtype=bf, device=dev)
+            wsb = ws_for(r.nm_spmm_bitmap_workspace(M, K, R))
+            f = (lambda X=X, Y=Y, wsb=wsb, M=M: chk(r.nm_spmm_bitmap(
+                X.data_ptr(), M, K, K, bvals.data_ptr(), ldvb, mk.data_ptr(), K // 8, boffs.data_ptr(), K // 64 + 1,
+                R, Y.data_ptr(), nm.NM_BF16, R, wsb.data_ptr(), wsb.numel(), sh)))
+            if M == 1:
+                row("slide68", "NEXT-4", f"spmm bitmap 14336x4096 ({label}) M={M}", f, "hbm",
+                    nnz * 2 + R * K // 8 + R * (K // 64 + 1) * 4 + M * K * 2 + M * R * 2)
+            else:
+                row("slide68", "NEXT-4", f"spmm bitmap 14336x4096 ({label}) M={M}", f, "mfma", 2 * M * R * K)
+            del X, Y, wsb
+        del bvals, boffs, rown
+    del keep, umask, popc
     # FP8 e4m3 precision of the same layer (SlideSparse section 3): the weight's codes slide-packed
     # under the |W| mask, the activation quantised per token and lifted once, the product over K'
     Wq = W.to(torch.float8_e4m3fn)

@@ -274,6 +274,35 @@ nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, c
                           int64_t ldb, int rank, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
                           nm_stream_t stream);
 
+/* Bitmap format of a pruned weight ("SALR", section 4: a bitmap of the kept positions
+ * and a compact array of the kept values, with a lookup table that locates each
+ * sub-block's values for the decode; any sparsity pattern, e.g. unstructured 50% or
+ * (2N-2):2N without the sliding-window expansion).
+ *   mask [R, ldm] bytes: the bitmap (the 1-bit mask of nm_mask: bit k%8 of byte k/8).
+ *   vals [R, ldv] bf16: row r's kept values in column order at positions 0 .. nnz_r - 1
+ *     (a kept value at position >= ldv is not stored and reads as zero; size ldv to the
+ *     largest row count, offs[r, K/64]).
+ *   offs [R, ldo] int32: offs[r, b] = kept values of row r before column 64 b,
+ *     offs[r, K/64] = nnz_r (ldo >= K/64 + 1).
+ * nm_bitmap_encode writes vals and offs from W (bf16 [R, K], ldw) and the mask.
+ * Requires K % 64 == 0, W 16-byte aligned with ldw % 8 == 0, mask 8-byte aligned with
+ * ldm % 8 == 0.  Allocates nothing. */
+nm_status nm_bitmap_encode(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask,
+                           int64_t ldm, void* vals, int64_t ldv, int32_t* offs, int64_t ldo, nm_stream_t stream);
+
+/* Y = X W_hat^T with W_hat in the bitmap format above: each K step of a block's tile is
+ * first rebuilt dense in LDS from the bitmap, the table and the values, then multiplied
+ * with dense bf16 MFMA (f32 accumulation; the two stages of the pages' pipeline).
+ *   X: bf16 [Mtok, K] (ldx, 16-byte aligned rows); vals with 16-byte aligned rows
+ *   (ldv % 8 == 0); Y: [Mtok, R] bf16 or f32 (ldy), rounded once.  Requires K % 64 == 0.
+ * ws: nm_spmm_bitmap_workspace(Mtok, K, R) bytes: from 512 tokens a dense bf16 copy of
+ * the weight (the decode then runs once, not once per token tile); f32 partials of a K
+ * split when the tiles alone leave the chip short of blocks. */
+size_t nm_spmm_bitmap_workspace(int64_t Mtok, int64_t K, int64_t R);
+nm_status nm_spmm_bitmap(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
+                         const uint8_t* mask, int64_t ldm, const int32_t* offs, int64_t ldo, int64_t R, void* Y,
+                         nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,6 +70,9 @@ SIGNATURES = {
     "nm_spmm_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_spmm": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P, _SZ, _P]),
     "nm_spmm_lowrank_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
+    "nm_bitmap_encode": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
+    "nm_spmm_bitmap_workspace": (_SZ, [_I64, _I64, _I64]),
+    "nm_spmm_bitmap": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P, _I, _I64, _P, _SZ, _P]),
     "nm_spmm_lowrank": (_I, [_P, _I64, _I64, _I64, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _I, _P, _I, _I64,
                              _P, _SZ, _P]),
 }
@@ -254,6 +257,32 @@ def nm_quant_lift(X: torch.Tensor, Ns: int = 4, qdt: int = NM_I8) -> tuple[torch
     sx = torch.empty(Mtok, dtype=torch.float32, device=X.device)
     _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, qdt, _ptr(Xq), Kl, _ptr(sx), _stream(X)))
     return Xq, sx
+
+
+def nm_bitmap_encode(W: torch.Tensor, mask: torch.Tensor, ldv: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Bitmap format of bf16 W under mask: (vals [R, ldv] bf16, offs [R, K/64 + 1] int32)."""
+    R, K = W.shape
+    ldv = K if ldv is None else ldv
+    vals = torch.zeros((R, ldv), dtype=torch.bfloat16, device=W.device)
+    offs = torch.empty((R, K // 64 + 1), dtype=torch.int32, device=W.device)
+    _check(raw.nm_bitmap_encode(_ptr(W), dtype_code(W), R, K, _ld(W), _ptr(mask), _ld(mask), _ptr(vals), ldv,
+                                _ptr(offs), _ld(offs), _stream(W)))
+    return vals, offs
+
+
+def nm_spmm_bitmap(X: torch.Tensor, vals: torch.Tensor, mask: torch.Tensor, offs: torch.Tensor, R: int | None = None,
+                   ydt: int = NM_BF16, out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W_hat^T with W_hat in the bitmap format (decode into LDS, then dense MFMA)."""
+    Mtok, K = X.shape
+    R = vals.shape[0] if R is None else R
+    Y = out if out is not None else torch.empty((Mtok, R), dtype=_TORCH[ydt], device=X.device)
+    need = raw.nm_spmm_bitmap_workspace(Mtok, K, R)
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, X.device)
+    _check(raw.nm_spmm_bitmap(_ptr(X), Mtok, K, _ld(X), _ptr(vals), _ld(vals), _ptr(mask), _ld(mask), _ptr(offs),
+                              _ld(offs), R, _ptr(Y), ydt, _ld(Y), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(X)))
+    return Y
 
 
 def nm_spmm_lowrank(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -403,6 +403,54 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
                        (hipStream_t)stream);
 }
 
+nm_status nm_bitmap_encode(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask,
+                           int64_t ldm, void* vals, int64_t ldv, int32_t* offs, int64_t ldo, nm_stream_t stream) {
+    const char* fn = "nm_bitmap_encode";
+    NM_REQ(R >= 0 && K >= 0 && ldv >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(wdt == NM_BF16, NM_ERR_DTYPE, "%s: W must be bf16", fn);
+    NM_REQ(K % 64 == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 64", fn);
+    if (R == 0) return NM_OK;
+    NM_REQ(W && mask && offs && (vals || ldv == 0), NM_ERR_NULL, "%s: NULL argument", fn);
+    NM_REQ(ldw >= K && ldm >= K / 8 && ldo >= K / 64 + 1, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
+    NM_REQ(aligned16(W) && ldw % 8 == 0 && ((uintptr_t)mask & 7u) == 0 && ldm % 8 == 0 && ((uintptr_t)offs & 3u) == 0 &&
+               ((uintptr_t)vals & 1u) == 0,
+           NM_ERR_ALIGN, "%s: W needs 16-byte aligned rows, mask 8-byte aligned rows", fn);
+    const Range rv = span(vals, R, ldv, ldv, 2), ro = span(offs, R, K / 64 + 1, ldo, 4);
+    NM_REQ(!overlap(rv, ro) && !overlap(rv, span(W, R, K, ldw, 2)) && !overlap(ro, span(W, R, K, ldw, 2)) &&
+               !overlap(rv, span(mask, R, K / 8, ldm, 1)) && !overlap(ro, span(mask, R, K / 8, ldm, 1)),
+           NM_ERR_ALIAS, "%s: an output overlaps an input or the other output", fn);
+    launch_bitmap_encode(W, R, K, ldw, mask, ldm, vals, ldv, offs, ldo, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+size_t nm_spmm_bitmap_workspace(int64_t Mtok, int64_t K, int64_t R) { return bitmap_spmm_ws(Mtok, K, R); }
+
+nm_status nm_spmm_bitmap(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
+                         const uint8_t* mask, int64_t ldm, const int32_t* offs, int64_t ldo, int64_t R, void* Y,
+                         nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_spmm_bitmap";
+    NM_REQ(Mtok >= 0 && K >= 0 && R >= 0 && ldv >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(ydt == NM_BF16 || ydt == NM_F32, NM_ERR_DTYPE, "%s: Y must be bf16 or f32", fn);
+    NM_REQ(K % 64 == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 64", fn);
+    if (Mtok == 0 || R == 0) return NM_OK;
+    NM_REQ(K > 0, NM_ERR_SHAPE, "%s: K == 0", fn);
+    NM_REQ(X && mask && offs && Y && vals, NM_ERR_NULL, "%s: NULL argument", fn);
+    NM_REQ(ldx >= K && ldm >= K / 8 && ldo >= K / 64 + 1 && ldy >= R && ldv >= 8, NM_ERR_SHAPE,
+           "%s: leading dimension too small (ldv >= 8)", fn);
+    NM_REQ(aligned16(X) && ldx % 8 == 0 && ((uintptr_t)mask & 7u) == 0 && ldm % 8 == 0 && ((uintptr_t)offs & 3u) == 0 &&
+               aligned16(vals) && ldv % 8 == 0,
+           NM_ERR_ALIGN, "%s: X and vals need 16-byte aligned rows, mask 8-byte aligned rows", fn);
+    const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
+    NM_REQ(!overlap(ry, span(X, Mtok, K, ldx, 2)) && !overlap(ry, span(vals, R, ldv, ldv, 2)) &&
+               !overlap(ry, span(mask, R, K / 8, ldm, 1)) && !overlap(ry, span(offs, R, K / 64 + 1, ldo, 4)),
+           NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
+    const size_t need = bitmap_spmm_ws(Mtok, K, R);
+    NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (need) NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
+    return launch_bitmap_spmm(X, Mtok, K, ldx, vals, ldv, mask, ldm, offs, ldo, R, Y, ydt, ldy, ws, ws_bytes,
+                              (hipStream_t)stream);
+}
+
 size_t nm_spmm_lowrank_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank) {
     if (Mtok <= 0 || K <= 0 || R <= 0 || rank <= 0) return 0;
     return spmm_lowrank_ws(Mtok, K, R, Ns, rank);

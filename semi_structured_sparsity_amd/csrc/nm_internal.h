@@ -121,6 +121,13 @@ nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ld
 nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
                       const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
                       float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
+// bitmap format (mask + compact values + per-64-column-block value offsets)
+void launch_bitmap_encode(const void* W, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                          void* vals, int64_t ldv, int32_t* offs, int64_t ldo, hipStream_t s);
+size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R);
+nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
+                             const uint8_t* mask, int64_t ldm, const int32_t* offs, int64_t ldo, int64_t R, void* Y,
+                             nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
 // Hutchinson
 size_t hutch_ws(int64_t n, int64_t K, int64_t R, int probes);
 void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes, uint64_t seed,

@@ -99,6 +99,12 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, ctypes.c_void_p(0x1008), 64, S, 16, 16, Y, 1, 8, S, 1 << 30,
                       None)) == "NM_ERR_ALIGN"
     assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 16, Y, 1, 8, S, 16, None)) == "NM_ERR_WORKSPACE"
+    # bitmap format: K a multiple of 64, bf16 weights, 8-byte aligned mask rows
+    assert _st(nm, r.nm_bitmap_encode(S, 1, 4, 96, 96, S, 12, Y, 96, S, 3, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_bitmap_encode(S, 0, 4, 64, 64, S, 8, Y, 64, S, 2, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_bitmap_encode(S, 1, 4, 64, 64, ctypes.c_void_p(0x1004), 8, Y, 64, S, 2, None)) == "NM_ERR_ALIGN"
+    assert _st(nm, r.nm_spmm_bitmap(S, 4, 64, 64, S, 64, S, 8, S, 1, 8, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_spmm_bitmap(S, 4, 64, 64, S, 64, S, 8, S, 2, 8, Y, 3, 8, None, 0, None)) == "NM_ERR_DTYPE"
 
 
 def test_empty_inputs_are_noops(nm):
