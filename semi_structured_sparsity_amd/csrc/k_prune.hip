@@ -385,6 +385,9 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
                                                            uint32_t* __restrict__ idx, int64_t ldi, int64_t row_base) {
     constexpr int PR = kPP24Rows;
     const int q = threadIdx.x & 3;
+    // a quad's mask bytes are one aligned word when the mask rows are word-aligned and the
+    // quad's 32 columns lie inside the row
+    const bool mask_words = (((uintptr_t)mask & 3u) == 0) && (ldm % 4) == 0 && (K % 32) == 0;
     const int64_t k0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
     const bool col_ok = k0 < K;
@@ -477,13 +480,27 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
         }
         const bool ok = col_ok && r < R;
         if (ok) {
-            *(uint2*)(vals + r * ldv + (k0 >> 1)) = make_uint2(packed[0], packed[1]);
-            if (!FM && mask) mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u32x2_t{packed[0], packed[1]}, (u32x2_t*)(vals + r * ldv + (k0 >> 1)));
         }
+        // the quad's four index bytes and four mask bytes are gathered into one word each
+        // (lane q's byte at bits 8q) and stored by lane 0 of the quad
         uint32_t v = ok ? nib << (8 * q) : 0u;
         v |= (uint32_t)__shfl_xor((int)v, 1);
         v |= (uint32_t)__shfl_xor((int)v, 2);
-        if (q == 0 && ok) idx[r * ldi + (k0 >> 5)] = v;
+        if (q == 0 && ok) __builtin_nontemporal_store(v, idx + r * ldi + (k0 >> 5));
+        if constexpr (!FM) {
+            if (mask) {
+                uint32_t mw = ok ? mbyte << (8 * q) : 0u;
+                mw |= (uint32_t)__shfl_xor((int)mw, 1);
+                mw |= (uint32_t)__shfl_xor((int)mw, 2);
+                if (mask_words) {
+                    if (q == 0 && ok) __builtin_nontemporal_store(mw, (uint32_t*)(mask + r * ldm + (k0 >> 3)));
+                } else if (ok) {
+                    mask[r * ldm + (k0 >> 3)] = (uint8_t)mbyte;
+                }
+            }
+        }
     }
 }
 
