@@ -382,6 +382,19 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Index words are read from LDS one dword per lane.  Such a read is served a half-wave
+// (32 lanes) at a time over 32 dword banks (measured with an LDS probe and the bank-conflict
+// counter), and the 32 lanes of a half-wave read one word from each of 32 consecutive rows.
+// A row of W index words (W a power of two, at most 32) therefore keeps logical word w at
+// w ^ iswz<W>(r), r counted from a multiple of 32: the 32 reads then hit 32 distinct banks.
+// Rows padded to a whole number of 16-byte pieces and swizzled by piece instead reach only
+// 8 banks (a 4-way conflict, 4x the read time).
+template <int W>
+__device__ __forceinline__ int iswz(int r) {
+    static_assert(W >= 1 && W <= 32 && (W & (W - 1)) == 0, "W a power of two up to 32");
+    return (r / (32 / W)) & (W - 1);
+}
+
 // A global_load_lds instruction costs about the same per 128-byte line it touches
 // whatever part of the line it uses (measured on the hardware), and a row's index
 // words for one stage fill only a few bytes of a line.  With IG > 1 the index
@@ -389,7 +402,12 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // of a row), into two group buffers after the ring: group h (stages h*IG ..
 // h*IG+IG-1) is loaded in IG batches of rows, one batch with each of the stages
 // (h-1)*IG+1 .. h*IG, so every stage issues the same number of loads.  Within a
-// row of a group buffer, piece c is stored at c ^ ((r>>2) & (IG-1)).
+// row of a group buffer, piece c is stored at c ^ ((r>>2) & (IG-1)), and a lane reads
+// its row's piece of a stage (the index words of all its depths) with one 16-byte read
+// at the stage's first depth: under that swizzle the 16 lanes served together hit
+// distinct banks.  Without groups (IG == 1) the index words travel one dword per lane
+// and each row of AI words is stored swizzled word by word (iswz), so that the
+// per-depth dword reads are conflict-free.
 template <typename T, int SR, int ST, int KB, int NS, int WRN, int WTN, int IG = 1>
 struct Ring {
     static constexpr int NW = WRN * WTN;               // waves per block (WRN along rows, WTN along tokens)
@@ -410,19 +428,21 @@ struct Ring {
     static constexpr int G_OFF = NS * STAGE;                          // IG > 1: the two group buffers
     static constexpr int LDS = NS * STAGE + (IG > 1 ? 2 * IGRP : 0);
     static constexpr int NA = BR * AROW / 1024 / NW;   // A wave-instructions per wave
-    // index rows loaded in 16-byte pieces when whole pieces split evenly over the waves, else dwords
-    static constexpr bool I16 = IG > 1 || (AI % 4 == 0 && (BR * AI * 4) % (1024 * NW) == 0);
-    static constexpr int NI = IG > 1 ? IGRP / 1024 / NW / IG : BR * AI * 4 / (I16 ? 1024 : 256) / NW;
+    // index loads per wave: 16-byte pieces per batch (IG > 1), else dwords per stage
+    static constexpr int NI = IG > 1 ? IGRP / 1024 / NW / IG : BR * AI * 4 / 256 / NW;
     static constexpr int NB = BT * KB / 1024 / NW;     // X wave-instructions per wave
     static constexpr int PER = NA + NI + NB;           // loads per wave per stage
     static_assert(LDS <= 160 * 1024, "LDS ring too large");
     static_assert(NA >= 1 && NI >= 1 && NB >= 1, "tile too small for its waves");
     static_assert(BR * AROW % (1024 * NW) == 0 && BT * KB % (1024 * NW) == 0, "loads must split evenly over the waves");
-    static_assert(IG > 1 || BR * AI * 4 % ((I16 ? 1024 : 256) * NW) == 0, "index loads must split evenly over the waves");
+    static_assert(IG > 1 || BR * AI * 4 % (256 * NW) == 0, "index loads must split evenly over the waves");
     // grouped index loads: the ring waits for every load at each stage end (NS == 2), one
-    // 16-byte piece per row per stage, and a power-of-two group
-    static_assert(IG == 1 || (NS == 2 && AI * 4 == 16 && (IG & (IG - 1)) == 0 && IGRP % (1024 * NW * IG) == 0),
-                  "grouped index loads need NS == 2, 16 index bytes per row per stage, IG a power of two");
+    // 16-byte piece per row per stage holding one word per depth (bf16), and a power-of-two
+    // group
+    static_assert(IG == 1 || (NS == 2 && AI * 4 == 16 && sizeof(T) == 2 && (IG & (IG - 1)) == 0 &&
+                              IGRP % (1024 * NW * IG) == 0),
+                  "grouped index loads need NS == 2, bf16 with 16 index bytes per row per stage, IG a power of two");
+    static_assert(AI <= 32 && (AI & (AI - 1)) == 0, "index words per row a power of two");
     static_assert(ND % 2 == 0, "depth ping-pong needs an even depth count");
     static_assert(ACH == 4 || ACH == 8, "weight-row chunk count without a swizzle");
     // Swizzles of 16-byte chunks, so that the 16 lanes served together by a 16-byte LDS read
@@ -633,11 +653,10 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     }
 #pragma unroll
     for (int i = 0; i < RG::NI; ++i) {
-        const int q = (wave * RG::NI + i) * 64 + lane;  // piece index (16-byte or dword)
-        constexpr int PPR = RG::I16 ? RG::AI / 4 : RG::AI;   // pieces per row
-        const int row = q / PPR, part = q % PPR;
+        const int q = (wave * RG::NI + i) * 64 + lane;  // dword slot of the stage's [BR, AI] index block
+        const int row = q / RG::AI, lw = (q % RG::AI) ^ iswz<RG::AI>(row);
         const int64_t gr = row < rmax ? row : rmax;
-        oI[i] = (uint32_t)(gr * a.ldi * 4 + part * (RG::I16 ? 16 : 4));
+        oI[i] = (uint32_t)(gr * a.ldi * 4 + lw * 4);
     }
 #pragma unroll
     for (int i = 0; i < RG::NB; ++i) {
@@ -666,18 +685,15 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
             if (s >= 1) issue_group((s - 1) / IG + 1, (s - 1) % IG);
         } else {
 #pragma unroll
-            for (int i = 0; i < RG::NI; ++i) {
-                if constexpr (RG::I16)
-                    dma16s(st + RG::I_OFF + (wave * RG::NI + i) * 1024, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
-                else
-                    dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
-            }
+            for (int i = 0; i < RG::NI; ++i)
+                dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
         }
 #pragma unroll
         for (int i = 0; i < RG::NB; ++i)
             dma16s(st + RG::B_OFF + (wave * RG::NB + i) * 1024, baseB, oB[i] + (uint32_t)(s * KB));
     };
     const int h = lane >> 5, l32 = lane & 31;
+    i32x4_t ipc[SR];   // IG > 1: the current stage's index piece of each row sub-tile (one word per depth)
     auto read_depth = [&](int S, int d, FR& f) __attribute__((always_inline)) {
         const int slot = S % NS;
         const uint8_t* sA = smem + slot * RG::STAGE + RG::A_OFF;
@@ -691,12 +707,10 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
             // bf16: the lane's 16 index bits are selected (shifted by 16h) at the SMFMAC, so
             // that no VALU op waits on this read ahead of unrelated SMFMACs
             if constexpr (IG > 1) {
-                const int pc = (S % IG) ^ ((row >> 2) & (IG - 1));
-                if constexpr (sizeof(T) == 2) f.iw[i] = sG[row * (4 * IG) + pc * 4 + d];
-                else f.iw[i] = sG[row * (4 * IG) + pc * 4 + 2 * d + h];
+                if (d == 0) ipc[i] = *(const i32x4_t*)(sG + row * (4 * IG) + ((S % IG) ^ ((row >> 2) & (IG - 1))) * 4);
+                f.iw[i] = (uint32_t)ipc[i][d];
             } else {
-                if constexpr (sizeof(T) == 2) f.iw[i] = sI[row * RG::AI + d];
-                else f.iw[i] = sI[row * RG::AI + 2 * d + h];
+                f.iw[i] = sI[row * RG::AI + ((sizeof(T) == 2 ? d : 2 * d + h) ^ iswz<RG::AI>(row))];
             }
         }
 #pragma unroll
@@ -830,7 +844,8 @@ struct Ring2 {
     // 16-byte chunk swizzles (conflict-free 16-lane LDS reads):
     //   value group row r (8 chunks): logical c at c ^ ((r >> 1) & 7)
     //   X token t (8 chunks): logical c at c ^ ((t >> 1) & 7)
-    //   index group row r (4 pieces): logical p at p ^ ((r >> 2) & 3)
+    //   index group row r: IP == 4, 16 words, logical word w at w ^ iswz<16>(r) (conflict-free
+    //   dword reads); IP == 16, 4 pieces, logical piece p at p ^ ((r >> 2) & 3)
     __device__ static int swa(int r) { return (r >> 1) & 7; }
     __device__ static int swb(int t) { return (t >> 1) & 7; }
     __device__ static int swi(int r) { return (r >> 2) & 3; }
@@ -875,9 +890,13 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
         // and the unit's logical byte offset in the row's 64 bytes
         const int q = (wave * RG::NIG + i) * 64 + lane;
         const int row = q / (64 / IP), u = q % (64 / IP);
-        const int pb = u * IP;                                  // physical byte in the row
         oI[i] = (uint32_t)row;
-        pI[i] = (((pb >> 4) ^ RG::swi(row)) << 4) | (pb & 15);  // logical byte
+        if constexpr (IP == 4) {
+            pI[i] = (u ^ iswz<16>(row)) * 4;                    // logical byte of physical word u
+        } else {
+            const int pb = u * IP;                              // physical byte in the row
+            pI[i] = (((pb >> 4) ^ RG::swi(row)) << 4) | (pb & 15);
+        }
     }
 #pragma unroll
     for (int i = 0; i < RG::NBX; ++i) {
@@ -922,9 +941,10 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
         for (int i = 0; i < SR; ++i) {
             const int row = (wr * SR + i) * 32 + l32;
             f.a[i] = *(const i32x4_t*)(sA + row * 128 + ((4 * ss + 2 * d + h) ^ RG::swa(row)) * 16);
-            // index word w of the row's group: piece w / 4 (swizzled), word w % 4
+            // index word w of the row's group
             const int w = si * RG::AI + (sizeof(T) == 2 ? d : 2 * d + h);
-            f.iw[i] = sI[row * 16 + ((w >> 2) ^ RG::swi(row)) * 4 + (w & 3)];
+            if constexpr (IP == 4) f.iw[i] = sI[row * 16 + (w ^ iswz<16>(row))];
+            else f.iw[i] = sI[row * 16 + ((w >> 2) ^ RG::swi(row)) * 4 + (w & 3)];
         }
 #pragma unroll
         for (int jj = 0; jj < ST; ++jj) {
@@ -1056,10 +1076,10 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int q = (wave * NI + i) * 64 + lane;   // index word of the stage's [BR, AI] block
-        const int row = q / AI, part = q % AI;
+        const int q = (wave * NI + i) * 64 + lane;   // dword slot of the stage's [BR, AI] index block
+        const int row = q / AI, lw = (q % AI) ^ iswz<AI>(row);
         const int64_t gr = row < rmax ? row : rmax;
-        oI[i] = (uint32_t)(gr * a.ldi * 4 + part * 4);
+        oI[i] = (uint32_t)(gr * a.ldi * 4 + lw * 4);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -1092,8 +1112,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int i = 0; i < SR; ++i) {
             const int row = i * 32 + l32;
             f.a[i] = *(const i32x4_t*)(sA + row * AROW + ((2 * d + h) ^ swa(row)) * 16);
-            if constexpr (es == 2) f.iw[i] = sI[row * AI + d];
-            else f.iw[i] = sI[row * AI + 2 * d + h];
+            f.iw[i] = sI[row * AI + ((es == 2 ? d : 2 * d + h) ^ iswz<AI>(row))];
         }
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
@@ -1463,7 +1482,7 @@ struct SpmmPlan {
 //   big   : split ring kernel (T, SR, ST, WRN, WTN, IP), 256 x 256 tile, 8 waves (two per
 //           SIMD); bf16 index batches load 4 bytes per lane (16 do not split over 8 waves)
 #define NM_RING_NARROW T, 4, 2, 256, 2, 2, 2
-#define NM_RING_BIG T, 4, 2, 2, 4, (sizeof(T) == 2 ? 4 : 16)
+#define NM_RING_BIG T, 4, 2, 2, 4, 4
 
 // Compute units of the current device (cached per device).
 static int64_t device_cus() {
