@@ -226,13 +226,15 @@ GATE_OPS_PER_STEP = 4 + 4 + 1 + 1 + 2 + 2
 
 def measure_rows(nm, torch, synth, dev, reps: int = 5):
     """Every hot-path row at the full size of each workload: kernel time from HIP events
-    around the raw C call (median of `reps`, each after a 1 GiB write that evicts L2 and
-    the Infinity Cache), with its algorithmic bytes or flops and the roofline fraction."""
+    around the raw C call (median of `reps`, each after a 1 GiB read that evicts L2 and
+    the Infinity Cache: a read leaves no dirty lines whose write-back would overlap the
+    timed call, as a 1 GiB write does), with its algorithmic bytes or flops and the
+    roofline fraction."""
     r = nm.raw
     bf, f32, i8, i32, u8 = torch.bfloat16, torch.float32, torch.int8, torch.int32, torch.uint8
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    flush = torch.empty(1 << 30, dtype=u8, device=dev)
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device=dev)   # 1 GiB
     out = []
 
     def chk(st):
@@ -242,7 +244,7 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     def timed(f):
         ts = []
         for i in range(reps):
-            flush.fill_(i & 0xFF)
+            flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             f()
