@@ -295,9 +295,10 @@ nm_status nm_bitmap_encode(const void* W, nm_dtype wdt, int64_t R, int64_t K, in
  * with dense bf16 MFMA (f32 accumulation; the two stages of the pages' pipeline).
  *   X: bf16 [Mtok, K] (ldx, 16-byte aligned rows); vals with 16-byte aligned rows
  *   (ldv % 8 == 0); Y: [Mtok, R] bf16 or f32 (ldy), rounded once.  Requires K % 64 == 0.
- * ws: nm_spmm_bitmap_workspace(Mtok, K, R) bytes: from 512 tokens a dense bf16 copy of
- * the weight (the decode then runs once, not once per token tile); f32 partials of a K
- * split when the tiles alone leave the chip short of blocks. */
+ * ws: nm_spmm_bitmap_workspace(Mtok, K, R) bytes: 0 up to 4 tokens (the rows are
+ * streamed, one wave per weight row); from 512 tokens a dense bf16 copy of the weight
+ * (the decode then runs once, not once per token tile); f32 partials of a K split when
+ * the tiles alone leave the chip short of blocks. */
 size_t nm_spmm_bitmap_workspace(int64_t Mtok, int64_t K, int64_t R);
 nm_status nm_spmm_bitmap(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
                          const uint8_t* mask, int64_t ldm, const int32_t* offs, int64_t ldo, int64_t R, void* Y,

@@ -402,6 +402,91 @@ __global__ __launch_bounds__(256, 2) void bitmap_dense_kernel(BitmapArgs a) {
     bm_store(a, acc, r0 + wr * 64, t0 + wt * 64, lane);
 }
 
+// ------------------------------------------------------------------ few tokens: row streaming
+// With a handful of tokens the product is a stream over the weight: one wave per weight
+// row, lane l expanding the row's 8-column groups l, l + 64, l + 128, ... (the stage-1
+// window decode above: consecutive lanes take consecutive stretches of the value row, so
+// a wave's loads cover it contiguously) and multiplying each with the tokens' 8 columns
+// (f32 multiply-adds in column order, groups in lane order).  U groups per lane are in
+// flight at once: their bitmap words, table entries and token columns are loaded
+// together, then their value windows, so a row costs two memory round trips per U groups
+// rather than two per group.  The lanes' sums are added by a butterfly across the wave,
+// whose result is the same on every lane and every run.
+constexpr int kBmRowTokens = 4;
+
+template <int MT, int U>
+__global__ __launch_bounds__(256) void bitmap_rows_kernel(BitmapArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t groups = a.K / 8, vchunks = a.ldv / 8;
+    const int mt = (int)a.Mtok;   // <= MT
+    for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * 4) {
+        const uint16_t* vrow = a.vals + r * a.ldv;
+        const uint8_t* mrow = a.mask + r * a.ldm;
+        const int32_t* orow = a.offs + r * a.ldo;
+        float acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+        for (int64_t g0 = lane; g0 < groups; g0 += 64 * U) {
+            // groups past the row are clamped to its last group and contribute nothing
+            int64_t gc[U];
+            bool ok[U];
+            uint64_t bits[U];
+            int32_t off[U];
+            uint4 xv[U][MT];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t g = g0 + 64 * u;
+                ok[u] = g < groups;
+                gc[u] = ok[u] ? g : groups - 1;
+                bits[u] = *(const uint64_t*)(mrow + (gc[u] >> 3) * 8);
+                off[u] = orow[gc[u] >> 3];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    xv[u][m] = *(const uint4*)(a.X + (m < mt ? m : 0) * a.ldx + gc[u] * 8);
+            }
+            BmWindow wnd[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) wnd[u] = bm_fetch(ok[u] ? bits[u] : 0ull, off[u], (int)(gc[u] & 7), vrow, vchunks);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                const uint4 wv = bm_expand(wnd[u]);
+                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+                float w[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[2 * e] = __uint_as_float(ww[e] << 16);
+                    w[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint32_t xx[4] = {xv[u][m].x, xv[u][m].y, xv[u][m].z, xv[u][m].w};
+                    float t = acc[m];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t = __fmaf_rn(w[2 * e], __uint_as_float(xx[e] << 16), t);
+                        t = __fmaf_rn(w[2 * e + 1], __uint_as_float(xx[e] & 0xffff0000u), t);
+                    }
+                    acc[m] = t;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < mt) {
+                    if (a.ydt == NM_F32) ((float*)a.Y)[m * a.ldy + r] = acc[m];
+                    else ((uint16_t*)a.Y)[m * a.ldy + r] = (uint16_t)f32_to_bf16_bits(acc[m]);
+                }
+            }
+        }
+    }
+}
+
 // Y[m, o] = sum of the splits' partials in split order, converted.
 __global__ __launch_bounds__(256) void bitmap_reduce_kernel(const float* __restrict__ part, int KS, int64_t M,
                                                             int64_t R, void* Y, int ydt, int64_t ldy) {
@@ -433,7 +518,7 @@ static size_t bm_dense_bytes(int64_t Mtok, int64_t K, int64_t R) {
 }
 
 size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R) {
-    if (Mtok <= 0 || K <= 0 || R <= 0) return 0;
+    if (Mtok <= 0 || K <= 0 || R <= 0 || Mtok <= kBmRowTokens) return 0;
     const int ks = bitmap_splits(Mtok, K, R);
     return bm_dense_bytes(Mtok, K, R) + (ks > 1 ? (size_t)ks * (size_t)Mtok * (size_t)R * 4 : 0);
 }
@@ -457,6 +542,13 @@ nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx
     a.R = R;
     a.ydt = (int)ydt;
     a.nsteps = (int)(K / kBmKC);
+    if (Mtok <= kBmRowTokens) {
+        // 4 waves (rows) per block, up to 8 blocks per CU
+        const dim3 g((unsigned)grid_cap(ceil_div(R, 4), 2048));
+        if (Mtok == 1) hipLaunchKernelGGL((bitmap_rows_kernel<1, 4>), g, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((bitmap_rows_kernel<kBmRowTokens, 4>), g, dim3(256), 0, s, a);
+        return check_launch("nm_spmm_bitmap");
+    }
     const size_t db = bm_dense_bytes(Mtok, K, R);
     if (db) {
         if (!ws || ws_bytes < db) return set_error(NM_ERR_WORKSPACE, "nm_spmm_bitmap: workspace of %zu bytes needed", db);

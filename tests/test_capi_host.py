@@ -105,6 +105,10 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, r.nm_bitmap_encode(S, 1, 4, 64, 64, ctypes.c_void_p(0x1004), 8, Y, 64, S, 2, None)) == "NM_ERR_ALIGN"
     assert _st(nm, r.nm_spmm_bitmap(S, 4, 64, 64, S, 64, S, 8, S, 1, 8, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
     assert _st(nm, r.nm_spmm_bitmap(S, 4, 64, 64, S, 64, S, 8, S, 2, 8, Y, 3, 8, None, 0, None)) == "NM_ERR_DTYPE"
+    # up to 4 tokens the bitmap product streams rows and needs no workspace; more tokens on
+    # few rows split K over blocks (f32 partials)
+    assert all(r.nm_spmm_bitmap_workspace(m, 4096, 14336) == 0 for m in (1, 2, 3, 4))
+    assert r.nm_spmm_bitmap_workspace(8, 4096, 512) > 0
 
 
 def test_empty_inputs_are_noops(nm):

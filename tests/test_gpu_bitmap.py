@@ -3,8 +3,8 @@
 (decode into LDS, then dense MFMA) against the oracle's masked product -- bit for bit on
 integer-valued inputs (every partial sum exact in f32), within 2e-2 ||x|| ||w_hat|| and
 the float-accumulation bound on random ones -- for unstructured masks of several
-densities, 2:4 and 6:8 masks, ragged edges, a K split over blocks and rows whose kept
-count exceeds the value capacity."""
+densities, 2:4 and 6:8 masks, ragged edges, a K split over blocks, up to 4 tokens (the
+row-streaming kernel) and rows whose kept count exceeds the value capacity."""
 import numpy as np
 import pytest
 import torch
@@ -75,7 +75,17 @@ def test_spmm_bitmap_integer_exact(nm, Mt, R, K, kind):
     assert torch.equal(Y16, torch.from_numpy(Y).to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("Mt,R,K,kind", [(8, 300, 2048, "0.5"), (400, 520, 1024, "6:8")])
+# up to 4 tokens: the row-streaming kernel (one wave per weight row); K off a multiple of
+# 512 columns leaves some lanes a group fewer, one row and K = 64 are the smallest cases
+@pytest.mark.parametrize("Mt,R,K,kind", [(1, 300, 4160, "6:8"), (2, 257, 1024, "0.5"), (3, 64, 64, "0.3"),
+                                         (4, 1000, 2048, "2:4"), (1, 1, 64, "0.5"), (4, 130, 8192, "0.9"),
+                                         (1, 513, 1536, "0.05")])
+def test_spmm_bitmap_few_tokens_integer_exact(nm, Mt, R, K, kind):
+    test_spmm_bitmap_integer_exact(nm, Mt, R, K, kind)
+
+
+@pytest.mark.parametrize("Mt,R,K,kind", [(8, 300, 2048, "0.5"), (400, 520, 1024, "6:8"), (1, 700, 4096, "6:8"),
+                                         (4, 300, 2048, "0.5")])
 def test_spmm_bitmap_random_tolerance(nm, Mt, R, K, kind):
     g = np.random.default_rng(Mt + R + K + 1)
     X = O.f32_to_bf16(g.standard_normal((Mt, K)).astype(np.float32))
@@ -92,9 +102,10 @@ def test_spmm_bitmap_random_tolerance(nm, Mt, R, K, kind):
     assert (np.abs(Y - ref) <= 1.01 * K * 2.0 ** -24 * absdot + 1e-30).all()
 
 
-def test_spmm_bitmap_values_past_capacity_read_as_zero(nm):
-    g = np.random.default_rng(8)
-    Mt, R, K, cap = 64, 96, 512, 200
+@pytest.mark.parametrize("Mt", [64, 2])
+def test_spmm_bitmap_values_past_capacity_read_as_zero(nm, Mt):
+    g = np.random.default_rng(8 + Mt)
+    R, K, cap = 96, 512, 200
     X = O.f32_to_bf16(g.integers(-3, 4, (Mt, K)).astype(np.float32))
     W = O.f32_to_bf16(g.integers(-3, 4, (R, K)).astype(np.float32))
     mask = _mask(g, W, "0.6")
