@@ -110,7 +110,19 @@ def test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns):
     assert np.array_equal(Y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("Mt,R,K", [(16, 300, 512), (200, 260, 1024), (5, 128, 4096)])
+# 1 to 4 tokens: K of 16 or 48 columns (one or three 16-column chunks, an odd index
+# word), K off the rings' stage grid, a K split over blocks, one row
+FEW = [(1, 1, 16), (2, 300, 48), (3, 257, 4160), (4, 130, 32), (1, 513, 2560), (4, 64, 4096), (1, 1000, 96)]
+
+
+@pytest.mark.parametrize("Mt,R,K", FEW)
+@pytest.mark.parametrize("Ns", [0, 4])
+def test_spmm_bf16_few_tokens_integer_exact(nm, Mt, R, K, Ns):
+    test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns)
+
+
+@pytest.mark.parametrize("Mt,R,K", [(16, 300, 512), (200, 260, 1024), (5, 128, 4096), (1, 300, 4096), (4, 260, 1024),
+                                    (3, 70, 2560)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_spmm_bf16_random_tolerance(nm, Mt, R, K, Ns):
     g = np.random.default_rng(Mt + R + K + 11 * Ns)
