@@ -5,6 +5,9 @@
 // bit per position plus the values.  The product runs in two stages per K step of a
 // block's tile: stage 1 rebuilds the dense weight tile in LDS from the bitmap, the table
 // and the values; stage 2 multiplies it with dense bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+// Up to 4 tokens the rows are streamed instead (one wave per row); from 512 tokens stage 1
+// runs once over the whole weight into the workspace, and stage 2 is the dense split
+// ring (k_spmm.hip) when the product has a 256 x 256 tile for every CU.
 //
 // Layout (the bitmap is the 1-bit mask of the other entry points):
 //   mask [R, ldm] bytes, bit k%8 of byte k/8 = position k kept;
@@ -557,6 +560,9 @@ nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx
         a.dense = (const uint16_t*)ws;
         ws = (uint8_t*)ws + db;
         ws_bytes -= db;
+        // enough 256 x 256 tiles for every CU: the dense split ring on the decoded weight
+        if (launch_dense_ring(a.dense, K, a.X, ldx, Mtok, K, R, Y, ydt, ldy, s) == NM_OK)
+            return check_launch("nm_spmm_bitmap");
     }
     const int ks = bitmap_splits(Mtok, K, R);
     a.steps_per_split = (int)ceil_div(a.nsteps, ks);

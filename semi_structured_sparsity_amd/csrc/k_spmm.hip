@@ -1021,6 +1021,116 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
                           (uint32_t*)smem + wave * kStageWords<SR>, lane);
 }
 
+// ------------------------------------------------------------------ dense split ring (bf16)
+// Y = X W^T for a dense bf16 weight W [R, K] (ldv) with the split ring's tile, waves,
+// swizzles, DMA and epilogue, and dense MFMA (v_mfma_f32_32x32x16_bf16, whose operand and
+// accumulator layouts are the sparse instruction's with 16-byte B fragments).  A stage is
+// 64 columns: 128 bytes of W per row and of X per token, each in a 2-stage ring (128 KB),
+// four MFMA depths.  One barrier per stage, before its last depth: stage s+1 has landed
+// and every wave has read stage s, whose buffers then take stage s+2.  Used for the
+// many-token product of weights decoded from the bitmap format.
+template <int SR, int ST, int WRN, int WTN>
+__global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs a) {
+    constexpr int NW = WRN * WTN, BR = WRN * SR * 32, BT = WTN * ST * 32;
+    constexpr int WSTAGE = BR * 128, XSTAGE = BT * 128;
+    constexpr int W_OFF = 0, X_OFF = 2 * WSTAGE, RING = X_OFF + 2 * XSTAGE;
+    constexpr int NWL = WSTAGE / 1024 / NW, NXL = XSTAGE / 1024 / NW;   // loads per wave per stage
+    static_assert(WSTAGE % (1024 * NW) == 0 && XSTAGE % (1024 * NW) == 0 && NWL >= 1 && NXL >= 1, "loads per wave");
+    constexpr int SMEM = RING > NW * kStageWords<SR> * 4 ? RING : NW * kStageWords<SR> * 4;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave % WRN, wt = wave / WRN;
+    int tr, tt;
+    tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
+    const int64_t r0 = (int64_t)tr * BR, t0 = (int64_t)tt * BT;
+    const int nsteps = a.nsteps;   // K / 64 >= 1
+    const uint32_t sbase = lds_addr(smem);
+    auto sw = [](int r) { return (r >> 1) & 7; };   // row / token r of 8 chunks: logical c at c ^ sw(r)
+    const void* baseW = uniform_ptr(a.vals + r0 * a.ldv * 2);
+    const void* baseX = uniform_ptr(a.X + t0 * a.ldx * 2);
+    const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
+    uint32_t oW[NWL], oX[NXL];
+#pragma unroll
+    for (int i = 0; i < NWL; ++i) {
+        const int row = (wave * NWL + i) * 8 + (lane >> 3);
+        const int64_t gr = row < rmax ? row : rmax;
+        oW[i] = (uint32_t)(gr * a.ldv * 2 + ((lane & 7) ^ sw(row)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) {
+        const int row = (wave * NXL + i) * 8 + (lane >> 3);
+        const int64_t gt = row < tmax ? row : tmax;
+        oX[i] = (uint32_t)(gt * a.ldx * 2 + ((lane & 7) ^ sw(row)) * 16);
+    }
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const uint32_t sw0 = sbase + (uint32_t)(W_OFF + (s & 1) * WSTAGE), sx0 = sbase + (uint32_t)(X_OFF + (s & 1) * XSTAGE);
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) dma16s(sw0 + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(s * 128));
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + (uint32_t)(s * 128));
+    };
+    struct Frag {
+        i32x4_t a[SR], b[ST];
+    };
+    const int h = lane >> 5, l32 = lane & 31;
+    auto read_depth = [&](int s, int d, Frag& f) __attribute__((always_inline)) {
+        const uint8_t* sW = smem + W_OFF + (s & 1) * WSTAGE;
+        const uint8_t* sX = smem + X_OFF + (s & 1) * XSTAGE;
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int row = (wr * SR + i) * 32 + l32;
+            f.a[i] = *(const i32x4_t*)(sW + row * 128 + ((2 * d + h) ^ sw(row)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int tok = (wt * ST + j) * 32 + l32;
+            f.b[j] = *(const i32x4_t*)(sX + tok * 128 + ((2 * d + h) ^ sw(tok)) * 16);
+        }
+    };
+    f32x16_t acc[SR][ST];
+#pragma unroll
+    for (int i = 0; i < SR; ++i)
+#pragma unroll
+        for (int j = 0; j < ST; ++j) acc[i][j] = f32x16_t{};
+    auto mfmas = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                                     __builtin_bit_cast(bf16x8_t, f.b[j]), acc[i][j], 0, 0, 0);
+    };
+    constexpr int PER = NWL + NXL;
+    Frag fa, fb;
+    issue(0);
+    if (nsteps > 1) {
+        issue(1);
+        wait_vm_barrier<PER>();
+    } else {
+        wait_vm_barrier<0>();
+    }
+    read_depth(0, 0, fa);
+    for (int s = 0; s < nsteps; ++s) {
+        read_depth(s, 1, fb);
+        mfmas(fa);
+        read_depth(s, 2, fa);
+        mfmas(fb);
+        read_depth(s, 3, fb);
+        mfmas(fa);
+        // stage s+1 landed (the last loads issued) and stage s read by every wave
+        wait_vm_barrier<0>();
+        if (s + 2 < nsteps) issue(s + 2);
+        if (s + 1 < nsteps) read_depth(s + 1, 0, fa);
+        mfmas(fb);
+    }
+    wait_vm_all();
+    __syncthreads();
+    store_tile<uint16_t, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + BR <= a.R && t0 + BT <= a.Mtok,
+                                 (uint32_t*)smem + wave * kStageWords<SR>, lane);
+}
+
 // ------------------------------------------------------------------ K-split ring kernel (up to 256 tokens)
 // With up to 256 tokens the 256-row tiles of the ring kernel are too few to fill the
 // chip, and a weight-streaming kernel that loads SMFMAC fragments straight from
@@ -1826,6 +1936,36 @@ nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ld
                               void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
     return spmm_impl(X, NM_BF16, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, nullptr, 1.0f, &lr, Y, ydt, ldy, ws,
                      ws_bytes, s);
+}
+
+// Y [Mtok, R] (ydt bf16 or f32, ldy) = X [Mtok, K] (ldx) W^T, W [R, K] (ldw) dense bf16.
+// NM_ERR_SHAPE (nothing launched) when the kernel does not apply: K % 64, unaligned rows,
+// operands past 32-bit offsets, or fewer 256 x 256 tiles than CUs.
+nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx, int64_t Mtok, int64_t K,
+                            int64_t R, void* Y, nm_dtype ydt, int64_t ldy, hipStream_t s) {
+    constexpr int SR = 4, ST = 2, WRN = 2, WTN = 4, BR = WRN * SR * 32, BT = WTN * ST * 32;
+    const int64_t tiles = ceil_div(R, BR) * ceil_div(Mtok, BT);
+    if (K % 64 || ((uintptr_t)W & 15u) || ((uintptr_t)X & 15u) || ldw % 8 || ldx % 8 || R * ldw * 2 >= (1LL << 32) ||
+        Mtok * ldx * 2 >= (1LL << 32) || tiles < device_cus())
+        return NM_ERR_SHAPE;
+    SpmmArgs a{};
+    a.X = (const uint8_t*)X;
+    a.vals = (const uint8_t*)W;
+    a.Y = Y;
+    a.ldx = ldx;
+    a.ldv = ldw;
+    a.ldy = ldy;
+    a.Mtok = Mtok;
+    a.K = K;
+    a.R = R;
+    a.ydt = (int)ydt;
+    a.scaled = 0;
+    a.rank = 0;
+    a.nsteps = (int)(K / 64);
+    a.tiles_r = (int)ceil_div(R, BR);
+    a.tiles_t = (int)ceil_div(Mtok, BT);
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    return check_launch("dense product");
 }
 
 }  // namespace nm

@@ -125,6 +125,11 @@ nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int6
 void launch_bitmap_encode(const void* W, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
                           void* vals, int64_t ldv, int32_t* offs, int64_t ldo, hipStream_t s);
 size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R);
+// Y = X W^T with a dense bf16 W [R, K] (ldw) on the dense split ring; NM_ERR_SHAPE without a
+// launch when it does not apply (K % 64, unaligned rows, 32-bit offsets, fewer 256 x 256
+// tiles than CUs).
+nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx, int64_t Mtok, int64_t K,
+                            int64_t R, void* Y, nm_dtype ydt, int64_t ldy, hipStream_t s);
 nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
                              const uint8_t* mask, int64_t ldm, const int32_t* offs, int64_t ldo, int64_t R, void* Y,
                              nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);

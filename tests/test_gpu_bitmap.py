@@ -4,7 +4,8 @@
 integer-valued inputs (every partial sum exact in f32), within 2e-2 ||x|| ||w_hat|| and
 the float-accumulation bound on random ones -- for unstructured masks of several
 densities, 2:4 and 6:8 masks, ragged edges, a K split over blocks, up to 4 tokens (the
-row-streaming kernel) and rows whose kept count exceeds the value capacity."""
+row-streaming kernel), a full round of 256 x 256 tiles (the dense split ring on the
+decoded weight) and rows whose kept count exceeds the value capacity."""
 import numpy as np
 import pytest
 import torch
@@ -59,7 +60,10 @@ def test_bitmap_encode_capacity_drops_last_values(nm):
 
 # (tokens, rows, K, mask): K split over blocks (few tiles), many tokens, ragged edges
 @pytest.mark.parametrize("Mt,R,K,kind", [(1, 200, 1024, "0.5"), (16, 130, 512, "2:4"), (100, 300, 2048, "6:8"),
-                                         (300, 260, 512, "0.5"), (520, 130, 256, "0.3"), (2100, 1030, 1152, "0.5")])
+                                         (300, 260, 512, "0.5"), (520, 130, 256, "0.3"), (2100, 1030, 1152, "0.5"),
+                                         # a full round of 256 x 256 tiles: the dense split ring on the decoded
+                                         # weight (exactly one round; ragged on both edges)
+                                         (2048, 8192, 256, "6:8"), (2100, 8200, 192, "0.5")])
 def test_spmm_bitmap_integer_exact(nm, Mt, R, K, kind):
     g = np.random.default_rng(Mt * 3 + R + K)
     X = O.f32_to_bf16(g.integers(-4, 5, (Mt, K)).astype(np.float32))
@@ -85,7 +89,7 @@ def test_spmm_bitmap_few_tokens_integer_exact(nm, Mt, R, K, kind):
 
 
 @pytest.mark.parametrize("Mt,R,K,kind", [(8, 300, 2048, "0.5"), (400, 520, 1024, "6:8"), (1, 700, 4096, "6:8"),
-                                         (4, 300, 2048, "0.5")])
+                                         (4, 300, 2048, "0.5"), (2048, 8192, 320, "0.5")])
 def test_spmm_bitmap_random_tolerance(nm, Mt, R, K, kind):
     g = np.random.default_rng(Mt + R + K + 1)
     X = O.f32_to_bf16(g.standard_normal((Mt, K)).astype(np.float32))
