@@ -561,8 +561,9 @@ nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx
         ws = (uint8_t*)ws + db;
         ws_bytes -= db;
         // enough 256 x 256 tiles for every CU: the dense split ring on the decoded weight
-        if (launch_dense_ring(a.dense, K, a.X, ldx, Mtok, K, R, Y, ydt, ldy, s) == NM_OK)
-            return check_launch("nm_spmm_bitmap");
+        // (NM_ERR_SHAPE: it does not apply, nothing was launched; any other status is final)
+        const nm_status dr = launch_dense_ring(a.dense, K, a.X, ldx, Mtok, K, R, Y, ydt, ldy, s);
+        if (dr != NM_ERR_SHAPE) return dr;
     }
     const int ks = bitmap_splits(Mtok, K, R);
     a.steps_per_split = (int)ceil_div(a.nsteps, ks);
