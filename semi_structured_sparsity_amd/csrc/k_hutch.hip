@@ -8,9 +8,11 @@
 //   gemm1: U_p = V_p X^T  [R, n] for all probes at once (probes stacked along
 //          rows), V generated in registers from a counter-based SplitMix64 and
 //          never stored; U is rounded to bf16 into the workspace.
-//   gemm2: for a [128 x 128] tile of D, loop over probes: G = U_p X (inner
-//          dimension n, from a transposed copy of X), then D += V_p .* G with
-//          V_p regenerated for the tile; D is written once, scaled by 2/P.
+//   gemm2: for a tile of D, loop over probes: G = U_p X (inner dimension n, from
+//          a transposed copy of X), then D += V_p .* G with V_p regenerated for
+//          the tile; D is written once, scaled by 2/P.  The dense split ring
+//          (k_spmm.hip) runs it on 256 x 256 tiles; hutch_gemm2_kernel below (128 x
+//          128 tiles) where that does not apply.
 // Operand layout (gfx950, verified on hardware): lane l holds A row (l%32),
 // K [8(l/32), +8); B column (l%32), K [8(l/32), +8); C column (l%32), rows
 // 8(e/4) + 4(l/32) + e%4.
@@ -25,10 +27,6 @@ constexpr int HT = 128;          // tile rows and columns
 constexpr int HK = 64;           // inner step
 constexpr int HS = HK * 2 + 16;  // LDS row stride in bytes (128 + pad)
 
-// Rademacher word: 64 signs for row o, columns [64*kb, 64*kb + 64) of probe p.
-__device__ __forceinline__ uint64_t rad_word(uint64_t seed, int p, int64_t o, int64_t kb, int64_t kblocks) {
-    return splitmix64_at(seed, ((uint64_t)p << 40) + (uint64_t)o * (uint64_t)kblocks + (uint64_t)kb);
-}
 
 // 8 sign bits -> 8 bf16 values of +-1 (bit set -> -1).
 __device__ __forceinline__ uint4 signs_to_bf16x8(uint32_t byte) {
@@ -288,8 +286,10 @@ void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t
                        dim3(256), 0, s, Xb, ldx, n, K, R, probes, seed, U);
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 64), (unsigned)ceil_div(n, 64)), dim3(256), 0, s,
                        Xb, ldx, n, K, XT);
-    hipLaunchKernelGGL(hutch_gemm2_kernel, dim3((unsigned)ceil_div(R, HT), (unsigned)ceil_div(K, HT)), dim3(256), 0, s,
-                       (const uint16_t*)U, (const uint16_t*)XT, n, K, R, probes, seed, D, ldd);
+    // the dense split ring where it applies (aligned workspace, 32-bit offsets), else 128 x 128 tiles
+    if (launch_hutch_ring(U, XT, n, K, R, probes, seed, D, ldd, s) == NM_ERR_SHAPE)
+        hipLaunchKernelGGL(hutch_gemm2_kernel, dim3((unsigned)ceil_div(R, HT), (unsigned)ceil_div(K, HT)), dim3(256), 0, s,
+                           (const uint16_t*)U, (const uint16_t*)XT, n, K, R, probes, seed, D, ldd);
 }
 
 }  // namespace nm

@@ -90,6 +90,9 @@ struct SpmmArgs {
     const uint16_t* lr_b;
     int64_t ldu, ldb;
     int rank;
+    // Hutchinson mode of the dense split ring: probes, their seed, stages per probe
+    uint64_t seed;
+    int probes, pstages;
 };
 
 // Per-dtype step geometry of the register-staged kernel: a step stages 128 bytes of
@@ -1029,7 +1032,14 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
 // four MFMA depths.  One barrier per stage, before its last depth: stage s+1 has landed
 // and every wave has read stage s, whose buffers then take stage s+2.  Used for the
 // many-token product of weights decoded from the bitmap format.
-template <int SR, int ST, int WRN, int WTN>
+// HUTCH: the Hutchinson second product D = (2/P) sum_p V_p .* (U_p X) (D [R, K] f32 as Y
+// [Mtok = R rows, R = K columns]): the A operand is the transposed calibration rows XT [K, n]
+// (vals), the B operand probe p's rows of U [P*R, n] (X); the stage index runs over
+// (probe, stage of n).  With signs s_p = +-1 one set of accumulators carries the sum:
+// before probe p's products it is multiplied by s_{p-1} s_p and after the last by
+// s_{P-1}, so that after probe p it holds s_p .* (D_{p-1} + s_p .* G_p).  Each lane's
+// signs are four Rademacher words per probe (its two rows of U, two 64-column blocks).
+template <int SR, int ST, int WRN, int WTN, bool HUTCH = false>
 __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs a) {
     constexpr int NW = WRN * WTN, BR = WRN * SR * 32, BT = WTN * ST * 32;
     constexpr int WSTAGE = BR * 128, XSTAGE = BT * 128;
@@ -1045,7 +1055,8 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     int tr, tt;
     tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
     const int64_t r0 = (int64_t)tr * BR, t0 = (int64_t)tt * BT;
-    const int nsteps = a.nsteps;   // K / 64 >= 1
+    const int nsteps = a.nsteps;   // K / 64 >= 1 (HUTCH: probes * stages per probe)
+    const int PS = HUTCH ? a.pstages : nsteps;
     const uint32_t sbase = lds_addr(smem);
     auto sw = [](int r) { return (r >> 1) & 7; };   // row / token r of 8 chunks: logical c at c ^ sw(r)
     const void* baseW = uniform_ptr(a.vals + r0 * a.ldv * 2);
@@ -1066,10 +1077,13 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     }
     auto issue = [&](int s) __attribute__((always_inline)) {
         const uint32_t sw0 = sbase + (uint32_t)(W_OFF + (s & 1) * WSTAGE), sx0 = sbase + (uint32_t)(X_OFF + (s & 1) * XSTAGE);
+        // HUTCH: stage s % PS of probe s / PS (the probe's U rows follow the previous probe's)
+        const int ks = HUTCH ? s % PS : s;
+        const uint32_t xp = HUTCH ? (uint32_t)(s / PS) * (uint32_t)(a.Mtok * a.ldx * 2) : 0u;
 #pragma unroll
-        for (int i = 0; i < NWL; ++i) dma16s(sw0 + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(s * 128));
+        for (int i = 0; i < NWL; ++i) dma16s(sw0 + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(ks * 128));
 #pragma unroll
-        for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + (uint32_t)(s * 128));
+        for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * 128));
     };
     struct Frag {
         i32x4_t a[SR], b[ST];
@@ -1102,6 +1116,33 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
                                                                      __builtin_bit_cast(bf16x8_t, f.b[j]), acc[i][j], 0, 0, 0);
     };
+    // HUTCH: a lane's sign words of a probe, per token sub-tile j (a row o of U) and 64-column
+    // block of its A rows (sub-tiles 0-1 and 2-3), recomputed where needed rather than kept
+    // live across the loop; flip multiplies acc by the signs of w
+    auto flip = [&](const uint64_t (&w)[ST][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i)
+#pragma unroll
+            for (int j = 0; j < ST; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int k = (wr * SR + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);   // multiple-of-64 base
+                    const uint32_t bit = (uint32_t)(w[j][i >> 1] >> (k & 63)) & 1u;
+                    acc[i][j][e] = __uint_as_float(__float_as_uint(acc[i][j][e]) ^ (bit << 31));
+                }
+    };
+    auto probe_words = [&](int p, uint64_t (&w)[ST][2]) __attribute__((always_inline)) {
+        const int64_t kblocks = a.R / 64;
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int64_t o = t0 + (wt * ST + j) * 32 + l32, oc = o < a.Mtok ? o : a.Mtok - 1;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t kb = (r0 + wr * SR * 32) / 64 + b, kbc = kb < kblocks ? kb : kblocks - 1;
+                w[j][b] = rad_word(a.seed, p, oc, kbc, kblocks);
+            }
+        }
+    };
     constexpr int PER = NWL + NXL;
     Frag fa, fb;
     issue(0);
@@ -1113,6 +1154,21 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     }
     read_depth(0, 0, fa);
     for (int s = 0; s < nsteps; ++s) {
+        if constexpr (HUTCH) {
+            if (s % PS == 0) {   // probe p = s / PS begins: acc *= s_{p-1} s_p (s_p for p = 0)
+                const int p = s / PS;
+                uint64_t wn[ST][2], wo[ST][2];
+                probe_words(p, wn);
+                if (p > 0) {
+                    probe_words(p - 1, wo);
+#pragma unroll
+                    for (int j = 0; j < ST; ++j)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) wn[j][b] ^= wo[j][b];
+                }
+                flip(wn);
+            }
+        }
         read_depth(s, 1, fb);
         mfmas(fa);
         read_depth(s, 2, fa);
@@ -1124,6 +1180,11 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         if (s + 2 < nsteps) issue(s + 2);
         if (s + 1 < nsteps) read_depth(s + 1, 0, fa);
         mfmas(fb);
+    }
+    if constexpr (HUTCH) {   // acc *= s_{P-1}
+        uint64_t wl[ST][2];
+        probe_words(a.probes - 1, wl);
+        flip(wl);
     }
     wait_vm_all();
     __syncthreads();
@@ -1966,6 +2027,37 @@ nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, i
     a.tiles_t = (int)ceil_div(Mtok, BT);
     hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
     return check_launch("dense product");
+}
+
+// D [R, K] (ldd) = (2/P) sum_p V_p .* (U_p X): U [P*R, n] and XT [K, n] bf16 in the workspace.
+nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, int64_t K, int64_t R, int probes,
+                            uint64_t seed, float* D, int64_t ldd, hipStream_t s) {
+    constexpr int SR = 4, ST = 2, WRN = 2, WTN = 4, BR = WRN * SR * 32, BT = WTN * ST * 32;
+    if (n % 64 || K % 64 || ((uintptr_t)U & 15u) || ((uintptr_t)XT & 15u) || (int64_t)probes * R * n * 2 >= (1LL << 32) ||
+        K * n * 2 >= (1LL << 32) || (int64_t)probes * (n / 64) >= (1LL << 31))
+        return NM_ERR_SHAPE;
+    SpmmArgs a{};
+    a.vals = (const uint8_t*)XT;   // A: rows k of D's columns
+    a.ldv = n;
+    a.X = (const uint8_t*)U;       // B: rows o of U_p
+    a.ldx = n;
+    a.Y = D;
+    a.ydt = NM_F32;
+    a.ldy = ldd;
+    a.Mtok = R;
+    a.R = K;
+    a.K = n;
+    a.scaled = 1;
+    a.w_scale = 2.0f / (float)probes;
+    a.seed = seed;
+    a.probes = probes;
+    a.pstages = (int)(n / 64);
+    a.nsteps = probes * a.pstages;
+    a.tiles_r = (int)ceil_div(K, BR);
+    a.tiles_t = (int)ceil_div(R, BT);
+    const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, true>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    return check_launch("nm_hdiag_hutchinson");
 }
 
 }  // namespace nm

@@ -63,6 +63,12 @@ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
     return z ^ (z >> 31);
 }
 
+// Rademacher word of the Hutchinson probes: 64 signs (bit set = -1) for row o, columns
+// [64*kb, 64*kb + 64) of probe p.
+__device__ __forceinline__ uint64_t rad_word(uint64_t seed, int p, int64_t o, int64_t kb, int64_t kblocks) {
+    return splitmix64_at(seed, ((uint64_t)p << 40) + (uint64_t)o * (uint64_t)kblocks + (uint64_t)kb);
+}
+
 inline int index_bits(int M) {
     int b = 0;
     while ((1 << b) < M) ++b;
@@ -128,6 +134,11 @@ size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R);
 // Y = X W^T with a dense bf16 W [R, K] (ldw) on the dense split ring; NM_ERR_SHAPE without a
 // launch when it does not apply (K % 64, unaligned rows, 32-bit offsets, fewer 256 x 256
 // tiles than CUs).
+// Hutchinson second product D = (2/P) sum_p V_p .* (U_p X) on the dense split ring (U [P*R, n]
+// probes stacked along rows, XT [K, n] the transposed calibration rows); NM_ERR_SHAPE without
+// a launch when it does not apply (unaligned workspace, 32-bit offsets).
+nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, int64_t K, int64_t R, int probes,
+                            uint64_t seed, float* D, int64_t ldd, hipStream_t s);
 nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx, int64_t Mtok, int64_t K,
                             int64_t R, void* Y, nm_dtype ydt, int64_t ldy, hipStream_t s);
 nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,

@@ -46,6 +46,33 @@ def test_hutchinson_matches_oracle_rows(nm, n, K, R, P):
     assert np.abs(D[rows] - ref).max() < 0.1 * tol.min() + 1e-6
 
 
+def test_hutchinson_unaligned_workspace_uses_tile_kernel(nm):
+    """A workspace 8 bytes off 16-byte alignment sends the second product to the 128 x 128
+    tile kernel instead of the split ring; on integer inputs both equal the oracle's rows
+    and each other exactly."""
+    n, K, R, P = 128, 256, 300, 4
+    g = np.random.default_rng(5)
+    Xb = O.f32_to_bf16(g.integers(-1, 2, (n, K)).astype(np.float32))
+    Xd = np_bf16(Xb).to(dev())
+    seed = 91
+    D_ring = nm.nm_hdiag_hutchinson(Xd, R, P, seed).cpu().numpy()
+    r = nm.raw
+    need = r.nm_hutchinson_workspace(n, K, R, P)
+    ws = torch.empty(need + 64, dtype=torch.uint8, device=dev())
+    D = torch.empty((R, K), dtype=torch.float32, device=dev())
+    st = r.nm_hdiag_hutchinson(Xd.data_ptr(), n, K, K, R, P, seed, D.data_ptr(), K, ws.data_ptr() + 8, need,
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == 0, nm.last_error()
+    torch.cuda.synchronize()
+    D_tile = D.cpu().numpy()
+    # |x| <= 1 and K = 256: every entry of V X^T is an integer of magnitude <= 256 (exact in
+    # bf16) and every sum after it an integer below 2^24, so both kernels are exact whatever
+    # their order
+    assert np.array_equal(D_ring, D_tile)
+    rows = np.unique(np.r_[0, R - 1, g.integers(0, R, 16)])
+    assert np.array_equal(D_tile[rows].astype(np.float64), O.hutchinson_rows(Xb, P, seed, rows))
+
+
 def test_stats_and_gate(nm):
     g = np.random.default_rng(8)
     R, K, steps = 96, 512, 8
