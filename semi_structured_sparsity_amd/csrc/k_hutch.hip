@@ -6,8 +6,10 @@
 //     D = (1/P) sum_p V_p .* (2 (V_p X^T) X).
 // Two dense bf16 MFMA GEMMs (v_mfma_f32_32x32x16_bf16, f32 accumulation):
 //   gemm1: U_p = V_p X^T  [R, n] for all probes at once (probes stacked along
-//          rows), V generated in registers from a counter-based SplitMix64 and
-//          never stored; U is rounded to bf16 into the workspace.
+//          rows), V generated from a counter-based SplitMix64 and never stored
+//          (into the LDS stages of the dense split ring, k_spmm.hip, or in
+//          registers in hutch_gemm1_kernel below); U is rounded to bf16 into the
+//          workspace.
 //   gemm2: for a tile of D, loop over probes: G = U_p X (inner dimension n, from
 //          a transposed copy of X), then D += V_p .* G with V_p regenerated for
 //          the tile; D is written once, scaled by 2/P.  The dense split ring
@@ -28,17 +30,6 @@ constexpr int HK = 64;           // inner step
 constexpr int HS = HK * 2 + 16;  // LDS row stride in bytes (128 + pad)
 
 
-// 8 sign bits -> 8 bf16 values of +-1 (bit set -> -1).
-__device__ __forceinline__ uint4 signs_to_bf16x8(uint32_t byte) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = 0x3F80u | (((byte >> (2 * e)) & 1u) << 15);
-        const uint32_t hi = 0x3F80u | (((byte >> (2 * e + 1)) & 1u) << 15);
-        w[e] = lo | (hi << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 // Stage a [128 x 64] bf16 tile (rows row0.., columns col0..) of a row-major
 // matrix into registers: 1024 16-byte chunks, 4 per thread; rows >= nrows load 0.
@@ -281,9 +272,12 @@ void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t
     uint16_t* U = (uint16_t*)ws;
     uint16_t* XT = U + (size_t)probes * (size_t)R * (size_t)n;
     const uint16_t* Xb = (const uint16_t*)X;
+    // the dense split ring with the probe rows generated into LDS where it applies, else the
+    // register-generating tile kernel
     constexpr int SR1 = 2;   // 128 stacked rows per block (256 measured no faster: the sign generation bounds it)
-    hipLaunchKernelGGL(hutch_gemm1_kernel<SR1>, dim3((unsigned)ceil_div((int64_t)probes * R, 64 * SR1), (unsigned)ceil_div(n, HT)),
-                       dim3(256), 0, s, Xb, ldx, n, K, R, probes, seed, U);
+    if (launch_hutch_u_ring(Xb, ldx, n, K, R, probes, seed, U, s) == NM_ERR_SHAPE)
+        hipLaunchKernelGGL(hutch_gemm1_kernel<SR1>, dim3((unsigned)ceil_div((int64_t)probes * R, 64 * SR1), (unsigned)ceil_div(n, HT)),
+                           dim3(256), 0, s, Xb, ldx, n, K, R, probes, seed, U);
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 64), (unsigned)ceil_div(n, 64)), dim3(256), 0, s,
                        Xb, ldx, n, K, XT);
     // the dense split ring where it applies (aligned workspace, 32-bit offsets), else 128 x 128 tiles

@@ -90,9 +90,11 @@ struct SpmmArgs {
     const uint16_t* lr_b;
     int64_t ldu, ldb;
     int rank;
-    // Hutchinson mode of the dense split ring: probes, their seed, stages per probe
+    // Hutchinson modes of the dense split ring: probes, their seed, stages per probe, rows
+    // per probe
     uint64_t seed;
     int probes, pstages;
+    int64_t prows;
 };
 
 // Per-dtype step geometry of the register-staged kernel: a step stages 128 bytes of
@@ -1039,8 +1041,15 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
 // before probe p's products it is multiplied by s_{p-1} s_p and after the last by
 // s_{P-1}, so that after probe p it holds s_p .* (D_{p-1} + s_p .* G_p).  Each lane's
 // signs are four Rademacher words per probe (its two rows of U, two 64-column blocks).
-template <int SR, int ST, int WRN, int WTN, bool HUTCH = false>
+// GEN: the Hutchinson first product U [P*R, n] = V X^T: the A operand is the calibration
+// rows X [n, K] (vals), the B operand the stacked probe rows q = p R + o of V, generated
+// into the B stages (one Rademacher word per row and stage, each of the 512 threads
+// expanding half a row into four swizzled 16-byte chunks); the barrier that follows every
+// stage's issue covers these LDS writes as it covers the DMA.
+// MODE: 0 plain, 1 HUTCH, 2 GEN.
+template <int SR, int ST, int WRN, int WTN, int MODE = 0>
 __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs a) {
+    constexpr bool HUTCH = MODE == 1, GEN = MODE == 2;
     constexpr int NW = WRN * WTN, BR = WRN * SR * 32, BT = WTN * ST * 32;
     constexpr int WSTAGE = BR * 128, XSTAGE = BT * 128;
     constexpr int W_OFF = 0, X_OFF = 2 * WSTAGE, RING = X_OFF + 2 * XSTAGE;
@@ -1063,6 +1072,16 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     const void* baseX = uniform_ptr(a.X + t0 * a.ldx * 2);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
     uint32_t oW[NWL], oX[NXL];
+    // GEN: this thread's row of the B stage and its stacked probe row (p, o)
+    static_assert(!GEN || (BT == 256 && NW == 8), "GEN: 512 threads cover 256 rows in halves");
+    const int grow = tid >> 1, ghalf = tid & 1;
+    int gp = 0;
+    int64_t go = 0;
+    if constexpr (GEN) {
+        const int64_t q = t0 + grow, qc = q < a.Mtok ? q : a.Mtok - 1;
+        gp = (int)(qc / a.prows);
+        go = qc - (int64_t)gp * a.prows;
+    }
 #pragma unroll
     for (int i = 0; i < NWL; ++i) {
         const int row = (wave * NWL + i) * 8 + (lane >> 3);
@@ -1082,8 +1101,18 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         const uint32_t xp = HUTCH ? (uint32_t)(s / PS) * (uint32_t)(a.Mtok * a.ldx * 2) : 0u;
 #pragma unroll
         for (int i = 0; i < NWL; ++i) dma16s(sw0 + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(ks * 128));
+        if constexpr (GEN) {
+            const uint64_t w = rad_word(a.seed, gp, go, s, a.K / 64);
+            uint8_t* xrow = smem + X_OFF + (s & 1) * XSTAGE + grow * 128;
 #pragma unroll
-        for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * 128));
+            for (int c = 0; c < 4; ++c) {
+                const int cl = ghalf * 4 + c;
+                *(uint4*)(xrow + ((cl ^ sw(grow)) * 16)) = signs_to_bf16x8((uint32_t)(w >> (8 * cl)) & 0xffu);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * 128));
+        }
     };
     struct Frag {
         i32x4_t a[SR], b[ST];
@@ -1143,7 +1172,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
             }
         }
     };
-    constexpr int PER = NWL + NXL;
+    constexpr int PER = NWL + (GEN ? 0 : NXL);   // DMA loads per stage
     Frag fa, fb;
     issue(0);
     if (nsteps > 1) {
@@ -2056,7 +2085,33 @@ nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, in
     a.tiles_r = (int)ceil_div(K, BR);
     a.tiles_t = (int)ceil_div(R, BT);
     const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
-    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, true>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 1>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    return check_launch("nm_hdiag_hutchinson");
+}
+
+// U [P*R, n] (bf16, row stride n) = V X^T, X [n, K] (ldx); V from the probes' Rademacher words.
+nm_status launch_hutch_u_ring(const uint16_t* X, int64_t ldx, int64_t n, int64_t K, int64_t R, int probes,
+                              uint64_t seed, uint16_t* U, hipStream_t s) {
+    constexpr int SR = 4, ST = 2, WRN = 2, WTN = 4, BR = WRN * SR * 32, BT = WTN * ST * 32;
+    // per-lane DMA offsets are 32-bit from the block's first row: 256 rows and a row's columns
+    if (K % 64 || ((uintptr_t)X & 15u) || ldx % 8 || (256 * ldx + K) * 2 >= (1LL << 32)) return NM_ERR_SHAPE;
+    SpmmArgs a{};
+    a.vals = (const uint8_t*)X;   // A: rows i of the calibration set
+    a.ldv = ldx;
+    a.Y = U;
+    a.ydt = NM_BF16;
+    a.ldy = n;
+    a.Mtok = (int64_t)probes * R;   // B: stacked probe rows
+    a.R = n;
+    a.K = K;
+    a.seed = seed;
+    a.probes = probes;
+    a.prows = R;
+    a.nsteps = (int)(K / 64);
+    a.tiles_r = (int)ceil_div(n, BR);
+    a.tiles_t = (int)ceil_div(a.Mtok, BT);
+    const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 2>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
     return check_launch("nm_hdiag_hutchinson");
 }
 

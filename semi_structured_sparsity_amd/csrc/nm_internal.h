@@ -69,6 +69,18 @@ __device__ __forceinline__ uint64_t rad_word(uint64_t seed, int p, int64_t o, in
     return splitmix64_at(seed, ((uint64_t)p << 40) + (uint64_t)o * (uint64_t)kblocks + (uint64_t)kb);
 }
 
+// 8 sign bits -> 8 bf16 values of +-1 (bit set -> -1).
+__device__ __forceinline__ uint4 signs_to_bf16x8(uint32_t byte) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = 0x3F80u | (((byte >> (2 * e)) & 1u) << 15);
+        const uint32_t hi = 0x3F80u | (((byte >> (2 * e + 1)) & 1u) << 15);
+        w[e] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 inline int index_bits(int M) {
     int b = 0;
     while ((1 << b) < M) ++b;
@@ -139,6 +151,11 @@ size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R);
 // a launch when it does not apply (unaligned workspace, 32-bit offsets).
 nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, int64_t K, int64_t R, int probes,
                             uint64_t seed, float* D, int64_t ldd, hipStream_t s);
+// Hutchinson first product U [P*R, n] (bf16, row stride n) = V X^T with the probe rows V
+// generated into the dense split ring's LDS stages; NM_ERR_SHAPE without a launch when it
+// does not apply (32-bit offsets).
+nm_status launch_hutch_u_ring(const uint16_t* X, int64_t ldx, int64_t n, int64_t K, int64_t R, int probes,
+                              uint64_t seed, uint16_t* U, hipStream_t s);
 nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx, int64_t Mtok, int64_t K,
                             int64_t R, void* Y, nm_dtype ydt, int64_t ldy, hipStream_t s);
 nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, int64_t ldv,
