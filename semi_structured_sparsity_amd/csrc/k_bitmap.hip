@@ -25,44 +25,62 @@ typedef int bm_i32x4_t __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ encode
 // One wave per row, 512 columns per pass: lane l owns 8 columns (one bitmap byte, one
-// 16-byte load of W).  The lanes' kept counts are scanned across the wave (inclusive
-// prefix by shuffles), so each lane knows where its values go; consecutive lanes write
-// consecutive stretches of the value row.  Lanes that start a 64-column block write its
+// 16-byte load of W, loaded a pass ahead).  The lanes' kept counts are scanned across the
+// wave (inclusive prefix by shuffles), each lane places its kept values at its prefix in
+// a per-wave LDS buffer, and the wave stores the pass's values with consecutive lanes on
+// consecutive positions of the value row.  Lanes that start a 64-column block write its
 // table entry.
 __global__ __launch_bounds__(256) void bitmap_encode_kernel(const uint16_t* __restrict__ W, int64_t ldw, int64_t R,
                                                             int64_t K, const uint8_t* __restrict__ mask, int64_t ldm,
                                                             uint16_t* __restrict__ vals, int64_t ldv,
                                                             int32_t* __restrict__ offs, int64_t ldo) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // a pass's kept values, compacted in column order (a wave's LDS accesses run in order,
+    // so only the compiler must keep the writes before the reads)
+    __shared__ uint16_t sval[4][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= R) return;   // the whole wave leaves together
     const int64_t nbytes = K / 8;
+    uint16_t* sv = sval[wave];
+    // the next pass's bitmap byte and 8 columns of W are loaded before this pass is stored
+    auto load = [&](int64_t q, uint32_t& mb, uint4& v) __attribute__((always_inline)) {
+        const bool in = q < nbytes;
+        mb = in ? mask[r * ldm + q] : 0u;
+        v = in ? *(const uint4*)(W + r * ldw + 8 * q) : make_uint4(0, 0, 0, 0);
+    };
+    uint32_t mbn;
+    uint4 vn;
+    load(lane, mbn, vn);
     int64_t base = 0;
     for (int64_t c0 = 0; c0 < nbytes; c0 += 64) {
         const int64_t q = c0 + lane;   // bitmap byte = 8-column group
-        const uint32_t mb = q < nbytes ? mask[r * ldm + q] : 0u;
+        const uint32_t mb = mbn;
+        const uint4 v = vn;
+        if (c0 + 64 < nbytes) load(q + 64, mbn, vn);
         const int cnt = __popc(mb);
         int incl = cnt;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
         }
-        const int64_t off = base + incl - cnt;
-        if (q < nbytes) {
-            if ((q & 7) == 0) offs[r * ldo + q / 8] = (int32_t)off;
-            const uint4 v = *(const uint4*)(W + r * ldw + 8 * q);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-            int64_t j = off;
+        const int rel = incl - cnt;   // this lane's first value within the pass
+        if (q < nbytes && (q & 7) == 0) offs[r * ldo + q / 8] = (int32_t)(base + rel);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        int k = rel;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if ((mb >> e) & 1u) {
-                    if (j < ldv) vals[r * ldv + j] = (uint16_t)(e & 1 ? w4[e >> 1] >> 16 : w4[e >> 1] & 0xffffu);
-                    ++j;
-                }
-            }
+        for (int e = 0; e < 8; ++e) {
+            if ((mb >> e) & 1u) sv[k++] = (uint16_t)(e & 1 ? w4[e >> 1] >> 16 : w4[e >> 1] & 0xffffu);
         }
-        base += __shfl(incl, 63, 64);
+        asm volatile("" ::: "memory");
+        const int total = __shfl(incl, 63, 64);
+        // consecutive lanes store consecutive values of the row (positions past ldv are dropped)
+        for (int t = lane; t < total; t += 64) {
+            const int64_t j = base + t;
+            if (j < ldv) vals[r * ldv + j] = sv[t];
+        }
+        asm volatile("" ::: "memory");
+        base += total;
     }
     if (lane == 0) offs[r * ldo + K / 64] = (int32_t)base;
 }
