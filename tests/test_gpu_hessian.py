@@ -29,7 +29,9 @@ def test_hutchinson_exact_for_orthogonal_columns(nm):
     assert np.array_equal(D, np.tile(2.0 * np.diag(X.T @ X).astype(np.float32), (R, 1)))
 
 
-@pytest.mark.parametrize("n,K,R,P", [(64, 128, 70, 2), (128, 256, 300, 8)])
+# one probe with one 64-column stage per probe (a sign flip at every stage boundary) and
+# one 64-column block of signs; several probes over ragged tiles
+@pytest.mark.parametrize("n,K,R,P", [(64, 128, 70, 2), (128, 256, 300, 8), (64, 64, 33, 1), (192, 320, 260, 3)])
 def test_hutchinson_matches_oracle_rows(nm, n, K, R, P):
     g = np.random.default_rng(n + K + R)
     Xb = O.f32_to_bf16(g.standard_normal((n, K)))
