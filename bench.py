@@ -491,8 +491,8 @@ def traffic_for(kernel_file: str, kernel: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build runs on a single MI355X. "
-              "The sharding design is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path runs on a single MI355X "
+              "and is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 

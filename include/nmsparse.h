@@ -81,7 +81,7 @@ const char* nm_last_error(void);
  * diagonal proxy lets importance scores refresh in O(d_in).)
  * X: [n, K] bf16 or f32, leading dim ldx elements.  H: [K] f32 out.
  * Accumulation is in f32 in a fixed (run-to-run identical) order.
- * ws: device workspace of nm_colsumsq_workspace(n, K) bytes; this build needs none
+ * ws: device workspace of nm_colsumsq_workspace(n, K) bytes; the current kernel needs none
  *     (the call returns 0) and ws may be NULL. */
 size_t nm_colsumsq_workspace(int64_t n, int64_t K);
 nm_status nm_hdiag_colsumsq(const void* X, nm_dtype xdt, int64_t n, int64_t K, int64_t ldx,
