@@ -453,13 +453,13 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     lm = torch.empty(steps, dtype=torch.float64, device=dev)
     wsg = ws_for(r.nm_gate_workspace(R, K, steps))
     row("hessian24", "A5+A6+A7", "gate/anneal -> 2:4 hard mask", lambda: chk(r.nm_gate(
-        S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps, None, K,
+        S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps, steps - 1, None, K,
         hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "alu", R * K * steps * GATE_OPS_PER_STEP)
     del S
     vals, idx = torch.empty((R, K // 2), dtype=bf, device=dev), torch.empty((R, K // 32), dtype=i32, device=dev)
     row("hessian24", "A8", "pack 28672x8192 from the hard mask", lambda: chk(r.nm_pack(
         W.data_ptr(), nm.NM_BF16, R, K, K, hm.data_ptr(), K // 8, 2, 4, nm.NM_BF16, vals.data_ptr(), K // 2,
-        idx.data_ptr(), K // 32, sh)), "hbm", R * K * 3.25)
+        idx.data_ptr(), K // 32, 0, sh)), "hbm", R * K * 3.25)
     M = 8192
     X = synth.activations_bf16(4, M, K).to(dev)
     Y = torch.empty((M, R), dtype=bf, device=dev)

@@ -36,6 +36,7 @@
  *    multiples of 16 bytes where a kernel uses vector access (NM_ERR_ALIGN).
  *  - Aliasing: outputs must not overlap inputs (NM_ERR_ALIAS).
  *  - Calls are stateless and thread-safe; calls on different streams may overlap.
+ *    The one exception to "never synchronises" is NM_FLAG_VALIDATE (below).
  */
 #ifndef NMSPARSE_H
 #define NMSPARSE_H
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 1
+#define NM_ABI_VERSION 2
 
 typedef void* nm_stream_t;
 
@@ -72,6 +73,17 @@ typedef enum { NM_F32 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3, NM_FP8 = 4 } nm_d
 
 typedef enum { NM_SCORE_HESSIAN = 0, NM_SCORE_MAGNITUDE = 1 } nm_score_mode;
 
+/* flags of the calls that pack a caller's mask (nm_pack, nm_slide_decompose).
+ * NM_FLAG_VALIDATE: before anything is written, count on the device the groups
+ * whose mask holds more bits than the format keeps (more than N of an N:M group,
+ * more than 2N-2 of a 2N slide group: "Sparse-BitNet", section 1 and "SlideSparse",
+ * section 2A), wait for the count (the call synchronises `stream`) and return
+ * NM_ERR_PATTERN, with the count in nm_last_error(), if there are any; nothing is
+ * packed then.  Without the flag such groups keep their first N (2N-2) set bits.
+ * Validating calls share one counter per device and are serialised within the
+ * process.  Other flag bits are rejected (NM_ERR_SHAPE). */
+#define NM_FLAG_VALIDATE 1u
+
 int nm_abi_version(void);
 const char* nm_last_error(void);
 
@@ -80,7 +92,9 @@ const char* nm_last_error(void);
  * activations: H[k] = sum_i X[i,k]^2.  ("Sparsity Induction", section 2C: the
  * diagonal proxy lets importance scores refresh in O(d_in).)
  * X: [n, K] bf16 or f32, leading dim ldx elements.  H: [K] f32 out.
- * Accumulation is in f32 in a fixed (run-to-run identical) order.
+ * The squares (exact in f64) are summed in f64 in a fixed (run-to-run identical)
+ * order and the sum is rounded to f32 once: H is the f32 rounding of the exact sum
+ * up to the f64 summation error (about n * 2^-53 relative).
  * ws: device workspace of nm_colsumsq_workspace(n, K) bytes; the current kernel needs none
  *     (the call returns 0) and ws may be NULL. */
 size_t nm_colsumsq_workspace(int64_t n, int64_t K);
@@ -132,13 +146,15 @@ nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, doub
  *   lmid[t] = sum m_t (1 - m_t)   (summed over 8 consecutive scores in f32, then
  *   in f64 in a fixed order).
  * The final projection keeps the top-N of m_{steps-1} per group -> hard_mask.
- * m_final (nullable): m_{steps-1} as f32 [R, K] (ldf).  stats: device [2] from
- * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0, 1 <= steps <= 64.
- * ws: nm_gate_workspace(R, K, steps) bytes. */
+ * m (nullable): m_t of step t = m_step (0 <= m_step < steps) as f32 [R, K] (ldf);
+ * m_step = steps-1 gives the last blend, which equals h because beta = 1 there,
+ * an earlier step shows the temperature sigmoid itself.  stats: device [2] from
+ * nm_score_stats.  lmid: device f64 [steps].  Requires K % M == 0,
+ * 1 <= steps <= 64.  ws: nm_gate_workspace(R, K, steps) bytes. */
 size_t nm_gate_workspace(int64_t R, int64_t K, int steps);
 nm_status nm_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats,
-                  int N, int M, float T0, float rho, int steps,
-                  float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
+                  int N, int M, float T0, float rho, int steps, int m_step,
+                  float* m, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
                   void* ws, size_t ws_bytes, nm_stream_t stream);
 
 /* ---------------------------------------------------------------- mask
@@ -157,10 +173,12 @@ nm_status nm_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int 
  * groups with fewer bits are padded with value 0 at the smallest unused
  * positions.  W: [R, K] (ldw) of dtype wdt; vals: [R, ldv] of dtype vdt
  * (f32 -> bf16 rounds to nearest even; otherwise the dtype must match);
- * idx: [R, ldi] uint32 words.  Supported: M in {4, 8}, 1 <= N < M. */
+ * idx: [R, ldi] uint32 words.  Supported: M in {4, 8}, 1 <= N < M.
+ * flags: 0 or NM_FLAG_VALIDATE. */
 nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
                   const uint8_t* mask, int64_t ldm, int N, int M, nm_dtype vdt,
-                  void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream);
+                  void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, unsigned flags,
+                  nm_stream_t stream);
 
 /* Fused score -> top-N mask -> pack in one pass over the weight.  The score is
  * taken from Wsc (dtype sdt, lds_ elements; HESSIAN with H/ldh/eps as in
@@ -184,14 +202,16 @@ nm_status nm_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float
  * smallest unused positions.  Output: lifted 2:4 vals [R, ldv] (ldv >= K'/2)
  * and idx [R, ldi] (ldi >= K'/32).  Supported: 2 <= Ns <= 8, K % (2 Ns) == 0.
  * Positions beyond a window's capacity (masks with more than 2N-2 bits in a
- * group) are dropped. */
+ * group) are dropped; NM_FLAG_VALIDATE in flags reports such groups instead. */
 nm_status nm_slide_decompose(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw,
                              const uint8_t* mask, int64_t ldm, int Ns, nm_dtype vdt,
-                             void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream);
+                             void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, unsigned flags,
+                             nm_stream_t stream);
 
 /* Fused (2Ns-2):2Ns mask selection and slide decomposition: top-(2Ns-2) of
  * every 2Ns by the score of Wsc (as nm_prune_pack), then the decomposition of
- * Wv under that mask.  mask may be NULL. */
+ * Wv under that mask.  mask may be NULL.  (The fused calls select exactly N, or
+ * 2N-2, positions per group themselves, so they take no validation flag.) */
 nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh,
                          float eps, nm_score_mode mode,
                          const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int Ns,

@@ -87,7 +87,8 @@ def _declare(L):
         "or_hutchinson_rows": (None, [P, I, I64, I64, I, U64, P, I64, P]),
         "or_hutchinson_u_rows": (None, [P, I, I64, I64, I, U64, P, I64, P]),
         "or_stats": (None, [P, I64, P, P]),
-        "or_gate_anneal": (None, [P, I64, I64, D, D, I, I, D, D, I, P, P, I64, P]),
+        "or_mask_overfull": (I64, [P, I64, I64, I64, I, I]),
+        "or_gate_anneal": (None, [P, I64, I64, D, D, I, I, D, D, I, I, P, P, I64, P]),
         "or_gate_value": (D, [F, D, D, D, D, I]),
         "or_num_threads": (I, []),
     }
@@ -190,6 +191,12 @@ def pack(W: np.ndarray, mask: np.ndarray, N: int, M: int, vdtype=None):
     mask = _c(mask, np.uint8)
     lib().or_pack(_p(W), _dt(W), R, K, K, _p(mask), mask.shape[1], N, M, vdt, _p(vals), slots, _p(idx), words)
     return vals, idx
+
+
+def mask_overfull(mask: np.ndarray, K: int, G: int, cap: int) -> int:
+    """Groups of G consecutive mask bits per row with more than cap set bits."""
+    mask = _c(mask, np.uint8)
+    return int(lib().or_mask_overfull(_p(mask), mask.shape[0], K, mask.shape[1], G, cap))
 
 
 def unpack(vals: np.ndarray, idx: np.ndarray, K: int, N: int, M: int) -> np.ndarray:
@@ -431,14 +438,17 @@ def stats(S: np.ndarray):
     return mu.value, sg.value
 
 
-def gate_anneal(S: np.ndarray, mu: float, sigma: float, N: int, M: int, T0: float, rho: float, steps: int):
-    """Returns (m_final float32 [R,K], hard mask bits, Lmid [steps] double)."""
+def gate_anneal(S: np.ndarray, mu: float, sigma: float, N: int, M: int, T0: float, rho: float, steps: int,
+                m_step: int | None = None):
+    """Returns (m_t float32 [R,K] of step t = m_step (default the last), hard mask
+    bits, Lmid [steps] double)."""
     S = _c(S, np.float32)
     R, K = S.shape
+    t = steps - 1 if m_step is None else m_step
     mf = np.empty((R, K), np.float32)
     hm = np.zeros((R, mask_bytes(K)), np.uint8)
     lm = np.empty(steps, np.float64)
-    lib().or_gate_anneal(_p(S), R, K, mu, sigma, N, M, T0, rho, steps, _p(mf), _p(hm), hm.shape[1], _p(lm))
+    lib().or_gate_anneal(_p(S), R, K, mu, sigma, N, M, T0, rho, steps, t, _p(mf), _p(hm), hm.shape[1], _p(lm))
     return mf, hm, lm
 
 

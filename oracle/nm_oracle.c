@@ -269,6 +269,22 @@ void or_pack(const void* W, int wdt, int64_t R, int64_t K, int64_t ldw,
     }
 }
 
+/* Pattern check of a caller's mask before packing: the number of groups of G
+ * consecutive mask bits of a row (G = M for N:M, 2N for the (2N-2):2N slide) that
+ * hold more than cap set bits (cap = N, or 2N-2).  [SB] section 1: an N:M group
+ * holds at most N nonzeros; [SS] 2A: the N-1 windows hold at most 2N-2.  The
+ * packers keep only the first cap set bits of such a group. */
+int64_t or_mask_overfull(const uint8_t* mask, int64_t R, int64_t K, int64_t ldm, int G, int cap) {
+    int64_t bad = 0;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t g = 0; g < K / G; ++g) {
+            int cnt = 0;
+            for (int i = 0; i < G; ++i) cnt += mask_get(mask, ldm, r, g * G + i) ? 1 : 0;
+            if (cnt > cap) ++bad;
+        }
+    return bad;
+}
+
 /* Inverse of or_pack: dense [R,K] in the value dtype, zeros off the kept set. */
 void or_unpack(const void* vals, int vdt, int64_t ldv, const uint32_t* idx, int64_t ldi,
                int64_t R, int64_t K, int N, int M, void* Wd) {
@@ -748,20 +764,23 @@ void or_stats(const float* S, int64_t count, double* mu, double* sigma) {
  *   m_t    = (1 - beta_t) g_t + beta_t h
  *   Lmid_t = sum m_t (1 - m_t)                 (binary-preference term)
  * The final projection keeps the top-N of m_{S-1} per group.
- * Outputs: m_final = m_{S-1} as float [R,K] (may be NULL), the hard mask bits,
- * and Lmid [S] in double.  All arithmetic in double. */
+ * Outputs: m_t of step t = m_step as float [R,K] (m_out may be NULL), the hard
+ * mask bits, and Lmid [S] in double.  All arithmetic in double. */
 void or_gate_anneal(const float* S, int64_t R, int64_t K, double mu, double sigma,
-                    int N, int M, double T0, double rho, int steps,
-                    float* m_final, uint8_t* hard_mask, int64_t ldm, double* lmid) {
+                    int N, int M, double T0, double rho, int steps, int m_step,
+                    float* m_out, uint8_t* hard_mask, int64_t ldm, double* lmid) {
     uint8_t* h = (uint8_t*)calloc((size_t)(R * ((K + 7) / 8)), 1);
     int64_t ldh = (K + 7) / 8;
     or_topn_mask(S, R, K, K, N, M, h, ldh);
     float* mlast = (float*)malloc((size_t)(R * K) * sizeof(float));
+    double* rowsum = (double*)malloc((size_t)(R > 0 ? R : 1) * sizeof(double));
     for (int t = 0; t < steps; ++t) {
         double T = T0 * pow(rho, (double)t);
         double beta = steps > 1 ? (double)t / (double)(steps - 1) : 1.0;
-        double acc = 0.0;
-        for (int64_t r = 0; r < R; ++r)
+        /* rows in parallel, each row's sum in column order, the row sums in row order */
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < R; ++r) {
+            double acc = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 double z = sigma > 0.0 ? ((double)S[r * K + k] - mu) / sigma : 0.0;
                 double g = 1.0 / (1.0 + exp(-z / T));
@@ -769,10 +788,15 @@ void or_gate_anneal(const float* S, int64_t R, int64_t K, double mu, double sigm
                 double m = (1.0 - beta) * g + beta * hv;
                 acc += m * (1.0 - m);
                 if (t == steps - 1) mlast[r * K + k] = (float)m;
+                if (m_out && t == m_step) m_out[r * K + k] = (float)m;
             }
+            rowsum[r] = acc;
+        }
+        double acc = 0.0;
+        for (int64_t r = 0; r < R; ++r) acc += rowsum[r];
         lmid[t] = acc;
     }
-    if (m_final) memcpy(m_final, mlast, (size_t)(R * K) * sizeof(float));
+    free(rowsum);
     or_topn_mask(mlast, R, K, K, N, M, hard_mask, ldm);
     free(mlast);
     free(h);

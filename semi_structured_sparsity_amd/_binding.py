@@ -25,6 +25,7 @@ STATUS_NAMES = ["NM_OK", "NM_ERR_NULL", "NM_ERR_SHAPE", "NM_ERR_PATTERN", "NM_ER
                 "NM_ERR_WORKSPACE", "NM_ERR_DEVICE", "NM_ERR_ALIAS"]
 NM_F32, NM_BF16, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4
 NM_SCORE_HESSIAN, NM_SCORE_MAGNITUDE = 0, 1
+NM_FLAG_VALIDATE = 1
 
 # NM_FP8 travels as torch.float8_e4m3fn (OCP e4m3 codes, one byte each)
 _DT = {torch.float32: NM_F32, torch.bfloat16: NM_BF16, torch.int8: NM_I8, torch.int32: NM_I32,
@@ -45,6 +46,7 @@ if not LIB_PATH.exists():
 raw = ctypes.CDLL(str(LIB_PATH))
 
 _P, _I64, _I, _F, _U64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+_U = ctypes.c_uint
 
 SIGNATURES = {
     "nm_abi_version": (_I, []),
@@ -57,12 +59,12 @@ SIGNATURES = {
     "nm_stats_workspace": (_SZ, [_I64, _I64]),
     "nm_score_stats": (_I, [_P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "nm_gate_workspace": (_SZ, [_I64, _I64, _I]),
-    "nm_gate": (_I, [_P, _I64, _I64, _I64, _P, _I, _I, _F, _F, _I, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "nm_gate": (_I, [_P, _I64, _I64, _I64, _P, _I, _I, _F, _F, _I, _I, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
     "nm_mask": (_I, [_P, _I64, _I64, _I64, _I, _I, _P, _I64, _P]),
-    "nm_pack": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _P]),
+    "nm_pack": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _U, _P]),
     "nm_prune_pack": (_I, [_P, _I, _I64, _P, _I64, _F, _I, _P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _I, _P, _I64,
                            _P, _I64, _P]),
-    "nm_slide_decompose": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _P, _I64, _P, _I64, _P]),
+    "nm_slide_decompose": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _P, _I64, _P, _I64, _U, _P]),
     "nm_prune_slide": (_I, [_P, _I, _I64, _P, _I64, _F, _I, _P, _I, _I64, _I64, _I64, _I, _P, _I64, _I, _P, _I64, _P,
                             _I64, _P]),
     "nm_absmean": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _SZ, _P]),
@@ -166,14 +168,16 @@ def nm_score_stats(S: torch.Tensor) -> torch.Tensor:
 
 
 def nm_gate(S: torch.Tensor, stats: torch.Tensor, N: int, M: int, T0: float, rho: float, steps: int,
-            want_m: bool = True):
+            want_m: bool = True, m_step: int | None = None):
+    """Returns (m_t [R, K] f32 of step m_step (default the last) or None, hard mask, lmid [steps])."""
     R, K = S.shape
+    t = steps - 1 if m_step is None else m_step
     mf = torch.empty((R, K), dtype=torch.float32, device=S.device) if want_m else None
     hm = torch.empty((R, (K + 7) // 8), dtype=torch.uint8, device=S.device)
     lm = torch.empty(steps, dtype=torch.float64, device=S.device)
     ws = _ws(raw.nm_gate_workspace(R, K, steps), S.device)
-    _check(raw.nm_gate(_ptr(S), R, K, _ld(S), _ptr(stats), N, M, T0, rho, steps, _ptr(mf), K, _ptr(hm), hm.shape[1],
-                       _ptr(lm), _ptr(ws), ws.numel(), _stream(S)))
+    _check(raw.nm_gate(_ptr(S), R, K, _ld(S), _ptr(stats), N, M, T0, rho, steps, t, _ptr(mf), K, _ptr(hm),
+                       hm.shape[1], _ptr(lm), _ptr(ws), ws.numel(), _stream(S)))
     return mf, hm, lm
 
 
@@ -190,13 +194,13 @@ def _pack_out(R, slots, words, vdt, device):
     return vals, idx
 
 
-def nm_pack(W: torch.Tensor, mask: torch.Tensor, N: int, M: int, vdt: int | None = None):
+def nm_pack(W: torch.Tensor, mask: torch.Tensor, N: int, M: int, vdt: int | None = None, flags: int = 0):
     R, K = W.shape
     vdt = dtype_code(W) if vdt is None else vdt
     slots = K // M * N
     vals, idx = _pack_out(R, slots, index_words(slots, M), vdt, W.device)
     _check(raw.nm_pack(_ptr(W), dtype_code(W), R, K, _ld(W), _ptr(mask), _ld(mask), N, M, vdt, _ptr(vals), slots,
-                       _ptr(idx), idx.shape[1], _stream(W)))
+                       _ptr(idx), idx.shape[1], flags, _stream(W)))
     return vals, idx
 
 
@@ -216,13 +220,13 @@ def nm_prune_pack(W: torch.Tensor, H: torch.Tensor | None, eps: float, mode: int
     return vals, idx, mask
 
 
-def nm_slide_decompose(W: torch.Tensor, mask: torch.Tensor, Ns: int, vdt: int | None = None):
+def nm_slide_decompose(W: torch.Tensor, mask: torch.Tensor, Ns: int, vdt: int | None = None, flags: int = 0):
     R, K = W.shape
     vdt = dtype_code(W) if vdt is None else vdt
     Kl = lifted_width(K, Ns)
     vals, idx = _pack_out(R, Kl // 2, (Kl + 31) // 32, vdt, W.device)
     _check(raw.nm_slide_decompose(_ptr(W), dtype_code(W), R, K, _ld(W), _ptr(mask), _ld(mask), Ns, vdt, _ptr(vals),
-                                  vals.shape[1], _ptr(idx), idx.shape[1], _stream(W)))
+                                  vals.shape[1], _ptr(idx), idx.shape[1], flags, _stream(W)))
     return vals, idx
 
 
@@ -250,9 +254,9 @@ def nm_absmean(W: torch.Tensor) -> torch.Tensor:
 
 
 def nm_quant_lift(X: torch.Tensor, Ns: int = 4, qdt: int = NM_I8) -> tuple[torch.Tensor, torch.Tensor]:
-    """Per-token int8 or FP8 codes of bf16 X (lifted for Ns = 4) and their scales."""
+    """Per-token int8 or FP8 codes of bf16 X (lifted for Ns >= 3) and their scales."""
     Mtok, K = X.shape
-    Kl = K // 8 * 12 if Ns else K
+    Kl = lifted_width(K, Ns) if Ns else K
     Xq = torch.empty((Mtok, Kl), dtype=_TORCH[qdt], device=X.device)
     sx = torch.empty(Mtok, dtype=torch.float32, device=X.device)
     _check(raw.nm_quant_lift(_ptr(X), dtype_code(X), Mtok, K, _ld(X), Ns, qdt, _ptr(Xq), Kl, _ptr(sx), _stream(X)))

@@ -235,6 +235,7 @@ void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t l
 // A thread owns one mask byte: 8 consecutive scores of a row (two 4-groups or
 // one 8-group).  For every step it forms the gate, the blend with the hard
 // target and the binary-preference term; the block sums that term per step.
+// The blend of one chosen step (m_step) is kept and written out when asked for.
 // SMAX bounds the step count at compile time so that the per-step sums live in
 // registers.  The gate uses the hardware 2^x and reciprocal (about 1 ulp each):
 // sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)).
@@ -254,8 +255,9 @@ __device__ __forceinline__ uint32_t group_topn_bits(const float* key, int g0, in
 template <int SMAX>
 __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restrict__ S, int64_t R, int64_t K,
                                                            int64_t lds, const double* __restrict__ stats, int N, int M,
-                                                           float T0, float rho, int steps, float* __restrict__ m_final,
-                                                           int64_t ldf, uint8_t* __restrict__ hard_mask, int64_t ldm,
+                                                           float T0, float rho, int steps, int m_step,
+                                                           float* __restrict__ m_out, int64_t ldf,
+                                                           uint8_t* __restrict__ hard_mask, int64_t ldm,
                                                            double* __restrict__ part) {
     __shared__ double sh[kRedThreads];
     const double mu = stats[0], sigma = stats[1];
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
         beta[t] = steps > 1 ? (float)t / (float)(steps - 1) : 1.0f;
         lm[t] = 0.0;
     }
-    const bool vec = (lds % 4) == 0 && (((uintptr_t)S) & 15) == 0 && (m_final == nullptr || ((ldf % 4) == 0 &&
-                                                                          (((uintptr_t)m_final) & 15) == 0));
+    const bool vec = (lds % 4) == 0 && (((uintptr_t)S) & 15) == 0 && (m_out == nullptr || ((ldf % 4) == 0 &&
+                                                                        (((uintptr_t)m_out) & 15) == 0));
     const int64_t stride = (int64_t)kGateBlocks * kRedThreads;
     const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
     int64_t r = u0 / bpr, b = u0 - r * bpr;                   // (row, byte) of unit u, advanced without division
@@ -307,9 +309,9 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
         float hv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = ((hbits >> i) & 1u) ? 1.0f : 0.0f;
-        float m[8];
+        float m[8], mo[8];   // m_t of the current step, and of step m_step
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = 0.f;
+        for (int i = 0; i < 8; ++i) m[i] = mo[i] = 0.f;
 #pragma unroll
         for (int t = 0; t < SMAX; ++t) {
             if (t < steps) {
@@ -323,6 +325,10 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
                     acc += mm * (1.0f - mm);
                 }
                 lm[t] += (double)acc;
+                if (t == m_step) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) mo[i] = m[i];
+                }
             }
         }
         // final projection: top-N of m_{steps-1}
@@ -339,12 +345,12 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
             for (int g = 0; g * M < ne; ++g) fbits |= group_topn_bits(km, g * M, M, N) << (g * M);
         }
         hard_mask[r * ldm + b] = (uint8_t)fbits;
-        if (m_final) {
+        if (m_out) {
             if (vec && ne == 8) {
-                *(float4*)(m_final + r * ldf + k0) = make_float4(m[0], m[1], m[2], m[3]);
-                *(float4*)(m_final + r * ldf + k0 + 4) = make_float4(m[4], m[5], m[6], m[7]);
+                *(float4*)(m_out + r * ldf + k0) = make_float4(mo[0], mo[1], mo[2], mo[3]);
+                *(float4*)(m_out + r * ldf + k0 + 4) = make_float4(mo[4], mo[5], mo[6], mo[7]);
             } else {
-                for (int i = 0; i < ne; ++i) m_final[r * ldf + k0 + i] = m[i];
+                for (int i = 0; i < ne; ++i) m_out[r * ldf + k0 + i] = mo[i];
             }
         }
         r += dr;
@@ -377,12 +383,12 @@ __global__ __launch_bounds__(kRedThreads) void gate_final_kernel(const double* _
 size_t gate_ws(int64_t, int64_t, int steps) { return (size_t)kGateBlocks * (size_t)(steps > 0 ? steps : 1) * sizeof(double); }
 
 void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
-                 float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
-                 void* ws, hipStream_t s) {
+                 float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
+                 double* lmid, void* ws, hipStream_t s) {
     double* part = (double*)ws;
 #define NM_GATE(SM)                                                                                            \
     hipLaunchKernelGGL(gate_kernel<SM>, dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, \
-                       rho, steps, m_final, ldf, hard_mask, ldm, part)
+                       rho, steps, m_step, m_out, ldf, hard_mask, ldm, part)
     if (steps <= 8) NM_GATE(8);
     else if (steps <= 16) NM_GATE(16);
     else NM_GATE(kMaxSteps);

@@ -7,6 +7,8 @@
 // (sections 1-2: N:M groups, magnitude top-N on master weights, quantise then
 // mask), "SlideSparse" (section 2A: N-1 width-4 stride-2 windows per 2N group),
 // "Sparsity Induction" (section 2C: diagonal Gauss-Newton proxy).
+#include <mutex>
+
 #include "nm_internal.h"
 
 namespace nm {
@@ -82,19 +84,21 @@ __device__ __forceinline__ uint32_t mask_bits_at(const uint8_t* mask, int64_t ld
 // One launch, no workspace.  A block owns CG column groups of 16 bytes (64 bf16 or 32
 // fp32 columns) over all rows: lane (cg, rl) walks rows rl, rl + 32, ... with eight
 // 16-byte loads in flight, then the 32 row-lane partials of each column are summed in
-// row-lane order through LDS, so the result does not depend on scheduling.
+// row-lane order through LDS, so the result does not depend on scheduling.  Squares of
+// bf16 or f32 values are exact in f64 and the sums are kept in f64 (exact for bf16 data of
+// moderate range); the column sum is rounded to f32 once at the end.
 constexpr int kColCG = 8, kColRL = 32;
 
 template <typename T>
 __global__ __launch_bounds__(256) void colsumsq_kernel(const T* __restrict__ X, int64_t n, int64_t K, int64_t ldx,
                                                        float* __restrict__ H) {
     constexpr int VEC = 16 / sizeof(T), CG = kColCG, RL = kColRL, U = 8;
-    __shared__ float red[RL][CG * VEC + 1];
+    __shared__ double red[RL][CG * VEC + 1];
     const int cg = threadIdx.x % CG, rl = threadIdx.x / CG;
     const int64_t c0 = (int64_t)blockIdx.x * CG * VEC + cg * VEC;
-    float acc[VEC];
+    double acc[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0;
     auto add = [&](const uint4& q) __attribute__((always_inline)) {
         const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -102,7 +106,8 @@ __global__ __launch_bounds__(256) void colsumsq_kernel(const T* __restrict__ X, 
             float x;
             if constexpr (sizeof(T) == 2) x = bf16_bits_to_f32((u[v >> 1] >> (16 * (v & 1))) & 0xffffu);
             else x = __uint_as_float(u[v]);
-            acc[v] = __fadd_rn(acc[v], __fmul_rn(x, x));
+            const double xd = (double)x;
+            acc[v] = __fma_rn(xd, xd, acc[v]);   // the square is exact: one rounding, the sum's
         }
     };
     if (c0 < K) {
@@ -122,9 +127,9 @@ __global__ __launch_bounds__(256) void colsumsq_kernel(const T* __restrict__ X, 
     if (threadIdx.x < CG * VEC) {
         const int64_t col = (int64_t)blockIdx.x * CG * VEC + threadIdx.x;
         if (col < K) {
-            float s = 0.f;
-            for (int i = 0; i < RL; ++i) s = __fadd_rn(s, red[i][threadIdx.x]);
-            H[col] = s;
+            double s = 0.0;
+            for (int i = 0; i < RL; ++i) s += red[i][threadIdx.x];
+            H[col] = (float)s;
         }
     }
 }
@@ -502,6 +507,53 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
             }
         }
     }
+}
+
+// ------------------------------------------------------------------ pattern check of a caller's mask
+// Groups of G consecutive mask bits of a row (G = M, or 2N for the slide; G <= 16) with
+// more than cap set bits: an N:M group holds at most N nonzeros ("Sparse-BitNet",
+// section 1), N-1 windows at most 2N-2 ("SlideSparse", section 2A), and the packers keep
+// only the first cap of them.  One thread per group; a group's bits span at most three
+// bytes, all inside the row's ceil(K/8).  The count lands in a per-device counter that
+// only the validating calls use (serialised by the host, which reads it back).
+__device__ unsigned long long g_overfull;
+
+__global__ void overfull_reset_kernel() { g_overfull = 0ull; }
+
+__global__ __launch_bounds__(256) void overfull_kernel(const uint8_t* __restrict__ mask, int64_t ldm, int64_t R,
+                                                       int64_t K, int G, int cap) {
+    const int64_t gpr = K / G, total = R * gpr;
+    uint32_t cnt = 0;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
+        const int64_t r = u / gpr, g = u - r * gpr;
+        const int64_t b0 = g * G, byte0 = b0 >> 3;
+        const int sh = (int)(b0 & 7), nb = (sh + G + 7) >> 3;
+        const uint8_t* row = mask + r * ldm + byte0;
+        uint32_t w = 0;
+        for (int i = 0; i < nb; ++i) w |= (uint32_t)row[i] << (8 * i);
+        cnt += __popc((w >> sh) & ((1u << G) - 1u)) > cap ? 1u : 0u;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(&g_overfull, (unsigned long long)cnt);
+}
+
+nm_status count_overfull(const uint8_t* mask, int64_t ldm, int64_t R, int64_t K, int G, int cap, hipStream_t s,
+                         int64_t* bad) {
+    static std::mutex mu;   // one validating call per process at a time: they share the counter
+    std::lock_guard<std::mutex> lock(mu);
+    hipLaunchKernelGGL(overfull_reset_kernel, dim3(1), dim3(1), 0, s);
+    const int64_t groups = R * (K / G);
+    hipLaunchKernelGGL(overfull_kernel, dim3(grid_cap(ceil_div(groups, 256), 4096)), dim3(256), 0, s, mask, ldm, R, K,
+                       G, cap);
+    nm_status st = check_launch("pattern check");
+    if (st != NM_OK) return st;
+    unsigned long long n = 0;
+    hipError_t e = hipMemcpyFromSymbolAsync(&n, HIP_SYMBOL(g_overfull), sizeof(n), 0, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return set_error(NM_ERR_DEVICE, "pattern check: %s", hipGetErrorString(e));
+    *bad = (int64_t)n;
+    return NM_OK;
 }
 
 void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,

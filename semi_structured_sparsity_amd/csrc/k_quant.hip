@@ -6,14 +6,17 @@
 // decide the codes):
 //   int8: s = max|x| / 127, q = rint(x / s), ties to even;
 //   fp8 : s = max|x| / 448, q = the OCP e4m3 code nearest x / s, ties to even;
-// a zero row gives s = 0 and codes 0.  With the lift, lifted column 12g + 4w + l
-// holds the code of column 8g + 2w + l (windows at offsets 0, 2, 4 of each group).
+// a zero row gives s = 0 and codes 0.  With the lift of a (2N-2):2N weight, lifted
+// column 4(N-1)g + 4w + l holds the code of column 2Ng + 2w + l (windows at offsets
+// 0, 2, .., 2N-4 of each group; for 6:8, 12g + 4w + l from 8g + 2w + l).
 //
 // One wave per token row, four rows per block: pass 1 takes the absolute maximum over
 // 16-byte loads of 8 columns and keeps up to 8 of them per lane in registers (K <= 4096
 // in one pass; longer rows re-read the rest, which is L2-resident by then); the maximum
 // is reduced across the wave; pass 2 rounds and writes each 8-column group as 12 lifted
-// bytes (three dwords) or, without the lift, 8 bytes.
+// bytes (three dwords; 6:8) or, without the lift, 8 bytes.  For other N, pass 2 takes one
+// window per lane: its 4 columns (two column pairs from the row, L2-resident by then),
+// rounded and written as one dword of the lifted row.
 #include "nm_internal.h"
 
 namespace nm {
@@ -39,10 +42,12 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
     return sign | mag;
 }
 
-template <bool LIFT, bool FP8>
+// LIFT: 0 no lift, 1 the 6:8 lift (Ns = 4), 2 the lift of any (2N-2):2N (runtime Ns)
+template <int LIFT, bool FP8>
 __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_t* __restrict__ X, int64_t ldx,
-                                                                   int64_t Mtok, int64_t K, int8_t* __restrict__ Xq,
-                                                                   int64_t ldq, float* __restrict__ sx) {
+                                                                   int64_t Mtok, int64_t K, int Ns,
+                                                                   int8_t* __restrict__ Xq, int64_t ldq,
+                                                                   float* __restrict__ sx) {
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
     if (m >= Mtok) return;   // whole waves only: no barrier below
@@ -73,23 +78,38 @@ __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_
     if (lane == 0) sx[m] = s;
 
     int8_t* qr = Xq + m * ldq;
+    auto code = [&](float x) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (FP8) {
+            return s > 0.0f ? e4m3_code(fminf(fmaxf(__fdiv_rn(x, s), -448.0f), 448.0f)) : 0u;
+        } else {
+            float q = 0.0f;
+            if (s > 0.0f) q = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.0f), 127.0f);
+            return (uint32_t)(int32_t)q & 0xffu;
+        }
+    };
+    if constexpr (LIFT == 2) {
+        // one window per lane: columns 2Ng + 2w .. +3 (two aligned column pairs)
+        const int64_t wpr = K / (2 * Ns) * (Ns - 1);
+        for (int64_t q = lane; q < wpr; q += 64) {
+            const int64_t g = q / (Ns - 1), w = q - g * (Ns - 1);
+            const uint32_t* src = (const uint32_t*)(xr + 2 * Ns * g + 2 * w);
+            const uint32_t p0 = src[0], p1 = src[1];
+            const uint32_t b0 = code(__builtin_bit_cast(float, (p0 & 0xffffu) << 16));
+            const uint32_t b1 = code(__builtin_bit_cast(float, (p0 >> 16) << 16));
+            const uint32_t b2 = code(__builtin_bit_cast(float, (p1 & 0xffffu) << 16));
+            const uint32_t b3 = code(__builtin_bit_cast(float, (p1 >> 16) << 16));
+            *(uint32_t*)(qr + 4 * q) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+        return;
+    }
     auto emit = [&](int64_t g, const uint4 v) __attribute__((always_inline)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float x = __builtin_bit_cast(float, ((w[i >> 1] >> (16 * (i & 1))) & 0xffffu) << 16);
-            if constexpr (FP8) {
-                b[i] = s > 0.0f ? e4m3_code(fminf(fmaxf(__fdiv_rn(x, s), -448.0f), 448.0f)) : 0u;
-            } else {
-                float q = 0.0f;
-                if (s > 0.0f) q = fminf(fmaxf(rintf(__fdiv_rn(x, s)), -127.0f), 127.0f);
-                b[i] = (uint32_t)(int32_t)q & 0xffu;
-            }
-        }
+        for (int i = 0; i < 8; ++i) b[i] = code(__builtin_bit_cast(float, ((w[i >> 1] >> (16 * (i & 1))) & 0xffffu) << 16));
         const uint32_t lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
         const uint32_t hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-        if constexpr (LIFT) {
+        if constexpr (LIFT == 1) {
             uint32_t* o = (uint32_t*)(qr + 12 * g);   // windows: bytes 0-3, 2-5, 4-7
             o[0] = lo;
             o[1] = (lo >> 16) | (hi << 16);
@@ -112,13 +132,18 @@ void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int 
     const dim3 g((unsigned)ceil_div(Mtok, kQuantThreads / 64)), b(kQuantThreads);
     const uint16_t* x = (const uint16_t*)X;
     int8_t* q = (int8_t*)Xq;
+#define NM_QL(L, F8) hipLaunchKernelGGL((quant_lift_kernel<L, F8>), g, b, 0, s, x, ldx, Mtok, K, Ns, q, ldq, x_scale)
+    const int lift = Ns == 0 ? 0 : (Ns == 4 ? 1 : 2);
     if (qdt == NM_FP8) {
-        if (Ns) hipLaunchKernelGGL((quant_lift_kernel<true, true>), g, b, 0, s, x, ldx, Mtok, K, q, ldq, x_scale);
-        else hipLaunchKernelGGL((quant_lift_kernel<false, true>), g, b, 0, s, x, ldx, Mtok, K, q, ldq, x_scale);
+        if (lift == 0) NM_QL(0, true);
+        else if (lift == 1) NM_QL(1, true);
+        else NM_QL(2, true);
     } else {
-        if (Ns) hipLaunchKernelGGL((quant_lift_kernel<true, false>), g, b, 0, s, x, ldx, Mtok, K, q, ldq, x_scale);
-        else hipLaunchKernelGGL((quant_lift_kernel<false, false>), g, b, 0, s, x, ldx, Mtok, K, q, ldq, x_scale);
+        if (lift == 0) NM_QL(0, false);
+        else if (lift == 1) NM_QL(1, false);
+        else NM_QL(2, false);
     }
+#undef NM_QL
 }
 
 }  // namespace nm

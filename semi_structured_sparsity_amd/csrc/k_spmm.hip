@@ -1697,7 +1697,7 @@ static int64_t device_cus() {
 }
 
 template <typename T>
-static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true) {
+static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok) {
     using G = Geo<T>;
     SpmmPlan p{};
     // up to 256 tokens: the K-split ring kernel on 64 x 32, 64 x 64 or 64 x 128 tiles, with
@@ -1788,14 +1788,15 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok = true
     return p;
 }
 
-// ------------------------------------------------------------------ 6:8 activation lift
-// The overlapping 2:4 windows of a 6:8 group (offsets 0, 2, 4 of its 8 columns)
-// multiply the lifted activation XL[m, 12q + 4w + j] = X[m, 8q + 2w + j].  For many
-// tokens it is written out once (memory-bound, 1.5x the bytes of X) so that the
-// product runs on the plain 2:4 kernels; one lane = one 8-column group.
+// ------------------------------------------------------------------ (2N-2):2N activation lift
+// The N-1 overlapping 2:4 windows of a 2N-column group (offsets 0, 2, .., 2N-4) multiply
+// the lifted activation XL[m, 4(N-1)q + 4w + j] = X[m, 2Nq + 2w + j].  Products that do
+// not gather it inside the product kernel write it out once (memory-bound, (2-2/N)x the
+// bytes of X) so that the product runs on the plain 2:4 kernels.
+// 6:8: one lane = one 8-column group, three windows from one 16-byte (bf16) or 8-byte load.
 template <typename T>
-__global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int64_t ldx, int64_t Mtok, int64_t K,
-                                                   T* __restrict__ XL, int64_t ldl) {
+__global__ __launch_bounds__(256) void lift68_kernel(const T* __restrict__ X, int64_t ldx, int64_t Mtok, int64_t K,
+                                                     T* __restrict__ XL, int64_t ldl) {
     const int64_t gpr = K / 8, total = Mtok * gpr;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += stride) {
@@ -1816,54 +1817,101 @@ __global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int6
     }
 }
 
-// 6:8 products lift X into the workspace first: the plain kernels on the lifted
-// activation beat in-kernel gathers at every token count measured
-static size_t lift_bytes(int64_t Mtok, int64_t K, int64_t es) {
-    return ((size_t)Mtok * (size_t)(K / 8 * 12) * (size_t)es + 255) & ~(size_t)255;
+// Any N: one lane = one window (4 lifted columns), read as two pairs of columns (a pair
+// starts at an even column, so it is 4-byte (bf16) or 2-byte (one-byte codes) aligned).
+template <typename T>
+__global__ __launch_bounds__(256) void lift_kernel(const T* __restrict__ X, int64_t ldx, int64_t Mtok, int64_t K,
+                                                   int Ns, T* __restrict__ XL, int64_t ldl) {
+    using P = typename std::conditional<sizeof(T) == 2, uint32_t, uint16_t>::type;   // a pair of columns
+    const int64_t wpr = K / (2 * Ns) * (Ns - 1), total = Mtok * wpr;   // windows per row
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += stride) {
+        const int64_t m = u / wpr, q = u - m * wpr;
+        const int64_t g = q / (Ns - 1), w = q - g * (Ns - 1);
+        const P* src = (const P*)(X + m * ldx + 2 * Ns * g + 2 * w);
+        const P lo = src[0], hi = src[1];
+        if constexpr (sizeof(T) == 2) *(uint2*)(XL + m * ldl + 4 * q) = make_uint2(lo, hi);
+        else *(uint32_t*)(XL + m * ldl + 4 * q) = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
 }
+
+static int64_t lifted_cols(int64_t K, int Ns) { return Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K; }
+
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+static size_t lift_bytes(int64_t Mtok, int64_t K, int Ns, int64_t es) {
+    return round256((size_t)Mtok * (size_t)lifted_cols(K, Ns) * (size_t)es);
+}
+
+// Workspace of one nm_spmm / nm_spmm_lowrank call, in the order it is carved:
+//   u, pu: the adapter's u = bf16(X A^T) and its K-split f32 partials (rank > 0),
+//   xl   : the lifted activation (Ns >= 3),
+//   f32  : the sparse product in f32 when the adapter term is added by its own kernel,
+//   part : split-K partials of the product.
+struct SpmmWs {
+    size_t u = 0, pu = 0, xl = 0, f32 = 0, part = 0;
+    size_t total() const { return u + pu + xl + f32 + part; }
+};
+
+// ring_ok: the product's operands allow the DMA ring kernels (decided by the caller from
+// the actual pointers and leading dimensions; the query takes the larger of both plans).
+static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok);
 
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
-    if (Ns) return lift_bytes(Mtok, K, xdt == NM_BF16 ? 2 : 1) + spmm_ws(Mtok, K / 8 * 12, R, 0, xdt);
-    // the plan depends on the element size only (int8 and FP8 share it)
-    SpmmPlan p = (xdt == NM_BF16) ? plan_for<uint16_t>(Mtok, K, R) : plan_for<int8_t>(Mtok, K, R);
-    if (p.KS <= 1) return 0;
-    return (size_t)p.KS * (size_t)Mtok * (size_t)R * 4;
+    const size_t a = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, true).total();
+    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, false).total();
+    return a > b ? a : b;
 }
 
-// plain 2:4 product of X [Mtok, K] (K = the lifted width for 6:8)
+// The DMA ring kernels take 16-byte pieces of the index rows and 32-bit per-lane offsets
+// from a block's base pointers.
+static bool ring_ok_for(const SpmmArgs& a, int64_t es) {
+    return ((uintptr_t)a.idx & 15u) == 0 && (a.ldi % 4) == 0 && a.R * a.ldv * es < (1LL << 32) &&
+           a.R * a.ldi * 4 < (1LL << 32) && a.Mtok * a.ldx * es < (1LL << 32);
+}
+
+static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok) {
+    SpmmWs w;
+    if (Mtok <= 0 || K <= 0 || R <= 0) return w;
+    const int64_t Kl = lifted_cols(K, Ns), es = xdt == NM_BF16 ? 2 : 1;
+    if (rank > 0) {
+        const LowRankPlan lp = lowrank_plan(Mtok, K);
+        w.u = round256((size_t)Mtok * rank * 2);
+        w.pu = round256((size_t)lp.S() * Mtok * rank * 4);
+    }
+    if (Ns) w.xl = lift_bytes(Mtok, K, Ns, es);
+    // the plan depends on the element size only (int8 and FP8 share it)
+    const SpmmPlan p = es == 2 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok) : plan_for<int8_t>(Mtok, Kl, R, ring_ok);
+    if (rank > 0 && !p.ring) w.f32 = round256((size_t)Mtok * (size_t)R * 4);
+    if (p.KS > 1) w.part = round256((size_t)p.KS * (size_t)Mtok * (size_t)R * 4);
+    return w;
+}
+
+// plain 2:4 product of X [Mtok, K] (K = the lifted width for (2N-2):2N); part: the split-K
+// partials, f32buf: the sparse product in f32 when an adapter term is added afterwards
+// (both carved from the workspace by the caller, sized by spmm_ws_layout)
 template <typename T>
-static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
-    // the ring kernel loads 16-byte pieces of the index rows
-    const bool ring_ok = ((uintptr_t)a.idx & 15u) == 0 && (a.ldi % 4) == 0 &&
-                         a.R * a.ldv * (int64_t)sizeof(T) < (1LL << 32) && a.R * a.ldi * 4 < (1LL << 32) &&
-                         a.Mtok * a.ldx * (int64_t)sizeof(T) < (1LL << 32);
+static nm_status run_spmm(SpmmArgs a, bool ring_ok, void* part, void* f32buf, hipStream_t s) {
     const SpmmPlan p = plan_for<T>(a.Mtok, a.K, a.R, ring_ok);
     a.nsteps = p.nsteps;
     a.KS = p.KS;
     a.steps_per_split = p.steps_per_split;
     a.tiles_r = p.tiles_r;
     a.tiles_t = p.tiles_t;
-    a.part = nullptr;
-    if (p.KS > 1) {
-        const size_t need = (size_t)p.KS * (size_t)a.Mtok * (size_t)a.R * 4;
-        if (!ws || ws_bytes < need) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", need);
-        a.part = ws;
-    }
+    a.part = p.KS > 1 ? part : nullptr;
     if (a.rank > 0 && !p.ring) {
         // the other kernels carry no adapter term: they write the sparse product in f32
         // into the workspace and lowrank_epilogue_kernel adds the term and converts
-        const size_t pb = ((size_t)a.Mtok * (size_t)a.R * 4 + 255) & ~(size_t)255;
-        if (!ws || ws_bytes < pb) return set_error(NM_ERR_WORKSPACE, "nm_spmm_lowrank: workspace too small");
         SpmmArgs b = a;
         b.rank = 0;
-        b.Y = ws;
+        b.Y = f32buf;
         b.ydt = NM_F32;
         b.ldy = a.R;
         b.scaled = 0;
-        const nm_status st = run_spmm<T>(b, (uint8_t*)ws + pb, ws_bytes - pb, s);
+        const nm_status st = run_spmm<T>(b, ring_ok, part, nullptr, s);
         if (st != NM_OK) return st;
         const dim3 g(grid_cap(ceil_div(a.Mtok * a.R, 256), 65536));
-        hipLaunchKernelGGL(lowrank_epilogue_kernel, g, dim3(256), 0, s, (const float*)ws, a);
+        hipLaunchKernelGGL(lowrank_epilogue_kernel, g, dim3(256), 0, s, (const float*)f32buf, a);
         return check_launch("nm_spmm_lowrank");
     }
     const dim3 grid((unsigned)(p.tiles_r * p.tiles_t), (unsigned)p.KS);
@@ -1926,22 +1974,18 @@ static nm_status run_spmm(SpmmArgs a, void* ws, size_t ws_bytes, hipStream_t s) 
     return check_launch("nm_spmm");
 }
 
-static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
-
 size_t spmm_lowrank_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank) {
-    if (Mtok <= 0 || K <= 0 || R <= 0) return 0;
-    const LowRankPlan lp = lowrank_plan(Mtok, K);
-    const size_t u = round256((size_t)Mtok * rank * 2) + round256((size_t)lp.S() * Mtok * rank * 4);
-    const int64_t Kl = Ns ? K / 8 * 12 : K;
-    const SpmmPlan p = plan_for<uint16_t>(Mtok, Kl, R);
-    const size_t f32 = p.ring ? 0 : round256((size_t)Mtok * (size_t)R * 4);
-    return u + spmm_ws(Mtok, K, R, Ns, NM_BF16) + f32;
+    const size_t a = spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, true).total();
+    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, false).total();
+    return a > b ? a : b;
 }
 
-static nm_status spmm_impl(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
-                           const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
-                           float w_scale, const LowRankIn* lr, void* Y, nm_dtype ydt, int64_t ldy, void* ws,
-                           size_t ws_bytes, hipStream_t s) {
+// Every workspace need of the call is known (and checked) before the first launch.
+static nm_status spmm_impl(const char* fn, const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,
+                           const void* vals, const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns,
+                           const float* x_scale, float w_scale, const LowRankIn* lr, void* Y, nm_dtype ydt,
+                           int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
+    if (Mtok == 0 || R == 0) return NM_OK;
     SpmmArgs a{};
     a.X = (const uint8_t*)X;
     a.vals = (const uint8_t*)vals;
@@ -1955,77 +1999,90 @@ static nm_status spmm_impl(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K,
     a.Mtok = Mtok;
     a.K = K;
     a.R = R;
-    const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
+    const int64_t Kl = lifted_cols(K, Ns);
     const int64_t es = xdt == NM_BF16 ? 2 : 1;
     a.comp_bytes = Kl / 2 * es;
     a.idx_words = (Kl + 31) / 32;   // the bitstream's last word is partial when K' % 32 == 16
     a.w_scale = w_scale;
     a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
     a.ydt = (int)ydt;
-    if (Mtok == 0 || R == 0) return NM_OK;
+    // the 2:4 product runs over the lifted width, on X itself or on the lifted activation
+    // that the workspace holds (256-byte aligned, row stride K')
+    if (Ns) {
+        a.K = Kl;
+        a.ldx = Kl;
+    }
+    const bool ring_ok = ring_ok_for(a, es);
+    const int rank = lr ? lr->rank : 0;
+    const SpmmWs w = spmm_ws_layout(Mtok, K, R, Ns, xdt, rank, ring_ok);
+    if (w.total() && (!ws || ws_bytes < w.total()))
+        return set_error(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, w.total());
+    uint8_t* wp = (uint8_t*)ws;
+    uint16_t* U = (uint16_t*)wp;
+    float* PU = (float*)(wp + w.u);
+    uint8_t* XL = wp + w.u + w.pu;
+    void* F32 = XL + w.xl;
+    void* PART = (uint8_t*)F32 + w.f32;
     if (lr) {
         // u = bf16(X A^T) from the original X, into the front of the workspace
         const LowRankPlan lp = lowrank_plan(Mtok, K);
-        const size_t ub = round256((size_t)Mtok * lr->rank * 2), pb = round256((size_t)lp.S() * Mtok * lr->rank * 4);
-        if (!ws || ws_bytes < ub + pb) return set_error(NM_ERR_WORKSPACE, "nm_spmm_lowrank: workspace too small");
-        uint16_t* U = (uint16_t*)ws;
-        float* P = (float*)((uint8_t*)ws + ub);
         const dim3 g((unsigned)ceil_div(Mtok, 32), (unsigned)lp.ks);
         const int RT = (int)ceil_div(lr->rank, 32);
         const uint16_t* Xb = (const uint16_t*)X;
         switch (RT) {
-            case 1: hipLaunchKernelGGL(lowrank_u_kernel<1>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 2: hipLaunchKernelGGL(lowrank_u_kernel<2>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 3: hipLaunchKernelGGL(lowrank_u_kernel<3>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 4: hipLaunchKernelGGL(lowrank_u_kernel<4>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 5: hipLaunchKernelGGL(lowrank_u_kernel<5>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 6: hipLaunchKernelGGL(lowrank_u_kernel<6>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            case 7: hipLaunchKernelGGL(lowrank_u_kernel<7>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
-            default: hipLaunchKernelGGL(lowrank_u_kernel<8>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, P); break;
+            case 1: hipLaunchKernelGGL(lowrank_u_kernel<1>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 2: hipLaunchKernelGGL(lowrank_u_kernel<2>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 3: hipLaunchKernelGGL(lowrank_u_kernel<3>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 4: hipLaunchKernelGGL(lowrank_u_kernel<4>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 5: hipLaunchKernelGGL(lowrank_u_kernel<5>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 6: hipLaunchKernelGGL(lowrank_u_kernel<6>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            case 7: hipLaunchKernelGGL(lowrank_u_kernel<7>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
+            default: hipLaunchKernelGGL(lowrank_u_kernel<8>, g, dim3(256), 0, s, Xb, ldx, lr->A, lr->lda, Mtok, K, lr->rank, lp.kchunk, PU); break;
         }
         const dim3 gr(grid_cap(ceil_div(Mtok * lr->rank, 256), 4096));
-        hipLaunchKernelGGL(lowrank_u_reduce_kernel, gr, dim3(256), 0, s, (const float*)P, lp.S(), Mtok, lr->rank, U);
+        hipLaunchKernelGGL(lowrank_u_reduce_kernel, gr, dim3(256), 0, s, (const float*)PU, lp.S(), Mtok, lr->rank, U);
         a.lr_u = U;
         a.ldu = lr->rank;
         a.lr_b = lr->B;
         a.ldb = lr->ldb;
         a.rank = lr->rank;
-        ws = (uint8_t*)ws + ub + pb;
-        ws_bytes -= ub + pb;
     }
     if (Ns) {
-        // 6:8: lift X into the workspace, then the plain product over the lifted width
-        const size_t xl = lift_bytes(Mtok, K, es);
-        if (!ws || ws_bytes < xl) return set_error(NM_ERR_WORKSPACE, "nm_spmm: workspace of %zu bytes needed", xl);
-        const dim3 g(grid_cap(ceil_div(Mtok * (K / 8), 256), 8192));
-        if (es == 1)   // int8 or FP8 codes: the lift moves bytes
-            hipLaunchKernelGGL(lift_kernel<int8_t>, g, dim3(256), 0, s, (const int8_t*)X, ldx, Mtok, K, (int8_t*)ws, Kl);
-        else
-            hipLaunchKernelGGL(lift_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, ldx, Mtok, K,
-                               (uint16_t*)ws, Kl);
-        a.X = (const uint8_t*)ws;
-        a.ldx = Kl;
-        a.K = Kl;
-        ws = (uint8_t*)ws + xl;
-        ws_bytes -= xl;
+        // (2N-2):2N: lift X into the workspace, then the plain product over the lifted width
+        if (Ns == 4) {
+            const dim3 g(grid_cap(ceil_div(Mtok * (K / 8), 256), 8192));
+            if (es == 1)   // int8 or FP8 codes: the lift moves bytes
+                hipLaunchKernelGGL(lift68_kernel<int8_t>, g, dim3(256), 0, s, (const int8_t*)X, ldx, Mtok, K, (int8_t*)XL, Kl);
+            else
+                hipLaunchKernelGGL(lift68_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, ldx, Mtok, K,
+                                   (uint16_t*)XL, Kl);
+        } else {
+            const dim3 g(grid_cap(ceil_div(Mtok * (Kl / 4), 256), 8192));
+            if (es == 1)
+                hipLaunchKernelGGL(lift_kernel<int8_t>, g, dim3(256), 0, s, (const int8_t*)X, ldx, Mtok, K, Ns, (int8_t*)XL, Kl);
+            else
+                hipLaunchKernelGGL(lift_kernel<uint16_t>, g, dim3(256), 0, s, (const uint16_t*)X, ldx, Mtok, K, Ns,
+                                   (uint16_t*)XL, Kl);
+        }
+        a.X = XL;
     }
-    if (xdt == NM_I8) return run_spmm<int8_t>(a, ws, ws_bytes, s);
-    if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ws, ws_bytes, s);
-    return run_spmm<uint16_t>(a, ws, ws_bytes, s);
+    if (xdt == NM_I8) return run_spmm<int8_t>(a, ring_ok, PART, F32, s);
+    if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ring_ok, PART, F32, s);
+    return run_spmm<uint16_t>(a, ring_ok, PART, F32, s);
 }
 
 nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
                       const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
                       float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
-    return spmm_impl(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, nullptr, Y, ydt, ldy, ws,
-                     ws_bytes, s);
+    return spmm_impl("nm_spmm", X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, nullptr, Y, ydt,
+                     ldy, ws, ws_bytes, s);
 }
 
 nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
                               const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const LowRankIn& lr,
                               void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s) {
-    return spmm_impl(X, NM_BF16, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, nullptr, 1.0f, &lr, Y, ydt, ldy, ws,
-                     ws_bytes, s);
+    return spmm_impl("nm_spmm_lowrank", X, NM_BF16, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, nullptr, 1.0f, &lr, Y,
+                     ydt, ldy, ws, ws_bytes, s);
 }
 
 // Y [Mtok, R] (ydt bf16 or f32, ldy) = X [Mtok, K] (ldx) W^T, W [R, K] (ldw) dense bf16.

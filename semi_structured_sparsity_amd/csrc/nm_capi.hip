@@ -157,26 +157,29 @@ nm_status nm_score_stats(const float* S, int64_t R, int64_t K, int64_t lds, doub
 size_t nm_gate_workspace(int64_t R, int64_t K, int steps) { return gate_ws(R, K, steps); }
 
 nm_status nm_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
-                  float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
-                  void* ws, size_t ws_bytes, nm_stream_t stream) {
+                  float rho, int steps, int m_step, float* m, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
+                  double* lmid, void* ws, size_t ws_bytes, nm_stream_t stream) {
     const char* fn = "nm_gate";
     NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
     nm_status st = check_pattern(N, M, fn);
     if (st != NM_OK) return st;
     NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
     NM_REQ(steps >= 1 && steps <= 64, NM_ERR_SHAPE, "%s: steps must be in [1, 64]", fn);
+    NM_REQ(!m || (m_step >= 0 && m_step < steps), NM_ERR_SHAPE, "%s: m_step must be in [0, steps)", fn);
     NM_REQ(T0 > 0.f && rho > 0.f, NM_ERR_SHAPE, "%s: T0 and rho must be positive", fn);
     NM_REQ(stats && lmid, NM_ERR_NULL, "%s: stats / lmid is NULL", fn);
     NM_REQ((S && hard_mask) || R * K == 0, NM_ERR_NULL, "%s: NULL pointer", fn);
-    NM_REQ(lds >= K && ldm >= (K + 7) / 8 && (!m_final || ldf >= K), NM_ERR_SHAPE, "%s: leading dimension too small",
-           fn);
+    NM_REQ(lds >= K && ldm >= (K + 7) / 8 && (!m || ldf >= K), NM_ERR_SHAPE, "%s: leading dimension too small", fn);
     const size_t need = gate_ws(R, K, steps);
     NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
-    const Range rs = span(S, R, K, lds, 4);
-    NM_REQ(!overlap(rs, span(hard_mask, R, (K + 7) / 8, ldm, 1)) && !overlap(rs, span(m_final, R, K, ldf, 4)) &&
-               !overlap(rs, span(lmid, 1, steps, steps, 8)),
-           NM_ERR_ALIAS, "%s: an output overlaps S", fn);
-    launch_gate(S, R, K, lds, stats, N, M, T0, rho, steps, m_final, ldf, hard_mask, ldm, lmid, ws,
+    const Range rs = span(S, R, K, lds, 4), rh = span(hard_mask, R, (K + 7) / 8, ldm, 1), rm = span(m, R, K, ldf, 4);
+    const Range rl = span(lmid, 1, steps, steps, 8), rw = Range{(uintptr_t)ws, (uintptr_t)ws + need};
+    const Range ins[2] = {rs, span(stats, 1, 2, 2, 8)};
+    for (const Range& x : ins)
+        NM_REQ(!overlap(x, rh) && !overlap(x, rm) && !overlap(x, rl) && !overlap(x, rw), NM_ERR_ALIAS,
+               "%s: an output or the workspace overlaps S or stats", fn);
+    NM_REQ(!overlap(rh, rm) && !overlap(rh, rl) && !overlap(rm, rl), NM_ERR_ALIAS, "%s: outputs overlap", fn);
+    launch_gate(S, R, K, lds, stats, N, M, T0, rho, steps, m ? m_step : -1, m, ldf, hard_mask, ldm, lmid, ws,
                 (hipStream_t)stream);
     return check_launch(fn);
 }
@@ -211,11 +214,24 @@ static nm_status check_pack_out(const char* fn, nm_dtype wdt, nm_dtype vdt, int6
     return NM_OK;
 }
 
+// NM_FLAG_VALIDATE: count the mask's groups with more than cap bits (a stream
+// synchronisation) and refuse to pack when there are any.
+static nm_status validate_mask(const char* fn, unsigned flags, const uint8_t* mask, int64_t ldm, int64_t R, int64_t K,
+                               int G, int cap, nm_stream_t stream) {
+    if (!(flags & NM_FLAG_VALIDATE)) return NM_OK;
+    int64_t bad = 0;
+    const nm_status st = count_overfull(mask, ldm, R, K, G, cap, (hipStream_t)stream, &bad);
+    if (st != NM_OK) return st;
+    NM_REQ(bad == 0, NM_ERR_PATTERN, "%s: %lld groups of %d have more than %d mask bits", fn, (long long)bad, G, cap);
+    return NM_OK;
+}
+
 nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
-                  int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi,
+                  int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, unsigned flags,
                   nm_stream_t stream) {
     const char* fn = "nm_pack";
     NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ((flags & ~NM_FLAG_VALIDATE) == 0, NM_ERR_SHAPE, "%s: unknown flags 0x%x", fn, flags);
     nm_status st = check_pattern(N, M, fn);
     if (st != NM_OK) return st;
     NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
@@ -229,6 +245,8 @@ nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw
     const Range rw = span(W, R, K, ldw, esize(wdt)), rm = span(mask, R, (K + 7) / 8, ldm, 1);
     NM_REQ(!overlap(rv, rw) && !overlap(rv, rm) && !overlap(ri, rw) && !overlap(ri, rm), NM_ERR_ALIAS,
            "%s: an output overlaps an input", fn);
+    st = validate_mask(fn, flags, mask, ldm, R, K, M, N, stream);
+    if (st != NM_OK) return st;
     launch_pack(W, wdt, R, K, ldw, mask, ldm, N, M, vdt, vals, ldv, idx, ldi, (hipStream_t)stream);
     return check_launch(fn);
 }
@@ -275,8 +293,10 @@ nm_status nm_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float
 static nm_status slide_common(const char* fn, bool select, const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H,
                               int64_t ldh, float eps, nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv,
                               int64_t R, int64_t K, int Ns, const uint8_t* mask_in, uint8_t* mask_out, int64_t ldm,
-                              nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, nm_stream_t stream) {
+                              nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, unsigned flags,
+                              nm_stream_t stream) {
     NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ((flags & ~NM_FLAG_VALIDATE) == 0, NM_ERR_SHAPE, "%s: unknown flags 0x%x", fn, flags);
     NM_REQ(Ns >= 2 && Ns <= 8, NM_ERR_PATTERN, "%s: slide N must be in [2, 8] (got %d)", fn, Ns);
     NM_REQ(K % (2 * Ns) == 0, NM_ERR_SHAPE, "%s: K %% 2N != 0", fn);
     if (R * K == 0) return NM_OK;
@@ -303,6 +323,10 @@ static nm_status slide_common(const char* fn, bool select, const void* Wsc, nm_d
         NM_REQ(!overlap(rv, x) && !overlap(ri, x) && !overlap(rm, x), NM_ERR_ALIAS, "%s: an output overlaps an input",
                fn);
     NM_REQ(!overlap(rm, rv) && !overlap(rm, ri), NM_ERR_ALIAS, "%s: mask overlaps vals/idx", fn);
+    if (!select) {
+        st = validate_mask(fn, flags, mask_in, ldm, R, K, 2 * Ns, 2 * Ns - 2, stream);
+        if (st != NM_OK) return st;
+    }
     launch_slide(Wsc, sdt, ldsc, H, ldh, eps, mode, select, Wv, wdt, ldwv, R, K, Ns, mask_in, mask_out, ldm, vdt, vals,
                  ldv, idx, ldi, (hipStream_t)stream);
     return check_launch(fn);
@@ -310,9 +334,9 @@ static nm_status slide_common(const char* fn, bool select, const void* Wsc, nm_d
 
 nm_status nm_slide_decompose(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask,
                              int64_t ldm, int Ns, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi,
-                             nm_stream_t stream) {
+                             unsigned flags, nm_stream_t stream) {
     return slide_common("nm_slide_decompose", false, nullptr, NM_F32, 0, nullptr, 0, 0.f, NM_SCORE_MAGNITUDE, W, wdt,
-                        ldw, R, K, Ns, mask, nullptr, ldm, vdt, vals, ldv, idx, ldi, stream);
+                        ldw, R, K, Ns, mask, nullptr, ldm, vdt, vals, ldv, idx, ldi, flags, stream);
 }
 
 nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
@@ -320,7 +344,7 @@ nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const floa
                          uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
                          int64_t ldi, nm_stream_t stream) {
     return slide_common("nm_prune_slide", true, Wsc, sdt, ldsc, H, ldh, eps, mode, Wv, wdt, ldwv, R, K, Ns, nullptr,
-                        mask, ldm, vdt, vals, ldv, idx, ldi, stream);
+                        mask, ldm, vdt, vals, ldv, idx, ldi, 0u, stream);
 }
 
 nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
@@ -343,13 +367,14 @@ nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, in
                         void* Xq, int64_t ldq, float* x_scale, nm_stream_t stream) {
     const char* fn = "nm_quant_lift";
     NM_REQ(Mtok >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
-    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported: no lift (Ns=0) and the 6:8 lift (Ns=4)", fn);
+    NM_REQ(Ns == 0 || (Ns >= 3 && Ns <= 8), NM_ERR_PATTERN,
+           "%s: supported: no lift (Ns=0) and the (2N-2):2N lift (3 <= Ns <= 8), got Ns=%d", fn, Ns);
     NM_REQ(xdt == NM_BF16 && (qdt == NM_I8 || qdt == NM_FP8), NM_ERR_DTYPE, "%s: X must be bf16, codes I8 or FP8",
            fn);
-    NM_REQ(K % 8 == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 8", fn);
+    NM_REQ(K % 8 == 0 && (Ns == 0 || K % (2 * Ns) == 0), NM_ERR_SHAPE, "%s: K must be a multiple of 8 and of 2N", fn);
     if (Mtok == 0 || K == 0) return NM_OK;
     NM_REQ(X && Xq && x_scale, NM_ERR_NULL, "%s: NULL argument", fn);
-    const int64_t Kl = Ns ? K / 8 * 12 : K;
+    const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
     NM_REQ(ldx >= K && ldq >= Kl, NM_ERR_SHAPE, "%s: leading dimension too small", fn);
     NM_REQ(aligned16(X) && (ldx * 2) % 16 == 0 && ((uintptr_t)Xq & (Ns ? 3u : 7u)) == 0 && ldq % (Ns ? 4 : 8) == 0,
            NM_ERR_ALIGN, "%s: X needs 16-byte aligned rows, Xq 4-byte (lifted) or 8-byte aligned rows", fn);
@@ -369,17 +394,20 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
                   float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream) {
     const char* fn = "nm_spmm";
     NM_REQ(Mtok >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
-    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported patterns are plain 2:4 (Ns=0) and 6:8 via slide (Ns=4)",
-           fn);
+    NM_REQ(Ns == 0 || (Ns >= 3 && Ns <= 8), NM_ERR_PATTERN,
+           "%s: supported patterns are plain 2:4 (Ns=0) and (2N-2):2N via slide (3 <= Ns <= 8), got Ns=%d", fn, Ns);
     NM_REQ((xdt == NM_BF16 && vdt == NM_BF16 && (ydt == NM_BF16 || ydt == NM_F32)) ||
                (xdt == NM_I8 && vdt == NM_I8 && (ydt == NM_I32 || ydt == NM_F32 || ydt == NM_BF16)) ||
                (xdt == NM_FP8 && vdt == NM_FP8 && (ydt == NM_F32 || ydt == NM_BF16)),
            NM_ERR_DTYPE, "%s: supported: bf16 x bf16 -> bf16/f32, int8 x int8 -> int32/f32/bf16, fp8 x fp8 -> f32/bf16",
            fn);
-    const int64_t kmult = Ns == 0 ? (xdt == NM_BF16 ? 16 : 32) : (xdt == NM_BF16 ? 32 : 64);
-    NM_REQ(K % kmult == 0, NM_ERR_SHAPE, "%s: K must be a multiple of %lld for this dtype and pattern", fn,
-           (long long)kmult);
+    // the 2:4 product runs over the lifted width K' = (2 - 2/N) K: K' a multiple of one sparse
+    // instruction's half depth (16 bf16, 32 one-byte columns)
+    const int64_t kmult = xdt == NM_BF16 ? 16 : 32;
+    NM_REQ(Ns == 0 || K % (2 * Ns) == 0, NM_ERR_SHAPE, "%s: K must be a multiple of 2N = %d", fn, 2 * Ns);
     const int64_t Kl = Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K;
+    NM_REQ(Kl % kmult == 0, NM_ERR_SHAPE, "%s: the (lifted) width %lld must be a multiple of %lld for this dtype", fn,
+           (long long)Kl, (long long)kmult);
     if (xdt == NM_I8) NM_REQ(Kl * 127 * 127 < (1LL << 31), NM_ERR_SHAPE, "%s: int8 sum may overflow int32", fn);
     if (Mtok == 0 || R == 0) return NM_OK;
     NM_REQ(Y, NM_ERR_NULL, "%s: Y is NULL", fn);
@@ -462,12 +490,13 @@ nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, c
                           nm_stream_t stream) {
     const char* fn = "nm_spmm_lowrank";
     NM_REQ(Mtok >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
-    NM_REQ(Ns == 0 || Ns == 4, NM_ERR_PATTERN, "%s: supported patterns are plain 2:4 (Ns=0) and 6:8 via slide (Ns=4)",
-           fn);
+    NM_REQ(Ns == 0 || (Ns >= 3 && Ns <= 8), NM_ERR_PATTERN,
+           "%s: supported patterns are plain 2:4 (Ns=0) and (2N-2):2N via slide (3 <= Ns <= 8), got Ns=%d", fn, Ns);
     NM_REQ(ydt == NM_BF16 || ydt == NM_F32, NM_ERR_DTYPE, "%s: Y must be bf16 or f32", fn);
     NM_REQ(rank >= 8 && rank <= 256 && rank % 8 == 0, NM_ERR_SHAPE, "%s: rank must be a multiple of 8 in [8, 256]", fn);
-    const int64_t kmult = Ns == 0 ? 16 : 32;
-    NM_REQ(K % kmult == 0, NM_ERR_SHAPE, "%s: K must be a multiple of %lld", fn, (long long)kmult);
+    NM_REQ(K % 16 == 0 && (Ns == 0 || K % (2 * Ns) == 0), NM_ERR_SHAPE, "%s: K must be a multiple of 16 and of 2N", fn);
+    NM_REQ((Ns ? K / (2 * Ns) * 4 * (Ns - 1) : K) % 16 == 0, NM_ERR_SHAPE,
+           "%s: the lifted width must be a multiple of 16", fn);
     if (Mtok == 0 || R == 0) return NM_OK;
     NM_REQ(K > 0, NM_ERR_SHAPE, "%s: K == 0", fn);
     NM_REQ(X && vals && idx && A && B && Y, NM_ERR_NULL, "%s: NULL argument", fn);

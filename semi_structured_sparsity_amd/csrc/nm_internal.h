@@ -103,6 +103,10 @@ void launch_mask(const float* S, int64_t R, int64_t K, int64_t lds, int N, int M
                  hipStream_t s);
 void launch_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const uint8_t* mask, int64_t ldm,
                  int N, int M, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, hipStream_t s);
+// Groups of G consecutive bits of a caller's mask with more than cap set bits, counted on
+// the device; synchronises the stream (NM_FLAG_VALIDATE).
+nm_status count_overfull(const uint8_t* mask, int64_t ldm, int64_t R, int64_t K, int G, int cap, hipStream_t s,
+                         int64_t* bad);
 void launch_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
                        nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N,
                        int M, uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,
@@ -118,8 +122,8 @@ void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* sta
 void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
                     hipStream_t s);
 void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
-                 float rho, int steps, float* m_final, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
-                 void* ws, hipStream_t s);
+                 float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
+                 double* lmid, void* ws, hipStream_t s);
 // sparse GEMM
 void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt, void* Xq,
                        int64_t ldq, float* x_scale, hipStream_t s);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol(nm):
     for s in syms:
         assert hasattr(nm.raw, s), f"libnmsparse.so does not export {s}"
         assert s in nm.SIGNATURES, f"binding has no signature for {s}"
-    assert nm.nm_abi_version() == 1
+    assert nm.nm_abi_version() == 2
 
 
 def test_binding_functions_have_c_names(nm):
@@ -55,11 +55,20 @@ def test_validation_errors_without_gpu(nm):
     # NULL pointers
     assert _st(nm, r.nm_mask(None, 4, 8, 8, 2, 4, S, 1, None)) == "NM_ERR_NULL"
     # slide N out of range and K not a multiple of 2N
-    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 16, 16, S, 2, 9, 1, S, 8, S, 1, None)) == "NM_ERR_PATTERN"
-    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 12, 12, S, 2, 4, 1, S, 8, S, 1, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 16, 16, S, 2, 9, 1, S, 8, S, 1, 0, None)) == "NM_ERR_PATTERN"
+    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 12, 12, S, 2, 4, 1, S, 8, S, 1, 0, None)) == "NM_ERR_SHAPE"
+    # flags other than NM_FLAG_VALIDATE are rejected before anything runs
+    assert _st(nm, r.nm_slide_decompose(S, 1, 4, 16, 16, S, 2, 4, 1, S, 12, S, 1, 2, None)) == "NM_ERR_SHAPE"
+    assert "unknown flags" in nm.last_error()
     # sparse GEMM: unsupported slide N, bad dtype pairing, K multiple, int32 overflow bound
     Y = ctypes.c_void_p(0x100000)
-    assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, S, 1, S, 8, 32, 4, 3, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_PATTERN"
+    for bad_ns in (1, 2, 9):
+        assert _st(nm, r.nm_spmm(S, 1, 4, 72, 72, S, 1, S, 8, 36, 4, bad_ns, None, 1.0, Y, 1, 8, None, 0,
+                                 None)) == "NM_ERR_PATTERN"
+    # (2N-2):2N for N = 3: K a multiple of 6, lifted width 4K/3 a multiple of 16 (bf16) / 32 (int8)
+    assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, S, 1, S, 8, 64, 4, 3, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_spmm(S, 1, 4, 18, 24, S, 1, S, 8, 16, 4, 3, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_spmm(S, 2, 4, 36, 48, S, 2, S, 8, 24, 4, 3, None, 1.0, Y, 3, 8, None, 0, None)) == "NM_ERR_SHAPE"
     assert _st(nm, r.nm_spmm(S, 1, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_DTYPE"
     assert _st(nm, r.nm_spmm(S, 2, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 2, 8, None, 0, None)) == "NM_ERR_DTYPE"
     assert _st(nm, r.nm_spmm(S, 1, 4, 40, 40, S, 1, S, 8, 20, 4, 0, None, 1.0, Y, 1, 8, None, 0, None)) == "NM_ERR_SHAPE"
@@ -76,12 +85,19 @@ def test_validation_errors_without_gpu(nm):
     # workspace missing
     assert _st(nm, r.nm_score_stats(S, 4, 8, 8, Y, None, 0, None)) == "NM_ERR_WORKSPACE"
     # gate: steps out of range, T0 not positive
-    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, 0.5, 0.5, 0, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
-    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, -1.0, 0.5, 8, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, 0.5, 0.5, 0, 0, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
+    assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, -1.0, 0.5, 8, 7, S, 8, Y, 1, S, S, 1 << 20, None)) == "NM_ERR_SHAPE"
+    # the step whose blend is written must be one of the steps
+    M_ = ctypes.c_void_p(0x200000)
+    for bad_t in (-1, 8):
+        assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, 0.5, 0.5, 8, bad_t, M_, 8, Y, 1, S, S, 1 << 20,
+                                 None)) == "NM_ERR_SHAPE"
+        assert "m_step" in nm.last_error()
     # Hutchinson alignment rules
     assert _st(nm, r.nm_hdiag_hutchinson(S, 64, 100, 100, 8, 2, 1, Y, 100, S, 1 << 30, None)) == "NM_ERR_ALIGN"
     # pack dtype rule (bf16 weights cannot pack to int8)
-    assert _st(nm, r.nm_pack(S, 1, 4, 8, 8, S, 1, 2, 4, 2, Y, 4, S, 1, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_pack(S, 1, 4, 8, 8, S, 1, 2, 4, 2, Y, 4, S, 1, 0, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_pack(S, 1, 4, 8, 8, S, 1, 2, 4, 1, Y, 4, S, 1, 0x10, None)) == "NM_ERR_SHAPE"
     # FP8: only FP8 x FP8 -> f32/bf16 products, one-byte K multiples, codes from bf16 only, no FP8 absmean
     F8 = nm.NM_FP8
     assert _st(nm, r.nm_spmm(S, F8, 4, 64, 64, S, 2, S, 8, 32, 4, 0, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_DTYPE"
@@ -89,6 +105,8 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, r.nm_spmm(S, F8, 4, 48, 48, S, F8, S, 8, 24, 4, 0, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_SHAPE"
     assert _st(nm, r.nm_spmm(S, F8, 4, 96, 96, S, F8, S, 8, 72, 8, 4, None, 1.0, Y, 0, 8, None, 0, None)) == "NM_ERR_SHAPE"
     assert _st(nm, r.nm_quant_lift(S, 1, 4, 64, 64, 4, 0, Y, 96, S, None)) == "NM_ERR_DTYPE"
+    assert _st(nm, r.nm_quant_lift(S, 1, 4, 64, 64, 2, 2, Y, 96, S, None)) == "NM_ERR_PATTERN"
+    assert _st(nm, r.nm_quant_lift(S, 1, 4, 64, 64, 3, 2, Y, 96, S, None)) == "NM_ERR_SHAPE"   # 64 % 6
     assert _st(nm, r.nm_quant_lift(S, F8, 4, 64, 64, 4, F8, Y, 96, S, None)) == "NM_ERR_DTYPE"
     assert _st(nm, r.nm_absmean(S, F8, 4, 8, 8, Y, S, 1 << 20, None)) == "NM_ERR_DTYPE"
     # sparse + low-rank: rank a multiple of 8 in [8, 256], bf16/f32 output, aligned A and B, enough workspace
@@ -115,4 +133,17 @@ def test_empty_inputs_are_noops(nm):
     r = nm.raw
     assert r.nm_mask(None, 0, 8, 8, 2, 4, None, 1, None) == 0
     assert r.nm_spmm(None, 1, 0, 64, 64, None, 1, None, 8, 32, 4, 0, None, 1.0, None, 1, 8, None, 0, None) == 0
-    assert r.nm_pack(None, 1, 0, 8, 8, None, 1, 2, 4, 1, None, 4, None, 1, None) == 0
+    assert r.nm_pack(None, 1, 0, 8, 8, None, 1, 2, 4, 1, None, 4, None, 1, 0, None) == 0
+
+
+def test_spmm_workspace_covers_every_plan(nm):
+    """The workspace query does not know the index pointer or ldi, which decide whether the
+    DMA ring kernels may run; it must cover the fallback plan too.  One token on the
+    11008 x 4096 layer: the ring plan needs no workspace, the fallback (an index view
+    that is only 4-byte aligned) splits K over two blocks and needs their f32 partials."""
+    r = nm.raw
+    need = r.nm_spmm_workspace(1, 4096, 11008, 0, nm.NM_BF16)
+    assert need >= 2 * 1 * 11008 * 4
+    # every plan of the lifted product includes the lifted activation
+    assert r.nm_spmm_workspace(16, 4096, 14336, 4, nm.NM_BF16) >= 16 * 6144 * 2
+    assert r.nm_spmm_workspace(16, 3072, 1024, 3, nm.NM_I8) >= 16 * 4096

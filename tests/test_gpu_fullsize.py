@@ -166,12 +166,23 @@ def test_hessian24_full_size(nm):
     assert abs(st[0] - mu) <= 1e-12 * abs(mu) and abs(st[1] - sg) <= 1e-12 * sg
     del Sh
     stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
-    _, hm, _ = nm.nm_gate(S, stats, 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS,
-                          want_m=False)
-    _, h_ref, _ = O.gate_anneal(Sr, mu, sg, 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS)
+    T0, rho, steps = synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS
+    # the hard mask in the benchmark's configuration (no blend written), then the blend of an
+    # early step element by element on the sampled rows and every step's L_mid over the
+    # whole tensor (the oracle runs the full tensor once, rows in parallel)
+    _, hm, lm_fast = nm.nm_gate(S, stats, 2, 4, T0, rho, steps, want_m=False)
+    t_mid = 2
+    m_mid, hm2, lm = nm.nm_gate(S, stats, 2, 4, T0, rho, steps, m_step=t_mid)
+    assert torch.equal(hm, hm2) and torch.equal(lm, lm_fast)
+    m_full, h_full, l_ref = O.gate_anneal(S.cpu().numpy(), mu, sg, 2, 4, T0, rho, steps, m_step=t_mid)
+    h_ref = h_full[rows]
     hmh = hm.cpu().numpy()
     assert np.array_equal(hmh[rows], h_ref)
-    del S
+    rows_d = torch.from_numpy(rows).to(dev())
+    assert np.abs(m_mid[rows_d].cpu().numpy() - m_full[rows]).max() <= 1e-5
+    assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5)
+    assert lm.cpu().numpy()[-1] == 0.0
+    del S, m_mid, m_full, h_full
     # the annealed hard mask is 2:4: pack it and multiply at M = 8192
     vals, idx = nm.nm_pack(Wd, hm, 2, 4)
     v_ref, i_ref = O.pack(Wr, h_ref, 2, 4)

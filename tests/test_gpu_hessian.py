@@ -75,6 +75,28 @@ def test_hutchinson_unaligned_workspace_uses_tile_kernel(nm):
     assert np.array_equal(D_tile[rows].astype(np.float64), O.hutchinson_rows(Xb, P, seed, rows))
 
 
+def test_hutchinson_long_rows_use_register_generating_kernel(nm):
+    """A row stride past 2^23 elements puts the DMA offsets of a 256-row block beyond 32
+    bits, so the first product runs on the tile kernel that generates the probe signs in
+    registers.  Integer inputs (|x| <= 1, K = 128) keep V X^T exact in bf16 and every later
+    sum an exact integer, and 4 probes make the 2/P scale exact: the result equals the
+    packed-stride run and the oracle exactly."""
+    n, K, R, P = 64, 128, 130, 4
+    ldx = (1 << 23) + 64
+    g = np.random.default_rng(6)
+    Xb = O.f32_to_bf16(g.integers(-1, 2, (n, K)).astype(np.float32))
+    seed = 5
+    D_ref = nm.nm_hdiag_hutchinson(np_bf16(Xb).to(dev()), R, P, seed).cpu().numpy()
+    big = torch.empty((n, ldx), dtype=torch.bfloat16, device=dev())   # about 1 GiB
+    big[:, :K] = np_bf16(Xb).to(dev())
+    assert (256 * ldx + K) * 2 >= 1 << 32
+    D = nm.nm_hdiag_hutchinson(big[:, :K], R, P, seed).cpu().numpy()
+    del big
+    assert np.array_equal(D, D_ref)
+    rows = np.unique(np.r_[0, R - 1, g.integers(0, R, 12)])
+    assert np.array_equal(D[rows].astype(np.float64), O.hutchinson_rows(Xb, P, seed, rows))
+
+
 def test_stats_and_gate(nm):
     g = np.random.default_rng(8)
     R, K, steps = 96, 512, 8
@@ -85,13 +107,41 @@ def test_stats_and_gate(nm):
     assert abs(st[0] - mu) <= 1e-12 * abs(mu) and abs(st[1] - sg) <= 1e-12 * sg
     # the gate is fed the oracle's statistics: one stage at a time
     stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
-    mf, hm, lm = nm.nm_gate(Sd, stats, 2, 4, 0.5, 0.5, steps)
-    m_ref, h_ref, l_ref = O.gate_anneal(S, mu, sg, 2, 4, 0.5, 0.5, steps)
-    assert np.array_equal(hm.cpu().numpy(), h_ref)
-    assert np.abs(mf.cpu().numpy() - m_ref).max() <= 1e-5
-    lm = lm.cpu().numpy()
-    assert np.allclose(lm, l_ref, rtol=1e-5, atol=1e-9)
-    assert lm[-1] == 0.0
+    for t in range(steps):
+        # m_t element by element at every step: the sigmoid of z / T_t blended toward h
+        mt, hm, lm = nm.nm_gate(Sd, stats, 2, 4, 0.5, 0.5, steps, m_step=t)
+        m_ref, h_ref, l_ref = O.gate_anneal(S, mu, sg, 2, 4, 0.5, 0.5, steps, m_step=t)
+        assert np.abs(mt.cpu().numpy() - m_ref).max() <= 1e-5, f"step {t}"
+        assert np.array_equal(hm.cpu().numpy(), h_ref)
+        lm = lm.cpu().numpy()
+        assert np.allclose(lm, l_ref, rtol=1e-5, atol=1e-9)
+        assert lm[-1] == 0.0
+    # the early steps are far from binary: the comparison above sees the sigmoid itself
+    m0, _, _ = O.gate_anneal(S, mu, sg, 2, 4, 0.5, 0.5, steps, m_step=0)
+    assert ((m0 > 0.05) & (m0 < 0.95)).mean() > 0.3
+
+
+@pytest.mark.parametrize("T0,rho,steps", [(0.5, 0.5, 8), (0.8, 0.6, 5), (2.0, 0.25, 4)])
+def test_gate_two_valued_closed_form(nm, T0, rho, steps):
+    """Scores 1 and 3, two of each per group: z = +-1 exactly, so at step t every kept
+    entry is (1-b) expit(1/T_t) + b and every dropped one (1-b) expit(-1/T_t)."""
+    from scipy.special import expit
+    g = np.random.default_rng(17)
+    R, K = 40, 256
+    S = np.empty((R, K), np.float32)
+    for r in range(R):
+        for q in range(K // 4):
+            S[r, 4 * q:4 * q + 4] = g.permutation([3.0, 1.0, 3.0, 1.0])
+    Sd = torch.from_numpy(S).to(dev())
+    assert np.allclose(nm.nm_score_stats(Sd).cpu().numpy(), [2.0, 1.0], rtol=1e-14)
+    stats = torch.tensor([2.0, 1.0], dtype=torch.float64, device=dev())
+    keep = S == 3.0
+    for t in range(steps):
+        T, b = T0 * rho ** t, t / (steps - 1)
+        mt, hm, lm = nm.nm_gate(Sd, stats, 2, 4, T0, rho, steps, m_step=t)
+        want = np.where(keep, (1 - b) * expit(1.0 / T) + b, (1 - b) * expit(-1.0 / T))
+        assert np.abs(mt.cpu().numpy() - want).max() <= 1e-6
+        assert np.array_equal(O.mask_to_bool(hm.cpu().numpy(), K), keep)
 
 
 def test_gate_68_and_constant_scores(nm):
@@ -100,8 +150,26 @@ def test_gate_68_and_constant_scores(nm):
     Sd = torch.from_numpy(S).to(dev())
     st = nm.nm_score_stats(Sd)
     assert float(st[1].cpu()) == 0.0
-    mf, hm, lm = nm.nm_gate(Sd, st, 6, 8, 0.5, 0.5, 8)
-    m_ref, h_ref, l_ref = O.gate_anneal(S, 0.25, 0.0, 6, 8, 0.5, 0.5, 8)
-    assert np.array_equal(hm.cpu().numpy(), h_ref)
-    assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5)
-    assert np.array_equal(mf.cpu().numpy(), m_ref)
+    for t in (0, 3, 7):
+        mf, hm, lm = nm.nm_gate(Sd, st, 6, 8, 0.5, 0.5, 8, m_step=t)
+        m_ref, h_ref, l_ref = O.gate_anneal(S, 0.25, 0.0, 6, 8, 0.5, 0.5, 8, m_step=t)
+        assert np.array_equal(hm.cpu().numpy(), h_ref)
+        assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5)
+        # z = 0: m = (1 - beta) / 2 + beta h, one f32 rounding per operation on the GPU
+        assert np.abs(mf.cpu().numpy() - m_ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("N,M,K", [(6, 8, 200), (2, 4, 204)])   # K = 204: a last half-filled mask byte
+def test_gate_random_every_step(nm, N, M, K):
+    g = np.random.default_rng(18 + K)
+    R, steps = 33, 6
+    S = g.standard_normal((R, K)).astype(np.float32)
+    Sd = torch.from_numpy(S).to(dev())
+    mu, sg = O.stats(S)
+    stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
+    for t in range(steps):
+        mt, hm, lm = nm.nm_gate(Sd, stats, N, M, 0.7, 0.5, steps, m_step=t)
+        m_ref, h_ref, l_ref = O.gate_anneal(S, mu, sg, N, M, 0.7, 0.5, steps, m_step=t)
+        assert np.abs(mt.cpu().numpy() - m_ref).max() <= 1e-5
+        assert np.array_equal(hm.cpu().numpy(), h_ref)
+        assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)

@@ -45,7 +45,7 @@ def _case(g, Mt, R, K, Ns, rank, integer=True):
         B = O.f32_to_bf16((g.standard_normal((R, rank)) * 0.02).astype(np.float32))
     S = O.score(W, None, 0.0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32) * (1e-3 if integer else 1e-9)
     if Ns:
-        mask = O.topn_mask(S, 6, 8)
+        mask = O.topn_mask(S, 2 * Ns - 2, 2 * Ns)
         vals, idx, bad = O.slide_decompose(W, mask, Ns)
         assert bad == 0
     else:
@@ -93,7 +93,8 @@ def test_spmm_lowrank_big_tiles_integer_exact_sampled(nm, Mt, R, K, rank, Ns):
     assert np.array_equal(Y[tm, ro].astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("Mt,R,K,rank,Ns", [(8, 300, 1024, 64, 0), (333, 520, 2048, 32, 0), (700, 256, 1024, 48, 4)])
+@pytest.mark.parametrize("Mt,R,K,rank,Ns", [(8, 300, 1024, 64, 0), (333, 520, 2048, 32, 0), (700, 256, 1024, 48, 4),
+                                            (40, 200, 768, 16, 3), (300, 260, 640, 32, 5)])
 def test_spmm_lowrank_random_tolerance(nm, Mt, R, K, rank, Ns):
     g = np.random.default_rng(Mt + 7 * R + K + rank)
     X, W, A, B, mask, vals, idx = _case(g, Mt, R, K, Ns, rank, integer=False)
@@ -105,6 +106,15 @@ def test_spmm_lowrank_random_tolerance(nm, Mt, R, K, rank, Ns):
     ub = np.abs(u) @ np.abs(O.bf16_to_f32(B).astype(np.float64)).T
     tol = 2e-2 * xn[:, None] * wn[None, :] + 2.0 ** -6 * ub
     assert (np.abs(Y - ref) <= tol).all()
+
+
+@pytest.mark.parametrize("Mt,R,K,rank,Ns", [(3, 130, 384, 16, 3), (300, 200, 768, 32, 3), (64, 96, 640, 8, 5)])
+def test_spmm_lowrank_general_slide_integer_exact(nm, Mt, R, K, rank, Ns):
+    g = np.random.default_rng(Mt + R + K + rank + 13 * Ns)
+    X, W, A, B, mask, vals, idx = _case(g, Mt, R, K, Ns, rank)
+    ref = O.sparse_lowrank(X, W, mask, A, B)
+    Y = _run(nm, X, vals, idx, A, B, R, Ns, nm.NM_F32).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64), ref)
 
 
 def test_spmm_lowrank_zero_adapter_equals_spmm(nm):

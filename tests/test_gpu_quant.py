@@ -31,12 +31,26 @@ def _x(g, Mt, K):
 @pytest.mark.parametrize("Mt,K", [(1, 64), (5, 8), (37, 2560), (300, 4096), (2, 4104)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_quant_lift_bit_exact(nm, Mt, K, Ns):
+    _quant_case(nm, Mt, K, Ns)
+
+
+# other (2N-2):2N lifts: K a multiple of 8 and of 2N
+@pytest.mark.parametrize("Ns,Mt,K", [(3, 1, 48), (3, 37, 2568), (5, 9, 640), (5, 300, 4000), (6, 4, 1152),
+                                     (7, 3, 56), (8, 65, 4096)])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_quant_lift_general_n_bit_exact(nm, Ns, Mt, K, fp8):
+    _quant_case(nm, Mt, K, Ns, fp8)
+
+
+def _quant_case(nm, Mt, K, Ns, fp8=False):
     g = np.random.default_rng(Mt * 31 + K + Ns)
     X = _x(g, Mt, K)
-    Xq, sx = nm.nm_quant_lift(torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev()), Ns)
-    q_ref, s_ref = O.quant_lift(X, Ns)
+    Xq, sx = nm.nm_quant_lift(torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev()), Ns,
+                              nm.NM_FP8 if fp8 else nm.NM_I8)
+    q_ref, s_ref = O.quant_lift(X, Ns, fp8=fp8)
     assert np.array_equal(sx.cpu().numpy(), s_ref)
-    assert np.array_equal(Xq.cpu().numpy(), q_ref)
+    got = Xq.cpu().view(torch.uint8).numpy() if fp8 else Xq.cpu().numpy()
+    assert np.array_equal(got, q_ref)
 
 
 def test_quant_lift_strided_input(nm):

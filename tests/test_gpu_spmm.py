@@ -27,7 +27,7 @@ def _int_bf16(g, shape, lim):
 
 
 def _pack_case(W_host, Ns, N=2, M=4, score=None):
-    """Oracle mask + oracle packing (plain 2:4 or lifted slide)."""
+    """Oracle mask + oracle packing (plain 2:4 or lifted slide of (2Ns-2):2Ns)."""
     K = W_host.shape[1]
     S = score if score is not None else O.score(W_host, None, 0.0, O.SCORE_MAGNITUDE)
     if Ns:
@@ -171,6 +171,79 @@ def test_spmm_int8_exact(nm, Mt, R, K, Ns):
     acc_ref, y_ref = O.masked_matmul_i8(Xq, Wt.numpy(), mask, sx, float(alpha))
     assert np.array_equal(acc, acc_ref)
     assert np.array_equal(y, y_ref)
+
+
+# (2N-2):2N for other N: (tokens, rows, K) with K a multiple of 2N and the lifted width a
+# multiple of 16 (bf16); few-token (K-split ring, or the weight-streaming kernel when the
+# lifted width is off the ring's stage grid), many-token ring and register-staged shapes
+GENERAL_NS = [(3, 1, 300, 384), (3, 40, 130, 96), (3, 300, 200, 768), (3, 2100, 600, 384),
+              (5, 1, 257, 640), (5, 64, 300, 320), (5, 520, 260, 1280),
+              (6, 16, 100, 384), (6, 300, 130, 768),
+              (7, 3, 90, 224), (7, 260, 300, 448),
+              (8, 1, 64, 512), (8, 129, 200, 256)]
+
+
+@pytest.mark.parametrize("Ns,Mt,R,K", GENERAL_NS)
+def test_spmm_general_slide_bf16_integer_exact(nm, Ns, Mt, R, K):
+    """The lifted product of any (2N-2):2N weight (N-1 overlapping 2:4 windows per 2N
+    group, activation lifted to (2 - 2/N) K) equals the oracle's masked product of the
+    unlifted activation bit for bit on integer-valued inputs."""
+    assert O.lifted_width(K, Ns) % 16 == 0
+    g = np.random.default_rng(Ns * 1000 + Mt + R + K)
+    X = _int_bf16(g, (Mt, K), 2)
+    W = _int_bf16(g, (R, K), 2)
+    mask, vals, idx = _pack_case(W, Ns, score=O.score(W, None, 0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32))
+    v, i = _to_dev(vals, idx)
+    Y = nm.nm_spmm(np_bf16(X).to(dev()), v, i, R=R, Ns=Ns, ydt=nm.NM_F32).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64), O.masked_matmul(X, W, mask))
+
+
+@pytest.mark.parametrize("Ns,Mt,R,K", [(3, 1, 70, 384), (3, 256, 130, 768), (3, 300, 64, 384),
+                                       (5, 33, 96, 640), (5, 2048, 300, 640), (6, 5, 64, 1152)])
+def test_spmm_general_slide_int8_exact(nm, Ns, Mt, R, K):
+    """int8 x ternary under a (2N-2):2N mask from the latent weights, lifted: exact int32."""
+    g = np.random.default_rng(Ns * 100 + Mt + R + K)
+    Wf, Wt = synth.ternary68_weights(R=R, K=K)
+    Xq = g.integers(-127, 128, (Mt, K)).astype(np.int8)
+    sx = g.uniform(0.5, 2.0, Mt).astype(np.float32) / 127
+    mask = O.topn_mask(O.score(host(Wf), None, 0.0, O.SCORE_MAGNITUDE), 2 * Ns - 2, 2 * Ns)
+    vals, idx, bad = O.slide_decompose(Wt.numpy(), mask, Ns)
+    assert bad == 0
+    v, i = _to_dev(vals, idx)
+    Xd = torch.from_numpy(Xq).to(dev())
+    acc = nm.nm_spmm(Xd, v, i, R=R, Ns=Ns, ydt=nm.NM_I32).cpu().numpy()
+    y = nm.nm_spmm(Xd, v, i, R=R, Ns=Ns, x_scale=torch.from_numpy(sx).to(dev()), w_scale=0.75,
+                   ydt=nm.NM_F32).cpu().numpy()
+    acc_ref, y_ref = O.masked_matmul_i8(Xq, Wt.numpy(), mask, sx, 0.75)
+    assert np.array_equal(acc, acc_ref)
+    assert np.array_equal(y, y_ref)
+
+
+def test_spmm_workspace_query_covers_fallback_plan(nm):
+    """An index view 4 bytes off 16-byte alignment with an odd row stride keeps the product
+    off the DMA ring kernels; at one token on 11008 x 4096 the fallback splits K over two
+    blocks.  The workspace from the query (which cannot see the pointer) must suffice, and
+    the product must still equal the oracle exactly."""
+    g = np.random.default_rng(21)
+    Mt, R, K = 1, 11008, 4096
+    X = _int_bf16(g, (Mt, K), 2)
+    W = _int_bf16(g, (R, K), 2)
+    mask, vals, idx = _pack_case(W, 0, score=O.score(W, None, 0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32))
+    words = K // 32
+    ibig = torch.zeros((R, words + 1), dtype=torch.int32)
+    ibig[:, 1:] = torch.from_numpy(idx.view(np.int32))
+    idd = ibig.to(dev())[:, 1:]                       # base + 4 bytes, ldi = 129
+    assert idd.data_ptr() % 16 == 4 and idd.stride(0) == words + 1
+    v = np_bf16(vals).to(dev())
+    Xd = np_bf16(X).to(dev())
+    need = nm.raw.nm_spmm_workspace(Mt, K, R, 0, nm.NM_BF16)
+    assert need >= 2 * Mt * R * 4
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    Y = nm.nm_spmm(Xd, v, idd, R=R, ydt=nm.NM_F32, ws=ws).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64), O.masked_matmul(X, W, mask))
+    # the aligned index rows (ring plan) give the same product
+    Y2 = nm.nm_spmm(Xd, v, torch.from_numpy(idx.view(np.int32)).to(dev()), R=R, ydt=nm.NM_F32, ws=ws).cpu().numpy()
+    assert np.array_equal(Y, Y2)
 
 
 def test_spmm_strided_views(nm):

@@ -227,6 +227,29 @@ def test_slide_overfull_group_is_reported():
     assert bad == 2
 
 
+@pytest.mark.parametrize("G,cap", [(4, 2), (8, 6), (8, 4), (6, 4), (10, 8), (14, 12), (16, 14)])
+def test_mask_overfull_counts_groups(G, cap):
+    """The pattern check counts groups of G consecutive bits with more than cap set:
+    against numpy's own bit unpacking and a per-group popcount, on random masks of a
+    density that leaves some groups over and some under (and a ragged last byte)."""
+    g = _rng(80 + G + cap)
+    R, K = 9, G * 13
+    p = (cap + 0.7) / G   # groups hover around the cap
+    bits = g.random((R, K)) < p
+    mask = np.zeros((R, (K + 7) // 8 + 3), np.uint8)   # row stride beyond ceil(K/8)
+    packed = np.packbits(bits, axis=1, bitorder="little")
+    mask[:, :packed.shape[1]] = packed
+    want = int((bits.reshape(R, K // G, G).sum(-1) > cap).sum())
+    assert 0 < want < R * K // G
+    assert O.mask_overfull(mask, K, G, cap) == want
+    # bits past K in the row's last byte and beyond never count
+    mask[:, (K // 8):] |= np.uint8(0xFF) << np.uint8(K % 8) if K % 8 else 0
+    mask[:, (K + 7) // 8:] = 0xFF
+    assert O.mask_overfull(mask, K, G, cap) == want
+    assert O.mask_overfull(O.bool_to_mask(np.ones((2, K), bool)), K, G, cap) == 2 * (K // G)
+    assert O.mask_overfull(O.bool_to_mask(np.zeros((2, K), bool)), K, G, cap) == 0
+
+
 @pytest.mark.parametrize("Ns", [3, 4])
 def test_lifted_product_equals_dense_masked(Ns):
     g = _rng(30 + Ns)
@@ -525,6 +548,61 @@ def test_anneal_projection_invariants():
         gt = np.array([[O.gate_value(float(S[r, k]), mu, sg, 0.5, 0.5, t) for k in range(K)] for r in range(R)])
         mt = ((1 - beta) * gt + beta * hb).astype(np.float32)
         assert np.array_equal(O.topn_mask(mt, 2, 4), h)
+
+
+def _two_valued_scores(R, K, g):
+    """Scores 1 and 3, two of each in every group of 4 (positions shuffled per group):
+    mean 2 and population standard deviation 1 exactly, so z = +-1 exactly and the
+    hard target keeps the 3s."""
+    S = np.empty((R, K), np.float32)
+    for r in range(R):
+        for q in range(K // 4):
+            S[r, 4 * q:4 * q + 4] = g.permutation([3.0, 1.0, 3.0, 1.0])
+    return S
+
+
+@pytest.mark.parametrize("T0,rho,temps", [
+    # T_t = T0 rho^t written out by hand for each schedule
+    (0.5, 0.5, [0.5, 0.25, 0.125, 0.0625, 0.03125, 0.015625, 0.0078125, 0.00390625]),
+    (0.8, 0.6, [0.8, 0.48, 0.288, 0.1728, 0.10368]),
+    (2.0, 0.25, [2.0, 0.5, 0.125, 0.03125]),
+])
+def test_gate_schedule_closed_form(T0, rho, temps):
+    """Two-valued scores with z = +-1 exactly: at step t the gate of a kept score is
+    expit(1/T_t) and of a dropped one expit(-1/T_t) (scipy's logistic function, not the
+    oracle's), beta_t = t/(S-1), so m_t and Lmid_t follow by hand for every step.  This
+    fixes the temperature's place (z/T, not z*T), the geometric schedule's exponent (t,
+    not t+1), the direction of the blend and the per-element output of any step."""
+    from scipy.special import expit
+    g = _rng(72)
+    R, K, steps = 6, 32, len(temps)
+    S = _two_valued_scores(R, K, g)
+    mu, sg = O.stats(S)
+    assert (mu, sg) == (2.0, 1.0)
+    keep = S == 3.0
+    n = R * K
+    for t, T in enumerate(temps):
+        beta = t / (steps - 1)
+        m_keep = (1 - beta) * expit(1.0 / T) + beta
+        m_drop = (1 - beta) * expit(-1.0 / T)
+        m, hard, lm = O.gate_anneal(S, mu, sg, 2, 4, T0, rho, steps, m_step=t)
+        want = np.where(keep, m_keep, m_drop).astype(np.float32)
+        assert np.array_equal(m, want), f"step {t}"
+        assert lm[t] == pytest.approx(n / 2 * (m_keep * (1 - m_keep) + m_drop * (1 - m_drop)), rel=1e-13)
+        assert np.array_equal(O.mask_to_bool(hard, K), keep)   # projection keeps the 3s
+        assert O.gate_value(3.0, mu, sg, T0, rho, t) == pytest.approx(expit(1.0 / T), rel=1e-14)
+        assert O.gate_value(1.0, mu, sg, T0, rho, t) == pytest.approx(expit(-1.0 / T), rel=1e-14, abs=1e-300)
+
+
+def test_gate_m_step_last_is_hard_target_and_default():
+    """m_step = S-1 (the default) gives m_{S-1} = h; an earlier step is strictly between."""
+    g = _rng(73)
+    S = _two_valued_scores(4, 16, g)
+    m_last, hard, _ = O.gate_anneal(S, 2.0, 1.0, 2, 4, 0.5, 0.5, 8)
+    m7, _, _ = O.gate_anneal(S, 2.0, 1.0, 2, 4, 0.5, 0.5, 8, m_step=7)
+    assert np.array_equal(m_last, m7) and np.array_equal(m_last, (S == 3.0).astype(np.float32))
+    m0, _, _ = O.gate_anneal(S, 2.0, 1.0, 2, 4, 0.5, 0.5, 8, m_step=0)
+    assert ((m0 > 0) & (m0 < 1)).all()
 
 
 # ------------------------------------------------------------------ sparse + low-rank linear (SALR 2-3)
