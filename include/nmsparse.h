@@ -273,6 +273,28 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
                   int Ns, const float* x_scale, float w_scale, void* Y, nm_dtype ydt, int64_t ldy,
                   void* ws, size_t ws_bytes, nm_stream_t stream);
 
+/* ---------------------------------------------------------------- no-allocation variant
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  nm_spmm with the
+ * same arguments minus the workspace; the workspace the call needs (the split-K
+ * partials and the lifted activation, nm_spmm_workspace(...) bytes) comes from a
+ * library-owned static device buffer of NM_SPMM_SCRATCH_BYTES per GPU, which each GPU
+ * the library runs on holds until the process ends.
+ *  - A call needing more than NM_SPMM_SCRATCH_BYTES returns NM_ERR_WORKSPACE before
+ *    anything is enqueued (use nm_spmm with a workspace then).
+ *  - Every call on a GPU shares that GPU's buffer: calls that overlap on one GPU (on
+ *    different streams, or from different host threads without ordering) race on it
+ *    and must be serialised by the caller.  Nothing in it needs to start at zero.
+ *  - stream must belong to the current device (NM_ERR_DEVICE otherwise).  The first
+ *    call on a device looks up the buffer's address on it; no call allocates, frees or
+ *    synchronises.
+ * Results are bit-identical to nm_spmm's for the same arguments. */
+#define NM_SPMM_SCRATCH_BYTES ((size_t)64 << 20)
+nm_status nm_spmm_noalloc(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,
+                          const void* vals, nm_dtype vdt, const uint32_t* idx, int64_t R, int64_t ldv,
+                          int64_t ldi, int Ns, const float* x_scale, float w_scale, void* Y, nm_dtype ydt,
+                          int64_t ldy, nm_stream_t stream);
+
 /* Sparse layer with stacked low-rank adapters ("SALR", section 3: every adapter of a
  * layer, the fine-tuning one and the truncated-SVD adapter of the pruning residual of
  * section 2, is stacked along the rank so that one product serves them all):

@@ -71,6 +71,7 @@ SIGNATURES = {
     "nm_quant_lift": (_I, [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _P]),
     "nm_spmm_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_spmm": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P, _SZ, _P]),
+    "nm_spmm_noalloc": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _P, _I64, _I64, _I64, _I, _P, _F, _P, _I, _I64, _P]),
     "nm_spmm_lowrank_workspace": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "nm_bitmap_encode": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "nm_spmm_bitmap_workspace": (_SZ, [_I64, _I64, _I64]),
@@ -321,4 +322,23 @@ def nm_spmm(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, R: int | Non
     _check(raw.nm_spmm(_ptr(X), xdt, Mtok, K, _ld(X), _ptr(vals), dtype_code(vals), _ptr(idx), R, _ld(vals), _ld(idx),
                        Ns, _ptr(x_scale), w_scale, _ptr(Y), ydt, _ld(Y), _ptr(ws), 0 if ws is None else ws.numel(),
                        _stream(X)))
+    return Y
+
+
+NM_SPMM_SCRATCH_BYTES = 64 << 20
+
+
+def nm_spmm_noalloc(X: torch.Tensor, vals: torch.Tensor, idx: torch.Tensor, R: int | None = None, Ns: int = 0,
+                    x_scale: torch.Tensor | None = None, w_scale: float = 1.0, ydt: int | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """nm_spmm with the library's own per-device scratch buffer instead of a workspace (for
+    callers that cannot allocate); give `out` to allocate nothing here either."""
+    Mtok, K = X.shape
+    R = vals.shape[0] if R is None else R
+    xdt = dtype_code(X)
+    if ydt is None:
+        ydt = {NM_BF16: NM_BF16, NM_I8: NM_I32, NM_FP8: NM_F32}[xdt]
+    Y = out if out is not None else torch.empty((Mtok, R), dtype=_TORCH[ydt], device=X.device)
+    _check(raw.nm_spmm_noalloc(_ptr(X), xdt, Mtok, K, _ld(X), _ptr(vals), dtype_code(vals), _ptr(idx), R, _ld(vals),
+                               _ld(idx), Ns, _ptr(x_scale), w_scale, _ptr(Y), ydt, _ld(Y), _stream(X)))
     return Y

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "nm_internal.h"
 
 namespace nm {
@@ -389,10 +391,14 @@ size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xd
     return spmm_ws(Mtok, K, R, Ns, xdt);
 }
 
-nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, nm_dtype vdt,
-                  const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
-                  float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream) {
-    const char* fn = "nm_spmm";
+}  // extern "C"
+
+// Argument checks of nm_spmm and nm_spmm_noalloc (everything but the workspace).  *run is
+// false when there is nothing to compute.
+static nm_status spmm_check(const char* fn, const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,
+                            const void* vals, nm_dtype vdt, const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi,
+                            int Ns, const float* x_scale, void* Y, nm_dtype ydt, int64_t ldy, bool* run) {
+    *run = false;
     NM_REQ(Mtok >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
     NM_REQ(Ns == 0 || (Ns >= 3 && Ns <= 8), NM_ERR_PATTERN,
            "%s: supported patterns are plain 2:4 (Ns=0) and (2N-2):2N via slide (3 <= Ns <= 8), got Ns=%d", fn, Ns);
@@ -424,10 +430,81 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
     NM_REQ(!overlap(ry, span(X, Mtok, K, ldx, es)) && !overlap(ry, span(vals, R, Kl / 2, ldv, es)) &&
                !overlap(ry, span(idx, R, iw, ldi, 4)) && !overlap(ry, span(x_scale, 1, Mtok, Mtok, 4)),
            NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
+    *run = true;
+    return NM_OK;
+}
+
+// ------------------------------------------------------------------ the product's own scratch
+// The workspace of nm_spmm_noalloc: a static device array of NM_SPMM_SCRATCH_BYTES, one copy per
+// GPU, held until the process ends.  In host code `g_spmm_scratch` names a host-side stand-in;
+// its device address on a GPU comes from hipGetSymbolAddress with that GPU current, looked up
+// once per device and kept in g_scratch_dev[] -- only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t g_spmm_scratch[NM_SPMM_SCRATCH_BYTES];
+
+static nm_status scratch_for(nm_stream_t stream, void** out) {
+    constexpr int kMaxDev = 64;
+    static void* dev_ptr[kMaxDev] = {};
+    static std::mutex mu;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(NM_ERR_DEVICE, "nm_spmm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    NM_REQ(dev >= 0 && dev < kMaxDev, NM_ERR_DEVICE, "nm_spmm_noalloc: device %d out of range", dev);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+        if (e != hipSuccess)
+            return set_error(NM_ERR_DEVICE, "nm_spmm_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+        NM_REQ(sdev == dev, NM_ERR_DEVICE, "nm_spmm_noalloc: the stream belongs to device %d, the current device is %d",
+               (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_spmm_scratch));
+        if (e != hipSuccess || !p)
+            return set_error(NM_ERR_DEVICE, "nm_spmm_noalloc: hipGetSymbolAddress of the scratch buffer: %s",
+                             hipGetErrorString(e));
+        dev_ptr[dev] = p;
+    }
+    *out = dev_ptr[dev];
+    return NM_OK;
+}
+
+extern "C" {
+
+nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, nm_dtype vdt,
+                  const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns, const float* x_scale,
+                  float w_scale, void* Y, nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_spmm";
+    bool run = false;
+    nm_status st = spmm_check(fn, X, xdt, Mtok, K, ldx, vals, vdt, idx, R, ldv, ldi, Ns, x_scale, Y, ydt, ldy, &run);
+    if (st != NM_OK || !run) return st;
+    const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
     const size_t need = spmm_ws(Mtok, K, R, Ns, xdt);
     NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
     if (need) NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
     return launch_spmm(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, Y, ydt, ldy, ws, ws_bytes,
+                       (hipStream_t)stream);
+}
+
+nm_status nm_spmm_noalloc(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
+                          nm_dtype vdt, const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi, int Ns,
+                          const float* x_scale, float w_scale, void* Y, nm_dtype ydt, int64_t ldy,
+                          nm_stream_t stream) {
+    const char* fn = "nm_spmm_noalloc";
+    bool run = false;
+    nm_status st = spmm_check(fn, X, xdt, Mtok, K, ldx, vals, vdt, idx, R, ldv, ldi, Ns, x_scale, Y, ydt, ldy, &run);
+    if (st != NM_OK || !run) return st;
+    const size_t need = spmm_ws(Mtok, K, R, Ns, xdt);
+    NM_REQ(need <= NM_SPMM_SCRATCH_BYTES, NM_ERR_WORKSPACE,
+           "%s: this product needs %zu bytes of workspace, more than the %zu-byte scratch buffer; use nm_spmm", fn,
+           need, (size_t)NM_SPMM_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        st = scratch_for(stream, &ws);
+        if (st != NM_OK) return st;
+    }
+    return launch_spmm(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, Y, ydt, ldy, ws, need,
                        (hipStream_t)stream);
 }
 

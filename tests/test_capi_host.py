@@ -136,6 +136,17 @@ def test_empty_inputs_are_noops(nm):
     assert r.nm_pack(None, 1, 0, 8, 8, None, 1, 2, 4, 1, None, 4, None, 1, 0, None) == 0
 
 
+def test_spmm_noalloc_rejects_beyond_scratch_without_gpu(nm):
+    """The size check of the no-allocation product precedes every HIP call."""
+    r = nm.raw
+    S, Y = ctypes.c_void_p(0x1000), ctypes.c_void_p(1 << 40)
+    Mt, R, K = 8192, 256, 4096
+    assert r.nm_spmm_workspace(Mt, K, R, 4, nm.NM_BF16) > nm.NM_SPMM_SCRATCH_BYTES
+    st = r.nm_spmm_noalloc(S, 1, Mt, K, K, ctypes.c_void_p(1 << 36), 1, ctypes.c_void_p(1 << 38), R, 3072, 192, 4,
+                           None, 1.0, Y, 1, R, None)
+    assert _st(nm, st) == "NM_ERR_WORKSPACE" and "scratch" in nm.last_error()
+
+
 def test_spmm_workspace_covers_every_plan(nm):
     """The workspace query does not know the index pointer or ldi, which decide whether the
     DMA ring kernels may run; it must cover the fallback plan too.  One token on the
