@@ -1,17 +1,23 @@
 """Benchmark of the N:M sparsification hot path on one MI355X.
 
-One step = one pass of the whole path on the 2:4 bf16 Llama-7B-shaped layers:
-  1. H = column sums of squares of the calibration activations X_cal [512, 4096]
-  2. fused Hessian score (H + eps) W^2 -> top-2 of 4 -> packed bf16 values +
-     2-bit indices (+ mask bits), for W_a [4096, 4096] and W_b [11008, 4096]
-  3. the structured-sparse GEMM Y = X W_hat^T on both packed layers at
-     M = 1, 16, 128 and 2048 tokens.
-Inputs are synthetic (seeded, LLM-shaped) and resident in HBM before timing.
+One step = one pass of the whole path on the Hessian soft-mask workload (hessian24):
+  1. Hutchinson estimate D [28672, 8192] of the Hessian diagonal of ||X W^T||^2 from the
+     calibration rows X [1024, 8192], 8 Rademacher probes (two bf16 MFMA products per probe)
+  2. score S = (D + eps) W^2, per weight
+  3. per-tensor mean and standard deviation of S (f64)
+  4. the temperature-sigmoid gate annealed over 8 steps (L_mid per step) and projected to
+     the 2:4 hard mask
+  5. W packed under the hard mask: bf16 values + 2-bit in-group indices
+  6. the structured-sparse GEMM Y = X W_hat^T at M = 8192 tokens.
+Inputs are synthetic (seeded, LLM-shaped) and resident in HBM before timing.  The step's
+launches are captured once into a HIP graph; every timed step runs after a 1 GiB read that
+evicts L2 and the 256 MB Infinity Cache (outside the timed events).
 
-Prints ONE JSON line.  value = dense-equivalent SpMM TFLOP per step (2*M*R*K
-summed over the eight products) divided by the whole step time.  The line also
-carries per-kernel HIP-event timings, the roofline of the dominant kernel and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line.  value = dense-equivalent TFLOP per step (Hutchinson's products,
+2 * 2 * P * R * K * n = 7.70 TFLOP, plus the SpMM's 2 * M * R * K = 3.85 TFLOP) divided by
+the step time.  The line also carries per-kernel HIP-event timings, the roofline of the
+dominant launch, every other workload's rows (llama24, tiny24, slide68, ternary68 and
+hessian24 stage by stage, each cold), and the CPU oracle timed on a row sample of the step.
 """
 from __future__ import annotations
 
@@ -19,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 from pathlib import Path
@@ -28,124 +35,99 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-TOKENS = (1, 16, 128, 2048)
-LAYERS = (("W_a", 4096, 0), ("W_b", 11008, 1))
-K = 4096
-N_CAL = 512
 EPS = 1e-6
+# hessian24
+R, K, N_CAL, M_TOK = 28672, 8192, 1024, 8192
+PAGES_CONTEXT = {
+    "note": "speedups the pages quote, on the hardware they name; context only, not targets",
+    "SparseForge": "2:4 end-to-end inference 1.40x-1.44x vs dense on NVIDIA H800 (TensorRT-LLM)",
+    "SALR": "up to 1.7x inference vs dense LoRA at 50% sparsity (hardware not named)",
+    "Sparse-BitNet": "6:8 kernels up to 1.30x vs dense (1.09x-1.30x) on NVIDIA A100 and B200",
+    "SlideSparse": "6:8 end-to-end 1.33x (INT8, NVIDIA A100); bound N/(N-1) = 1.33x",
+}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time (all threads)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements on the other workloads")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements of every workload")
+    p.add_argument("--no-dense", action="store_true", help="skip the hipBLASLt dense context")
     p.add_argument("--eager", action="store_true",
                    help="time the step as individual launches instead of one HIP-graph replay")
-    p.add_argument("--streams", choices=("one", "layers", "small"), default="layers",
-                   help="capture the step on one stream, or forked after H into the two layers' chains "
-                        "(default), or the few-token products beside the 2048-token ones")
     p.add_argument("--pmc-pass", action="store_true",
                    help="run one step plus a plain 256 MiB copy (for HBM counter scaling) and exit")
+    p.add_argument("--rows-only", action="store_true", help="run the per-row measurements only (for profiling)")
     return p.parse_args()
 
 
 class Step:
-    """Preallocated buffers and the raw C-ABI calls of one step."""
+    """Preallocated buffers and the raw C-ABI calls of one hessian24 step."""
 
     def __init__(self, nm, torch, synth, dev):
-        self.nm, self.torch = nm, torch
-        bf = torch.bfloat16
-        self.Xcal = synth.llama24_calib(N_CAL, K).to(dev)
-        self.H = torch.empty(K, dtype=torch.float32, device=dev)
-        self.ws_h = torch.empty(max(1, nm.raw.nm_colsumsq_workspace(N_CAL, K)), dtype=torch.uint8, device=dev)
-        self.layers = []
-        for name, R, tid in LAYERS:
-            W = synth.llama24_weight(R, K, tensor_id=tid).to(dev)
-            vals = torch.empty((R, K // 2), dtype=bf, device=dev)
-            idx = torch.empty((R, K // 32), dtype=torch.int32, device=dev)
-            mask = torch.empty((R, K // 8), dtype=torch.uint8, device=dev)
-            self.layers.append(dict(name=name, R=R, W=W, vals=vals, idx=idx, mask=mask))
-        self.X = {M: synth.activations_bf16(1, M, K).to(dev) for M in TOKENS}
-        self.Y = {(l["name"], M): torch.empty((M, l["R"]), dtype=bf, device=dev) for l in self.layers for M in TOKENS}
-        for l in self.layers:   # one workspace per layer: the two layers' chains may run concurrently
-            need = max(nm.raw.nm_spmm_workspace(M, K, l["R"], 0, nm.NM_BF16) for M in TOKENS)
-            l["ws"] = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        self.nm, self.torch, self.synth = nm, torch, synth
+        r = nm.raw
+        bf, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+        self.P, self.steps = synth.HESSIAN24_PROBES, synth.HESSIAN24_STEPS
+        self.Xc = synth.hessian24_calib(N_CAL, K).to(dev)
+        self.W = synth.hessian24_weight(R, K).to(dev)
+        self.X = synth.activations_bf16(4, M_TOK, K).to(dev)
+        self.D = torch.empty((R, K), dtype=f32, device=dev)
+        self.S = torch.empty((R, K), dtype=f32, device=dev)
+        self.st = torch.empty(2, dtype=torch.float64, device=dev)
+        self.hm = torch.empty((R, K // 8), dtype=u8, device=dev)
+        self.lm = torch.empty(self.steps, dtype=torch.float64, device=dev)
+        self.vals = torch.empty((R, K // 2), dtype=bf, device=dev)
+        self.idx = torch.empty((R, K // 32), dtype=torch.int32, device=dev)
+        self.Y = torch.empty((M_TOK, R), dtype=bf, device=dev)
+
+        def ws(n):
+            return torch.empty(max(1, int(n)), dtype=u8, device=dev)
+        self.ws_h = ws(r.nm_hutchinson_workspace(N_CAL, K, R, self.P))
+        self.ws_s = ws(r.nm_stats_workspace(R, K))
+        self.ws_g = ws(r.nm_gate_workspace(R, K, self.steps))
+        self.ws_y = ws(r.nm_spmm_workspace(M_TOK, K, R, 0, nm.NM_BF16))
         torch.cuda.synchronize()
 
     def launches(self):
-        """(kernel name, callable) in step order; each callable takes a stream handle.
-        The first launch (H) feeds both layers; after it, each layer's launches depend
-        only on that layer's earlier launches."""
-        nm, r = self.nm, self.nm.raw
-        out = []
+        """(name, callable taking a stream handle) in step order."""
+        nm, r, sy = self.nm, self.nm.raw, self.synth
 
         def chk(st):
             if st != 0:
                 raise nm.NMError(st, nm.last_error())
 
-        def colsumsq(stream):
-            chk(r.nm_hdiag_colsumsq(self.Xcal.data_ptr(), nm.NM_BF16, N_CAL, K, K, self.H.data_ptr(),
-                                    self.ws_h.data_ptr(), self.ws_h.numel(), stream))
-        out.append(("colsumsq", colsumsq))
-        for l in self.layers:
-            def prune(stream, l=l):
-                chk(r.nm_prune_pack(l["W"].data_ptr(), nm.NM_BF16, K, self.H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN,
-                                    l["W"].data_ptr(), nm.NM_BF16, K, l["R"], K, 2, 4, l["mask"].data_ptr(), K // 8,
-                                    nm.NM_BF16, l["vals"].data_ptr(), K // 2, l["idx"].data_ptr(), K // 32, stream))
-            out.append((f"prune_pack {l['name']}", prune))
-        for l in self.layers:
-            for M in TOKENS:
-                def spmm(stream, l=l, M=M):
-                    Y = self.Y[(l["name"], M)]
-                    chk(r.nm_spmm(self.X[M].data_ptr(), nm.NM_BF16, M, K, K, l["vals"].data_ptr(), nm.NM_BF16,
-                                  l["idx"].data_ptr(), l["R"], K // 2, K // 32, 0, None, 1.0, Y.data_ptr(), nm.NM_BF16,
-                                  l["R"], l["ws"].data_ptr(), l["ws"].numel(), stream))
-                out.append((f"spmm {l['name']} M={M}", spmm))
-        return out
+        return [
+            ("hutchinson", lambda s: chk(r.nm_hdiag_hutchinson(
+                self.Xc.data_ptr(), N_CAL, K, K, R, self.P, sy.HESSIAN24_SEED, self.D.data_ptr(), K,
+                self.ws_h.data_ptr(), self.ws_h.numel(), s))),
+            ("score", lambda s: chk(r.nm_score(
+                self.W.data_ptr(), nm.NM_BF16, R, K, K, self.D.data_ptr(), K, sy.HESSIAN24_EPS, nm.NM_SCORE_HESSIAN,
+                self.S.data_ptr(), K, s))),
+            ("stats", lambda s: chk(r.nm_score_stats(
+                self.S.data_ptr(), R, K, K, self.st.data_ptr(), self.ws_s.data_ptr(), self.ws_s.numel(), s))),
+            ("gate", lambda s: chk(r.nm_gate(
+                self.S.data_ptr(), R, K, K, self.st.data_ptr(), 2, 4, sy.HESSIAN24_T0, sy.HESSIAN24_RHO, self.steps,
+                self.steps - 1, None, K, self.hm.data_ptr(), K // 8, self.lm.data_ptr(), self.ws_g.data_ptr(),
+                self.ws_g.numel(), s))),
+            ("pack", lambda s: chk(r.nm_pack(
+                self.W.data_ptr(), nm.NM_BF16, R, K, K, self.hm.data_ptr(), K // 8, 2, 4, nm.NM_BF16,
+                self.vals.data_ptr(), K // 2, self.idx.data_ptr(), K // 32, 0, s))),
+            (f"spmm M={M_TOK}", lambda s: chk(r.nm_spmm(
+                self.X.data_ptr(), nm.NM_BF16, M_TOK, K, K, self.vals.data_ptr(), nm.NM_BF16, self.idx.data_ptr(), R,
+                K // 2, K // 32, 0, None, 1.0, self.Y.data_ptr(), nm.NM_BF16, R, self.ws_y.data_ptr(),
+                self.ws_y.numel(), s))),
+        ]
 
     def run(self, stream):
         for _, f in self.launches():
             f(stream)
 
-    def run_two(self, main, side, split="layers"):
-        """The step on two torch streams, forked after H and joined at the end, so that
-        independent kernels can share the GPU.  split="layers": W_a's chain on `main`,
-        W_b's on `side`.  split="small": H and both packs on `main`, then the two
-        2048-token products on `main` and the few-token products on `side`."""
-        torch = self.torch
-        launches = self.launches()
-        fork = torch.cuda.Event()
-        if split == "layers":
-            launches[0][1](main.cuda_stream)
-            fork.record(main)
-            side.wait_event(fork)
-            for name, f in launches[1:]:
-                f((main if self.layers[0]["name"] in name else side).cuda_stream)
-        else:
-            rest = []
-            for name, f in launches:
-                if name.startswith("spmm"):
-                    rest.append((name, f))
-                else:
-                    f(main.cuda_stream)
-            fork.record(main)
-            side.wait_event(fork)
-            big = f"M={TOKENS[-1]}"
-            for name, f in sorted(rest, key=lambda t: not t[0].endswith(big) or "W_a" in t[0]):
-                f((main if name.endswith(big) else side).cuda_stream)
-        join = torch.cuda.Event()
-        join.record(side)
-        main.wait_event(join)
-
     def outputs(self):
-        out = [self.H]
-        for l in self.layers:
-            out += [l["vals"], l["idx"], l["mask"]]
-        return out + list(self.Y.values())
+        return [self.D, self.S, self.st, self.hm, self.lm, self.vals, self.idx, self.Y]
 
     def snapshot(self):
         return [t.clone() for t in self.outputs()]
@@ -158,25 +140,47 @@ class Step:
         return all(self.torch.equal(a, b) for a, b in zip(self.outputs(), ref))
 
 
-def algorithmic_work():
-    """Per-launch algorithmic bytes (HBM-bound kernels) or flops (GEMMs)."""
-    w = {"colsumsq": dict(bound="hbm", bytes=N_CAL * K * 2 + K * 4)}
-    for name, R, _ in LAYERS:
-        # read W (2 B) ; write 2 of 4 values (1 B), 2-bit indices (0.125 B), mask bit (0.125 B) per weight; read H
-        w[f"prune_pack {name}"] = dict(bound="hbm", bytes=int(R * K * 3.25) + K * 4)
-        for M in TOKENS:
-            packed = R * K // 2 * 2 + R * K // 32 * 4
-            w[f"spmm {name} M={M}"] = dict(
-                # up to 128 tokens the product is bound by the packed weight's HBM stream
-                bound="hbm" if M <= 128 else "mfma",
-                flops_dense_eq=2 * M * R * K,          # dense-equivalent work
-                flops=2 * M * R * K // 2,              # multiply-adds on kept weights only (2 of 4)
-                bytes=packed + M * K * 2 + M * R * 2)  # packed weight + X + Y
-    return w
+HUTCH_FLOPS = 2 * 2 * 8 * R * K * N_CAL            # two products per probe, 8 probes
+SPMM_DENSE_EQ = 2 * M_TOK * R * K                   # dense-equivalent work of the sparse product
+# the gate's work per score and step, in full-rate lane operations: one 2^x and one
+# reciprocal (4 each), then the scale, 1 + e, the blend toward h (2) and m (1 - m) (2)
+GATE_OPS_PER_STEP = 4 + 4 + 1 + 1 + 2 + 2
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz full-rate lane operations per
+# second; a transcendental (2^x, 1/x) issues at a quarter of that rate.
+VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
+
+
+def algorithmic_work(steps):
+    """Per-launch algorithmic bytes (HBM-bound kernels), lane operations (VALU) or flops."""
+    return {
+        "hutchinson": dict(bound="mfma", flops=HUTCH_FLOPS, flops_dense_eq=HUTCH_FLOPS),
+        # read W (2 B) and D (4 B), write S (4 B) per weight
+        "score": dict(bound="hbm", bytes=R * K * 10),
+        "stats": dict(bound="hbm", bytes=R * K * 4),
+        # per weight and step: the gate's lane operations; bytes: read S (4 B), write the mask bit
+        "gate": dict(bound="alu", ops=R * K * steps * GATE_OPS_PER_STEP, bytes=R * K * 4 + R * K // 8),
+        # read W (2 B) and the mask bit, write 2 of 4 values (1 B) and 2-bit indices (0.125 B)
+        "pack": dict(bound="hbm", bytes=int(R * K * 3.25)),
+        f"spmm M={M_TOK}": dict(bound="mfma", flops=SPMM_DENSE_EQ // 2, flops_dense_eq=SPMM_DENSE_EQ,
+                                bytes=R * K // 2 * 2 + R * K // 32 * 4 + M_TOK * K * 2 + M_TOK * R * 2),
+    }
+
+
+def cpu_model():
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(target_s: float):
-    """The oracle on a row sample of the same step, scaled to dense-eq TFLOP/s."""
+    """The oracle on the step restricted to a sample of output rows (Hutchinson rows, their
+    score, the statistics and gate of the sampled scores, the pack, and the masked product of
+    those rows with all 8192 tokens), in the step's unit (dense-equivalent TFLOP/s); once on
+    every host thread and once on one."""
     import numpy as np
 
     import oracle as O
@@ -185,43 +189,49 @@ def cpu_baseline(target_s: float):
     import torch
 
     def bits(t):
-        return t.view(torch.int16).numpy().view(np.uint16)
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    Xcal = bits(synth.llama24_calib(N_CAL, K))
-    Ws = {name: bits(synth.llama24_weight(R, K, tensor_id=tid)) for name, R, tid in LAYERS}
-    Xs = {M: bits(synth.activations_bf16(1, M, K)) for M in TOKENS}
+    Xc = bits(synth.hessian24_calib(N_CAL, K))
+    W = bits(synth.hessian24_weight(R, K))
+    X = bits(synth.activations_bf16(4, M_TOK, K))
+    P, steps = synth.HESSIAN24_PROBES, synth.HESSIAN24_STEPS
+    per_row = 2 * 2 * P * K * N_CAL + 2 * M_TOK * K    # dense-equivalent flops per output row
 
-    def run(rows):
+    def run(nrows):
+        rows = np.linspace(0, R - 1, nrows).astype(np.int64)
         t0 = time.perf_counter()
-        H = O.colsumsq(Xcal).astype(np.float32)
-        flops = 0
-        for name, R, tid in LAYERS:
-            W = np.ascontiguousarray(Ws[name][:rows])
-            S = O.score(W, H, EPS)
-            mask = O.topn_mask(S, 2, 4)
-            O.pack(W, mask, 2, 4)
-            for M in TOKENS:
-                O.masked_matmul(Xs[M], W, mask)
-                flops += 2 * M * rows * K
-        return time.perf_counter() - t0, flops
+        D = O.hutchinson_rows(Xc, P, synth.HESSIAN24_SEED, rows).astype(np.float32)
+        Wr = np.ascontiguousarray(W[rows])
+        S = O.score(Wr, D, synth.HESSIAN24_EPS)
+        mu, sg = O.stats(S)
+        _, hm, _ = O.gate_anneal(S, mu, sg, 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps)
+        O.pack(Wr, hm, 2, 4)
+        O.masked_matmul(X, Wr, hm)
+        return time.perf_counter() - t0
 
-    # time a small sample, then size the real one to the target
-    t_small, _ = run(8)
-    rows = int(max(8, min(4096, 8 * target_s / max(t_small, 1e-3))))
-    t, flops = run(rows)
-    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=O.num_threads(), kind="oracle",
-                sample=f"whole step on the first {rows} output rows of each layer (H, score, top-2 of 4, pack, "
-                       f"and the masked matmul at M=1,16,128,2048), {t:.1f} s")
+    threads = O.num_threads()
+    out = dict(unit="TFLOP/s", kind="oracle", cpu=cpu_model(), threads_available=os.cpu_count())
+    t8 = run(threads)
+    rows_all = int(max(threads, min(4096, threads * target_s / max(t8, 1e-3))))
+    t = run(rows_all)
+    out.update(value=rows_all * per_row / t / 1e12, cores=threads,
+               sample=f"hessian24 step on {rows_all} evenly spaced output rows of 28672 (Hutchinson rows with 8 "
+                      f"probes, score, statistics and gate of the sampled scores, pack, masked product with all "
+                      f"8192 tokens), {t:.1f} s on {threads} threads; full step extrapolated "
+                      f"{t * R / rows_all:.0f} s")
+    O.set_threads(1)
+    try:
+        t1 = run(2)
+        rows_1 = int(max(2, min(256, 2 * target_s / 3 / max(t1, 1e-3))))
+        t1 = run(rows_1)
+        out["one_thread"] = dict(value=rows_1 * per_row / t1 / 1e12, rows=rows_1, seconds=round(t1, 1))
+    finally:
+        O.set_threads(threads)
+    return out
 
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
-# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz full-rate lane operations per
-# second; a transcendental (2^x, 1/x) issues at a quarter of that rate.
-VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
-# the gate's work per score and step, in full-rate lane operations: one 2^x and one
-# reciprocal (4 each), then the scale, 1 + e, the blend toward h (2) and m (1 - m) (2)
-GATE_OPS_PER_STEP = 4 + 4 + 1 + 1 + 2 + 2
 
 
 def measure_rows(nm, torch, synth, dev, reps: int = 5):
@@ -283,6 +293,33 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         return lambda: chk(r.nm_spmm(X.data_ptr(), xdt, M, K, K, vals.data_ptr(), vdt, idx.data_ptr(), R, Kl // 2,
                                      Kl // 32, Ns, None if xs is None else xs.data_ptr(), a, Y.data_ptr(), ydt, R,
                                      None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(), sh))
+
+    # ---- llama24: H from X_cal, fused Hessian score / top-2 of 4 / pack, SpMM at M in {1, 16, 128, 2048}
+    K = 4096
+    Xcal = synth.llama24_calib(512, K).to(dev)
+    H = torch.empty(K, dtype=f32, device=dev)
+    row("llama24", "A1", "colsumsq 512x4096", lambda: chk(r.nm_hdiag_colsumsq(
+        Xcal.data_ptr(), nm.NM_BF16, 512, K, K, H.data_ptr(), None, 0, sh)), "latency", 512 * K * 2 + K * 4)
+    for lname, R, tid in (("W_a", 4096, 0), ("W_b", 11008, 1)):
+        W = synth.llama24_weight(R, K, tensor_id=tid).to(dev)
+        vals, idx, mask = (torch.empty((R, K // 2), dtype=bf, device=dev),
+                           torch.empty((R, K // 32), dtype=i32, device=dev), torch.empty((R, K // 8), dtype=u8, device=dev))
+        row("llama24", "A3+A7+A8", f"prune_pack {lname} {R}x{K}", lambda: chk(r.nm_prune_pack(
+            W.data_ptr(), nm.NM_BF16, K, H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN, W.data_ptr(), nm.NM_BF16, K, R, K,
+            2, 4, mask.data_ptr(), K // 8, nm.NM_BF16, vals.data_ptr(), K // 2, idx.data_ptr(), K // 32, sh)), "hbm",
+            int(R * K * 3.25) + K * 4)
+        for M in (1, 16, 128, 2048):
+            X = synth.activations_bf16(1, M, K).to(dev)
+            Y = torch.empty((M, R), dtype=bf, device=dev)
+            ws = ws_for(r.nm_spmm_workspace(M, K, R, 0, nm.NM_BF16))
+            f = spmm(X, nm.NM_BF16, M, K, vals, nm.NM_BF16, idx, R, 0, Y, nm.NM_BF16, ws=ws)
+            if M <= 128:
+                row("llama24", "A12", f"spmm {lname} M={M}", f, "hbm", R * K // 2 * 2 + R * K // 32 * 4 + M * K * 2 + M * R * 2)
+            else:
+                row("llama24", "A12", f"spmm {lname} M={M}", f, "mfma", 2 * M * R * K // 2)
+            del X, Y, ws
+        del W, vals, idx, mask
+    del Xcal, H
 
     # ---- tiny24: fused Hessian score / top-2 of 4 / pack from fp32 W, SpMM at M = 16 (launch-latency bound)
     W, H, X = synth.tiny24_inputs()
@@ -429,7 +466,7 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
             row("ternary68", "A11+A13", f"spmm int8 lifted 6912x2560 M={M}", f, "mfma_i8", 2 * M * R * Kl // 2)
     del Wf, Wt, vals, idx, mask
 
-    # ---- hessian24: Hutchinson diagonal, score, z-score statistics, gate/anneal, pack, SpMM M = 8192
+    # ---- hessian24, stage by stage (each cold; the same launches as the headline step)
     R, K, n, P = 28672, 8192, 1024, synth.HESSIAN24_PROBES
     Xc = synth.hessian24_calib(n, K).to(dev)
     W = synth.hessian24_weight(R, K).to(dev)
@@ -469,23 +506,30 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     return out
 
 
-def traffic_for(kernel_file: str, kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
-    source has not changed since they were taken."""
+def traffic_for(key: str, files):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if none of the kernel
+    sources has changed since they were taken."""
     f = ROOT / "profiles" / "traffic.json"
     if not f.exists():
         return None
     try:
         d = json.loads(f.read_text())
-        e = d.get(kernel)
+        e = d.get(key)
         if not e:
             return None
-        src = (ROOT / "semi_structured_sparsity_amd" / "csrc" / kernel_file).read_bytes()
-        if hashlib.sha256(src).hexdigest() != e["source_sha256"]:
+        h = hashlib.sha256()
+        for name in files:
+            h.update((ROOT / "semi_structured_sparsity_amd" / "csrc" / name).read_bytes())
+        if h.hexdigest() != e["source_sha256"]:
             return None
         return int(e["bytes_per_launch"])
     except Exception:
         return None
+
+
+# kernel sources of each launch (for the staleness check of committed counter figures)
+SOURCES = {"hutchinson": ("k_hutch.hip", "k_spmm.hip"), "score": ("k_prune.hip",), "stats": ("k_gate.hip",),
+           "gate": ("k_gate.hip",), "pack": ("k_prune.hip",), f"spmm M={M_TOK}": ("k_spmm.hip",)}
 
 
 def main():
@@ -500,9 +544,12 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    st = Step(nm, torch, synth, dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    if args.rows_only:
+        print(json.dumps({"rows": measure_rows(nm, torch, synth, dev)}))
+        return
+    st = Step(nm, torch, synth, dev)
 
     if args.pmc_pass:
         st.run(sh)
@@ -514,8 +561,8 @@ def main():
         return
 
     # The step's launches are captured once into a HIP graph and replayed, so the timed
-    # region measures the GPU rather than Python's launch overhead.  The replay is
-    # checked bit for bit against an eager run of the same step.
+    # region measures the GPU rather than Python's launch overhead.  The replay is checked
+    # bit for bit against an eager run of the same step.
     graph_ok = None
     if args.eager:
         run_step = lambda: st.run(sh)
@@ -524,92 +571,131 @@ def main():
         torch.cuda.synchronize()
         ref = st.snapshot()
         g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
         with torch.cuda.graph(g):
-            cur = torch.cuda.current_stream(dev)
-            if args.streams == "one":
-                st.run(cur.cuda_stream)
-            else:
-                st.run_two(cur, side, args.streams)
+            st.run(torch.cuda.current_stream(dev).cuda_stream)
         st.clear_outputs()
         g.replay()
         torch.cuda.synchronize()
         graph_ok = st.same(ref)
+        del ref
         if not graph_ok:
             print("graph replay differs from the eager step", file=sys.stderr)
             sys.exit(1)
         run_step = g.replay
 
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)   # 1 GiB, read before every timed step
+
+    def evict():
+        flush.sum()
+
     for _ in range(args.warmup):
+        evict()
         run_step()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in ev:
+        evict()
+        e0.record(stream)
         run_step()
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = wall / args.steps * 1e3
-
-    # per-kernel durations: HIP events around each launch on the launch stream
-    launches = st.launches()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
-          for _ in range(args.steps)]
-    for s in range(args.steps):
-        for j, (_, f) in enumerate(launches):
-            ev[s][j][0].record(stream)
-            f(sh)
-            ev[s][j][1].record(stream)
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = sum(step_ms) / len(step_ms)
+    # the same steps back to back (warm caches), for comparison
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    w1.record(stream)
     torch.cuda.synchronize()
-    work = algorithmic_work()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    # per-launch durations: HIP events around each C call on the launch stream, eager, each
+    # step after the same eviction
+    launches = st.launches()
+    kev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        evict()
+        for j, (_, f) in enumerate(launches):
+            kev[s][j][0].record(stream)
+            f(sh)
+            kev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    work = algorithmic_work(st.steps)
     kernels = []
     for j, (name, _) in enumerate(launches):
-        t_ms = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
+        t_s = sum(kev[s][j][0].elapsed_time(kev[s][j][1]) for s in range(args.steps)) / args.steps * 1e-3
         w = work[name]
-        k = dict(name=name, us=round(t_ms * 1e3, 2), bound=w["bound"])
-        k["GBps"] = round(w["bytes"] / (t_ms * 1e-3) / 1e9, 1)
+        k = dict(name=name, us=round(t_s * 1e6, 2), bound=w["bound"])
+        if "bytes" in w:
+            k["GBps"] = round(w["bytes"] / t_s / 1e9, 1)
         if "flops" in w:
-            k["eff_TFLOPs"] = round(w["flops_dense_eq"] / (t_ms * 1e-3) / 1e12, 2)
-            k["TFLOPs"] = round(w["flops"] / (t_ms * 1e-3) / 1e12, 2)
-        k["frac"] = round(k["GBps"] / HBM_PEAK_GBPS if w["bound"] == "hbm" else k["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+            k["TFLOPs"] = round(w["flops"] / t_s / 1e12, 2)
+            k["eff_TFLOPs"] = round(w["flops_dense_eq"] / t_s / 1e12, 2)
+        if w["bound"] == "hbm":
+            k["frac"] = round(k["GBps"] / HBM_PEAK_GBPS, 4)
+        elif w["bound"] == "mfma":
+            k["frac"] = round(k["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+        else:
+            k["GOPs"] = round(w["ops"] / t_s / 1e9, 1)
+            k["frac"] = round(k["GOPs"] / VALU_PEAK_GOPS, 4)
         kernels.append(k)
     dom = max(kernels, key=lambda k: k["us"])
     wd = work[dom["name"]]
     if dom["bound"] == "hbm":
-        kfile = "k_prune.hip"
         roof = dict(bound="hbm", achieved=dom["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s", frac=dom["frac"])
     else:
-        kfile = "k_spmm.hip"
         roof = dict(bound="mfma", achieved=dom["TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=dom["frac"])
     roof["kernel"] = dom["name"]
-    roof["traffic"] = traffic_for(kfile, dom["name"])
+    roof["traffic"] = traffic_for(dom["name"], SOURCES[dom["name"]])
+    roof["algorithmic"] = wd.get("flops", wd.get("bytes"))
 
-    spmm_flops = sum(w["flops_dense_eq"] for n, w in work.items() if n.startswith("spmm"))
-    maskpack = [k for k in kernels if k["name"].startswith("prune_pack")]
-    mp_bytes = sum(work[k["name"]]["bytes"] for k in maskpack)
-    mp_us = sum(k["us"] for k in maskpack)
-    spmm_us = sum(k["us"] for k in kernels if k["name"].startswith("spmm"))
+    mp = [k for k in kernels if k["name"] in ("score", "stats", "gate", "pack")]
+    mp_bytes = sum(work[k["name"]]["bytes"] for k in mp)
+    mp_us = sum(k["us"] for k in mp)
 
-    # context only (never on the library path): hipBLASLt's dense bf16 GEMM of the dominant
-    # product's shape, X [2048, 4096] x W_b^T, with the same HIP-event timing
-    Xd, Wd = st.X[TOKENS[-1]], st.layers[-1]["W"]
-    for _ in range(3):
-        torch.matmul(Xd, Wd.t())
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        torch.matmul(Xd, Wd.t())
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dense_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    dense_ctx = dict(what=f"torch.matmul (hipBLASLt) dense bf16, same shape as {dom['name']}; context only",
-                     us=round(dense_us, 2), sparse_us=dom["us"],
-                     sparse_speedup=round(dense_us / dom["us"], 3))
+    dense_ctx = None
+    if not args.no_dense:
+        # context only (never on the library path): hipBLASLt dense bf16 GEMMs of the same shapes
+        # -- the SpMM's dense equivalent, and Hutchinson's two products per probe (8 probes
+        # stacked along the rows)
+        def tmm(f, reps=5):
+            for _ in range(2):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+        Wt = st.W.t()
+        d_spmm = tmm(lambda: torch.matmul(st.X, Wt))
+        V = torch.randint(0, 2, (st.P * R, K), device=dev, dtype=torch.int8).to(torch.bfloat16) * 2 - 1
+        XcT = st.Xc.t().contiguous()
+        U = torch.empty((st.P * R, N_CAL), dtype=torch.bfloat16, device=dev)
+        d_u = tmm(lambda: torch.matmul(V, XcT, out=U))
+        G = torch.empty((st.P * R, K), dtype=torch.bfloat16, device=dev)
+        d_g = tmm(lambda: torch.matmul(U, st.Xc, out=G))
+        del V, U, G, XcT
+        kd = {k["name"]: k["us"] for k in kernels}
+        dense_ctx = dict(
+            what="torch.matmul (hipBLASLt) dense bf16 GEMMs of the same shapes; context only",
+            spmm_dense_us=round(d_spmm, 1), spmm_sparse_us=kd[f"spmm M={M_TOK}"],
+            spmm_sparse_speedup=round(d_spmm / kd[f"spmm M={M_TOK}"], 3),
+            hutchinson_dense_products_us=round(d_u + d_g, 1), hutchinson_us=kd["hutchinson"],
+            hutchinson_vs_dense=round((d_u + d_g) / kd["hutchinson"], 3))
+        torch.cuda.empty_cache()
 
+    flops_step = HUTCH_FLOPS + SPMM_DENSE_EQ
     rows = None if args.no_rows else measure_rows(nm, torch, synth, dev)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     line = {
         "metric": "N:M SpMM effective TFLOP/s + mask/pack GB/s, as % of MI355X roofline",
-        "value": round(spmm_flops / (ms * 1e-3) / 1e12, 3),
+        "value": round(flops_step / (ms * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -620,21 +706,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama24: 2:4 bf16 Llama-7B-shaped layers W 4096x4096 and 11008x4096 (1% outlier "
-                               "input channels x20), H from X_cal 512x4096, fused score/top-2-of-4/pack, "
-                               "SpMM at M in {1,16,128,2048}",
-                   "pattern": "2:4", "K": K, "tokens": list(TOKENS)},
-        "spmm_effective_TFLOPs": round(spmm_flops / (spmm_us * 1e-6) / 1e12, 2),
+        "config": {"workload": "hessian24: W 28672x8192 bf16 ~0.015 N(0,1), Hutchinson diagonal of ||X W^T||^2 "
+                               "from X 1024x8192 with 8 Rademacher probes, score (D+eps) W^2, per-tensor z-score, "
+                               "sigmoid gate T0=0.5 annealed over 8 steps to a 2:4 hard mask, pack, SpMM at M=8192",
+                   "pattern": "2:4", "R": R, "K": K, "calibration_rows": N_CAL, "tokens": M_TOK, "probes": st.P},
+        "cache": "cold: a 1 GiB read evicts L2 and the Infinity Cache before every timed step (not timed)",
+        "warm_ms_per_step": round(warm_ms, 4),
+        "wall_s": round(wall, 3),
+        "step_flops": flops_step,
+        "spmm_effective_TFLOPs": next(k["eff_TFLOPs"] for k in kernels if k["name"].startswith("spmm")),
         "maskpack_GBps": round(mp_bytes / (mp_us * 1e-6) / 1e9, 1),
         "maskpack_frac_hbm": round(mp_bytes / (mp_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "timing": "eager launches" if args.eager else (
-            "HIP graph replay of the whole step" + {
-                "one": " on one stream",
-                "layers": ", the two layers' chains on two streams after H",
-                "small": ", the few-token products on a second stream beside the 2048-token ones"}[args.streams] +
-            " (checked equal to an eager step)"),
+        "timing": "eager launches" if args.eager else "HIP graph replay of the whole step (checked equal to an "
+                                                      "eager step); HIP events on the launch stream",
         "roofline": roof,
         "dense_context": dense_ctx,
+        "pages_context": PAGES_CONTEXT,
         "kernels": kernels,
         "rows": rows,
         "cpu_baseline": cpu,

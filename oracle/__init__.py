@@ -91,6 +91,7 @@ def _declare(L):
         "or_gate_anneal": (None, [P, I64, I64, D, D, I, I, D, D, I, I, P, P, I64, P]),
         "or_gate_value": (D, [F, D, D, D, D, I]),
         "or_num_threads": (I, []),
+        "or_set_threads": (None, [I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -454,6 +455,10 @@ def gate_anneal(S: np.ndarray, mu: float, sigma: float, N: int, M: int, T0: floa
 
 def num_threads() -> int:
     return int(lib().or_num_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().or_set_threads(int(n))
 
 
 def gate_value(s: float, mu: float, sigma: float, T0: float, rho: float, t: int) -> float:

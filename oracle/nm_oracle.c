@@ -805,6 +805,9 @@ void or_gate_anneal(const float* S, int64_t R, int64_t K, double mu, double sigm
 /* Number of threads the parallel loops above use. */
 int or_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the thread count of the parallel loops (results do not depend on it). */
+void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Gate value for a single element at step t (for sampled checks). */
 double or_gate_value(float s, double mu, double sigma, double T0, double rho, int t) {
     double T = T0 * pow(rho, (double)t);
