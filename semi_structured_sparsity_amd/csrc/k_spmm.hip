@@ -79,6 +79,7 @@ struct SpmmArgs {
     int64_t Mtok, K, R;
     int64_t comp_bytes;    // packed value bytes per row (K'/2 * sizeof(T))
     int64_t idx_words;     // index words per row (ceil(K'/32): two 2-bit fields per 4 lifted columns)
+    int64_t xrow_bytes;    // bytes of one row of the original (unlifted) X, for the in-kernel lift
     float w_scale;
     int scaled;
     int ydt;
@@ -1030,10 +1031,12 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
 // Y = X W^T for a dense bf16 weight W [R, K] (ldv) with the split ring's tile, waves,
 // swizzles, DMA and epilogue, and dense MFMA (v_mfma_f32_32x32x16_bf16, whose operand and
 // accumulator layouts are the sparse instruction's with 16-byte B fragments).  A stage is
-// 64 columns: 128 bytes of W per row and of X per token, each in a 2-stage ring (128 KB),
-// four MFMA depths.  One barrier per stage, before its last depth: stage s+1 has landed
-// and every wave has read stage s, whose buffers then take stage s+2.  Used for the
-// many-token product of weights decoded from the bitmap format.
+// SK columns (SK * 2 bytes of W per row and of X per token, SK / 16 MFMA depths) in an
+// NS-slot LDS ring: with a 64-column stage two slots fill 128 KB, with a 32-column stage
+// five fill 160 KB and keep four stages in flight while one is multiplied.
+// One barrier per stage, before its last depth: stage s+1 has landed and every wave has
+// read stage s, whose slot then takes stage s+NS.  Used for the many-token product of
+// weights decoded from the bitmap format and for both Hutchinson products.
 // HUTCH: the Hutchinson second product D = (2/P) sum_p V_p .* (U_p X) (D [R, K] f32 as Y
 // [Mtok = R rows, R = K columns]): the A operand is the transposed calibration rows XT [K, n]
 // (vals), the B operand probe p's rows of U [P*R, n] (X); the stage index runs over
@@ -1043,16 +1046,19 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
 // signs are four Rademacher words per probe (its two rows of U, two 64-column blocks).
 // GEN: the Hutchinson first product U [P*R, n] = V X^T: the A operand is the calibration
 // rows X [n, K] (vals), the B operand the stacked probe rows q = p R + o of V, generated
-// into the B stages (one Rademacher word per row and stage, each of the 512 threads
-// expanding half a row into four swizzled 16-byte chunks); the barrier that follows every
+// into the B stages (one Rademacher word per row and 64 columns; each of the 512 threads
+// expands half a stage row into swizzled 16-byte chunks); the barrier that follows every
 // stage's issue covers these LDS writes as it covers the DMA.
 // MODE: 0 plain, 1 HUTCH, 2 GEN.
-template <int SR, int ST, int WRN, int WTN, int MODE = 0>
+template <int SR, int ST, int WRN, int WTN, int MODE = 0, int SK = 64, int NS = 2>
 __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs a) {
     constexpr bool HUTCH = MODE == 1, GEN = MODE == 2;
     constexpr int NW = WRN * WTN, BR = WRN * SR * 32, BT = WTN * ST * 32;
-    constexpr int WSTAGE = BR * 128, XSTAGE = BT * 128;
-    constexpr int W_OFF = 0, X_OFF = 2 * WSTAGE, RING = X_OFF + 2 * XSTAGE;
+    constexpr int ROWB = SK * 2, CH = ROWB / 16, D = SK / 16;   // bytes and chunks per row per stage, depths
+    static_assert(SK == 64 || SK == 32, "64- or 32-column stages");
+    static_assert(D % 2 == 0, "depth ping-pong needs an even depth count");
+    constexpr int WSTAGE = BR * ROWB, XSTAGE = BT * ROWB, SLOT = WSTAGE + XSTAGE;
+    constexpr int RING = NS * SLOT;
     constexpr int NWL = WSTAGE / 1024 / NW, NXL = XSTAGE / 1024 / NW;   // loads per wave per stage
     static_assert(WSTAGE % (1024 * NW) == 0 && XSTAGE % (1024 * NW) == 0 && NWL >= 1 && NXL >= 1, "loads per wave");
     constexpr int SMEM = RING > NW * kStageWords<SR> * 4 ? RING : NW * kStageWords<SR> * 4;
@@ -1064,10 +1070,12 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     int tr, tt;
     tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
     const int64_t r0 = (int64_t)tr * BR, t0 = (int64_t)tt * BT;
-    const int nsteps = a.nsteps;   // K / 64 >= 1 (HUTCH: probes * stages per probe)
+    const int nsteps = a.nsteps;   // K / SK >= 1 (HUTCH: probes * stages per probe)
     const int PS = HUTCH ? a.pstages : nsteps;
     const uint32_t sbase = lds_addr(smem);
-    auto sw = [](int r) { return (r >> 1) & 7; };   // row / token r of 8 chunks: logical c at c ^ sw(r)
+    // row / token r of CH chunks: logical chunk c at c ^ sw(r) (16 consecutive rows read by a
+    // 16-byte LDS read then hit 64 distinct banks)
+    auto sw = [](int r) { return CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
     const void* baseW = uniform_ptr(a.vals + r0 * a.ldv * 2);
     const void* baseX = uniform_ptr(a.X + t0 * a.ldx * 2);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
@@ -1082,36 +1090,41 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         gp = (int)(qc / a.prows);
         go = qc - (int64_t)gp * a.prows;
     }
+    constexpr int RPL = 64 / CH;   // rows per DMA instruction
 #pragma unroll
     for (int i = 0; i < NWL; ++i) {
-        const int row = (wave * NWL + i) * 8 + (lane >> 3);
+        const int row = (wave * NWL + i) * RPL + lane / CH;
         const int64_t gr = row < rmax ? row : rmax;
-        oW[i] = (uint32_t)(gr * a.ldv * 2 + ((lane & 7) ^ sw(row)) * 16);
+        oW[i] = (uint32_t)(gr * a.ldv * 2 + ((lane % CH) ^ sw(row)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < NXL; ++i) {
-        const int row = (wave * NXL + i) * 8 + (lane >> 3);
+        const int row = (wave * NXL + i) * RPL + lane / CH;
         const int64_t gt = row < tmax ? row : tmax;
-        oX[i] = (uint32_t)(gt * a.ldx * 2 + ((lane & 7) ^ sw(row)) * 16);
+        oX[i] = (uint32_t)(gt * a.ldx * 2 + ((lane % CH) ^ sw(row)) * 16);
     }
     auto issue = [&](int s) __attribute__((always_inline)) {
-        const uint32_t sw0 = sbase + (uint32_t)(W_OFF + (s & 1) * WSTAGE), sx0 = sbase + (uint32_t)(X_OFF + (s & 1) * XSTAGE);
+        const uint32_t slot = sbase + (uint32_t)((s % NS) * SLOT);
         // HUTCH: stage s % PS of probe s / PS (the probe's U rows follow the previous probe's)
         const int ks = HUTCH ? s % PS : s;
         const uint32_t xp = HUTCH ? (uint32_t)(s / PS) * (uint32_t)(a.Mtok * a.ldx * 2) : 0u;
 #pragma unroll
-        for (int i = 0; i < NWL; ++i) dma16s(sw0 + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(ks * 128));
+        for (int i = 0; i < NWL; ++i) dma16s(slot + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(ks * ROWB));
         if constexpr (GEN) {
-            const uint64_t w = rad_word(a.seed, gp, go, s, a.K / 64);
-            uint8_t* xrow = smem + X_OFF + (s & 1) * XSTAGE + grow * 128;
+            // the stage's SK columns are bits [SK * (s % (64 / SK)), +SK) of the row's word of
+            // its 64-column block; this thread writes CH / 2 chunks of 8 columns
+            const uint64_t w = rad_word(a.seed, gp, go, s / (64 / SK), a.K / 64);
+            const int bb = (SK == 32 ? 4 * (s & 1) : 0) + ghalf * (CH / 2);   // first sign byte
+            uint8_t* xrow = smem + (s % NS) * SLOT + WSTAGE + grow * ROWB;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int cl = ghalf * 4 + c;
-                *(uint4*)(xrow + ((cl ^ sw(grow)) * 16)) = signs_to_bf16x8((uint32_t)(w >> (8 * cl)) & 0xffu);
+            for (int c = 0; c < CH / 2; ++c) {
+                const int cl = ghalf * (CH / 2) + c;
+                *(uint4*)(xrow + ((cl ^ sw(grow)) * 16)) = signs_to_bf16x8((uint32_t)(w >> (8 * (bb + c))) & 0xffu);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < NXL; ++i) dma16s(sx0 + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * 128));
+            for (int i = 0; i < NXL; ++i)
+                dma16s(slot + WSTAGE + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * ROWB));
         }
     };
     struct Frag {
@@ -1119,17 +1132,17 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     };
     const int h = lane >> 5, l32 = lane & 31;
     auto read_depth = [&](int s, int d, Frag& f) __attribute__((always_inline)) {
-        const uint8_t* sW = smem + W_OFF + (s & 1) * WSTAGE;
-        const uint8_t* sX = smem + X_OFF + (s & 1) * XSTAGE;
+        const uint8_t* sW = smem + (s % NS) * SLOT;
+        const uint8_t* sX = sW + WSTAGE;
 #pragma unroll
         for (int i = 0; i < SR; ++i) {
             const int row = (wr * SR + i) * 32 + l32;
-            f.a[i] = *(const i32x4_t*)(sW + row * 128 + ((2 * d + h) ^ sw(row)) * 16);
+            f.a[i] = *(const i32x4_t*)(sW + row * ROWB + ((2 * d + h) ^ sw(row)) * 16);
         }
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
             const int tok = (wt * ST + j) * 32 + l32;
-            f.b[j] = *(const i32x4_t*)(sX + tok * 128 + ((2 * d + h) ^ sw(tok)) * 16);
+            f.b[j] = *(const i32x4_t*)(sX + tok * ROWB + ((2 * d + h) ^ sw(tok)) * 16);
         }
     };
     f32x16_t acc[SR][ST];
@@ -1173,15 +1186,18 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         }
     };
     constexpr int PER = NWL + (GEN ? 0 : NXL);   // DMA loads per stage
-    Frag fa, fb;
-    issue(0);
-    if (nsteps > 1) {
-        issue(1);
-        wait_vm_barrier<PER>();
-    } else {
-        wait_vm_barrier<0>();
-    }
-    read_depth(0, 0, fa);
+    // Prologue: stages 0..NS-1 fill the ring; wait for stage 0 (the others may stay in
+    // flight) and read its depth 0.  Each depth's fragments are read while the previous
+    // depth's MFMAs issue; the last depth of stage s waits for stage s+1 (stages s+2 ..
+    // s+NS-1 may stay in flight), meets the other waves, refills stage s's slot with stage
+    // s+NS and reads depth 0 of stage s+1.
+    Frag fr[2];
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+        if (p < nsteps) issue(p);
+    if (nsteps >= NS) wait_vm_barrier<(NS - 1) * PER>();
+    else wait_vm_barrier<0>();
+    read_depth(0, 0, fr[0]);
     for (int s = 0; s < nsteps; ++s) {
         if constexpr (HUTCH) {
             if (s % PS == 0) {   // probe p = s / PS begins: acc *= s_{p-1} s_p (s_p for p = 0)
@@ -1198,17 +1214,20 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
                 flip(wn);
             }
         }
-        read_depth(s, 1, fb);
-        mfmas(fa);
-        read_depth(s, 2, fa);
-        mfmas(fb);
-        read_depth(s, 3, fb);
-        mfmas(fa);
-        // stage s+1 landed (the last loads issued) and stage s read by every wave
-        wait_vm_barrier<0>();
-        if (s + 2 < nsteps) issue(s + 2);
-        if (s + 1 < nsteps) read_depth(s + 1, 0, fa);
-        mfmas(fb);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (d + 1 < D) {
+                read_depth(s, d + 1, fr[(d + 1) & 1]);
+            } else if (s + 1 < nsteps) {
+                // stage s+1 landed (the loads of s+2 .. s+NS-1 may stay in flight) and stage s
+                // read by every wave
+                if (s + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * PER>();
+                else wait_vm_barrier<0>();
+                if (s + NS < nsteps) issue(s + NS);
+                read_depth(s + 1, 0, fr[0]);
+            }
+            mfmas(fr[d & 1]);
+        }
     }
     if constexpr (HUTCH) {   // acc *= s_{P-1}
         uint64_t wl[ST][2];
@@ -1229,7 +1248,15 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
 // whole-line DMA as in the ring kernel, and wave w computes depth w of every stage
 // over the whole tile.  The four partial tiles are summed through LDS in wave order.
 // gridDim.y splits the stages over blocks (partials + the fixed-order reduce kernel).
-template <typename T, int SR, int ST, int KB, int NS>
+// LIFT (6:8 weights, "SlideSparse" section 2B: the lifted activation is an index remap of
+// X): the activation is never lifted in memory.  Stage s multiplies lifted columns whose
+// windows lie in a run of at most 12 (bf16) or 23 (one-byte) 8-column groups of X; the X
+// slot of a token holds 256 original bytes from the 16-byte-aligned start of that run
+// (loaded by the same whole-line DMA, clamped to the row), and each lane assembles its
+// lifted B fragment from the slot: window w of group q is original columns 8q + 2w .. +3,
+// i.e. dwords w, w+1 of the group's 16 bytes (bf16) or bytes 2w .. 2w+3 of its 8 (one-
+// byte codes: one byte-aligned funnel shift of the group's two dwords).
+template <typename T, int SR, int ST, int KB, int NS, bool LIFT = false>
 __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     constexpr int es = sizeof(T);
     constexpr int KO = KB / es, KDEP = es == 2 ? 32 : 64;
@@ -1266,7 +1293,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
     const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
-    uint32_t oA[NA], oI[NI], oB[NB];
+    uint32_t oA[NA], oI[NI], oB[NB], oBc[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int q = (wave * NA + i) * 64 + lane;
@@ -1286,8 +1313,15 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         const int row = (wave * NB + i) * (64 / BCH) + lane / BCH;
         const int c = (lane % BCH) ^ swb(row);
         const int64_t gt = row < tmax ? row : tmax;
-        oB[i] = (uint32_t)(gt * a.ldx * es + c * 16);
+        oB[i] = (uint32_t)(gt * a.ldx * es + (LIFT ? 0 : c * 16));
+        oBc[i] = (uint32_t)(c * 16);
     }
+    // LIFT: first original byte of stage sg's slot (a multiple of 16), and the last 16-byte
+    // chunk of an X row (slot chunks past the row end load it; they are never used)
+    auto slot_start = [](int sg) -> uint32_t {
+        return es == 2 ? (uint32_t)(16 * ((32 * sg) / 3)) : (uint32_t)(8 * (((64 * sg) / 3) & ~1));
+    };
+    const uint32_t xlast = (uint32_t)(a.xrow_bytes - 16);
     auto issue = [&](int sl) __attribute__((always_inline)) {   // local stage sl of this block's range
         const int sg = s_begin + sl;
         const uint32_t st = sbase + (uint32_t)((sl % NS) * STAGE);
@@ -1295,8 +1329,17 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int i = 0; i < NA; ++i) dma16s(st + (wave * NA + i) * 1024, baseA, oA[i] + (uint32_t)(sg * AROW));
 #pragma unroll
         for (int i = 0; i < NI; ++i) dma4s(st + I_OFF + (wave * NI + i) * 256, baseI, oI[i] + (uint32_t)(sg * AI * 4));
+        if constexpr (LIFT) {
+            const uint32_t xs = slot_start(sg);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) dma16s(st + B_OFF + (wave * NB + i) * 1024, baseB, oB[i] + (uint32_t)(sg * KB));
+            for (int i = 0; i < NB; ++i) {
+                const uint32_t o = xs + oBc[i];
+                dma16s(st + B_OFF + (wave * NB + i) * 1024, baseB, oB[i] + (o < xlast ? o : xlast));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) dma16s(st + B_OFF + (wave * NB + i) * 1024, baseB, oB[i] + (uint32_t)(sg * KB));
+        }
     };
     struct Frag {
         i32x4_t a[SR];
@@ -1304,6 +1347,54 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         i32x8_t b[ST];
     };
     const int d = wave;   // this wave's depth in every stage
+    // LIFT: the lane's B fragment of depth d in stage sg from the token's slot of original
+    // columns (trow, chunk swizzle sw).  The fragment's two 16-byte halves are lifted bytes
+    // 64d + 16h + 32r (r = 0, 1) of the stage: lifted windows J .. (2 of 4 bf16 columns, or
+    // 4 of 4 one-byte codes), window J = group J/3, offset J%3 of the 6:8 lift.
+    auto lifted_frag = [&](const uint8_t* trow, int sw, int sg) __attribute__((always_inline)) -> i32x8_t {
+        i32x8_t out;
+        if constexpr (es == 2) {
+            const int qb = (32 * sg) / 3;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int J = 32 * sg + 8 * d + 2 * h + 4 * r;   // first window of this half
+                const int q = J / 3, w = J - 3 * q, ql = q - qb;
+                const i32x4_t g0 = *(const i32x4_t*)(trow + ((ql ^ sw) * 16));
+                const i32x4_t g1 = *(const i32x4_t*)(trow + (((ql + 1) ^ sw) * 16));
+                // window J: dwords w, w+1 of group ql; window J+1: dwords w+1, w+2 of group ql
+                // (w < 2) or dwords 0, 1 of group ql + 1 (w == 2)
+                const int e0 = w == 0 ? g0[0] : (w == 1 ? g0[1] : g0[2]);
+                const int e1 = w == 0 ? g0[1] : (w == 1 ? g0[2] : g0[3]);
+                const int e2 = w == 0 ? g0[1] : (w == 1 ? g0[2] : g1[0]);
+                const int e3 = w == 0 ? g0[2] : (w == 1 ? g0[3] : g1[1]);
+                out[4 * r + 0] = e0;
+                out[4 * r + 1] = e1;
+                out[4 * r + 2] = e2;
+                out[4 * r + 3] = e3;
+            }
+        } else {
+            const int gb = ((64 * sg) / 3) & ~1;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int J = 64 * sg + 16 * d + 4 * h + 8 * r;   // windows J .. J+3
+                const int q = J / 3, w = J - 3 * q, ql = q - gb;
+                // groups ql and ql + 1 (8 bytes each, halves of 16-byte chunks)
+                const uint2 ga = *(const uint2*)(trow + (((ql >> 1) ^ sw) * 16) + 8 * (ql & 1));
+                const uint2 gc = *(const uint2*)(trow + ((((ql + 1) >> 1) ^ sw) * 16) + 8 * ((ql + 1) & 1));
+                // window of group g at offset v: bytes 2v .. 2v+3 of the group (v_alignbyte takes
+                // a byte shift of 0-3 only: offset 2 is the high dword itself)
+                auto win = [](uint2 g, int v) {
+                    return v == 2 ? (int)g.y : (int)__builtin_amdgcn_alignbyte(g.y, g.x, (uint32_t)(2 * v));
+                };
+                // windows J .. J+3 by the offset of J: (w = 0) g0 0,1,2 g1 0; (1) g0 1,2 g1 0,1; (2) g0 2 g1 0,1,2
+                out[4 * r + 0] = win(ga, w);
+                out[4 * r + 1] = w == 2 ? win(gc, 0) : win(ga, w + 1);
+                out[4 * r + 2] = w == 0 ? win(ga, 2) : win(gc, w - 1);
+                out[4 * r + 3] = win(gc, w);
+            }
+        }
+        return out;
+    };
     auto read = [&](int sl, Frag& f) __attribute__((always_inline)) {
         const uint8_t* sA = smem + (sl % NS) * STAGE;
         const uint32_t* sI = (const uint32_t*)(sA + I_OFF);
@@ -1318,9 +1409,13 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int j = 0; j < ST; ++j) {
             const int tok = j * 32 + l32;
             const uint8_t* trow = sB + tok * KB;
-            const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ swb(tok)) * 16);
-            const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ swb(tok)) * 16);
-            f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (LIFT) {
+                f.b[j] = lifted_frag(trow, swb(tok), s_begin + sl);
+            } else {
+                const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ swb(tok)) * 16);
+                const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ swb(tok)) * 16);
+                f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
         }
     };
     using AccV = typename Mma<T>::Acc;
@@ -1855,11 +1950,15 @@ struct SpmmWs {
 
 // ring_ok: the product's operands allow the DMA ring kernels (decided by the caller from
 // the actual pointers and leading dimensions; the query takes the larger of both plans).
-static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok);
+// fused: the lift happens inside the K-split ring kernel (no lifted activation stored).
+static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok,
+                             bool fused);
+// 6:8 products of up to 256 tokens on the K-split ring lift inside the kernel
+static bool lift_fused(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, bool ring_ok);
 
 size_t spmm_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt) {
-    const size_t a = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, true).total();
-    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, false).total();
+    const size_t a = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, true, lift_fused(Mtok, K, R, Ns, xdt, true)).total();
+    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, xdt, 0, false, false).total();
     return a > b ? a : b;
 }
 
@@ -1870,7 +1969,18 @@ static bool ring_ok_for(const SpmmArgs& a, int64_t es) {
            a.R * a.ldi * 4 < (1LL << 32) && a.Mtok * a.ldx * es < (1LL << 32);
 }
 
-static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok) {
+static bool lift_fused(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, bool ring_ok) {
+    if (Ns != 4) return false;
+    const int64_t Kl = lifted_cols(K, Ns);
+    const SpmmPlan p = xdt == NM_BF16 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok) : plan_for<int8_t>(Mtok, Kl, R, ring_ok);
+    // one-byte codes: the in-kernel gather (two 8-byte reads and a funnel shift per window
+    // pair) costs more than a separate lift on the 128-token tiles (6912 x 2560 int8 at 256
+    // tokens: 38.3 us fused against 32.7 us lifting first; at one token 14.6 against 16.2)
+    return p.mid != 0 && (xdt == NM_BF16 || p.mid <= 2);
+}
+
+static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, int rank, bool ring_ok,
+                             bool fused) {
     SpmmWs w;
     if (Mtok <= 0 || K <= 0 || R <= 0) return w;
     const int64_t Kl = lifted_cols(K, Ns), es = xdt == NM_BF16 ? 2 : 1;
@@ -1879,7 +1989,7 @@ static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtyp
         w.u = round256((size_t)Mtok * rank * 2);
         w.pu = round256((size_t)lp.S() * Mtok * rank * 4);
     }
-    if (Ns) w.xl = lift_bytes(Mtok, K, Ns, es);
+    if (Ns && !fused) w.xl = lift_bytes(Mtok, K, Ns, es);
     // the plan depends on the element size only (int8 and FP8 share it)
     const SpmmPlan p = es == 2 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok) : plan_for<int8_t>(Mtok, Kl, R, ring_ok);
     if (rank > 0 && !p.ring) w.f32 = round256((size_t)Mtok * (size_t)R * 4);
@@ -1891,7 +2001,7 @@ static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtyp
 // partials, f32buf: the sparse product in f32 when an adapter term is added afterwards
 // (both carved from the workspace by the caller, sized by spmm_ws_layout)
 template <typename T>
-static nm_status run_spmm(SpmmArgs a, bool ring_ok, void* part, void* f32buf, hipStream_t s) {
+static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void* f32buf, hipStream_t s) {
     const SpmmPlan p = plan_for<T>(a.Mtok, a.K, a.R, ring_ok);
     a.nsteps = p.nsteps;
     a.KS = p.KS;
@@ -1908,7 +2018,7 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, void* part, void* f32buf, hi
         b.ydt = NM_F32;
         b.ldy = a.R;
         b.scaled = 0;
-        const nm_status st = run_spmm<T>(b, ring_ok, part, nullptr, s);
+        const nm_status st = run_spmm<T>(b, ring_ok, lift, part, nullptr, s);
         if (st != NM_OK) return st;
         const dim3 g(grid_cap(ceil_div(a.Mtok * a.R, 256), 65536));
         hipLaunchKernelGGL(lowrank_epilogue_kernel, g, dim3(256), 0, s, (const float*)f32buf, a);
@@ -1919,9 +2029,18 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, void* part, void* f32buf, hi
         // up to 32 tokens a 6-stage ring (17 KB a stage): more weight bytes in flight per CU
         // when the weight comes from HBM (measured 13-15% faster there at one token; a
         // 6-stage ring for 64 tokens measured no faster than 3 stages)
-        if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6>), grid, dim3(256), 0, s, a);
-        else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
+        if (lift) {   // 6:8: the activation is lifted inside the kernel (one-byte codes: up to 64 tokens)
+            if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6, true>), grid, dim3(256), 0, s, a);
+            else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3, true>), grid, dim3(256), 0, s, a);
+            else if constexpr (sizeof(T) == 2)
+                hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3, true>), grid, dim3(256), 0, s, a);
+            else
+                return set_error(NM_ERR_DEVICE, "nm_spmm: no in-kernel lift for one-byte codes on 128-token tiles");
+        } else {
+            if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6>), grid, dim3(256), 0, s, a);
+            else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
+        }
     } else if (p.skinny == 1) {
         // 32-row tiles, 4 waves split K, 16 depths in flight per wave
         hipLaunchKernelGGL((spmm_skinny_kernel<T, 1, 1, 4, 16>), dim3((unsigned)ceil_div(a.R, 32), p.KS), dim3(256), 0, s, a);
@@ -1975,8 +2094,9 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, void* part, void* f32buf, hi
 }
 
 size_t spmm_lowrank_ws(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank) {
-    const size_t a = spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, true).total();
-    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, false).total();
+    const size_t a =
+        spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, true, lift_fused(Mtok, K, R, Ns, NM_BF16, true)).total();
+    const size_t b = spmm_ws_layout(Mtok, K, R, Ns, NM_BF16, rank, false, false).total();
     return a > b ? a : b;
 }
 
@@ -2006,15 +2126,19 @@ static nm_status spmm_impl(const char* fn, const void* X, nm_dtype xdt, int64_t 
     a.w_scale = w_scale;
     a.scaled = (x_scale != nullptr || w_scale != 1.0f) ? 1 : 0;
     a.ydt = (int)ydt;
-    // the 2:4 product runs over the lifted width, on X itself or on the lifted activation
-    // that the workspace holds (256-byte aligned, row stride K')
-    if (Ns) {
-        a.K = Kl;
+    // the 2:4 product runs over the lifted width, on X itself (lifted inside the kernel, up
+    // to 256 tokens of 6:8) or on the lifted activation that the workspace holds (256-byte
+    // aligned, row stride K')
+    a.K = Kl;
+    a.xrow_bytes = K * es;
+    bool ring_ok = ring_ok_for(a, es);
+    const bool fused = lift_fused(Mtok, K, R, Ns, xdt, ring_ok);
+    if (Ns && !fused) {
         a.ldx = Kl;
+        ring_ok = ring_ok_for(a, es);
     }
-    const bool ring_ok = ring_ok_for(a, es);
     const int rank = lr ? lr->rank : 0;
-    const SpmmWs w = spmm_ws_layout(Mtok, K, R, Ns, xdt, rank, ring_ok);
+    const SpmmWs w = spmm_ws_layout(Mtok, K, R, Ns, xdt, rank, ring_ok, fused);
     if (w.total() && (!ws || ws_bytes < w.total()))
         return set_error(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, w.total());
     uint8_t* wp = (uint8_t*)ws;
@@ -2047,7 +2171,7 @@ static nm_status spmm_impl(const char* fn, const void* X, nm_dtype xdt, int64_t 
         a.ldb = lr->ldb;
         a.rank = lr->rank;
     }
-    if (Ns) {
+    if (Ns && !fused) {
         // (2N-2):2N: lift X into the workspace, then the plain product over the lifted width
         if (Ns == 4) {
             const dim3 g(grid_cap(ceil_div(Mtok * (K / 8), 256), 8192));
@@ -2066,9 +2190,9 @@ static nm_status spmm_impl(const char* fn, const void* X, nm_dtype xdt, int64_t 
         }
         a.X = XL;
     }
-    if (xdt == NM_I8) return run_spmm<int8_t>(a, ring_ok, PART, F32, s);
-    if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ring_ok, PART, F32, s);
-    return run_spmm<uint16_t>(a, ring_ok, PART, F32, s);
+    if (xdt == NM_I8) return run_spmm<int8_t>(a, ring_ok, fused, PART, F32, s);
+    if (xdt == NM_FP8) return run_spmm<fp8e4m3>(a, ring_ok, fused, PART, F32, s);
+    return run_spmm<uint16_t>(a, ring_ok, fused, PART, F32, s);
 }
 
 nm_status launch_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, const void* vals,
@@ -2084,6 +2208,12 @@ nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ld
     return spmm_impl("nm_spmm_lowrank", X, NM_BF16, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, nullptr, 1.0f, &lr, Y,
                      ydt, ldy, ws, ws_bytes, s);
 }
+
+// Stage width and ring depth of the dense split ring (Hutchinson's products, bitmap decode).
+// Measured on the Hutchinson call at 28672 x 8192, n = 1024, 8 probes (same result bit for
+// bit): 64-column stages in 2 slots 7.17 ms, 32-column stages in 4 slots 7.68 ms, in 5
+// slots 7.73 ms -- more bytes in flight do not help; the extra barriers cost.
+constexpr int kDenseSK = 64, kDenseNS = 2;
 
 // Y [Mtok, R] (ydt bf16 or f32, ldy) = X [Mtok, K] (ldx) W^T, W [R, K] (ldw) dense bf16.
 // NM_ERR_SHAPE (nothing launched) when the kernel does not apply: K % 64, unaligned rows,
@@ -2108,10 +2238,11 @@ nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, i
     a.ydt = (int)ydt;
     a.scaled = 0;
     a.rank = 0;
-    a.nsteps = (int)(K / 64);
+    a.nsteps = (int)(K / kDenseSK);
     a.tiles_r = (int)ceil_div(R, BR);
     a.tiles_t = (int)ceil_div(Mtok, BT);
-    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 0, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
+                       dim3(64 * WRN * WTN), 0, s, a);
     return check_launch("dense product");
 }
 
@@ -2137,12 +2268,13 @@ nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, in
     a.w_scale = 2.0f / (float)probes;
     a.seed = seed;
     a.probes = probes;
-    a.pstages = (int)(n / 64);
+    a.pstages = (int)(n / kDenseSK);
     a.nsteps = probes * a.pstages;
     a.tiles_r = (int)ceil_div(K, BR);
     a.tiles_t = (int)ceil_div(R, BT);
     const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
-    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 1>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 1, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
+                       dim3(64 * WRN * WTN), 0, s, a);
     return check_launch("nm_hdiag_hutchinson");
 }
 
@@ -2164,11 +2296,12 @@ nm_status launch_hutch_u_ring(const uint16_t* X, int64_t ldx, int64_t n, int64_t
     a.seed = seed;
     a.probes = probes;
     a.prows = R;
-    a.nsteps = (int)(K / 64);
+    a.nsteps = (int)(K / kDenseSK);
     a.tiles_r = (int)ceil_div(n, BR);
     a.tiles_t = (int)ceil_div(a.Mtok, BT);
     const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
-    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 2>), dim3((unsigned)tiles), dim3(64 * WRN * WTN), 0, s, a);
+    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 2, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
+                       dim3(64 * WRN * WTN), 0, s, a);
     return check_launch("nm_hdiag_hutchinson");
 }
 

@@ -219,6 +219,69 @@ def test_spmm_general_slide_int8_exact(nm, Ns, Mt, R, K):
     assert np.array_equal(y, y_ref)
 
 
+# 6:8 products of up to 256 tokens lift the activation inside the K-split ring kernel: token
+# counts on each of its three tile sizes (32, 64, 128 tokens), stage counts with every
+# phase of the 3-stage window pattern and K splits over blocks, rows of X with padding
+# beyond K (the slot's chunks past the row end are clamped to it)
+@pytest.mark.parametrize("dt", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("Mt,R,K,pad", [(1, 64, 256, 0), (1, 64, 1024, 16), (17, 130, 768, 16), (64, 96, 4096, 0), (100, 300, 512, 32),
+                                       (200, 70, 1280, 0), (256, 64, 2560, 64), (3, 513, 2560, 0)])
+def test_spmm_lift_in_kernel_exact(nm, dt, Mt, R, K, pad):
+    g = np.random.default_rng(Mt + R + K + pad + len(dt))
+    Kl = O.lifted_width(K, 4)
+    if dt != "bf16" and Kl % 256:
+        pytest.skip("one-byte lifted K-split ring needs K' % 256 == 0")
+    if dt == "bf16":
+        X, W = _int_bf16(g, (Mt, K), 2), _int_bf16(g, (R, K), 2)
+        Xo, Wo = X, W
+        S = O.bf16_to_f32(W)
+    elif dt == "i8":
+        X, W = g.integers(-127, 128, (Mt, K)).astype(np.int8), g.integers(-1, 2, (R, K)).astype(np.int8)
+        Xo, Wo = X, W
+        S = W.astype(np.float32)
+    else:
+        X = O.e4m3_encode(g.integers(-8, 9, (Mt, K)).astype(np.float32))
+        W = O.e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float32))
+        Xo, Wo = O.e4m3_decode(X), O.e4m3_decode(W)
+        S = Wo
+    mask = O.topn_mask(np.abs(S) + g.random((R, K)).astype(np.float32), 6, 8)
+    vals, idx, bad = O.slide_decompose(W.view(np.int8) if dt == "fp8" else W, mask, 4)
+    assert bad == 0
+    i = torch.from_numpy(idx.view(np.int32)).to(dev())
+    if dt == "bf16":
+        v = np_bf16(vals).to(dev())
+        Xbig = torch.zeros((Mt, K + pad), dtype=torch.bfloat16)
+        Xbig[:, :K] = np_bf16(X)
+    elif dt == "i8":
+        v = torch.from_numpy(vals).to(dev())
+        Xbig = torch.zeros((Mt, K + pad), dtype=torch.int8)
+        Xbig[:, :K] = torch.from_numpy(X)
+    else:
+        v = torch.from_numpy(vals.view(np.uint8)).view(torch.float8_e4m3fn).to(dev())
+        Xbig = torch.zeros((Mt, K + pad), dtype=torch.uint8)
+        Xbig[:, :K] = torch.from_numpy(X)
+        Xbig = Xbig.view(torch.float8_e4m3fn)
+    Xd = Xbig.to(dev())[:, :K]
+    ydt = nm.NM_I32 if dt == "i8" else nm.NM_F32
+    Y = nm.nm_spmm(Xd, v, i, R=R, Ns=4, ydt=ydt).cpu().numpy()
+    if dt == "fp8":
+        ref = O.masked_matmul_fp8(X, W, mask)
+    elif dt == "i8":
+        ref, _ = O.masked_matmul_i8(X, W, mask, np.ones(Mt, np.float32), 1.0)
+    else:
+        ref = O.masked_matmul(Xo, Wo, mask)
+    assert np.array_equal(Y.astype(np.float64), np.asarray(ref, np.float64))
+    # the same product on the lifted activation (the plain kernel over K') agrees bit for bit
+    if dt == "bf16":
+        XL = np_bf16(O.lift(X, 4))
+    elif dt == "i8":
+        XL = torch.from_numpy(O.lift(X, 4))
+    else:
+        XL = torch.from_numpy(O.lift(X.view(np.int8), 4).view(np.uint8)).view(torch.float8_e4m3fn)
+    Y2 = nm.nm_spmm(XL.to(dev()), v, i, R=R, Ns=0, ydt=ydt).cpu().numpy()
+    assert np.array_equal(Y, Y2)
+
+
 def test_spmm_workspace_query_covers_fallback_plan(nm):
     """An index view 4 bytes off 16-byte alignment with an odd row stride keeps the product
     off the DMA ring kernels; at one token on 11008 x 4096 the fallback splits K over two
