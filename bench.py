@@ -1,10 +1,11 @@
 """Benchmark of the N:M sparsification hot path on one MI355X.
 
 One step = one pass of the whole path on the Hessian soft-mask workload (hessian24):
-  1. Hutchinson estimate D [28672, 8192] of the Hessian diagonal of ||X W^T||^2 from the
-     calibration rows X [1024, 8192], 8 Rademacher probes (two bf16 MFMA products per probe)
-  2. score S = (D + eps) W^2, per weight
-  3. per-tensor mean and standard deviation of S (f64)
+  1-3. Hutchinson estimate D [28672, 8192] of the Hessian diagonal of ||X W^T||^2 from the
+     calibration rows X [1024, 8192], 8 Rademacher probes (two bf16 MFMA products per probe),
+     the score S = (D + eps) W^2 per weight and the per-tensor mean and standard deviation
+     of S (f64), in one call whose second product writes S and its moments (D is never
+     stored)
   4. the temperature-sigmoid gate annealed over 8 steps (L_mid per step) and projected to
      the 2:4 hard mask
   5. W packed under the hard mask: bf16 values + 2-bit in-group indices
@@ -75,7 +76,6 @@ class Step:
         self.Xc = synth.hessian24_calib(N_CAL, K).to(dev)
         self.W = synth.hessian24_weight(R, K).to(dev)
         self.X = synth.activations_bf16(4, M_TOK, K).to(dev)
-        self.D = torch.empty((R, K), dtype=f32, device=dev)
         self.S = torch.empty((R, K), dtype=f32, device=dev)
         self.st = torch.empty(2, dtype=torch.float64, device=dev)
         self.hm = torch.empty((R, K // 8), dtype=u8, device=dev)
@@ -86,8 +86,7 @@ class Step:
 
         def ws(n):
             return torch.empty(max(1, int(n)), dtype=u8, device=dev)
-        self.ws_h = ws(r.nm_hutchinson_workspace(N_CAL, K, R, self.P))
-        self.ws_s = ws(r.nm_stats_workspace(R, K))
+        self.ws_h = ws(r.nm_hutchinson_score_workspace(N_CAL, K, R, self.P))
         self.ws_g = ws(r.nm_gate_workspace(R, K, self.steps))
         self.ws_y = ws(r.nm_spmm_workspace(M_TOK, K, R, 0, nm.NM_BF16))
         torch.cuda.synchronize()
@@ -101,14 +100,10 @@ class Step:
                 raise nm.NMError(st, nm.last_error())
 
         return [
-            ("hutchinson", lambda s: chk(r.nm_hdiag_hutchinson(
-                self.Xc.data_ptr(), N_CAL, K, K, R, self.P, sy.HESSIAN24_SEED, self.D.data_ptr(), K,
-                self.ws_h.data_ptr(), self.ws_h.numel(), s))),
-            ("score", lambda s: chk(r.nm_score(
-                self.W.data_ptr(), nm.NM_BF16, R, K, K, self.D.data_ptr(), K, sy.HESSIAN24_EPS, nm.NM_SCORE_HESSIAN,
-                self.S.data_ptr(), K, s))),
-            ("stats", lambda s: chk(r.nm_score_stats(
-                self.S.data_ptr(), R, K, K, self.st.data_ptr(), self.ws_s.data_ptr(), self.ws_s.numel(), s))),
+            ("hutchinson+score+stats", lambda s: chk(r.nm_hutchinson_score(
+                self.Xc.data_ptr(), N_CAL, K, K, R, self.P, sy.HESSIAN24_SEED, self.W.data_ptr(), nm.NM_BF16, K,
+                sy.HESSIAN24_EPS, self.S.data_ptr(), K, self.st.data_ptr(), self.ws_h.data_ptr(), self.ws_h.numel(),
+                s))),
             ("gate", lambda s: chk(r.nm_gate(
                 self.S.data_ptr(), R, K, K, self.st.data_ptr(), 2, 4, sy.HESSIAN24_T0, sy.HESSIAN24_RHO, self.steps,
                 self.steps - 1, None, K, self.hm.data_ptr(), K // 8, self.lm.data_ptr(), self.ws_g.data_ptr(),
@@ -127,7 +122,7 @@ class Step:
             f(stream)
 
     def outputs(self):
-        return [self.D, self.S, self.st, self.hm, self.lm, self.vals, self.idx, self.Y]
+        return [self.S, self.st, self.hm, self.lm, self.vals, self.idx, self.Y]
 
     def snapshot(self):
         return [t.clone() for t in self.outputs()]
@@ -142,23 +137,30 @@ class Step:
 
 HUTCH_FLOPS = 2 * 2 * 8 * R * K * N_CAL            # two products per probe, 8 probes
 SPMM_DENSE_EQ = 2 * M_TOK * R * K                   # dense-equivalent work of the sparse product
-# the gate's work per score and step, in full-rate lane operations: one 2^x and one
-# reciprocal (4 each), then the scale, 1 + e, the blend toward h (2) and m (1 - m) (2)
-GATE_OPS_PER_STEP = 4 + 4 + 1 + 1 + 2 + 2
+# the gate's work per score, in full-rate lane operations.  A step with a sigmoid: the scale,
+# one 2^x (4: quarter rate), 1 + e, one reciprocal (4), the blend toward h (2) and m (1 - m)
+# (2); with rho = 1/2 every step after the first squares the previous exponential (1) in
+# place of the scale and the 2^x; the last step (beta = 1) blends nothing.
+GATE_OPS_PER_STEP = 1 + 4 + 1 + 4 + 2 + 2
+
+
+def gate_ops(steps, rho):
+    if steps < 2:
+        return 0
+    later = 1 + 1 + 4 + 2 + 2 if rho == 0.5 else GATE_OPS_PER_STEP
+    return GATE_OPS_PER_STEP + (steps - 2) * later
 # VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz full-rate lane operations per
 # second; a transcendental (2^x, 1/x) issues at a quarter of that rate.
 VALU_PEAK_GOPS = 256 * 4 * 16 * 2.4
 
 
-def algorithmic_work(steps):
+def algorithmic_work(steps, rho):
     """Per-launch algorithmic bytes (HBM-bound kernels), lane operations (VALU) or flops."""
     return {
-        "hutchinson": dict(bound="mfma", flops=HUTCH_FLOPS, flops_dense_eq=HUTCH_FLOPS),
-        # read W (2 B) and D (4 B), write S (4 B) per weight
-        "score": dict(bound="hbm", bytes=R * K * 10),
-        "stats": dict(bound="hbm", bytes=R * K * 4),
-        # per weight and step: the gate's lane operations; bytes: read S (4 B), write the mask bit
-        "gate": dict(bound="alu", ops=R * K * steps * GATE_OPS_PER_STEP, bytes=R * K * 4 + R * K // 8),
+        # the two products' flops; bytes of the fused score: read W (2 B), write S (4 B) per weight
+        "hutchinson+score+stats": dict(bound="mfma", flops=HUTCH_FLOPS, flops_dense_eq=HUTCH_FLOPS, bytes=R * K * 6),
+        # per weight: the gate's lane operations over all steps; bytes: read S (4 B), write the mask bit
+        "gate": dict(bound="alu", ops=R * K * gate_ops(steps, rho), bytes=R * K * 4 + R * K // 8),
         # read W (2 B) and the mask bit, write 2 of 4 values (1 B) and 2-bit indices (0.125 B)
         "pack": dict(bound="hbm", bytes=int(R * K * 3.25)),
         f"spmm M={M_TOK}": dict(bound="mfma", flops=SPMM_DENSE_EQ // 2, flops_dense_eq=SPMM_DENSE_EQ,
@@ -477,11 +479,17 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         "mfma", 2 * P * 2 * R * K * n)
     del wsh
     S = torch.empty((R, K), dtype=f32, device=dev)
+    st = torch.empty(2, dtype=torch.float64, device=dev)
+    wsf = ws_for(r.nm_hutchinson_score_workspace(n, K, R, P))
+    row("hessian24", "A2+A3+A4", "hutchinson + score + statistics (fused, diagonal not stored)", lambda: chk(
+        r.nm_hutchinson_score(Xc.data_ptr(), n, K, K, R, P, synth.HESSIAN24_SEED, W.data_ptr(), nm.NM_BF16, K,
+                              synth.HESSIAN24_EPS, S.data_ptr(), K, st.data_ptr(), wsf.data_ptr(), wsf.numel(), sh)),
+        "mfma", 2 * P * 2 * R * K * n)
+    del wsf
     row("hessian24", "A3", "score (H+eps) W^2, per-weight H", lambda: chk(r.nm_score(
         W.data_ptr(), nm.NM_BF16, R, K, K, D.data_ptr(), K, synth.HESSIAN24_EPS, nm.NM_SCORE_HESSIAN, S.data_ptr(), K,
         sh)), "hbm", R * K * 10)
     del D
-    st = torch.empty(2, dtype=torch.float64, device=dev)
     wss = ws_for(r.nm_stats_workspace(R, K))
     row("hessian24", "A4", "score mean/std (f64)", lambda: chk(r.nm_score_stats(
         S.data_ptr(), R, K, K, st.data_ptr(), wss.data_ptr(), wss.numel(), sh)), "hbm", R * K * 4)
@@ -491,7 +499,8 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     wsg = ws_for(r.nm_gate_workspace(R, K, steps))
     row("hessian24", "A5+A6+A7", "gate/anneal -> 2:4 hard mask", lambda: chk(r.nm_gate(
         S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, synth.HESSIAN24_T0, synth.HESSIAN24_RHO, steps, steps - 1, None, K,
-        hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "alu", R * K * steps * GATE_OPS_PER_STEP)
+        hm.data_ptr(), K // 8, lm.data_ptr(), wsg.data_ptr(), wsg.numel(), sh)), "alu",
+        R * K * gate_ops(steps, synth.HESSIAN24_RHO))
     del S
     vals, idx = torch.empty((R, K // 2), dtype=bf, device=dev), torch.empty((R, K // 32), dtype=i32, device=dev)
     row("hessian24", "A8", "pack 28672x8192 from the hard mask", lambda: chk(r.nm_pack(
@@ -528,8 +537,8 @@ def traffic_for(key: str, files):
 
 
 # kernel sources of each launch (for the staleness check of committed counter figures)
-SOURCES = {"hutchinson": ("k_hutch.hip", "k_spmm.hip"), "score": ("k_prune.hip",), "stats": ("k_gate.hip",),
-           "gate": ("k_gate.hip",), "pack": ("k_prune.hip",), f"spmm M={M_TOK}": ("k_spmm.hip",)}
+SOURCES = {"hutchinson+score+stats": ("k_hutch.hip", "k_spmm.hip", "k_gate.hip"), "gate": ("k_gate.hip",),
+           "pack": ("k_prune.hip",), f"spmm M={M_TOK}": ("k_spmm.hip",)}
 
 
 def main():
@@ -624,7 +633,7 @@ def main():
             f(sh)
             kev[s][j][1].record(stream)
     torch.cuda.synchronize()
-    work = algorithmic_work(st.steps)
+    work = algorithmic_work(st.steps, synth.HESSIAN24_RHO)
     kernels = []
     for j, (name, _) in enumerate(launches):
         t_s = sum(kev[s][j][0].elapsed_time(kev[s][j][1]) for s in range(args.steps)) / args.steps * 1e-3
@@ -653,7 +662,7 @@ def main():
     roof["traffic"] = traffic_for(dom["name"], SOURCES[dom["name"]])
     roof["algorithmic"] = wd.get("flops", wd.get("bytes"))
 
-    mp = [k for k in kernels if k["name"] in ("score", "stats", "gate", "pack")]
+    mp = [k for k in kernels if k["name"] in ("gate", "pack")]
     mp_bytes = sum(work[k["name"]]["bytes"] for k in mp)
     mp_us = sum(k["us"] for k in mp)
 
@@ -686,8 +695,8 @@ def main():
             what="torch.matmul (hipBLASLt) dense bf16 GEMMs of the same shapes; context only",
             spmm_dense_us=round(d_spmm, 1), spmm_sparse_us=kd[f"spmm M={M_TOK}"],
             spmm_sparse_speedup=round(d_spmm / kd[f"spmm M={M_TOK}"], 3),
-            hutchinson_dense_products_us=round(d_u + d_g, 1), hutchinson_us=kd["hutchinson"],
-            hutchinson_vs_dense=round((d_u + d_g) / kd["hutchinson"], 3))
+            hutchinson_dense_products_us=round(d_u + d_g, 1), hutchinson_score_us=kd["hutchinson+score+stats"],
+            hutchinson_vs_dense=round((d_u + d_g) / kd["hutchinson+score+stats"], 3))
         torch.cuda.empty_cache()
 
     flops_step = HUTCH_FLOPS + SPMM_DENSE_EQ

@@ -117,6 +117,23 @@ nm_status nm_hdiag_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, 
                               uint64_t seed, float* D, int64_t ldd, void* ws, size_t ws_bytes,
                               nm_stream_t stream);
 
+/* Hutchinson diagonal, score and its statistics in one pass over the curvature
+ * ("SparseForge", Methodology 2: the Hutchinson/Rademacher diagonal D of the Hessian
+ * weights the score s = (D + eps) * W^2, and the scores are standardised per tensor):
+ * S = (D + eps) * W^2 with D as nm_hdiag_hutchinson computes it and the score's
+ * arithmetic of nm_score, so S equals nm_hdiag_hutchinson followed by nm_score bit for
+ * bit; D itself is never stored.  stats (nullable, device f64 [2]): mean and population
+ * standard deviation of S as nm_score_stats gives them (combined in another fixed order:
+ * equal to about 1e-15 relative).  W: bf16 [R, K] (ldw, 8-byte aligned rows); S: f32
+ * [R, K] (lds, 16-byte aligned rows).  Requirements of nm_hdiag_hutchinson, plus
+ * probes * R * n * 2 < 2^32 (NM_ERR_SHAPE otherwise) and a 16-byte aligned workspace.
+ * ws: nm_hutchinson_score_workspace(n, K, R, probes) bytes. */
+size_t nm_hutchinson_score_workspace(int64_t n, int64_t K, int64_t R, int probes);
+nm_status nm_hutchinson_score(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes,
+                              uint64_t seed, const void* W, nm_dtype wdt, int64_t ldw, float eps,
+                              float* S, int64_t lds, double* stats, void* ws, size_t ws_bytes,
+                              nm_stream_t stream);
+
 /* ---------------------------------------------------------------- score
  * Importance score ("SparseForge", Methodology 2: s = (H + eps) * W^2 with H a
  * Hessian-diagonal approximation; "Sparse-BitNet", section 2: magnitude |W|).

@@ -55,6 +55,8 @@ SIGNATURES = {
     "nm_hdiag_colsumsq": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "nm_hutchinson_workspace": (_SZ, [_I64, _I64, _I64, _I]),
     "nm_hdiag_hutchinson": (_I, [_P, _I64, _I64, _I64, _I64, _I, _U64, _P, _I64, _P, _SZ, _P]),
+    "nm_hutchinson_score_workspace": (_SZ, [_I64, _I64, _I64, _I]),
+    "nm_hutchinson_score": (_I, [_P, _I64, _I64, _I64, _I64, _I, _U64, _P, _I, _I64, _F, _P, _I64, _P, _P, _SZ, _P]),
     "nm_score": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _F, _I, _P, _I64, _P]),
     "nm_stats_workspace": (_SZ, [_I64, _I64]),
     "nm_score_stats": (_I, [_P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
@@ -150,6 +152,20 @@ def nm_hdiag_hutchinson(X: torch.Tensor, R: int, probes: int, seed: int) -> torc
     _check(raw.nm_hdiag_hutchinson(_ptr(X), n, K, _ld(X), R, probes, seed, _ptr(D), K, _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(X)))
     return D
+
+
+def nm_hutchinson_score(X: torch.Tensor, W: torch.Tensor, probes: int, seed: int, eps: float,
+                        want_stats: bool = True):
+    """S = (D + eps) W^2 with D the Hutchinson diagonal of ||X W^T||^2 (never stored), and
+    the per-tensor (mean, std) of S: returns (S [R, K] f32, stats [2] f64 or None)."""
+    n, K = X.shape
+    R = W.shape[0]
+    S = torch.empty((R, K), dtype=torch.float32, device=X.device)
+    st = torch.empty(2, dtype=torch.float64, device=X.device) if want_stats else None
+    ws = _ws(raw.nm_hutchinson_score_workspace(n, K, R, probes), X.device)
+    _check(raw.nm_hutchinson_score(_ptr(X), n, K, _ld(X), R, probes, seed, _ptr(W), dtype_code(W), _ld(W), eps,
+                                   _ptr(S), K, _ptr(st), _ptr(ws), 0 if ws is None else ws.numel(), _stream(X)))
+    return S, st
 
 
 def nm_score(W: torch.Tensor, H: torch.Tensor | None, eps: float, mode: int = NM_SCORE_HESSIAN) -> torch.Tensor:

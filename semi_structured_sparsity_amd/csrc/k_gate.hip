@@ -39,19 +39,6 @@ __device__ __forceinline__ float load_elem(const void* p, nm_dtype dt, int64_t i
     return (float)((const int32_t*)p)[i];
 }
 
-// Moments of a thread's, a block's or the tensor's elements: count, mean, sum of
-// squared deviations.  Combined pairwise (Chan et al.'s update), always in the same
-// order, so the statistics are run-to-run identical.
-struct Moments {
-    double n, mean, m2;
-};
-__device__ __forceinline__ Moments moments_combine(Moments a, Moments b) {
-    if (a.n == 0.0) return b;
-    if (b.n == 0.0) return a;
-    const double n = a.n + b.n, d = b.mean - a.mean;
-    return Moments{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
-}
-
 // Fixed-order tree of the block's per-thread moments; the result is left in sh[*][0].
 __device__ __forceinline__ void block_moments(Moments m, double (*sh)[kRedThreads]) {
     sh[0][threadIdx.x] = m.n;
@@ -149,12 +136,12 @@ __global__ __launch_bounds__(kRedThreads) void moments_partial_kernel(const floa
 // ... in order, then the threads' moments meet in the block tree.  (A combine
 // divides in f64; a single thread folding all blocks one after another would
 // spend its time waiting on those divisions.)
-__global__ __launch_bounds__(kRedThreads) void moments_final_kernel(const double* __restrict__ part,
+__global__ __launch_bounds__(kRedThreads) void moments_final_kernel(const double* __restrict__ part, int nparts,
                                                                     double* __restrict__ stats) {
     __shared__ double sh[3][kRedThreads];
     Moments m{0.0, 0.0, 0.0};
-    for (int i = threadIdx.x; i < kRedBlocks; i += kRedThreads)
-        m = moments_combine(m, Moments{part[i], part[kRedBlocks + i], part[2 * kRedBlocks + i]});
+    for (int i = threadIdx.x; i < nparts; i += kRedThreads)
+        m = moments_combine(m, Moments{part[i], part[nparts + i], part[2 * nparts + i]});
     block_moments(m, sh);
     if (threadIdx.x == 0) {
         const double nn = sh[0][0], mean = sh[1][0], m2 = sh[2][0];
@@ -214,7 +201,11 @@ void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* sta
         hipLaunchKernelGGL(moments_partial_kernel<4>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
     else
         hipLaunchKernelGGL(moments_partial_kernel<1>, dim3(kRedBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, part);
-    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, stats);
+    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, kRedBlocks, stats);
+}
+
+void launch_moments_final(const double* part, int nparts, double* stats, hipStream_t s) {
+    hipLaunchKernelGGL(moments_final_kernel, dim3(1), dim3(kRedThreads), 0, s, part, nparts, stats);
 }
 
 void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
@@ -238,7 +229,8 @@ void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t l
 // The blend of one chosen step (m_step) is kept and written out when asked for.
 // SMAX bounds the step count at compile time so that the per-step sums live in
 // registers.  The gate uses the hardware 2^x and reciprocal (about 1 ulp each):
-// sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)).
+// sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)).  A step with beta = 1 blends nothing
+// of the sigmoid: its m is the hard target and contributes 0 to L_mid.
 __device__ __forceinline__ uint32_t group_topn_bits(const float* key, int g0, int M, int N) {
     uint32_t gb = 0;
     for (int i = 0; i < M; ++i) {
@@ -252,7 +244,7 @@ __device__ __forceinline__ uint32_t group_topn_bits(const float* key, int g0, in
     return gb;
 }
 
-template <int SMAX>
+template <int SMAX, bool HALVING>
 __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restrict__ S, int64_t R, int64_t K,
                                                            int64_t lds, const double* __restrict__ stats, int N, int M,
                                                            float T0, float rho, int steps, int m_step,
@@ -266,6 +258,10 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
     const int64_t total = R * bpr;
     float cs[SMAX], beta[SMAX];  // log2(e) / T_t and the blend factor of step t
     double lm[SMAX];
+    // HALVING (rho = 1/2): T_t halves every step, so in f32 the exponent -z log2(e) / T_t is
+    // exactly twice the previous step's (scaling by a power of two commutes with rounding)
+    // and the exponential is the previous one squared: one multiply instead of a 2^x (the
+    // product's relative error grows by at most 2^t ulps, about 4e-6 at t = 6)
 #pragma unroll
     for (int t = 0; t < SMAX; ++t) {
         const float T = T0 * powf(rho, (float)t);
@@ -309,22 +305,29 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
         float hv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = ((hbits >> i) & 1u) ? 1.0f : 0.0f;
-        float m[8], mo[8];   // m_t of the current step, and of step m_step
+        float m[8], mo[8], e[8];   // m_t of the current step and of step m_step; 2^(-z log2(e) / T_t)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = mo[i] = 0.f;
+        for (int i = 0; i < 8; ++i) m[i] = mo[i] = e[i] = 0.f;
 #pragma unroll
         for (int t = 0; t < SMAX; ++t) {
             if (t < steps) {
-                float acc = 0.f;   // <= 8 terms in [0, 1/4]: f32 here, f64 across units
+                if (beta[t] == 1.0f) {
+                    // the blend is the hard target itself (the sigmoid's weight is 0): m (1 - m) = 0
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
-                    const float g = __builtin_amdgcn_rcpf(1.0f + e);
-                    m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];
-                    const float mm = i < ne ? m[i] : 0.f;   // past the row end: adds 0
-                    acc += mm * (1.0f - mm);
+                    for (int i = 0; i < 8; ++i) m[i] = hv[i];
+                } else {
+                    float acc = 0.f;   // <= 8 terms in [0, 1/4]: f32 here, f64 across units
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (HALVING && t > 0) e[i] = e[i] * e[i];
+                        else e[i] = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
+                        const float g = __builtin_amdgcn_rcpf(1.0f + e[i]);
+                        m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];
+                        const float mm = i < ne ? m[i] : 0.f;   // past the row end: adds 0
+                        acc += mm * (1.0f - mm);
+                    }
+                    lm[t] += (double)acc;
                 }
-                lm[t] += (double)acc;
                 if (t == m_step) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) mo[i] = m[i];
@@ -386,12 +389,20 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
                  float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
                  double* lmid, void* ws, hipStream_t s) {
     double* part = (double*)ws;
-#define NM_GATE(SM)                                                                                            \
-    hipLaunchKernelGGL(gate_kernel<SM>, dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, T0, \
-                       rho, steps, m_step, m_out, ldf, hard_mask, ldm, part)
-    if (steps <= 8) NM_GATE(8);
-    else if (steps <= 16) NM_GATE(16);
-    else NM_GATE(kMaxSteps);
+#define NM_GATE(SM, HV)                                                                                             \
+    hipLaunchKernelGGL((gate_kernel<SM, HV>), dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, \
+                       T0, rho, steps, m_step, m_out, ldf, hard_mask, ldm, part)
+    const bool halving = rho == 0.5f;
+    if (steps <= 8) {
+        if (halving) NM_GATE(8, true);
+        else NM_GATE(8, false);
+    } else if (steps <= 16) {
+        if (halving) NM_GATE(16, true);
+        else NM_GATE(16, false);
+    } else {
+        if (halving) NM_GATE(kMaxSteps, true);
+        else NM_GATE(kMaxSteps, false);
+    }
 #undef NM_GATE
     hipLaunchKernelGGL(gate_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, steps, lmid);
 }

@@ -281,9 +281,38 @@ void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t
     hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 64), (unsigned)ceil_div(n, 64)), dim3(256), 0, s,
                        Xb, ldx, n, K, XT);
     // the dense split ring where it applies (aligned workspace, 32-bit offsets), else 128 x 128 tiles
-    if (launch_hutch_ring(U, XT, n, K, R, probes, seed, D, ldd, s) == NM_ERR_SHAPE)
+    if (launch_hutch_ring(U, XT, n, K, R, probes, seed, D, ldd, s, nullptr) == NM_ERR_SHAPE)
         hipLaunchKernelGGL(hutch_gemm2_kernel, dim3((unsigned)ceil_div(R, HT), (unsigned)ceil_div(K, HT)), dim3(256), 0, s,
                            (const uint16_t*)U, (const uint16_t*)XT, n, K, R, probes, seed, D, ldd);
+}
+
+// Fused diagonal -> score -> moments: the second product's epilogue writes
+// S = (D + eps) W^2 instead of D (same arithmetic as nm_score on the stored D), and the
+// per-block moments of S, which the final kernel combines into (mean, std).  Needs the
+// dense split ring (checked by the caller): no fallback kernel carries the epilogue.
+size_t hutch_score_ws(int64_t n, int64_t K, int64_t R, int probes) {
+    const size_t h = (hutch_ws(n, K, R, probes) + 255) & ~(size_t)255;
+    return h + (size_t)3 * (size_t)hutch_ring_blocks(K, R) * sizeof(double);
+}
+
+nm_status launch_hutchinson_score(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes,
+                                  uint64_t seed, const uint16_t* W, int64_t ldw, float eps, float* S, int64_t lds,
+                                  double* stats, void* ws, hipStream_t s) {
+    uint16_t* U = (uint16_t*)ws;
+    uint16_t* XT = U + (size_t)probes * (size_t)R * (size_t)n;
+    double* mpart = (double*)((uint8_t*)ws + ((hutch_ws(n, K, R, probes) + 255) & ~(size_t)255));
+    const uint16_t* Xb = (const uint16_t*)X;
+    constexpr int SR1 = 2;
+    if (launch_hutch_u_ring(Xb, ldx, n, K, R, probes, seed, U, s) == NM_ERR_SHAPE)
+        hipLaunchKernelGGL(hutch_gemm1_kernel<SR1>, dim3((unsigned)ceil_div((int64_t)probes * R, 64 * SR1), (unsigned)ceil_div(n, HT)),
+                           dim3(256), 0, s, Xb, ldx, n, K, R, probes, seed, U);
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)ceil_div(K, 64), (unsigned)ceil_div(n, 64)), dim3(256), 0, s,
+                       Xb, ldx, n, K, XT);
+    const HutchScore sc{W, ldw, eps, mpart};
+    const nm_status st = launch_hutch_ring(U, XT, n, K, R, probes, seed, S, lds, s, &sc);
+    if (st != NM_OK) return set_error(st, "nm_hutchinson_score: the dense split ring does not apply");
+    if (stats) launch_moments_final(mpart, (int)hutch_ring_blocks(K, R), stats, s);
+    return check_launch("nm_hutchinson_score");
 }
 
 }  // namespace nm

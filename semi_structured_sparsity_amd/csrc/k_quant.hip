@@ -10,19 +10,19 @@
 // column 4(N-1)g + 4w + l holds the code of column 2Ng + 2w + l (windows at offsets
 // 0, 2, .., 2N-4 of each group; for 6:8, 12g + 4w + l from 8g + 2w + l).
 //
-// One wave per token row, four rows per block: pass 1 takes the absolute maximum over
-// 16-byte loads of 8 columns and keeps up to 8 of them per lane in registers (K <= 4096
-// in one pass; longer rows re-read the rest, which is L2-resident by then); the maximum
-// is reduced across the wave; pass 2 rounds and writes each 8-column group as 12 lifted
-// bytes (three dwords; 6:8) or, without the lift, 8 bytes.  For other N, pass 2 takes one
-// window per lane: its 4 columns (two column pairs from the row, L2-resident by then),
-// rounded and written as one dword of the lifted row.
+// One block of 256 threads per token row: pass 1 takes the absolute maximum over 16-byte
+// loads of 8 columns and keeps up to 8 of them per thread in registers (K <= 16384 in one
+// pass; longer rows re-read the rest, which is L2-resident by then); the maximum is reduced
+// across the wave and then across the block's four waves; pass 2 rounds and writes each
+// 8-column group as 12 lifted bytes (three dwords; 6:8) or, without the lift, 8 bytes.
+// For other N, pass 2 takes one window per thread: its 4 columns (two column pairs from the
+// row, L2-resident by then), rounded and written as one dword of the lifted row.
 #include "nm_internal.h"
 
 namespace nm {
 
-constexpr int kQuantThreads = 256;   // four waves, one token row each
-constexpr int kQuantCache = 8;       // 8-column groups per lane kept in registers
+constexpr int kQuantThreads = 256;   // one token row per block
+constexpr int kQuantCache = 8;       // 8-column groups per thread kept in registers
 
 // OCP e4m3 code of v, |v| <= 448, finite: nearest code, ties to even.  The f32
 // exponent E picks the binade; (fraction - 1) * 8 and v * 2^9 are exact, so one
@@ -48,9 +48,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_
                                                                    int64_t Mtok, int64_t K, int Ns,
                                                                    int8_t* __restrict__ Xq, int64_t ldq,
                                                                    float* __restrict__ sx) {
-    const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
-    if (m >= Mtok) return;   // whole waves only: no barrier below
+    const int lane = threadIdx.x;   // the thread's place in the row
+    const int64_t m = blockIdx.x;
     const uint16_t* xr = X + m * ldx;
     const int64_t groups = K / 8;
     uint4 cache[kQuantCache];
@@ -66,14 +65,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_
     };
 #pragma unroll
     for (int c = 0; c < kQuantCache; ++c) {
-        const int64_t g = lane + 64 * c;
+        const int64_t g = lane + kQuantThreads * c;
         cache[c] = g < groups ? *(const uint4*)(xr + 8 * g) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < kQuantCache; ++c) absmax8(cache[c]);
-    for (int64_t g = lane + 64 * kQuantCache; g < groups; g += 64) absmax8(*(const uint4*)(xr + 8 * g));
+    for (int64_t g = lane + kQuantThreads * kQuantCache; g < groups; g += kQuantThreads)
+        absmax8(*(const uint4*)(xr + 8 * g));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float wmax[kQuantThreads / 64];
+    if ((lane & 63) == 0) wmax[lane >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);   // max: order-free
     const float s = __fdiv_rn(amax, FP8 ? 448.0f : 127.0f);
     if (lane == 0) sx[m] = s;
 
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_
     if constexpr (LIFT == 2) {
         // one window per lane: columns 2Ng + 2w .. +3 (two aligned column pairs)
         const int64_t wpr = K / (2 * Ns) * (Ns - 1);
-        for (int64_t q = lane; q < wpr; q += 64) {
+        for (int64_t q = lane; q < wpr; q += kQuantThreads) {
             const int64_t g = q / (Ns - 1), w = q - g * (Ns - 1);
             const uint32_t* src = (const uint32_t*)(xr + 2 * Ns * g + 2 * w);
             const uint32_t p0 = src[0], p1 = src[1];
@@ -120,16 +125,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_lift_kernel(const uint16_
     };
 #pragma unroll
     for (int c = 0; c < kQuantCache; ++c) {
-        const int64_t g = lane + 64 * c;
+        const int64_t g = lane + kQuantThreads * c;
         if (g < groups) emit(g, cache[c]);
     }
-    for (int64_t g = lane + 64 * kQuantCache; g < groups; g += 64) emit(g, *(const uint4*)(xr + 8 * g));
+    for (int64_t g = lane + kQuantThreads * kQuantCache; g < groups; g += kQuantThreads)
+        emit(g, *(const uint4*)(xr + 8 * g));
 }
 
 void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt, void* Xq,
                        int64_t ldq, float* x_scale, hipStream_t s) {
     if (Mtok == 0) return;
-    const dim3 g((unsigned)ceil_div(Mtok, kQuantThreads / 64)), b(kQuantThreads);
+    const dim3 g((unsigned)Mtok), b(kQuantThreads);
     const uint16_t* x = (const uint16_t*)X;
     int8_t* q = (int8_t*)Xq;
 #define NM_QL(L, F8) hipLaunchKernelGGL((quant_lift_kernel<L, F8>), g, b, 0, s, x, ldx, Mtok, K, Ns, q, ldq, x_scale)

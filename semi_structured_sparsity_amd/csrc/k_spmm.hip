@@ -96,6 +96,12 @@ struct SpmmArgs {
     uint64_t seed;
     int probes, pstages;
     int64_t prows;
+    // score epilogue of the Hutchinson second product: W [rows of D, K] bf16 (ldw), eps, and
+    // the per-block moments of the scores ([count | mean | m2][blocks])
+    const uint16_t* sw;
+    int64_t ldsw;
+    float eps;
+    double* mpart;
 };
 
 // Per-dtype step geometry of the register-staged kernel: a step stages 128 bytes of
@@ -1027,6 +1033,59 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
                           (uint32_t*)smem + wave * kStageWords<SR>, lane);
 }
 
+// Score epilogue of the Hutchinson second product (a fused diagonal -> score step): the
+// tile's D values (acc * scale, rounded to f32 as D would be stored) become
+// s = (d + eps) * (w * w) with one rounding per operation in the order t = w*w, u = d + eps,
+// s = u*t -- the score of the per-weight curvature -- and are written to S (Y, ldy) as
+// whole 16-byte runs of a row; each lane also folds its scores into moments (shifted sums
+// in f64 about its first score) for the per-tensor statistics.  Rows of the tile are D's
+// columns k (rw ..), tokens D's rows o (tw ..); K (a.R) is a multiple of 64.
+template <int SR, int ST>
+__device__ __forceinline__ Moments store_score_tile(const SpmmArgs& a, const f32x16_t (&acc)[SR][ST], int64_t rw,
+                                                    int64_t tw, uint32_t* stage, int lane) {
+    static_assert(SR == 4, "one token row of the wave's tile (4 sub-tiles) per half-wave");
+    const int h = lane >> 5, l32 = lane & 31;
+    const int ri = l32 >> 3, rq = (l32 & 7) >> 1, rh = l32 & 1;
+    double n = 0.0, s1 = 0.0, s2 = 0.0, c = 0.0;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i) *(f32x16_t*)&stage[(i * 64 + lane) * 20] = acc[i][j];
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int tk = 2 * p + h;
+            const int64_t o = tw + j * 32 + tk, k = rw + 4 * l32;
+            const uint4 raw = *(const uint4*)&stage[(ri * 64 + tk + 32 * rh) * 20 + 4 * rq];
+            if (o >= a.Mtok || k >= a.R) continue;
+            const uint2 wq = *(const uint2*)(a.sw + o * a.ldsw + k);
+            const uint32_t wb[4] = {wq.x & 0xffffu, wq.x >> 16, wq.y & 0xffffu, wq.y >> 16};
+            const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+            float sc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float d = __fmul_rn(a.w_scale, __uint_as_float(v[e]));
+                const float w = bf16_bits_to_f32(wb[e]);
+                sc[e] = __fmul_rn(__fadd_rn(d, a.eps), __fmul_rn(w, w));
+                if (n == 0.0) c = (double)sc[e];
+                const double dd = (double)sc[e] - c;
+                s1 += dd;
+                s2 += dd * dd;
+                n += 1.0;
+            }
+            *(float4*)((float*)a.Y + o * a.ldy + k) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+    Moments m{n, n > 0.0 ? c + s1 / n : 0.0, n > 0.0 ? s2 - s1 * (s1 / n) : 0.0};
+    if (m.m2 < 0.0) m.m2 = 0.0;
+    return m;
+}
+
 // ------------------------------------------------------------------ dense split ring (bf16)
 // Y = X W^T for a dense bf16 weight W [R, K] (ldv) with the split ring's tile, waves,
 // swizzles, DMA and epilogue, and dense MFMA (v_mfma_f32_32x32x16_bf16, whose operand and
@@ -1049,10 +1108,12 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
 // into the B stages (one Rademacher word per row and 64 columns; each of the 512 threads
 // expands half a stage row into swizzled 16-byte chunks); the barrier that follows every
 // stage's issue covers these LDS writes as it covers the DMA.
-// MODE: 0 plain, 1 HUTCH, 2 GEN.
+// HUTCH_SCORE: HUTCH whose epilogue writes the score of D (store_score_tile) and the block's
+// moments of it instead of D.
+// MODE: 0 plain, 1 HUTCH, 2 GEN, 3 HUTCH_SCORE.
 template <int SR, int ST, int WRN, int WTN, int MODE = 0, int SK = 64, int NS = 2>
 __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs a) {
-    constexpr bool HUTCH = MODE == 1, GEN = MODE == 2;
+    constexpr bool HUTCH = MODE == 1 || MODE == 3, GEN = MODE == 2;
     constexpr int NW = WRN * WTN, BR = WRN * SR * 32, BT = WTN * ST * 32;
     constexpr int ROWB = SK * 2, CH = ROWB / 16, D = SK / 16;   // bytes and chunks per row per stage, depths
     static_assert(SK == 64 || SK == 32, "64- or 32-column stages");
@@ -1236,8 +1297,32 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     }
     wait_vm_all();
     __syncthreads();
-    store_tile<uint16_t, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + BR <= a.R && t0 + BT <= a.Mtok,
-                                 (uint32_t*)smem + wave * kStageWords<SR>, lane);
+    if constexpr (MODE == 3) {
+        Moments m = store_score_tile<SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32,
+                                             (uint32_t*)smem + wave * kStageWords<SR>, lane);
+        // the block's moments: a fixed-order tree over its threads through LDS
+        __syncthreads();
+        double* sh = (double*)smem;   // [3][64 * NW]
+        constexpr int NT = 64 * NW;
+        sh[tid] = m.n;
+        sh[NT + tid] = m.mean;
+        sh[2 * NT + tid] = m.m2;
+        __syncthreads();
+        for (int w = NT / 2; w > 0; w >>= 1) {
+            if (tid < w) {
+                const Moments o = moments_combine(Moments{sh[tid], sh[NT + tid], sh[2 * NT + tid]},
+                                                  Moments{sh[tid + w], sh[NT + tid + w], sh[2 * NT + tid + w]});
+                sh[tid] = o.n;
+                sh[NT + tid] = o.mean;
+                sh[2 * NT + tid] = o.m2;
+            }
+            __syncthreads();
+        }
+        if (tid < 3) a.mpart[(int64_t)tid * gridDim.x + blockIdx.x] = sh[tid * NT];
+    } else {
+        store_tile<uint16_t, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + BR <= a.R && t0 + BT <= a.Mtok,
+                                     (uint32_t*)smem + wave * kStageWords<SR>, lane);
+    }
 }
 
 // ------------------------------------------------------------------ K-split ring kernel (up to 256 tokens)
@@ -2247,8 +2332,10 @@ nm_status launch_dense_ring(const uint16_t* W, int64_t ldw, const uint16_t* X, i
 }
 
 // D [R, K] (ldd) = (2/P) sum_p V_p .* (U_p X): U [P*R, n] and XT [K, n] bf16 in the workspace.
+// With sc (score epilogue): S [R, K] (ldd) = (D + eps) W^2 instead of D, and the moments of S
+// per block into sc->mpart ([3][hutch_ring_blocks(K, R)]).
 nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, int64_t K, int64_t R, int probes,
-                            uint64_t seed, float* D, int64_t ldd, hipStream_t s) {
+                            uint64_t seed, float* D, int64_t ldd, hipStream_t s, const HutchScore* sc) {
     constexpr int SR = 4, ST = 2, WRN = 2, WTN = 4, BR = WRN * SR * 32, BT = WTN * ST * 32;
     if (n % 64 || K % 64 || ((uintptr_t)U & 15u) || ((uintptr_t)XT & 15u) || (int64_t)probes * R * n * 2 >= (1LL << 32) ||
         K * n * 2 >= (1LL << 32) || (int64_t)probes * (n / 64) >= (1LL << 31))
@@ -2273,10 +2360,21 @@ nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, in
     a.tiles_r = (int)ceil_div(K, BR);
     a.tiles_t = (int)ceil_div(R, BT);
     const int64_t tiles = (int64_t)a.tiles_r * a.tiles_t;
-    hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 1, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
-                       dim3(64 * WRN * WTN), 0, s, a);
+    if (sc) {
+        a.sw = sc->W;
+        a.ldsw = sc->ldw;
+        a.eps = sc->eps;
+        a.mpart = sc->mpart;
+        hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 3, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
+                           dim3(64 * WRN * WTN), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((dense_ring_kernel<SR, ST, WRN, WTN, 1, kDenseSK, kDenseNS>), dim3((unsigned)tiles),
+                           dim3(64 * WRN * WTN), 0, s, a);
+    }
     return check_launch("nm_hdiag_hutchinson");
 }
+
+int64_t hutch_ring_blocks(int64_t K, int64_t R) { return ceil_div(K, 256) * ceil_div(R, 256); }
 
 // U [P*R, n] (bf16, row stride n) = V X^T, X [n, K] (ldx); V from the probes' Rademacher words.
 nm_status launch_hutch_u_ring(const uint16_t* X, int64_t ldx, int64_t n, int64_t K, int64_t R, int probes,

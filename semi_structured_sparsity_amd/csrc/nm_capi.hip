@@ -123,6 +123,43 @@ nm_status nm_hdiag_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, 
     return check_launch(fn);
 }
 
+size_t nm_hutchinson_score_workspace(int64_t n, int64_t K, int64_t R, int probes) {
+    if (n <= 0 || K <= 0 || R <= 0 || probes <= 0) return 0;
+    return hutch_score_ws(n, K, R, probes);
+}
+
+nm_status nm_hutchinson_score(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes, uint64_t seed,
+                              const void* W, nm_dtype wdt, int64_t ldw, float eps, float* S, int64_t lds,
+                              double* stats, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_hutchinson_score";
+    NM_REQ(n >= 0 && K >= 0 && R >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    NM_REQ(probes >= 1, NM_ERR_SHAPE, "%s: probes must be >= 1", fn);
+    NM_REQ(wdt == NM_BF16, NM_ERR_DTYPE, "%s: W must be bf16", fn);
+    if (R == 0 || K == 0) return NM_OK;
+    NM_REQ(X && W && S, NM_ERR_NULL, "%s: NULL pointer", fn);
+    NM_REQ(n >= 1, NM_ERR_SHAPE, "%s: need at least one calibration row", fn);
+    NM_REQ(ldx >= K && ldw >= K && lds >= K, NM_ERR_SHAPE, "%s: leading dimension < K", fn);
+    NM_REQ(K % 64 == 0 && n % 64 == 0 && ldx % 8 == 0 && aligned16(X), NM_ERR_ALIGN,
+           "%s: need K %% 64 == 0, n %% 64 == 0, 16-byte aligned X with ldx %% 8 == 0", fn);
+    NM_REQ(((uintptr_t)W & 7u) == 0 && ldw % 4 == 0 && aligned16(S) && lds % 4 == 0 && aligned16(ws), NM_ERR_ALIGN,
+           "%s: need 8-byte aligned W (ldw %% 4), 16-byte aligned S (lds %% 4) and workspace", fn);
+    // the fused epilogue lives in the dense split ring: its 32-bit offsets must hold
+    NM_REQ((int64_t)probes * R < (1LL << 31) && (uint64_t)R * (uint64_t)(K / 64) < (1ull << 40) &&
+               (int64_t)probes * R * n * 2 < (1LL << 32) && K * n * 2 < (1LL << 32),
+           NM_ERR_SHAPE, "%s: problem too large for the fused kernel (use nm_hdiag_hutchinson + nm_score)", fn);
+    const size_t need = hutch_score_ws(n, K, R, probes);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    const Range rs = span(S, R, K, lds, 4), rw = Range{(uintptr_t)ws, (uintptr_t)ws + need};
+    const Range rst = span(stats, 1, 2, 2, 8);
+    NM_REQ(!overlap(rs, span(X, n, K, ldx, 2)) && !overlap(rs, span(W, R, K, ldw, 2)) && !overlap(rs, rw) &&
+               !overlap(rst, rs) && !overlap(rst, rw) && !overlap(rst, span(X, n, K, ldx, 2)) &&
+               !overlap(rst, span(W, R, K, ldw, 2)) && !overlap(rw, span(X, n, K, ldx, 2)) &&
+               !overlap(rw, span(W, R, K, ldw, 2)),
+           NM_ERR_ALIAS, "%s: an output or the workspace overlaps an input", fn);
+    return launch_hutchinson_score(X, n, K, ldx, R, probes, seed, (const uint16_t*)W, ldw, eps, S, lds, stats, ws,
+                                   (hipStream_t)stream);
+}
+
 nm_status nm_score(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, const float* H, int64_t ldh,
                    float eps, nm_score_mode mode, float* S, int64_t lds, nm_stream_t stream) {
     const char* fn = "nm_score";

@@ -81,6 +81,19 @@ __device__ __forceinline__ uint4 signs_to_bf16x8(uint32_t byte) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Moments of a thread's, a block's or the tensor's elements: count, mean, sum of
+// squared deviations.  Combined pairwise (Chan, Golub and LeVeque's update), always in
+// the same order, so the statistics are run-to-run identical.
+struct Moments {
+    double n, mean, m2;
+};
+__device__ __forceinline__ Moments moments_combine(Moments a, Moments b) {
+    if (a.n == 0.0) return b;
+    if (b.n == 0.0) return a;
+    const double n = a.n + b.n, d = b.mean - a.mean;
+    return Moments{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
+}
+
 inline int index_bits(int M) {
     int b = 0;
     while ((1 << b) < M) ++b;
@@ -119,6 +132,8 @@ void launch_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, i
 size_t reduce_ws(int64_t R, int64_t K);
 size_t gate_ws(int64_t R, int64_t K, int steps);
 void launch_stats(const float* S, int64_t R, int64_t K, int64_t lds, double* stats, void* ws, hipStream_t s);
+// stats = (mean, population std) from nparts block moments laid out [count | mean | m2][nparts]
+void launch_moments_final(const double* part, int nparts, double* stats, hipStream_t s);
 void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw, float* alpha, void* ws,
                     hipStream_t s);
 void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
@@ -153,8 +168,16 @@ size_t bitmap_spmm_ws(int64_t Mtok, int64_t K, int64_t R);
 // Hutchinson second product D = (2/P) sum_p V_p .* (U_p X) on the dense split ring (U [P*R, n]
 // probes stacked along rows, XT [K, n] the transposed calibration rows); NM_ERR_SHAPE without
 // a launch when it does not apply (unaligned workspace, 32-bit offsets).
+// Score epilogue of the second product: W [R, K] bf16 (ldw), eps, block moments out.
+struct HutchScore {
+    const uint16_t* W;
+    int64_t ldw;
+    float eps;
+    double* mpart;
+};
 nm_status launch_hutch_ring(const uint16_t* U, const uint16_t* XT, int64_t n, int64_t K, int64_t R, int probes,
-                            uint64_t seed, float* D, int64_t ldd, hipStream_t s);
+                            uint64_t seed, float* D, int64_t ldd, hipStream_t s, const HutchScore* sc = nullptr);
+int64_t hutch_ring_blocks(int64_t K, int64_t R);   // blocks (and moment partials) of the score epilogue
 // Hutchinson first product U [P*R, n] (bf16, row stride n) = V X^T with the probe rows V
 // generated into the dense split ring's LDS stages; NM_ERR_SHAPE without a launch when it
 // does not apply (32-bit offsets).
@@ -167,6 +190,10 @@ nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx
                              nm_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
 // Hutchinson
 size_t hutch_ws(int64_t n, int64_t K, int64_t R, int probes);
+size_t hutch_score_ws(int64_t n, int64_t K, int64_t R, int probes);
+nm_status launch_hutchinson_score(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes,
+                                  uint64_t seed, const uint16_t* W, int64_t ldw, float eps, float* S, int64_t lds,
+                                  double* stats, void* ws, hipStream_t s);
 void launch_hutchinson(const void* X, int64_t n, int64_t K, int64_t ldx, int64_t R, int probes, uint64_t seed,
                        float* D, int64_t ldd, void* ws, hipStream_t s);
 

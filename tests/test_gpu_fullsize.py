@@ -159,11 +159,17 @@ def test_hessian24_full_size(nm):
     Sr = O.score(Wr, Dr, eps)
     assert np.array_equal(S[torch.from_numpy(rows).to(dev())].cpu().numpy(), Sr)
     del D
+    # the fused call of the benchmark's step (diagonal never stored) gives the same scores
+    Sf, stf = nm.nm_hutchinson_score(Xd, Wd, P, seed, eps)
+    assert torch.equal(Sf, S)
+    del Sf
     # per-tensor statistics of S, then the gate fed those statistics
     st = nm.nm_score_stats(S).cpu().numpy()
     Sh = S.cpu().numpy()
     mu, sg = O.stats(Sh)
     assert abs(st[0] - mu) <= 1e-12 * abs(mu) and abs(st[1] - sg) <= 1e-12 * sg
+    stf = stf.cpu().numpy()
+    assert abs(stf[0] - mu) <= 1e-12 * abs(mu) and abs(stf[1] - sg) <= 1e-12 * sg
     del Sh
     stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
     T0, rho, steps = synth.HESSIAN24_T0, synth.HESSIAN24_RHO, synth.HESSIAN24_STEPS

@@ -97,6 +97,47 @@ def test_hutchinson_long_rows_use_register_generating_kernel(nm):
     assert np.array_equal(D[rows].astype(np.float64), O.hutchinson_rows(Xb, P, seed, rows))
 
 
+# the fused diagonal -> score -> statistics call: K a multiple of 64 but not of the 256-column
+# tile, rows past a tile, one and several probes
+@pytest.mark.parametrize("n,K,R,P", [(64, 128, 70, 1), (128, 320, 300, 8), (192, 256, 520, 3)])
+def test_hutchinson_score_fused_equals_separate_calls(nm, n, K, R, P):
+    g = np.random.default_rng(n * 3 + K + R)
+    Xb = O.f32_to_bf16(g.standard_normal((n, K)))
+    Wb = O.f32_to_bf16(g.standard_normal((R, K)) * 0.02)
+    Xd, Wd = np_bf16(Xb).to(dev()), np_bf16(Wb).to(dev())
+    seed, eps = 19, 1e-6
+    S, st = nm.nm_hutchinson_score(Xd, Wd, P, seed, eps)
+    D = nm.nm_hdiag_hutchinson(Xd, R, P, seed)
+    S2 = nm.nm_score(Wd, D, eps)
+    assert torch.equal(S, S2)                       # same D, same score arithmetic
+    st2 = nm.nm_score_stats(S2).cpu().numpy()
+    mu, sg = O.stats(S.cpu().numpy())
+    st = st.cpu().numpy()
+    assert abs(st[0] - mu) <= 1e-12 * abs(mu) and abs(st[1] - sg) <= 1e-12 * sg
+    assert abs(st[0] - st2[0]) <= 1e-13 * abs(mu) and abs(st[1] - st2[1]) <= 1e-13 * sg
+    # and S against the oracle's score of the oracle's rows of D, to the Hutchinson bound
+    rows = np.unique(np.r_[0, R - 1, g.integers(0, R, 8)])
+    ref_d = O.hutchinson_rows(Xb, P, seed, rows)
+    d_gpu = D[torch.from_numpy(rows).to(dev())].cpu().numpy()
+    assert np.array_equal(S.cpu().numpy()[rows], O.score(Wb[rows], d_gpu, eps))
+    U = O.hutchinson_u_rows(Xb, P, seed, rows)
+    xk = np.sqrt((O.bf16_to_f32(Xb).astype(np.float64) ** 2).sum(0))
+    tol = 2e-2 * (2.0 / P) * np.sqrt((U ** 2).sum(-1)).sum(1)[:, None] * xk[None, :]
+    assert (np.abs(d_gpu - ref_d) <= tol).all()
+
+
+def test_hutchinson_score_without_stats_and_rejections(nm):
+    g = np.random.default_rng(2)
+    n, K, R, P = 64, 128, 40, 2
+    Xd = np_bf16(O.f32_to_bf16(g.standard_normal((n, K)))).to(dev())
+    Wd = np_bf16(O.f32_to_bf16(g.standard_normal((R, K)))).to(dev())
+    S, st = nm.nm_hutchinson_score(Xd, Wd, P, 7, 1e-6, want_stats=False)
+    assert st is None
+    assert torch.equal(S, nm.nm_score(Wd, nm.nm_hdiag_hutchinson(Xd, R, P, 7), 1e-6))
+    with pytest.raises(nm.NMError):   # f32 weights are not taken
+        nm.nm_hutchinson_score(Xd, Wd.float(), P, 7, 1e-6)
+
+
 def test_stats_and_gate(nm):
     g = np.random.default_rng(8)
     R, K, steps = 96, 512, 8
