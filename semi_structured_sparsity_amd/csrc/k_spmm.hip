@@ -949,15 +949,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
         const uint8_t* sA = smem + RG::A_OFF + (g & 1) * RG::AGRP;
         const uint32_t* sI = (const uint32_t*)(smem + RG::I_OFF + (j & 1) * RG::IGRP);
         const uint8_t* sB = smem + RG::X_OFF + (s & 1) * RG::XSTAGE;
-#pragma unroll
-        for (int i = 0; i < SR; ++i) {
-            const int row = (wr * SR + i) * 32 + l32;
-            f.a[i] = *(const i32x4_t*)(sA + row * 128 + ((4 * ss + 2 * d + h) ^ RG::swa(row)) * 16);
-            // index word w of the row's group
-            const int w = si * RG::AI + (sizeof(T) == 2 ? d : 2 * d + h);
-            if constexpr (IP == 4) f.iw[i] = sI[row * 16 + (w ^ iswz<16>(row))];
-            else f.iw[i] = sI[row * 16 + ((w >> 2) ^ RG::swi(row)) * 4 + (w & 3)];
-        }
+        // X pieces first: a depth's first SMFMAC then waits only for the earliest reads
 #pragma unroll
         for (int jj = 0; jj < ST; ++jj) {
             const int tok = (wt * ST + jj) * 32 + l32;
@@ -966,6 +958,15 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
             const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ sw) * 16);
             const i32x4_t hi = *(const i32x4_t*)(trow + ((4 * d + 2 + h) ^ sw) * 16);
             f.b[jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int i = 0; i < SR; ++i) {
+            const int row = (wr * SR + i) * 32 + l32;
+            f.a[i] = *(const i32x4_t*)(sA + row * 128 + ((4 * ss + 2 * d + h) ^ RG::swa(row)) * 16);
+            // index word w of the row's group
+            const int w = si * RG::AI + (sizeof(T) == 2 ? d : 2 * d + h);
+            if constexpr (IP == 4) f.iw[i] = sI[row * 16 + (w ^ iswz<16>(row))];
+            else f.iw[i] = sI[row * 16 + ((w >> 2) ^ RG::swi(row)) * 4 + (w & 3)];
         }
     };
 
@@ -996,6 +997,19 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
     issue_x(0);
     wait_vm_barrier<0>();
     read_depth(0, 0, fa);
+    // a depth's fragment reads (SR value pieces, SR index words, 2 ST X pieces) spread over
+    // the first SMFMACs of the previous depth, in a scheduling region of their own
+    auto interleave = [&]() __attribute__((always_inline)) {
+        constexpr int NR = 2 * SR + 2 * ST, RPM = 3;
+        static_assert(NR % RPM == 0 && NR / RPM <= SR * ST, "reads spread over the depth's SMFMACs");
+#pragma unroll
+        for (int i = 0; i < NR / RPM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, SR * ST - NR / RPM, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     for (int g = 0; g < NG; ++g) {
         const int s0 = 2 * g;
         const bool more = g + 1 < NG;                     // X 2g+2, values g+1 exist
@@ -1005,15 +1019,21 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void spmm_ring2_kernel(SpmmArgs 
         if (it) issue_i(g / RG::IB + 1, g % RG::IB);
         read_depth(s0, 1, fb);
         mfmas(fa);
+        interleave();
         // mid(g): X s0+1 done; the values and index batch of top(g) may stay in flight
         if (more && it) wait_vm_barrier<NAG + NIG>();
         else if (more) wait_vm_barrier<NAG>();
         else wait_vm_barrier<0>();
-        read_depth(s0 + 1, 0, fa);
         if (more) issue_x(s0 + 2);
+        read_depth(s0 + 1, 0, fa);
         mfmas(fb);
+        interleave();
         read_depth(s0 + 1, 1, fb);
         mfmas(fa);
+        interleave();
+        // fb complete before the branch (the barrier in it waits for them anyway), so the
+        // SMFMACs after the join wait for nothing
+        __builtin_amdgcn_s_waitcnt(0xc07f);
         if (more) {
             // top(g+1): X s0+2 was the last load issued, so everything is waited for
             wait_vm_barrier<0>();
@@ -1247,6 +1267,17 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         }
     };
     constexpr int PER = NWL + (GEN ? 0 : NXL);   // DMA loads per stage
+    // a depth's SR + ST fragment reads, one after each of its first SR + ST MFMAs (in the
+    // scheduling region that holds them)
+    auto interleave_reads_mfmas = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SR + ST; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, SR * ST - (SR + ST), 0);
+        __builtin_amdgcn_sched_barrier(0);   // the next depth is a region of its own
+    };
     // Prologue: stages 0..NS-1 fill the ring; wait for stage 0 (the others may stay in
     // flight) and read its depth 0.  Each depth's fragments are read while the previous
     // depth's MFMAs issue; the last depth of stage s waits for stage s+1 (stages s+2 ..
@@ -1279,15 +1310,21 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         for (int d = 0; d < D; ++d) {
             if (d + 1 < D) {
                 read_depth(s, d + 1, fr[(d + 1) & 1]);
-            } else if (s + 1 < nsteps) {
-                // stage s+1 landed (the loads of s+2 .. s+NS-1 may stay in flight) and stage s
-                // read by every wave
-                if (s + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * PER>();
-                else wait_vm_barrier<0>();
-                if (s + NS < nsteps) issue(s + NS);
-                read_depth(s + 1, 0, fr[0]);
+            } else {
+                // the last depth's fragments complete before the branch (the barrier below
+                // waits for them anyway), so the MFMAs after the join wait for nothing
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                if (s + 1 < nsteps) {
+                    // stage s+1 landed (the loads of s+2 .. s+NS-1 may stay in flight) and
+                    // stage s read by every wave
+                    if (s + NS - 1 < nsteps) wait_vm_barrier<(NS - 2) * PER>();
+                    else wait_vm_barrier<0>();
+                    if (s + NS < nsteps) issue(s + NS);
+                    read_depth(s + 1, 0, fr[0]);
+                }
             }
             mfmas(fr[d & 1]);
+            if (d + 1 < D) interleave_reads_mfmas();
         }
     }
     if constexpr (HUTCH) {   // acc *= s_{P-1}
@@ -2297,7 +2334,13 @@ nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ld
 // Stage width and ring depth of the dense split ring (Hutchinson's products, bitmap decode).
 // Measured on the Hutchinson call at 28672 x 8192, n = 1024, 8 probes (same result bit for
 // bit): 64-column stages in 2 slots 7.17 ms, 32-column stages in 4 slots 7.68 ms, in 5
-// slots 7.73 ms -- more bytes in flight do not help; the extra barriers cost.
+// slots 7.73 ms -- more bytes in flight do not help; the extra barriers cost.  Neither did
+// an L2 prefetch of the next stage's lines (one dword per line, 7.05 against 6.82 ms), nor
+// four waves of 128 x 128 per tile with AGPR accumulators (a dense 28672 x 8192 product at
+// 8192 tokens: 4.13 against 3.52 ms; one wave per SIMD leaves nothing to cover the waits).
+// Under this load the clock falls to 1.6-1.8 GHz (GRBM cycles over the dispatch time); a
+// copy that skips the stage loads runs at 1.9-2.1 GHz: the operand traffic costs power as
+// well as issue slots, and a 256 x 256 tile is the largest two waves per SIMD can hold.
 constexpr int kDenseSK = 64, kDenseNS = 2;
 
 // Y [Mtok, R] (ydt bf16 or f32, ldy) = X [Mtok, K] (ldx) W^T, W [R, K] (ldw) dense bf16.
