@@ -246,12 +246,14 @@ nm_status nm_prune_slide(const void* Wsc, nm_dtype sdt, int64_t ldsc, const floa
  *                  q = the e4m3 code nearest X[m,k] / x_scale[m] (ties to even; the
  *                  quotient is within 448, and is clamped to it);
  *   a zero row gives x_scale = 0 and codes 0.
- * Written lifted when Ns == 4: Xq[m, 12g + 4w + l] = q[m, 8g + 2w + l], i.e.
- * one byte per code, [Mtok, K' = 3K/2] (ldq >= K'), the activation nm_spmm
+ * Written lifted when Ns >= 3 ((2Ns-2):2Ns, 3 <= Ns <= 8): window w of group g
+ * (Ns - 1 windows of 4 codes per group of 2Ns) is Xq[m, 4(Ns-1)g + 4w + l] =
+ * q[m, 2Ns g + 2w + l] -- for Ns == 4 (6:8) Xq[m, 12g + 4w + l] = q[m, 8g + 2w + l] --
+ * one byte per code, [Mtok, K' = (2 - 2/Ns) K] (ldq >= K'), the activation nm_spmm
  * multiplies with Ns = 0 over K' against a slide-decomposed weight; Ns == 0
- * writes q as is (ldq >= K).  Requires K % 8 == 0, X 16-byte aligned with
- * 16-byte row strides, Xq 4-byte (lifted) or 8-byte aligned rows.  x_scale:
- * device f32 [Mtok].  Allocates nothing. */
+ * writes q as is (ldq >= K).  Requires K % 8 == 0 and K % 2Ns == 0, X 16-byte
+ * aligned with 16-byte row strides, Xq 4-byte (lifted) or 8-byte aligned rows.
+ * x_scale: device f32 [Mtok].  Allocates nothing. */
 nm_status nm_quant_lift(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt,
                         void* Xq, int64_t ldq, float* x_scale, nm_stream_t stream);
 
@@ -264,13 +266,14 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
 
 /* ---------------------------------------------------------------- sparse GEMM
  * Structured-sparse linear layer Y = X * W_hat^T on packed weights
- * ("SlideSparse", sections 2B-2C: the lifted activation is an index remap,
- * written once into the workspace here; the product then runs on 2:4 sparse
- * matrix instructions).  Runs on gfx950 SMFMAC (the packed weight is the
- * sparse operand).
+ * ("SlideSparse", sections 2B-2C: the lifted activation is an index remap of X;
+ * the product then runs on 2:4 sparse matrix instructions).  Runs on gfx950
+ * SMFMAC (the packed weight is the sparse operand).  With Ns == 4 (6:8) and up to
+ * 256 tokens (bf16) or 64 (one-byte codes) the lift happens inside the product's
+ * activation loads; otherwise X is lifted once into the workspace.
  *   X: [Mtok, K] (ldx elements), K the ORIGINAL input width.
  *   vals/idx: 2:4 packed weight over K (Ns == 0) or over the lifted width
- *   K' = (2 - 2/Ns) K (Ns >= 3; supported Ns == 4, i.e. 6:8), rows R;
+ *   K' = (2 - 2/Ns) K ((2Ns-2):2Ns, 3 <= Ns <= 8), rows R;
  *   ldv >= K'/2, ldi >= ceil(K'/32).
  *   xdt/vdt: BF16/BF16 (f32 accumulation), I8/I8 (exact int32 accumulation) or
  *   FP8/FP8 (e4m3 codes; exact products, f32 accumulation).
@@ -278,12 +281,14 @@ nm_status nm_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t 
  *   for FP8 inputs F32 or BF16.
  *   Float outputs are y = acc when x_scale == NULL and w_scale == 1, else
  *   y = (w_scale * x_scale[m]) * acc in f32 (x_scale NULL counts as 1).
- *   Requires K % 16 (bf16) or K % 32 (one-byte types) == 0 for Ns == 0, and
- *   K % 32 (bf16) or K % 64 (one-byte types) == 0 for Ns == 4.
+ *   Requires K % 2Ns == 0 (Ns >= 3) and K' a multiple of 16 (bf16) or 32 (one-byte
+ *   types), K' = K for Ns == 0 (NM_ERR_SHAPE otherwise).
  *   int8 requires K' * 127 * 127 < 2^31 so that int32 accumulation is exact.
- * ws: nm_spmm_workspace(...) bytes: 0 for most plain 2:4 shapes; split-K partials for
- * few tokens on few rows; for 6:8, the lifted activation
- * [Mtok, K'] that the plain kernels then multiply. */
+ * ws: nm_spmm_workspace(...) bytes, 16-byte aligned (NM_ERR_ALIGN otherwise): 0 for most
+ * plain 2:4 shapes; the split-K partials for few tokens on few rows (summed in split order
+ * by a second kernel); the lifted activation [Mtok, K'] where the lift is not done in the
+ * product.  Its contents need not be initialised, but one workspace must not serve two
+ * calls that may overlap. */
 size_t nm_spmm_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt);
 nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t ldx,
                   const void* vals, nm_dtype vdt, const uint32_t* idx, int64_t R, int64_t ldv, int64_t ldi,
@@ -318,15 +323,16 @@ nm_status nm_spmm_noalloc(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, 
  *   Y = X W_hat^T + u B^T,   u = bf16(X A^T)   (u rounded once to nearest even from its
  *   f32 sum; every other sum in f32, output rounded once to ydt).
  *   X: bf16 [Mtok, K] (ldx), K the original width; vals/idx: bf16 2:4 packed weight as for
- *   nm_spmm (Ns 0, or 4 for 6:8 over K' = 3K/2); A: bf16 [rank, K] (lda), the stacked
+ *   nm_spmm (Ns 0, or 3 <= Ns <= 8 over K' = (2 - 2/Ns) K); A: bf16 [rank, K] (lda), the stacked
  *   down-projections; B: bf16 [R, rank] (ldb), the stacked up-projections (the row-major
  *   weights of a LoRA pair of linear layers).  rank: a multiple of 8 in [8, 256].
  *   Y: [Mtok, R] (ldy), bf16 or f32.  No scales.
- *   Requires K % 16 (Ns 0) or K % 32 (Ns 4) == 0; X, vals, idx, A and B 16-byte aligned
- *   with 16-byte row strides.
- * ws: nm_spmm_lowrank_workspace(Mtok, K, R, Ns, rank) bytes (u and its K-split partials,
- * the lifted activation for Ns 4, and for products that are not run by the many-token
- * kernels an f32 copy of the sparse product).  Allocates nothing. */
+ *   Requires K % 16 == 0, and for Ns >= 3 K % 2Ns == 0 and K' % 16 == 0; X, vals, idx, A
+ *   and B 16-byte aligned with 16-byte row strides.
+ * ws: nm_spmm_lowrank_workspace(Mtok, K, R, Ns, rank) bytes, 16-byte aligned (u and its
+ * K-split partials, the sparse product's own workspace as for nm_spmm, and for products
+ * that are not run by the many-token kernels an f32 copy of the sparse product).
+ * Allocates nothing. */
 size_t nm_spmm_lowrank_workspace(int64_t Mtok, int64_t K, int64_t R, int Ns, int rank);
 nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, const void* vals, const uint32_t* idx,
                           int64_t R, int64_t ldv, int64_t ldi, int Ns, const void* A, int64_t lda, const void* B,

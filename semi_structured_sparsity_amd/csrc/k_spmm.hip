@@ -1378,22 +1378,40 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
 // lifted B fragment from the slot: window w of group q is original columns 8q + 2w .. +3,
 // i.e. dwords w, w+1 of the group's 16 bytes (bf16) or bytes 2w .. 2w+3 of its 8 (one-
 // byte codes: one byte-aligned funnel shift of the group's two dwords).
-template <typename T, int SR, int ST, int KB, int NS, bool LIFT = false>
+// XRES (up to 32 tokens, no lift): the block's X range -- its valid token rows, the
+// columns of its stages -- is loaded into LDS once, ahead of the ring, and the ring carries
+// the weight alone.  Under a full-chip weight stream a load from HBM takes about 4 us, so a
+// CU's share of the bandwidth needs about 100 KB of weight in flight; with 32 token rows of
+// X in every stage (one token valid at M = 1) a 6-stage ring held about 50 KB.  X rows sit
+// 16 bytes apart beyond whole KB (16 lanes reading 16 tokens at one column hit distinct
+// banks); token slots past the last valid token read the last valid row (their sums are
+// never stored).
+// Measured on 4096 x 4096 and 11008 x 4096 at 1 and 16 tokens: 6-8% faster than X in the
+// ring.  A 14-stage weight ring with 16 KB of resident rows and no K split was slower (the
+// 11008-row weight at one token: 17.8 against 16.2 us); reading that weight alone in the
+// same stage order takes about 10 us.
+constexpr int kXresBytes = 64 * 1024 + 32 * 16;
+
+template <typename T, int SR, int ST, int KB, int NS, bool LIFT = false, int XRB_ = 0>
 __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
+    constexpr bool XRES = XRB_ > 0;
     constexpr int es = sizeof(T);
     constexpr int KO = KB / es, KDEP = es == 2 ? 32 : 64;
     static_assert(KO / KDEP == 4, "one depth per wave per stage");
+    static_assert(!(LIFT && XRES), "the resident X holds original columns of the unlifted product only");
     constexpr int BR = 32 * SR, BT = 32 * ST;
     constexpr int AROW = KO / 2 * es, ACH = AROW / 16, AI = KO / 32, BCH = KB / 16;
     static_assert(ACH == 8 && BCH == 16, "swizzles below are for 8-chunk weight rows and 16-chunk X rows");
-    constexpr int I_OFF = BR * AROW, B_OFF = I_OFF + BR * AI * 4, STAGE = B_OFF + BT * KB;
-    constexpr int NA = BR * AROW / 1024 / 4, NI = BR * AI * 4 / 256 / 4, NB = BT * KB / 1024 / 4;
+    constexpr int I_OFF = BR * AROW, B_OFF = I_OFF + BR * AI * 4, STAGE = B_OFF + (XRES ? 0 : BT * KB);
+    constexpr int NA = BR * AROW / 1024 / 4, NI = BR * AI * 4 / 256 / 4, NB = XRES ? 0 : BT * KB / 1024 / 4;
     constexpr int PER = NA + NI + NB;   // loads per wave per stage
-    static_assert(NA >= 1 && NI >= 1 && NB >= 1 && (BR * AROW) % 4096 == 0 && (BR * AI * 4) % 1024 == 0 &&
+    static_assert(NA >= 1 && NI >= 1 && (XRES || NB >= 1) && (BR * AROW) % 4096 == 0 && (BR * AI * 4) % 1024 == 0 &&
                       (BT * KB) % 4096 == 0,
                   "loads must split evenly over the 4 waves");
+    static_assert(!XRES || ST == 1, "resident X for up to 32 tokens");
+    constexpr int X_OFF = NS * STAGE, XRB = XRB_;
     constexpr int RED = 4 * 64 * 16 * 4;                // one sub-tile of all four waves
-    constexpr int LDS = NS * STAGE > RED ? NS * STAGE : RED;
+    constexpr int LDS = X_OFF + XRB > RED ? X_OFF + XRB : RED;
     static_assert(LDS <= 160 * 1024, "LDS ring too large");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
@@ -1415,7 +1433,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
     const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
-    uint32_t oA[NA], oI[NI], oB[NB], oBc[NB];
+    uint32_t oA[NA], oI[NI], oB[NB > 0 ? NB : 1], oBc[NB > 0 ? NB : 1];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int q = (wave * NA + i) * 64 + lane;
@@ -1451,7 +1469,9 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int i = 0; i < NA; ++i) dma16s(st + (wave * NA + i) * 1024, baseA, oA[i] + (uint32_t)(sg * AROW));
 #pragma unroll
         for (int i = 0; i < NI; ++i) dma4s(st + I_OFF + (wave * NI + i) * 256, baseI, oI[i] + (uint32_t)(sg * AI * 4));
-        if constexpr (LIFT) {
+        if constexpr (XRES) {
+            // X is resident
+        } else if constexpr (LIFT) {
             const uint32_t xs = slot_start(sg);
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
@@ -1463,6 +1483,10 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
             for (int i = 0; i < NB; ++i) dma16s(st + B_OFF + (wave * NB + i) * 1024, baseB, oB[i] + (uint32_t)(sg * KB));
         }
     };
+    // XRES: valid token rows of the tile, padded LDS row bytes of the resident X
+    const int xmv = XRES ? (int)(a.Mtok - t0 < BT ? a.Mtok - t0 : BT) : 0;
+    const int xcpr = XRES ? (nloc * KB + 1023) / 1024 : 0;   // 1 KB loads per row
+    const int xrowp = xcpr * 1024 + 16;
     struct Frag {
         i32x4_t a[SR];
         uint32_t iw[SR];
@@ -1531,7 +1555,12 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
         for (int j = 0; j < ST; ++j) {
             const int tok = j * 32 + l32;
             const uint8_t* trow = sB + tok * KB;
-            if constexpr (LIFT) {
+            if constexpr (XRES) {
+                const uint8_t* xr = smem + X_OFF + (tok < xmv ? tok : xmv - 1) * xrowp + sl * KB;
+                const i32x4_t lo = *(const i32x4_t*)(xr + (4 * d + h) * 16);
+                const i32x4_t hi = *(const i32x4_t*)(xr + (4 * d + 2 + h) * 16);
+                f.b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else if constexpr (LIFT) {
                 f.b[j] = lifted_frag(trow, swb(tok), s_begin + sl);
             } else {
                 const i32x4_t lo = *(const i32x4_t*)(trow + ((4 * d + h) ^ swb(tok)) * 16);
@@ -1561,6 +1590,21 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     // stage S's slot has been read by all), refills that slot with stage S+NS and reads
     // stage S+1 into the other fragment set.
     Frag fa, fb;
+    if constexpr (XRES) {
+        // the tile's X range ahead of the ring's first stages (so the wait for stage 0 covers
+        // it): row t, 1 KB piece c; lanes past the range reload its last 16 bytes into the
+        // row's padding.  The caller guarantees xmv * xrowp <= XRB; rows that would not fit
+        // are not loaded.
+        const int rows = xmv * xrowp <= XRB ? xmv : XRB / xrowp;
+        const uint32_t kbytes = (uint32_t)(nloc * KB);
+        for (int q = wave; q < rows * xcpr; q += 4) {
+            const int t = q / xcpr, c = q - t * xcpr;
+            uint32_t off = (uint32_t)(c * 1024 + lane * 16);
+            off = off < kbytes - 16 ? off : kbytes - 16;
+            dma16s(sbase + (uint32_t)(X_OFF + t * xrowp + c * 1024), baseB,
+                   (uint32_t)(t * a.ldx * es) + (uint32_t)(s_begin * KB) + off);
+        }
+    }
 #pragma unroll
     for (int p = 0; p < NS; ++p)
         if (p < nloc) issue(p);
@@ -1890,6 +1934,7 @@ struct SpmmPlan {
     int64_t split_rows;  // > 0: big tiles on rows [0, split_rows), narrow tiles on the rest
     int mid;     // K-split ring: 0 none, else 32-token sub-tiles per block (1, 2 or 4)
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
+    int xres;    // K-split ring with X resident in LDS (up to 64 KB, 8-stage weight ring)
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
@@ -1914,7 +1959,7 @@ static int64_t device_cus() {
 }
 
 template <typename T>
-static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok) {
+static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok, bool xres_ok = true) {
     using G = Geo<T>;
     SpmmPlan p{};
     // up to 256 tokens: the K-split ring kernel on 64 x 32, 64 x 64 or 64 x 128 tiles, with
@@ -1933,6 +1978,13 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok) {
             while ((int64_t)p.tiles_r * p.tiles_t * KS < 160 && p.nsteps >= 8 * KS) KS *= 2;
             p.steps_per_split = (int)ceil_div(p.nsteps, KS);
             p.KS = (int)ceil_div(p.nsteps, p.steps_per_split);
+            // up to 32 tokens of an unlifted X whose range per block fits 64 KB: X resident in
+            // LDS, an 8-stage weight ring
+            p.xres = 0;
+            if (xres_ok && p.mid == 1) {
+                const int64_t rows = Mtok < 32 ? Mtok : 32;
+                if (rows * (ceil_div((int64_t)p.steps_per_split * 256, 1024) * 1024 + 16) <= kXresBytes) p.xres = 1;
+            }
             return p;
         }
     }
@@ -2113,7 +2165,8 @@ static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtyp
     }
     if (Ns && !fused) w.xl = lift_bytes(Mtok, K, Ns, es);
     // the plan depends on the element size only (int8 and FP8 share it)
-    const SpmmPlan p = es == 2 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok) : plan_for<int8_t>(Mtok, Kl, R, ring_ok);
+    const SpmmPlan p = es == 2 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok, !fused)
+                               : plan_for<int8_t>(Mtok, Kl, R, ring_ok, !fused);
     if (rank > 0 && !p.ring) w.f32 = round256((size_t)Mtok * (size_t)R * 4);
     if (p.KS > 1) w.part = round256((size_t)p.KS * (size_t)Mtok * (size_t)R * 4);
     return w;
@@ -2124,7 +2177,7 @@ static SpmmWs spmm_ws_layout(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtyp
 // (both carved from the workspace by the caller, sized by spmm_ws_layout)
 template <typename T>
 static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void* f32buf, hipStream_t s) {
-    const SpmmPlan p = plan_for<T>(a.Mtok, a.K, a.R, ring_ok);
+    const SpmmPlan p = plan_for<T>(a.Mtok, a.K, a.R, ring_ok, !lift);
     a.nsteps = p.nsteps;
     a.KS = p.KS;
     a.steps_per_split = p.steps_per_split;
@@ -2159,7 +2212,9 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void*
             else
                 return set_error(NM_ERR_DEVICE, "nm_spmm: no in-kernel lift for one-byte codes on 128-token tiles");
         } else {
-            if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6>), grid, dim3(256), 0, s, a);
+            if (p.xres)
+                hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 8, false, kXresBytes>), grid, dim3(256), 0, s, a);
+            else if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6>), grid, dim3(256), 0, s, a);
             else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 4, 256, 3>), grid, dim3(256), 0, s, a);
         }

@@ -519,6 +519,7 @@ nm_status nm_spmm(const void* X, nm_dtype xdt, int64_t Mtok, int64_t K, int64_t 
     const Range ry = span(Y, Mtok, R, ldy, esize(ydt));
     const size_t need = spmm_ws(Mtok, K, R, Ns, xdt);
     NM_REQ(need == 0 || (ws && ws_bytes >= need), NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(need == 0 || aligned16(ws), NM_ERR_ALIGN, "%s: ws must be 16-byte aligned", fn);
     if (need) NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
     return launch_spmm(X, xdt, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, x_scale, w_scale, Y, ydt, ldy, ws, ws_bytes,
                        (hipStream_t)stream);
@@ -628,6 +629,7 @@ nm_status nm_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ldx, c
            NM_ERR_ALIAS, "%s: Y overlaps an input", fn);
     const size_t need = spmm_lowrank_ws(Mtok, K, R, Ns, rank);
     NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    NM_REQ(aligned16(ws), NM_ERR_ALIGN, "%s: ws must be 16-byte aligned", fn);
     NM_REQ(!overlap(ry, Range{(uintptr_t)ws, (uintptr_t)ws + need}), NM_ERR_ALIAS, "%s: Y overlaps ws", fn);
     const LowRankIn lr{(const uint16_t*)A, lda, (const uint16_t*)B, ldb, rank};
     return launch_spmm_lowrank(X, Mtok, K, ldx, vals, idx, R, ldv, ldi, Ns, lr, Y, ydt, ldy, ws, ws_bytes,

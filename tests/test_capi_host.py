@@ -117,6 +117,14 @@ def test_validation_errors_without_gpu(nm):
     assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, ctypes.c_void_p(0x1008), 64, S, 16, 16, Y, 1, 8, S, 1 << 30,
                       None)) == "NM_ERR_ALIGN"
     assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 16, Y, 1, 8, S, 16, None)) == "NM_ERR_WORKSPACE"
+    assert _st(nm, lr(S, 4, 64, 64, S, S, 8, 32, 4, 0, S, 64, S, 16, 16, Y, 1, 8, ctypes.c_void_p(0x40000008), 1 << 30,
+                      None)) == "NM_ERR_ALIGN"
+    # a product that needs a workspace (few tokens: K split over blocks) takes it 16-byte aligned
+    need = r.nm_spmm_workspace(4, 4096, 256, 0, nm.NM_BF16)
+    assert need > 0
+    assert _st(nm, r.nm_spmm(S, 1, 4, 4096, 4096, ctypes.c_void_p(0x10000000), 1, ctypes.c_void_p(0x20000000), 256,
+                             2048, 128, 0, None, 1.0, ctypes.c_void_p(0x30000000), 1, 256, ctypes.c_void_p(0x40000008),
+                             need, None)) == "NM_ERR_ALIGN"
     # bitmap format: K a multiple of 64, bf16 weights, 8-byte aligned mask rows
     assert _st(nm, r.nm_bitmap_encode(S, 1, 4, 96, 96, S, 12, Y, 96, S, 3, None)) == "NM_ERR_SHAPE"
     assert _st(nm, r.nm_bitmap_encode(S, 0, 4, 64, 64, S, 8, Y, 64, S, 2, None)) == "NM_ERR_DTYPE"

@@ -110,9 +110,12 @@ def test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns):
     assert np.array_equal(Y.astype(np.float64), ref)
 
 
-# 1 to 4 tokens: K of 16 or 48 columns (one or three 16-column chunks, an odd index
-# word), K off the rings' stage grid, a K split over blocks, one row
-FEW = [(1, 1, 16), (2, 300, 48), (3, 257, 4160), (4, 130, 32), (1, 513, 2560), (4, 64, 4096), (1, 1000, 96)]
+# 1 to 32 tokens: K of 16 or 48 columns (one or three 16-column chunks, an odd index
+# word), K off the rings' stage grid, a K split over blocks, one row, the X range of a
+# block held in LDS
+FEW = [(1, 1, 16), (2, 300, 48), (3, 257, 4160), (4, 130, 32), (1, 513, 2560), (4, 64, 4096), (1, 1000, 96),
+       (32, 200, 4096), (17, 130, 2048),   # X resident in LDS: a full 64 KB range, and 17 valid rows
+       (1, 4096, 4096), (2, 4100, 4096)]   # resident X rows of the whole K on many row tiles
 
 
 @pytest.mark.parametrize("Mt,R,K", FEW)
@@ -148,7 +151,7 @@ def test_spmm_bf16_random_tolerance(nm, Mt, R, K, Ns):
 
 
 @pytest.mark.parametrize("Mt,R,K", [(1, 70, 2560), (33, 96, 256), (256, 130, 512), (300, 64, 2560),
-                                    (20, 100, 192), (70, 90, 128)])
+                                    (20, 100, 192), (70, 90, 128), (1, 4160, 2560)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_spmm_int8_exact(nm, Mt, R, K, Ns):
     g = np.random.default_rng(Mt + R + K + Ns)
@@ -340,3 +343,75 @@ def test_spmm_deterministic(nm):
     a = nm.nm_spmm(Xd, v, i, ydt=nm.NM_F32)
     b = nm.nm_spmm(Xd, v, i, ydt=nm.NM_F32)
     assert torch.equal(a, b)
+
+
+# few-token shapes whose K is split over blocks (partials in the workspace, then a reduce)
+SPLIT = [(4, 256, 4096, "bf16"), (1, 64, 4096, "bf16"), (64, 300, 4096, "i8"), (3, 130, 2560, "i8")]
+
+
+def _split_case(nm, g, Mt, R, K, dt):
+    if dt == "bf16":
+        X, W = _int_bf16(g, (Mt, K), 2), _int_bf16(g, (R, K), 2)
+        mask, vals, idx = _pack_case(W, 0, score=O.score(W, None, 0, O.SCORE_MAGNITUDE) + g.random((R, K)).astype(np.float32))
+        Xd, ydt = np_bf16(X).to(dev()), nm.NM_F32
+        ref = O.masked_matmul(X, W, mask)
+    else:
+        X, W = g.integers(-127, 128, (Mt, K)).astype(np.int8), g.integers(-127, 128, (R, K)).astype(np.int8)
+        mask, vals, idx = _pack_case(W, 0, score=np.abs(W).astype(np.float32) + g.random((R, K)).astype(np.float32))
+        Xd, ydt = torch.from_numpy(X).to(dev()), nm.NM_I32
+        ref = O.masked_matmul_i8(X, W, mask, np.ones(Mt, np.float32), 1.0)[0]
+    v, i = _to_dev(vals, idx)
+    return Xd, v, i, ydt, ref
+
+
+@pytest.mark.parametrize("Mt,R,K,dt", SPLIT)
+def test_spmm_split_finish_any_workspace_contents(nm, Mt, R, K, dt):
+    """The split-K partials live in the workspace: whatever it holds before the call
+    (random bytes, all ones, what a previous call left), the product is exact, call after
+    call on the same workspace, and after a call of another shape on it."""
+    g = np.random.default_rng(Mt + R + K)
+    Xd, v, i, ydt, ref = _split_case(nm, g, Mt, R, K, dt)
+    xdt = nm.NM_BF16 if dt == "bf16" else nm.NM_I8
+    need = nm.raw.nm_spmm_workspace(Mt, K, R, 0, xdt)
+    assert need > 0, "the shape must split K over blocks"
+    need = max(need, nm.raw.nm_spmm_workspace(2, 4096, 192, 0, nm.NM_BF16))   # the other shape below
+    for fill in ("random", "ones", "reuse", "reuse"):
+        ws = torch.empty(need + 4096, dtype=torch.uint8, device=dev()) if fill != "reuse" else ws
+        if fill == "random":
+            ws.copy_(torch.from_numpy(g.integers(0, 256, ws.numel(), dtype=np.uint8)).to(dev()))
+        elif fill == "ones":
+            ws.fill_(255)
+        Y = nm.nm_spmm(Xd, v, i, R=R, ydt=ydt, ws=ws).cpu().numpy()
+        assert np.array_equal(Y.astype(np.float64) if dt == "bf16" else Y, ref), fill
+    # another split shape on the same workspace, then this one again
+    Xo, vo, io, ydto, refo = _split_case(nm, g, 2, 192, 4096, "bf16")
+    assert np.array_equal(nm.nm_spmm(Xo, vo, io, R=192, ydt=ydto, ws=ws).cpu().numpy().astype(np.float64), refo)
+    Y = nm.nm_spmm(Xd, v, i, R=R, ydt=ydt, ws=ws).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64) if dt == "bf16" else Y, ref)
+
+
+def test_spmm_split_finish_graph_replays(nm):
+    """A captured split-K product (two launches) replayed several times, with eager calls of
+    another shape on the same workspace in between, gives the exact product on every replay."""
+    g = np.random.default_rng(77)
+    Mt, R, K = 4, 256, 4096
+    Xd, v, i, ydt, ref = _split_case(nm, g, Mt, R, K, "bf16")
+    Xo, vo, io, _, refo = _split_case(nm, g, 2, 192, 4096, "bf16")
+    need = max(nm.raw.nm_spmm_workspace(Mt, K, R, 0, nm.NM_BF16), nm.raw.nm_spmm_workspace(2, K, 192, 0, nm.NM_BF16))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    Y = torch.empty((Mt, R), dtype=torch.float32, device=dev())
+    Yo = torch.empty((2, 192), dtype=torch.float32, device=dev())
+    nm.nm_spmm(Xd, v, i, R=R, ydt=ydt, ws=ws, out=Y)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nm.nm_spmm(Xd, v, i, R=R, ydt=ydt, ws=ws, out=Y)
+    for rep in range(4):
+        Y.fill_(-1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref), rep
+        if rep % 2 == 0:   # an eager call of another shape on the same workspace
+            nm.nm_spmm(Xo, vo, io, R=192, ydt=ydt, ws=ws, out=Yo)
+            torch.cuda.synchronize()
+            assert np.array_equal(Yo.cpu().numpy().astype(np.float64), refo)
