@@ -260,8 +260,9 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
     double lm[SMAX];
     // HALVING (rho = 1/2): T_t halves every step, so in f32 the exponent -z log2(e) / T_t is
     // exactly twice the previous step's (scaling by a power of two commutes with rounding)
-    // and the exponential is the previous one squared: one multiply instead of a 2^x (the
-    // product's relative error grows by at most 2^t ulps, about 4e-6 at t = 6)
+    // and the exponential is the previous one squared: one multiply instead of a 2^x.  Each
+    // squaring doubles the relative error carried from the last 2^x, so the chain restarts
+    // with a 2^x every fourth step (at most three squarings: about 8 ulps, 5e-7)
 #pragma unroll
     for (int t = 0; t < SMAX; ++t) {
         const float T = T0 * powf(rho, (float)t);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
                     float acc = 0.f;   // <= 8 terms in [0, 1/4]: f32 here, f64 across units
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        if (HALVING && t > 0) e[i] = e[i] * e[i];
+                        if (HALVING && (t & 3) != 0) e[i] = e[i] * e[i];
                         else e[i] = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
                         const float g = __builtin_amdgcn_rcpf(1.0f + e[i]);
                         m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];

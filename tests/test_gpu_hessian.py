@@ -214,3 +214,23 @@ def test_gate_random_every_step(nm, N, M, K):
         assert np.abs(mt.cpu().numpy() - m_ref).max() <= 1e-5
         assert np.array_equal(hm.cpu().numpy(), h_ref)
         assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)
+
+
+@pytest.mark.parametrize("steps,rho", [(24, 0.5), (24, 0.6)])
+def test_gate_long_schedules_every_step(nm, steps, rho):
+    """Many annealing steps: with rho = 1/2 the factor of a step is the previous one squared
+    between exact 2^x evaluations, so its rounding must stay within the gate tolerance on the
+    steps whose temperature puts the sigmoid of near-zero scores in its sensitive range."""
+    g = np.random.default_rng(steps + int(rho * 10))
+    R, K = 40, 512
+    S = g.standard_normal((R, K)).astype(np.float32)
+    S[:, :64] = (g.standard_normal((R, 64)) * 1e-3).astype(np.float32)   # scores near the mean
+    Sd = torch.from_numpy(S).to(dev())
+    mu, sg = O.stats(S)
+    stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
+    for t in range(steps):
+        mt, hm, lm = nm.nm_gate(Sd, stats, 2, 4, 4.0, rho, steps, m_step=t)
+        m_ref, h_ref, l_ref = O.gate_anneal(S, mu, sg, 2, 4, 4.0, rho, steps, m_step=t)
+        assert np.abs(mt.cpu().numpy() - m_ref).max() <= 1e-5, t
+        assert np.array_equal(hm.cpu().numpy(), h_ref)
+        assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)
