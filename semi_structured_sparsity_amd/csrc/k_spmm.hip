@@ -1378,6 +1378,10 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
 // lifted B fragment from the slot: window w of group q is original columns 8q + 2w .. +3,
 // i.e. dwords w, w+1 of the group's 16 bytes (bf16) or bytes 2w .. 2w+3 of its 8 (one-
 // byte codes: one byte-aligned funnel shift of the group's two dwords).
+// Partial tiles summed through LDS: a lane's 16 accumulators at a stride of 20 floats, so
+// the 16 lanes of a 16-byte store hit distinct banks (a 16-float stride puts them on 4)
+constexpr int kRedStride = 20;
+
 // XRES (up to 32 tokens, no lift): the block's X range -- its valid token rows, the
 // columns of its stages -- is loaded into LDS once, ahead of the ring, and the ring carries
 // the weight alone.  Under a full-chip weight stream a load from HBM takes about 4 us, so a
@@ -1410,7 +1414,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
                   "loads must split evenly over the 4 waves");
     static_assert(!XRES || ST == 1, "resident X for up to 32 tokens");
     constexpr int X_OFF = NS * STAGE, XRB = XRB_;
-    constexpr int RED = 4 * 64 * 16 * 4;                // one sub-tile of all four waves
+    constexpr int RED = 4 * 64 * kRedStride * 4;        // one sub-tile of all four waves
     constexpr int LDS = X_OFF + XRB > RED ? X_OFF + XRB : RED;
     static_assert(LDS <= 160 * 1024, "LDS ring too large");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -1637,7 +1641,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
             __syncthreads();
-            *(AccV*)&red[(wave * 64 + lane) * 16] = acc[i][j];
+            *(AccV*)&red[(wave * 64 + lane) * kRedStride] = acc[i][j];
             __syncthreads();
             for (int q = tid; q < 1024; q += 256) {
                 const int tk = q >> 5, row = q & 31;   // Y element (token, row) of the sub-tile
@@ -1646,7 +1650,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
                 using AccS = typename Mma<T>::AccS;
                 AccS v = 0;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
+                for (int w = 0; w < 4; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * kRedStride + e]);
                 if (gt >= a.Mtok || gr >= a.R) continue;
                 if (a.part) {
                     ((AccS*)a.part)[((int64_t)split * a.Mtok + gt) * a.R + gr] = v;
@@ -1690,7 +1694,7 @@ template <typename T, int SRk, int STk, int KSPLIT, int U>
 __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
     constexpr int es = sizeof(T);
     constexpr int KDEP = es == 2 ? 32 : 64;      // columns per SMFMAC
-    __shared__ float red[KSPLIT * 64 * 16];
+    __shared__ __attribute__((aligned(16))) float red[KSPLIT * 64 * kRedStride];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
@@ -1781,7 +1785,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
             __syncthreads();
             // one vector store of the whole accumulator (storing its 16 elements one by one
             // through bit casts was compiled into four copies of the first 16 bytes)
-            *(AccV*)&red[(wave * 64 + lane) * 16] = acc[i][j];
+            *(AccV*)&red[(wave * 64 + lane) * kRedStride] = acc[i][j];
             __syncthreads();
             for (int q = tid; q < 1024; q += KSPLIT * 64) {
                 const int tok = q >> 5, row = q & 31;                      // Y element (token, row) of the sub-tile
@@ -1789,7 +1793,7 @@ __global__ __launch_bounds__(KSPLIT * 64) void spmm_skinny_kernel(SpmmArgs a) {
                 const int64_t gt = t0 + 32 * j + tok, gr = r0 + 32 * i + row;
                 using AccS = typename Mma<T>::AccS;
                 AccS v = 0;
-                for (int w = 0; w < KSPLIT; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * 16 + e]);
+                for (int w = 0; w < KSPLIT; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * kRedStride + e]);
                 if (a.part) {
                     if (gt < a.Mtok && gr < a.R) ((AccS*)a.part)[((int64_t)split * a.Mtok + gt) * a.R + gr] = v;
                 } else if (gt < a.Mtok && gr < a.R) {
@@ -1969,7 +1973,22 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok, bool 
     {
         constexpr int KOm = 256 / (int)sizeof(T);
         const bool mid = ring_ok && Mtok <= 256 && (K % KOm) == 0;
-        p.mid = mid ? (Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 4)) : 0;
+        // token tile: the narrowest (32, 64 or 128 tokens) whose tiles fit one round on the
+        // CUs, else the widest.  Narrow tiles carry less X per stage, so more of the ring is
+        // weight in flight; the token tiles of a row tile share the weight through L2.
+        // Measured: 4096 rows at 128 tokens 23.8 -> 18.9 us on 32-token tiles (256 tiles,
+        // no K split); where 32-token tiles need 2.7-3.4 rounds (11008 rows at 128 tokens,
+        // 14336 rows of 6:8 at 64, 6912 int8 rows at 256) they were 24-66% slower.
+        p.mid = 0;
+        if (mid) {
+            const int64_t cus = device_cus(), rt = ceil_div(R, 64);
+            p.mid = Mtok <= 32 ? 1 : (Mtok <= 64 ? 2 : 4);   // the widest tile the tokens need
+            for (int m = 1; m < p.mid; m *= 2)
+                if (rt * ceil_div(Mtok, 32 * m) <= cus) {
+                    p.mid = m;
+                    break;
+                }
+        }
         if (p.mid) {
             p.tiles_r = (int)ceil_div(R, 64);
             p.tiles_t = (int)ceil_div(Mtok, 32 * p.mid);
