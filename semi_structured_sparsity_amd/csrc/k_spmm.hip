@@ -629,7 +629,11 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     int tr, tt;
     tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
     const int64_t r0 = (int64_t)tr * RG::BR, t0 = (int64_t)tt * RG::BT;
-    const int nsteps = a.nsteps;
+    // gridDim.y > 1: the stages split over blocks (split blockIdx.y takes stages s_begin ..
+    // s_begin + nsteps - 1 and writes f32 / i32 partials); stage indices below are local
+    const int spp = gridDim.y > 1 ? a.steps_per_split : a.nsteps;
+    const int split = blockIdx.y, s_begin = split * spp;
+    const int nsteps = a.nsteps - s_begin < spp ? a.nsteps - s_begin : spp;
     const uint32_t sbase = lds_addr(smem);
     const int64_t es = sizeof(T);
 
@@ -683,26 +687,27 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
 #pragma unroll
         for (int i = 0; i < RG::NI; ++i) {
             const int stg = g * IG + gC[p][i];
-            const int sc = stg < nsteps ? stg : nsteps - 1;
+            const int sc = s_begin + (stg < nsteps ? stg : nsteps - 1);
             dma16s(gb + (uint32_t)(((p * RG::NW + wave) * RG::NI + i) * 1024), baseI, gI[p][i] + (uint32_t)(sc * 16));
         }
     };
     auto issue = [&](int s) __attribute__((always_inline)) {
         const uint32_t st = sbase + (uint32_t)((s % NS) * RG::STAGE);
+        const int sg = s_begin + s;   // the stage's place in the whole K
 #pragma unroll
         for (int i = 0; i < RG::NA; ++i)
-            dma16s(st + RG::A_OFF + (wave * RG::NA + i) * 1024, baseA, oA[i] + (uint32_t)(s * RG::AROW));
+            dma16s(st + RG::A_OFF + (wave * RG::NA + i) * 1024, baseA, oA[i] + (uint32_t)(sg * RG::AROW));
         if constexpr (IG > 1) {
             // stage s >= 1 carries batch (s-1) % IG of group (s-1) / IG + 1; group 0 is loaded up front
             if (s >= 1) issue_group((s - 1) / IG + 1, (s - 1) % IG);
         } else {
 #pragma unroll
             for (int i = 0; i < RG::NI; ++i)
-                dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(s * RG::AI * 4));
+                dma4s(st + RG::I_OFF + (wave * RG::NI + i) * 256, baseI, oI[i] + (uint32_t)(sg * RG::AI * 4));
         }
 #pragma unroll
         for (int i = 0; i < RG::NB; ++i)
-            dma16s(st + RG::B_OFF + (wave * RG::NB + i) * 1024, baseB, oB[i] + (uint32_t)(s * KB));
+            dma16s(st + RG::B_OFF + (wave * RG::NB + i) * 1024, baseB, oB[i] + (uint32_t)(sg * KB));
     };
     const int h = lane >> 5, l32 = lane & 31;
     i32x4_t ipc[SR];   // IG > 1: the current stage's index piece of each row sub-tile (one word per depth)
@@ -795,13 +800,24 @@ __global__ __launch_bounds__(64 * WRN * WTN, OCC) void spmm_ring_kernel(SpmmArgs
     for (; S + 1 < nsteps; ++S) stage(S, std::true_type{});
     if (S < nsteps) stage(S, std::false_type{});
     wait_vm_all();
-    if constexpr (sizeof(T) == 2) {
-        if (a.rank > 0) add_lowrank<SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, lane);
+    if constexpr (sizeof(T) == 2) {   // the adapter term once, in the first split
+        if (a.rank > 0 && split == 0) add_lowrank<SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, lane);
     }
 
     // every wave has finished reading the ring: its LDS becomes the output staging buffers
     __syncthreads();
     static_assert(RG::LDS >= RG::NW * kStageWords<SR> * 4, "staging buffers fit in the ring");
+    if (a.part) {   // this split's partial tile, unscaled, into [split][Mtok][R]
+        SpmmArgs b = a;
+        using AccS = typename Mma<T>::AccS;
+        b.Y = (AccS*)a.part + (int64_t)split * a.Mtok * a.R;
+        b.ydt = std::is_same<AccS, float>::value ? NM_F32 : NM_I32;
+        b.ldy = a.R;
+        b.scaled = 0;
+        store_tile<T, SR, ST>(b, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, false, (uint32_t*)smem + wave * kStageWords<SR>,
+                              lane);
+        return;
+    }
     store_tile<T, SR, ST>(a, acc, r0 + wr * SR * 32, t0 + wt * ST * 32, r0 + RG::BR <= a.R && t0 + RG::BT <= a.Mtok,
                           (uint32_t*)smem + wave * kStageWords<SR>, lane);
 }
@@ -2004,6 +2020,32 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok, bool 
                 const int64_t rows = Mtok < 32 ? Mtok : 32;
                 if (rows * (ceil_div((int64_t)p.steps_per_split * 256, 1024) * 1024 + 16) <= kXresBytes) p.xres = 1;
             }
+            // bf16, 65-256 tokens on 128-token tiles (X not lifted in the kernel): a block of
+            // the K-split ring takes 64 rows and reads its tokens' whole X range -- four times
+            // the weight's bytes in every stage, which leaves the ring little weight in
+            // flight.  The narrow ring's 256 x 128 tiles read a quarter of that per weight
+            // byte; their stages are split over blocks until about one round runs, the
+            // splits' partials summed by the reduce kernel.  Measured: 11008 rows at 128
+            // tokens 38.9 -> 36.2 us; for int8 (6912 rows, 256 tokens, 15 stages) slower,
+            // 30.9 -> 36.6 us, as each split holds only 4 stages of a 2-slot ring.
+            using RNm = Ring<NM_RING_NARROW>;
+            if (sizeof(T) == 2 && p.mid == 4 && xres_ok && ring_ok && (K % RNm::KO) == 0) {
+                const int64_t cus = device_cus();
+                const int64_t tiles = ceil_div(R, RNm::BR) * ceil_div(Mtok, RNm::BT);
+                const int64_t ns = K / RNm::KO;
+                int64_t ks = cus / tiles;
+                if (ks > ns / 2) ks = ns / 2;
+                if (ks < 1) ks = 1;
+                SpmmPlan q{};
+                q.ring = true;
+                q.large = Mtok > 128;
+                q.tiles_r = (int)ceil_div(R, RNm::BR);
+                q.tiles_t = (int)ceil_div(Mtok, RNm::BT);
+                q.nsteps = (int)ns;
+                q.steps_per_split = (int)ceil_div(ns, ks);
+                q.KS = (int)ceil_div(ns, q.steps_per_split);
+                return q;
+            }
             return p;
         }
     }
@@ -2165,7 +2207,9 @@ static bool ring_ok_for(const SpmmArgs& a, int64_t es) {
 static bool lift_fused(int64_t Mtok, int64_t K, int64_t R, int Ns, nm_dtype xdt, bool ring_ok) {
     if (Ns != 4) return false;
     const int64_t Kl = lifted_cols(K, Ns);
-    const SpmmPlan p = xdt == NM_BF16 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok) : plan_for<int8_t>(Mtok, Kl, R, ring_ok);
+    // the token tile of the K-split ring the lifted product would run on
+    const SpmmPlan p = xdt == NM_BF16 ? plan_for<uint16_t>(Mtok, Kl, R, ring_ok, false)
+                                      : plan_for<int8_t>(Mtok, Kl, R, ring_ok, false);
     // one-byte codes: the in-kernel gather (two 8-byte reads and a funnel shift per window
     // pair) costs more than a separate lift on the 128-token tiles (6912 x 2560 int8 at 256
     // tokens: 38.3 us fused against 32.7 us lifting first; at one token 14.6 against 16.2)
@@ -2263,7 +2307,12 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void*
             b.tiles_r = (int)ceil_div(b.R, big ? RB::BR : RN::BR);
             b.tiles_t = (int)ceil_div(a.Mtok, big ? RB::BT : RN::BT);
             b.nsteps = (int)(a.K / (big ? RB::KO : RN::KO));
-            const dim3 g((unsigned)(b.tiles_r * b.tiles_t));
+            // the narrow ring's stages split over blocks (few tokens): partials into the workspace
+            const bool split = !big && p.KS > 1;
+            b.part = split ? a.part : nullptr;
+            b.KS = split ? p.KS : 1;
+            b.steps_per_split = split ? p.steps_per_split : b.nsteps;
+            const dim3 g((unsigned)(b.tiles_r * b.tiles_t), (unsigned)b.KS);
             if (big) hipLaunchKernelGGL((spmm_ring2_kernel<NM_RING_BIG>), g, dim3(512), 0, s, b);
             // bf16: index words loaded 4 stages at a time (whole 64-byte runs of a row)
             else hipLaunchKernelGGL((spmm_ring_kernel<NM_RING_NARROW, 1, sizeof(T) == 2 ? 4 : 1>), g, dim3(256), 0, s, b);
@@ -2274,7 +2323,7 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void*
         } else {
             launch(p.big, 0, a.R);
         }
-        return check_launch("nm_spmm");
+        if (p.KS <= 1) return check_launch("nm_spmm");
     } else if (p.large)
         hipLaunchKernelGGL((spmm_kernel<T, 2, 2, 2, 2>), grid, dim3(256), 0, s, a);
     else

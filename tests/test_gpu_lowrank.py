@@ -63,6 +63,7 @@ def _run(nm, X, vals, idx, A, B, R, Ns, ydt):
 # (tokens, rows, K, rank): few-token kernels with the add pass (1, 3, 4, 16, 100, 200), the
 # 256 x 128 kernel (300, 520), ragged edges everywhere; ranks with a partial 16-wide step
 @pytest.mark.parametrize("Mt,R,K,rank", [(1, 96, 256, 8), (3, 130, 512, 16), (4, 300, 1024, 64), (16, 130, 512, 16),
+                                         (256, 4160, 512, 16),   # 256 x 128 tiles, K split: the term once
                                          (100, 200, 1024, 72), (200, 64, 256, 64),
                                          (300, 260, 512, 24), (520, 300, 1024, 128), (300, 200, 256, 256)])
 @pytest.mark.parametrize("Ns", [0, 4])

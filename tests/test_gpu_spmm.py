@@ -415,3 +415,19 @@ def test_spmm_split_finish_graph_replays(nm):
             nm.nm_spmm(Xo, vo, io, R=192, ydt=ydt, ws=ws, out=Yo)
             torch.cuda.synchronize()
             assert np.array_equal(Yo.cpu().numpy().astype(np.float64), refo)
+
+
+# 65-256 tokens on many rows (32- and 64-token tiles would need more than one round): bf16
+# runs the 256 x 128 ring with its stages split over blocks (partials, then the reduce), or
+# unsplit at two stages; int8 the K-split ring's 128-token tiles
+RING_SPLIT = [(256, 4160, 512), (200, 4200, 1024), (130, 8300, 256)]
+
+
+@pytest.mark.parametrize("Mt,R,K", RING_SPLIT)
+def test_spmm_ring_split_bf16_integer_exact(nm, Mt, R, K):
+    test_spmm_bf16_integer_exact(nm, Mt, R, K, 0)
+
+
+@pytest.mark.parametrize("Mt,R,K", RING_SPLIT)
+def test_spmm_ring_split_int8_exact(nm, Mt, R, K):
+    test_spmm_int8_exact(nm, Mt, R, K, 0)
