@@ -513,8 +513,7 @@ __global__ __launch_bounds__(256) void bitmap_reduce_kernel(const float* __restr
                                                             int64_t R, void* Y, int ydt, int64_t ldy) {
     const int64_t total = M * R;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        float v = 0.0f;
-        for (int k = 0; k < KS; ++k) v += part[(int64_t)k * total + i];
+        const float v = split_sum(part + i, KS, total);
         const int64_t m = i / R, o = i - m * R;
         if (ydt == NM_F32) ((float*)Y)[m * ldy + o] = v;
         else ((uint16_t*)Y)[m * ldy + o] = (uint16_t)f32_to_bf16_bits(v);

@@ -1836,8 +1836,7 @@ __global__ __launch_bounds__(256) void spmm_reduce_kernel(SpmmArgs a) {
     const int64_t total = a.Mtok * a.R;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t tok = t / a.R, r = t - tok * a.R;
-        Acc v = 0;
-        for (int z = 0; z < a.KS; ++z) v += ((const Acc*)a.part)[(int64_t)z * total + t];
+        const Acc v = split_sum((const Acc*)a.part + t, a.KS, total);
         const int64_t o = tok * a.ldy + r;
         if (a.ydt == NM_I32) {
             ((int32_t*)a.Y)[o] = (int32_t)v;
@@ -1912,8 +1911,7 @@ __global__ __launch_bounds__(256) void lowrank_u_reduce_kernel(const float* __re
                                                                uint16_t* __restrict__ U) {
     const int64_t total = M * rank;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        float v = 0.0f;
-        for (int sp = 0; sp < S; ++sp) v += P[(int64_t)sp * total + i];
+        const float v = split_sum(P + i, S, total);
         U[i] = (uint16_t)f32_to_bf16_bits(v);
     }
 }

@@ -27,6 +27,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 // Rank key of a score for top-N selection: NaN ranks below everything and
 // -0 compares equal to +0 (x + 0 maps -0 to +0).
+// sum over z < n of p[z * stride], added in z order starting from 0 (the order of a plain
+// loop), with the loads of up to 8 terms issued together: the terms are split-K partials
+// written by an earlier kernel on other XCDs, and one dependent load at a time costs a
+// memory round trip per term
+template <typename Acc>
+__device__ __forceinline__ Acc split_sum(const Acc* __restrict__ p, int n, int64_t stride) {
+    Acc v = 0;
+    for (int z = 0; z < n; z += 8) {
+        Acc t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = z + i < n ? p[(int64_t)(z + i) * stride] : Acc(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (z + i < n) v += t[i];
+    }
+    return v;
+}
+
 __device__ __forceinline__ float rank_key(float x) { return (x != x) ? -__builtin_inff() : __fadd_rn(x, 0.0f); }
 
 // Keep-bits of the top-N of M keys (ties to the lower index): bit i set iff
