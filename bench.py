@@ -265,12 +265,41 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return sorted(ts)[len(ts) // 2]
 
-    def row(cfg, rowid, name, f, bound, work):
+    def streamed(make, operands):
+        """Per-call time with launches back to back, each call on its own copy of the weight
+        operands: enough copies that they fill twice the 256 MB Infinity Cache, so every call
+        reads its weight from HBM (as a model's consecutive layers do).  Median of 3 passes
+        over the copies, each pass one HIP-event interval."""
+        nbytes = sum(t.numel() * t.element_size() for t in operands)
+        n = max(4, min(64, -(-(512 << 20) // nbytes)))
+        copies = [tuple(t.clone() for t in operands) for _ in range(n)]
+        calls = [make(*c) for c in copies]
+        for c in calls:
+            c()
+        ts = []
+        for _ in range(3):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for c in calls:
+                c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3 / n)
+        del copies, calls
+        return sorted(ts)[1], n
+
+    def row(cfg, rowid, name, f, bound, work, stream_of=None):
         t = timed(f)
         e = dict(config=cfg, row=rowid, name=name, us=round(t * 1e6, 2), bound=bound)
         if bound == "hbm":
             e["GBps"] = round(work / t / 1e9, 1)
             e["frac"] = round(e["GBps"] / HBM_PEAK_GBPS, 4)
+            if stream_of is not None:   # (factory of a call on given weight operands, the operands)
+                ts, n = streamed(*stream_of)
+                e["us_stream"] = round(ts * 1e6, 2)
+                e["frac_stream"] = round(work / ts / 1e9 / HBM_PEAK_GBPS, 4)
+                e["stream_copies"] = n
         elif bound == "mfma":
             e["TFLOPs"] = round(work / t / 1e12, 2)
             e["frac"] = round(e["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
@@ -316,7 +345,9 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
             ws = ws_for(r.nm_spmm_workspace(M, K, R, 0, nm.NM_BF16))
             f = spmm(X, nm.NM_BF16, M, K, vals, nm.NM_BF16, idx, R, 0, Y, nm.NM_BF16, ws=ws)
             if M <= 128:
-                row("llama24", "A12", f"spmm {lname} M={M}", f, "hbm", R * K // 2 * 2 + R * K // 32 * 4 + M * K * 2 + M * R * 2)
+                row("llama24", "A12", f"spmm {lname} M={M}", f, "hbm", R * K // 2 * 2 + R * K // 32 * 4 + M * K * 2 + M * R * 2,
+                    stream_of=(lambda v, i, X=X, Y=Y, ws=ws, M=M, R=R: spmm(X, nm.NM_BF16, M, K, v, nm.NM_BF16, i, R, 0, Y,
+                                                                           nm.NM_BF16, ws=ws), (vals, idx)))
             else:
                 row("llama24", "A12", f"spmm {lname} M={M}", f, "mfma", 2 * M * R * K // 2)
             del X, Y, ws
@@ -354,7 +385,9 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         ws = ws_for(r.nm_spmm_workspace(M, K, R, Ns, nm.NM_BF16))
         f = spmm(X, nm.NM_BF16, M, K, vals, nm.NM_BF16, idx, R, Ns, Y, nm.NM_BF16, ws=ws)
         if M <= 64:
-            row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "hbm", R * K * 1.6875 + M * K * 2 + M * R * 2)
+            row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "hbm", R * K * 1.6875 + M * K * 2 + M * R * 2,
+                stream_of=(lambda v, i, X=X, Y=Y, ws=ws, M=M: spmm(X, nm.NM_BF16, M, K, v, nm.NM_BF16, i, R, Ns, Y,
+                                                                  nm.NM_BF16, ws=ws), (vals, idx)))
         else:
             row("slide68", "A11+A12", f"spmm lifted 14336x4096 M={M}", f, "mfma", 2 * M * R * Kl // 2)
     # the same layer with a stacked rank-64 low-rank adapter pair (SALR section 3):
@@ -424,7 +457,10 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         f = spmm(XL, nm.NM_FP8, M, Kl, vq, nm.NM_FP8, idx, R, 0, Y, nm.NM_BF16, xs=sx, a=1.0, ws=ws)
         if M <= 64:
             row("slide68", "NEXT-2", f"spmm fp8 lifted 14336x4096 M={M}", f, "hbm",
-                R * Kl * (0.5 + 0.0625) + M * Kl + 4 * M + M * R * 2)
+                R * Kl * (0.5 + 0.0625) + M * Kl + 4 * M + M * R * 2,
+                stream_of=(lambda v, i, XL=XL, sx=sx, Y=Y, ws=ws, M=M: spmm(XL, nm.NM_FP8, M, Kl, v, nm.NM_FP8, i, R, 0,
+                                                                           Y, nm.NM_BF16, xs=sx, a=1.0, ws=ws),
+                           (vq, idx)))
         else:
             row("slide68", "NEXT-2", f"spmm fp8 lifted 14336x4096 M={M}", f, "mfma_fp8", 2 * M * R * Kl // 2)
         del X, XL, sx, Y
@@ -463,7 +499,9 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         f = spmm(Xq, nm.NM_I8, M, K, vals, nm.NM_I8, idx, R, Ns, Y, nm.NM_F32, xs=sx, a=a, ws=ws)
         if M <= 256:
             row("ternary68", "A11+A13", f"spmm int8 lifted 6912x2560 M={M}", f, "hbm",
-                R * K * (0.75 + 0.09375) + M * K + 4 * M + 4 * M * R)
+                R * K * (0.75 + 0.09375) + M * K + 4 * M + 4 * M * R,
+                stream_of=(lambda v, i, Xq=Xq, sx=sx, Y=Y, ws=ws, M=M: spmm(Xq, nm.NM_I8, M, K, v, nm.NM_I8, i, R, Ns, Y,
+                                                                           nm.NM_F32, xs=sx, a=a, ws=ws), (vals, idx)))
         else:
             row("ternary68", "A11+A13", f"spmm int8 lifted 6912x2560 M={M}", f, "mfma_i8", 2 * M * R * Kl // 2)
     del Wf, Wt, vals, idx, mask
