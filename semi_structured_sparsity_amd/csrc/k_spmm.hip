@@ -2459,6 +2459,10 @@ nm_status launch_spmm_lowrank(const void* X, int64_t Mtok, int64_t K, int64_t ld
 // an L2 prefetch of the next stage's lines (one dword per line, 7.05 against 6.82 ms), nor
 // four waves of 128 x 128 per tile with AGPR accumulators (a dense 28672 x 8192 product at
 // 8192 tokens: 4.13 against 3.52 ms; one wave per SIMD leaves nothing to cover the waits).
+// Nor a ping-pong schedule (waves w and w + 4 of a SIMD alternating a phase of fragment
+// reads with a phase of 16 or 32 MFMAs, a block barrier after every phase, the second
+// four waves one phase late): the same Hutchinson time, the U product 6% and the dense
+// product 15% slower.  The one barrier per stage is not what holds the MFMA pipes idle.
 // Under this load the clock falls to 1.6-1.8 GHz (GRBM cycles over the dispatch time); a
 // copy that skips the stage loads runs at 1.9-2.1 GHz: the operand traffic costs power as
 // well as issue slots, and a 256 x 256 tile is the largest two waves per SIMD can hold.
