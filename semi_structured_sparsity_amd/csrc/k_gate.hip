@@ -373,6 +373,103 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
     }
 }
 
+// The same pass for whole 8-score units (K a multiple of 8, 16-byte aligned rows) and a
+// step count S fixed at compile time, M = GM: every step's beta is a constant, so the
+// steps unroll with no per-step branch and the per-step sums stay in registers.  The
+// arithmetic of each step is that of gate_kernel, operation for operation (beta * h is
+// the select h ? beta : 0, which is exact), so both give the same bits.  The last step
+// has beta = 1: its blend is the hard target, whose top-N (exactly N ones per group) is
+// the hard target itself, so the final projection is h.  WANT_M: keep and write the
+// blend of step m_step.
+template <int S, int GM, bool HALVING, bool WANT_M>
+__global__ __launch_bounds__(kRedThreads) void gate_fast_kernel(const float* __restrict__ Sc, int64_t R, int64_t K,
+                                                                int64_t lds, const double* __restrict__ stats, int N,
+                                                                float T0, float rho, int m_step, float* __restrict__ m_out,
+                                                                int64_t ldf, uint8_t* __restrict__ hard_mask, int64_t ldm,
+                                                                double* __restrict__ part) {
+    static_assert(S >= 2 && (GM == 4 || GM == 8), "fixed schedules of at least two steps, 2:4-like or 6:8-like groups");
+    __shared__ double sh[kRedThreads];
+    const double mu = stats[0], sigma = stats[1];
+    const double inv_sigma = sigma > 0.0 ? 1.0 / sigma : 0.0;
+    const int64_t bpr = K / 8;
+    const int64_t total = R * bpr;
+    float cs[S - 1];
+    double lm[S - 1];
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) {
+        const float T = T0 * powf(rho, (float)t);
+        cs[t] = 1.4426950408889634f / T;
+        lm[t] = 0.0;
+    }
+    const int64_t stride = (int64_t)kGateBlocks * kRedThreads;
+    const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
+    int64_t r = u0 / bpr, b = u0 - r * bpr;
+    const int64_t dr = stride / bpr, db = stride - dr * bpr;
+    for (int64_t u = u0; u < total; u += stride) {
+        const int64_t k0 = b * 8;
+        const float4 v0 = *(const float4*)(Sc + r * lds + k0);
+        const float4 v1 = *(const float4*)(Sc + r * lds + k0 + 4);
+        const float s[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        float z[8], key[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            z[i] = sigma > 0.0 ? (float)(((double)s[i] - mu) * inv_sigma) : 0.f;
+            key[i] = rank_key(s[i]);
+        }
+        uint32_t hbits;
+        if constexpr (GM == 4) {
+            const float ka[4] = {key[0], key[1], key[2], key[3]}, kb[4] = {key[4], key[5], key[6], key[7]};
+            hbits = topn_bits<4>(ka, N) | (topn_bits<4>(kb, N) << 4);
+        } else {
+            hbits = topn_bits<8>(key, N);
+        }
+        bool h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (hbits >> i) & 1u;
+        float e[8], mo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = mo[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t) {
+            constexpr float kOne = 1.0f;
+            const float beta = (float)t / (float)(S - 1);
+            const float wg = kOne - beta;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (HALVING && (t & 3) != 0) e[i] = e[i] * e[i];
+                else e[i] = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
+                const float g = __builtin_amdgcn_rcpf(1.0f + e[i]);
+                const float m = wg * g + (h[i] ? beta : 0.f);
+                acc += m * (1.0f - m);
+                if constexpr (WANT_M) mo[i] = t == m_step ? m : mo[i];
+            }
+            lm[t] += (double)acc;
+        }
+        hard_mask[r * ldm + b] = (uint8_t)hbits;
+        if constexpr (WANT_M) {
+            if (m_step == S - 1) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mo[i] = h[i] ? 1.0f : 0.0f;
+            }
+            *(float4*)(m_out + r * ldf + k0) = make_float4(mo[0], mo[1], mo[2], mo[3]);
+            *(float4*)(m_out + r * ldf + k0 + 4) = make_float4(mo[4], mo[5], mo[6], mo[7]);
+        }
+        r += dr;
+        b += db;
+        if (b >= bpr) {
+            b -= bpr;
+            r += 1;
+        }
+    }
+    // the per-step sums in the same order as gate_kernel (the beta = 1 step adds nothing)
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        const double v = block_sum(t < S - 1 ? lm[t < S - 1 ? t : 0] : 0.0, sh);
+        if (threadIdx.x == 0) part[(int64_t)t * kGateBlocks + blockIdx.x] = v;
+    }
+}
+
 __global__ __launch_bounds__(kRedThreads) void gate_final_kernel(const double* __restrict__ part, int steps,
                                                                  double* __restrict__ lmid) {
     __shared__ double sh[kRedThreads];
@@ -390,6 +487,35 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
                  float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
                  double* lmid, void* ws, hipStream_t s) {
     double* part = (double*)ws;
+    // the default schedule (8 steps) on whole 8-score units: the unrolled kernel
+    const bool fast = steps == 8 && (M == 4 || M == 8) && K % 8 == 0 && lds % 4 == 0 && ((uintptr_t)S & 15) == 0 &&
+                      (m_out == nullptr || (ldf % 4 == 0 && ((uintptr_t)m_out & 15) == 0));
+    if (fast) {
+#define NM_GATE_FAST(GM, HV, WM)                                                                                        \
+    hipLaunchKernelGGL((gate_fast_kernel<8, GM, HV, WM>), dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, \
+                       N, T0, rho, m_step, m_out, ldf, hard_mask, ldm, part)
+        const bool halving = rho == 0.5f, wm = m_out != nullptr;
+        if (M == 4) {
+            if (halving) {
+                if (wm) NM_GATE_FAST(4, true, true);
+                else NM_GATE_FAST(4, true, false);
+            } else {
+                if (wm) NM_GATE_FAST(4, false, true);
+                else NM_GATE_FAST(4, false, false);
+            }
+        } else {
+            if (halving) {
+                if (wm) NM_GATE_FAST(8, true, true);
+                else NM_GATE_FAST(8, true, false);
+            } else {
+                if (wm) NM_GATE_FAST(8, false, true);
+                else NM_GATE_FAST(8, false, false);
+            }
+        }
+#undef NM_GATE_FAST
+        hipLaunchKernelGGL(gate_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double*)part, steps, lmid);
+        return;
+    }
 #define NM_GATE(SM, HV)                                                                                             \
     hipLaunchKernelGGL((gate_kernel<SM, HV>), dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, N, M, \
                        T0, rho, steps, m_step, m_out, ldf, hard_mask, ldm, part)

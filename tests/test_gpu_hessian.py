@@ -234,3 +234,30 @@ def test_gate_long_schedules_every_step(nm, steps, rho):
         assert np.abs(mt.cpu().numpy() - m_ref).max() <= 1e-5, t
         assert np.array_equal(hm.cpu().numpy(), h_ref)
         assert np.allclose(lm.cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)
+
+
+@pytest.mark.parametrize("N,M,rho", [(2, 4, 0.5), (2, 4, 0.6), (6, 8, 0.5), (6, 8, 0.6)])
+def test_gate_default_schedule_kernels_agree(nm, N, M, rho):
+    """The default 8-step schedule on whole 8-score units runs an unrolled kernel; a view
+    with an odd leading dimension takes the general kernel.  Both do the same arithmetic,
+    so every output agrees bit for bit; both are held to the oracle as well."""
+    g = np.random.default_rng(31 + M + int(rho * 10))
+    R, K, steps = 57, 512, 8
+    S = (g.standard_normal((R, K)) * 1.3 + 0.2).astype(np.float32)
+    S[:, :32] = 0.2   # ties inside groups and z = 0
+    Sd = torch.from_numpy(S).to(dev())
+    pad = torch.zeros((R, K + 1), dtype=torch.float32, device=dev())
+    pad[:, :K] = Sd
+    Sv = pad[:, :K]   # leading dimension K + 1: the general kernel
+    mu, sg = O.stats(S)
+    stats = torch.tensor([mu, sg], dtype=torch.float64, device=dev())
+    for t in list(range(steps)) + [None]:
+        a = nm.nm_gate(Sd, stats, N, M, 0.5, rho, steps, want_m=t is not None, m_step=t)
+        b = nm.nm_gate(Sv, stats, N, M, 0.5, rho, steps, want_m=t is not None, m_step=t)
+        assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), t
+        if t is not None:
+            assert torch.equal(a[0], b[0]), t
+            m_ref, h_ref, l_ref = O.gate_anneal(S, mu, sg, N, M, 0.5, rho, steps, m_step=t)
+            assert np.abs(a[0].cpu().numpy() - m_ref).max() <= 1e-5, t
+            assert np.array_equal(a[1].cpu().numpy(), h_ref)
+            assert np.allclose(a[2].cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)
