@@ -60,11 +60,12 @@ __device__ __forceinline__ void block_moments(Moments m, double (*sh)[kRedThread
 
 // Elements of [R, K] (leading dim ld) are visited in units of VEC consecutive
 // elements of a row; thread u of the fixed grid takes units u, u + stride, ...,
-// UN units per round with all UN loads issued before any is used.  When VEC > 1
+// UN units per round with all UN loads issued before any is used (the grid then
+// reads UN regions a grid's width apart at a time).  When VEC > 1
 // the caller guarantees K % VEC == 0, ld % VEC == 0 and 16-byte alignment.
 template <typename T, int VEC, typename F>
 __device__ __forceinline__ void for_units(const T* __restrict__ X, int64_t R, int64_t K, int64_t ld, F&& f) {
-    constexpr int UN = 8;
+    constexpr int UN = 4;   // 8 or 16 in flight measured slower (the S statistics pass 177 -> 199 / 209 us)
     const int64_t upr = K / VEC, total = R * upr;
     const int64_t stride = (int64_t)kRedBlocks * kRedThreads;
     const int64_t u0 = (int64_t)blockIdx.x * kRedThreads + threadIdx.x;
