@@ -420,9 +420,11 @@ __global__ __launch_bounds__(kRedThreads) void gate_fast_kernel(const float* __r
         uint32_t hbits;
         if constexpr (GM == 4) {
             const float ka[4] = {key[0], key[1], key[2], key[3]}, kb[4] = {key[4], key[5], key[6], key[7]};
-            hbits = topn_bits<4>(ka, N) | (topn_bits<4>(kb, N) << 4);
+            if (N == 2) hbits = top2of4_bits(ka) | (top2of4_bits(kb) << 4);
+            else hbits = topn_bits<4>(ka, N) | (topn_bits<4>(kb, N) << 4);
         } else {
-            hbits = topn_bits<8>(key, N);
+            if (N == 6) hbits = top6of8_bits(key);
+            else hbits = topn_bits<8>(key, N);
         }
         bool h[8];
 #pragma unroll

@@ -396,7 +396,9 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
     const int64_t k0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     const int64_t r0 = row_base + (int64_t)blockIdx.y * PR;
     const bool col_ok = k0 < K;
-    uint32_t wb[PR][8];  // bf16 bit patterns of the values (the stored form)
+    // the values' bf16 bit patterns as loaded (two per word, the lower column in the low
+    // half), and their f32 values for the score
+    uint32_t wu[PR][4];
     float w[PR][8];
     uint32_t mbin[PR];   // FM: the input mask byte of each row
 #pragma unroll
@@ -406,9 +408,7 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
         if constexpr (FM) mbin[p] = mask[r * ldm + (kc >> 3)];
         if constexpr (sizeof(TW) == 2) {
             const uint4 v = *(const uint4*)(W + r * ldw + kc);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wb[p][i] = (u[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            wu[p][0] = v.x; wu[p][1] = v.y; wu[p][2] = v.z; wu[p][3] = v.w;
         } else {
             const float4 a = *(const float4*)(W + r * ldw + kc);
             const float4 c = *(const float4*)(W + r * ldw + kc + 4);
@@ -427,10 +427,13 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
 #pragma unroll
     for (int p = 0; p < PR; ++p) {
         const int64_t r = r0 + p;
+        if constexpr (sizeof(TW) == 2) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if constexpr (sizeof(TW) == 2) w[p][i] = bf16_bits_to_f32(wb[p][i]);
-            else wb[p][i] = f32_to_bf16_bits(w[p][i]);
+            for (int i = 0; i < 8; ++i)
+                w[p][i] = __uint_as_float((i & 1) ? (wu[p][i >> 1] & 0xffff0000u) : (wu[p][i >> 1] << 16));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wu[p][j] = f32_to_bf16_bits(w[p][2 * j]) | (f32_to_bf16_bits(w[p][2 * j + 1]) << 16);
         }
         float key[8];
         if constexpr (FM) {
@@ -468,18 +471,20 @@ __global__ __launch_bounds__(256) void prune_pack24_kernel(const TW* __restrict_
                 bits = real | (have < 2 ? f1 : 0u) | (have < 1 ? f2 : 0u);
             } else {
                 const float kk[4] = {key[4 * gi], key[4 * gi + 1], key[4 * gi + 2], key[4 * gi + 3]};
-                bits = topn_bits<4>(kk, 2);
+                bits = top2of4_bits(kk);
                 real = bits;
             }
+            // exactly two bits: the kept positions p0 < p1; their 16-bit values are bytes
+            // 2p, 2p+1 of the group's 8 bytes, picked by one byte permute (selector 12 gives
+            // a zero byte: the value of a padded slot)
             const uint32_t p0 = __builtin_ctz(bits);
             const uint32_t p1 = 31u - __builtin_clz(bits);
-            uint32_t v0 = 0, v1 = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v0 = (p0 == (uint32_t)i && ((real >> i) & 1u)) ? wb[p][4 * gi + i] : v0;
-                v1 = (p1 == (uint32_t)i && ((real >> i) & 1u)) ? wb[p][4 * gi + i] : v1;
+            uint32_t s0 = 0x0100u + p0 * 0x0202u, s1 = 0x0100u + p1 * 0x0202u;
+            if constexpr (FM) {
+                s0 = ((real >> p0) & 1u) ? s0 : 0x0c0cu;
+                s1 = ((real >> p1) & 1u) ? s1 : 0x0c0cu;
             }
-            packed[gi] = v0 | (v1 << 16);
+            packed[gi] = __builtin_amdgcn_perm(wu[p][2 * gi + 1], wu[p][2 * gi], s0 | (s1 << 16));
             mbyte |= bits << (4 * gi);
             nib |= (p0 | (p1 << 2)) << (4 * gi);
         }
@@ -860,7 +865,7 @@ __global__ __launch_bounds__(256) void slide68_kernel(const TS* __restrict__ Wsc
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 key[i] = rank_key(SEL == 0 ? fabsf(sc[p][i]) : hess_score(sc[p][i], h[i], eps));
-            bits = topn_bits<8>(key, 6);
+            bits = top6of8_bits(key);
             if (mask_out && ok) mask_out[r * ldm + (k0 >> 3)] = (uint8_t)bits;
         }
         // kept positions ascending -> earliest covering window with a free slot (tabulated)

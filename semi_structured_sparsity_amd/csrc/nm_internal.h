@@ -45,7 +45,9 @@ __device__ __forceinline__ Acc split_sum(const Acc* __restrict__ p, int n, int64
     return v;
 }
 
-__device__ __forceinline__ float rank_key(float x) { return (x != x) ? -__builtin_inff() : __fadd_rn(x, 0.0f); }
+// Ranking key of a score: NaN ranks below everything (max(NaN, -inf) is -inf); -0 and +0
+// compare equal, as the keys only ever meet in comparisons.
+__device__ __forceinline__ float rank_key(float x) { return __builtin_fmaxf(x, -__builtin_inff()); }
 
 // Keep-bits of the top-N of M keys (ties to the lower index): bit i set iff
 // fewer than N members beat member i; j beats i iff key_j > key_i, or the keys
@@ -69,6 +71,56 @@ __device__ __forceinline__ uint32_t topn_bits(const float (&k)[M], int N) {
 #pragma unroll
     for (int i = 0; i < M; ++i) bits |= (beaten[i] < N ? 1u : 0u) << i;
     return bits;
+}
+
+// topn_bits<4>(k, 2) as lane-mask logic: member i is kept when it beats at least two of
+// the other three (i beats j > i iff k_i >= k_j).  The six comparisons are the only
+// per-lane work besides forming the bits; the majorities are boolean operations on
+// wave masks.
+__device__ __forceinline__ uint32_t top2of4_bits(const float (&k)[4]) {
+    const bool c01 = k[0] >= k[1], c02 = k[0] >= k[2], c03 = k[0] >= k[3];
+    const bool c12 = k[1] >= k[2], c13 = k[1] >= k[3], c23 = k[2] >= k[3];
+    const bool b0 = (c01 && (c02 || c03)) || (c02 && c03);
+    const bool b1 = (!c01 && (c12 || c13)) || (c12 && c13);
+    const bool b2 = (!c02 && (!c12 || c23)) || (!c12 && c23);
+    const bool b3 = (!c03 && (!c13 || !c23)) || (!c13 && !c23);
+    return (b0 ? 1u : 0u) | (b1 ? 2u : 0u) | (b2 ? 4u : 0u) | (b3 ? 8u : 0u);
+}
+
+// topn_bits<8>(k, 6): every member but the two weakest, where x is weaker than y when
+// k_x < k_y, or the keys are equal and x has the higher index.  A knockout over the
+// index ranges [0,2), [2,4), ... carries each range's weakest (a) and second weakest (b);
+// a member of a right range is weaker than one of the left range iff its key is <=.
+// Merging ranges L and R: the weakest is the weaker of the two a's, the second weakest
+// the weaker of the winner's b and the loser's a.
+__device__ __forceinline__ uint32_t top6of8_bits(const float (&k)[8]) {
+    float ka[4], kb[4];
+    int ia[4], ib[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const bool r = k[2 * q + 1] <= k[2 * q];
+        ka[q] = r ? k[2 * q + 1] : k[2 * q];
+        kb[q] = r ? k[2 * q] : k[2 * q + 1];
+        ia[q] = r ? 2 * q + 1 : 2 * q;
+        ib[q] = r ? 2 * q : 2 * q + 1;
+    }
+    auto merge = [](float la, float lb, int lia, int lib, float ra, float rb, int ria, int rib, float& ma, float& mb,
+                    int& mia, int& mib) __attribute__((always_inline)) {
+        const bool r = ra <= la;   // the right range holds the weakest
+        ma = r ? ra : la;
+        mia = r ? ria : lia;
+        const float kr = r ? rb : ra, kl = r ? la : lb;   // the right and the left candidate
+        const int ir = r ? rib : ria, il = r ? lia : lib;
+        const bool rr = kr <= kl;
+        mb = rr ? kr : kl;
+        mib = rr ? ir : il;
+    };
+    float a01, b01, a23, b23, a, b;
+    int i01, j01, i23, j23, ia8, ib8;
+    merge(ka[0], kb[0], ia[0], ib[0], ka[1], kb[1], ia[1], ib[1], a01, b01, i01, j01);
+    merge(ka[2], kb[2], ia[2], ib[2], ka[3], kb[3], ia[3], ib[3], a23, b23, i23, j23);
+    merge(a01, b01, i01, j01, a23, b23, i23, j23, a, b, ia8, ib8);
+    return 0xffu & ~((1u << ia8) | (1u << ib8));
 }
 
 // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) as a counter-based
