@@ -186,6 +186,34 @@ def test_prune_pack_fused(nm, case):
     assert np.array_equal(u32_np(idx), i_ref)
 
 
+@pytest.mark.parametrize("kind,mode", [("pack24", "mag"), ("pack24", "hess"), ("slide68", "mag"), ("slide68", "hess")])
+def test_fused_topn_ties_and_special_values(nm, kind, mode):
+    """The fused 2-of-4 and 6-of-8 selections on weights drawn from a handful of values
+    (ties in most groups), with NaN, infinities and signed zeros: masks, values and
+    indices bit for bit against the oracle's counting rule."""
+    g = np.random.default_rng(41 + (kind == "slide68") + 2 * (mode == "hess"))
+    R, K = 53, 1024
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.0, -2.0, 0.5, np.nan, np.inf, -np.inf], np.float32)
+    Wf = pool[g.choice(len(pool), (R, K), p=[0.2, 0.1, 0.15, 0.15, 0.1, 0.1, 0.1, 0.04, 0.03, 0.03])]
+    W = _bf16(Wf)
+    Hn = g.choice(np.array([0.25, 0.5, 1.0], np.float32), K) if mode == "hess" else None
+    smode = nm.NM_SCORE_HESSIAN if mode == "hess" else nm.NM_SCORE_MAGNITUDE
+    Hd = torch.from_numpy(Hn).to(dev()) if Hn is not None else None
+    S = O.score(host(W), Hn, 1e-6, O.SCORE_HESSIAN if mode == "hess" else O.SCORE_MAGNITUDE)
+    if kind == "pack24":
+        vals, idx, mask = nm.nm_prune_pack(W.to(dev()), Hd, 1e-6, smode, 2, 4)
+        m_ref = O.topn_mask(S, 2, 4)
+        v_ref, i_ref = O.pack(host(W), m_ref, 2, 4, O.BF16)
+    else:
+        vals, idx, mask = nm.nm_prune_slide(W.to(dev()), Hd, 1e-6, smode, 4)
+        m_ref = O.topn_mask(S, 6, 8)
+        v_ref, i_ref, bad = O.slide_decompose(host(W), m_ref, 4)
+        assert bad == 0
+    assert np.array_equal(mask.cpu().numpy(), m_ref)
+    assert np.array_equal(host(vals).view(np.uint16), v_ref.view(np.uint16))
+    assert np.array_equal(u32_np(idx), i_ref)
+
+
 def test_prune_pack_ternary_quant_then_mask(nm):
     """Mask from the bf16 master weights, values from the ternary code."""
     Wf, Wt = synth.ternary68_weights(R=70, K=256)
