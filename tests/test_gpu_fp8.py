@@ -69,7 +69,7 @@ def _absdot(Xc, Wc, mask):
     return np.abs(O.e4m3_decode(Xc)).astype(np.float64) @ np.abs(Wm).T
 
 
-@pytest.mark.parametrize("Mt,K", [(1, 64), (5, 8), (37, 2560), (300, 4096), (2, 4104)])
+@pytest.mark.parametrize("Mt,K", [(1, 64), (5, 8), (37, 2560), (300, 4096), (257, 1032), (2, 4104)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_quant_lift_fp8_bit_exact(nm, Mt, K, Ns):
     g = np.random.default_rng(Mt * 17 + K + Ns)

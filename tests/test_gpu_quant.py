@@ -28,7 +28,7 @@ def _x(g, Mt, K):
     return X
 
 
-@pytest.mark.parametrize("Mt,K", [(1, 64), (5, 8), (37, 2560), (300, 4096), (2, 4104)])
+@pytest.mark.parametrize("Mt,K", [(1, 64), (5, 8), (37, 2560), (300, 4096), (257, 1032), (2, 4104)])
 @pytest.mark.parametrize("Ns", [0, 4])
 def test_quant_lift_bit_exact(nm, Mt, K, Ns):
     _quant_case(nm, Mt, K, Ns)
