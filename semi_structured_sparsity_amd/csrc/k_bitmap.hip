@@ -428,82 +428,104 @@ __global__ __launch_bounds__(256, 2) void bitmap_dense_kernel(BitmapArgs a) {
 // row, lane l expanding the row's 8-column groups l, l + 64, l + 128, ... (the stage-1
 // window decode above: consecutive lanes take consecutive stretches of the value row, so
 // a wave's loads cover it contiguously) and multiplying each with the tokens' 8 columns
-// (f32 multiply-adds in column order, groups in lane order).  U groups per lane are in
-// flight at once: their bitmap words, table entries and token columns are loaded
-// together, then their value windows, so a row costs two memory round trips per U groups
-// rather than two per group.  The lanes' sums are added by a butterfly across the wave,
-// whose result is the same on every lane and every run.
+// (f32 multiply-adds in column order, groups in lane order).  A step takes U groups per
+// lane; a wave walks the (row, step) pairs of its rows in one sequence, and the next
+// step's bitmap words, table entries and token columns are loaded while this step's value
+// windows load and multiply, so a step waits for one memory round trip, not two
+// (slide68 at one token 45 -> 41 us with U = 2; U = 4 held too many registers, 43.5 us,
+// and without the overlap U = 4 was the best, U = 8 and 16 slower).  The lanes' sums are
+// added by a butterfly across the wave, whose result is the same on every lane and run.
 constexpr int kBmRowTokens = 4;
 
 template <int MT, int U>
 __global__ __launch_bounds__(256) void bitmap_rows_kernel(BitmapArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t groups = a.K / 8, vchunks = a.ldv / 8;
+    const int64_t steps = (groups + 64 * U - 1) / (64 * U);   // per row, >= 1
+    const int64_t wstride = (int64_t)gridDim.x * 4;
     const int mt = (int)a.Mtok;   // <= MT
-    for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < a.R; r += (int64_t)gridDim.x * 4) {
-        const uint16_t* vrow = a.vals + r * a.ldv;
-        const uint8_t* mrow = a.mask + r * a.ldm;
-        const int32_t* orow = a.offs + r * a.ldo;
-        float acc[MT];
+    int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= a.R) return;   // the whole wave; this kernel has no barrier
+    uint64_t bits[U], nbits[U];
+    int32_t off[U], noff[U];
+    uint4 xv[U][MT], nxv[U][MT];
+    // step st of row rr: groups st * 64 U + lane + 64 u (past the row: its last group, unused)
+    auto meta = [&](int64_t rr, int64_t st, uint64_t (&b)[U], int32_t (&o)[U], uint4 (&x)[U][MT])
+                    __attribute__((always_inline)) {
+        const uint8_t* mrow = a.mask + rr * a.ldm;
+        const int32_t* orow = a.offs + rr * a.ldo;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-        for (int64_t g0 = lane; g0 < groups; g0 += 64 * U) {
-            // groups past the row are clamped to its last group and contribute nothing
-            int64_t gc[U];
-            bool ok[U];
-            uint64_t bits[U];
-            int32_t off[U];
-            uint4 xv[U][MT];
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = st * 64 * U + lane + 64 * u, gc = g < groups ? g : groups - 1;
+            b[u] = g < groups ? *(const uint64_t*)(mrow + (gc >> 3) * 8) : 0ull;
+            o[u] = orow[gc >> 3];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t g = g0 + 64 * u;
-                ok[u] = g < groups;
-                gc[u] = ok[u] ? g : groups - 1;
-                bits[u] = *(const uint64_t*)(mrow + (gc[u] >> 3) * 8);
-                off[u] = orow[gc[u] >> 3];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    xv[u][m] = *(const uint4*)(a.X + (m < mt ? m : 0) * a.ldx + gc[u] * 8);
-            }
-            BmWindow wnd[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) wnd[u] = bm_fetch(ok[u] ? bits[u] : 0ull, off[u], (int)(gc[u] & 7), vrow, vchunks);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!ok[u]) continue;
-                const uint4 wv = bm_expand(wnd[u]);
-                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-                float w[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w[2 * e] = __uint_as_float(ww[e] << 16);
-                    w[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint32_t xx[4] = {xv[u][m].x, xv[u][m].y, xv[u][m].z, xv[u][m].w};
-                    float t = acc[m];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t = __fmaf_rn(w[2 * e], __uint_as_float(xx[e] << 16), t);
-                        t = __fmaf_rn(w[2 * e + 1], __uint_as_float(xx[e] & 0xffff0000u), t);
-                    }
-                    acc[m] = t;
-                }
-            }
+            for (int m = 0; m < MT; ++m) x[u][m] = *(const uint4*)(a.X + (m < mt ? m : 0) * a.ldx + gc * 8);
         }
+    };
+    meta(r, 0, bits, off, xv);
+    float acc[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    int64_t st = 0;
+    while (true) {
+        const uint16_t* vrow = a.vals + r * a.ldv;
+        BmWindow wnd[U];
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
-        if (lane == 0) {
+        for (int u = 0; u < U; ++u) wnd[u] = bm_fetch(bits[u], off[u], lane & 7, vrow, vchunks);
+        const bool last = st + 1 == steps;
+        const int64_t rn = last ? r + wstride : r, sn = last ? 0 : st + 1;
+        const bool more = rn < a.R;
+        if (more) meta(rn, sn, nbits, noff, nxv);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (st * 64 * U + lane + 64 * u >= groups) continue;   // past the row
+            const uint4 wv = bm_expand(wnd[u]);
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[2 * e] = __uint_as_float(ww[e] << 16);
+                w[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if (m < mt) {
-                    if (a.ydt == NM_F32) ((float*)a.Y)[m * a.ldy + r] = acc[m];
-                    else ((uint16_t*)a.Y)[m * a.ldy + r] = (uint16_t)f32_to_bf16_bits(acc[m]);
+                const uint32_t xx[4] = {xv[u][m].x, xv[u][m].y, xv[u][m].z, xv[u][m].w};
+                float t = acc[m];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    t = __fmaf_rn(w[2 * e], __uint_as_float(xx[e] << 16), t);
+                    t = __fmaf_rn(w[2 * e + 1], __uint_as_float(xx[e] & 0xffff0000u), t);
+                }
+                acc[m] = t;
+            }
+        }
+        if (last) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) acc[m] += __shfl_xor(acc[m], o);
+            if (lane == 0) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m < mt) {
+                        if (a.ydt == NM_F32) ((float*)a.Y)[m * a.ldy + r] = acc[m];
+                        else ((uint16_t*)a.Y)[m * a.ldy + r] = (uint16_t)f32_to_bf16_bits(acc[m]);
+                    }
                 }
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+        }
+        if (!more) break;
+        r = rn;
+        st = sn;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            bits[u] = nbits[u];
+            off[u] = noff[u];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xv[u][m] = nxv[u][m];
         }
     }
 }
@@ -565,8 +587,8 @@ nm_status launch_bitmap_spmm(const void* X, int64_t Mtok, int64_t K, int64_t ldx
     if (Mtok <= kBmRowTokens) {
         // 4 waves (rows) per block, up to 8 blocks per CU
         const dim3 g((unsigned)grid_cap(ceil_div(R, 4), 2048));
-        if (Mtok == 1) hipLaunchKernelGGL((bitmap_rows_kernel<1, 4>), g, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((bitmap_rows_kernel<kBmRowTokens, 4>), g, dim3(256), 0, s, a);
+        if (Mtok == 1) hipLaunchKernelGGL((bitmap_rows_kernel<1, 2>), g, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((bitmap_rows_kernel<kBmRowTokens, 2>), g, dim3(256), 0, s, a);
         return check_launch("nm_spmm_bitmap");
     }
     const size_t db = bm_dense_bytes(Mtok, K, R);
