@@ -230,8 +230,9 @@ void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t l
 // The blend of one chosen step (m_step) is kept and written out when asked for.
 // SMAX bounds the step count at compile time so that the per-step sums live in
 // registers.  The gate uses the hardware 2^x and reciprocal (about 1 ulp each):
-// sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)).  A step with beta = 1 blends nothing
-// of the sigmoid: its m is the hard target and contributes 0 to L_mid.
+// sigmoid(z/T) = 1 / (1 + 2^(-z * log2(e) / T)); the blend (1 - beta) g + beta h and the
+// sum of m (1 - m) are fused multiply-adds.  A step with beta = 1 blends nothing of the
+// sigmoid: its m is the hard target and contributes 0 to L_mid.
 __device__ __forceinline__ uint32_t group_topn_bits(const float* key, int g0, int M, int N) {
     uint32_t gb = 0;
     for (int i = 0; i < M; ++i) {
@@ -324,9 +325,9 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
                         if (HALVING && (t & 3) != 0) e[i] = e[i] * e[i];
                         else e[i] = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
                         const float g = __builtin_amdgcn_rcpf(1.0f + e[i]);
-                        m[i] = (1.0f - beta[t]) * g + beta[t] * hv[i];
+                        m[i] = __builtin_fmaf(1.0f - beta[t], g, beta[t] * hv[i]);
                         const float mm = i < ne ? m[i] : 0.f;   // past the row end: adds 0
-                        acc += mm * (1.0f - mm);
+                        acc = __builtin_fmaf(mm, 1.0f - mm, acc);
                     }
                     lm[t] += (double)acc;
                 }
@@ -443,8 +444,8 @@ __global__ __launch_bounds__(kRedThreads) void gate_fast_kernel(const float* __r
                 if (HALVING && (t & 3) != 0) e[i] = e[i] * e[i];
                 else e[i] = __builtin_amdgcn_exp2f(-z[i] * cs[t]);
                 const float g = __builtin_amdgcn_rcpf(1.0f + e[i]);
-                const float m = wg * g + (h[i] ? beta : 0.f);
-                acc += m * (1.0f - m);
+                const float m = __builtin_fmaf(wg, g, h[i] ? beta : 0.f);
+                acc = __builtin_fmaf(m, 1.0f - m, acc);
                 if constexpr (WANT_M) mo[i] = t == m_step ? m : mo[i];
             }
             lm[t] += (double)acc;
