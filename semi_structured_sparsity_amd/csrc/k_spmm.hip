@@ -1140,10 +1140,12 @@ __device__ __forceinline__ Moments store_score_tile(const SpmmArgs& a, const f32
 // s_{P-1}, so that after probe p it holds s_p .* (D_{p-1} + s_p .* G_p).  Each lane's
 // signs are four Rademacher words per probe (its two rows of U, two 64-column blocks).
 // GEN: the Hutchinson first product U [P*R, n] = V X^T: the A operand is the calibration
-// rows X [n, K] (vals), the B operand the stacked probe rows q = p R + o of V, generated
-// into the B stages (one Rademacher word per row and 64 columns; each of the 512 threads
-// expands half a stage row into swizzled 16-byte chunks); the barrier that follows every
-// stage's issue covers these LDS writes as it covers the DMA.
+// rows X [n, K] (vals), the B operand the stacked probe rows q = p R + o of V, made in
+// registers: a stage's 64 columns of a row are one Rademacher word, which each lane turns
+// into its +-1 bf16 fragments with a few bit operations per depth.  The B operand never
+// passes through LDS (measured: the whole Hutchinson call 6.62-6.74 -> 6.23-6.34 ms
+// against signs written into LDS stages and read back as fragments; a 3- or 4-slot ring
+// for the A stages then measured the same as 2).
 // HUTCH_SCORE: HUTCH whose epilogue writes the score of D (store_score_tile) and the block's
 // moments of it instead of D.
 // MODE: 0 plain, 1 HUTCH, 2 GEN, 3 HUTCH_SCORE.
@@ -1154,7 +1156,8 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     constexpr int ROWB = SK * 2, CH = ROWB / 16, D = SK / 16;   // bytes and chunks per row per stage, depths
     static_assert(SK == 64 || SK == 32, "64- or 32-column stages");
     static_assert(D % 2 == 0, "depth ping-pong needs an even depth count");
-    constexpr int WSTAGE = BR * ROWB, XSTAGE = BT * ROWB, SLOT = WSTAGE + XSTAGE;
+    // GEN: the B operand is made in registers, so a slot holds the A stage alone
+    constexpr int WSTAGE = BR * ROWB, XSTAGE = BT * ROWB, SLOT = WSTAGE + (GEN ? 0 : XSTAGE);
     constexpr int RING = NS * SLOT;
     constexpr int NWL = WSTAGE / 1024 / NW, NXL = XSTAGE / 1024 / NW;   // loads per wave per stage
     static_assert(WSTAGE % (1024 * NW) == 0 && XSTAGE % (1024 * NW) == 0 && NWL >= 1 && NXL >= 1, "loads per wave");
@@ -1177,15 +1180,16 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     const void* baseX = uniform_ptr(a.X + t0 * a.ldx * 2);
     const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
     uint32_t oW[NWL], oX[NXL];
-    // GEN: this thread's row of the B stage and its stacked probe row (p, o)
-    static_assert(!GEN || (BT == 256 && NW == 8), "GEN: 512 threads cover 256 rows in halves");
-    const int grow = tid >> 1, ghalf = tid & 1;
-    int gp = 0;
-    int64_t go = 0;
+    // GEN: half-wave h of a lane's B sub-tiles j = 0, 1 draws the Rademacher words of
+    // sub-tile j = h's row (its stacked probe row q = p R + o); the counter of stage s is
+    // gctr + s (64-column stages)
+    static_assert(!GEN || (ST == 2 && SK == 64), "GEN: two token sub-tiles, one word per row and stage");
+    uint64_t gctr = 0;
     if constexpr (GEN) {
-        const int64_t q = t0 + grow, qc = q < a.Mtok ? q : a.Mtok - 1;
-        gp = (int)(qc / a.prows);
-        go = qc - (int64_t)gp * a.prows;
+        const int64_t q = t0 + (wt * ST + (lane >> 5)) * 32 + (lane & 31), qc = q < a.Mtok ? q : a.Mtok - 1;
+        const int gp = (int)(qc / a.prows);
+        const int64_t go = qc - (int64_t)gp * a.prows;
+        gctr = ((uint64_t)gp << 40) + (uint64_t)go * (uint64_t)(a.K / 64);
     }
     constexpr int RPL = 64 / CH;   // rows per DMA instruction
 #pragma unroll
@@ -1207,18 +1211,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         const uint32_t xp = HUTCH ? (uint32_t)(s / PS) * (uint32_t)(a.Mtok * a.ldx * 2) : 0u;
 #pragma unroll
         for (int i = 0; i < NWL; ++i) dma16s(slot + (wave * NWL + i) * 1024, baseW, oW[i] + (uint32_t)(ks * ROWB));
-        if constexpr (GEN) {
-            // the stage's SK columns are bits [SK * (s % (64 / SK)), +SK) of the row's word of
-            // its 64-column block; this thread writes CH / 2 chunks of 8 columns
-            const uint64_t w = rad_word(a.seed, gp, go, s / (64 / SK), a.K / 64);
-            const int bb = (SK == 32 ? 4 * (s & 1) : 0) + ghalf * (CH / 2);   // first sign byte
-            uint8_t* xrow = smem + (s % NS) * SLOT + WSTAGE + grow * ROWB;
-#pragma unroll
-            for (int c = 0; c < CH / 2; ++c) {
-                const int cl = ghalf * (CH / 2) + c;
-                *(uint4*)(xrow + ((cl ^ sw(grow)) * 16)) = signs_to_bf16x8((uint32_t)(w >> (8 * (bb + c))) & 0xffu);
-            }
-        } else {
+        if constexpr (!GEN) {
 #pragma unroll
             for (int i = 0; i < NXL; ++i)
                 dma16s(slot + WSTAGE + (wave * NXL + i) * 1024, baseX, oX[i] + xp + (uint32_t)(ks * ROWB));
@@ -1236,10 +1229,36 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
             const int row = (wr * SR + i) * 32 + l32;
             f.a[i] = *(const i32x4_t*)(sW + row * ROWB + ((2 * d + h) ^ sw(row)) * 16);
         }
+        if constexpr (!GEN) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                const int tok = (wt * ST + j) * 32 + l32;
+                f.b[j] = *(const i32x4_t*)(sX + tok * ROWB + ((2 * d + h) ^ sw(tok)) * 16);
+            }
+        }
+    };
+    // GEN: the stage's words of sub-tiles j = 0, 1 (as dword pairs) for every lane: this
+    // half-wave's word and, across the halves, the other's
+    auto gen_words = [&](int s, uint32_t (&w)[ST][2]) __attribute__((always_inline)) {
+        const uint64_t z = splitmix64_at(a.seed, gctr + (uint64_t)s);
+        const uint32_t lo = (uint32_t)z, hi = (uint32_t)(z >> 32);
+        const uint32_t olo = (uint32_t)__shfl_xor((int)lo, 32), ohi = (uint32_t)__shfl_xor((int)hi, 32);
+        w[0][0] = h ? olo : lo;
+        w[0][1] = h ? ohi : hi;
+        w[1][0] = h ? lo : olo;
+        w[1][1] = h ? hi : ohi;
+    };
+    // GEN: depth d's B fragment of sub-tile j is columns 16 d + 8 h .. +8 of the stage, i.e.
+    // sign byte 2 d + h of the row's word; bf16 pair e of it is 0x3F80 | sign << 15 for
+    // columns 2e and 2e+1: with v = u | u << 15, v << (15 - 2e) carries bit 2e of u to bit
+    // 15 and bit 2e+1 to bit 31
+    auto make_b = [&](int d, const uint32_t (&w)[ST][2], Frag& f) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
-            const int tok = (wt * ST + j) * 32 + l32;
-            f.b[j] = *(const i32x4_t*)(sX + tok * ROWB + ((2 * d + h) ^ sw(tok)) * 16);
+            const uint32_t u = __builtin_amdgcn_ubfe(w[j][d >> 1], 16 * (d & 1) + 8 * h, 8);
+            const uint32_t v = u | (u << 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f.b[j][e] = (int)(((v << (15 - 2 * e)) & 0x80008000u) | 0x3F803F80u);
         }
     };
     f32x16_t acc[SR][ST];
@@ -1285,13 +1304,14 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     constexpr int PER = NWL + (GEN ? 0 : NXL);   // DMA loads per stage
     // a depth's SR + ST fragment reads, one after each of its first SR + ST MFMAs (in the
     // scheduling region that holds them)
+    constexpr int NRD = GEN ? SR : SR + ST;   // LDS fragment reads per depth
     auto interleave_reads_mfmas = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < SR + ST; ++i) {
+        for (int i = 0; i < NRD; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, SR * ST - (SR + ST), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SR * ST - NRD, 0);
         __builtin_amdgcn_sched_barrier(0);   // the next depth is a region of its own
     };
     // Prologue: stages 0..NS-1 fill the ring; wait for stage 0 (the others may stay in
@@ -1305,8 +1325,16 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         if (p < nsteps) issue(p);
     if (nsteps >= NS) wait_vm_barrier<(NS - 1) * PER>();
     else wait_vm_barrier<0>();
+    uint32_t gw[ST][2], gn[ST][2];   // GEN: the words of stages s and s + 1
     read_depth(0, 0, fr[0]);
+    if constexpr (GEN) {
+        gen_words(0, gw);
+        make_b(0, gw, fr[0]);
+    }
     for (int s = 0; s < nsteps; ++s) {
+        if constexpr (GEN) {
+            if (s + 1 < nsteps) gen_words(s + 1, gn);
+        }
         if constexpr (HUTCH) {
             if (s % PS == 0) {   // probe p = s / PS begins: acc *= s_{p-1} s_p (s_p for p = 0)
                 const int p = s / PS;
@@ -1326,6 +1354,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         for (int d = 0; d < D; ++d) {
             if (d + 1 < D) {
                 read_depth(s, d + 1, fr[(d + 1) & 1]);
+                if constexpr (GEN) make_b(d + 1, gw, fr[(d + 1) & 1]);
             } else {
                 // the last depth's fragments complete before the branch (the barrier below
                 // waits for them anyway), so the MFMAs after the join wait for nothing
@@ -1337,10 +1366,18 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
                     else wait_vm_barrier<0>();
                     if (s + NS < nsteps) issue(s + NS);
                     read_depth(s + 1, 0, fr[0]);
+                    if constexpr (GEN) make_b(0, gn, fr[0]);
                 }
             }
             mfmas(fr[d & 1]);
             if (d + 1 < D) interleave_reads_mfmas();
+        }
+        if constexpr (GEN) {
+#pragma unroll
+            for (int j = 0; j < ST; ++j) {
+                gw[j][0] = gn[j][0];
+                gw[j][1] = gn[j][1];
+            }
         }
     }
     if constexpr (HUTCH) {   // acc *= s_{P-1}
