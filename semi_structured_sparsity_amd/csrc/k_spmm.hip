@@ -1277,17 +1277,25 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     // HUTCH: a lane's sign words of a probe, per token sub-tile j (a row o of U) and 64-column
     // block of its A rows (sub-tiles 0-1 and 2-3), recomputed where needed rather than kept
     // live across the loop; flip multiplies acc by the signs of w
+    // (element e of sub-tile i is column 64 m + 32 (i & 1) + 8 (e / 4) + 4 h + e % 4 of a
+    // 64-column block m: bit 8 (e / 4) + e % 4 of the word's half i & 1 shifted down by 4 h;
+    // adding bit << 31 toggles the sign bit)
     auto flip = [&](const uint64_t (&w)[ST][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SR; ++i)
 #pragma unroll
-            for (int j = 0; j < ST; ++j)
+            for (int j = 0; j < ST; ++j) {
+                const uint32_t x = (uint32_t)(w[j][i >> 1] >> (32 * (i & 1) + 4 * h));
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int k = (wr * SR + i) * 32 + 8 * (e / 4) + 4 * h + (e % 4);   // multiple-of-64 base
-                    const uint32_t bit = (uint32_t)(w[j][i >> 1] >> (k & 63)) & 1u;
-                    acc[i][j][e] = __uint_as_float(__float_as_uint(acc[i][j][e]) ^ (bit << 31));
+                    // written out, or the compiler turns the extract and shift into a
+                    // shift and a mask (three operations instead of two)
+                    const uint32_t bit = __builtin_amdgcn_ubfe(x, 8 * (e / 4) + (e % 4), 1);
+                    uint32_t r;
+                    asm("v_lshl_add_u32 %0, %1, 31, %2" : "=v"(r) : "v"(bit), "v"(__float_as_uint(acc[i][j][e])));
+                    acc[i][j][e] = __uint_as_float(r);
                 }
+            }
     };
     auto probe_words = [&](int p, uint64_t (&w)[ST][2]) __attribute__((always_inline)) {
         const int64_t kblocks = a.R / 64;
@@ -1326,6 +1334,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
     if (nsteps >= NS) wait_vm_barrier<(NS - 1) * PER>();
     else wait_vm_barrier<0>();
     uint32_t gw[ST][2], gn[ST][2];   // GEN: the words of stages s and s + 1
+    uint64_t wp[ST][2] = {};         // HUTCH: the sign words of the previous probe (none: 0)
     read_depth(0, 0, fr[0]);
     if constexpr (GEN) {
         gen_words(0, gw);
@@ -1337,16 +1346,16 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
         }
         if constexpr (HUTCH) {
             if (s % PS == 0) {   // probe p = s / PS begins: acc *= s_{p-1} s_p (s_p for p = 0)
-                const int p = s / PS;
-                uint64_t wn[ST][2], wo[ST][2];
-                probe_words(p, wn);
-                if (p > 0) {
-                    probe_words(p - 1, wo);
+                uint64_t wn[ST][2];
+                probe_words(s / PS, wn);
 #pragma unroll
-                    for (int j = 0; j < ST; ++j)
+                for (int j = 0; j < ST; ++j)
 #pragma unroll
-                        for (int b = 0; b < 2; ++b) wn[j][b] ^= wo[j][b];
-                }
+                    for (int b = 0; b < 2; ++b) {
+                        const uint64_t t = wn[j][b] ^ wp[j][b];
+                        wp[j][b] = wn[j][b];
+                        wn[j][b] = t;
+                    }
                 flip(wn);
             }
         }
@@ -1380,11 +1389,7 @@ __global__ __launch_bounds__(64 * WRN * WTN, 1) void dense_ring_kernel(SpmmArgs 
             }
         }
     }
-    if constexpr (HUTCH) {   // acc *= s_{P-1}
-        uint64_t wl[ST][2];
-        probe_words(a.probes - 1, wl);
-        flip(wl);
-    }
+    if constexpr (HUTCH) flip(wp);   // acc *= s_{P-1}
     wait_vm_all();
     __syncthreads();
     if constexpr (MODE == 3) {
