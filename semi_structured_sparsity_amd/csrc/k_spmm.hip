@@ -1995,6 +1995,7 @@ struct SpmmPlan {
     int mid;     // K-split ring: 0 none, else 32-token sub-tiles per block (1, 2 or 4)
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int xres;    // K-split ring with X resident in LDS (up to 64 KB, 8-stage weight ring)
+    int sr1;     // K-split ring on 32-row tiles (one-byte codes up to 32 tokens)
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
@@ -2049,6 +2050,19 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok, bool 
             p.tiles_r = (int)ceil_div(R, 64);
             p.tiles_t = (int)ceil_div(Mtok, 32 * p.mid);
             p.nsteps = (int)(K / KOm);
+            // one-byte codes up to 32 tokens: where 64-row tiles are too few for the CUs (their
+            // stages would be split over blocks, with a reduce launch after) but 32-row tiles
+            // make at least as many blocks as that split and fit one round, the 32-row tiles
+            // run unsplit.  A block then streams the same bytes (half the rows, all the
+            // stages) and the partials and their reduce launch are gone.
+            p.sr1 = 0;
+            if (sizeof(T) == 1 && p.mid == 1) {
+                const int64_t t32 = ceil_div(R, 32) * p.tiles_t;
+                if ((int64_t)p.tiles_r * p.tiles_t < 160 && t32 >= 160 && t32 <= device_cus()) {
+                    p.sr1 = 1;
+                    p.tiles_r = (int)ceil_div(R, 32);
+                }
+            }
             int KS = 1;
             while ((int64_t)p.tiles_r * p.tiles_t * KS < 160 && p.nsteps >= 8 * KS) KS *= 2;
             p.steps_per_split = (int)ceil_div(p.nsteps, KS);
@@ -2307,7 +2321,18 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void*
         // up to 32 tokens a 6-stage ring (17 KB a stage): more weight bytes in flight per CU
         // when the weight comes from HBM (measured 13-15% faster there at one token; a
         // 6-stage ring for 64 tokens measured no faster than 3 stages)
-        if (lift) {   // 6:8: the activation is lifted inside the kernel (one-byte codes: up to 64 tokens)
+        if (p.sr1) {
+            // 32-row tiles of one-byte codes: a 12-stage ring (13 KB a stage), 16 weight
+            // stages beside a resident X
+            if constexpr (sizeof(T) == 1) {
+                if (lift) hipLaunchKernelGGL((spmm_ringk_kernel<T, 1, 1, 256, 12, true>), grid, dim3(256), 0, s, a);
+                else if (p.xres)
+                    hipLaunchKernelGGL((spmm_ringk_kernel<T, 1, 1, 256, 16, false, kXresBytes>), grid, dim3(256), 0, s, a);
+                else hipLaunchKernelGGL((spmm_ringk_kernel<T, 1, 1, 256, 12, false>), grid, dim3(256), 0, s, a);
+            } else {
+                return set_error(NM_ERR_DEVICE, "nm_spmm: 32-row K-split tiles are for one-byte codes");
+            }
+        } else if (lift) {   // 6:8: the activation is lifted inside the kernel (one-byte codes: up to 64 tokens)
             if (p.mid == 1) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 1, 256, 6, true>), grid, dim3(256), 0, s, a);
             else if (p.mid == 2) hipLaunchKernelGGL((spmm_ringk_kernel<T, 2, 2, 256, 3, true>), grid, dim3(256), 0, s, a);
             else if constexpr (sizeof(T) == 2)

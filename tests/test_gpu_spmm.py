@@ -176,6 +176,47 @@ def test_spmm_int8_exact(nm, Mt, R, K, Ns):
     assert np.array_equal(y, y_ref)
 
 
+# One-byte codes at up to 32 tokens on weights whose 64-row tiles are too few for the CUs but
+# whose 32-row tiles fill one round (160..256 of them on 256 CUs) run the K-split ring on
+# 32-row tiles without splitting K: lifted in the kernel (6:8) and plain 2:4, the resident-X
+# form at one token, ragged row counts and every token row of a 32-token tile.
+@pytest.mark.parametrize("dt,Ns,Mt,R,K", [("i8", 4, 1, 6912, 2560), ("i8", 0, 1, 6912, 2560), ("i8", 4, 17, 5200, 2560),
+                                          ("i8", 0, 32, 8192, 1024), ("i8", 0, 5, 5150, 768), ("fp8", 4, 3, 5200, 2560),
+                                          ("fp8", 0, 32, 6000, 512),
+                                          ("i8", 0, 32, 5200, 2560)])
+def test_spmm_one_byte_32row_tiles_exact(nm, dt, Ns, Mt, R, K):
+    g = np.random.default_rng(Mt + R + K + Ns + len(dt))
+    if dt == "i8":
+        X, W = g.integers(-127, 128, (Mt, K)).astype(np.int8), g.integers(-1, 2, (R, K)).astype(np.int8)
+        S = W.astype(np.float32)
+    else:
+        X = O.e4m3_encode(g.integers(-8, 9, (Mt, K)).astype(np.float32))
+        W = O.e4m3_encode(g.integers(-4, 5, (R, K)).astype(np.float32))
+        S = O.e4m3_decode(W)
+    Wc = W.view(np.int8) if dt == "fp8" else W
+    if Ns:
+        mask = O.topn_mask(np.abs(S) + g.random((R, K)).astype(np.float32), 6, 8)
+        vals, idx, bad = O.slide_decompose(Wc, mask, Ns)
+        assert bad == 0
+    else:
+        mask = O.topn_mask(np.abs(S) + g.random((R, K)).astype(np.float32), 2, 4)
+        vals, idx = O.pack(Wc, mask, 2, 4)
+    i = torch.from_numpy(idx.view(np.int32)).to(dev())
+    if dt == "i8":
+        v, Xd, ydt = torch.from_numpy(vals).to(dev()), torch.from_numpy(X).to(dev()), nm.NM_I32
+        ref, _ = O.masked_matmul_i8(X, W, mask, np.ones(Mt, np.float32), 1.0)
+    else:
+        v = torch.from_numpy(vals.view(np.uint8)).view(torch.float8_e4m3fn).to(dev())
+        Xd = torch.from_numpy(X).view(torch.float8_e4m3fn).to(dev())
+        ydt = nm.NM_F32
+        ref = O.masked_matmul_fp8(X, W, mask)
+    if Ns == 0:
+        # unsplit: the plan needs no split-K partials
+        assert nm.raw.nm_spmm_workspace(Mt, K, R, 0, nm.dtype_code(Xd)) == 0
+    Y = nm.nm_spmm(Xd, v, i, R=R, Ns=Ns, ydt=ydt).cpu().numpy()
+    assert np.array_equal(Y.astype(np.float64), np.asarray(ref, np.float64))
+
+
 # (2N-2):2N for other N: (tokens, rows, K) with K a multiple of 2N and the lifted width a
 # multiple of 16 (bf16); few-token (K-split ring, or the weight-streaming kernel when the
 # lifted width is off the ring's stage grid), many-token ring and register-staged shapes
