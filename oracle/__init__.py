@@ -43,6 +43,21 @@ def build(force: bool = False) -> Path:
     return _LIB
 
 
+SANITIZE_FLAGS = ["-std=c11", "-O1", "-g", "-fopenmp", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer"]
+
+
+def build_sanitize_check(out: Path | None = None) -> Path:
+    """Compile sanitize_check.c (every oracle routine over exactly sized buffers) with
+    AddressSanitizer and UndefinedBehaviorSanitizer into a standalone program (gcc)."""
+    out = Path(out) if out is not None else _HERE / "sanitize_check"
+    tmp = out.with_name(out.name + f".tmp{os.getpid()}")
+    subprocess.check_call(["gcc", *SANITIZE_FLAGS, "-I", str(_HERE), str(_HERE / "sanitize_check.c"), "-o", str(tmp),
+                           "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 _lib = None
 
 
