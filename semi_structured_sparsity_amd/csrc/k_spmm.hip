@@ -85,6 +85,7 @@ struct SpmmArgs {
     int ydt;
     int nsteps, KS, steps_per_split;
     int tiles_r, tiles_t;
+    int tile_rows;         // K-split ring: weight rows per row tile (0: the tile's height)
     // rank-r adapter term added to the accumulators (bf16 products only; rank 0: none):
     // u [Mtok, rank] (ldu) and the stacked up-projection B [R, rank] (ldb), both bf16
     const uint16_t* lr_u;
@@ -1482,7 +1483,10 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     const int h = lane >> 5, l32 = lane & 31;
     int tr, tt;
     tile_of(blockIdx.x, gridDim.x, a.tiles_r, a.tiles_t, tr, tt);
-    const int64_t r0 = (int64_t)tr * BR, t0 = (int64_t)tt * BT;
+    // a row tile holds TRW <= BR weight rows; its other rows re-read the last one (their
+    // sums are not stored)
+    const int TRW = a.tile_rows > 0 && a.tile_rows < BR ? a.tile_rows : BR;
+    const int64_t r0 = (int64_t)tr * TRW, t0 = (int64_t)tt * BT;
     const int split = blockIdx.y;
     const int s_begin = split * a.steps_per_split;
     const int s_end = (s_begin + a.steps_per_split) < a.nsteps ? (s_begin + a.steps_per_split) : a.nsteps;
@@ -1494,7 +1498,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
     const void* baseA = uniform_ptr(a.vals + r0 * a.ldv * es);
     const void* baseI = uniform_ptr(a.idx + r0 * a.ldi);
     const void* baseB = uniform_ptr(a.X + t0 * a.ldx * es);
-    const int64_t rmax = a.R - 1 - r0, tmax = a.Mtok - 1 - t0;
+    const int64_t rmax = (a.R - 1 - r0) < (TRW - 1) ? (a.R - 1 - r0) : (TRW - 1), tmax = a.Mtok - 1 - t0;
     uint32_t oA[NA], oI[NI], oB[NB > 0 ? NB : 1], oBc[NB > 0 ? NB : 1];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -1709,7 +1713,7 @@ __global__ __launch_bounds__(256, 1) void spmm_ringk_kernel(SpmmArgs a) {
                 AccS v = 0;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) v += __builtin_bit_cast(AccS, red[(w * 64 + src_lane) * kRedStride + e]);
-                if (gt >= a.Mtok || gr >= a.R) continue;
+                if (gt >= a.Mtok || gr >= a.R || 32 * i + row >= TRW) continue;
                 if (a.part) {
                     ((AccS*)a.part)[((int64_t)split * a.Mtok + gt) * a.R + gr] = v;
                     continue;
@@ -1996,6 +2000,7 @@ struct SpmmPlan {
     int skinny;  // 0: none, 1: <=32 tokens, 2: <=64, 3: <=128
     int xres;    // K-split ring with X resident in LDS (up to 64 KB, 8-stage weight ring)
     int sr1;     // K-split ring on 32-row tiles (one-byte codes up to 32 tokens)
+    int tile_rows;   // K-split ring: weight rows per row tile when fewer than the tile height
     int tiles_r, tiles_t, nsteps, KS, steps_per_split;
 };
 
@@ -2050,17 +2055,26 @@ static SpmmPlan plan_for(int64_t Mtok, int64_t K, int64_t R, bool ring_ok, bool 
             p.tiles_r = (int)ceil_div(R, 64);
             p.tiles_t = (int)ceil_div(Mtok, 32 * p.mid);
             p.nsteps = (int)(K / KOm);
-            // one-byte codes up to 32 tokens: where 64-row tiles are too few for the CUs (their
-            // stages would be split over blocks, with a reduce launch after) but 32-row tiles
-            // make at least as many blocks as that split and fit one round, the 32-row tiles
-            // run unsplit.  A block then streams the same bytes (half the rows, all the
-            // stages) and the partials and their reduce launch are gone.
+            // Up to 64 tokens the product streams the weight, and a CU's share of the HBM
+            // bandwidth is set by the reads it keeps in flight, so every CU should stream.
+            // Where 64-row tiles leave CUs idle (or would split K), each row tile takes
+            // ceil(R / (CUs / token tiles)) rows, when that is at least 32: one round of equal
+            // tiles and no split; a tile's rows past its share re-read its last row (L2 hits,
+            // at most half its weight loads; their sums are not stored).  One-byte codes whose
+            // share is 16-32 rows run on 32-row tiles (their index rows fill whole DMA batches
+            // there; bf16 ones do not).
             p.sr1 = 0;
-            if (sizeof(T) == 1 && p.mid == 1) {
-                const int64_t t32 = ceil_div(R, 32) * p.tiles_t;
-                if ((int64_t)p.tiles_r * p.tiles_t < 160 && t32 >= 160 && t32 <= device_cus()) {
-                    p.sr1 = 1;
-                    p.tiles_r = (int)ceil_div(R, 32);
+            p.tile_rows = 0;
+            if (p.mid <= 2) {
+                const int64_t per = device_cus() / p.tiles_t;
+                if (per >= 1 && (int64_t)p.tiles_r < per) {
+                    const int64_t rows = ceil_div(R, per);
+                    const bool one32 = sizeof(T) == 1 && p.mid == 1 && rows <= 32;
+                    if (rows < 64 && (rows >= 32 || (one32 && rows >= 16))) {
+                        p.tile_rows = (int)rows;
+                        p.tiles_r = (int)ceil_div(R, rows);
+                        p.sr1 = one32 ? 1 : 0;
+                    }
                 }
             }
             int KS = 1;
@@ -2300,6 +2314,7 @@ static nm_status run_spmm(SpmmArgs a, bool ring_ok, bool lift, void* part, void*
     a.steps_per_split = p.steps_per_split;
     a.tiles_r = p.tiles_r;
     a.tiles_t = p.tiles_t;
+    a.tile_rows = p.tile_rows;
     a.part = p.KS > 1 ? part : nullptr;
     if (a.rank > 0 && !p.ring) {
         // the other kernels carry no adapter term: they write the sparse product in f32

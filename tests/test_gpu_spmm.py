@@ -115,7 +115,8 @@ def test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns):
 # block held in LDS
 FEW = [(1, 1, 16), (2, 300, 48), (3, 257, 4160), (4, 130, 32), (1, 513, 2560), (4, 64, 4096), (1, 1000, 96),
        (32, 200, 4096), (17, 130, 2048),   # X resident in LDS: a full 64 KB range, and 17 valid rows
-       (1, 4096, 4096), (2, 4100, 4096)]   # resident X rows of the whole K on many row tiles
+       (1, 4096, 4096), (2, 4100, 4096),   # resident X rows of the whole K on many row tiles
+       (1, 11008, 1024), (17, 9001, 512), (64, 10000, 256), (40, 14336, 768)]   # row tiles of R / CUs rows
 
 
 @pytest.mark.parametrize("Mt,R,K", FEW)
@@ -176,14 +177,15 @@ def test_spmm_int8_exact(nm, Mt, R, K, Ns):
     assert np.array_equal(y, y_ref)
 
 
-# One-byte codes at up to 32 tokens on weights whose 64-row tiles are too few for the CUs but
-# whose 32-row tiles fill one round (160..256 of them on 256 CUs) run the K-split ring on
-# 32-row tiles without splitting K: lifted in the kernel (6:8) and plain 2:4, the resident-X
+# One-byte codes at up to 64 tokens on weights whose 64-row tiles are too few for the CUs run
+# the K-split ring on row tiles of R / CUs rows without splitting K (32-row tiles for shares of
+# 16-32 rows, 64-row tiles above): lifted in the kernel (6:8) and plain 2:4, the resident-X
 # form at one token, ragged row counts and every token row of a 32-token tile.
 @pytest.mark.parametrize("dt,Ns,Mt,R,K", [("i8", 4, 1, 6912, 2560), ("i8", 0, 1, 6912, 2560), ("i8", 4, 17, 5200, 2560),
                                           ("i8", 0, 32, 8192, 1024), ("i8", 0, 5, 5150, 768), ("fp8", 4, 3, 5200, 2560),
                                           ("fp8", 0, 32, 6000, 512),
-                                          ("i8", 0, 32, 5200, 2560)])
+                                          ("i8", 0, 32, 5200, 2560), ("i8", 0, 3, 9000, 1024), ("fp8", 4, 1, 12000, 512),
+                                          ("i8", 4, 64, 9000, 1024)])
 def test_spmm_one_byte_32row_tiles_exact(nm, dt, Ns, Mt, R, K):
     g = np.random.default_rng(Mt + R + K + Ns + len(dt))
     if dt == "i8":
