@@ -197,6 +197,24 @@ nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw
                   void* vals, int64_t ldv, uint32_t* idx, int64_t ldi, unsigned flags,
                   nm_stream_t stream);
 
+/* The gate/anneal of nm_gate and the packing of W under its hard mask (nm_pack
+ * of hard_mask) in one call ("SparseForge", Methodology 3: the anneal ends in
+ * the hard top-N target, the mask the compressed weight is then stored with).
+ * S, stats, N, M, T0, rho, steps, m_step, m, hard_mask, lmid and the workspace
+ * (nm_gate_workspace(R, K, steps) bytes) as in nm_gate; W [R, K] (ldw) of dtype
+ * wdt, vals [R, ldv] of dtype vdt and idx [R, ldi] as in nm_pack.  Every output
+ * is bit for bit that of nm_gate followed by nm_pack on the same stream.  For
+ * 2:4 with the default 8 steps, bf16 W and vals, K a multiple of 32, 16-byte
+ * aligned S, W and m rows and 8-byte aligned vals rows, one pass reads S and W
+ * once (the pack rides along the gate's vector-bound pass); otherwise the two
+ * kernels run one after the other.  No input may overlap an output or the
+ * workspace, nor outputs each other (NM_ERR_ALIAS). */
+nm_status nm_gate_pack(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats,
+                       int N, int M, float T0, float rho, int steps, int m_step,
+                       float* m, int64_t ldf, uint8_t* hard_mask, int64_t ldm, double* lmid,
+                       const void* W, nm_dtype wdt, int64_t ldw, nm_dtype vdt, void* vals, int64_t ldv,
+                       uint32_t* idx, int64_t ldi, void* ws, size_t ws_bytes, nm_stream_t stream);
+
 /* Fused score -> top-N mask -> pack in one pass over the weight.  The score is
  * taken from Wsc (dtype sdt, lds_ elements; HESSIAN with H/ldh/eps as in
  * nm_score, or MAGNITUDE), the packed values from Wv (dtype wdt, ldwv), which

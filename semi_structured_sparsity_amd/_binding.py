@@ -62,6 +62,8 @@ SIGNATURES = {
     "nm_score_stats": (_I, [_P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "nm_gate_workspace": (_SZ, [_I64, _I64, _I]),
     "nm_gate": (_I, [_P, _I64, _I64, _I64, _P, _I, _I, _F, _F, _I, _I, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
+    "nm_gate_pack": (_I, [_P, _I64, _I64, _I64, _P, _I, _I, _F, _F, _I, _I, _P, _I64, _P, _I64, _P,
+                          _P, _I, _I64, _I, _P, _I64, _P, _I64, _P, _SZ, _P]),
     "nm_mask": (_I, [_P, _I64, _I64, _I64, _I, _I, _P, _I64, _P]),
     "nm_pack": (_I, [_P, _I, _I64, _I64, _I64, _P, _I64, _I, _I, _I, _P, _I64, _P, _I64, _U, _P]),
     "nm_prune_pack": (_I, [_P, _I, _I64, _P, _I64, _F, _I, _P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _I, _P, _I64,
@@ -196,6 +198,25 @@ def nm_gate(S: torch.Tensor, stats: torch.Tensor, N: int, M: int, T0: float, rho
     _check(raw.nm_gate(_ptr(S), R, K, _ld(S), _ptr(stats), N, M, T0, rho, steps, t, _ptr(mf), K, _ptr(hm),
                        hm.shape[1], _ptr(lm), _ptr(ws), ws.numel(), _stream(S)))
     return mf, hm, lm
+
+
+def nm_gate_pack(S: torch.Tensor, stats: torch.Tensor, W: torch.Tensor, N: int, M: int, T0: float, rho: float,
+                 steps: int, want_m: bool = True, m_step: int | None = None, vdt: int | None = None):
+    """nm_gate and the pack of W under its hard mask in one call: returns (m_t or None,
+    hard mask, lmid, vals, idx)."""
+    R, K = S.shape
+    t = steps - 1 if m_step is None else m_step
+    vdt = dtype_code(W) if vdt is None else vdt
+    mf = torch.empty((R, K), dtype=torch.float32, device=S.device) if want_m else None
+    hm = torch.empty((R, (K + 7) // 8), dtype=torch.uint8, device=S.device)
+    lm = torch.empty(steps, dtype=torch.float64, device=S.device)
+    slots = K // M * N
+    vals, idx = _pack_out(R, slots, index_words(slots, M), vdt, S.device)
+    ws = _ws(raw.nm_gate_workspace(R, K, steps), S.device)
+    _check(raw.nm_gate_pack(_ptr(S), R, K, _ld(S), _ptr(stats), N, M, T0, rho, steps, t, _ptr(mf), K, _ptr(hm),
+                            hm.shape[1], _ptr(lm), _ptr(W), dtype_code(W), _ld(W), vdt, _ptr(vals), slots, _ptr(idx),
+                            idx.shape[1], _ptr(ws), ws.numel(), _stream(S)))
+    return mf, hm, lm, vals, idx
 
 
 def nm_mask(S: torch.Tensor, N: int, M: int) -> torch.Tensor:

@@ -396,12 +396,28 @@ __global__ __launch_bounds__(kRedThreads) void gate_kernel(const float* __restri
 // has beta = 1: its blend is the hard target, whose top-N (exactly N ones per group) is
 // the hard target itself, so the final projection is h.  WANT_M: keep and write the
 // blend of step m_step.
-template <int S, int GM, bool HALVING, bool WANT_M>
+// PACK (2:4, K a multiple of 32): the unit's 8 bf16 weights are also packed under the hard
+// mask, as the 2:4 packer does from a given mask: per 4-group the two kept values
+// (positions p0 < p1, bytes 2p, 2p+1 of the group's 8) by one byte permute, and p0 | p1 << 2
+// as the group's index nibble; the 4 lanes of a quad hold 32 consecutive columns of one row
+// (the units of a row are consecutive and 4 | K/8), so their nibbles make one index word.
+// The gate is bound by its vector instructions, so the weight's stream rides along.
+struct GatePackOut {
+    const uint16_t* W;   // [R, ldw] bf16
+    int64_t ldw;
+    uint16_t* vals;      // [R, ldv] bf16 kept values
+    int64_t ldv;
+    uint32_t* idx;       // [R, ldi] 2-bit in-group positions
+    int64_t ldi;
+};
+
+template <int S, int GM, bool HALVING, bool WANT_M, bool PACK = false>
 __global__ __launch_bounds__(kRedThreads) void gate_fast_kernel(const float* __restrict__ Sc, int64_t R, int64_t K,
                                                                 int64_t lds, const double* __restrict__ stats, int N,
                                                                 float T0, float rho, int m_step, float* __restrict__ m_out,
                                                                 int64_t ldf, uint8_t* __restrict__ hard_mask, int64_t ldm,
-                                                                double* __restrict__ part) {
+                                                                double* __restrict__ part, GatePackOut po) {
+    static_assert(!PACK || GM == 4, "the fused pack is for 2:4");
     static_assert(S >= 2 && (GM == 4 || GM == 8), "fixed schedules of at least two steps, 2:4-like or 6:8-like groups");
     __shared__ double sh[kRedThreads];
     const double mu = stats[0], sigma = stats[1];
@@ -439,6 +455,26 @@ __global__ __launch_bounds__(kRedThreads) void gate_fast_kernel(const float* __r
         } else {
             if (N == 6) hbits = top6of8_bits(key);
             else hbits = topn_bits<8>(key, N);
+        }
+        if constexpr (PACK) {
+            const uint4 wv = *(const uint4*)(po.W + r * po.ldw + k0);
+            const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t packed[2], nib = 0;
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+                const uint32_t bits = (hbits >> (4 * gi)) & 0xFu;
+                const uint32_t p0 = __builtin_ctz(bits), p1 = 31u - __builtin_clz(bits);
+                const uint32_t s0 = 0x0100u + p0 * 0x0202u, s1 = 0x0100u + p1 * 0x0202u;
+                packed[gi] = __builtin_amdgcn_perm(wu[2 * gi + 1], wu[2 * gi], s0 | (s1 << 16));
+                nib |= (p0 | (p1 << 2)) << (4 * gi);
+            }
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u32x2_t{packed[0], packed[1]}, (u32x2_t*)(po.vals + r * po.ldv + (k0 >> 1)));
+            const int q = threadIdx.x & 3;
+            uint32_t v = nib << (8 * q);
+            v |= (uint32_t)__shfl_xor((int)v, 1);
+            v |= (uint32_t)__shfl_xor((int)v, 2);
+            if (q == 0) __builtin_nontemporal_store(v, po.idx + r * po.ldi + (k0 >> 5));
         }
         bool h[8];
 #pragma unroll
@@ -511,7 +547,7 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
     if (fast) {
 #define NM_GATE_FAST(GM, HV, WM)                                                                                        \
     hipLaunchKernelGGL((gate_fast_kernel<8, GM, HV, WM>), dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, stats, \
-                       N, T0, rho, m_step, m_out, ldf, hard_mask, ldm, part)
+                       N, T0, rho, m_step, m_out, ldf, hard_mask, ldm, part, GatePackOut{})
         const bool halving = rho == 0.5f, wm = m_out != nullptr;
         if (M == 4) {
             if (halving) {
@@ -550,6 +586,34 @@ void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double
     }
 #undef NM_GATE
     hipLaunchKernelGGL(gate_final_kernel, dim3((unsigned)steps), dim3(kRedThreads), 0, s, (const double*)part, lmid);
+}
+
+bool launch_gate_pack(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
+                      float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
+                      double* lmid, const uint16_t* W, int64_t ldw, uint16_t* vals, int64_t ldv, uint32_t* idx,
+                      int64_t ldi, void* ws, hipStream_t s) {
+    // the unrolled 8-step kernel on 2:4 with whole index words per row, 16-byte weight rows
+    // and 8-byte value rows
+    const bool fused = steps == 8 && M == 4 && N == 2 && K % 32 == 0 && lds % 4 == 0 && ((uintptr_t)S & 15) == 0 &&
+                       (m_out == nullptr || (ldf % 4 == 0 && ((uintptr_t)m_out & 15) == 0)) && ldw % 8 == 0 &&
+                       ((uintptr_t)W & 15) == 0 && ldv % 4 == 0 && ((uintptr_t)vals & 7) == 0;
+    if (!fused) return false;
+    double* part = (double*)ws;
+    const GatePackOut po{W, ldw, vals, ldv, idx, ldi};
+#define NM_GATE_PACK(HV, WM)                                                                                            \
+    hipLaunchKernelGGL((gate_fast_kernel<8, 4, HV, WM, true>), dim3(kGateBlocks), dim3(kRedThreads), 0, s, S, R, K, lds, \
+                       stats, N, T0, rho, m_step, m_out, ldf, hard_mask, ldm, part, po)
+    const bool halving = rho == 0.5f, wm = m_out != nullptr;
+    if (halving) {
+        if (wm) NM_GATE_PACK(true, true);
+        else NM_GATE_PACK(true, false);
+    } else {
+        if (wm) NM_GATE_PACK(false, true);
+        else NM_GATE_PACK(false, false);
+    }
+#undef NM_GATE_PACK
+    hipLaunchKernelGGL(gate_final_kernel, dim3((unsigned)steps), dim3(kRedThreads), 0, s, (const double*)part, lmid);
+    return true;
 }
 
 }  // namespace nm

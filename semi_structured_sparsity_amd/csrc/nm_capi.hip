@@ -290,6 +290,51 @@ nm_status nm_pack(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t ldw
     return check_launch(fn);
 }
 
+nm_status nm_gate_pack(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M,
+                       float T0, float rho, int steps, int m_step, float* m, int64_t ldf, uint8_t* hard_mask,
+                       int64_t ldm, double* lmid, const void* W, nm_dtype wdt, int64_t ldw, nm_dtype vdt, void* vals,
+                       int64_t ldv, uint32_t* idx, int64_t ldi, void* ws, size_t ws_bytes, nm_stream_t stream) {
+    const char* fn = "nm_gate_pack";
+    NM_REQ(R >= 0 && K >= 0, NM_ERR_SHAPE, "%s: negative size", fn);
+    nm_status st = check_pattern(N, M, fn);
+    if (st != NM_OK) return st;
+    NM_REQ(K % M == 0, NM_ERR_SHAPE, "%s: K %% M != 0", fn);
+    NM_REQ(steps >= 1 && steps <= 64, NM_ERR_SHAPE, "%s: steps must be in [1, 64]", fn);
+    NM_REQ(!m || (m_step >= 0 && m_step < steps), NM_ERR_SHAPE, "%s: m_step must be in [0, steps)", fn);
+    NM_REQ(T0 > 0.f && rho > 0.f, NM_ERR_SHAPE, "%s: T0 and rho must be positive", fn);
+    NM_REQ(stats && lmid, NM_ERR_NULL, "%s: stats / lmid is NULL", fn);
+    NM_REQ((S && hard_mask && W) || R * K == 0, NM_ERR_NULL, "%s: NULL pointer", fn);
+    NM_REQ(lds >= K && ldm >= (K + 7) / 8 && ldw >= K && (!m || ldf >= K), NM_ERR_SHAPE,
+           "%s: leading dimension too small", fn);
+    const size_t need = gate_ws(R, K, steps);
+    NM_REQ(ws && ws_bytes >= need, NM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    const int64_t slots = K / M * N, words = idx_words_needed(K, N, M);
+    if (R * K > 0) {
+        st = check_pack_out(fn, wdt, vdt, R, K, slots, words, vals, ldv, idx, ldi);
+        if (st != NM_OK) return st;
+    }
+    const Range outs[6] = {span(hard_mask, R, (K + 7) / 8, ldm, 1), span(m, R, K, ldf, 4),
+                           span(lmid, 1, steps, steps, 8), span(vals, R, slots, ldv, esize(vdt)),
+                           span(idx, R, words, ldi, 4), Range{(uintptr_t)ws, (uintptr_t)ws + need}};
+    const Range ins[3] = {span(S, R, K, lds, 4), span(stats, 1, 2, 2, 8), span(W, R, K, ldw, esize(wdt))};
+    for (const Range& x : ins)
+        for (const Range& y : outs)
+            NM_REQ(!overlap(x, y), NM_ERR_ALIAS, "%s: an output or the workspace overlaps an input", fn);
+    for (int a = 0; a < 6; ++a)
+        for (int b = a + 1; b < 6; ++b) NM_REQ(!overlap(outs[a], outs[b]), NM_ERR_ALIAS, "%s: outputs overlap", fn);
+    const int ms = m ? m_step : -1;
+    const bool fused = R * K > 0 && wdt == NM_BF16 && vdt == NM_BF16 &&
+                       launch_gate_pack(S, R, K, lds, stats, N, M, T0, rho, steps, ms, m, ldf, hard_mask, ldm, lmid,
+                                        (const uint16_t*)W, ldw, (uint16_t*)vals, ldv, idx, ldi, ws, (hipStream_t)stream);
+    if (!fused) {
+        // any other shape: the gate, then the pack of its hard mask on the same stream
+        launch_gate(S, R, K, lds, stats, N, M, T0, rho, steps, ms, m, ldf, hard_mask, ldm, lmid, ws, (hipStream_t)stream);
+        if (R * K > 0)
+            launch_pack(W, wdt, R, K, ldw, hard_mask, ldm, N, M, vdt, vals, ldv, idx, ldi, (hipStream_t)stream);
+    }
+    return check_launch(fn);
+}
+
 nm_status nm_prune_pack(const void* Wsc, nm_dtype sdt, int64_t ldsc, const float* H, int64_t ldh, float eps,
                         nm_score_mode mode, const void* Wv, nm_dtype wdt, int64_t ldwv, int64_t R, int64_t K, int N,
                         int M, uint8_t* mask, int64_t ldm, nm_dtype vdt, void* vals, int64_t ldv, uint32_t* idx,

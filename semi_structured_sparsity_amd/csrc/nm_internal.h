@@ -209,6 +209,12 @@ void launch_absmean(const void* W, nm_dtype wdt, int64_t R, int64_t K, int64_t l
 void launch_gate(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
                  float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
                  double* lmid, void* ws, hipStream_t s);
+// the gate with the 2:4 pack of bf16 W under its hard mask in the same pass; false (nothing
+// launched) where the fused kernel does not apply
+bool launch_gate_pack(const float* S, int64_t R, int64_t K, int64_t lds, const double* stats, int N, int M, float T0,
+                      float rho, int steps, int m_step, float* m_out, int64_t ldf, uint8_t* hard_mask, int64_t ldm,
+                      double* lmid, const uint16_t* W, int64_t ldw, uint16_t* vals, int64_t ldv, uint32_t* idx,
+                      int64_t ldi, void* ws, hipStream_t s);
 // sparse GEMM
 void launch_quant_lift(const void* X, int64_t Mtok, int64_t K, int64_t ldx, int Ns, nm_dtype qdt, void* Xq,
                        int64_t ldq, float* x_scale, hipStream_t s);

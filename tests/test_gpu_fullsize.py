@@ -177,6 +177,10 @@ def test_hessian24_full_size(nm):
     # early step element by element on the sampled rows and every step's L_mid over the
     # whole tensor (the oracle runs the full tensor once, rows in parallel)
     _, hm, lm_fast = nm.nm_gate(S, stats, 2, 4, T0, rho, steps, want_m=False)
+    # the benchmark's fused gate + pack pass gives the same mask, sums and packed weight
+    _, hm_f, lm_f, vals_f, idx_f = nm.nm_gate_pack(S, stats, Wd, 2, 4, T0, rho, steps, want_m=False)
+    assert torch.equal(hm_f, hm) and torch.equal(lm_f, lm_fast)
+    del hm_f, lm_f
     t_mid = 2
     m_mid, hm2, lm = nm.nm_gate(S, stats, 2, 4, T0, rho, steps, m_step=t_mid)
     assert torch.equal(hm, hm2) and torch.equal(lm, lm_fast)
@@ -191,6 +195,8 @@ def test_hessian24_full_size(nm):
     del S, m_mid, m_full, h_full
     # the annealed hard mask is 2:4: pack it and multiply at M = 8192
     vals, idx = nm.nm_pack(Wd, hm, 2, 4)
+    assert torch.equal(vals_f.view(torch.int16), vals.view(torch.int16)) and torch.equal(idx_f, idx)
+    del vals_f, idx_f
     v_ref, i_ref = O.pack(Wr, h_ref, 2, 4)
     assert np.array_equal(bf16_np(vals)[rows], v_ref) and np.array_equal(u32_np(idx)[rows], i_ref)
     M = 8192

@@ -261,3 +261,37 @@ def test_gate_default_schedule_kernels_agree(nm, N, M, rho):
             assert np.abs(a[0].cpu().numpy() - m_ref).max() <= 1e-5, t
             assert np.array_equal(a[1].cpu().numpy(), h_ref)
             assert np.allclose(a[2].cpu().numpy(), l_ref, rtol=1e-5, atol=1e-9)
+
+
+# nm_gate_pack: the fused 2:4 pass (default 8 steps, K a multiple of 32, bf16), ragged row
+# counts and both schedules of the fused kernel, and shapes that run the gate and then the
+# pack (K not a multiple of 32, 6:8, other step counts, f32 weights packed to bf16)
+@pytest.mark.parametrize("R,K,N,M,steps,rho,wdt", [(96, 512, 2, 4, 8, 0.5, "bf16"), (131, 1024, 2, 4, 8, 0.8, "bf16"),
+                                                   (64, 520, 2, 4, 8, 0.5, "bf16"), (40, 512, 6, 8, 8, 0.5, "bf16"),
+                                                   (50, 256, 2, 4, 5, 0.7, "bf16"), (33, 384, 2, 4, 8, 0.5, "f32")])
+def test_gate_pack_equals_gate_then_pack(nm, R, K, N, M, steps, rho, wdt):
+    g = np.random.default_rng(R + K + N + steps)
+    # scores with ties (a coarse grid) so that the top-N tie rule is exercised as well
+    S = np.round(g.standard_normal((R, K)) ** 2 * 8).astype(np.float32) / 8
+    Sd = torch.from_numpy(S).to(dev())
+    st = nm.nm_score_stats(Sd)
+    Wf = (g.standard_normal((R, K)) * 0.02).astype(np.float32)
+    W = np_bf16(O.f32_to_bf16(Wf)).to(dev()) if wdt == "bf16" else torch.from_numpy(Wf).to(dev())
+    for m_step in (None, 2):
+        mf, hm, lm = nm.nm_gate(Sd, st, N, M, 0.5, rho, steps, m_step=m_step)
+        v_ref, i_ref = nm.nm_pack(W, hm, N, M, vdt=nm.NM_BF16)
+        mf2, hm2, lm2, v, i = nm.nm_gate_pack(Sd, st, W, N, M, 0.5, rho, steps, m_step=m_step, vdt=nm.NM_BF16)
+        assert torch.equal(hm2, hm) and torch.equal(lm2, lm)
+        assert torch.equal(mf2.view(torch.int32), mf.view(torch.int32))
+        assert torch.equal(v.view(torch.int16), v_ref.view(torch.int16)) and torch.equal(i, i_ref)
+    # and against the oracle: the hard mask is the scores' top-N, the pack that of the weight under it
+    m_or = O.topn_mask(S, N, M)
+    assert np.array_equal(hm2.cpu().numpy(), m_or)
+    Wh = O.f32_to_bf16(Wf) if wdt == "bf16" else Wf
+    vo, io = O.pack(Wh, m_or, N, M, O.BF16)
+    assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), vo)
+    assert np.array_equal(i.cpu().numpy().view(np.uint32), io)
+    # without the blend output
+    _, hm3, lm3, v3, i3 = nm.nm_gate_pack(Sd, st, W, N, M, 0.5, rho, steps, want_m=False, vdt=nm.NM_BF16)
+    assert torch.equal(hm3, hm) and torch.equal(lm3, lm) and torch.equal(v3.view(torch.int16), v.view(torch.int16))
+    assert torch.equal(i3, i)
