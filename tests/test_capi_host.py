@@ -93,6 +93,15 @@ def test_validation_errors_without_gpu(nm):
         assert _st(nm, r.nm_gate(S, 4, 8, 8, S, 2, 4, 0.5, 0.5, 8, bad_t, M_, 8, Y, 1, S, S, 1 << 20,
                                  None)) == "NM_ERR_SHAPE"
         assert "m_step" in nm.last_error()
+    # gate + pack: the gate's rules, the pack's dtype rule, and no output over an input
+    P_ = lambda a: ctypes.c_void_p(a)
+    def gp(steps=8, W=P_(0x6000), vdt=1, vals=P_(0x7000)):
+        return _st(nm, r.nm_gate_pack(S, 4, 8, 8, P_(0x3000), 2, 4, 0.5, 0.5, steps, 7, None, 8, P_(0x5000), 1,
+                                      P_(0x4000), W, 1, 8, vdt, vals, 4, P_(0x8000), 1, P_(0x100000), 1 << 20, None))
+    assert gp(steps=0) == "NM_ERR_SHAPE"
+    assert gp(W=None) == "NM_ERR_NULL"
+    assert gp(vdt=2) == "NM_ERR_DTYPE"
+    assert gp(vals=P_(0x1040)) == "NM_ERR_ALIAS"
     # Hutchinson alignment rules
     assert _st(nm, r.nm_hdiag_hutchinson(S, 64, 100, 100, 8, 2, 1, Y, 100, S, 1 << 30, None)) == "NM_ERR_ALIGN"
     # pack dtype rule (bf16 weights cannot pack to int8)
