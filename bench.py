@@ -333,10 +333,12 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
         W = synth.llama24_weight(R, K, tensor_id=tid).to(dev)
         vals, idx, mask = (torch.empty((R, K // 2), dtype=bf, device=dev),
                            torch.empty((R, K // 32), dtype=i32, device=dev), torch.empty((R, K // 8), dtype=u8, device=dev))
-        row("llama24", "A3+A7+A8", f"prune_pack {lname} {R}x{K}", lambda: chk(r.nm_prune_pack(
-            W.data_ptr(), nm.NM_BF16, K, H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN, W.data_ptr(), nm.NM_BF16, K, R, K,
-            2, 4, mask.data_ptr(), K // 8, nm.NM_BF16, vals.data_ptr(), K // 2, idx.data_ptr(), K // 32, sh)), "hbm",
-            int(R * K * 3.25) + K * 4)
+        def prune_pack(Wc, R=R, vals=vals, idx=idx, mask=mask):
+            return lambda: chk(r.nm_prune_pack(
+                Wc.data_ptr(), nm.NM_BF16, K, H.data_ptr(), 0, EPS, nm.NM_SCORE_HESSIAN, Wc.data_ptr(), nm.NM_BF16, K, R,
+                K, 2, 4, mask.data_ptr(), K // 8, nm.NM_BF16, vals.data_ptr(), K // 2, idx.data_ptr(), K // 32, sh))
+        row("llama24", "A3+A7+A8", f"prune_pack {lname} {R}x{K}", prune_pack(W), "hbm", int(R * K * 3.25) + K * 4,
+            stream_of=(prune_pack, (W,)))
         for M in (1, 16, 128, 2048):
             X = synth.activations_bf16(1, M, K).to(dev)
             Y = torch.empty((M, R), dtype=bf, device=dev)
@@ -471,14 +473,18 @@ def measure_rows(nm, torch, synth, dev, reps: int = 5):
     Wf, Wt = Wf.to(dev), Wt.to(dev)
     vals, idx, mask = (torch.empty((R, Kl // 2), dtype=i8, device=dev), torch.empty((R, Kl // 32), dtype=i32, device=dev),
                        torch.empty((R, K // 8), dtype=u8, device=dev))
-    row("ternary68", "A3+A7+A9+A10", "prune_slide 6912x2560 (|W_fp| mask on W_t)", lambda: chk(r.nm_prune_slide(
-        Wf.data_ptr(), nm.NM_BF16, K, None, 0, 0.0, nm.NM_SCORE_MAGNITUDE, Wt.data_ptr(), nm.NM_I8, K, R, K, Ns,
-        mask.data_ptr(), K // 8, nm.NM_I8, vals.data_ptr(), Kl // 2, idx.data_ptr(), Kl // 32, sh)), "hbm",
-        R * K * (2 + 1 + 0.75 + 0.1875 + 0.125))
+    def prune_slide_t(Wfc, Wtc):
+        return lambda: chk(r.nm_prune_slide(
+            Wfc.data_ptr(), nm.NM_BF16, K, None, 0, 0.0, nm.NM_SCORE_MAGNITUDE, Wtc.data_ptr(), nm.NM_I8, K, R, K, Ns,
+            mask.data_ptr(), K // 8, nm.NM_I8, vals.data_ptr(), Kl // 2, idx.data_ptr(), Kl // 32, sh))
+    row("ternary68", "A3+A7+A9+A10", "prune_slide 6912x2560 (|W_fp| mask on W_t)", prune_slide_t(Wf, Wt), "hbm",
+        R * K * (2 + 1 + 0.75 + 0.1875 + 0.125), stream_of=(prune_slide_t, (Wf, Wt)))
     alpha = torch.empty(1, dtype=f32, device=dev)
     wsa = ws_for(r.nm_stats_workspace(R, K))
-    row("ternary68", "A10", "absmean 6912x2560", lambda: chk(r.nm_absmean(
-        Wf.data_ptr(), nm.NM_BF16, R, K, K, alpha.data_ptr(), wsa.data_ptr(), wsa.numel(), sh)), "hbm", R * K * 2)
+    def absmean(Wfc):
+        return lambda: chk(r.nm_absmean(Wfc.data_ptr(), nm.NM_BF16, R, K, K, alpha.data_ptr(), wsa.data_ptr(),
+                                        wsa.numel(), sh))
+    row("ternary68", "A10", "absmean 6912x2560", absmean(Wf), "hbm", R * K * 2, stream_of=(absmean, (Wf,)))
     # the online step before the int8 product, from bf16 activations (SlideSparse 2B/2C)
     Mq = 2048
     Xb = synth.ternary68_activations_bf16(Mq, K).to(dev)
