@@ -116,7 +116,8 @@ def test_spmm_bf16_integer_exact(nm, Mt, R, K, Ns):
 FEW = [(1, 1, 16), (2, 300, 48), (3, 257, 4160), (4, 130, 32), (1, 513, 2560), (4, 64, 4096), (1, 1000, 96),
        (32, 200, 4096), (17, 130, 2048),   # X resident in LDS: a full 64 KB range, and 17 valid rows
        (1, 4096, 4096), (2, 4100, 4096),   # resident X rows of the whole K on many row tiles
-       (1, 11008, 1024), (17, 9001, 512), (64, 10000, 256), (40, 14336, 768)]   # row tiles of R / CUs rows
+       (1, 11008, 1024), (17, 9001, 512), (64, 10000, 256), (40, 14336, 768),   # row tiles of R / CUs rows
+       (1, 5000, 1024), (16, 5120, 512)]   # 16-31 rows where the K split would not fill whole rounds
 
 
 @pytest.mark.parametrize("Mt,R,K", FEW)
