@@ -295,3 +295,63 @@ def test_gate_pack_equals_gate_then_pack(nm, R, K, N, M, steps, rho, wdt):
     _, hm3, lm3, v3, i3 = nm.nm_gate_pack(Sd, st, W, N, M, 0.5, rho, steps, want_m=False, vdt=nm.NM_BF16)
     assert torch.equal(hm3, hm) and torch.equal(lm3, lm) and torch.equal(v3.view(torch.int16), v.view(torch.int16))
     assert torch.equal(i3, i)
+
+
+def test_step_calls_graph_replays(nm):
+    """The benchmark step's three calls (fused Hutchinson score, gate + pack, sparse product)
+    captured in one HIP graph and replayed several times, outputs overwritten before each
+    replay and eager calls of other shapes on the same workspaces in between: every replay
+    reproduces the eager step bit for bit."""
+    r = nm.raw
+    g = np.random.default_rng(31)
+    n, K, R, P, steps, Mt = 256, 1024, 512, 4, 8, 300
+    X = np_bf16(O.f32_to_bf16(g.standard_normal((n, K)))).to(dev())
+    W = np_bf16(O.f32_to_bf16(g.standard_normal((R, K)) * 0.015)).to(dev())
+    X2 = np_bf16(O.f32_to_bf16(g.standard_normal((Mt, K)))).to(dev())
+    S0, st0 = nm.nm_hutchinson_score(X, W, P, 5, 1e-6)
+    _, hm0, lm0, v0, i0 = nm.nm_gate_pack(S0, st0, W, 2, 4, 0.5, 0.5, steps, want_m=False)
+    Y0 = nm.nm_spmm(X2, v0, i0)
+    refs = [t.clone() for t in (S0, st0, hm0, lm0, v0, i0, Y0)]
+    u8 = torch.uint8
+    S, st = torch.empty_like(S0), torch.empty_like(st0)
+    hm, lm, v, i, Y = torch.empty_like(hm0), torch.empty_like(lm0), torch.empty_like(v0), torch.empty_like(i0), \
+        torch.empty_like(Y0)
+    wsh = torch.empty(r.nm_hutchinson_score_workspace(n, K, R, P), dtype=u8, device=dev())
+    wsg = torch.empty(r.nm_gate_workspace(R, K, steps), dtype=u8, device=dev())
+    wsy = torch.empty(max(1, r.nm_spmm_workspace(Mt, K, R, 0, nm.NM_BF16)), dtype=u8, device=dev())
+
+    def chk(code):
+        assert code == 0, nm.last_error()
+
+    def step(sh):
+        chk(r.nm_hutchinson_score(X.data_ptr(), n, K, K, R, P, 5, W.data_ptr(), nm.NM_BF16, K, 1e-6, S.data_ptr(), K,
+                                  st.data_ptr(), wsh.data_ptr(), wsh.numel(), sh))
+        chk(r.nm_gate_pack(S.data_ptr(), R, K, K, st.data_ptr(), 2, 4, 0.5, 0.5, steps, steps - 1, None, K,
+                           hm.data_ptr(), K // 8, lm.data_ptr(), W.data_ptr(), nm.NM_BF16, K, nm.NM_BF16, v.data_ptr(),
+                           K // 2, i.data_ptr(), K // 32, wsg.data_ptr(), wsg.numel(), sh))
+        chk(r.nm_spmm(X2.data_ptr(), nm.NM_BF16, Mt, K, K, v.data_ptr(), nm.NM_BF16, i.data_ptr(), R, K // 2, K // 32,
+                      0, None, 1.0, Y.data_ptr(), nm.NM_BF16, R, wsy.data_ptr(), wsy.numel(), sh))
+
+    step(torch.cuda.current_stream().cuda_stream)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream().cuda_stream)
+    Xo = np_bf16(O.f32_to_bf16(g.standard_normal((128, K)))).to(dev())
+    Wo = np_bf16(O.f32_to_bf16(g.standard_normal((256, K)) * 0.015)).to(dev())
+    for rep in range(4):
+        for t in (S, st, hm, lm, v, i, Y):
+            t.view(torch.uint8).fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((S, st, hm, lm, v, i, Y), refs):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+        if rep % 2 == 0:   # eager calls of other shapes on the same workspaces
+            sh = torch.cuda.current_stream().cuda_stream
+            So = torch.empty((256, K), dtype=torch.float32, device=dev())
+            chk(r.nm_hutchinson_score(Xo.data_ptr(), 128, K, K, 256, 2, 9, Wo.data_ptr(), nm.NM_BF16, K, 1e-6,
+                                      So.data_ptr(), K, st.data_ptr(), wsh.data_ptr(), wsh.numel(), sh))
+            chk(r.nm_gate_pack(So.data_ptr(), 256, K, K, st.data_ptr(), 2, 4, 0.5, 0.8, steps, steps - 1, None, K,
+                               hm.data_ptr(), K // 8, lm.data_ptr(), Wo.data_ptr(), nm.NM_BF16, K, nm.NM_BF16,
+                               v.data_ptr(), K // 2, i.data_ptr(), K // 32, wsg.data_ptr(), wsg.numel(), sh))
+            torch.cuda.synchronize()
