@@ -295,6 +295,12 @@ def test_gate_pack_equals_gate_then_pack(nm, R, K, N, M, steps, rho, wdt):
     _, hm3, lm3, v3, i3 = nm.nm_gate_pack(Sd, st, W, N, M, 0.5, rho, steps, want_m=False, vdt=nm.NM_BF16)
     assert torch.equal(hm3, hm) and torch.equal(lm3, lm) and torch.equal(v3.view(torch.int16), v.view(torch.int16))
     assert torch.equal(i3, i)
+    # a weight view 4 bytes off 16-byte alignment (padded rows): the gate, then the pack
+    Wp = torch.zeros((R, K + 8), dtype=W.dtype, device=dev())
+    Wp[:, 2:K + 2] = W
+    _, hm4, lm4, v4, i4 = nm.nm_gate_pack(Sd, st, Wp[:, 2:K + 2], N, M, 0.5, rho, steps, want_m=False, vdt=nm.NM_BF16)
+    assert torch.equal(hm4, hm) and torch.equal(lm4, lm) and torch.equal(v4.view(torch.int16), v.view(torch.int16))
+    assert torch.equal(i4, i)
 
 
 def test_step_calls_graph_replays(nm):
