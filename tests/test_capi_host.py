@@ -175,3 +175,16 @@ def test_spmm_workspace_covers_every_plan(nm):
     # every plan of the lifted product includes the lifted activation
     assert r.nm_spmm_workspace(16, 4096, 14336, 4, nm.NM_BF16) >= 16 * 6144 * 2
     assert r.nm_spmm_workspace(16, 3072, 1024, 3, nm.NM_I8) >= 16 * 4096
+
+
+def test_device_error_without_gpu(nm):
+    """With no GPU, a call that passes validation reports NM_ERR_DEVICE from its launch (with
+    the runtime's message), rather than failing silently.  Skipped where a GPU is visible:
+    the call's pointers are fake."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this check launches on placeholder pointers")
+    r = nm.raw
+    S, mask = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x100000)
+    assert _st(nm, r.nm_mask(S, 4, 8, 8, 2, 4, mask, 1, None)) == "NM_ERR_DEVICE"
+    assert "nm_mask" in nm.last_error()
